@@ -1,0 +1,124 @@
+"""Seeded synthetic inputs for the DeltaProduct forward workloads.
+
+This module only draws inputs.  It holds none of the forward's arithmetic
+(no key normalisation, no beta range, no recurrence); both the HIP path and
+the fp64 oracle consume the tensors it returns, byte for byte.
+
+Recipe (shapes and distributions of the workloads the DeltaProduct and OSDN
+study-note pages describe; no dataset or trained weight is involved):
+
+* one CPU ``torch.Generator`` per workload, seeded ``1000 + id``;
+* every draw is fp32 N(0, 1), taken in the fixed order q, k, v, beta, g, h0;
+* q: N(0,1) scaled to unit L2 norm per (b, t, h)  -> ``[B, L, H, dk]``;
+* k: SiLU(N(0,1)) per sub-step, passed *unnormalised* (the forward normalises
+  read keys itself), or plain N(0,1) for the asymmetric-write-key workload
+  -> ``[B, L, H, n_h, dk]``;
+* v: N(0,1) (times ``v_scale``) -> ``[B, L, H, n_h, dv]``;
+* beta: 2*sigmoid(N(0,1)) in (0, 2), or sigmoid(N(0,1)) in (0, 1) ->
+  ``[B, L, H, n_h]`` fp32;
+* g (gated workload only): exp(-softplus(N(0,1))) in (0, 1] -> ``[B, L, H]``
+  fp32;
+* h0 (where used): N(0,1) * 0.1 fp32 (variance 0.01) -> ``[B, H, dk, dv]``;
+* q, k, v are then stored in the path dtype (fp32, or bf16 rounded to
+  nearest-even by torch); beta, g and h0 always stay fp32.
+"""
+from dataclasses import dataclass, replace
+from typing import Optional
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    cid: int            # workload id; seed = 1000 + cid
+    B: int
+    H: int
+    L: int
+    n_h: int
+    dk: int
+    dv: int
+    chunk: int
+    dtype: str          # "f32" or "bf16": storage type of q, k, v and out
+    key: str = "silu"   # "silu": SiLU(N(0,1)) ; "normal": N(0,1)
+    v_scale: float = 1.0
+    beta: str = "2sig"  # "2sig": 2*sigmoid(N) ; "sig": sigmoid(N)
+    gate: bool = False
+    h0_std: float = 0.0  # 0: no initial state
+    asym: bool = False   # write keys come from the OSDN phase-1 scan
+
+    @property
+    def seed(self) -> int:
+        return 1000 + self.cid
+
+    @property
+    def tokens(self) -> int:
+        return self.B * self.L
+
+    def scaled(self, **kw) -> "Workload":
+        """Same recipe, other sizes or seed (e.g. a small parity case)."""
+        return replace(self, **kw)
+
+
+WORKLOADS = {
+    # tiny fp32 case: B1 H1 L64 n_h2 dk=dv=16 chunk16
+    "c1": Workload("c1", 1, B=1, H=1, L=64, n_h=2, dk=16, dv=16, chunk=16, dtype="f32"),
+    # bf16 inputs, fp32 state: B4 H8 L2048 n_h2 d64 chunk64
+    "c2": Workload("c2", 2, B=4, H=8, L=2048, n_h=2, dk=64, dv=64, chunk=64, dtype="bf16"),
+    # LM-layer shape: B4 H16 L4096 n_h3 d128 chunk64, v / sqrt(128)
+    "c3": Workload("c3", 3, B=4, H=16, L=4096, n_h=3, dk=128, dv=128, chunk=64, dtype="bf16",
+                   v_scale=128 ** -0.5),
+    # the same shape with n_h = 2 (the headline metric names n_h = 2 and 3)
+    "c3b": Workload("c3b", 32, B=4, H=16, L=4096, n_h=2, dk=128, dv=128, chunk=64,
+                    dtype="bf16", v_scale=128 ** -0.5),
+    # gated, with an initial state: B2 H16 L8192 n_h2 d128 chunk64
+    "c4": Workload("c4", 4, B=2, H=16, L=8192, n_h=2, dk=128, dv=128, chunk=64, dtype="bf16",
+                   gate=True, h0_std=0.1),
+    # asymmetric write key (OSDN phase 1 + phase 2): B8 H16 L4096 n_h1 d128 chunk64
+    "c5": Workload("c5", 5, B=8, H=16, L=4096, n_h=1, dk=128, dv=128, chunk=64, dtype="bf16",
+                   key="normal", beta="sig", asym=True),
+}
+
+
+def torch_dtype(name: str) -> torch.dtype:
+    return {"f32": torch.float32, "bf16": torch.bfloat16}[name]
+
+
+def make(w: Workload, seed: Optional[int] = None) -> dict:
+    """Draw the inputs of workload ``w`` on the CPU.
+
+    Returns a dict with ``q, k, v, beta, g, h0`` (g/h0 may be None) as CPU
+    tensors in their stored dtypes, plus ``n_h`` and ``chunk``.
+    """
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(w.seed if seed is None else seed)
+    B, L, H, n_h, dk, dv = w.B, w.L, w.H, w.n_h, w.dk, w.dv
+
+    def normal(*shape):
+        return torch.randn(*shape, generator=gen, dtype=torch.float32)
+
+    q = normal(B, L, H, dk)
+    q = q / q.norm(dim=-1, keepdim=True).clamp_min(1e-30)
+    k = normal(B, L, H, n_h, dk)
+    if w.key == "silu":
+        k = torch.nn.functional.silu(k)
+    v = normal(B, L, H, n_h, dv) * w.v_scale
+    braw = normal(B, L, H, n_h)
+    beta = 2.0 * torch.sigmoid(braw) if w.beta == "2sig" else torch.sigmoid(braw)
+    g = None
+    if w.gate:
+        g = torch.exp(-torch.nn.functional.softplus(normal(B, L, H)))
+    h0 = None
+    if w.h0_std > 0:
+        h0 = normal(B, H, dk, dv) * w.h0_std
+    dt = torch_dtype(w.dtype)
+    return {
+        "q": q.to(dt).contiguous(),
+        "k": k.to(dt).contiguous(),
+        "v": v.to(dt).contiguous(),
+        "beta": beta.contiguous(),
+        "g": None if g is None else g.contiguous(),
+        "h0": None if h0 is None else h0.contiguous(),
+        "n_h": n_h,
+        "chunk": w.chunk,
+    }

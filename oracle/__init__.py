@@ -1,0 +1,151 @@
+"""fp64 CPU oracle for the DeltaProduct forward and the OSDN phase-1 scan.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, ``__graft_entry__.smoke()`` and the
+benchmark's ``cpu_baseline`` leg may import this package.  The product path
+(``linear_rnn_sequence_amd``) never imports it and shares no code with it.
+
+The arithmetic lives in ``dp_oracle.c`` (plain sequential loops in IEEE
+double, one sub-step at a time); this module only converts arrays to
+contiguous float64 and calls it through ctypes.  Sources, by page title:
+
+* "DeltaProduct: Improving State-Tracking in Linear RNNs via Householder
+  Products" -- sec. 2.1 Eq.(2) (delta rule), sec. 2.2 Eq.(3) (n_h ordered
+  generalized-Householder sub-steps), sec. 2.6 (per-token gate applied before
+  the sub-steps; readout H^T q), sec. 4.1 / Sec.5.1 (only each token's last
+  sub-step is read out).
+* "OSDN: Improving Delta Rule with Provable Online Preconditioning in Linear
+  Attention" -- sec. 2.2 Eqs.(2)/(5) (asymmetric write key), sec. 2.4 Alg.1
+  (phase-1 preconditioner, emit-then-update).
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_LIB = None
+_D = ctypes.POINTER(ctypes.c_double)
+_LP = ctypes.POINTER(ctypes.c_long)
+
+
+def _load():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        lib = ctypes.CDLL(_build.LIB)
+        lib.oracle_fwd.restype = ctypes.c_int
+        lib.oracle_fwd.argtypes = [_D, _D, _D, _D, _D, _D, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   _D, _D, _D, ctypes.c_int]
+        lib.oracle_fwd_heads.restype = ctypes.c_int
+        lib.oracle_fwd_heads.argtypes = [_D, _D, _D, _D, _D, _D, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int, _D, _LP, ctypes.c_int, _D, _D,
+                                         ctypes.c_int]
+        lib.oracle_precond.restype = ctypes.c_int
+        lib.oracle_precond.argtypes = [_D, _D, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_double, ctypes.c_double,
+                                       ctypes.c_double, ctypes.c_double, _D, _D,
+                                       ctypes.c_int]
+        lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_num_threads.argtypes = []
+        _LIB = lib
+    return _LIB
+
+
+def _f64(x):
+    """Contiguous float64 numpy copy (exact upcast of fp32 / bf16 values)."""
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # torch tensor
+        x = x.detach().to("cpu")
+        import torch
+        x = x.to(torch.float64).numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(_D)
+
+
+def num_threads() -> int:
+    """Threads the oracle's OpenMP loops use by default."""
+    return _load().oracle_num_threads()
+
+
+def _shapes(q, k, v, beta, g, kt, h0):
+    if q.ndim != 4 or k.ndim != 5 or v.ndim != 5 or beta.ndim != 4:
+        raise ValueError("expected q[B,L,H,dk], k[B,L,H,n_h,dk], v[B,L,H,n_h,dv], beta[B,L,H,n_h]")
+    B, L, H, dk = q.shape
+    n_h = k.shape[3]
+    dv = v.shape[4]
+    if k.shape != (B, L, H, n_h, dk) or v.shape != (B, L, H, n_h, dv):
+        raise ValueError("shape mismatch between q, k, v")
+    if beta.shape != (B, L, H, n_h):
+        raise ValueError("beta must be [B,L,H,n_h]")
+    if g is not None and g.shape != (B, L, H):
+        raise ValueError("g must be [B,L,H]")
+    if kt is not None and kt.shape != k.shape:
+        raise ValueError("kt must have the shape of k")
+    if h0 is not None and h0.shape != (B, H, dk, dv):
+        raise ValueError("h0 must be [B,H,dk,dv]")
+    return B, L, H, n_h, dk, dv
+
+
+def fwd(q, k, v, beta, g=None, kt=None, h0=None, nthreads=0):
+    """Sequential fp64 forward over every head.
+
+    Returns ``(out [B,L,H,dv], final_state [B,H,dk,dv])`` as float64 arrays.
+    """
+    q, k, v, beta, g, kt, h0 = (_f64(a) for a in (q, k, v, beta, g, kt, h0))
+    B, L, H, n_h, dk, dv = _shapes(q, k, v, beta, g, kt, h0)
+    out = np.zeros((B, L, H, dv), np.float64)
+    fs = np.zeros((B, H, dk, dv), np.float64)
+    rc = _load().oracle_fwd(_ptr(q), _ptr(k), _ptr(kt), _ptr(v), _ptr(beta), _ptr(g), n_h, B,
+                            H, L, dk, dv, _ptr(h0), _ptr(out), _ptr(fs), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_fwd failed ({rc})")
+    return out, fs
+
+
+def fwd_heads(q, k, v, beta, heads, g=None, kt=None, h0=None, nthreads=0):
+    """Forward for the listed flattened heads ``b*H + h`` only.
+
+    Returns compact ``(out [n,L,dv], final_state [n,dk,dv])``; each head is
+    computed exactly as :func:`fwd` computes it.
+    """
+    q, k, v, beta, g, kt, h0 = (_f64(a) for a in (q, k, v, beta, g, kt, h0))
+    B, L, H, n_h, dk, dv = _shapes(q, k, v, beta, g, kt, h0)
+    hs = np.ascontiguousarray(np.asarray(heads, dtype=np.int64))
+    n = hs.size
+    out = np.zeros((n, L, dv), np.float64)
+    fs = np.zeros((n, dk, dv), np.float64)
+    rc = _load().oracle_fwd_heads(_ptr(q), _ptr(k), _ptr(kt), _ptr(v), _ptr(beta), _ptr(g),
+                                  n_h, B, H, L, dk, dv, _ptr(h0), hs.ctypes.data_as(_LP), n,
+                                  _ptr(out), _ptr(fs), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_fwd_heads failed ({rc})")
+    return out, fs
+
+
+def precond(k, beta, eta=3e-3, dmin=0.5, dmax=2.0, eps=1e-6, d0=None, nthreads=0):
+    """OSDN phase 1 over ``k [B,L,H,dk]`` (raw keys) and ``beta [B,L,H]``.
+
+    Returns ``(kt [B,L,H,dk], d_final [B,H,dk])``; ``d0`` defaults to ones.
+    """
+    k = _f64(k)
+    beta = _f64(beta)
+    if k.ndim != 4 or beta.shape != k.shape[:3]:
+        raise ValueError("expected k[B,L,H,dk] and beta[B,L,H]")
+    B, L, H, dk = k.shape
+    d = np.ones((B, H, dk), np.float64) if d0 is None else _f64(d0).copy()
+    if d.shape != (B, H, dk):
+        raise ValueError("d0 must be [B,H,dk]")
+    kt = np.zeros((B, L, H, dk), np.float64)
+    rc = _load().oracle_precond(_ptr(k), _ptr(beta), B, H, L, dk, float(eta), float(dmin),
+                                float(dmax), float(eps), _ptr(d), _ptr(kt), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_precond failed ({rc})")
+    return kt, d

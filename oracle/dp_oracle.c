@@ -1,0 +1,275 @@
+/*
+ * dp_oracle.c -- slow, plain fp64 CPU oracle for the DeltaProduct forward
+ * recurrence and the OSDN phase-1 preconditioner scan.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file; only the tests, the smoke check and the benchmark's CPU
+ * baseline leg use it.  It shares no code, header, table or helper with the
+ * HIP kernels.
+ *
+ * Sources (titles of the pages this follows):
+ *   [DP]   "DeltaProduct: Improving State-Tracking in Linear RNNs via
+ *          Householder Products" (study notes, arXiv 2502.10297v7).
+ *   [OSDN] "OSDN: Improving Delta Rule with Provable Online Preconditioning
+ *          in Linear Attention" (study notes, arXiv 2605.13473v1).
+ *
+ * What is computed is the plain sequential definition, one sub-step at a
+ * time, in the order the pages state it:
+ *   - per token, optional scalar forget gate applied once, before the first
+ *     Householder sub-step ([DP] sec. 2.6, gated DeltaProduct; the
+ *     conceptual per-token pseudocode there);
+ *   - per sub-step j: unit key k = k_raw / max(|k_raw|_2, 1e-6)
+ *     ([DP] sec. 2.2, key normalisation), beta clamped to [0, 2]
+ *     ([DP] sec. 2.5, the range where every factor has spectral norm <= 1),
+ *     prediction error e = v - H^T k, then H += beta * w e^T
+ *     ([DP] sec. 2.1 Eq.(2) delta rule and sec. 2.2 Eq.(3)); the write key
+ *     w is k itself, or a separately supplied write key for the asymmetric
+ *     rule ([OSDN] sec. 2.2, Eqs.(2)/(5): residual with the read key, write
+ *     with the scaled key);
+ *   - readout o = H^T q after the token's last sub-step ([DP] sec. 2.6 and
+ *     sec. 4.1 / Sec.5.1: only the last sub-step of each token is kept).
+ * Phase 1 of OSDN ([OSDN] sec. 2.4, Alg.1): emit d_t * k_t first, then
+ * d <- clamp(d + eta*beta*(1 - beta<d, k*k>)/max(|k|^2, eps) * (k*k)).
+ *
+ * All arithmetic is IEEE double, in the order written, no blocking, fusion or
+ * reordering.  Heads (b, h) are independent, so they are spread over OpenMP
+ * threads; each head runs strictly sequentially.
+ *
+ * Layouts (row-major, all double):
+ *   q     [B, L, H, dk]
+ *   k     [B, L, H, n_h, dk]   raw keys (normalised here)
+ *   kt    [B, L, H, n_h, dk]   write keys, used as given (NULL: symmetric)
+ *   v     [B, L, H, n_h, dv]
+ *   beta  [B, L, H, n_h]
+ *   g     [B, L, H]            (NULL: no gate)
+ *   h0    [B, H, dk, dv]       initial state (NULL: zero)
+ *   out   [B, L, H, dv]
+ *   final_state [B, H, dk, dv] (NULL: not returned)
+ * The state H of a head is dk x dv (key dimension by value dimension), the
+ * orientation of [DP] sec. 2.1; [OSDN] uses its transpose S = H^T.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_KEY_EPS 1e-6
+
+static double clampd(double x, double lo, double hi)
+{
+    if (x < lo) return lo;
+    if (x > hi) return hi;
+    return x;
+}
+
+/* unit read key: k / max(|k|_2, 1e-6)  ([DP] sec. 2.2) */
+static void unit_key(const double* kr, int dk, double* kh)
+{
+    double n2 = 0.0;
+    for (int r = 0; r < dk; ++r) n2 += kr[r] * kr[r];
+    double nrm = sqrt(n2);
+    double den = nrm > ORACLE_KEY_EPS ? nrm : ORACLE_KEY_EPS;
+    for (int r = 0; r < dk; ++r) kh[r] = kr[r] / den;
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/*
+ * One head (b, h) of the sequential DeltaProduct forward ([DP] sec. 2.2
+ * Eq.(3), sec. 2.6), with an optional asymmetric write key ([OSDN] sec. 2.2).
+ * out_h points at this head's first output row; consecutive tokens are
+ * out_stride doubles apart.  S (dk*dv), kh (dk) and e (dv) are scratch.
+ */
+static void run_head(const double* q, const double* k, const double* kt, const double* v,
+                     const double* beta, const double* g, int n_h, long b, long h, int H,
+                     int L, int dk, int dv, const double* h0_h, double* out_h,
+                     size_t out_stride, double* fs_h, double* S, double* kh, double* e)
+{
+    if (h0_h)
+        memcpy(S, h0_h, sizeof(double) * (size_t)dk * dv);
+    else
+        memset(S, 0, sizeof(double) * (size_t)dk * dv);
+
+    for (long t = 0; t < L; ++t) {
+        const size_t tok = ((size_t)b * L + t) * H + h; /* (b, t, h) */
+        if (g) {
+            /* H_{i,0} = g_i H_{i-1}: once per token, before its sub-steps */
+            const double gt = g[tok];
+            for (size_t x = 0; x < (size_t)dk * dv; ++x) S[x] *= gt;
+        }
+        for (int j = 0; j < n_h; ++j) {
+            const size_t sub = tok * n_h + j; /* (b, t, h, j) */
+            unit_key(k + sub * dk, dk, kh);
+            const double bt = clampd(beta[sub], 0.0, 2.0);
+            const double* w = kt ? kt + sub * dk : kh;
+            const double* vv = v + sub * dv;
+            /* e = v - H^T k  (prediction error on the read key) */
+            for (int c = 0; c < dv; ++c) {
+                double acc = 0.0;
+                for (int r = 0; r < dk; ++r) acc += S[(size_t)r * dv + c] * kh[r];
+                e[c] = vv[c] - acc;
+            }
+            /* H += beta * w e^T */
+            for (int r = 0; r < dk; ++r) {
+                const double bw = bt * w[r];
+                for (int c = 0; c < dv; ++c) S[(size_t)r * dv + c] += bw * e[c];
+            }
+        }
+        /* o = H^T q after the token's last sub-step */
+        const double* qq = q + tok * dk;
+        double* oo = out_h + (size_t)t * out_stride;
+        for (int c = 0; c < dv; ++c) {
+            double acc = 0.0;
+            for (int r = 0; r < dk; ++r) acc += S[(size_t)r * dv + c] * qq[r];
+            oo[c] = acc;
+        }
+    }
+    if (fs_h) memcpy(fs_h, S, sizeof(double) * (size_t)dk * dv);
+}
+
+/*
+ * Forward over the heads listed in heads[0..nsel) (flattened b * H + h), or
+ * over all B*H heads when heads is NULL.  With heads == NULL, out is the full
+ * [B, L, H, dv] tensor and final_state [B, H, dk, dv]; with a list, both are
+ * compact: out [nsel, L, dv], final_state [nsel, dk, dv].  Returns 0, -1 on
+ * bad arguments, -2 when scratch memory could not be allocated.
+ */
+static int fwd_impl(const double* q, const double* k, const double* kt, const double* v,
+                    const double* beta, const double* g, int n_h, int B, int H, int L,
+                    int dk, int dv, const double* h0, const long* heads, int nsel,
+                    double* out, double* final_state, int nthreads)
+{
+    if (!q || !k || !v || !beta || !out) return -1;
+    if (n_h < 1 || B < 0 || H < 0 || L < 0 || dk < 1 || dv < 1) return -1;
+    const long nbh = (long)B * H;
+    const long nrun = heads ? nsel : nbh;
+    if (heads) {
+        if (nsel < 0) return -1;
+        for (long i = 0; i < nsel; ++i)
+            if (heads[i] < 0 || heads[i] >= nbh) return -1;
+    }
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#else
+    (void)nthreads;
+#endif
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads) reduction(| : bad)
+    for (long i = 0; i < nrun; ++i) {
+        const long bh = heads ? heads[i] : i;
+        const long b = bh / H, h = bh % H;
+        double* S = (double*)malloc(sizeof(double) * (size_t)dk * dv);
+        double* kh = (double*)malloc(sizeof(double) * (size_t)dk);
+        double* e = (double*)malloc(sizeof(double) * (size_t)dv);
+        if (!S || !kh || !e) {
+            free(S); free(kh); free(e);
+            bad |= 1;
+            continue;
+        }
+        const double* h0_h = h0 ? h0 + (size_t)bh * dk * dv : NULL;
+        double* out_h;
+        size_t out_stride;
+        double* fs_h;
+        if (heads) {
+            out_h = out + (size_t)i * L * dv;
+            out_stride = (size_t)dv;
+            fs_h = final_state ? final_state + (size_t)i * dk * dv : NULL;
+        } else {
+            out_h = out + ((size_t)b * L * H + h) * dv;
+            out_stride = (size_t)H * dv;
+            fs_h = final_state ? final_state + (size_t)bh * dk * dv : NULL;
+        }
+        run_head(q, k, kt, v, beta, g, n_h, b, h, H, L, dk, dv, h0_h, out_h, out_stride,
+                 fs_h, S, kh, e);
+        free(S); free(kh); free(e);
+    }
+    return bad ? -2 : 0;
+}
+
+/* Full forward over all heads.  nthreads <= 0: OpenMP default. */
+int oracle_fwd(const double* q, const double* k, const double* kt, const double* v,
+               const double* beta, const double* g, int n_h, int B, int H, int L,
+               int dk, int dv, const double* h0, double* out, double* final_state,
+               int nthreads)
+{
+    return fwd_impl(q, k, kt, v, beta, g, n_h, B, H, L, dk, dv, h0, NULL, 0, out,
+                    final_state, nthreads);
+}
+
+/*
+ * Forward for a subset of heads (sampled checks of large workloads): each
+ * listed head is computed exactly as oracle_fwd computes it; outputs compact.
+ */
+int oracle_fwd_heads(const double* q, const double* k, const double* kt, const double* v,
+                     const double* beta, const double* g, int n_h, int B, int H, int L,
+                     int dk, int dv, const double* h0, const long* heads, int nsel,
+                     double* out, double* final_state, int nthreads)
+{
+    if (!heads) return -1;
+    return fwd_impl(q, k, kt, v, beta, g, n_h, B, H, L, dk, dv, h0, heads, nsel, out,
+                    final_state, nthreads);
+}
+
+/*
+ * OSDN phase 1 ([OSDN] sec. 2.3-2.4, Alg.1), per head, sequential over
+ * tokens.  Keys are [B, L, H, dk] raw keys, normalised here with the same
+ * rule as the forward; beta [B, L, H] is clamped to [0, 2] as in the forward.
+ * d_state [B, H, dk]: d_1 on entry, d_{L+1} on exit.  kt_out [B, L, H, dk]:
+ * the write keys d_t * k_t, emitted BEFORE d is updated.
+ */
+int oracle_precond(const double* k, const double* beta, int B, int H, int L, int dk,
+                   double eta, double dmin, double dmax, double eps, double* d_state,
+                   double* kt_out, int nthreads)
+{
+    if (!k || !beta || !d_state || !kt_out) return -1;
+    if (B < 0 || H < 0 || L < 0 || dk < 1) return -1;
+    long nbh = (long)B * H;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#else
+    (void)nthreads;
+#endif
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads) reduction(| : bad)
+    for (long bh = 0; bh < nbh; ++bh) {
+        const long b = bh / H, h = bh % H;
+        double* d = d_state + (size_t)bh * dk;
+        double* kh = (double*)malloc(sizeof(double) * (size_t)dk);
+        if (!kh) {
+            bad |= 1;
+            continue;
+        }
+        for (long t = 0; t < L; ++t) {
+            const size_t tok = ((size_t)b * L + t) * H + h;
+            unit_key(k + tok * dk, dk, kh);
+            const double bt = clampd(beta[tok], 0.0, 2.0);
+            /* emit the write key with the current d_t */
+            double* ko = kt_out + tok * dk;
+            for (int r = 0; r < dk; ++r) ko[r] = d[r] * kh[r];
+            /* s = k*k, n = |k|^2, a = beta <d, s> */
+            double n = 0.0, ds = 0.0;
+            for (int r = 0; r < dk; ++r) {
+                const double s = kh[r] * kh[r];
+                n += s;
+                ds += d[r] * s;
+            }
+            const double a = bt * ds;
+            const double nb = n > eps ? n : eps;
+            const double coef = eta * bt * (1.0 - a) / nb;
+            /* projected step onto the box [dmin, dmax]^dk */
+            for (int r = 0; r < dk; ++r) d[r] = clampd(d[r] + coef * (kh[r] * kh[r]), dmin, dmax);
+        }
+        free(kh);
+    }
+    return bad ? -2 : 0;
+}

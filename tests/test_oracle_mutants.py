@@ -1,0 +1,99 @@
+"""The oracle pins must catch plausible mistakes (CPU only).
+
+Each case plants one mistake in a temporary copy of the oracle's C source
+(never in the oracle itself), builds it, and runs tests/test_oracle_pins.py
+against that copy in a subprocess.  The pins pass on the real oracle, so every
+planted mistake must make at least one of them fail.
+"""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# name -> (text in dp_oracle.c, replacement)
+MUTANTS = {
+    "reverse_substep_order": (
+        "for (int j = 0; j < n_h; ++j) {\n            const size_t sub = tok * n_h + j;",
+        "for (int jj = 0; jj < n_h; ++jj) {\n            const int j = n_h - 1 - jj;\n"
+        "            const size_t sub = tok * n_h + j;"),
+    "residual_sign": ("e[c] = vv[c] - acc;", "e[c] = vv[c] + acc;"),
+    "transposed_state_read": ("acc += S[(size_t)r * dv + c] * kh[r];",
+                              "acc += S[(size_t)c * dv + r] * kh[r];"),
+    "beta_not_clamped": ("const double bt = clampd(beta[sub], 0.0, 2.0);",
+                         "const double bt = beta[sub];"),
+    "write_key_ignored": ("const double* w = kt ? kt + sub * dk : kh;", "const double* w = kh;"),
+    "key_not_normalised": ("for (int r = 0; r < dk; ++r) kh[r] = kr[r] / den;",
+                           "for (int r = 0; r < dk; ++r) kh[r] = kr[r];"),
+    "gate_after_substeps": (
+        "        if (g) {\n            /* H_{i,0} = g_i H_{i-1}: once per token, before its sub-steps */\n"
+        "            const double gt = g[tok];\n"
+        "            for (size_t x = 0; x < (size_t)dk * dv; ++x) S[x] *= gt;\n        }\n"
+        "        for (int j = 0; j < n_h; ++j) {",
+        "        for (int j = 0; j < n_h; ++j) {\n"
+        "            if (g && j == 1) {\n                const double gt = g[tok];\n"
+        "                for (size_t x = 0; x < (size_t)dk * dv; ++x) S[x] *= gt;\n            }"),
+    "readout_before_last_substep": ("        /* o = H^T q after the token's last sub-step */",
+                                    "        if (0) /* moved */"),
+    "phase1_missing_beta_in_a": ("const double a = bt * ds;", "const double a = ds;"),
+    "phase1_emit_after_update": (
+        "            for (int r = 0; r < dk; ++r) ko[r] = d[r] * kh[r];\n",
+        "            double* ko_late = ko;\n"),
+    "phase1_no_projection": ("d[r] = clampd(d[r] + coef * (kh[r] * kh[r]), dmin, dmax);",
+                             "d[r] = d[r] + coef * (kh[r] * kh[r]);"),
+}
+
+_EMIT_LATE = (
+    "            for (int r = 0; r < dk; ++r) d[r] = clampd(d[r] + coef * (kh[r] * kh[r]), dmin, dmax);\n",
+    "            for (int r = 0; r < dk; ++r) d[r] = clampd(d[r] + coef * (kh[r] * kh[r]), dmin, dmax);\n"
+    "            for (int r = 0; r < dk; ++r) ko_late[r] = d[r] * kh[r];\n")
+
+_READOUT_FIX = (
+    "        if (0) /* moved */\n        const double* qq = q + tok * dk;",
+    "        const double* qq = q + tok * dk;")
+
+
+def _mutate(src, name):
+    a, b = MUTANTS[name]
+    assert src.count(a) >= 1, name
+    s = src.replace(a, b)
+    if name == "phase1_emit_after_update":
+        s = s.replace(*_EMIT_LATE)
+    if name == "readout_before_last_substep":
+        # read out after the first sub-step instead of the last
+        s = s.replace(_READOUT_FIX[0], _READOUT_FIX[1])
+        s = s.replace(
+            "                for (int c = 0; c < dv; ++c) S[(size_t)r * dv + c] += bw * e[c];\n            }\n        }",
+            "                for (int c = 0; c < dv; ++c) S[(size_t)r * dv + c] += bw * e[c];\n            }\n"
+            "            if (j == 0) {\n                const double* q0 = q + tok * dk;\n"
+            "                double* o0 = out_h + (size_t)t * out_stride;\n"
+            "                for (int c = 0; c < dv; ++c) {\n                    double acc = 0.0;\n"
+            "                    for (int r = 0; r < dk; ++r) acc += S[(size_t)r * dv + c] * q0[r];\n"
+            "                    o0[c] = acc;\n                }\n            }\n        }\n        if (0) {")
+        s = s.replace("            oo[c] = acc;\n        }\n    }\n    if (fs_h)",
+                      "            oo[c] = acc;\n        }\n        }\n    }\n    if (fs_h)")
+    return s
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    src = open(os.path.join(ROOT, "oracle", "dp_oracle.c")).read()
+    mut = _mutate(src, name)
+    assert mut != src
+    shutil.copytree(os.path.join(ROOT, "oracle"), tmp_path / "oracle",
+                    ignore=shutil.ignore_patterns("*.so", "__pycache__"))
+    shutil.copytree(os.path.join(ROOT, "tests"), tmp_path / "tests",
+                    ignore=shutil.ignore_patterns("__pycache__", "test_oracle_mutants.py",
+                                                  "test_*gpu*.py", "test_api*.py"))
+    (tmp_path / "oracle" / "dp_oracle.c").write_text(mut)
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-shared", "-fPIC",
+                    str(tmp_path / "oracle" / "dp_oracle.c"), "-o",
+                    str(tmp_path / "oracle" / "liboracle.so"), "-lm"], check=True)
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        "--rootdir", str(tmp_path), str(tmp_path / "tests" / "test_oracle_pins.py")],
+                       capture_output=True, text=True, cwd=str(tmp_path), timeout=600)
+    assert "passed" in r.stdout or "failed" in r.stdout, r.stdout + r.stderr
+    assert r.returncode != 0, f"mutant {name} survived every pin:\n{r.stdout[-2000:]}"
