@@ -1,0 +1,300 @@
+#!/usr/bin/env python3
+"""Benchmark: chunkwise DeltaProduct forward on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input
+already resident in HBM: for the symmetric workloads the prep/UT launch and
+the chunk-scan launch; for the asymmetric-write-key workload the OSDN phase-1
+scan first.  Prints ONE JSON line on stdout; diagnostics go to stderr.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3]
+
+Per-kernel durations come from HIP events recorded on the launch stream
+around every launch inside the timed region.  The CPU baseline is the fp64
+oracle on a bounded sample of heads of the same workload, on this host.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tokens/sec & MFMA TFLOP/s, DeltaProduct fwd n_h=2/3, dk=dv=128, L=4096"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3       # MI355X dense fp32 MFMA
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c3", help="c1, c2, c3, c3b, c4 or c5")
+    ap.add_argument("--also", default="c3b",
+                    help="comma-separated extra workloads timed in the same run ('' = none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU sample (0: auto)")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------- accounting
+
+def elem_bytes(w):
+    return 4 if w.dtype == "f32" else 2
+
+
+def alg_bytes(w):
+    """Algorithmic HBM bytes of one forward (single pass over inputs and outputs).
+
+    Per head and sub-step: k (dk), v (dv), beta (4 B) and, for the write-key
+    workload, kt (dk); per head and token: q (dk), out (dv) and g (4 B) when
+    gated; per head: the fp32 state out (and in, when there is an initial state).
+    """
+    s = elem_bytes(w)
+    N = w.L * w.n_h
+    per_head = N * (w.dk * s + w.dv * s + 4) + w.L * (w.dk + w.dv) * s
+    if w.asym:
+        per_head += N * w.dk * s
+    if w.gate:
+        per_head += w.L * 4
+    per_head += w.dk * w.dv * 4 * (2 if w.h0_std > 0 else 1)
+    return w.B * w.H * per_head
+
+
+def precond_bytes(w):
+    """Phase 1: read k and beta, write kt, per token and head; d in and out."""
+    s = elem_bytes(w)
+    return w.B * w.H * (w.L * (2 * w.dk * s + 4) + 2 * w.dk * 4)
+
+
+def chunk_flops(w):
+    """Chunkwise MFMA flops of the forward, dense C x C blocks (the standard
+    accounting: A, W and U products, W*H and the state update, Q*H, scores and
+    scores times pseudo-values), summed over chunks."""
+    C = w.chunk
+    N = w.L * w.n_h
+    nc = -(-N // C)
+    R = C / w.n_h
+    per = (2 * C * C * (2 * w.dk + w.dv) + 4 * C * w.dk * w.dv + 2 * R * w.dk * w.dv
+           + 2 * R * C * (w.dk + w.dv))
+    return w.B * w.H * nc * per
+
+
+def recurrent_flops(w):
+    """Flops of the sequential recurrence: per token n_h * 4 dk dv + 2 dk dv (+ dk dv gate)."""
+    per_tok = w.n_h * 4 * w.dk * w.dv + 2 * w.dk * w.dv + (w.dk * w.dv if w.gate else 0)
+    return w.B * w.L * w.H * per_tok
+
+
+def issued_flops(w, plan):
+    """MFMA flops the two kernels actually issue (tile-padded), per forward."""
+    C, dk, BV, RT = w.chunk, w.dk, plan["BV"], plan["readout_rows"]
+    N = w.L * w.n_h
+    nc = -(-N // C)
+    NT = C // 16
+    ut = (NT * (NT + 1) // 2) * 16 * 16 * dk * 2
+    for dist in range(1, NT):  # blocked inverse, fp32
+        ut += (NT - dist) * (dist + 1) * 16 * 16 * 16 * 2
+    scan = 2 * (C * BV * dk + C * RT * dk + RT * BV * dk + C * C * BV + RT * C * BV + dk * C * BV)
+    heads = w.B * w.H
+    return heads * nc * ut, heads * nc * scan * (w.dv // BV)
+
+
+# ---------------------------------------------------------------- GPU timing
+
+def time_gpu(w, steps, warmup):
+    import torch
+
+    import linear_rnn_sequence_amd as dp
+    from linear_rnn_sequence_amd.inputs import make
+
+    dev = torch.device("cuda:0")
+    t0 = time.perf_counter()
+    inp = make(w)
+    log(f"[bench] {w.name}: inputs drawn in {time.perf_counter() - t0:.1f}s")
+    d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    dt = d["q"].dtype
+    plan = dp.launch_info(w.n_h, w.B, w.H, w.L, w.dk, w.dv, w.chunk, dt, asym=w.asym)
+    ws = dp.alloc_workspace(w.n_h, w.B, w.H, w.L, w.dk, w.dv, w.chunk, dt, dev)
+    out = torch.empty(w.B, w.L, w.H, w.dv, dtype=dt, device=dev)
+    fs = torch.empty(w.B, w.H, w.dk, w.dv, dtype=torch.float32, device=dev)
+    k1 = b1 = kt = dstate = d1 = None
+    if w.asym:
+        k1 = d["k"][:, :, :, 0, :].contiguous()
+        b1 = d["beta"][..., 0].contiguous()
+        kt = torch.empty_like(k1)
+        d1 = torch.ones(w.B, w.H, w.dk, dtype=torch.float32, device=dev)
+        dstate = torch.empty_like(d1)
+    args = (d["q"], d["k"], d["v"], d["beta"], d["g"])
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if w.asym:
+            dstate.copy_(d1)
+            if ev is not None:
+                ev[0].record(stream)
+            dp.osdn_precond(k1, b1, d_state=dstate, kt=kt)
+        kk = None if kt is None else kt.unsqueeze(3)
+        if ev is not None:
+            ev[1].record(stream)
+        dp.fwd(*args, chunk=w.chunk, h0=d["h0"], kt=kk, out=out, final_state=fs, workspace=ws,
+               stages=dp.STAGE_UT)
+        if ev is not None:
+            ev[2].record(stream)
+        dp.fwd(*args, chunk=w.chunk, h0=d["h0"], kt=kk, out=out, final_state=fs, workspace=ws,
+               stages=dp.STAGE_SCAN)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ut_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / steps
+    scan_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / steps
+    pre_ms = (sum(e[0].elapsed_time(e[1]) for e in evs) / steps) if w.asym else 0.0
+    return dict(elapsed=elapsed, ms_per_step=1e3 * elapsed / steps, ut_ms=ut_ms, scan_ms=scan_ms,
+                pre_ms=pre_ms, plan=plan, inputs=inp)
+
+
+# ---------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(w, inp, nheads):
+    import oracle
+    from linear_rnn_sequence_amd.inputs import sampled_heads, select_heads, select_state
+
+    threads = oracle.num_threads()
+    n = nheads or min(w.B * w.H, max(4, 2 * threads))
+    heads = sampled_heads(w.B, w.H, n)
+    H = w.H
+    sub = {k: (None if inp[k] is None else select_heads(inp[k], heads, H))
+           for k in ("q", "k", "v", "beta", "g")}
+    h0 = None if inp["h0"] is None else select_state(inp["h0"], heads, H)
+    import numpy as np
+    import torch
+    conv = {k: (None if v is None else np.ascontiguousarray(v.to(torch.float64).numpy()))
+            for k, v in sub.items()}
+    h0c = None if h0 is None else np.ascontiguousarray(h0.to(torch.float64).numpy())
+    t0 = time.perf_counter()
+    if w.asym:
+        kt, _ = oracle.precond(conv["k"][:, :, :, 0, :], conv["beta"][..., 0])
+        oracle.fwd(conv["q"], conv["k"], conv["v"], conv["beta"], g=conv["g"],
+                   kt=kt[:, :, :, None, :], h0=h0c)
+    else:
+        oracle.fwd(conv["q"], conv["k"], conv["v"], conv["beta"], g=conv["g"], h0=h0c)
+    t = time.perf_counter() - t0
+    tokens = len(heads) * w.L  # token-heads processed; the workload has B*L tokens x H heads
+    value = tokens / w.H / t   # whole-workload tokens/s at this rate
+    return {"value": value, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(heads)} of {w.B * w.H} heads (b,h) of {w.name}, full L={w.L} "
+                      f"(all {w.n_h} sub-steps per token{', phase 1 included' if w.asym else ''}); "
+                      f"fp64 sequential recurrence, {t:.2f}s wall on {threads} threads",
+            "seconds": t}
+
+
+# ---------------------------------------------------------------- main
+
+def describe(w):
+    extra = (", gated, h0" if w.gate else "") + (", write key (OSDN phase 1 + 2)" if w.asym else "")
+    return (f"{w.name}: DeltaProduct fwd B={w.B} H={w.H} L={w.L} n_h={w.n_h} dk={w.dk} dv={w.dv} "
+            f"chunk={w.chunk} {w.dtype}{extra}")
+
+
+def main():
+    a = parse()
+    if a.gpus != 1 or os.environ.get("WORLD_SIZE", "1") not in ("1", ""):
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the forward shards over heads with no communication; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(3)
+    from __graft_entry__ import _ensure_built
+
+    _ensure_built()
+    from linear_rnn_sequence_amd.inputs import WORKLOADS
+
+    w = WORKLOADS[a.workload]
+    r = time_gpu(w, a.steps, a.warmup)
+    tokens = w.B * w.L
+    value = tokens / (r["ms_per_step"] / 1e3)
+    cf = chunk_flops(w)
+    rf = recurrent_flops(w)
+    ut_issued, scan_issued = issued_flops(w, r["plan"])
+    ab = alg_bytes(w)
+    peak_mfma = FP32_PEAK_TFLOPS if w.dtype == "f32" else BF16_PEAK_TFLOPS
+    kernels = {
+        "dp_ut_kernel": {"ms": r["ut_ms"], "issued_tflops": ut_issued / (r["ut_ms"] * 1e9),
+                         "workgroups": r["plan"]["ut_wgs"]},
+        "dp_scan_kernel": {"ms": r["scan_ms"], "issued_tflops": scan_issued / (r["scan_ms"] * 1e9),
+                           "workgroups": r["plan"]["scan_wgs"], "BV": r["plan"]["BV"]},
+    }
+    if w.asym:
+        kernels["dp_precond_kernel"] = {"ms": r["pre_ms"],
+                                        "gbs": precond_bytes(w) / (r["pre_ms"] * 1e6)}
+    # dominant kernel: the chunk scan streams every input and output of the forward
+    dom = max(kernels, key=lambda k: kernels[k]["ms"])
+    dom_ms = kernels[dom]["ms"]
+    achieved = ab / (dom_ms * 1e6) if dom != "dp_precond_kernel" else precond_bytes(w) / (dom_ms * 1e6)
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded, shapes and distributions of the pages' workloads)",
+        "config": {"workload": describe(w), "B": w.B, "H": w.H, "L": w.L, "n_h": w.n_h,
+                   "dk": w.dk, "dv": w.dv, "chunk": w.chunk, "gate": w.gate, "asym": w.asym,
+                   "global_batch": w.B, "seq_len": w.L, "parallelism": "none (1 GPU)"},
+        "mfma_tflops": cf / (r["ms_per_step"] * 1e9),
+        "mfma_tflops_frac": cf / (r["ms_per_step"] * 1e9) / peak_mfma,
+        "recurrent_tflops": rf / (r["ms_per_step"] * 1e9),
+        "alg_gbs": ab / (r["ms_per_step"] * 1e6),
+        "kernels": kernels,
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "alg_bytes_per_launch": ab},
+    }
+    also = {}
+    for name in [x for x in a.also.split(",") if x and x != a.workload]:
+        w2 = WORKLOADS[name]
+        r2 = time_gpu(w2, a.steps, a.warmup)
+        also[name] = {"workload": describe(w2),
+                      "value": w2.B * w2.L / (r2["ms_per_step"] / 1e3), "unit": "tokens/s",
+                      "ms_per_step": r2["ms_per_step"],
+                      "mfma_tflops": chunk_flops(w2) / (r2["ms_per_step"] * 1e9),
+                      "ut_ms": r2["ut_ms"], "scan_ms": r2["scan_ms"]}
+        del r2
+    if also:
+        line["also"] = also
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, r["inputs"], a.cpu_heads)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,184 @@
+/*
+ * dp.h -- C ABI of the MI355X (gfx950) DeltaProduct forward library, libdp.so.
+ *
+ * What is computed (by page title; section / equation on that page):
+ *
+ *  "DeltaProduct: Improving State-Tracking in Linear RNNs via Householder
+ *   Products" (study notes of arXiv 2502.10297v7)
+ *   - sec. 2.2, Eq.(3): each token i applies n_h ordered generalized
+ *     Householder updates to a per-head dk x dv matrix memory,
+ *       H_{i,j} = (I - b_{ij} k_{ij} k_{ij}^T) H_{i,j-1} + b_{ij} k_{ij} v_{ij}^T,
+ *     with H_{i,0} = H_{i-1} and unit keys k_{ij} (L2-normalised here);
+ *   - sec. 2.6: an optional per-token gate g_i scales the state once,
+ *     before the token's first sub-step (H_{i,0} = g_i H_{i-1}); the
+ *     readout is o_i = H_i^T q_i;
+ *   - sec. 4.1 (Sec.5.1): the computation runs as a chunkwise delta-rule scan
+ *     over the expanded sequence of L*n_h interleaved sub-steps with gate
+ *     (g_1, 1, .., 1, g_2, 1, ..), keeping only each token's last sub-step.
+ *  "OSDN: Improving Delta Rule with Provable Online Preconditioning in Linear
+ *   Attention" (study notes of arXiv 2605.13473v1)
+ *   - sec. 2.2, Eqs.(2)/(5): asymmetric write key; the residual uses the
+ *     read key k, the write uses kt: H += b kt (v - H^T k)^T;
+ *   - sec. 2.5 (App.A.2): chunkwise form T = (I + tril(B K Kt^T, -1))^-1,
+ *     W = T B K, U = T B V, state S += (U - W S^T)^T Kt, scores Q Kt^T;
+ *   - sec. 2.4 (Alg.1): phase-1 preconditioner scan producing kt = d_t * k_t.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the
+ *     library never allocates, frees or keeps them.  Layouts are dense,
+ *     row-major, in the order given.  q, k, kt and v must be 16-byte aligned.
+ *   - "T" is the path element type: IEEE float for *_f32 entry points,
+ *     bfloat16 (raw uint16 bits) for *_bf16.  beta, g, h0, final_state and
+ *     the phase-1 vector d are always float32.
+ *   - Validation happens on the host, before any HIP call; on failure the
+ *     call returns a negative dp_status and enqueues nothing.  On success the
+ *     work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and the call returns DP_OK without waiting for it.
+ *   - Inputs are read-only and must not overlap out, final_state or the
+ *     workspace.  h0 and final_state MAY be the same buffer (in-place resume).
+ *   - The library keeps no global state: calls on different streams may run
+ *     concurrently as long as their buffers are disjoint.
+ *   - NaN and Inf in the inputs propagate; nothing is silently repaired.
+ *   - Supported shapes: dk, dv in {16, 32, 64, 128}; chunk in {16, 32, 64}
+ *     (counted in sub-steps of the expanded sequence); 1 <= n_h <= 64.
+ *     B, H >= 1, L >= 0.  L*n_h need not be a multiple of chunk: the tail is
+ *     padded internally with beta = 0 sub-steps, which are exact identities.
+ */
+#ifndef DP_H
+#define DP_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DP_OK = 0,
+    DP_EINVAL = -1,     /* null required pointer, bad size, misaligned pointer */
+    DP_ENOTSUP = -2,    /* dk/dv/chunk/n_h outside the supported set */
+    DP_EWORKSPACE = -3, /* workspace missing or smaller than dp_fwd_workspace_size */
+    DP_EHIP = -4        /* a HIP launch or runtime call failed */
+} dp_status;
+
+typedef void* dp_stream; /* hipStream_t */
+
+/* Stage bits for dp_fwd_staged_*.  DP_STAGE_ALL is what dp_fwd_* run. */
+#define DP_STAGE_UT 1   /* per-chunk prep + UT transform -> workspace          */
+#define DP_STAGE_SCAN 2 /* inter-chunk state scan + readout + final state       */
+#define DP_STAGE_ALL 3
+
+/* Static string for a status code (never NULL). */
+const char* dp_status_str(int status);
+
+/*
+ * Workspace bytes needed by dp_fwd_* / dp_fwd_wk_* for these sizes.
+ * elem_bytes: 4 for the f32 path, 2 for the bf16 path.  Writes *bytes and
+ * returns DP_OK, or a negative status (sizes validated as for dp_fwd_*).
+ * The workspace holds, per chunk of every head, the matrix T*diag(beta)
+ * (chunk x chunk, type T) and two floats per sub-step (1/|k| and the
+ * chunk-local cumulative log-gate).
+ */
+int dp_fwd_workspace_size(int n_h, int B, int H, int L, int dk, int dv, int chunk,
+                          int elem_bytes, size_t* bytes);
+
+/*
+ * Launch plan the forward would use for these sizes (for measurement and
+ * tuning; nothing is launched).  asym: 0 symmetric, 1 write-key variant.
+ * info[0] = BV, the value columns per scan workgroup (16, 32 or 64)
+ * info[1] = scan workgroups (B*H*dv/BV), info[2] = UT workgroups (chunks),
+ * info[3] = scan LDS bytes, info[4] = UT LDS bytes, info[5] = readout rows
+ * per chunk (padded to 16).  Returns DP_OK or a validation status.
+ */
+int dp_fwd_launch_info(int n_h, int B, int H, int L, int dk, int dv, int chunk, int elem_bytes,
+                       int asym, int* info);
+
+/*
+ * Symmetric DeltaProduct forward (DeltaProduct notes sec. 2.2 Eq.(3),
+ * sec. 2.6, sec. 4.1).
+ *   q     [B, L, H, dk]         T   readout queries, used as given
+ *   k     [B, L, H, n_h, dk]    T   raw keys; each is divided by
+ *                                   max(|k|_2, 1e-6) inside
+ *   v     [B, L, H, n_h, dv]    T
+ *   beta  [B, L, H, n_h]      f32   clamped to [0, 2] inside
+ *   g     [B, L, H]           f32   per-token gate in [0, 1]; NULL = no gate.
+ *                                   g = 0 is handled as log(FLT_MIN).
+ *   out   [B, L, H, dv]         T   written: H_t^T q_t after token t's last
+ *                                   sub-step (rounded to nearest even for bf16)
+ *   final_state [B, H, dk, dv] f32  written with H_L; NULL = not returned
+ *   h0    [B, H, dk, dv]      f32   initial state H_0; NULL = zero
+ *   workspace / workspace_bytes     device scratch of at least
+ *                                   dp_fwd_workspace_size() bytes, 256-byte
+ *                                   aligned; its contents on entry are ignored
+ * Errors: DP_EINVAL, DP_ENOTSUP, DP_EWORKSPACE (before any HIP call),
+ * DP_EHIP (launch failure).
+ */
+int dp_fwd_f32(const float* q, const float* k, const float* v, const float* beta,
+               const float* g, int n_h, int B, int H, int L, int dk, int dv, int chunk,
+               float* out, float* final_state, const float* h0, void* workspace,
+               size_t workspace_bytes, dp_stream stream);
+int dp_fwd_bf16(const void* q, const void* k, const void* v, const float* beta,
+                const float* g, int n_h, int B, int H, int L, int dk, int dv, int chunk,
+                void* out, float* final_state, const float* h0, void* workspace,
+                size_t workspace_bytes, dp_stream stream);
+
+/*
+ * Asymmetric write-key forward (OSDN notes sec. 2.2 Eqs.(2)/(5), sec. 2.5):
+ * the residual and the transform's left factor use the normalised read key k,
+ * the write and the readout scores use kt exactly as given (not normalised).
+ *   kt    [B, L, H, n_h, dk]    T   write keys (e.g. from dp_osdn_precond_*)
+ * Every other argument is as for dp_fwd_*.
+ */
+int dp_fwd_wk_f32(const float* q, const float* k, const float* kt, const float* v,
+                  const float* beta, const float* g, int n_h, int B, int H, int L, int dk,
+                  int dv, int chunk, float* out, float* final_state, const float* h0,
+                  void* workspace, size_t workspace_bytes, dp_stream stream);
+int dp_fwd_wk_bf16(const void* q, const void* k, const void* kt, const void* v,
+                   const float* beta, const float* g, int n_h, int B, int H, int L, int dk,
+                   int dv, int chunk, void* out, float* final_state, const float* h0,
+                   void* workspace, size_t workspace_bytes, dp_stream stream);
+
+/*
+ * The forward split into its two launches, for measurement and inspection:
+ * `stages` is a mask of DP_STAGE_UT (fills the workspace) and DP_STAGE_SCAN
+ * (consumes it).  kt may be NULL (symmetric) or a write-key tensor
+ * (asymmetric).  Running DP_STAGE_UT then DP_STAGE_SCAN with the same
+ * arguments is exactly dp_fwd_* / dp_fwd_wk_*; DP_STAGE_SCAN alone requires
+ * a workspace filled by DP_STAGE_UT for the same k, kt, beta, g and sizes.
+ */
+int dp_fwd_staged_f32(const float* q, const float* k, const float* kt, const float* v,
+                      const float* beta, const float* g, int n_h, int B, int H, int L,
+                      int dk, int dv, int chunk, float* out, float* final_state,
+                      const float* h0, void* workspace, size_t workspace_bytes, int stages,
+                      dp_stream stream);
+int dp_fwd_staged_bf16(const void* q, const void* k, const void* kt, const void* v,
+                       const float* beta, const float* g, int n_h, int B, int H, int L,
+                       int dk, int dv, int chunk, void* out, float* final_state,
+                       const float* h0, void* workspace, size_t workspace_bytes, int stages,
+                       dp_stream stream);
+
+/*
+ * OSDN phase 1 (OSDN notes sec. 2.3-2.4, Alg.1), one sequential scan per head:
+ *   k_t  <- k_t / max(|k_t|_2, 1e-6),  s = k_t * k_t,  b = clamp(beta_t, 0, 2)
+ *   kt_t  = d_t * k_t                          (emitted before the update)
+ *   d_{t+1} = clamp(d_t + eta * b * (1 - b <d_t, s>) / max(<1, s>, eps) * s,
+ *                   dmin, dmax)                (elementwise projection)
+ *   k       [B, L, H, dk]   T    raw keys (the n_h = 1 key layout)
+ *   beta    [B, L, H]     f32
+ *   d_state [B, H, dk]    f32    in: d_1 (the notes use all ones); out: d_{L+1}
+ *   kt      [B, L, H, dk]   T    written
+ * eta, dmin, dmax, eps: the notes' final setting is 3e-3, 0.5, 2, 1e-6;
+ * requires 0 < dmin <= dmax and eps > 0.  dk in {16, 32, 64, 128}.
+ */
+int dp_osdn_precond_f32(const float* k, const float* beta, int B, int H, int L, int dk,
+                        float eta, float dmin, float dmax, float eps, float* d_state,
+                        float* kt, dp_stream stream);
+int dp_osdn_precond_bf16(const void* k, const float* beta, int B, int H, int L, int dk,
+                         float eta, float dmin, float dmax, float eps, float* d_state,
+                         void* kt, dp_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DP_H */

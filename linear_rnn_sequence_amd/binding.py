@@ -1,0 +1,206 @@
+"""Thin ctypes binding of libdp.so (the C ABI in include/dp.h).
+
+Argument marshalling only: shapes are read off the tensors, outputs and the
+workspace are allocated with torch on the inputs' device, and every step of
+the forward runs in the library's HIP kernels on torch's current stream.
+There is no fallback: if libdp.so is missing or a call fails, this raises.
+"""
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdp.so")
+
+DP_OK, DP_EINVAL, DP_ENOTSUP, DP_EWORKSPACE, DP_EHIP = 0, -1, -2, -3, -4
+STAGE_UT, STAGE_SCAN, STAGE_ALL = 1, 2, 3
+
+# every symbol include/dp.h declares
+EXPORTS = (
+    "dp_status_str", "dp_fwd_workspace_size", "dp_fwd_launch_info",
+    "dp_fwd_f32", "dp_fwd_bf16", "dp_fwd_wk_f32", "dp_fwd_wk_bf16",
+    "dp_fwd_staged_f32", "dp_fwd_staged_bf16",
+    "dp_osdn_precond_f32", "dp_osdn_precond_bf16",
+)
+
+_lib = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+
+
+class DPError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {status_str(code)} ({code})")
+
+
+def load() -> ctypes.CDLL:
+    """Load libdp.so from the package directory (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+        lib = ctypes.CDLL(LIB_PATH)
+        lib.dp_status_str.restype = ctypes.c_char_p
+        lib.dp_status_str.argtypes = [_I]
+        lib.dp_fwd_workspace_size.restype = _I
+        lib.dp_fwd_workspace_size.argtypes = [_I] * 8 + [ctypes.POINTER(ctypes.c_size_t)]
+        lib.dp_fwd_launch_info.restype = _I
+        lib.dp_fwd_launch_info.argtypes = [_I] * 9 + [ctypes.POINTER(ctypes.c_int)]
+        fwd_args = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P,
+                    ctypes.c_size_t, _P]
+        for name in ("dp_fwd_f32", "dp_fwd_bf16"):
+            getattr(lib, name).restype = _I
+            getattr(lib, name).argtypes = fwd_args
+        wk_args = [_P] + fwd_args
+        for name in ("dp_fwd_wk_f32", "dp_fwd_wk_bf16"):
+            getattr(lib, name).restype = _I
+            getattr(lib, name).argtypes = wk_args
+        staged = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P,
+                  ctypes.c_size_t, _I, _P]
+        for name in ("dp_fwd_staged_f32", "dp_fwd_staged_bf16"):
+            getattr(lib, name).restype = _I
+            getattr(lib, name).argtypes = staged
+        pre = [_P, _P, _I, _I, _I, _I, _F, _F, _F, _F, _P, _P, _P]
+        for name in ("dp_osdn_precond_f32", "dp_osdn_precond_bf16"):
+            getattr(lib, name).restype = _I
+            getattr(lib, name).argtypes = pre
+        _lib = lib
+    return _lib
+
+
+def status_str(code: int) -> str:
+    return load().dp_status_str(int(code)).decode()
+
+
+def _check(code: int, where: str):
+    if code != DP_OK:
+        raise DPError(code, where)
+
+
+def _suffix(dt: torch.dtype) -> str:
+    if dt == torch.float32:
+        return "f32"
+    if dt == torch.bfloat16:
+        return "bf16"
+    raise TypeError(f"unsupported dtype {dt}; expected float32 or bfloat16")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, name, dtype, shape, device):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def workspace_size(n_h, B, H, L, dk, dv, chunk, dtype) -> int:
+    """Bytes of device workspace dp_fwd needs (dtype: torch.float32/bfloat16)."""
+    elem = 4 if dtype == torch.float32 else 2
+    out = ctypes.c_size_t(0)
+    _check(load().dp_fwd_workspace_size(n_h, B, H, L, dk, dv, chunk, elem, ctypes.byref(out)),
+           "dp_fwd_workspace_size")
+    return int(out.value)
+
+
+def launch_info(n_h, B, H, L, dk, dv, chunk, dtype, asym=False) -> dict:
+    """The launch plan libdp would use for these sizes (nothing is launched)."""
+    elem = 4 if dtype == torch.float32 else 2
+    info = (ctypes.c_int * 6)()
+    _check(load().dp_fwd_launch_info(n_h, B, H, L, dk, dv, chunk, elem, int(bool(asym)), info),
+           "dp_fwd_launch_info")
+    return dict(BV=info[0], scan_wgs=info[1], ut_wgs=info[2], scan_lds=info[3], ut_lds=info[4],
+                readout_rows=info[5])
+
+
+def alloc_workspace(n_h, B, H, L, dk, dv, chunk, dtype, device) -> torch.Tensor:
+    nbytes = workspace_size(n_h, B, H, L, dk, dv, chunk, dtype)
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def fwd(q, k, v, beta, g=None, *, chunk: int = 64, h0=None, kt=None, out=None,
+        final_state=None, return_state: bool = True, workspace=None,
+        stages: int = STAGE_ALL, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """DeltaProduct forward through libdp.
+
+    q [B,L,H,dk], k [B,L,H,n_h,dk], v [B,L,H,n_h,dv] (float32 or bfloat16, one
+    dtype), beta [B,L,H,n_h] f32, g [B,L,H] f32 or None, h0 [B,H,dk,dv] f32 or
+    None, kt (write keys, shape of k) or None.  Returns (out, final_state);
+    final_state is None when return_state is False and none was passed.
+    """
+    if q.dim() != 4 or k.dim() != 5 or v.dim() != 5:
+        raise ValueError("expected q[B,L,H,dk], k[B,L,H,n_h,dk], v[B,L,H,n_h,dv]")
+    B, L, H, dk = q.shape
+    n_h, dv = k.shape[3], v.shape[4]
+    dev, dt = q.device, q.dtype
+    suf = _suffix(dt)
+    _need(k, "k", dt, (B, L, H, n_h, dk), dev)
+    _need(kt, "kt", dt, (B, L, H, n_h, dk), dev)
+    _need(v, "v", dt, (B, L, H, n_h, dv), dev)
+    _need(beta, "beta", torch.float32, (B, L, H, n_h), dev)
+    _need(g, "g", torch.float32, (B, L, H), dev)
+    _need(h0, "h0", torch.float32, (B, H, dk, dv), dev)
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    if out is None:
+        out = torch.empty(B, L, H, dv, dtype=dt, device=dev)
+    _need(out, "out", dt, (B, L, H, dv), dev)
+    if final_state is None and return_state:
+        final_state = torch.empty(B, H, dk, dv, dtype=torch.float32, device=dev)
+    _need(final_state, "final_state", torch.float32, (B, H, dk, dv), dev)
+    if workspace is None:
+        workspace = alloc_workspace(n_h, B, H, L, dk, dv, chunk, dt, dev)
+    fn = getattr(load(), f"dp_fwd_staged_{suf}")
+    rc = fn(_ptr(q), _ptr(k), _ptr(kt), _ptr(v), _ptr(beta), _ptr(g), n_h, B, H, L, dk, dv,
+            chunk, _ptr(out), _ptr(final_state), _ptr(h0), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), stages, _stream(stream))
+    _check(rc, f"dp_fwd_staged_{suf}")
+    return out, final_state
+
+
+def osdn_precond(k, beta, *, eta: float = 3e-3, dmin: float = 0.5, dmax: float = 2.0,
+                 eps: float = 1e-6, d_state=None, kt=None, stream=None):
+    """OSDN phase 1 through libdp: k [B,L,H,dk], beta [B,L,H] f32.
+
+    d_state [B,H,dk] f32 is d_1 on entry (default ones) and d_{L+1} on return.
+    Returns (kt [B,L,H,dk], d_state).
+    """
+    if k.dim() != 4:
+        raise ValueError("expected k[B,L,H,dk]")
+    B, L, H, dk = k.shape
+    dev, dt = k.device, k.dtype
+    suf = _suffix(dt)
+    _need(beta, "beta", torch.float32, (B, L, H), dev)
+    if not k.is_contiguous():
+        raise ValueError("k must be contiguous")
+    if d_state is None:
+        d_state = torch.ones(B, H, dk, dtype=torch.float32, device=dev)
+    _need(d_state, "d_state", torch.float32, (B, H, dk), dev)
+    if kt is None:
+        kt = torch.empty(B, L, H, dk, dtype=dt, device=dev)
+    _need(kt, "kt", dt, (B, L, H, dk), dev)
+    fn = getattr(load(), f"dp_osdn_precond_{suf}")
+    rc = fn(_ptr(k), _ptr(beta), B, H, L, dk, eta, dmin, dmax, eps, _ptr(d_state), _ptr(kt),
+            _stream(stream))
+    _check(rc, f"dp_osdn_precond_{suf}")
+    return kt, d_state

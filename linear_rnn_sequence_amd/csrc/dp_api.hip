@@ -1,0 +1,362 @@
+// dp_api.hip -- C ABI of libdp.so (declared in include/dp.h).
+//
+// Every entry point validates its arguments on the host before touching the
+// HIP runtime, then enqueues the kernels of dp_kernels.hpp on the caller's
+// stream and returns.  The library allocates nothing and keeps no state.
+#include <limits.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "dp.h"
+#include "dp_kernels.hpp"
+
+DP_DECLARE_LAUNCHERS(f32, 16)
+DP_DECLARE_LAUNCHERS(f32, 32)
+DP_DECLARE_LAUNCHERS(f32, 64)
+DP_DECLARE_LAUNCHERS(f32, 128)
+DP_DECLARE_LAUNCHERS(bf16, 16)
+DP_DECLARE_LAUNCHERS(bf16, 32)
+DP_DECLARE_LAUNCHERS(bf16, 64)
+DP_DECLARE_LAUNCHERS(bf16, 128)
+
+namespace {
+
+constexpr int kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
+constexpr size_t kWsAlign = 256;
+
+struct Shape {
+  int n_h, B, H, L, dk, dv, chunk;
+};
+
+bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int check_shape(const Shape& s) {
+  if (s.n_h <= 0 || s.B <= 0 || s.H <= 0 || s.L < 0 || s.dk <= 0 || s.dv <= 0 || s.chunk <= 0)
+    return DP_EINVAL;
+  if (!dim_ok(s.dk) || !dim_ok(s.dv)) return DP_ENOTSUP;
+  if (s.chunk != 16 && s.chunk != 32 && s.chunk != 64) return DP_ENOTSUP;
+  if (s.n_h > 64) return DP_ENOTSUP;
+  const long long N = (long long)s.L * s.n_h;
+  if (N > (long long)INT_MAX - 64) return DP_ENOTSUP;  // sub-step indices are 32-bit
+  const long long nc = (N + s.chunk - 1) / s.chunk;
+  if ((long long)s.B * s.H * nc > (long long)INT_MAX) return DP_ENOTSUP;  // grid size
+  if ((long long)s.B * s.H * 8 > (long long)INT_MAX) return DP_ENOTSUP;
+  return DP_OK;
+}
+
+int num_chunks(const Shape& s) {
+  const long long N = (long long)s.L * s.n_h;
+  return (int)((N + s.chunk - 1) / s.chunk);
+}
+
+size_t ws_t_bytes(const Shape& s, int elem) {
+  return align_up((size_t)s.B * s.H * num_chunks(s) * s.chunk * s.chunk * elem, kWsAlign);
+}
+
+size_t ws_total(const Shape& s, int elem) {
+  return ws_t_bytes(s, elem) + (size_t)s.B * s.H * num_chunks(s) * s.chunk * sizeof(float2);
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int a16(int x) { return (x + 15) & ~15; }
+
+// Readout rows a chunk can hold (ceil(C / n_h)), rounded up to MFMA tiles.
+int readout_rows(int C, int n_h) {
+  const int r = (C + n_h - 1) / n_h;
+  return r >= C ? C : ((r + 15) / 16) * 16;
+}
+
+// Fill the scan kernel's LDS offsets; returns total bytes.
+int scan_layout(dp::FwdArgs& a, int elem, int DK, int C, int BV) {
+  const int VE = 16 / elem;
+  const int LDK = DK + VE, LDC = C + VE;
+  int off = 0;
+  auto take = [&](int bytes) {
+    const int o = off;
+    off += a16(bytes);
+    return o;
+  };
+  a.oK = take(C * LDK * elem);
+  a.oKt = a.asym ? take(C * LDK * elem) : a.oK;
+  a.oQ = take(a.RT * LDK * elem);
+  a.oT = take(C * LDC * elem);
+  a.oHt = take(BV * LDK * elem);
+  a.oXt = take(BV * LDC * elem);
+  a.oUo = take(BV * LDC * elem);
+  a.oUs = take(BV * LDC * elem);
+  a.oP = take(a.RT * LDC * elem);
+  a.oR = take(C * 4);
+  a.oG = take(C * 4);
+  a.oLoc = take(a.RT * 4);
+  return off;
+}
+
+int ut_lds(int elem, int DK, int C, int asym) { return dp::ut_lds_bytes(elem, DK, C, asym); }
+
+// Value-block width of the scan: the widest BV (fewer redundant key-side
+// products per head) that still gives at least one workgroup per CU
+// (256 CUs), else the narrowest.  DP_SCAN_BV overrides it (16, 32 or 64).
+int pick_bv(int BH, int dv) {
+  const char* env = getenv("DP_SCAN_BV");
+  if (env != nullptr) {
+    const int v = atoi(env);
+    if ((v == 16 || v == 32 || v == 64) && v <= dv) return v;
+  }
+  for (int bv = 64; bv >= 16; bv >>= 1) {
+    if (bv > dv) continue;
+    if ((long long)BH * (dv / bv) >= 256) return bv;
+  }
+  return 16;
+}
+
+// Choose BV and fill the scan layout of `a` (a.RT and a.asym must be set).
+int plan(dp::FwdArgs& a, int elem, int dk, int chunk, int* BV_out, int* lds_out) {
+  int BV = pick_bv(a.B * a.H, a.dv);
+  int lds = 0;
+  for (;; BV >>= 1) {
+    if (BV < 16) return DP_ENOTSUP;
+    lds = scan_layout(a, elem, dk, chunk, BV);
+    if (lds <= kMaxLds) break;
+  }
+  if (ut_lds(elem, dk, chunk, a.asym) > kMaxLds) return DP_ENOTSUP;
+  a.nvb = a.dv / BV;
+  *BV_out = BV;
+  *lds_out = lds;
+  return DP_OK;
+}
+
+hipError_t dispatch_fwd(int elem, int dk, const dp::FwdArgs& a, int C, int BV, int lds,
+                        int stages, hipStream_t st) {
+  if (elem == 4) {
+    switch (dk) {
+      case 16: return dp_launch_fwd_f32_16(a, C, BV, lds, stages, st);
+      case 32: return dp_launch_fwd_f32_32(a, C, BV, lds, stages, st);
+      case 64: return dp_launch_fwd_f32_64(a, C, BV, lds, stages, st);
+      case 128: return dp_launch_fwd_f32_128(a, C, BV, lds, stages, st);
+    }
+  } else {
+    switch (dk) {
+      case 16: return dp_launch_fwd_bf16_16(a, C, BV, lds, stages, st);
+      case 32: return dp_launch_fwd_bf16_32(a, C, BV, lds, stages, st);
+      case 64: return dp_launch_fwd_bf16_64(a, C, BV, lds, stages, st);
+      case 128: return dp_launch_fwd_bf16_128(a, C, BV, lds, stages, st);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t dispatch_precond(int elem, int dk, const dp::PrecondArgs& a, hipStream_t st) {
+  if (elem == 4) {
+    switch (dk) {
+      case 16: return dp_launch_precond_f32_16(a, st);
+      case 32: return dp_launch_precond_f32_32(a, st);
+      case 64: return dp_launch_precond_f32_64(a, st);
+      case 128: return dp_launch_precond_f32_128(a, st);
+    }
+  } else {
+    switch (dk) {
+      case 16: return dp_launch_precond_bf16_16(a, st);
+      case 32: return dp_launch_precond_bf16_32(a, st);
+      case 64: return dp_launch_precond_bf16_64(a, st);
+      case 128: return dp_launch_precond_bf16_128(a, st);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+int fwd_impl(int elem, const void* q, const void* k, const void* kt, const void* v,
+             const float* beta, const float* g, int n_h, int B, int H, int L, int dk, int dv,
+             int chunk, void* out, float* final_state, const float* h0, void* workspace,
+             size_t workspace_bytes, int stages, dp_stream stream) {
+  const Shape s{n_h, B, H, L, dk, dv, chunk};
+  int rc = check_shape(s);
+  if (rc != DP_OK) return rc;
+  if (stages < 1 || stages > DP_STAGE_ALL) return DP_EINVAL;
+  if (q == nullptr || k == nullptr || v == nullptr || beta == nullptr || out == nullptr)
+    return DP_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (kt != nullptr && !aligned16(kt)))
+    return DP_EINVAL;
+  const size_t need = ws_total(s, elem);
+  if (workspace_bytes < need || (need > 0 && workspace == nullptr)) return DP_EWORKSPACE;
+  if (((uintptr_t)workspace & (kWsAlign - 1)) != 0) return DP_EWORKSPACE;
+
+  dp::FwdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.kt = kt;
+  a.v = v;
+  a.beta = beta;
+  a.g = g;
+  a.h0 = h0;
+  a.out = out;
+  a.fstate = final_state;
+  a.wsT = workspace;
+  a.wsS = reinterpret_cast<float2*>(static_cast<char*>(workspace) + ws_t_bytes(s, elem));
+  a.N = L * n_h;
+  a.B = B;
+  a.H = H;
+  a.L = L;
+  a.n_h = n_h;
+  a.dv = dv;
+  a.nc = num_chunks(s);
+  a.RT = readout_rows(chunk, n_h);
+  a.asym = kt != nullptr ? 1 : 0;
+
+  int BV = 0, lds = 0;
+  rc = plan(a, elem, dk, chunk, &BV, &lds);
+  if (rc != DP_OK) return rc;
+
+  int run = stages;
+  if (a.nc == 0) run &= ~DP_STAGE_UT;  // nothing to transform; the scan copies h0
+  const hipError_t e = dispatch_fwd(elem, dk, a, chunk, BV, lds, run,
+                                    static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DP_OK : DP_EHIP;
+}
+
+int precond_impl(int elem, const void* k, const float* beta, int B, int H, int L, int dk,
+                 float eta, float dmin, float dmax, float eps, float* d_state, void* kt,
+                 dp_stream stream) {
+  if (k == nullptr || beta == nullptr || d_state == nullptr || kt == nullptr) return DP_EINVAL;
+  if (B <= 0 || H <= 0 || L < 0) return DP_EINVAL;
+  if (!dim_ok(dk)) return DP_ENOTSUP;
+  if (!(eps > 0.f) || !(dmin > 0.f) || !(dmin <= dmax) || !(eta == eta)) return DP_EINVAL;
+  if ((long long)B * H * (long long)L > (long long)1 << 40) return DP_ENOTSUP;
+  if (L == 0) return DP_OK;
+  dp::PrecondArgs a;
+  a.k = k;
+  a.beta = beta;
+  a.d = d_state;
+  a.kt = kt;
+  a.B = B;
+  a.H = H;
+  a.L = L;
+  a.eta = eta;
+  a.dmin = dmin;
+  a.dmax = dmax;
+  a.eps = eps;
+  const hipError_t e = dispatch_precond(elem, dk, a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DP_OK : DP_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dp_status_str(int status) {
+  switch (status) {
+    case DP_OK: return "DP_OK";
+    case DP_EINVAL: return "DP_EINVAL: invalid argument (null pointer, size or alignment)";
+    case DP_ENOTSUP: return "DP_ENOTSUP: unsupported shape (dk/dv/chunk/n_h)";
+    case DP_EWORKSPACE: return "DP_EWORKSPACE: workspace missing, misaligned or too small";
+    case DP_EHIP: return "DP_EHIP: HIP launch or runtime error";
+    default: return "unknown dp status";
+  }
+}
+
+int dp_fwd_workspace_size(int n_h, int B, int H, int L, int dk, int dv, int chunk,
+                          int elem_bytes, size_t* bytes) {
+  if (bytes == nullptr) return DP_EINVAL;
+  if (elem_bytes != 2 && elem_bytes != 4) return DP_EINVAL;
+  const Shape s{n_h, B, H, L, dk, dv, chunk};
+  const int rc = check_shape(s);
+  if (rc != DP_OK) return rc;
+  *bytes = ws_total(s, elem_bytes);
+  return DP_OK;
+}
+
+int dp_fwd_launch_info(int n_h, int B, int H, int L, int dk, int dv, int chunk, int elem_bytes,
+                       int asym, int* info) {
+  if (info == nullptr || (elem_bytes != 2 && elem_bytes != 4) || (asym != 0 && asym != 1))
+    return DP_EINVAL;
+  const Shape s{n_h, B, H, L, dk, dv, chunk};
+  const int rc = check_shape(s);
+  if (rc != DP_OK) return rc;
+  dp::FwdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.B = B;
+  a.H = H;
+  a.dv = dv;
+  a.RT = readout_rows(chunk, n_h);
+  a.asym = asym;
+  int BV = 0, lds = 0;
+  const int prc = plan(a, elem_bytes, dk, chunk, &BV, &lds);
+  if (prc != DP_OK) return prc;
+  info[0] = BV;
+  info[1] = B * H * a.nvb;
+  info[2] = B * H * num_chunks(s);
+  info[3] = lds;
+  info[4] = ut_lds(elem_bytes, dk, chunk, asym);
+  info[5] = a.RT;
+  return DP_OK;
+}
+
+int dp_fwd_f32(const float* q, const float* k, const float* v, const float* beta,
+               const float* g, int n_h, int B, int H, int L, int dk, int dv, int chunk,
+               float* out, float* final_state, const float* h0, void* workspace,
+               size_t workspace_bytes, dp_stream stream) {
+  return fwd_impl(4, q, k, nullptr, v, beta, g, n_h, B, H, L, dk, dv, chunk, out, final_state,
+                  h0, workspace, workspace_bytes, DP_STAGE_ALL, stream);
+}
+
+int dp_fwd_bf16(const void* q, const void* k, const void* v, const float* beta,
+                const float* g, int n_h, int B, int H, int L, int dk, int dv, int chunk,
+                void* out, float* final_state, const float* h0, void* workspace,
+                size_t workspace_bytes, dp_stream stream) {
+  return fwd_impl(2, q, k, nullptr, v, beta, g, n_h, B, H, L, dk, dv, chunk, out, final_state,
+                  h0, workspace, workspace_bytes, DP_STAGE_ALL, stream);
+}
+
+int dp_fwd_wk_f32(const float* q, const float* k, const float* kt, const float* v,
+                  const float* beta, const float* g, int n_h, int B, int H, int L, int dk,
+                  int dv, int chunk, float* out, float* final_state, const float* h0,
+                  void* workspace, size_t workspace_bytes, dp_stream stream) {
+  if (kt == nullptr) return DP_EINVAL;
+  return fwd_impl(4, q, k, kt, v, beta, g, n_h, B, H, L, dk, dv, chunk, out, final_state, h0,
+                  workspace, workspace_bytes, DP_STAGE_ALL, stream);
+}
+
+int dp_fwd_wk_bf16(const void* q, const void* k, const void* kt, const void* v,
+                   const float* beta, const float* g, int n_h, int B, int H, int L, int dk,
+                   int dv, int chunk, void* out, float* final_state, const float* h0,
+                   void* workspace, size_t workspace_bytes, dp_stream stream) {
+  if (kt == nullptr) return DP_EINVAL;
+  return fwd_impl(2, q, k, kt, v, beta, g, n_h, B, H, L, dk, dv, chunk, out, final_state, h0,
+                  workspace, workspace_bytes, DP_STAGE_ALL, stream);
+}
+
+int dp_fwd_staged_f32(const float* q, const float* k, const float* kt, const float* v,
+                      const float* beta, const float* g, int n_h, int B, int H, int L,
+                      int dk, int dv, int chunk, float* out, float* final_state,
+                      const float* h0, void* workspace, size_t workspace_bytes, int stages,
+                      dp_stream stream) {
+  return fwd_impl(4, q, k, kt, v, beta, g, n_h, B, H, L, dk, dv, chunk, out, final_state, h0,
+                  workspace, workspace_bytes, stages, stream);
+}
+
+int dp_fwd_staged_bf16(const void* q, const void* k, const void* kt, const void* v,
+                       const float* beta, const float* g, int n_h, int B, int H, int L,
+                       int dk, int dv, int chunk, void* out, float* final_state,
+                       const float* h0, void* workspace, size_t workspace_bytes, int stages,
+                       dp_stream stream) {
+  return fwd_impl(2, q, k, kt, v, beta, g, n_h, B, H, L, dk, dv, chunk, out, final_state, h0,
+                  workspace, workspace_bytes, stages, stream);
+}
+
+int dp_osdn_precond_f32(const float* k, const float* beta, int B, int H, int L, int dk,
+                        float eta, float dmin, float dmax, float eps, float* d_state,
+                        float* kt, dp_stream stream) {
+  return precond_impl(4, k, beta, B, H, L, dk, eta, dmin, dmax, eps, d_state, kt, stream);
+}
+
+int dp_osdn_precond_bf16(const void* k, const float* beta, int B, int H, int L, int dk,
+                         float eta, float dmin, float dmax, float eps, float* d_state,
+                         void* kt, dp_stream stream) {
+  return precond_impl(2, k, beta, B, H, L, dk, eta, dmin, dmax, eps, d_state, kt, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,194 @@
+// dp_device.hpp -- gfx950 device helpers shared by the DeltaProduct kernels:
+// element conversion, 16-byte vector moves, MFMA fragment traits and small
+// lane reductions.  CDNA4 only: 64-lane wavefronts, v_mfma_f32_16x16x32_bf16
+// for the bf16 path and v_mfma_f32_16x16x4_f32 for the fp32 path.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dp {
+
+using bf16_t = uint16_t;  // bfloat16 storage (raw bits)
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------ conversions
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float((uint32_t)x << 16); }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float x);
+
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) {
+  return x;
+}
+
+// fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.
+template <>
+__device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x0040u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+// Elements of type T held in one 16-byte vector.
+template <typename T>
+struct Vec {
+  static constexpr int N = 16 / (int)sizeof(T);
+};
+
+// Unpack a 16-byte vector of T into N floats.
+__device__ __forceinline__ void unpack16(const u32x4_t& v, float* f, float /*tag*/) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(v[i]);
+}
+__device__ __forceinline__ void unpack16(const u32x4_t& v, float* f, bf16_t /*tag*/) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(v[i] << 16);
+    f[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+  }
+}
+
+__device__ __forceinline__ u32x4_t ld16(const void* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
+__device__ __forceinline__ void st16(void* p, const u32x4_t& v) {
+  *reinterpret_cast<u32x4_t*>(p) = v;
+}
+
+// Store 4 consecutive elements (fp32 inputs) as T at p.
+__device__ __forceinline__ void st4(float* p, float a, float b, float c, float d) {
+  f32x4_t v = {a, b, c, d};
+  *reinterpret_cast<f32x4_t*>(p) = v;
+}
+__device__ __forceinline__ void st4(bf16_t* p, float a, float b, float c, float d) {
+  u32x2_t v;
+  v[0] = (uint32_t)from_f32<bf16_t>(a) | ((uint32_t)from_f32<bf16_t>(b) << 16);
+  v[1] = (uint32_t)from_f32<bf16_t>(c) | ((uint32_t)from_f32<bf16_t>(d) << 16);
+  *reinterpret_cast<u32x2_t*>(p) = v;
+}
+
+// ------------------------------------------------------------ MFMA traits
+//
+// D(16x16, fp32) += A(16 x KS) * B(KS x 16).  Both operands are read from
+// buffers laid out "row by k": A as A[m][k] = base[(row0 + m) * ld + k0 + k],
+// B as B[k][n] = base[(row0 + n) * ld + k0 + k] (i.e. the buffer holds B^T).
+// Lane l holds row/column (l & 15) and the k slice selected by (l >> 4); the
+// same k slice is used for A and B, so the contraction is correct for any
+// hardware assignment of k within a lane group.  The accumulator layout is
+// D[4 * (l >> 4) + i][l & 15], i = 0..3.
+//
+// load_t reads the transpose: element (m, k) at base[(k0 + k) * ld + row0 + m].
+
+template <typename T>
+struct Mfma;
+
+template <>
+struct Mfma<bf16_t> {
+  static constexpr int KS = 32;  // k per instruction
+  using frag_t = bf16x8_t;
+
+  __device__ __forceinline__ static frag_t load(const bf16_t* base, int ld, int row0, int k0) {
+    const int l = threadIdx.x & 63;
+    const bf16_t* p = base + (row0 + (l & 15)) * ld + k0 + 8 * (l >> 4);
+    return *reinterpret_cast<const frag_t*>(p);
+  }
+  __device__ __forceinline__ static frag_t load_t(const bf16_t* base, int ld, int row0, int k0) {
+    const int l = threadIdx.x & 63;
+    const bf16_t* p = base + (k0 + 8 * (l >> 4)) * ld + row0 + (l & 15);
+    u16x8_t v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = p[e * ld];
+    return __builtin_bit_cast(frag_t, v);
+  }
+  __device__ __forceinline__ static f32x4_t mma(const frag_t& a, const frag_t& b, const f32x4_t& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <>
+struct Mfma<float> {
+  static constexpr int KS = 4;
+  using frag_t = float;
+
+  __device__ __forceinline__ static frag_t load(const float* base, int ld, int row0, int k0) {
+    const int l = threadIdx.x & 63;
+    return base[(row0 + (l & 15)) * ld + k0 + (l >> 4)];
+  }
+  __device__ __forceinline__ static frag_t load_t(const float* base, int ld, int row0, int k0) {
+    const int l = threadIdx.x & 63;
+    return base[(k0 + (l >> 4)) * ld + row0 + (l & 15)];
+  }
+  __device__ __forceinline__ static f32x4_t mma(const frag_t& a, const frag_t& b, const f32x4_t& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+};
+
+// acc += A[row0a.., 0..K) * B[0..K, row0b..]  (both "row by k" buffers)
+template <typename T, int K>
+__device__ __forceinline__ f32x4_t mm_tile(f32x4_t acc, const T* a, int lda, int ra, const T* b,
+                                           int ldb, int rb) {
+  using M = Mfma<T>;
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += M::KS) acc = M::mma(M::load(a, lda, ra, k0), M::load(b, ldb, rb, k0), acc);
+  return acc;
+}
+
+// acc += A^T-read operand (element (m,k) at a[k*lda + ra + m]) times B.
+template <typename T, int K>
+__device__ __forceinline__ f32x4_t mm_tile_ta(f32x4_t acc, const T* a, int lda, int ra, const T* b,
+                                              int ldb, int rb) {
+  using M = Mfma<T>;
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += M::KS)
+    acc = M::mma(M::load_t(a, lda, ra, k0), M::load(b, ldb, rb, k0), acc);
+  return acc;
+}
+
+// acc += A * B-transposed-read operand (element (n,k) of B^T at b[k*ldb + rb + n]).
+template <typename T, int K>
+__device__ __forceinline__ f32x4_t mm_tile_tb(f32x4_t acc, const T* a, int lda, int ra, const T* b,
+                                              int ldb, int rb) {
+  using M = Mfma<T>;
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += M::KS)
+    acc = M::mma(M::load(a, lda, ra, k0), M::load_t(b, ldb, rb, k0), acc);
+  return acc;
+}
+
+// ------------------------------------------------------------ lane reductions
+
+// Sum over aligned groups of W consecutive lanes (W a power of two <= 64).
+template <int W>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+  for (int m = W / 2; m >= 1; m >>= 1) x += __shfl_xor(x, m, W);
+  return x;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wavefront.
+__device__ __forceinline__ float wave_inclusive_scan(float x) {
+  const int l = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    float y = __shfl_up(x, d, 64);
+    if (l >= d) x += y;
+  }
+  return x;
+}
+
+// clamp that lets NaN through (comparisons with NaN are false)
+__device__ __forceinline__ float clamp_keep_nan(float x, float lo, float hi) {
+  return x < lo ? lo : (x > hi ? hi : x);
+}
+
+}  // namespace dp

@@ -1,0 +1,4 @@
+// Instantiates the f32 forward and phase-1 kernels for dk = 32.
+#include "dp_kernels.hpp"
+
+DP_DEFINE_LAUNCHERS(float, f32, 32)

@@ -122,3 +122,33 @@ def make(w: Workload, seed: Optional[int] = None) -> dict:
         "n_h": n_h,
         "chunk": w.chunk,
     }
+
+
+# ------------------------------------------------------------------ head sampling
+# Heads (b, h) are independent, so a large workload can be checked or timed on
+# a sample of heads.  These helpers only index; they compute nothing.
+
+def sampled_heads(B: int, H: int, n: int) -> list:
+    """n flattened heads b*H + h spread evenly over the grid (first and last included)."""
+    total = B * H
+    if n >= total:
+        return list(range(total))
+    return sorted({round(i * (total - 1) / (n - 1)) for i in range(n)}) if n > 1 else [0]
+
+
+def select_heads(t: torch.Tensor, heads, H: int) -> torch.Tensor:
+    """Stack the listed heads of a token-major [B, L, H, ...] tensor into [1, L, n, ...]."""
+    parts = []
+    for bh in heads:
+        b, h = divmod(int(bh), H)
+        parts.append(t[b:b + 1, :, h:h + 1])
+    return torch.cat(parts, dim=2).contiguous()
+
+
+def select_state(t: torch.Tensor, heads, H: int) -> torch.Tensor:
+    """Stack the listed heads of a [B, H, ...] tensor into [1, n, ...]."""
+    parts = []
+    for bh in heads:
+        b, h = divmod(int(bh), H)
+        parts.append(t[b:b + 1, h:h + 1])
+    return torch.cat(parts, dim=1).contiguous()

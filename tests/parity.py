@@ -1,0 +1,57 @@
+"""Helpers of the GPU parity tests: run the HIP path through the C ABI and the
+fp64 oracle on the same stored bytes, and measure the error the way the
+tolerances are stated: max |x_gpu - x_oracle| / RMS(x_oracle), per tensor."""
+import sys
+
+import numpy as np
+import torch
+
+import linear_rnn_sequence_amd as dp
+import oracle
+from linear_rnn_sequence_amd.inputs import sampled_heads, select_heads, select_state  # noqa: F401
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def rel_err(x, ref) -> float:
+    x = np.asarray(x, np.float64)
+    ref = np.asarray(ref, np.float64)
+    if ref.size == 0:
+        return 0.0
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    if rms == 0.0:
+        return float(np.max(np.abs(x - ref)))
+    return float(np.max(np.abs(x - ref)) / rms)
+
+
+def f64(t):
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def to_dev(inp, device="cuda"):
+    return {k: (v.to(device) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+
+
+def gpu_forward(inp, chunk=None, kt=None, h0="input", stream=None):
+    """Run dp.fwd on the GPU copies of `inp`; returns (out, final_state) on the device."""
+    d = to_dev(inp)
+    h0t = d["h0"] if h0 == "input" else h0
+    ktt = None if kt is None else kt.to("cuda")
+    out, fs = dp.fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], chunk=chunk or inp["chunk"],
+                     h0=h0t, kt=ktt, stream=stream)
+    torch.cuda.synchronize()
+    return out, fs
+
+
+def oracle_heads(inp, heads, kt=None):
+    """Oracle forward of the listed heads only (stacked along H, B = 1)."""
+    H = inp["q"].shape[2]
+    sel = lambda t: None if t is None else select_heads(t, heads, H)
+    h0 = None if inp["h0"] is None else select_state(inp["h0"], heads, H)
+    return oracle.fwd(sel(inp["q"]), sel(inp["k"]), sel(inp["v"]), sel(inp["beta"]),
+                      g=sel(inp["g"]), kt=None if kt is None else sel(kt), h0=h0)

@@ -1,0 +1,161 @@
+"""C-ABI checks that need no GPU: every symbol include/dp.h declares is
+exported by libdp.so, and every validation error is returned on the host
+before any HIP call (so these run on a machine without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_rnn_sequence_amd as dp
+from linear_rnn_sequence_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from linear_rnn_sequence_amd import build as b
+        b.build()
+    return dp.load()
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "dp.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dp_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = header_functions()
+    for required in ("dp_fwd_bf16", "dp_fwd_f32", "dp_fwd_wk_bf16", "dp_fwd_wk_f32",
+                     "dp_osdn_precond_bf16", "dp_fwd_workspace_size", "dp_status_str"):
+        assert required in names
+    assert sorted(names) == sorted(dp.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_library_is_gfx950_and_loads_on_cpu(lib):
+    # the code object inside libdp.so targets gfx950 only
+    blob = open(binding.LIB_PATH, "rb").read()
+    assert b"gfx950" in blob
+    for other in (b"gfx942", b"gfx90a", b"gfx1100"):
+        assert other not in blob
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4):
+        assert dp.status_str(code).startswith("DP_")
+    assert "unknown" in dp.status_str(7)
+
+
+SZ = ctypes.c_size_t
+
+
+def ws(n_h, B, H, L, dk, dv, chunk, elem):
+    out = SZ(0)
+    rc = dp.load().dp_fwd_workspace_size(n_h, B, H, L, dk, dv, chunk, elem, ctypes.byref(out))
+    return rc, out.value
+
+
+def test_workspace_size_formula(lib):
+    rc, n = ws(3, 4, 16, 4096, 128, 128, 64, 2)
+    assert rc == 0
+    nc = 4096 * 3 // 64
+    t_bytes = 4 * 16 * nc * 64 * 64 * 2
+    assert n == t_bytes + 4 * 16 * nc * 64 * 8
+    rc, n = ws(2, 1, 1, 33, 16, 16, 16, 4)  # ragged: 66 sub-steps -> 5 chunks
+    assert rc == 0 and n == ((1 * 5 * 16 * 16 * 4 + 255) // 256) * 256 + 5 * 16 * 8
+    assert ws(2, 1, 1, 0, 16, 16, 16, 4) == (0, 0)
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, 1, 1, 8, 16, 16, 16, 2), dp.binding.DP_EINVAL),     # n_h = 0
+    ((2, 0, 1, 8, 16, 16, 16, 2), dp.binding.DP_EINVAL),     # B = 0
+    ((2, 1, 1, -1, 16, 16, 16, 2), dp.binding.DP_EINVAL),    # L < 0
+    ((2, 1, 1, 8, 48, 16, 16, 2), dp.binding.DP_ENOTSUP),    # dk not in the set
+    ((2, 1, 1, 8, 16, 256, 16, 2), dp.binding.DP_ENOTSUP),   # dv not in the set
+    ((2, 1, 1, 8, 16, 16, 128, 2), dp.binding.DP_ENOTSUP),   # chunk not in the set
+    ((65, 1, 1, 8, 16, 16, 16, 2), dp.binding.DP_ENOTSUP),   # n_h too large
+    ((2, 1, 1, 8, 16, 16, 16, 3), dp.binding.DP_EINVAL),     # elem bytes
+])
+def test_workspace_size_validation(lib, args, code):
+    assert ws(*args)[0] == code
+
+
+FAKE = 1 << 20  # a 256-aligned non-null address; validation fails before any use
+
+
+def fwd_call(lib, suffix="bf16", q=FAKE, k=FAKE, v=FAKE, beta=FAKE, g=None, n_h=2, B=1, H=1,
+             L=8, dk=16, dv=16, chunk=16, out=FAKE, fs=None, h0=None, wsp=FAKE, wsb=1 << 30,
+             kt=None, stages=3):
+    fn = getattr(lib, f"dp_fwd_staged_{suffix}")
+    return fn(q, k, kt, v, beta, g, n_h, B, H, L, dk, dv, chunk, out, fs, h0, wsp, wsb, stages,
+              None)
+
+
+@pytest.mark.parametrize("suffix", ["bf16", "f32"])
+def test_fwd_validation_errors_before_hip(lib, suffix):
+    E = dp.binding
+    assert fwd_call(lib, suffix, q=None) == E.DP_EINVAL
+    assert fwd_call(lib, suffix, k=None) == E.DP_EINVAL
+    assert fwd_call(lib, suffix, v=None) == E.DP_EINVAL
+    assert fwd_call(lib, suffix, beta=None) == E.DP_EINVAL
+    assert fwd_call(lib, suffix, out=None) == E.DP_EINVAL
+    assert fwd_call(lib, suffix, q=FAKE + 8) == E.DP_EINVAL          # misaligned
+    assert fwd_call(lib, suffix, kt=FAKE + 4) == E.DP_EINVAL
+    assert fwd_call(lib, suffix, n_h=0) == E.DP_EINVAL
+    assert fwd_call(lib, suffix, H=0) == E.DP_EINVAL
+    assert fwd_call(lib, suffix, dk=24) == E.DP_ENOTSUP
+    assert fwd_call(lib, suffix, dv=8) == E.DP_ENOTSUP
+    assert fwd_call(lib, suffix, chunk=8) == E.DP_ENOTSUP
+    assert fwd_call(lib, suffix, n_h=100) == E.DP_ENOTSUP
+    assert fwd_call(lib, suffix, stages=0) == E.DP_EINVAL
+    assert fwd_call(lib, suffix, stages=4) == E.DP_EINVAL
+    assert fwd_call(lib, suffix, wsb=16) == E.DP_EWORKSPACE           # too small
+    assert fwd_call(lib, suffix, wsp=None) == E.DP_EWORKSPACE         # missing
+    assert fwd_call(lib, suffix, wsp=FAKE + 16) == E.DP_EWORKSPACE    # misaligned
+
+
+def test_wk_requires_write_key(lib):
+    args = (FAKE, FAKE, None, FAKE, FAKE, None, 1, 1, 1, 8, 16, 16, 16, FAKE, None, None, FAKE,
+            1 << 30, None)
+    assert lib.dp_fwd_wk_bf16(*args) == dp.binding.DP_EINVAL
+    assert lib.dp_fwd_wk_f32(*args) == dp.binding.DP_EINVAL
+
+
+def test_precond_validation_errors_before_hip(lib):
+    E = dp.binding
+    f = lib.dp_osdn_precond_bf16
+
+    def call(k=FAKE, beta=FAKE, B=1, H=1, L=4, dk=16, eta=3e-3, dmin=0.5, dmax=2.0, eps=1e-6,
+             d=FAKE, kt=FAKE):
+        return f(k, beta, B, H, L, dk, eta, dmin, dmax, eps, d, kt, None)
+
+    assert call(k=None) == E.DP_EINVAL
+    assert call(d=None) == E.DP_EINVAL
+    assert call(kt=None) == E.DP_EINVAL
+    assert call(B=0) == E.DP_EINVAL
+    assert call(dk=48) == E.DP_ENOTSUP
+    assert call(eps=0.0) == E.DP_EINVAL
+    assert call(dmin=2.0, dmax=1.0) == E.DP_EINVAL
+    assert call(dmin=0.0) == E.DP_EINVAL
+    assert call(eta=float("nan")) == E.DP_EINVAL
+    assert call(L=0) == E.DP_OK  # nothing to do, nothing enqueued
+
+
+def test_binding_rejects_bad_tensors_on_cpu():
+    import torch
+    q = torch.zeros(1, 4, 1, 16)
+    k = torch.zeros(1, 4, 1, 2, 16)
+    v = torch.zeros(1, 4, 1, 2, 16)
+    beta = torch.zeros(1, 4, 1, 2)
+    with pytest.raises(TypeError):
+        dp.fwd(q.double(), k, v, beta)
+    with pytest.raises(ValueError):
+        dp.fwd(q, k[:, :3], v, beta)
