@@ -56,10 +56,12 @@ def alg_bytes(w):
     Per head and sub-step: k (dk), v (dv), beta (4 B) and, for the write-key
     workload, kt (dk); per head and token: q (dk), out (dv) and g (4 B) when
     gated; per head: the fp32 state out (and in, when there is an initial state).
+    The output counts at its stored width (fp32 for workloads run with fp32 out).
     """
     s = elem_bytes(w)
     N = w.L * w.n_h
-    per_head = N * (w.dk * s + w.dv * s + 4) + w.L * (w.dk + w.dv) * s
+    so = 4 if w.out_f32 else s
+    per_head = N * (w.dk * s + w.dv * s + 4) + w.L * (w.dk * s + w.dv * so)
     if w.asym:
         per_head += N * w.dk * s
     if w.gate:
@@ -123,7 +125,7 @@ def time_gpu(w, steps, warmup):
     dt = d["q"].dtype
     plan = dp.launch_info(w.n_h, w.B, w.H, w.L, w.dk, w.dv, w.chunk, dt, asym=w.asym)
     ws = dp.alloc_workspace(w.n_h, w.B, w.H, w.L, w.dk, w.dv, w.chunk, dt, dev)
-    out = torch.empty(w.B, w.L, w.H, w.dv, dtype=dt, device=dev)
+    out = torch.empty(w.B, w.L, w.H, w.dv, dtype=inp["out_dtype"], device=dev)
     fs = torch.empty(w.B, w.H, w.dk, w.dv, dtype=torch.float32, device=dev)
     k1 = b1 = kt = dstate = d1 = None
     if w.asym:

@@ -35,10 +35,15 @@
  *     work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
  *     and the call returns DP_OK without waiting for it.
  *   - Inputs are read-only and must not overlap out, final_state or the
- *     workspace.  h0 and final_state MAY be the same buffer (in-place resume).
+ *     workspace.  When L == 0 the per-token tensors are empty and may be NULL.  h0 and final_state MAY be the same buffer (in-place resume).
  *   - The library keeps no global state: calls on different streams may run
  *     concurrently as long as their buffers are disjoint.
  *   - NaN and Inf in the inputs propagate; nothing is silently repaired.
+ *   - Precision: the state and every accumulation are fp32.  On the bf16
+ *     path the computed MFMA operands (normalised keys, queries, write keys,
+ *     a rounded copy of the state, T diag(beta), pseudo-values, scores) are
+ *     fp16, so q, kt, v and the state must stay within fp16 range
+ *     (|x| < 65504); the fp32 path uses fp32 throughout.
  *   - Supported shapes: dk, dv in {16, 32, 64, 128}; chunk in {16, 32, 64}
  *     (counted in sub-steps of the expanded sequence); 1 <= n_h <= 64.
  *     B, H >= 1, L >= 0.  L*n_h need not be a multiple of chunk: the tail is
@@ -63,7 +68,7 @@ typedef enum {
 
 typedef void* dp_stream; /* hipStream_t */
 
-/* Stage bits for dp_fwd_staged_*.  DP_STAGE_ALL is what dp_fwd_* run. */
+/* Stage bits for dp_fwd_ex_*.  DP_STAGE_ALL is what dp_fwd_* run. */
 #define DP_STAGE_UT 1   /* per-chunk prep + UT transform -> workspace          */
 #define DP_STAGE_SCAN 2 /* inter-chunk state scan + readout + final state       */
 #define DP_STAGE_ALL 3
@@ -139,29 +144,34 @@ int dp_fwd_wk_bf16(const void* q, const void* k, const void* kt, const void* v,
                    void* workspace, size_t workspace_bytes, dp_stream stream);
 
 /*
- * The forward split into its two launches, for measurement and inspection:
- * `stages` is a mask of DP_STAGE_UT (fills the workspace) and DP_STAGE_SCAN
- * (consumes it).  kt may be NULL (symmetric) or a write-key tensor
- * (asymmetric).  Running DP_STAGE_UT then DP_STAGE_SCAN with the same
- * arguments is exactly dp_fwd_* / dp_fwd_wk_*; DP_STAGE_SCAN alone requires
- * a workspace filled by DP_STAGE_UT for the same k, kt, beta, g and sizes.
+ * General form of the forward: kt may be NULL (symmetric, as dp_fwd_*) or a
+ * write-key tensor (as dp_fwd_wk_*), and `flags` is an OR of
+ *   DP_STAGE_UT    run the per-chunk prep + UT launch (fills the workspace)
+ *   DP_STAGE_SCAN  run the chunk-scan launch (reads the workspace; writes out
+ *                  and final_state)
+ *   DP_OUT_F32     write `out` as float32 [B, L, H, dv] instead of T (bf16
+ *                  path only; the fp32 path always writes float32)
+ * At least one stage bit must be set.  DP_STAGE_UT then DP_STAGE_SCAN with
+ * the same arguments is exactly one DP_STAGE_ALL call; DP_STAGE_SCAN alone
+ * requires a workspace filled by DP_STAGE_UT for the same k, kt, beta, g
+ * and sizes.  The stages exist for measurement and inspection.
  */
-int dp_fwd_staged_f32(const float* q, const float* k, const float* kt, const float* v,
-                      const float* beta, const float* g, int n_h, int B, int H, int L,
-                      int dk, int dv, int chunk, float* out, float* final_state,
-                      const float* h0, void* workspace, size_t workspace_bytes, int stages,
-                      dp_stream stream);
-int dp_fwd_staged_bf16(const void* q, const void* k, const void* kt, const void* v,
-                       const float* beta, const float* g, int n_h, int B, int H, int L,
-                       int dk, int dv, int chunk, void* out, float* final_state,
-                       const float* h0, void* workspace, size_t workspace_bytes, int stages,
-                       dp_stream stream);
+#define DP_OUT_F32 4
+
+int dp_fwd_ex_f32(const float* q, const float* k, const float* kt, const float* v,
+                  const float* beta, const float* g, int n_h, int B, int H, int L, int dk,
+                  int dv, int chunk, float* out, float* final_state, const float* h0,
+                  void* workspace, size_t workspace_bytes, int flags, dp_stream stream);
+int dp_fwd_ex_bf16(const void* q, const void* k, const void* kt, const void* v,
+                   const float* beta, const float* g, int n_h, int B, int H, int L, int dk,
+                   int dv, int chunk, void* out, float* final_state, const float* h0,
+                   void* workspace, size_t workspace_bytes, int flags, dp_stream stream);
 
 /*
  * OSDN phase 1 (OSDN notes sec. 2.3-2.4, Alg.1), one sequential scan per head:
  *   k_t  <- k_t / max(|k_t|_2, 1e-6),  s = k_t * k_t,  b = clamp(beta_t, 0, 2)
  *   kt_t  = d_t * k_t                          (emitted before the update)
- *   d_{t+1} = clamp(d_t + eta * b * (1 - b <d_t, s>) / max(<1, s>, eps) * s,
+ *   d_{t+1} = clamp(d_t + eta * b * (1 - b <d_t, s>) / max(sum(s), eps) * s,
  *                   dmin, dmax)                (elementwise projection)
  *   k       [B, L, H, dk]   T    raw keys (the n_h = 1 key layout)
  *   beta    [B, L, H]     f32

@@ -15,13 +15,13 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdp.so")
 
 DP_OK, DP_EINVAL, DP_ENOTSUP, DP_EWORKSPACE, DP_EHIP = 0, -1, -2, -3, -4
-STAGE_UT, STAGE_SCAN, STAGE_ALL = 1, 2, 3
+STAGE_UT, STAGE_SCAN, STAGE_ALL, OUT_F32 = 1, 2, 3, 4
 
 # every symbol include/dp.h declares
 EXPORTS = (
     "dp_status_str", "dp_fwd_workspace_size", "dp_fwd_launch_info",
     "dp_fwd_f32", "dp_fwd_bf16", "dp_fwd_wk_f32", "dp_fwd_wk_bf16",
-    "dp_fwd_staged_f32", "dp_fwd_staged_bf16",
+    "dp_fwd_ex_f32", "dp_fwd_ex_bf16",
     "dp_osdn_precond_f32", "dp_osdn_precond_bf16",
 )
 
@@ -59,11 +59,11 @@ def load() -> ctypes.CDLL:
         for name in ("dp_fwd_wk_f32", "dp_fwd_wk_bf16"):
             getattr(lib, name).restype = _I
             getattr(lib, name).argtypes = wk_args
-        staged = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P,
-                  ctypes.c_size_t, _I, _P]
-        for name in ("dp_fwd_staged_f32", "dp_fwd_staged_bf16"):
+        ex = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P,
+              ctypes.c_size_t, _I, _P]
+        for name in ("dp_fwd_ex_f32", "dp_fwd_ex_bf16"):
             getattr(lib, name).restype = _I
-            getattr(lib, name).argtypes = staged
+            getattr(lib, name).argtypes = ex
         pre = [_P, _P, _I, _I, _I, _I, _F, _F, _F, _F, _P, _P, _P]
         for name in ("dp_osdn_precond_f32", "dp_osdn_precond_bf16"):
             getattr(lib, name).restype = _I
@@ -140,13 +140,15 @@ def alloc_workspace(n_h, B, H, L, dk, dv, chunk, dtype, device) -> torch.Tensor:
 
 def fwd(q, k, v, beta, g=None, *, chunk: int = 64, h0=None, kt=None, out=None,
         final_state=None, return_state: bool = True, workspace=None,
-        stages: int = STAGE_ALL, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+        stages: int = STAGE_ALL, out_dtype=None,
+        stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """DeltaProduct forward through libdp.
 
     q [B,L,H,dk], k [B,L,H,n_h,dk], v [B,L,H,n_h,dv] (float32 or bfloat16, one
     dtype), beta [B,L,H,n_h] f32, g [B,L,H] f32 or None, h0 [B,H,dk,dv] f32 or
-    None, kt (write keys, shape of k) or None.  Returns (out, final_state);
-    final_state is None when return_state is False and none was passed.
+    None, kt (write keys, shape of k) or None.  out_dtype: the input dtype
+    (default) or torch.float32.  Returns (out, final_state); final_state is
+    None when return_state is False and none was passed.
     """
     if q.dim() != 4 or k.dim() != 5 or v.dim() != 5:
         raise ValueError("expected q[B,L,H,dk], k[B,L,H,n_h,dk], v[B,L,H,n_h,dv]")
@@ -162,19 +164,25 @@ def fwd(q, k, v, beta, g=None, *, chunk: int = 64, h0=None, kt=None, out=None,
     _need(h0, "h0", torch.float32, (B, H, dk, dv), dev)
     if not q.is_contiguous():
         raise ValueError("q must be contiguous")
+    if out is not None and out_dtype is None:
+        out_dtype = out.dtype
+    odt = dt if out_dtype is None else out_dtype
+    if odt not in (dt, torch.float32):
+        raise TypeError(f"out_dtype must be {dt} or torch.float32")
+    flags = stages | (OUT_F32 if odt == torch.float32 else 0)
     if out is None:
-        out = torch.empty(B, L, H, dv, dtype=dt, device=dev)
-    _need(out, "out", dt, (B, L, H, dv), dev)
+        out = torch.empty(B, L, H, dv, dtype=odt, device=dev)
+    _need(out, "out", odt, (B, L, H, dv), dev)
     if final_state is None and return_state:
         final_state = torch.empty(B, H, dk, dv, dtype=torch.float32, device=dev)
     _need(final_state, "final_state", torch.float32, (B, H, dk, dv), dev)
     if workspace is None:
         workspace = alloc_workspace(n_h, B, H, L, dk, dv, chunk, dt, dev)
-    fn = getattr(load(), f"dp_fwd_staged_{suf}")
+    fn = getattr(load(), f"dp_fwd_ex_{suf}")
     rc = fn(_ptr(q), _ptr(k), _ptr(kt), _ptr(v), _ptr(beta), _ptr(g), n_h, B, H, L, dk, dv,
             chunk, _ptr(out), _ptr(final_state), _ptr(h0), _ptr(workspace),
-            workspace.numel() * workspace.element_size(), stages, _stream(stream))
-    _check(rc, f"dp_fwd_staged_{suf}")
+            workspace.numel() * workspace.element_size(), flags, _stream(stream))
+    _check(rc, f"dp_fwd_ex_{suf}")
     return out, final_state
 
 

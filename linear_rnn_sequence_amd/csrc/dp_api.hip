@@ -64,6 +64,18 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 int a16(int x) { return (x + 15) & ~15; }
 
+// Magic number for s / d, 0 <= s < 2^31, 1 <= d <= 64: with l = ceil(log2 d),
+// shift = 31 + l and magic = ceil(2^shift / d), s / d == (s * magic) >> shift
+// (the rounding error s * (magic * d - 2^shift) / (d 2^shift) stays below 1/d).
+void fastdiv_magic(int d, uint32_t* magic, int* shift) {
+  int l = 0;
+  while ((1 << l) < d) ++l;
+  const int sh = 31 + l;
+  const unsigned long long m = ((1ull << sh) + (unsigned long long)d - 1) / (unsigned long long)d;
+  *magic = (uint32_t)m;
+  *shift = sh;
+}
+
 // Readout rows a chunk can hold (ceil(C / n_h)), rounded up to MFMA tiles.
 int readout_rows(int C, int n_h) {
   const int r = (C + n_h - 1) / n_h;
@@ -82,16 +94,23 @@ int scan_layout(dp::FwdArgs& a, int elem, int DK, int C, int BV) {
   };
   a.oK = take(C * LDK * elem);
   a.oKt = a.asym ? take(C * LDK * elem) : a.oK;
-  a.oQ = take(a.RT * LDK * elem);
+  // the readout queries are dead after the first phase of a chunk and Up / Us
+  // are written after it: they share one region
+  const int q_bytes = a.RT * LDK * elem, u_bytes = a16(BV * LDC * elem);
+  a.oQ = take(q_bytes > 2 * u_bytes ? q_bytes : 2 * u_bytes);
+  a.oUo = a.oQ;
+  a.oUs = a.oQ + u_bytes;
   a.oT = take(C * LDC * elem);
   a.oHt = take(BV * LDK * elem);
   a.oXt = take(BV * LDC * elem);
-  a.oUo = take(BV * LDC * elem);
-  a.oUs = take(BV * LDC * elem);
   a.oP = take(a.RT * LDC * elem);
-  a.oR = take(C * 4);
+  a.oV = take(C * (BV + 4) * 4);
   a.oG = take(C * 4);
+  a.oEG = take(C * 4);
+  a.oEL = take(C * 4);
   a.oLoc = take(a.RT * 4);
+  a.oRow = take(2 * C * 8);
+  a.oTok = take(2 * a.RT * 8);
   return off;
 }
 
@@ -171,12 +190,15 @@ hipError_t dispatch_precond(int elem, int dk, const dp::PrecondArgs& a, hipStrea
 int fwd_impl(int elem, const void* q, const void* k, const void* kt, const void* v,
              const float* beta, const float* g, int n_h, int B, int H, int L, int dk, int dv,
              int chunk, void* out, float* final_state, const float* h0, void* workspace,
-             size_t workspace_bytes, int stages, dp_stream stream) {
+             size_t workspace_bytes, int flags, dp_stream stream) {
   const Shape s{n_h, B, H, L, dk, dv, chunk};
   int rc = check_shape(s);
   if (rc != DP_OK) return rc;
-  if (stages < 1 || stages > DP_STAGE_ALL) return DP_EINVAL;
-  if (q == nullptr || k == nullptr || v == nullptr || beta == nullptr || out == nullptr)
+  if ((flags & ~(DP_STAGE_ALL | DP_OUT_F32)) != 0) return DP_EINVAL;
+  const int stages = flags & DP_STAGE_ALL;
+  if (stages == 0) return DP_EINVAL;
+  // with L == 0 the per-token tensors are empty and may be null
+  if (L > 0 && (q == nullptr || k == nullptr || v == nullptr || beta == nullptr || out == nullptr))
     return DP_EINVAL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (kt != nullptr && !aligned16(kt)))
     return DP_EINVAL;
@@ -206,6 +228,8 @@ int fwd_impl(int elem, const void* q, const void* k, const void* kt, const void*
   a.nc = num_chunks(s);
   a.RT = readout_rows(chunk, n_h);
   a.asym = kt != nullptr ? 1 : 0;
+  a.out_f32 = (elem == 4 || (flags & DP_OUT_F32) != 0) ? 1 : 0;
+  fastdiv_magic(n_h, &a.nh_magic, &a.nh_shift);
 
   int BV = 0, lds = 0;
   rc = plan(a, elem, dk, chunk, &BV, &lds);
@@ -329,22 +353,20 @@ int dp_fwd_wk_bf16(const void* q, const void* k, const void* kt, const void* v,
                   workspace, workspace_bytes, DP_STAGE_ALL, stream);
 }
 
-int dp_fwd_staged_f32(const float* q, const float* k, const float* kt, const float* v,
-                      const float* beta, const float* g, int n_h, int B, int H, int L,
-                      int dk, int dv, int chunk, float* out, float* final_state,
-                      const float* h0, void* workspace, size_t workspace_bytes, int stages,
-                      dp_stream stream) {
+int dp_fwd_ex_f32(const float* q, const float* k, const float* kt, const float* v,
+                  const float* beta, const float* g, int n_h, int B, int H, int L, int dk,
+                  int dv, int chunk, float* out, float* final_state, const float* h0,
+                  void* workspace, size_t workspace_bytes, int flags, dp_stream stream) {
   return fwd_impl(4, q, k, kt, v, beta, g, n_h, B, H, L, dk, dv, chunk, out, final_state, h0,
-                  workspace, workspace_bytes, stages, stream);
+                  workspace, workspace_bytes, flags, stream);
 }
 
-int dp_fwd_staged_bf16(const void* q, const void* k, const void* kt, const void* v,
-                       const float* beta, const float* g, int n_h, int B, int H, int L,
-                       int dk, int dv, int chunk, void* out, float* final_state,
-                       const float* h0, void* workspace, size_t workspace_bytes, int stages,
-                       dp_stream stream) {
+int dp_fwd_ex_bf16(const void* q, const void* k, const void* kt, const void* v,
+                   const float* beta, const float* g, int n_h, int B, int H, int L, int dk,
+                   int dv, int chunk, void* out, float* final_state, const float* h0,
+                   void* workspace, size_t workspace_bytes, int flags, dp_stream stream) {
   return fwd_impl(2, q, k, kt, v, beta, g, n_h, B, H, L, dk, dv, chunk, out, final_state, h0,
-                  workspace, workspace_bytes, stages, stream);
+                  workspace, workspace_bytes, flags, stream);
 }
 
 int dp_osdn_precond_f32(const float* k, const float* beta, int B, int H, int L, int dk,

@@ -1,7 +1,8 @@
 // dp_device.hpp -- gfx950 device helpers shared by the DeltaProduct kernels:
 // element conversion, 16-byte vector moves, MFMA fragment traits and small
-// lane reductions.  CDNA4 only: 64-lane wavefronts, v_mfma_f32_16x16x32_bf16
-// for the bf16 path and v_mfma_f32_16x16x4_f32 for the fp32 path.
+// lane reductions.  CDNA4 only: 64-lane wavefronts; v_mfma_f32_16x16x32_bf16
+// and v_mfma_f32_16x16x32_f16 for the bf16 path, v_mfma_f32_16x16x4_f32 for
+// the fp32 path.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -10,17 +11,35 @@
 namespace dp {
 
 using bf16_t = uint16_t;  // bfloat16 storage (raw bits)
+using f16_t = _Float16;   // IEEE half
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+// Workgroup barrier that orders LDS only.  Global loads issued before it stay
+// in flight (the compiler waits for them where their registers are used), so
+// a prefetch of the next chunk overlaps the current chunk's compute.  The
+// kernels exchange data between waves through LDS only.
+__device__ __forceinline__ void block_sync_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// s / d for 0 <= s < 2^31 with a host-computed magic number (see fastdiv_magic).
+__device__ __forceinline__ int fastdiv(int s, uint32_t magic, int shift) {
+  return (int)(((unsigned long long)(unsigned)s * magic) >> shift);
+}
 
 // ------------------------------------------------------------ conversions
 
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float((uint32_t)x << 16); }
+__device__ __forceinline__ float to_f32(f16_t x) { return (float)x; }
 
 template <typename T>
 __device__ __forceinline__ T from_f32(float x);
@@ -37,6 +56,12 @@ __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) {
   if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x0040u);
   u += 0x7fffu + ((u >> 16) & 1u);
   return (bf16_t)(u >> 16);
+}
+
+// fp32 -> fp16, round to nearest even (hardware conversion).
+template <>
+__device__ __forceinline__ f16_t from_f32<f16_t>(float x) {
+  return (f16_t)x;
 }
 
 // Elements of type T held in one 16-byte vector.
@@ -65,10 +90,26 @@ __device__ __forceinline__ void st16(void* p, const u32x4_t& v) {
   *reinterpret_cast<u32x4_t*>(p) = v;
 }
 
+// Store 16 bytes of consecutive elements (fp32 inputs, 16/sizeof(T) of them) as T.
+__device__ __forceinline__ void st_vec16(float* p, const float* f) {
+  f32x4_t v = {f[0], f[1], f[2], f[3]};
+  *reinterpret_cast<f32x4_t*>(p) = v;
+}
+__device__ __forceinline__ void st_vec16(f16_t* p, const float* f) {
+  f16x8_t v;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (f16_t)f[i];
+  *reinterpret_cast<f16x8_t*>(p) = v;
+}
+
 // Store 4 consecutive elements (fp32 inputs) as T at p.
 __device__ __forceinline__ void st4(float* p, float a, float b, float c, float d) {
   f32x4_t v = {a, b, c, d};
   *reinterpret_cast<f32x4_t*>(p) = v;
+}
+__device__ __forceinline__ void st4(f16_t* p, float a, float b, float c, float d) {
+  f16x4_t v = {(f16_t)a, (f16_t)b, (f16_t)c, (f16_t)d};
+  *reinterpret_cast<f16x4_t*>(p) = v;
 }
 __device__ __forceinline__ void st4(bf16_t* p, float a, float b, float c, float d) {
   u32x2_t v;
@@ -113,6 +154,63 @@ struct Mfma<bf16_t> {
   __device__ __forceinline__ static f32x4_t mma(const frag_t& a, const frag_t& b, const f32x4_t& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
+  // 16-deep step (v_mfma_f32_16x16x16_bf16) for a contraction of length 16
+  using frag4_t = s16x4_t;
+  __device__ __forceinline__ static frag4_t load4(const bf16_t* base, int ld, int row0, int k0) {
+    const int l = threadIdx.x & 63;
+    return *reinterpret_cast<const frag4_t*>(base + (row0 + (l & 15)) * ld + k0 + 4 * (l >> 4));
+  }
+  __device__ __forceinline__ static frag4_t load4_t(const bf16_t* base, int ld, int row0, int k0) {
+    const int l = threadIdx.x & 63;
+    const bf16_t* p = base + (k0 + 4 * (l >> 4)) * ld + row0 + (l & 15);
+    frag4_t v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (short)p[e * ld];
+    return v;
+  }
+  __device__ __forceinline__ static f32x4_t mma4(const frag4_t& a, const frag4_t& b, const f32x4_t& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+  }
+};
+
+template <>
+struct Mfma<f16_t> {
+  static constexpr int KS = 32;
+  using frag_t = f16x8_t;
+
+  __device__ __forceinline__ static frag_t load(const f16_t* base, int ld, int row0, int k0) {
+    const int l = threadIdx.x & 63;
+    const f16_t* p = base + (row0 + (l & 15)) * ld + k0 + 8 * (l >> 4);
+    return *reinterpret_cast<const frag_t*>(p);
+  }
+  __device__ __forceinline__ static frag_t load_t(const f16_t* base, int ld, int row0, int k0) {
+    const int l = threadIdx.x & 63;
+    const f16_t* p = base + (k0 + 8 * (l >> 4)) * ld + row0 + (l & 15);
+    frag_t v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = p[e * ld];
+    return v;
+  }
+  __device__ __forceinline__ static f32x4_t mma(const frag_t& a, const frag_t& b, const f32x4_t& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  // 16-deep step (v_mfma_f32_16x16x16_f16) for a contraction of length 16
+  using frag4_t = f16x4_t;
+  __device__ __forceinline__ static frag4_t load4(const f16_t* base, int ld, int row0, int k0) {
+    const int l = threadIdx.x & 63;
+    return *reinterpret_cast<const frag4_t*>(base + (row0 + (l & 15)) * ld + k0 + 4 * (l >> 4));
+  }
+  __device__ __forceinline__ static frag4_t load4_t(const f16_t* base, int ld, int row0, int k0) {
+    const int l = threadIdx.x & 63;
+    const f16_t* p = base + (k0 + 4 * (l >> 4)) * ld + row0 + (l & 15);
+    frag4_t v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = p[e * ld];
+    return v;
+  }
+  __device__ __forceinline__ static f32x4_t mma4(const frag4_t& a, const frag4_t& b, const f32x4_t& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+  }
 };
 
 template <>
@@ -131,15 +229,27 @@ struct Mfma<float> {
   __device__ __forceinline__ static f32x4_t mma(const frag_t& a, const frag_t& b, const f32x4_t& c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
   }
+  using frag4_t = float;  // unused: every contraction length is a multiple of 4
+  __device__ __forceinline__ static frag4_t load4(const float*, int, int, int) { return 0.f; }
+  __device__ __forceinline__ static frag4_t load4_t(const float*, int, int, int) { return 0.f; }
+  __device__ __forceinline__ static f32x4_t mma4(const frag4_t&, const frag4_t&, const f32x4_t& c) {
+    return c;
+  }
 };
 
-// acc += A[row0a.., 0..K) * B[0..K, row0b..]  (both "row by k" buffers)
+// acc += A[ra.., 0..K) * B[0..K, rb..]  (both "row by k" buffers).  K is a
+// multiple of the instruction depth, or of 16 for the 16-bit types (the last
+// 16 of the contraction then use the 16-deep instruction).
 template <typename T, int K>
 __device__ __forceinline__ f32x4_t mm_tile(f32x4_t acc, const T* a, int lda, int ra, const T* b,
                                            int ldb, int rb) {
   using M = Mfma<T>;
+  static_assert(K % M::KS == 0 || K % M::KS == 16, "contraction length");
 #pragma unroll
-  for (int k0 = 0; k0 < K; k0 += M::KS) acc = M::mma(M::load(a, lda, ra, k0), M::load(b, ldb, rb, k0), acc);
+  for (int k0 = 0; k0 + M::KS <= K; k0 += M::KS)
+    acc = M::mma(M::load(a, lda, ra, k0), M::load(b, ldb, rb, k0), acc);
+  if constexpr (K % M::KS == 16)
+    acc = M::mma4(M::load4(a, lda, ra, K - 16), M::load4(b, ldb, rb, K - 16), acc);
   return acc;
 }
 
@@ -148,9 +258,12 @@ template <typename T, int K>
 __device__ __forceinline__ f32x4_t mm_tile_ta(f32x4_t acc, const T* a, int lda, int ra, const T* b,
                                               int ldb, int rb) {
   using M = Mfma<T>;
+  static_assert(K % M::KS == 0 || K % M::KS == 16, "contraction length");
 #pragma unroll
-  for (int k0 = 0; k0 < K; k0 += M::KS)
+  for (int k0 = 0; k0 + M::KS <= K; k0 += M::KS)
     acc = M::mma(M::load_t(a, lda, ra, k0), M::load(b, ldb, rb, k0), acc);
+  if constexpr (K % M::KS == 16)
+    acc = M::mma4(M::load4_t(a, lda, ra, K - 16), M::load4(b, ldb, rb, K - 16), acc);
   return acc;
 }
 
@@ -159,9 +272,12 @@ template <typename T, int K>
 __device__ __forceinline__ f32x4_t mm_tile_tb(f32x4_t acc, const T* a, int lda, int ra, const T* b,
                                               int ldb, int rb) {
   using M = Mfma<T>;
+  static_assert(K % M::KS == 0 || K % M::KS == 16, "contraction length");
 #pragma unroll
-  for (int k0 = 0; k0 < K; k0 += M::KS)
+  for (int k0 = 0; k0 + M::KS <= K; k0 += M::KS)
     acc = M::mma(M::load(a, lda, ra, k0), M::load_t(b, ldb, rb, k0), acc);
+  if constexpr (K % M::KS == 16)
+    acc = M::mma4(M::load4(a, lda, ra, K - 16), M::load4_t(b, ldb, rb, K - 16), acc);
   return acc;
 }
 

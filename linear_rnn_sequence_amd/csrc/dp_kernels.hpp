@@ -31,6 +31,12 @@
 //                   readout rows and the state update on MFMA; at the end it
 //                   writes the final state.
 // A third kernel, dp_precond_kernel, is the OSDN phase-1 scan.
+//
+// Precision: on the bf16 path the inputs are bf16, every accumulation and the
+// carried state are fp32, and the MFMA operands that are computed (T diag(beta),
+// the state copy, X, Up, the masked scores, the normalised keys) are fp16 -- the
+// same MFMA rate as bf16 with 3 more mantissa bits.  The fp32 path uses fp32
+// MFMA throughout.
 #pragma once
 
 #include <float.h>
@@ -40,6 +46,16 @@
 namespace dp {
 
 constexpr int kThreads = 256;  // 4 wavefronts
+
+// MFMA operand type for computed operands: fp16 on the bf16 path, fp32 on the fp32 path.
+template <typename T>
+struct OpType {
+  using type = T;
+};
+template <>
+struct OpType<bf16_t> {
+  using type = f16_t;
+};
 
 struct FwdArgs {
   const void* q;
@@ -51,12 +67,15 @@ struct FwdArgs {
   const float* h0;  // nullptr: zero initial state
   void* out;
   float* fstate;    // nullptr: final state not returned
-  void* wsT;        // [B*H*nc][C][C] of T: T diag(beta)
+  void* wsT;        // [B*H*nc][C][C]: T diag(beta), operand type (fp16 / fp32)
   float2* wsS;      // [B*H*nc][C]: (1/|k|, G)
   int N;            // L * n_h sub-steps per head
   int B, H, L, n_h, dv, nc, RT, nvb, asym;
+  int out_f32;      // 1: out is fp32 whatever the input type
+  uint32_t nh_magic;  // s / n_h == fastdiv(s, nh_magic, nh_shift) for 0 <= s < 2^31
+  int nh_shift;
   // dp_scan_kernel LDS byte offsets
-  int oK, oKt, oQ, oT, oHt, oXt, oUo, oUs, oP, oR, oG, oLoc;
+  int oK, oKt, oQ, oT, oHt, oXt, oUo, oUs, oP, oV, oG, oEG, oEL, oLoc, oRow, oTok;
 };
 
 struct PrecondArgs {
@@ -68,14 +87,15 @@ struct PrecondArgs {
   float eta, dmin, dmax, eps;
 };
 
-// Row index of sub-step s of head (b, h) in a [B, L, H, n_h, *] tensor.
-__device__ __forceinline__ long long sub_row(int s, int n_h, int b, int h, int L, int H) {
-  const int t = s / n_h;
-  const int j = s - t * n_h;
-  return (((long long)b * L + t) * H + h) * n_h + j;
-}
-
 __host__ __device__ constexpr int align16(int x) { return (x + 15) & ~15; }
+
+// Row of sub-step s of head (b, h) in a [B, L, H, n_h, *] tensor:
+// ((b L + t) H + h) n_h + j with t = s / n_h, j = s % n_h.
+__device__ __forceinline__ long long sub_row(const FwdArgs& p, int s, int b, int h) {
+  const int t = fastdiv(s, p.nh_magic, p.nh_shift);
+  const int j = s - t * p.n_h;
+  return (((long long)b * p.L + t) * p.H + h) * p.n_h + j;
+}
 
 // LDS bytes of dp_ut_kernel: K (and Kw) rows, fp32 M, 3 scalar vectors,
 // fp32 T and the per-wave partial-sum tiles of the blocked inverse.
@@ -88,11 +108,14 @@ __host__ __device__ constexpr int ut_lds_bytes(int elem, int DK, int C, int asym
 // dp_ut_kernel: per-chunk prep + UT transform.
 template <typename T, int DK, int C>
 __global__ __launch_bounds__(kThreads) void dp_ut_kernel(FwdArgs p) {
+  using OT = typename OpType<T>::type;
   constexpr int VE = Vec<T>::N;
   constexpr int LDK = DK + VE;  // 16-byte row pad
   constexpr int LDA = C + 4;
   constexpr int NT = C / 16;
   constexpr int TPR = DK / VE;  // threads per key row (<= 32)
+  constexpr int KV = C * TPR;   // 16-byte vectors in a key tile
+  constexpr int KIT = (KV + kThreads - 1) / kThreads;
   static_assert(TPR <= 64 && (64 % TPR) == 0, "row group must fit in a wavefront");
 
   extern __shared__ __align__(16) unsigned char smem[];
@@ -103,8 +126,8 @@ __global__ __launch_bounds__(kThreads) void dp_ut_kernel(FwdArgs p) {
   float* sR = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(sA) + align16(C * LDA * 4));
   float* sB = sR + C;
   float* sG = sB + C;
-  float* sTf = sG + C;             // C x LDA fp32: T
-  float* sSc = sTf + C * LDA;      // 4 x 16 x 17 fp32: per-wave partial sums
+  float* sTf = sG + C;         // C x LDA fp32: T
+  float* sSc = sTf + C * LDA;  // 4 x 16 x 17 fp32: per-wave partial sums
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const long long chunk = blockIdx.x;
@@ -114,47 +137,61 @@ __global__ __launch_bounds__(kThreads) void dp_ut_kernel(FwdArgs p) {
   const T* kp = static_cast<const T*>(p.k);
   const T* ktp = static_cast<const T*>(p.kt);
 
-  // 1. gather the chunk's key rows; row norms by a TPR-lane reduction
-  for (int idx = tid; idx < C * TPR; idx += kThreads) {
+  // 1. issue every global load of the chunk first: key rows, beta, gate
+  u32x4_t rk[KIT], rkt[KIT];
+#pragma unroll
+  for (int it = 0; it < KIT; ++it) {
+    const int idx = tid + it * kThreads;
     const int r = idx / TPR, cg = idx % TPR;
     const int s = s0 + r;
-    u32x4_t val = {0u, 0u, 0u, 0u}, valt = {0u, 0u, 0u, 0u};
-    if (s < p.N) {
-      const long long off = sub_row(s, p.n_h, b, h, p.L, p.H) * DK + cg * VE;
-      val = ld16(kp + off);
-      if (p.asym) valt = ld16(ktp + off);
+    rk[it] = u32x4_t{0u, 0u, 0u, 0u};
+    rkt[it] = u32x4_t{0u, 0u, 0u, 0u};
+    if (idx < KV && s < p.N) {
+      const long long off = sub_row(p, s, b, h) * DK + cg * VE;
+      rk[it] = ld16(kp + off);
+      if (p.asym) rkt[it] = ld16(ktp + off);
     }
-    st16(sK + r * LDK + cg * VE, val);
-    if (p.asym) st16(sKt + r * LDK + cg * VE, valt);
+  }
+  float braw = 0.f, lam = 0.f;
+  bool first = false;
+  if (tid < C && s0 + tid < p.N) {
+    const int s = s0 + tid;
+    const int t = fastdiv(s, p.nh_magic, p.nh_shift);
+    const int j = s - t * p.n_h;
+    const long long tok = ((long long)b * p.L + t) * p.H + h;
+    braw = p.beta[tok * p.n_h + j];
+    first = (j == 0);
+    if (p.g != nullptr && first) lam = logf(fmaxf(p.g[tok], FLT_MIN));
+  }
+  // 2. key tiles to LDS; row norms by a TPR-lane reduction (every lane joins)
+#pragma unroll
+  for (int it = 0; it < KIT; ++it) {
+    const int idx = tid + it * kThreads;
+    const int r = idx / TPR, cg = idx % TPR;
+    if (idx < KV) {
+      st16(sK + r * LDK + cg * VE, rk[it]);
+      if (p.asym) st16(sKt + r * LDK + cg * VE, rkt[it]);
+    }
     float f[VE];
-    unpack16(val, f, T{});
+    unpack16(rk[it], f, T{});
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < VE; ++e) ss = fmaf(f[e], f[e], ss);
     ss = group_sum<TPR>(ss);
-    if (cg == 0) sR[r] = (s < p.N) ? 1.f / fmaxf(sqrtf(ss), 1e-6f) : 0.f;
+    if (idx < KV && cg == 0) sR[r] = (s0 + r < p.N) ? 1.f / fmaxf(sqrtf(ss), 1e-6f) : 0.f;
   }
-  // 2. beta range and chunk-local cumulative log-gate (sub-steps s < C in wave 0)
+  // 3. beta range and chunk-local cumulative log-gate (C <= 64: wave 0)
   if (wave == 0) {
-    float lam = 0.f, bt = 0.f;
-    const int s = s0 + lane;
-    if (lane < C && s < p.N) {
-      const int t = s / p.n_h;
-      const int j = s - t * p.n_h;
-      const long long tok = ((long long)b * p.L + t) * p.H + h;
-      bt = clamp_keep_nan(p.beta[tok * p.n_h + j], 0.f, 2.f);
-      if (p.g != nullptr && j == 0) lam = logf(fmaxf(p.g[tok], FLT_MIN));
-    }
     const float G = wave_inclusive_scan(lam);
     if (lane < C) {
-      sB[lane] = bt;
+      sB[lane] = clamp_keep_nan(braw, 0.f, 2.f);
       sG[lane] = G;
     }
   }
-  __syncthreads();
+  block_sync_lds();
   if (tid < C) p.wsS[chunk * C + tid] = make_float2(sR[tid], sG[tid]);
 
-  // 3. M = strict_tril(diag(beta) (E o Kn Kw^T)) on MFMA (lower tiles only)
+  // 4. M = strict_tril(diag(beta) (E o Kn Kw^T)) on MFMA (lower tiles only)
   for (int tile = wave; tile < NT * NT; tile += 4) {
     const int ti = tile / NT, tj = tile % NT;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -169,13 +206,13 @@ __global__ __launch_bounds__(kThreads) void dp_ut_kernel(FwdArgs p) {
       sA[ii * LDA + jj] = val;
     }
   }
-  __syncthreads();
+  block_sync_lds();
 
-  // 4. T = (I + M)^{-1} (fp32), blocked over 16 x 16 tiles:
+  // 5. T = (I + M)^{-1} (fp32), blocked over 16 x 16 tiles:
   //    diagonal tiles D_b = (I + M_bb)^{-1} by forward substitution (one
   //    16-lane group per tile, one column per lane), then the off-diagonal
-  //    tiles level by level (i - j = 1, 2, ..):  T_ij = -D_i sum_{k=j}^{i-1} M_ik T_kj
-  //    on fp32 MFMA.
+  //    tiles level by level (i - j = 1, 2, ..):
+  //    T_ij = -D_i sum_{k=j}^{i-1} M_ik T_kj  on fp32 MFMA.
   if (wave == 0) {
     const int gb = lane >> 4, cc = lane & 15;
     if (gb < NT) {
@@ -192,7 +229,7 @@ __global__ __launch_bounds__(kThreads) void dp_ut_kernel(FwdArgs p) {
       for (int i = 0; i < 16; ++i) sTf[(gb * 16 + i) * LDA + gb * 16 + cc] = t[i];
     }
   }
-  __syncthreads();
+  block_sync_lds();
 #pragma unroll
   for (int dist = 1; dist < NT; ++dist) {
     const int j = wave, i = wave + dist;  // NT - dist <= 3 tiles per level
@@ -205,58 +242,96 @@ __global__ __launch_bounds__(kThreads) void dp_ut_kernel(FwdArgs p) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) sS[(4 * (lane >> 4) + e) * 17 + (lane & 15)] = acc[e];
     }
-    __syncthreads();
+    block_sync_lds();
     if (i < NT) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
       acc = mm_tile_tb<float, 16>(acc, sTf + i * 16 * LDA + i * 16, LDA, 0, sS, 17, 0);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sTf[(i * 16 + 4 * (lane >> 4) + e) * LDA + j * 16 + (lane & 15)] = -acc[e];
+      for (int e = 0; e < 4; ++e)
+        sTf[(i * 16 + 4 * (lane >> 4) + e) * LDA + j * 16 + (lane & 15)] = -acc[e];
     }
-    __syncthreads();
+    block_sync_lds();
   }
-  // T diag(beta) -> workspace (upper tiles are zero)
+  // 6. T diag(beta) -> workspace in the operand type, 8 columns per store
+  //    (upper tiles are zero)
   {
-    T* wt = static_cast<T*>(p.wsT) + chunk * C * C;
-    for (int idx = tid; idx < C * C; idx += kThreads) {
-      const int i = idx / C, j = idx % C;
-      const float val = ((j >> 4) > (i >> 4)) ? 0.f : sTf[i * LDA + j] * sB[j];
-      wt[idx] = from_f32<T>(val);
+    OT* wt = static_cast<OT*>(p.wsT) + chunk * C * C;
+    constexpr int NV8 = C * C / 8;
+    for (int v8 = tid; v8 < NV8; v8 += kThreads) {
+      const int i = v8 / (C / 8), j0 = (v8 % (C / 8)) * 8;
+      float f[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int j = j0 + e;
+        f[e] = ((j >> 4) > (i >> 4)) ? 0.f : sTf[i * LDA + j] * sB[j];
+      }
+      if constexpr (sizeof(OT) == 2) {
+        st_vec16(wt + i * C + j0, f);
+      } else {
+        st_vec16(wt + i * C + j0, f);
+        st_vec16(wt + i * C + j0 + 4, f + 4);
+      }
     }
   }
 }
 
 // ---------------------------------------------------------------------------
 // dp_scan_kernel: sequential chunk scan for one (head, value block).
-template <typename T, int DK, int C, int BV>
+//
+// Software pipeline: the global loads of chunk c+1 (key rows, T diag(beta),
+// gates, readout queries, values) are issued into registers after chunk c's
+// tiles are committed to LDS and land while chunk c is computed.  Every load
+// is unconditional (rows past the end are clamped to row 0 and zeroed when
+// committed), so no wait is forced before the compute.  Row indices of the
+// next chunk's sub-steps and readout tokens are computed once per chunk into
+// LDS.  All barriers order LDS only.  NRT = readout-row tiles per chunk.
+template <typename T, int DK, int C, int BV, int NRT>
 __global__ __launch_bounds__(kThreads) void dp_scan_kernel(FwdArgs p) {
+  using OT = typename OpType<T>::type;  // MFMA operand type
+  static_assert(sizeof(OT) == sizeof(T), "operand and input types share a width");
   constexpr int VE = Vec<T>::N;
-  constexpr int LDK = DK + VE;
-  constexpr int LDC = C + VE;
+  constexpr int LDK = DK + VE;  // rows of dk operands + 16 B
+  constexpr int LDC = C + VE;   // rows of C operands + 16 B
+  constexpr int LDV = BV + 4;   // fp32 value rows
+  constexpr int RT = NRT * 16;
   constexpr int NCT = C / 16, NVT = BV / 16, NDT = DK / 16;
-  constexpr int NYT = NCT * NVT;  // Y and Up tiles
+  constexpr int NYT = NCT * NVT;  // X and Up tiles
   constexpr int YPW = (NYT + 3) / 4;
+  constexpr int NPT = NCT * NRT;  // score tiles
+  constexpr int PPW = (NPT + 3) / 4;
+  constexpr int NZT = NRT * NVT;  // readout tiles
+  constexpr int ZPW = (NZT + 3) / 4;
   constexpr int NHT = NDT * NVT;  // state tiles
   constexpr int HPW = (NHT + 3) / 4;
-  constexpr int ZPW = (NCT * NVT + 3) / 4;  // readout tiles, at most (C/16) x NVT
-  constexpr int TPR = DK / VE;
-  constexpr int TPRC = C / VE;
+  constexpr int TPR = DK / VE;   // 16-byte vectors per key / query row
+  constexpr int TPRC = C / VE;   // per T row
+  constexpr int BVV = BV / VE;   // per value row
+  constexpr int KV = C * TPR, KIT = (KV + kThreads - 1) / kThreads;
+  constexpr int QV = RT * TPR, QIT = (QV + kThreads - 1) / kThreads;
+  constexpr int TV = C * TPRC, TIT = (TV + kThreads - 1) / kThreads;
+  constexpr int VV = C * BVV, VIT = (VV + kThreads - 1) / kThreads;
 
   extern __shared__ __align__(16) unsigned char smem[];
-  T* sK = reinterpret_cast<T*>(smem + p.oK);
-  T* sKt = reinterpret_cast<T*>(smem + p.oKt);
-  T* sQ = reinterpret_cast<T*>(smem + p.oQ);
-  T* sT = reinterpret_cast<T*>(smem + p.oT);
-  T* sHt = reinterpret_cast<T*>(smem + p.oHt);
-  T* sXt = reinterpret_cast<T*>(smem + p.oXt);
-  T* sUo = reinterpret_cast<T*>(smem + p.oUo);
-  T* sUs = reinterpret_cast<T*>(smem + p.oUs);
-  T* sP = reinterpret_cast<T*>(smem + p.oP);
-  float* sR = reinterpret_cast<float*>(smem + p.oR);
-  float* sG = reinterpret_cast<float*>(smem + p.oG);
-  int* sLoc = reinterpret_cast<int*>(smem + p.oLoc);
-  const T* sKw = p.asym ? sKt : sK;
+  OT* sK = reinterpret_cast<OT*>(smem + p.oK);    // unit read keys
+  OT* sKt = reinterpret_cast<OT*>(smem + p.oKt);  // write keys (asymmetric)
+  OT* sQ = reinterpret_cast<OT*>(smem + p.oQ);    // readout queries
+  OT* sT = reinterpret_cast<OT*>(smem + p.oT);    // T diag(beta)
+  OT* sHt = reinterpret_cast<OT*>(smem + p.oHt);  // H^T (operand copy of the fp32 state)
+  OT* sXt = reinterpret_cast<OT*>(smem + p.oXt);  // X^T
+  OT* sUo = reinterpret_cast<OT*>(smem + p.oUo);  // Up^T
+  OT* sUs = reinterpret_cast<OT*>(smem + p.oUs);  // (diag(e^{G_last - G}) Up)^T
+  OT* sP = reinterpret_cast<OT*>(smem + p.oP);    // masked, gated scores
+  float* sV = reinterpret_cast<float*>(smem + p.oV);    // values, C x LDV fp32
+  float* sG = reinterpret_cast<float*>(smem + p.oG);    // G
+  float* sEG = reinterpret_cast<float*>(smem + p.oEG);  // e^G
+  float* sEL = reinterpret_cast<float*>(smem + p.oEL);  // e^{G_last - G}
+  int* sLoc = reinterpret_cast<int*>(smem + p.oLoc);    // readout row -> sub-step in chunk
+  long long* sRow = reinterpret_cast<long long*>(smem + p.oRow);  // [2][C] sub-step rows
+  long long* sTok = reinterpret_cast<long long*>(smem + p.oTok);  // [2][RT] readout tokens
+  const OT* sKw = p.asym ? sKt : sK;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
   // XCD-aware mapping: consecutive workgroup ids go round-robin over the 8
   // XCDs, so spread ids so that the value blocks of one head share an XCD
@@ -266,13 +341,140 @@ __global__ __launch_bounds__(kThreads) void dp_scan_kernel(FwdArgs p) {
   const int bh = f / p.nvb, vb = f % p.nvb;
   const int b = bh / p.H, h = bh % p.H;
   const int v0 = vb * BV;
-  const int n_h = p.n_h, RT = p.RT, NRT = RT / 16;
+  const int n_h = p.n_h, nc = p.nc;
   const T* kp = static_cast<const T*>(p.k);
   const T* ktp = static_cast<const T*>(p.kt);
-  const T* vp = static_cast<const T*>(p.v);
+  const T* vp = static_cast<const T*>(p.v) + v0;
   const T* qp = static_cast<const T*>(p.q);
-  const T* wsT = static_cast<const T*>(p.wsT);
-  T* op = static_cast<T*>(p.out);
+  const OT* wsT = static_cast<const OT*>(p.wsT) + (long long)bh * nc * C * C;
+  const float2* wsS = p.wsS + (long long)bh * nc * C;
+  const long long tok0 = (long long)b * p.L * p.H + h;  // token (b, 0, h)
+
+  // row indices of chunk c's sub-steps / readout tokens into buffer c & 1
+  auto index_chunk = [&](int c) {
+    const int s0 = c * C;
+    long long* rows = sRow + (c & 1) * C;
+    long long* toks = sTok + (c & 1) * RT;
+    if (tid < C) {
+      const int s = s0 + tid;
+      long long row = 0;
+      if (s < p.N) {
+        const int t = fastdiv(s, p.nh_magic, p.nh_shift);
+        row = (tok0 + (long long)t * p.H) * n_h + (s - t * n_h);
+      }
+      rows[tid] = row;
+    }
+    if (tid < RT) {
+      const int r0 = s0 + (n_h - 1 - (s0 - fastdiv(s0, p.nh_magic, p.nh_shift) * n_h));
+      const int s = r0 + tid * n_h;
+      toks[tid] = (s < s0 + C && s < p.N) ? tok0 + (long long)fastdiv(s, p.nh_magic, p.nh_shift) * p.H
+                                           : -1;
+    }
+  };
+
+  // ---- prefetch registers (one chunk)
+  u32x4_t rk[KIT], rkt[KIT], rq[QIT], rt[TIT], rvv[VIT];
+  float rinv[KIT];
+  float rg;
+
+  auto prefetch = [&](int c) {
+    const long long* rows = sRow + (c & 1) * C;
+    const long long* toks = sTok + (c & 1) * RT;
+    const OT* tsrc = wsT + (long long)c * C * C;
+    const float2* ssrc = wsS + (long long)c * C;
+#pragma unroll
+    for (int it = 0; it < KIT; ++it) {
+      const int idx = (KV % kThreads == 0) ? tid + it * kThreads : min(tid + it * kThreads, KV - 1);
+      const int r = idx / TPR, cg = idx % TPR;
+      const long long off = rows[r] * DK + cg * VE;
+      rk[it] = ld16(kp + off);
+      if (p.asym) rkt[it] = ld16(ktp + off);
+      rinv[it] = ssrc[r].x;
+    }
+#pragma unroll
+    for (int it = 0; it < TIT; ++it) {
+      const int idx = (TV % kThreads == 0) ? tid + it * kThreads : min(tid + it * kThreads, TV - 1);
+      rt[it] = ld16(tsrc + idx * VE);
+    }
+    rg = ssrc[min(tid, C - 1)].y;
+#pragma unroll
+    for (int it = 0; it < QIT; ++it) {
+      const int idx = (QV % kThreads == 0) ? tid + it * kThreads : min(tid + it * kThreads, QV - 1);
+      const int i = idx / TPR, cg = idx % TPR;
+      const long long tk = toks[i];
+      rq[it] = ld16(qp + (tk < 0 ? 0 : tk) * DK + cg * VE);
+    }
+#pragma unroll
+    for (int it = 0; it < VIT; ++it) {
+      const int idx = (VV % kThreads == 0) ? tid + it * kThreads : min(tid + it * kThreads, VV - 1);
+      const int r = idx / BVV, cv = idx % BVV;
+      rvv[it] = ld16(vp + rows[r] * p.dv + cv * VE);
+    }
+  };
+
+  // ---- registers -> LDS (chunk c); also index chunk c+1
+  auto commit = [&](int c) {
+    const int s0 = c * C;
+    const long long* toks = sTok + (c & 1) * RT;
+#pragma unroll
+    for (int it = 0; it < KIT; ++it) {
+      const int idx = tid + it * kThreads;
+      const int r = idx / TPR, cg = idx % TPR;
+      if (KV % kThreads == 0 || idx < KV) {
+        float fv[VE];
+        unpack16(rk[it], fv, T{});
+#pragma unroll
+        for (int e = 0; e < VE; ++e) fv[e] *= rinv[it];  // 1/|k|, 0 past the end
+        st_vec16(sK + r * LDK + cg * VE, fv);
+        if (p.asym) {
+          unpack16(rkt[it], fv, T{});
+          const float keep = (s0 + r < p.N) ? 1.f : 0.f;
+#pragma unroll
+          for (int e = 0; e < VE; ++e) fv[e] *= keep;
+          st_vec16(sKt + r * LDK + cg * VE, fv);
+        }
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < TIT; ++it) {
+      const int idx = tid + it * kThreads;
+      const int r = idx / TPRC, cg = idx % TPRC;
+      if (TV % kThreads == 0 || idx < TV) st16(sT + r * LDC + cg * VE, rt[it]);
+    }
+#pragma unroll
+    for (int it = 0; it < QIT; ++it) {
+      const int idx = tid + it * kThreads;
+      const int i = idx / TPR, cg = idx % TPR;
+      if (QV % kThreads == 0 || idx < QV) {
+        float fv[VE];
+        unpack16(rq[it], fv, T{});
+        const float keep = toks[i] >= 0 ? 1.f : 0.f;
+#pragma unroll
+        for (int e = 0; e < VE; ++e) fv[e] *= keep;
+        st_vec16(sQ + i * LDK + cg * VE, fv);
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < VIT; ++it) {
+      const int idx = tid + it * kThreads;
+      const int r = idx / BVV, cv = idx % BVV;
+      if (VV % kThreads == 0 || idx < VV) {
+        float fv[VE];
+        unpack16(rvv[it], fv, T{});
+        const float keep = (s0 + r < p.N) ? 1.f : 0.f;
+#pragma unroll
+        for (int e = 0; e < VE; e += 4)
+          st4(sV + r * LDV + cv * VE + e, fv[e] * keep, fv[e + 1] * keep, fv[e + 2] * keep,
+              fv[e + 3] * keep);
+      }
+    }
+    if (tid < C) {
+      sG[tid] = rg;
+      sEG[tid] = expf(rg);
+    }
+    if (tid < RT) sLoc[tid] = toks[tid] >= 0 ? (s0 + (n_h - 1 - (s0 - fastdiv(s0, p.nh_magic, p.nh_shift) * n_h)) + tid * n_h) - s0 : -1;
+    if (c + 1 < nc) index_chunk(c + 1);
+  };
 
   // state H (dk x BV, fp32) in accumulators: wave owns tiles wave + 4u
   f32x4_t hacc[HPW];
@@ -292,99 +494,51 @@ __global__ __launch_bounds__(kThreads) void dp_scan_kernel(FwdArgs p) {
     }
   }
 
-  for (int c = 0; c < p.nc; ++c) {
+  if (nc > 0) {
+    index_chunk(0);
+    block_sync_lds();
+    prefetch(0);
+  }
+  for (int c = 0; c < nc; ++c) {
     const int s0 = c * C;
-    const long long chunk = (long long)bh * p.nc + c;
-    __syncthreads();  // the previous chunk is done with every tile below
+    block_sync_lds();  // the previous chunk is done with every tile below
+    commit(c);
+    block_sync_lds();
+    if (c + 1 < nc) prefetch(c + 1);
 
-    // ---- loads: key rows, T diag(beta), scalars, readout queries, values
-    for (int idx = tid; idx < C * TPR; idx += kThreads) {
-      const int r = idx / TPR, cg = idx % TPR;
-      const int s = s0 + r;
-      u32x4_t val = {0u, 0u, 0u, 0u}, valt = {0u, 0u, 0u, 0u};
-      if (s < p.N) {
-        const long long off = sub_row(s, n_h, b, h, p.L, p.H) * DK + cg * VE;
-        val = ld16(kp + off);
-        if (p.asym) valt = ld16(ktp + off);
-      }
-      st16(sK + r * LDK + cg * VE, val);
-      if (p.asym) st16(sKt + r * LDK + cg * VE, valt);
-    }
-    for (int idx = tid; idx < C * TPRC; idx += kThreads) {
-      const int r = idx / TPRC, cg = idx % TPRC;
-      st16(sT + r * LDC + cg * VE, ld16(wsT + chunk * C * C + r * C + cg * VE));
-    }
-    if (tid < C) {
-      const float2 sc = p.wsS[chunk * C + tid];
-      sR[tid] = sc.x;
-      sG[tid] = sc.y;
-    }
-    // readout rows: sub-steps r0 + i*n_h (r0 = first s >= s0 with s % n_h == n_h-1)
-    const int r0 = s0 + (n_h - 1 - s0 % n_h);
-    if (tid < RT) {
-      const int s = r0 + tid * n_h;
-      sLoc[tid] = (s < s0 + C && s < p.N) ? s - s0 : -1;
-    }
-    for (int idx = tid; idx < RT * TPR; idx += kThreads) {
-      const int i = idx / TPR, cg = idx % TPR;
-      const int s = r0 + i * n_h;
-      u32x4_t val = {0u, 0u, 0u, 0u};
-      if (s < s0 + C && s < p.N) {
-        const int t = s / n_h;
-        val = ld16(qp + (((long long)b * p.L + t) * p.H + h) * DK + cg * VE);
-      }
-      st16(sQ + i * LDK + cg * VE, val);
-    }
-    float vreg[YPW][4];
-#pragma unroll
-    for (int u = 0; u < YPW; ++u) {
-      const int tile = wave + 4 * u;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) vreg[u][e] = 0.f;
-      if (tile < NYT) {
-        const int ct = tile / NVT, nt = tile % NVT;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int s = s0 + ct * 16 + 4 * grp + e;
-          if (s < p.N) vreg[u][e] = to_f32(vp[sub_row(s, n_h, b, h, p.L, p.H) * p.dv + v0 + nt * 16 + col]);
-        }
-      }
-    }
-    __syncthreads();
-
-    // ---- phase 1: X = V - diag(rinv e^G) (K H0);  P^T = Kw Q^T (masked);  Z = Q H0
+    // ---- phase 1: X = V - diag(e^G) (Kn H0);  P^T = Kw Q^T (masked, gated);  Z = Q H0
+    if (tid < C) sEL[tid] = expf(sG[C - 1] - sG[tid]);
 #pragma unroll
     for (int u = 0; u < YPW; ++u) {
       const int tile = wave + 4 * u;
       if (tile < NYT) {
         const int ct = tile / NVT, nt = tile % NVT;
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mm_tile<T, DK>(acc, sK, LDK, ct * 16, sHt, LDK, nt * 16);
+        acc = mm_tile<OT, DK>(acc, sK, LDK, ct * 16, sHt, LDK, nt * 16);
+        const int r0 = ct * 16 + 4 * grp;
         float x[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = ct * 16 + 4 * grp + e;
-          x[e] = vreg[u][e] - sR[i] * expf(sG[i]) * acc[e];
-        }
-        st4(sXt + (nt * 16 + col) * LDC + ct * 16 + 4 * grp, x[0], x[1], x[2], x[3]);
+        for (int e = 0; e < 4; ++e) x[e] = sV[(r0 + e) * LDV + nt * 16 + col] - sEG[r0 + e] * acc[e];
+        st4(sXt + (nt * 16 + col) * LDC + r0, x[0], x[1], x[2], x[3]);
       }
     }
-    for (int tile = wave; tile < NCT * NRT; tile += 4) {
-      const int jt = tile / NRT, it = tile % NRT;
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mm_tile<T, DK>(acc, sKw, LDK, jt * 16, sQ, LDK, it * 16);
-      const int i = it * 16 + col;
-      const int loc = sLoc[i];
-      float pv[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = jt * 16 + 4 * grp + e;
-        const float rw = p.asym ? 1.f : sR[j];
-        pv[e] = (loc >= 0 && j <= loc) ? acc[e] * rw * expf(sG[loc] - sG[j]) : 0.f;
+    for (int u = 0; u < PPW; ++u) {
+      const int tile = wave + 4 * u;
+      if (tile < NPT) {
+        const int jt = tile / NRT, it = tile % NRT;
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mm_tile<OT, DK>(acc, sKw, LDK, jt * 16, sQ, LDK, it * 16);
+        const int i = it * 16 + col;
+        const int loc = sLoc[i];
+        const float gl = loc >= 0 ? sG[loc] : 0.f;
+        const int j0 = jt * 16 + 4 * grp;
+        float pv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pv[e] = (j0 + e <= loc) ? acc[e] * expf(gl - sG[j0 + e]) : 0.f;
+        st4(sP + i * LDC + j0, pv[0], pv[1], pv[2], pv[3]);
       }
-      st4(sP + i * LDC + jt * 16 + 4 * grp, pv[0], pv[1], pv[2], pv[3]);
     }
-    const int NZT = NRT * NVT;
     f32x4_t zacc[ZPW];
 #pragma unroll
     for (int u = 0; u < ZPW; ++u) {
@@ -392,38 +546,32 @@ __global__ __launch_bounds__(kThreads) void dp_scan_kernel(FwdArgs p) {
       const int tile = wave + 4 * u;
       if (tile < NZT) {
         const int it = tile / NVT, nt = tile % NVT;
-        zacc[u] = mm_tile<T, DK>(zacc[u], sQ, LDK, it * 16, sHt, LDK, nt * 16);
+        zacc[u] = mm_tile<OT, DK>(zacc[u], sQ, LDK, it * 16, sHt, LDK, nt * 16);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int loc = sLoc[it * 16 + 4 * grp + e];
-          zacc[u][e] *= (loc >= 0) ? expf(sG[loc]) : 0.f;
+          zacc[u][e] *= (loc >= 0) ? sEG[loc] : 0.f;
         }
       }
     }
-    __syncthreads();
+    block_sync_lds();
 
     // ---- phase 2: Up = (T diag(beta)) X ; copies for the readout and the update
-    const float Glast = sG[C - 1];
 #pragma unroll
     for (int u = 0; u < YPW; ++u) {
       const int tile = wave + 4 * u;
       if (tile < NYT) {
         const int ct = tile / NVT, nt = tile % NVT;
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mm_tile<T, C>(acc, sT, LDC, ct * 16, sXt, LDC, nt * 16);
+        acc = mm_tile<OT, C>(acc, sT, LDC, ct * 16, sXt, LDC, nt * 16);
         const int rowoff = (nt * 16 + col) * LDC + ct * 16 + 4 * grp;
         st4(sUo + rowoff, acc[0], acc[1], acc[2], acc[3]);
-        float us[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = ct * 16 + 4 * grp + e;
-          const float rw = p.asym ? 1.f : sR[j];
-          us[e] = acc[e] * rw * expf(Glast - sG[j]);
-        }
-        st4(sUs + rowoff, us[0], us[1], us[2], us[3]);
+        const int j0 = ct * 16 + 4 * grp;
+        st4(sUs + rowoff, acc[0] * sEL[j0], acc[1] * sEL[j0 + 1], acc[2] * sEL[j0 + 2],
+            acc[3] * sEL[j0 + 3]);
       }
     }
-    __syncthreads();
+    block_sync_lds();
 
     // ---- phase 3: O = Z + P Up (written out);  H = e^{G_last} H + Kw^T Us
 #pragma unroll
@@ -431,18 +579,22 @@ __global__ __launch_bounds__(kThreads) void dp_scan_kernel(FwdArgs p) {
       const int tile = wave + 4 * u;
       if (tile < NZT) {
         const int it = tile / NVT, nt = tile % NVT;
-        zacc[u] = mm_tile<T, C>(zacc[u], sP, LDC, it * 16, sUo, LDC, nt * 16);
+        zacc[u] = mm_tile<OT, C>(zacc[u], sP, LDC, it * 16, sUo, LDC, nt * 16);
+        const long long* toks = sTok + (c & 1) * RT;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int loc = sLoc[it * 16 + 4 * grp + e];
-          if (loc >= 0) {
-            const int t = (s0 + loc) / n_h;
-            op[(((long long)b * p.L + t) * p.H + h) * p.dv + v0 + nt * 16 + col] = from_f32<T>(zacc[u][e]);
+          const long long tk = toks[it * 16 + 4 * grp + e];
+          if (tk >= 0) {
+            const long long o = tk * p.dv + v0 + nt * 16 + col;
+            if (p.out_f32)
+              static_cast<float*>(p.out)[o] = zacc[u][e];
+            else
+              static_cast<T*>(p.out)[o] = from_f32<T>(zacc[u][e]);
           }
         }
       }
     }
-    const float dec = expf(Glast);
+    const float dec = sEG[C - 1];
 #pragma unroll
     for (int u = 0; u < HPW; ++u) {
       const int tile = wave + 4 * u;
@@ -450,11 +602,12 @@ __global__ __launch_bounds__(kThreads) void dp_scan_kernel(FwdArgs p) {
         const int dt = tile / NVT, nt = tile % NVT;
 #pragma unroll
         for (int e = 0; e < 4; ++e) hacc[u][e] *= dec;
-        hacc[u] = mm_tile_ta<T, C>(hacc[u], sKw, LDK, dt * 16, sUs, LDC, nt * 16);
+        hacc[u] = mm_tile_ta<OT, C>(hacc[u], sKw, LDK, dt * 16, sUs, LDC, nt * 16);
         st4(sHt + (nt * 16 + col) * LDK + dt * 16 + 4 * grp, hacc[u][0], hacc[u][1], hacc[u][2],
             hacc[u][3]);
       }
     }
+    (void)s0;
   }
 
   if (p.fstate != nullptr) {
@@ -584,32 +737,45 @@ hipError_t launch_ut(const FwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <typename T, int DK, int C, int BV>
+template <typename T, int DK, int C, int BV, int NRT>
 hipError_t launch_scan(const FwdArgs& a, int lds, hipStream_t st) {
-  static const bool attr = allow_big_lds(reinterpret_cast<const void*>(&dp_scan_kernel<T, DK, C, BV>));
+  static const bool attr =
+      allow_big_lds(reinterpret_cast<const void*>(&dp_scan_kernel<T, DK, C, BV, NRT>));
   (void)attr;
   const long long nwg = (long long)a.B * a.H * a.nvb;
-  hipLaunchKernelGGL((dp_scan_kernel<T, DK, C, BV>), dim3((unsigned)nwg), dim3(kThreads), lds, st, a);
+  hipLaunchKernelGGL((dp_scan_kernel<T, DK, C, BV, NRT>), dim3((unsigned)nwg), dim3(kThreads), lds,
+                     st, a);
   return hipGetLastError();
+}
+
+template <typename T, int DK, int C, int BV>
+hipError_t launch_scan_nrt(const FwdArgs& a, int lds, hipStream_t st) {
+  switch (a.RT / 16) {
+    case 1: return launch_scan<T, DK, C, BV, 1>(a, lds, st);
+    case 2: if constexpr (C >= 32) return launch_scan<T, DK, C, BV, 2>(a, lds, st); break;
+    case 3: if constexpr (C >= 64) return launch_scan<T, DK, C, BV, 3>(a, lds, st); break;
+    case 4: if constexpr (C >= 64) return launch_scan<T, DK, C, BV, 4>(a, lds, st); break;
+  }
+  return hipErrorInvalidValue;
 }
 
 template <typename T, int DK>
 hipError_t launch_fwd_dk(const FwdArgs& a, int C, int BV, int lds_scan, int stages, hipStream_t st) {
   hipError_t e = hipSuccess;
-#define DP_CASE_C(CC)                                                         \
-  case CC:                                                                    \
-    if (stages & 1) {                                                         \
-      e = launch_ut<T, DK, CC>(a, st);                                        \
-      if (e != hipSuccess) return e;                                          \
-    }                                                                         \
-    if (stages & 2) {                                                         \
-      switch (BV) {                                                           \
-        case 16: e = launch_scan<T, DK, CC, 16>(a, lds_scan, st); break;      \
-        case 32: e = launch_scan<T, DK, CC, 32>(a, lds_scan, st); break;      \
-        case 64: e = launch_scan<T, DK, CC, 64>(a, lds_scan, st); break;      \
-        default: return hipErrorInvalidValue;                                 \
-      }                                                                       \
-    }                                                                         \
+#define DP_CASE_C(CC)                                                          \
+  case CC:                                                                     \
+    if (stages & 1) {                                                          \
+      e = launch_ut<T, DK, CC>(a, st);                                         \
+      if (e != hipSuccess) return e;                                           \
+    }                                                                          \
+    if (stages & 2) {                                                          \
+      switch (BV) {                                                            \
+        case 16: e = launch_scan_nrt<T, DK, CC, 16>(a, lds_scan, st); break;   \
+        case 32: e = launch_scan_nrt<T, DK, CC, 32>(a, lds_scan, st); break;   \
+        case 64: e = launch_scan_nrt<T, DK, CC, 64>(a, lds_scan, st); break;   \
+        default: return hipErrorInvalidValue;                                  \
+      }                                                                        \
+    }                                                                          \
     return e;
   switch (C) {
     DP_CASE_C(16)

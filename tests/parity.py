@@ -37,13 +37,14 @@ def to_dev(inp, device="cuda"):
     return {k: (v.to(device) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
 
 
-def gpu_forward(inp, chunk=None, kt=None, h0="input", stream=None):
+def gpu_forward(inp, chunk=None, kt=None, h0="input", stream=None, out_dtype="input"):
     """Run dp.fwd on the GPU copies of `inp`; returns (out, final_state) on the device."""
     d = to_dev(inp)
     h0t = d["h0"] if h0 == "input" else h0
     ktt = None if kt is None else kt.to("cuda")
+    odt = inp.get("out_dtype") if out_dtype == "input" else out_dtype
     out, fs = dp.fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], chunk=chunk or inp["chunk"],
-                     h0=h0t, kt=ktt, stream=stream)
+                     h0=h0t, kt=ktt, stream=stream, out_dtype=odt)
     torch.cuda.synchronize()
     return out, fs
 

@@ -94,7 +94,7 @@ FAKE = 1 << 20  # a 256-aligned non-null address; validation fails before any us
 def fwd_call(lib, suffix="bf16", q=FAKE, k=FAKE, v=FAKE, beta=FAKE, g=None, n_h=2, B=1, H=1,
              L=8, dk=16, dv=16, chunk=16, out=FAKE, fs=None, h0=None, wsp=FAKE, wsb=1 << 30,
              kt=None, stages=3):
-    fn = getattr(lib, f"dp_fwd_staged_{suffix}")
+    fn = getattr(lib, f"dp_fwd_ex_{suffix}")
     return fn(q, k, kt, v, beta, g, n_h, B, H, L, dk, dv, chunk, out, fs, h0, wsp, wsb, stages,
               None)
 
@@ -116,7 +116,8 @@ def test_fwd_validation_errors_before_hip(lib, suffix):
     assert fwd_call(lib, suffix, chunk=8) == E.DP_ENOTSUP
     assert fwd_call(lib, suffix, n_h=100) == E.DP_ENOTSUP
     assert fwd_call(lib, suffix, stages=0) == E.DP_EINVAL
-    assert fwd_call(lib, suffix, stages=4) == E.DP_EINVAL
+    assert fwd_call(lib, suffix, stages=4) == E.DP_EINVAL            # no stage bit
+    assert fwd_call(lib, suffix, stages=8 | 3) == E.DP_EINVAL        # unknown flag
     assert fwd_call(lib, suffix, wsb=16) == E.DP_EWORKSPACE           # too small
     assert fwd_call(lib, suffix, wsp=None) == E.DP_EWORKSPACE         # missing
     assert fwd_call(lib, suffix, wsp=FAKE + 16) == E.DP_EWORKSPACE    # misaligned

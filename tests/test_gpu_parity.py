@@ -144,7 +144,7 @@ def test_resume_split_equals_single_call(dtype):
     # in-place resume: h0 and final_state may be the same buffer
     st = f1.clone()
     o2b, _ = dp.fwd(*(second[k].cuda() for k in ("q", "k", "v", "beta")), second["g"].cuda(),
-                    chunk=w.chunk, h0=st, final_state=st)
+                    chunk=w.chunk, h0=st, final_state=st, out_dtype=second["out_dtype"])
     torch.cuda.synchronize()
     assert torch.equal(o2b, o2) and torch.equal(st, f2)
 
@@ -163,6 +163,17 @@ def test_staged_equals_single_launch_and_is_deterministic(dtype):
     torch.cuda.synchronize()
     assert torch.equal(o_all, o_all2) and torch.equal(f_all, f_all2)
     assert torch.equal(o_all, o_st) and torch.equal(f_all, f_st)
+
+
+def test_out_f32_flag_is_the_unrounded_output():
+    """DP_OUT_F32 writes the same values the bf16 output rounds (to nearest even)."""
+    w = WORKLOADS["c3"].scaled(B=2, H=2, L=200)
+    inp = make(w)
+    o16, f16 = gpu_forward(inp, out_dtype=torch.bfloat16)
+    o32, f32 = gpu_forward(inp, out_dtype=torch.float32)
+    assert o16.dtype == torch.bfloat16 and o32.dtype == torch.float32
+    assert torch.equal(o32.to(torch.bfloat16), o16)
+    assert torch.equal(f16, f32)
 
 
 # ------------------------------------------------------------------ exact constructions (fp32 path)
