@@ -132,8 +132,38 @@ int pick_bv(int BH, int dv) {
   return 16;
 }
 
+// Value columns per workgroup of the bf16 scan (16 per wavefront, 1, 2 or 4
+// wavefronts): the widest that still gives at least one workgroup per CU
+// (256 CUs), else one wavefront.  DP_SCAN_NW overrides it (1, 2 or 4).
+int pick_bv16(int BH, int dv) {
+  const char* env = getenv("DP_SCAN_NW");
+  if (env != nullptr) {
+    const int nw = atoi(env);
+    if ((nw == 1 || nw == 2 || nw == 4) && 16 * nw <= dv) return 16 * nw;
+  }
+  for (int nw = 4; nw >= 1; nw >>= 1) {
+    if (16 * nw > dv) continue;
+    if ((long long)BH * (dv / (16 * nw)) >= 256) return 16 * nw;
+  }
+  return 16;
+}
+
 // Choose BV and fill the scan layout of `a` (a.RT and a.asym must be set).
 int plan(dp::FwdArgs& a, int elem, int dk, int chunk, int* BV_out, int* lds_out) {
+  if (elem == 2) {
+    int BV = pick_bv16(a.B * a.H, a.dv);
+    dp::Scan16Layout L = dp::scan16_layout(dk, chunk, BV, a.RT, a.asym);
+    while (L.total > kMaxLds && BV > 16) {  // fewer value columns, smaller buffers
+      BV >>= 1;
+      L = dp::scan16_layout(dk, chunk, BV, a.RT, a.asym);
+    }
+    if (L.total > kMaxLds) return DP_ENOTSUP;
+    if (ut_lds(elem, dk, chunk, a.asym) > kMaxLds) return DP_ENOTSUP;
+    a.nvb = a.dv / BV;
+    *BV_out = BV;
+    *lds_out = L.total;
+    return DP_OK;
+  }
   int BV = pick_bv(a.B * a.H, a.dv);
   int lds = 0;
   for (;; BV >>= 1) {

@@ -281,6 +281,76 @@ __device__ __forceinline__ f32x4_t mm_tile_tb(f32x4_t acc, const T* a, int lda, 
   return acc;
 }
 
+// ------------------------------------------------------------ fp16 register-operand MFMA
+//
+// The register-resident scan keeps its B operands (state, X, pseudo-values) in
+// accumulator layout: lane (g = l >> 4, n = l & 15) of a 16x16 tile holds rows
+// 4g..4g+3 of column n.  A 32-deep step over two such tiles t, t+1 uses, for
+// lane group g, the k set {16t + 4g + e} U {16t + 16 + 4g + e} (e = 0..3), so
+// B comes straight from the two tiles and A is read with the same k set.
+
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+__device__ __forceinline__ f16x4_t to_h4(const f32x4_t& t) { return __builtin_convertvector(t, f16x4_t); }
+__device__ __forceinline__ f16x8_t cat8(const f16x4_t& a, const f16x4_t& b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ f32x4_t mfma32h(const f16x8_t& a, const f16x8_t& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma16h(const f16x4_t& a, const f16x4_t& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+// A rows straight from LDS: row `row`, k set of the step starting at k0.
+__device__ __forceinline__ f16x8_t lds_a32(const f16_t* base, int ld, int row, int k0) {
+  const f16_t* p = base + row * ld + k0 + 4 * ((threadIdx.x >> 4) & 3);
+  return cat8(*reinterpret_cast<const f16x4_t*>(p), *reinterpret_cast<const f16x4_t*>(p + 16));
+}
+__device__ __forceinline__ f16x4_t lds_a16(const f16_t* base, int ld, int row, int k0) {
+  return *reinterpret_cast<const f16x4_t*>(base + row * ld + k0 + 4 * ((threadIdx.x >> 4) & 3));
+}
+// A = transpose of a row-major LDS tile: element (m, k) = base[k * ld + d0 + m],
+// k set {j0 + 4g + e}, via ds_read_b64_tr_b16: in each 16-lane group, source
+// lane i (e = i / 4, a = i % 4) points at base[(j0 + 4g + e) * ld + d0 + 4a];
+// output lane m then receives element (m, j0 + 4g + e) for e = 0..3.
+__device__ __forceinline__ f16x4_t lds_t16(const f16_t* base, int ld, int d0, int j0) {
+  const int l = threadIdx.x & 63, i = l & 15, g = l >> 4;
+  const f16_t* p = base + (j0 + 4 * g + (i >> 2)) * ld + d0 + 4 * (i & 3);
+  return __builtin_bit_cast(f16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p));
+}
+
+// acc += A (16 x K: LDS rows `row`) * B (K x 16: register tiles b[0..K/16))
+template <int K>
+__device__ __forceinline__ f32x4_t mm_ar(f32x4_t acc, const f16_t* a, int lda, int row, const f16x4_t* b) {
+  static_assert(K % 16 == 0, "K");
+#pragma unroll
+  for (int t = 0; t + 1 < K / 16; t += 2) acc = mfma32h(lds_a32(a, lda, row, 16 * t), cat8(b[t], b[t + 1]), acc);
+  if constexpr ((K / 16) % 2 == 1) acc = mfma16h(lds_a16(a, lda, row, K - 16), b[K / 16 - 1], acc);
+  return acc;
+}
+// acc += A (16 x K: transpose of LDS rows, element (m,k) = a[k * lda + d0 + m]) * B (register tiles)
+template <int K>
+__device__ __forceinline__ f32x4_t mm_atr(f32x4_t acc, const f16_t* a, int lda, int d0, const f16x4_t* b) {
+  static_assert(K % 16 == 0, "K");
+#pragma unroll
+  for (int t = 0; t + 1 < K / 16; t += 2)
+    acc = mfma32h(cat8(lds_t16(a, lda, d0, 16 * t), lds_t16(a, lda, d0, 16 * t + 16)), cat8(b[t], b[t + 1]),
+                  acc);
+  if constexpr ((K / 16) % 2 == 1) acc = mfma16h(lds_t16(a, lda, d0, K - 16), b[K / 16 - 1], acc);
+  return acc;
+}
+// acc += A (LDS rows ra) * B (LDS rows rb, the "row by k" buffer of B^T)
+template <int K>
+__device__ __forceinline__ f32x4_t mm_ll(f32x4_t acc, const f16_t* a, int lda, int ra, const f16_t* b, int ldb,
+                                         int rb) {
+  static_assert(K % 16 == 0, "K");
+#pragma unroll
+  for (int t = 0; t + 1 < K / 16; t += 2)
+    acc = mfma32h(lds_a32(a, lda, ra, 16 * t), lds_a32(b, ldb, rb, 16 * t), acc);
+  if constexpr ((K / 16) % 2 == 1) acc = mfma16h(lds_a16(a, lda, ra, K - 16), lds_a16(b, ldb, rb, K - 16), acc);
+  return acc;
+}
+
 // ------------------------------------------------------------ lane reductions
 
 // Sum over aligned groups of W consecutive lanes (W a power of two <= 64).

@@ -625,6 +625,368 @@ __global__ __launch_bounds__(kThreads) void dp_scan_kernel(FwdArgs p) {
 }
 
 // ---------------------------------------------------------------------------
+// dp_scan16_kernel: warp-specialised, register-resident chunk scan of the
+// bf16 path.
+//
+// A workgroup takes one head and 16*NWC value columns with NWC consumer and
+// NWP producer wavefronts.
+//  * Each consumer owns 16 value columns and keeps, in accumulator registers,
+//    its slice of the fp32 state H (dk x 16) and, per chunk, X, Up and the
+//    readout tiles.  Those are the B operands of all of its products (fp16,
+//    see mm_ar / mm_atr), so the chain  H -> X = V - e^G Kn H ->
+//    Up = (T diag(beta)) X -> H' = e^{G_last} H + Kw^T (e^{G_last - G} Up)
+//    has no LDS traffic of its own.
+//  * Producers load chunk c+1 from HBM, normalise the keys, convert keys,
+//    queries and values to fp16, commit them with T diag(beta) and the gate
+//    scales to the other LDS buffer and compute the chunk's masked scores
+//    P = (Q Kw^T) o E, while the consumers work on chunk c.  Keys are
+//    normalised before they become fp16 operands (scaling an fp16 operand
+//    by 1/|k| instead could overflow for tiny keys).
+//  * Consumers read their value columns with one transposed LDS read per
+//    16 rows, which lands them directly in accumulator layout.
+// Two LDS buffers, two barriers per chunk:
+//   X(c) | producers: commit(c+1)     | consumers: X, Up, Q H   of chunk c
+//   Y(c) | producers: scores(c+1)     | consumers: P Up, state  of chunk c
+// LDS layout of one buffer (byte offsets).
+struct Scan16Layout {
+  int K, Kt, T, Q, P, V, G, EG, EL, Loc, Tok, buf, total;
+};
+
+__host__ __device__ constexpr Scan16Layout scan16_layout(int DK, int C, int BV, int RT, int asym) {
+  Scan16Layout L{};
+  int off = 0;
+  L.K = off;   off += align16(C * (DK + 8) * 2);
+  L.Kt = off;  off += asym ? align16(C * (DK + 8) * 2) : 0;
+  L.T = off;   off += align16(C * (C + 8) * 2);
+  L.Q = off;   off += align16(RT * (DK + 8) * 2);
+  L.P = off;   off += align16(RT * (C + 8) * 2);
+  L.V = off;   off += align16(C * (BV + 8) * 2);
+  L.G = off;   off += align16(C * 4);
+  L.EG = off;  off += align16(C * 4);
+  L.EL = off;  off += align16(C * 4);
+  L.Loc = off; off += align16(RT * 4);
+  L.Tok = off; off += align16(RT * 8);
+  L.buf = off;
+  L.total = 2 * off;
+  if (!asym) L.Kt = L.K;
+  return L;
+}
+
+template <int DK, int C, int NWC, int NWP, int NRT, bool ASYM>
+__global__ __launch_bounds__(64 * (NWC + NWP)) void dp_scan16_kernel(FwdArgs p) {
+  using T = bf16_t;
+  constexpr int NPR = 64 * NWP;  // producer threads
+  constexpr int BV = 16 * NWC;
+  constexpr int VE = 8;
+  constexpr int LDK = DK + 8, LDC = C + 8;
+  constexpr int RT = 16 * NRT;
+  constexpr int NCT = C / 16, NDT = DK / 16;
+  constexpr int LDV = BV + 8;
+  constexpr int TPR = DK / VE, TPRC = C / VE, BVV = BV / VE;
+  constexpr int KV = C * TPR, KIT = (KV + NPR - 1) / NPR;
+  constexpr int QV = RT * TPR, QIT = (QV + NPR - 1) / NPR;
+  constexpr int TV = C * TPRC, TIT = (TV + NPR - 1) / NPR;
+  constexpr int VV = C * BVV, VIT = (VV + NPR - 1) / NPR;
+  constexpr int NPT = NCT * NRT, PPW = (NPT + NWP - 1) / NWP;
+  constexpr Scan16Layout Lo = scan16_layout(DK, C, BV, RT, ASYM ? 1 : 0);
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool consumer = wave < NWC;
+  const int col = lane & 15, grp = lane >> 4;
+  // XCD-aware mapping: consecutive workgroup ids go round-robin over the 8
+  // XCDs, so spread ids so that the value blocks of one head share an XCD
+  // (and its L2) for the key / T / query tiles they all read.
+  const int nwg = gridDim.x, bid = blockIdx.x;
+  const int f = (nwg % 8 == 0) ? (bid % 8) * (nwg / 8) + bid / 8 : bid;
+  const int bh = f / p.nvb, vb = f % p.nvb;
+  const int b = bh / p.H, h = bh % p.H;
+  const int v0 = vb * BV;  // first value column of the workgroup
+  const int n_h = p.n_h, nc = p.nc;
+  const long long tok0 = (long long)b * p.L * p.H + h;  // token (b, 0, h)
+  auto first_readout = [&](int s0) { return s0 + (n_h - 1 - (s0 - fastdiv(s0, p.nh_magic, p.nh_shift) * n_h)); };
+  auto buffer = [&](int c) { return smem + (c & 1) * Lo.buf; };
+
+  if (!consumer) {
+    // =================================================================== producers
+    const int ptid = tid - 64 * NWC;
+    const int pw = wave - NWC;
+    const T* kp = static_cast<const T*>(p.k);
+    const T* ktp = static_cast<const T*>(p.kt);
+    const T* qp = static_cast<const T*>(p.q);
+    const T* vp = static_cast<const T*>(p.v) + v0;
+    const f16_t* wsT = static_cast<const f16_t*>(p.wsT) + (long long)bh * nc * C * C;
+    const float2* wsS = p.wsS + (long long)bh * nc * C;
+    auto row_of = [&](int s) -> long long {  // row of sub-step s (row 0 past the end)
+      if (s >= p.N) return 0;
+      const int t = fastdiv(s, p.nh_magic, p.nh_shift);
+      return (tok0 + (long long)t * p.H) * n_h + (s - t * n_h);
+    };
+
+    u32x4_t rk[KIT], rkt[ASYM ? KIT : 1], rq[QIT], rt[TIT], rv[VIT];
+    float rinv[KIT];
+    float rg = 0.f, rgl = 0.f;
+    auto load = [&](int c) {
+      const int s0 = c * C;
+      const float2* ss = wsS + (long long)c * C;
+#pragma unroll
+      for (int it = 0; it < KIT; ++it) {
+        const int idx = (KV % NPR == 0) ? ptid + it * NPR : min(ptid + it * NPR, KV - 1);
+        const int r = idx / TPR, cg = idx % TPR;
+        const long long off = row_of(s0 + r) * DK + cg * VE;
+        rk[it] = ld16(kp + off);
+        if constexpr (ASYM) rkt[it] = ld16(ktp + off);
+        rinv[it] = ss[r].x;  // 0 past the end
+      }
+      const f16_t* tsrc = wsT + (long long)c * C * C;
+#pragma unroll
+      for (int it = 0; it < TIT; ++it) {
+        const int idx = (TV % NPR == 0) ? ptid + it * NPR : min(ptid + it * NPR, TV - 1);
+        rt[it] = ld16(tsrc + idx * VE);
+      }
+      const int r0 = first_readout(s0);
+#pragma unroll
+      for (int it = 0; it < QIT; ++it) {
+        const int idx = (QV % NPR == 0) ? ptid + it * NPR : min(ptid + it * NPR, QV - 1);
+        const int i = idx / TPR, cg = idx % TPR;
+        const int s = r0 + i * n_h;
+        const long long tk =
+            (s < s0 + C && s < p.N) ? tok0 + (long long)fastdiv(s, p.nh_magic, p.nh_shift) * p.H : 0;
+        rq[it] = ld16(qp + tk * DK + cg * VE);
+      }
+#pragma unroll
+      for (int it = 0; it < VIT; ++it) {
+        const int idx = (VV % NPR == 0) ? ptid + it * NPR : min(ptid + it * NPR, VV - 1);
+        const int r = idx / BVV, cv = idx % BVV;
+        rv[it] = ld16(vp + row_of(s0 + r) * p.dv + cv * VE);
+      }
+      rg = ss[min(ptid, C - 1)].y;
+      rgl = ss[C - 1].y;
+    };
+    auto commit = [&](int c) {
+      unsigned char* B = buffer(c);
+      f16_t* sK = reinterpret_cast<f16_t*>(B + Lo.K);
+      f16_t* sKt = reinterpret_cast<f16_t*>(B + Lo.Kt);
+      f16_t* sT = reinterpret_cast<f16_t*>(B + Lo.T);
+      f16_t* sQ = reinterpret_cast<f16_t*>(B + Lo.Q);
+      f16_t* sV = reinterpret_cast<f16_t*>(B + Lo.V);
+      float* sG = reinterpret_cast<float*>(B + Lo.G);
+      float* sEG = reinterpret_cast<float*>(B + Lo.EG);
+      float* sEL = reinterpret_cast<float*>(B + Lo.EL);
+      int* sLoc = reinterpret_cast<int*>(B + Lo.Loc);
+      long long* sTok = reinterpret_cast<long long*>(B + Lo.Tok);
+      const int s0 = c * C;
+      const int r0 = first_readout(s0);
+#pragma unroll
+      for (int it = 0; it < KIT; ++it) {
+        const int idx = ptid + it * NPR;
+        const int r = idx / TPR, cg = idx % TPR;
+        if (KV % NPR == 0 || idx < KV) {
+          // rows past the end hold row 0 of the tensor and 1/|k| = 0; their
+          // beta is 0 too, so their pseudo-values vanish and scores mask them
+          float fv[VE];
+          unpack16(rk[it], fv, T{});
+#pragma unroll
+          for (int e = 0; e < VE; ++e) fv[e] *= rinv[it];
+          st_vec16(sK + r * LDK + cg * VE, fv);
+          if constexpr (ASYM) {
+            unpack16(rkt[it], fv, T{});
+            st_vec16(sKt + r * LDK + cg * VE, fv);
+          }
+        }
+      }
+#pragma unroll
+      for (int it = 0; it < TIT; ++it) {
+        const int idx = ptid + it * NPR;
+        const int r = idx / TPRC, cg = idx % TPRC;
+        if (TV % NPR == 0 || idx < TV) st16(sT + r * LDC + cg * VE, rt[it]);
+      }
+#pragma unroll
+      for (int it = 0; it < QIT; ++it) {
+        const int idx = ptid + it * NPR;
+        const int i = idx / TPR, cg = idx % TPR;
+        if (QV % NPR == 0 || idx < QV) {  // rows of missing readouts are masked later
+          float fv[VE];
+          unpack16(rq[it], fv, T{});
+          st_vec16(sQ + i * LDK + cg * VE, fv);
+        }
+      }
+#pragma unroll
+      for (int it = 0; it < VIT; ++it) {
+        const int idx = ptid + it * NPR;
+        const int r = idx / BVV, cv = idx % BVV;
+        if (VV % NPR == 0 || idx < VV) {
+          const float keep = (s0 + r < p.N) ? 1.f : 0.f;
+          float fv[VE];
+          unpack16(rv[it], fv, T{});
+#pragma unroll
+          for (int e = 0; e < VE; ++e) fv[e] *= keep;
+          st_vec16(sV + r * LDV + cv * VE, fv);
+        }
+      }
+      if (ptid < C) {
+        sG[ptid] = rg;
+        sEG[ptid] = expf(rg);
+        sEL[ptid] = expf(rgl - rg);
+      }
+      if (ptid < RT) {
+        const int s = r0 + ptid * n_h;
+        const bool ok = s < s0 + C && s < p.N;
+        sLoc[ptid] = ok ? s - s0 : -1;
+        sTok[ptid] = ok ? tok0 + (long long)fastdiv(s, p.nh_magic, p.nh_shift) * p.H : -1;
+      }
+    };
+    // masked, gated scores P^T[j][i] = (Kw_j . q_i) e^{G_loc(i) - G_j} for j <= loc(i)
+    auto scores = [&](int c) {
+      unsigned char* B = buffer(c);
+      const f16_t* sKw = reinterpret_cast<const f16_t*>(B + Lo.Kt);
+      const f16_t* sQ = reinterpret_cast<const f16_t*>(B + Lo.Q);
+      f16_t* sP = reinterpret_cast<f16_t*>(B + Lo.P);
+      const float* sG = reinterpret_cast<const float*>(B + Lo.G);
+      const int* sLoc = reinterpret_cast<const int*>(B + Lo.Loc);
+#pragma unroll
+      for (int u = 0; u < PPW; ++u) {
+        const int tile = pw + NWP * u;
+        if (tile < NPT) {
+          const int jt = tile / NRT, it = tile % NRT;
+          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+          acc = mm_ll<DK>(acc, sKw, LDK, jt * 16 + col, sQ, LDK, it * 16 + col);
+          const int i = it * 16 + col;
+          const int loc = sLoc[i];
+          const float gl = loc >= 0 ? sG[loc] : 0.f;
+          const int j0 = jt * 16 + 4 * grp;
+          const f32x4_t g4 = *reinterpret_cast<const f32x4_t*>(sG + j0);
+          float pv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pv[e] = (j0 + e <= loc) ? acc[e] * expf(gl - g4[e]) : 0.f;
+          st4(sP + i * LDC + j0, pv[0], pv[1], pv[2], pv[3]);
+        }
+      }
+    };
+
+    // prologue: chunk 0 committed and scored before the consumers start
+    if (nc > 0) {
+      load(0);
+      commit(0);
+      if (nc > 1) load(1);
+    }
+    block_sync_lds();  // P0
+    if (nc > 0) scores(0);
+    for (int c = 0; c < nc; ++c) {
+      block_sync_lds();  // X(c)
+      if (c + 1 < nc) {
+        commit(c + 1);
+        if (c + 2 < nc) load(c + 2);
+      }
+      block_sync_lds();  // Y(c)
+      if (c + 1 < nc) scores(c + 1);
+    }
+    return;
+  }
+
+  // ===================================================================== consumers
+  const int vw = 16 * wave;  // this wavefront's columns inside the block
+  f32x4_t hacc[NDT];
+  f16x4_t hq[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    hacc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (p.h0 != nullptr) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        hacc[dt][e] = p.h0[((long long)bh * DK + dt * 16 + 4 * grp + e) * p.dv + v0 + vw + col];
+    }
+    hq[dt] = to_h4(hacc[dt]);
+  }
+  block_sync_lds();  // P0
+  for (int c = 0; c < nc; ++c) {
+    unsigned char* B = buffer(c);
+    const f16_t* sK = reinterpret_cast<const f16_t*>(B + Lo.K);
+    const f16_t* sKw = reinterpret_cast<const f16_t*>(B + Lo.Kt);
+    const f16_t* sT = reinterpret_cast<const f16_t*>(B + Lo.T);
+    const f16_t* sQ = reinterpret_cast<const f16_t*>(B + Lo.Q);
+    const f16_t* sP = reinterpret_cast<const f16_t*>(B + Lo.P);
+    const f16_t* sV = reinterpret_cast<const f16_t*>(B + Lo.V);
+    const float* sEG = reinterpret_cast<const float*>(B + Lo.EG);
+    const float* sEL = reinterpret_cast<const float*>(B + Lo.EL);
+    const int* sLoc = reinterpret_cast<const int*>(B + Lo.Loc);
+    const long long* sTok = reinterpret_cast<const long long*>(B + Lo.Tok);
+    block_sync_lds();  // X(c): chunk c's tiles and scores are in LDS
+
+    // ---- X = V - diag(e^G) (Kn H)
+    f16x4_t xq[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mm_ar<DK>(acc, sK, LDK, ct * 16 + col, hq);
+      const f32x4_t eg = *reinterpret_cast<const f32x4_t*>(sEG + ct * 16 + 4 * grp);
+      const f16x4_t v4 = lds_t16(sV, LDV, vw, ct * 16);  // V[16 ct + 4 grp + e][vw + col]
+      f32x4_t x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = (float)v4[e] - eg[e] * acc[e];
+      xq[ct] = to_h4(x);
+    }
+    // ---- Up = (T diag(beta)) X; Us = diag(e^{G_last - G}) Up
+    f16x4_t uq[NCT], usq[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mm_ar<C>(acc, sT, LDC, ct * 16 + col, xq);
+      const f32x4_t el = *reinterpret_cast<const f32x4_t*>(sEL + ct * 16 + 4 * grp);
+      uq[ct] = to_h4(acc);
+      usq[ct] = to_h4(acc * el);
+    }
+    // ---- diag(e^G) Q H for the readout rows
+    f32x4_t z[NRT];
+#pragma unroll
+    for (int it = 0; it < NRT; ++it) {
+      z[it] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      z[it] = mm_ar<DK>(z[it], sQ, LDK, it * 16 + col, hq);
+      const int4 loc4 = *reinterpret_cast<const int4*>(sLoc + it * 16 + 4 * grp);
+      z[it][0] *= loc4.x >= 0 ? sEG[loc4.x] : 0.f;
+      z[it][1] *= loc4.y >= 0 ? sEG[loc4.y] : 0.f;
+      z[it][2] *= loc4.z >= 0 ? sEG[loc4.z] : 0.f;
+      z[it][3] *= loc4.w >= 0 ? sEG[loc4.w] : 0.f;
+    }
+    block_sync_lds();  // Y(c)
+
+    // ---- O = diag(e^G) Q H + P Up, written out
+#pragma unroll
+    for (int it = 0; it < NRT; ++it) {
+      z[it] = mm_ar<C>(z[it], sP, LDC, it * 16 + col, uq);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const long long tk = sTok[it * 16 + 4 * grp + e];
+        if (tk >= 0) {
+          const long long o = tk * p.dv + v0 + vw + col;
+          if (p.out_f32)
+            static_cast<float*>(p.out)[o] = z[it][e];
+          else
+            static_cast<T*>(p.out)[o] = from_f32<T>(z[it][e]);
+        }
+      }
+    }
+    // ---- H = e^{G_last} H + Kw^T Us
+    const float dec = sEG[C - 1];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      hacc[dt] = hacc[dt] * dec;
+      hacc[dt] = mm_atr<C>(hacc[dt], sKw, LDK, dt * 16, usq);
+      hq[dt] = to_h4(hacc[dt]);
+    }
+  }
+
+  if (p.fstate != nullptr) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        p.fstate[((long long)bh * DK + dt * 16 + 4 * grp + e) * p.dv + v0 + vw + col] = hacc[dt][e];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // dp_precond_kernel: OSDN phase 1 (OSDN notes sec. 2.3-2.4, Alg.1).
 // One wavefront holds 4 heads, 16 lanes per head, DK/16 coordinates per lane;
 // each head is a sequential scan over its L tokens.  Tokens are fetched PF at
@@ -759,6 +1121,58 @@ hipError_t launch_scan_nrt(const FwdArgs& a, int lds, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
+// Producer wavefronts per workgroup of dp_scan16_kernel for NWC consumers.
+constexpr int scan16_producers(int nwc) { return nwc >= 2 ? 2 : 1; }
+
+template <int DK, int C, int NWC, int NRT>
+hipError_t launch_scan16(const FwdArgs& a, int lds, hipStream_t st) {
+  constexpr int NWP = scan16_producers(NWC);
+  const long long nwg = (long long)a.B * a.H * a.nvb;
+  if (a.asym) {
+    static const bool attr = allow_big_lds(reinterpret_cast<const void*>(&dp_scan16_kernel<DK, C, NWC, NWP, NRT, true>));
+    (void)attr;
+    hipLaunchKernelGGL((dp_scan16_kernel<DK, C, NWC, NWP, NRT, true>), dim3((unsigned)nwg), dim3(64 * (NWC + NWP)),
+                       lds, st, a);
+  } else {
+    static const bool attr = allow_big_lds(reinterpret_cast<const void*>(&dp_scan16_kernel<DK, C, NWC, NWP, NRT, false>));
+    (void)attr;
+    hipLaunchKernelGGL((dp_scan16_kernel<DK, C, NWC, NWP, NRT, false>), dim3((unsigned)nwg), dim3(64 * (NWC + NWP)),
+                       lds, st, a);
+  }
+  return hipGetLastError();
+}
+
+template <int DK, int C, int NWC>
+hipError_t launch_scan16_nrt(const FwdArgs& a, int lds, hipStream_t st) {
+  switch (a.RT / 16) {
+    case 1: return launch_scan16<DK, C, NWC, 1>(a, lds, st);
+    case 2: if constexpr (C >= 32) return launch_scan16<DK, C, NWC, 2>(a, lds, st); break;
+    case 3: if constexpr (C >= 64) return launch_scan16<DK, C, NWC, 3>(a, lds, st); break;
+    case 4: if constexpr (C >= 64) return launch_scan16<DK, C, NWC, 4>(a, lds, st); break;
+  }
+  return hipErrorInvalidValue;
+}
+
+// Scan launch: the bf16 path uses the register-resident dp_scan16_kernel with
+// BV / 16 wavefronts per workgroup; the fp32 path the LDS-staged dp_scan_kernel.
+template <typename T, int DK, int C>
+hipError_t launch_scan_any(const FwdArgs& a, int BV, int lds, hipStream_t st) {
+  if constexpr (sizeof(T) == 2) {
+    switch (BV) {
+      case 16: return launch_scan16_nrt<DK, C, 1>(a, lds, st);
+      case 32: return launch_scan16_nrt<DK, C, 2>(a, lds, st);
+      case 64: return launch_scan16_nrt<DK, C, 4>(a, lds, st);
+    }
+  } else {
+    switch (BV) {
+      case 16: return launch_scan_nrt<T, DK, C, 16>(a, lds, st);
+      case 32: return launch_scan_nrt<T, DK, C, 32>(a, lds, st);
+      case 64: return launch_scan_nrt<T, DK, C, 64>(a, lds, st);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
 template <typename T, int DK>
 hipError_t launch_fwd_dk(const FwdArgs& a, int C, int BV, int lds_scan, int stages, hipStream_t st) {
   hipError_t e = hipSuccess;
@@ -768,14 +1182,7 @@ hipError_t launch_fwd_dk(const FwdArgs& a, int C, int BV, int lds_scan, int stag
       e = launch_ut<T, DK, CC>(a, st);                                         \
       if (e != hipSuccess) return e;                                           \
     }                                                                          \
-    if (stages & 2) {                                                          \
-      switch (BV) {                                                            \
-        case 16: e = launch_scan_nrt<T, DK, CC, 16>(a, lds_scan, st); break;   \
-        case 32: e = launch_scan_nrt<T, DK, CC, 32>(a, lds_scan, st); break;   \
-        case 64: e = launch_scan_nrt<T, DK, CC, 64>(a, lds_scan, st); break;   \
-        default: return hipErrorInvalidValue;                                  \
-      }                                                                        \
-    }                                                                          \
+    if (stages & 2) e = launch_scan_any<T, DK, CC>(a, BV, lds_scan, st);      \
     return e;
   switch (C) {
     DP_CASE_C(16)
