@@ -41,7 +41,50 @@ def parse():
                     help="comma-separated extra workloads timed in the same run ('' = none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU sample (0: auto)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run device-to-device copies of BYTES (counter calibration)")
     return ap.parse_args()
+
+
+def copy_probe(nbytes):
+    """Device-to-device copies of a known size: what the HBM read / write
+    counters report for them calibrates the counters of the forward's kernels."""
+    import torch
+
+    n = nbytes // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n * 4, "copies": 3}), flush=True)
+
+
+def source_digest():
+    """sha256 over the kernel sources (csrc/*.hip, *.hpp), in name order."""
+    import glob
+    import hashlib
+
+    hsh = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "linear_rnn_sequence_amd", "csrc", "*"))):
+        if f.endswith((".hip", ".hpp")):
+            hsh.update(os.path.basename(f).encode())
+            with open(f, "rb") as fh:
+                hsh.update(fh.read())
+    return hsh.hexdigest()
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` for `workload` from the committed counter
+    summary, or None when there is none or the kernel sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256") != source_digest():
+        return None
+    return rec.get("bytes_per_launch")
 
 
 # ---------------------------------------------------------------- accounting
@@ -217,10 +260,13 @@ def describe(w):
 
 def main():
     a = parse()
+    if a.copy_probe:
+        copy_probe(a.copy_probe)
+        return
     if a.gpus != 1 or os.environ.get("WORLD_SIZE", "1") not in ("1", ""):
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the forward shards over heads with no communication; see the design notes). "
-              "Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: there is no multi-GPU path here (the forward "
+              "shards over heads or value columns with no communication). Run with --gpus 1.",
+              file=sys.stderr)
         sys.exit(2)
     import torch
 
@@ -241,11 +287,12 @@ def main():
     ut_issued, scan_issued = issued_flops(w, r["plan"])
     ab = alg_bytes(w)
     peak_mfma = FP32_PEAK_TFLOPS if w.dtype == "f32" else BF16_PEAK_TFLOPS
+    scan_name = "dp_scan16_kernel" if w.dtype == "bf16" else "dp_scan_kernel"
     kernels = {
         "dp_ut_kernel": {"ms": r["ut_ms"], "issued_tflops": ut_issued / (r["ut_ms"] * 1e9),
                          "workgroups": r["plan"]["ut_wgs"]},
-        "dp_scan_kernel": {"ms": r["scan_ms"], "issued_tflops": scan_issued / (r["scan_ms"] * 1e9),
-                           "workgroups": r["plan"]["scan_wgs"], "BV": r["plan"]["BV"]},
+        scan_name: {"ms": r["scan_ms"], "issued_tflops": scan_issued / (r["scan_ms"] * 1e9),
+                    "workgroups": r["plan"]["scan_wgs"], "value_columns": r["plan"]["BV"]},
     }
     if w.asym:
         kernels["dp_precond_kernel"] = {"ms": r["pre_ms"],
@@ -276,8 +323,8 @@ def main():
         "alg_gbs": ab / (r["ms_per_step"] * 1e6),
         "kernels": kernels,
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "alg_bytes_per_launch": ab},
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(w.name, dom), "alg_bytes_per_launch": ab},
     }
     also = {}
     for name in [x for x in a.also.split(",") if x and x != a.workload]:
