@@ -217,37 +217,73 @@ def time_gpu(w, steps, warmup):
 
 # ---------------------------------------------------------------- CPU baseline
 
-def cpu_baseline(w, inp, nheads):
+def cpu_baseline(w, inp, nheads, min_seconds=10.0, max_pass_seconds=30.0, max_passes=100):
+    """Time the fp64 oracle on this host's cores on the same input bytes.
+
+    The sample is the whole workload (every head, full length) when one pass
+    is estimated to take at most ``max_pass_seconds``; otherwise the largest
+    set of evenly spread heads that fits about half of that.  Passes repeat
+    until ``min_seconds`` of wall time have accumulated; the rate is taken
+    from the median pass.
+    """
+    import statistics
+
+    import numpy as np
+    import torch
+
     import oracle
     from linear_rnn_sequence_amd.inputs import sampled_heads, select_heads, select_state
 
     threads = oracle.num_threads()
-    n = nheads or min(w.B * w.H, max(4, 2 * threads))
-    heads = sampled_heads(w.B, w.H, n)
-    H = w.H
-    sub = {k: (None if inp[k] is None else select_heads(inp[k], heads, H))
-           for k in ("q", "k", "v", "beta", "g")}
-    h0 = None if inp["h0"] is None else select_state(inp["h0"], heads, H)
-    import numpy as np
-    import torch
-    conv = {k: (None if v is None else np.ascontiguousarray(v.to(torch.float64).numpy()))
-            for k, v in sub.items()}
-    h0c = None if h0 is None else np.ascontiguousarray(h0.to(torch.float64).numpy())
-    t0 = time.perf_counter()
-    if w.asym:
-        kt, _ = oracle.precond(conv["k"][:, :, :, 0, :], conv["beta"][..., 0])
-        oracle.fwd(conv["q"], conv["k"], conv["v"], conv["beta"], g=conv["g"],
-                   kt=kt[:, :, :, None, :], h0=h0c)
+    total = w.B * w.H
+
+    def prepare(heads):
+        sub = {k: (None if inp[k] is None else select_heads(inp[k], heads, w.H))
+               for k in ("q", "k", "v", "beta", "g")}
+        conv = {k: (None if v is None else np.ascontiguousarray(v.to(torch.float64).numpy()))
+                for k, v in sub.items()}
+        conv["h0"] = (None if inp["h0"] is None else
+                      np.ascontiguousarray(select_state(inp["h0"], heads, w.H)
+                                           .to(torch.float64).numpy()))
+        return conv
+
+    def one_pass(c):
+        t0 = time.perf_counter()
+        if w.asym:
+            kt, _ = oracle.precond(c["k"][:, :, :, 0, :], c["beta"][..., 0])
+            oracle.fwd(c["q"], c["k"], c["v"], c["beta"], g=c["g"], kt=kt[:, :, :, None, :],
+                       h0=c["h0"])
+        else:
+            oracle.fwd(c["q"], c["k"], c["v"], c["beta"], g=c["g"], h0=c["h0"])
+        return time.perf_counter() - t0
+
+    if nheads:
+        heads = sampled_heads(w.B, w.H, nheads)
     else:
-        oracle.fwd(conv["q"], conv["k"], conv["v"], conv["beta"], g=conv["g"], h0=h0c)
-    t = time.perf_counter() - t0
-    tokens = len(heads) * w.L  # token-heads processed; the workload has B*L tokens x H heads
-    value = tokens / w.H / t   # whole-workload tokens/s at this rate
+        pilot = sampled_heads(w.B, w.H, min(total, threads))
+        t_pilot = one_pass(prepare(pilot))
+        waves = -(-total // threads)
+        if t_pilot * waves <= max_pass_seconds:
+            heads = list(range(total))
+        else:
+            fit = max(1, int(0.5 * max_pass_seconds / max(t_pilot, 1e-9)))
+            heads = sampled_heads(w.B, w.H, min(total, fit * threads))
+    conv = prepare(heads)
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        times.append(one_pass(conv))
+        if time.perf_counter() - t_start >= min_seconds or len(times) >= max_passes:
+            break
+    t = statistics.median(times)
+    value = len(heads) * w.L / w.H / t   # whole-workload tokens/s at this rate
+    what = ("the whole workload" if len(heads) == total
+            else f"{len(heads)} of {total} heads (b,h)")
     return {"value": value, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(heads)} of {w.B * w.H} heads (b,h) of {w.name}, full L={w.L} "
-                      f"(all {w.n_h} sub-steps per token{', phase 1 included' if w.asym else ''}); "
-                      f"fp64 sequential recurrence, {t:.2f}s wall on {threads} threads",
-            "seconds": t}
+            "sample": f"{what} of {w.name}, full L={w.L}, all {w.n_h} sub-steps per token"
+                      f"{', phase 1 included' if w.asym else ''}; fp64 sequential recurrence; "
+                      f"median of {len(times)} passes ({sum(times):.1f}s wall) on {threads} threads",
+            "seconds_per_pass": t}
 
 
 # ---------------------------------------------------------------- main
