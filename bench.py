@@ -138,18 +138,31 @@ def recurrent_flops(w):
     return w.B * w.L * w.H * per_tok
 
 
+def kernel_names(w):
+    """(prep / UT kernel, scan kernel) names of the path a workload runs on."""
+    if w.dtype == "bf16" and not w.asym:
+        return "dp_prep_kernel", "dp_chain_kernel"
+    if w.dtype == "bf16":
+        return "dp_ut_kernel", "dp_scan16_kernel"
+    return "dp_ut_kernel", "dp_scan_kernel"
+
+
 def issued_flops(w, plan):
     """MFMA flops the two kernels actually issue (tile-padded), per forward."""
-    C, dk, BV, RT = w.chunk, w.dk, plan["BV"], plan["readout_rows"]
+    C, dk, dv, BV, RT = w.chunk, w.dk, w.dv, plan["BV"], plan["readout_rows"]
     N = w.L * w.n_h
     nc = -(-N // C)
     NT = C // 16
     ut = (NT * (NT + 1) // 2) * 16 * 16 * dk * 2
     for dist in range(1, NT):  # blocked inverse, fp32
         ut += (NT - dist) * (dist + 1) * 16 * 16 * 16 * 2
-    scan = 2 * (C * BV * dk + C * RT * dk + RT * BV * dk + C * C * BV + RT * C * BV + dk * C * BV)
     heads = w.B * w.H
-    return heads * nc * ut, heads * nc * scan * (w.dv // BV)
+    if kernel_names(w)[0] == "dp_prep_kernel":
+        ut += 2 * RT * C * dk  # scores of the readout rows
+        per16 = 2 * 16 * (C * dk + C * C + RT * dk + RT * C + dk * C)  # per 16 value columns
+        return heads * nc * ut, heads * nc * per16 * (dv // 16)
+    scan = 2 * (C * BV * dk + C * RT * dk + RT * BV * dk + C * C * BV + RT * C * BV + dk * C * BV)
+    return heads * nc * ut, heads * nc * scan * (dv // BV)
 
 
 # ---------------------------------------------------------------- GPU timing
@@ -323,10 +336,10 @@ def main():
     ut_issued, scan_issued = issued_flops(w, r["plan"])
     ab = alg_bytes(w)
     peak_mfma = FP32_PEAK_TFLOPS if w.dtype == "f32" else BF16_PEAK_TFLOPS
-    scan_name = "dp_scan16_kernel" if w.dtype == "bf16" else "dp_scan_kernel"
+    ut_name, scan_name = kernel_names(w)
     kernels = {
-        "dp_ut_kernel": {"ms": r["ut_ms"], "issued_tflops": ut_issued / (r["ut_ms"] * 1e9),
-                         "workgroups": r["plan"]["ut_wgs"]},
+        ut_name: {"ms": r["ut_ms"], "issued_tflops": ut_issued / (r["ut_ms"] * 1e9),
+                  "workgroups": r["plan"]["ut_wgs"]},
         scan_name: {"ms": r["scan_ms"], "issued_tflops": scan_issued / (r["scan_ms"] * 1e9),
                     "workgroups": r["plan"]["scan_wgs"], "value_columns": r["plan"]["BV"]},
     }

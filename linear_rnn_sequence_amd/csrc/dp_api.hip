@@ -56,7 +56,19 @@ size_t ws_t_bytes(const Shape& s, int elem) {
   return align_up((size_t)s.B * s.H * num_chunks(s) * s.chunk * s.chunk * elem, kWsAlign);
 }
 
+// Readout rows a chunk can hold (ceil(C / n_h)), rounded up to MFMA tiles.
+int readout_rows(int C, int n_h) {
+  const int r = (C + n_h - 1) / n_h;
+  return r >= C ? C : ((r + 15) / 16) * 16;
+}
+
+// bf16: one operand block per chunk (dp_prep_kernel's output); it also covers
+// the T / (1/|k|, G) layout the write-key path uses.  fp32: T and (1/|k|, G).
 size_t ws_total(const Shape& s, int elem) {
+  if (elem == 2) {
+    const dp::Chunk16Layout W = dp::chunk16_layout(s.dk, s.chunk, readout_rows(s.chunk, s.n_h));
+    return align_up((size_t)s.B * s.H * num_chunks(s) * W.bytes, kWsAlign);
+  }
   return ws_t_bytes(s, elem) + (size_t)s.B * s.H * num_chunks(s) * s.chunk * sizeof(float2);
 }
 
@@ -74,12 +86,6 @@ void fastdiv_magic(int d, uint32_t* magic, int* shift) {
   const unsigned long long m = ((1ull << sh) + (unsigned long long)d - 1) / (unsigned long long)d;
   *magic = (uint32_t)m;
   *shift = sh;
-}
-
-// Readout rows a chunk can hold (ceil(C / n_h)), rounded up to MFMA tiles.
-int readout_rows(int C, int n_h) {
-  const int r = (C + n_h - 1) / n_h;
-  return r >= C ? C : ((r + 15) / 16) * 16;
 }
 
 // Fill the scan kernel's LDS offsets; returns total bytes.
@@ -150,6 +156,16 @@ int pick_bv16(int BH, int dv) {
 
 // Choose BV and fill the scan layout of `a` (a.RT and a.asym must be set).
 int plan(dp::FwdArgs& a, int elem, int dk, int chunk, int* BV_out, int* lds_out) {
+  if (elem == 2 && !a.asym) {
+    int BV = pick_bv16(a.B * a.H, a.dv);
+    while (dp::chain_lds_bytes(dk, chunk, a.RT, BV) > kMaxLds && BV > 16) BV >>= 1;
+    if (dp::chain_lds_bytes(dk, chunk, a.RT, BV) > kMaxLds) return DP_ENOTSUP;
+    if (dp::prep_lds_bytes(dk, chunk, a.RT) > kMaxLds) return DP_ENOTSUP;
+    a.nvb = a.dv / BV;
+    *BV_out = BV;
+    *lds_out = dp::chain_lds_bytes(dk, chunk, a.RT, BV);
+    return DP_OK;
+  }
   if (elem == 2) {
     int BV = pick_bv16(a.B * a.H, a.dv);
     dp::Scan16Layout L = dp::scan16_layout(dk, chunk, BV, a.RT, a.asym);
@@ -344,7 +360,7 @@ int dp_fwd_launch_info(int n_h, int B, int H, int L, int dk, int dv, int chunk, 
   info[1] = B * H * a.nvb;
   info[2] = B * H * num_chunks(s);
   info[3] = lds;
-  info[4] = ut_lds(elem_bytes, dk, chunk, asym);
+  info[4] = (elem_bytes == 2 && !asym) ? dp::prep_lds_bytes(dk, chunk, a.RT) : ut_lds(elem_bytes, dk, chunk, asym);
   info[5] = a.RT;
   return DP_OK;
 }

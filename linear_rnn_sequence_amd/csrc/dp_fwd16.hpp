@@ -1,0 +1,550 @@
+// dp_fwd16.hpp -- the bf16 forward with symmetric keys: a parallel chunk-prep
+// kernel and a register-resident chunk scan fed by direct-to-LDS copies.
+//
+// Same chunkwise form as the rest of the library (DeltaProduct study notes
+// sec. 2.2 Eq.(3), sec. 2.6 and sec. 4.1; chunkwise WY/UT form of the OSDN
+// study notes sec. 2.5 / App. A.2, with the chunk-local log-gate G):
+//
+//   T  = (I + strict_tril(diag(beta) (E o Kn Kn^T)))^{-1}
+//   Up = (T diag(beta)) (V - diag(e^G) Kn H0)
+//   O  = diag(e^{G_loc}) Q H0 + P Up,   P = (tril_incl(Q Kn^T) o E) on readout rows
+//   H1 = e^{G_last} H0 + Kn^T (diag(e^{G_last - G}) Up)
+//
+// dp_prep_kernel (one workgroup per chunk, all chunks in parallel) computes
+// every operand that does not depend on the state and writes it to the
+// workspace in its final fp16 form:  T diag(beta), the unit keys Kn, the
+// readout queries Q, the masked and decayed scores P, and per-chunk scalars
+// (e^G, e^{G_last - G}, e^{G_loc} and the output offset of each readout row).
+// dp_chain_kernel then only runs the recurrence: NWC consumer wavefronts keep
+// their 16 value columns of the fp32 state in registers, and one copy
+// wavefront streams each chunk's operands (and the values) into a ring of
+// LDS stages with global_load_lds_dwordx4, two chunks ahead.
+//
+// Tile layout ("block-major"): a tile of R rows and W fp16 columns is stored
+// as W/8 blocks of R x 16 bytes (block q holds columns 8q..8q+7 of every row).
+// In LDS, the rows of odd blocks are permuted (row r in slot r ^ 8).  Both
+// operand read patterns of the scan are then free of bank conflicts: a row
+// read (16 rows x 8 bytes of one block per half-wave) touches 256 contiguous
+// bytes, and a transposed read (ds_read_b64_tr_b16: 8 rows x 2 adjacent
+// blocks per half-wave) touches two 128-byte halves of the 64 banks.  Every
+// lane-dependent part of an address is fixed per lane, so all tile offsets
+// are instruction immediates.
+#pragma once
+
+#include "dp_device.hpp"
+
+namespace dp {
+
+// Byte offsets of one chunk's operand block (workspace and LDS stage alike).
+struct Chunk16Layout {
+  int oT, oK, oQ, oP, oS;  // T diag(beta), Kn, readout Q, scores P, scalars
+  int oEG, oEL, oEGL, oOff;  // scalars (relative to oS)
+  int bytes;                 // whole block, a multiple of 16
+};
+
+__host__ __device__ constexpr Chunk16Layout chunk16_layout(int DK, int C, int RT) {
+  Chunk16Layout L{};
+  L.oT = 0;
+  L.oK = L.oT + C * C * 2;
+  L.oQ = L.oK + C * DK * 2;
+  L.oP = L.oQ + RT * DK * 2;
+  L.oS = L.oP + RT * C * 2;
+  L.oEG = 0;
+  L.oEL = 4 * C;
+  L.oEGL = 8 * C;
+  L.oOff = (8 * C + 4 * RT + 7) & ~7;
+  L.bytes = L.oS + ((L.oOff + 8 * RT + 15) & ~15);
+  return L;
+}
+
+// LDS of dp_chain_kernel: kStages copies of (chunk block, value tile).
+constexpr int kChainStages = 3;
+__host__ __device__ constexpr int chain_stage_bytes(int DK, int C, int RT, int BV) {
+  return chunk16_layout(DK, C, RT).bytes + C * BV * 2;
+}
+__host__ __device__ constexpr int chain_lds_bytes(int DK, int C, int RT, int BV) {
+  return kChainStages * chain_stage_bytes(DK, C, RT, BV);
+}
+
+// LDS of dp_prep_kernel: fp16 key and query rows, fp32 M and T, beta / G /
+// scalars, readout locations and the partial-sum tiles of the blocked inverse.
+__host__ __device__ constexpr int prep_lds_bytes(int DK, int C, int RT) {
+  return C * (DK + 8) * 2 + RT * (DK + 8) * 2 + 2 * C * (C + 4) * 4 + 2 * C * 4 + RT * 4 +
+         4 * 16 * 17 * 4;
+}
+
+// ---------------------------------------------------------------------------
+// dp_prep_kernel: one chunk per workgroup.
+template <int DK, int C, int NRT>
+__global__ __launch_bounds__(256) void dp_prep_kernel(FwdArgs p) {
+  constexpr int RT = 16 * NRT;
+  constexpr int TPR = DK / 8;  // 16-byte granules per key row
+  constexpr int LDK = DK + 8, LDA = C + 4;
+  constexpr int NT = C / 16;
+  constexpr int KV = C * TPR, KIT = (KV + 255) / 256;
+  constexpr int QV = RT * TPR, QIT = (QV + 255) / 256;
+  constexpr Chunk16Layout W = chunk16_layout(DK, C, RT);
+  static_assert(TPR <= 64 && 64 % TPR == 0, "row group must fit in a wavefront");
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  f16_t* sK = reinterpret_cast<f16_t*>(smem);
+  f16_t* sQ = sK + C * LDK;
+  float* sA = reinterpret_cast<float*>(sQ + RT * LDK);
+  float* sTf = sA + C * LDA;
+  float* sB = sTf + C * LDA;
+  float* sG = sB + C;
+  int* sLoc = reinterpret_cast<int*>(sG + C);
+  float* sSc = reinterpret_cast<float*>(sLoc + RT);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const long long chunk = blockIdx.x;
+  const int bh = (int)(chunk / p.nc), c = (int)(chunk % p.nc);
+  const int b = bh / p.H, h = bh % p.H;
+  const int s0 = c * C, n_h = p.n_h;
+  const int r0 = s0 + (n_h - 1 - (s0 - fastdiv(s0, p.nh_magic, p.nh_shift) * n_h));  // first readout
+  const long long tok0 = (long long)b * p.L * p.H + h;  // token (b, 0, h)
+  const bf16_t* kp = static_cast<const bf16_t*>(p.k);
+  const bf16_t* qp = static_cast<const bf16_t*>(p.q);
+  unsigned char* wsc = static_cast<unsigned char*>(p.wsT) + chunk * W.bytes;
+
+  // 1. global loads: key rows, readout query rows, beta, gate
+  u32x4_t rk[KIT], rq[QIT];
+#pragma unroll
+  for (int it = 0; it < KIT; ++it) {
+    const int idx = tid + it * 256;
+    const int r = idx / TPR, cg = idx % TPR;
+    const int s = s0 + r;
+    rk[it] = u32x4_t{0u, 0u, 0u, 0u};
+    if (idx < KV && s < p.N) rk[it] = ld16(kp + sub_row(p, s, b, h) * DK + cg * 8);
+  }
+#pragma unroll
+  for (int it = 0; it < QIT; ++it) {
+    const int idx = tid + it * 256;
+    const int i = idx / TPR, cg = idx % TPR;
+    const int s = r0 + i * n_h;
+    rq[it] = u32x4_t{0u, 0u, 0u, 0u};
+    if (idx < QV && s < s0 + C && s < p.N) {
+      const long long tk = tok0 + (long long)fastdiv(s, p.nh_magic, p.nh_shift) * p.H;
+      rq[it] = ld16(qp + tk * DK + cg * 8);
+    }
+  }
+  float braw = 0.f, lam = 0.f;
+  if (tid < C && s0 + tid < p.N) {
+    const int s = s0 + tid;
+    const int t = fastdiv(s, p.nh_magic, p.nh_shift);
+    const int j = s - t * n_h;
+    const long long tok = tok0 + (long long)t * p.H;
+    braw = p.beta[tok * n_h + j];
+    if (p.g != nullptr && j == 0) lam = logf(fmaxf(p.g[tok], FLT_MIN));
+  }
+
+  // 2. unit keys (row norms by a TPR-lane reduction) and queries, as fp16 rows
+#pragma unroll
+  for (int it = 0; it < KIT; ++it) {
+    const int idx = tid + it * 256;
+    const int r = idx / TPR, cg = idx % TPR;
+    float f[8];
+    unpack16(rk[it], f, bf16_t{});
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = fmaf(f[e], f[e], ss);
+    ss = group_sum<TPR>(ss);
+    const float rinv = 1.f / fmaxf(sqrtf(ss), 1e-6f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] *= rinv;
+    if (idx < KV) st_vec16(sK + r * LDK + cg * 8, f);
+  }
+#pragma unroll
+  for (int it = 0; it < QIT; ++it) {
+    const int idx = tid + it * 256;
+    const int i = idx / TPR, cg = idx % TPR;
+    float f[8];
+    unpack16(rq[it], f, bf16_t{});
+    if (idx < QV) st_vec16(sQ + i * LDK + cg * 8, f);
+  }
+
+  // 3. beta range, cumulative log-gate and the per-chunk scalars (wave 0)
+  if (wave == 0) {
+    const float G = wave_inclusive_scan(lam);
+    const float Gl = __shfl(G, C - 1, 64);
+    float* sEG = reinterpret_cast<float*>(wsc + W.oS + W.oEG);
+    float* sEL = reinterpret_cast<float*>(wsc + W.oS + W.oEL);
+    float* sEGL = reinterpret_cast<float*>(wsc + W.oS + W.oEGL);
+    long long* sOff = reinterpret_cast<long long*>(wsc + W.oS + W.oOff);
+    if (lane < C) {
+      sB[lane] = clamp_keep_nan(braw, 0.f, 2.f);
+      sG[lane] = G;
+      sEG[lane] = expf(G);
+      sEL[lane] = expf(Gl - G);
+    }
+    const int s = r0 + lane * n_h;
+    const bool ok = lane < RT && s < s0 + C && s < p.N;
+    const int loc = ok ? s - s0 : 0;
+    const float Gloc = __shfl(G, loc, 64);
+    if (lane < RT) {
+      sLoc[lane] = ok ? loc : -1;
+      sEGL[lane] = ok ? expf(Gloc) : 0.f;
+      sOff[lane] = ok ? (tok0 + (long long)fastdiv(s, p.nh_magic, p.nh_shift) * p.H) * p.dv : -1ll;
+    }
+  }
+  __syncthreads();
+
+  // 4. Kn and Q to the workspace, block-major (16 consecutive rows of a block
+  //    per quarter-wave: contiguous global stores, conflict-free LDS reads)
+  for (int idx = tid; idx < KV; idx += 256) {
+    const int q = idx / C, r = idx % C;
+    st16(wsc + W.oK + (q * C + r) * 16, ld16(sK + r * LDK + q * 8));
+  }
+  for (int idx = tid; idx < QV; idx += 256) {
+    const int q = idx / RT, i = idx % RT;
+    st16(wsc + W.oQ + (q * RT + i) * 16, ld16(sQ + i * LDK + q * 8));
+  }
+
+  // 5. M = strict_tril(diag(beta) (E o Kn Kn^T)) on MFMA (lower tiles only)
+  for (int tile = wave; tile < NT * NT; tile += 4) {
+    const int ti = tile / NT, tj = tile % NT;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    if (tj <= ti) acc = mm_ll<DK>(acc, sK, LDK, ti * 16 + (lane & 15), sK, LDK, tj * 16 + (lane & 15));
+    const int jj = tj * 16 + (lane & 15);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int ii = ti * 16 + 4 * (lane >> 4) + e;
+      float val = 0.f;
+      if (jj < ii) val = sB[ii] * expf(sG[ii] - sG[jj]) * acc[e];
+      sA[ii * LDA + jj] = val;
+    }
+  }
+  // 6. masked, decayed scores of the readout rows:  P[i][j] = (q_i . kn_j)
+  //    e^{G_loc(i) - G_j} for j <= loc(i).  Computed transposed (lane: four
+  //    consecutive j of one i) and stored block-major in 8-byte pieces.
+  for (int tile = wave; tile < NRT * NT; tile += 4) {
+    const int it = tile / NT, jt = tile % NT;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    acc = mm_ll<DK>(acc, sK, LDK, jt * 16 + (lane & 15), sQ, LDK, it * 16 + (lane & 15));
+    const int i = it * 16 + (lane & 15);
+    const int loc = sLoc[i];
+    const int j0 = jt * 16 + 4 * (lane >> 4);
+    const float gl = loc >= 0 ? sG[loc] : 0.f;
+    float pv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = j0 + e;
+      pv[e] = (j <= loc) ? acc[e] * (p.g != nullptr ? expf(gl - sG[j]) : 1.f) : 0.f;
+    }
+    st4(reinterpret_cast<f16_t*>(wsc + W.oP + ((j0 >> 3) * RT + i) * 16 + (j0 & 7) * 2), pv[0], pv[1], pv[2],
+        pv[3]);
+  }
+  __syncthreads();
+
+  // 7. T = (I + M)^{-1} (fp32), blocked over 16 x 16 tiles: diagonal tiles by
+  //    forward substitution (one 16-lane group per tile, one column per
+  //    lane), then the off-diagonal tiles level by level (i - j = 1, 2, ..):
+  //    T_ij = -T_ii sum_{k=j}^{i-1} M_ik T_kj  on fp32 MFMA.
+  if (wave == 0) {
+    const int gb = lane >> 4, cc = lane & 15;
+    if (gb < NT) {
+      float t[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float acc = (i == cc) ? 1.f : 0.f;
+        const float* ar = sA + (gb * 16 + i) * LDA + gb * 16;
+#pragma unroll
+        for (int j = 0; j < i; ++j) acc = fmaf(-ar[j], t[j], acc);
+        t[i] = acc;
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sTf[(gb * 16 + i) * LDA + gb * 16 + cc] = t[i];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int dist = 1; dist < NT; ++dist) {
+    const int j = wave, i = wave + dist;
+    float* sS = sSc + wave * 16 * 17;
+    if (i < NT) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      for (int kb = j; kb < i; ++kb)
+        acc = mm_tile_tb<float, 16>(acc, sA + i * 16 * LDA + kb * 16, LDA, 0, sTf + kb * 16 * LDA + j * 16, LDA, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sS[(4 * (lane >> 4) + e) * 17 + (lane & 15)] = acc[e];
+    }
+    __syncthreads();
+    if (i < NT) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mm_tile_tb<float, 16>(acc, sTf + i * 16 * LDA + i * 16, LDA, 0, sS, 17, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sTf[(i * 16 + 4 * (lane >> 4) + e) * LDA + j * 16 + (lane & 15)] = -acc[e];
+    }
+    __syncthreads();
+  }
+  // 8. T diag(beta) (upper tiles zero) to the workspace, block-major
+  for (int idx = tid; idx < C * C / 8; idx += 256) {
+    const int q = idx / C, i = idx % C;
+    float f[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int j = q * 8 + e;
+      f[e] = ((j >> 4) > (i >> 4)) ? 0.f : sTf[i * LDA + j] * sB[j];
+    }
+    st_vec16(reinterpret_cast<f16_t*>(wsc + W.oT + (q * C + i) * 16), f);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dp_chain_kernel: the sequential part, one workgroup per (head, BV columns).
+
+// Block-major tile reads.  `base` already holds the lane part of the address
+// (see lane_row / lane_tr), so every tile offset is an immediate.
+//
+// A operand of a 32-deep step from rows: lane (n = l & 15, g = l >> 4) needs
+// columns 32t + 4g + e and 32t + 16 + 4g + e of row `row0 + n`: blocks
+// 4t + (g >> 1) and 4t + 2 + (g >> 1), 8-byte half (g & 1).
+__device__ __forceinline__ int lane_row(int rows) {
+  const int l = threadIdx.x & 63, n = l & 15, g = l >> 4, hi = g >> 1;
+  return hi * rows * 16 + (n ^ (8 * hi)) * 16 + 8 * (g & 1);
+}
+// Transposed A operand (ds_read_b64_tr_b16): source lane i = 4e + a of
+// group g points at row j0 + 4g + e, columns d0 + 4a .. d0 + 4a + 3, i.e.
+// block d0 / 8 + (a >> 1), 8-byte half (a & 1).
+__device__ __forceinline__ int lane_tr(int rows) {
+  const int l = threadIdx.x & 63, i = l & 15, g = l >> 4, e = i >> 2, a = i & 3, hi = a >> 1;
+  return hi * rows * 16 + ((4 * g + e) ^ (8 * hi)) * 16 + 8 * (a & 1);
+}
+
+template <int ROWS>
+__device__ __forceinline__ f16x8_t blk_a32(const unsigned char* base, int row0, int t) {
+  const unsigned char* p = base + row0 * 16 + 4 * t * ROWS * 16;
+  return cat8(*reinterpret_cast<const f16x4_t*>(p), *reinterpret_cast<const f16x4_t*>(p + 2 * ROWS * 16));
+}
+template <int ROWS>
+__device__ __forceinline__ f16x4_t blk_a16(const unsigned char* base, int row0, int k0) {
+  return *reinterpret_cast<const f16x4_t*>(base + row0 * 16 + (k0 / 8) * ROWS * 16);
+}
+template <int ROWS>
+__device__ __forceinline__ s16x4_t blk_t16_raw(const unsigned char* base, int d0, int j0) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(base + (d0 / 8) * ROWS * 16 + j0 * 16));
+}
+template <int ROWS>
+__device__ __forceinline__ f16x4_t blk_t16(const unsigned char* base, int d0, int j0) {
+  return __builtin_bit_cast(f16x4_t, blk_t16_raw<ROWS>(base, d0, j0));
+}
+
+// acc += A (16 x K from block-major rows row0..row0+15) * B (register tiles)
+template <int ROWS, int K>
+__device__ __forceinline__ f32x4_t mm_blk(f32x4_t acc, const unsigned char* base, int row0, const f16x4_t* b) {
+  static_assert(K % 16 == 0, "K");
+#pragma unroll
+  for (int t = 0; t < K / 32; ++t) acc = mfma32h(blk_a32<ROWS>(base, row0, t), cat8(b[2 * t], b[2 * t + 1]), acc);
+  if constexpr (K % 32 == 16) acc = mfma16h(blk_a16<ROWS>(base, row0, K - 16), b[K / 16 - 1], acc);
+  return acc;
+}
+// acc += A (16 x K: transpose of block-major rows 0..K-1, columns d0..d0+15) * B
+template <int ROWS, int K>
+__device__ __forceinline__ f32x4_t mm_blk_t(f32x4_t acc, const unsigned char* base, int d0, const f16x4_t* b) {
+  static_assert(K % 16 == 0, "K");
+#pragma unroll
+  for (int t = 0; t < K / 32; ++t)
+    acc = mfma32h(cat8(blk_t16<ROWS>(base, d0, 32 * t), blk_t16<ROWS>(base, d0, 32 * t + 16)),
+                  cat8(b[2 * t], b[2 * t + 1]), acc);
+  if constexpr (K % 32 == 16) acc = mfma16h(blk_t16<ROWS>(base, d0, K - 16), b[K / 16 - 1], acc);
+  return acc;
+}
+
+__device__ __forceinline__ void dma16(const void* src, unsigned char* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
+}
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int DK, int C, int NWC, int NRT>
+__global__ __launch_bounds__(64 * (NWC + 1)) void dp_chain_kernel(FwdArgs p) {
+  constexpr int RT = 16 * NRT, BV = 16 * NWC;
+  constexpr int NCT = C / 16, NDT = DK / 16;
+  constexpr Chunk16Layout W = chunk16_layout(DK, C, RT);
+  constexpr int VB = C * BV * 2;                      // value tile bytes
+  constexpr int STAGE = W.bytes + VB;
+  constexpr int NIB = (W.bytes + 1023) / 1024;        // copies per chunk block
+  constexpr int NIV = VB / 1024 > 0 ? VB / 1024 : 1;  // copies per value tile
+  constexpr int VPI = VB >= 1024 ? 64 : VB / 16;      // lanes per value copy
+  constexpr int NI = NIB + NIV;
+  static_assert(NI < 64, "copies per chunk exceed the vmcnt range");
+  static_assert(VB % 16 == 0 && (VB < 1024 || VB % 1024 == 0), "value tile");
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // XCD-aware mapping: consecutive workgroup ids go round-robin over the 8
+  // XCDs, so spread ids so that the value blocks of one head share an XCD
+  // (and its L2) for the operand blocks they all read.
+  const int nwg = gridDim.x, bid = blockIdx.x;
+  const int f = (nwg % 8 == 0) ? (bid % 8) * (nwg / 8) + bid / 8 : bid;
+  const int bh = f / p.nvb, vb = f % p.nvb;
+  const int b = bh / p.H, h = bh % p.H;
+  const int v0 = vb * BV;
+  const int nc = p.nc;
+  const unsigned char* wsh = static_cast<const unsigned char*>(p.wsT) + (long long)bh * nc * W.bytes;
+
+  if (wave == NWC) {
+    // ================================================================ copy wave
+    // Source offset of each lane in each copy of the chunk block: the odd
+    // blocks of every tile region get their rows permuted (r -> r ^ 8).
+    int soff[NIB];
+#pragma unroll
+    for (int m = 0; m < NIB; ++m) {
+      const int o = 1024 * m + 16 * lane;
+      int src = o;
+      auto region = [&](int start, int rows, int bytes) {
+        if (o >= start && o < start + bytes) {
+          const int rel = o - start, blk = rel / (rows * 16), r = (rel / 16) % rows;
+          src = start + blk * rows * 16 + (r ^ (8 * (blk & 1))) * 16;
+        }
+      };
+      region(W.oT, C, C * C * 2);
+      region(W.oK, C, C * DK * 2);
+      region(W.oQ, RT, RT * DK * 2);
+      region(W.oP, RT, RT * C * 2);
+      soff[m] = src;
+    }
+    const bf16_t* vp = static_cast<const bf16_t*>(p.v) + v0;
+    const long long tok0 = (long long)b * p.L * p.H + h;
+    auto issue = [&](int c) {
+      unsigned char* st = smem + (c % kChainStages) * STAGE;
+      const unsigned char* src = wsh + (long long)c * W.bytes;
+#pragma unroll
+      for (int m = 0; m < NIB; ++m)
+        if (1024 * m + 16 * lane < W.bytes) dma16(src + soff[m], st + 1024 * m);
+      // value tile: block q = columns v0 + 8q.., rows = sub-steps (odd blocks permuted)
+#pragma unroll
+      for (int m = 0; m < NIV; ++m) {
+        const int o = 1024 * m + 16 * lane;
+        const int blk = o / (C * 16), r = (o / 16) % C;
+        int s = c * C + (r ^ (8 * (blk & 1)));
+        s = s < p.N ? s : p.N - 1;  // rows past the end: any valid row (their beta is 0)
+        const int t = fastdiv(s, p.nh_magic, p.nh_shift);
+        const long long row = (tok0 + (long long)t * p.H) * p.n_h + (s - t * p.n_h);
+        if (lane < VPI) dma16(vp + row * p.dv + 8 * blk, st + W.bytes + 1024 * m);
+      }
+    };
+    if (nc > 0) {
+      issue(0);
+      if (nc > 1) {
+        issue(1);
+        wait_vmcnt<NI>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      block_sync_lds();  // X(0)
+    }
+    for (int c = 0; c + 1 < nc; ++c) {
+      if (c + 2 < nc) {
+        issue(c + 2);  // into the stage chunk c - 1 used
+        wait_vmcnt<NI>();  // chunk c + 1 has landed
+      } else {
+        wait_vmcnt<0>();
+      }
+      block_sync_lds();  // X(c + 1)
+    }
+    return;
+  }
+
+  // ==================================================================== consumers
+  const int col = lane & 15, grp = lane >> 4;
+  const int vw = 16 * wave;  // this wavefront's columns inside the block
+  const int lrC = lane_row(C), lrR = lane_row(RT), ltC = lane_tr(C);
+  f32x4_t hacc[NDT];
+  f16x4_t hq[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    hacc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (p.h0 != nullptr) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) hacc[dt][e] = p.h0[((long long)bh * DK + dt * 16 + 4 * grp + e) * p.dv + v0 + vw + col];
+    }
+    hq[dt] = to_h4(hacc[dt]);
+  }
+  const bool gated = p.g != nullptr;
+  if (nc > 0) block_sync_lds();  // X(0)
+  for (int c = 0; c < nc; ++c) {
+    const unsigned char* st = smem + (c % kChainStages) * STAGE;
+    const unsigned char* aK = st + W.oK + lrC;
+    const unsigned char* tK = st + W.oK + ltC;
+    const unsigned char* aT = st + W.oT + lrC;
+    const unsigned char* aQ = st + W.oQ + lrR;
+    const unsigned char* aP = st + W.oP + lrR;
+    const unsigned char* tV = st + W.bytes + ltC;
+    const float* sEG = reinterpret_cast<const float*>(st + W.oS + W.oEG);
+    const float* sEL = reinterpret_cast<const float*>(st + W.oS + W.oEL);
+    const float* sEGL = reinterpret_cast<const float*>(st + W.oS + W.oEGL);
+    const long long* sOff = reinterpret_cast<const long long*>(st + W.oS + W.oOff);
+
+    // ---- X = V - diag(e^G) (Kn H)
+    f16x4_t xq[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mm_blk<C, DK>(acc, aK, ct * 16, hq);
+      const f32x4_t eg = *reinterpret_cast<const f32x4_t*>(sEG + ct * 16 + 4 * grp);
+      const s16x4_t vr = blk_t16_raw<C>(tV, vw, ct * 16);  // V[16 ct + 4 grp + e][vw + col], bf16
+      f32x4_t x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = __uint_as_float((uint32_t)(uint16_t)vr[e] << 16) - eg[e] * acc[e];
+      xq[ct] = to_h4(x);
+    }
+    // ---- Up = (T diag(beta)) X;  Us = diag(e^{G_last - G}) Up
+    f16x4_t uq[NCT], usq[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mm_blk<C, C>(acc, aT, ct * 16, xq);
+      uq[ct] = to_h4(acc);
+      if (gated) {
+        const f32x4_t el = *reinterpret_cast<const f32x4_t*>(sEL + ct * 16 + 4 * grp);
+        usq[ct] = to_h4(acc * el);
+      } else {
+        usq[ct] = uq[ct];
+      }
+    }
+    // ---- O = diag(e^{G_loc}) Q H + P Up for the readout rows, written out
+#pragma unroll
+    for (int it = 0; it < NRT; ++it) {
+      f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+      z = mm_blk<RT, DK>(z, aQ, it * 16, hq);
+      const f32x4_t egl = *reinterpret_cast<const f32x4_t*>(sEGL + it * 16 + 4 * grp);
+      z = z * egl;
+      z = mm_blk<RT, C>(z, aP, it * 16, uq);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const long long o = sOff[it * 16 + 4 * grp + e];
+        if (o >= 0) {
+          if (p.out_f32)
+            static_cast<float*>(p.out)[o + v0 + vw + col] = z[e];
+          else
+            static_cast<bf16_t*>(p.out)[o + v0 + vw + col] = __builtin_bit_cast(bf16_t, (__bf16)z[e]);
+        }
+      }
+    }
+    // ---- H = e^{G_last} H + Kn^T Us
+    const float dec = sEG[C - 1];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      if (gated) hacc[dt] = hacc[dt] * dec;
+      hacc[dt] = mm_blk_t<C, C>(hacc[dt], tK, dt * 16, usq);
+      hq[dt] = to_h4(hacc[dt]);
+    }
+    if (c + 1 < nc) block_sync_lds();  // X(c + 1)
+  }
+
+  if (p.fstate != nullptr) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        p.fstate[((long long)bh * DK + dt * 16 + 4 * grp + e) * p.dv + v0 + vw + col] = hacc[dt][e];
+  }
+}
+
+}  // namespace dp

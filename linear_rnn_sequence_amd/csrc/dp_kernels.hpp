@@ -1089,6 +1089,12 @@ inline bool allow_big_lds(const void* fn) {
   return e == hipSuccess;
 }
 
+}  // namespace dp
+
+#include "dp_fwd16.hpp"
+
+namespace dp {
+
 template <typename T, int DK, int C>
 hipError_t launch_ut(const FwdArgs& a, hipStream_t st) {
   const int lds = ut_lds_bytes((int)sizeof(T), DK, C, a.asym);
@@ -1173,11 +1179,63 @@ hipError_t launch_scan_any(const FwdArgs& a, int BV, int lds, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
+// bf16 with symmetric keys: dp_prep_kernel then dp_chain_kernel.
+template <int DK, int C, int NRT>
+hipError_t launch_prep(const FwdArgs& a, hipStream_t st) {
+  static const bool attr = allow_big_lds(reinterpret_cast<const void*>(&dp_prep_kernel<DK, C, NRT>));
+  (void)attr;
+  const long long nchunks = (long long)a.B * a.H * a.nc;
+  hipLaunchKernelGGL((dp_prep_kernel<DK, C, NRT>), dim3((unsigned)nchunks), dim3(256),
+                     prep_lds_bytes(DK, C, 16 * NRT), st, a);
+  return hipGetLastError();
+}
+
+template <int DK, int C, int NWC, int NRT>
+hipError_t launch_chain(const FwdArgs& a, hipStream_t st) {
+  static const bool attr = allow_big_lds(reinterpret_cast<const void*>(&dp_chain_kernel<DK, C, NWC, NRT>));
+  (void)attr;
+  const long long nwg = (long long)a.B * a.H * a.nvb;
+  hipLaunchKernelGGL((dp_chain_kernel<DK, C, NWC, NRT>), dim3((unsigned)nwg), dim3(64 * (NWC + 1)),
+                     chain_lds_bytes(DK, C, 16 * NRT, 16 * NWC), st, a);
+  return hipGetLastError();
+}
+
+template <int DK, int C, int NRT>
+hipError_t launch_sym16_nrt(const FwdArgs& a, int BV, int stages, hipStream_t st) {
+  if (stages & 1) {
+    const hipError_t e = launch_prep<DK, C, NRT>(a, st);
+    if (e != hipSuccess) return e;
+  }
+  if (stages & 2) {
+    switch (BV) {
+      case 16: return launch_chain<DK, C, 1, NRT>(a, st);
+      case 32: return launch_chain<DK, C, 2, NRT>(a, st);
+      case 64: return launch_chain<DK, C, 4, NRT>(a, st);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  return hipSuccess;
+}
+
+template <int DK, int C>
+hipError_t launch_sym16(const FwdArgs& a, int BV, int stages, hipStream_t st) {
+  switch (a.RT / 16) {
+    case 1: return launch_sym16_nrt<DK, C, 1>(a, BV, stages, st);
+    case 2: if constexpr (C >= 32) return launch_sym16_nrt<DK, C, 2>(a, BV, stages, st); break;
+    case 3: if constexpr (C >= 64) return launch_sym16_nrt<DK, C, 3>(a, BV, stages, st); break;
+    case 4: if constexpr (C >= 64) return launch_sym16_nrt<DK, C, 4>(a, BV, stages, st); break;
+  }
+  return hipErrorInvalidValue;
+}
+
 template <typename T, int DK>
 hipError_t launch_fwd_dk(const FwdArgs& a, int C, int BV, int lds_scan, int stages, hipStream_t st) {
   hipError_t e = hipSuccess;
 #define DP_CASE_C(CC)                                                          \
   case CC:                                                                     \
+    if constexpr (sizeof(T) == 2) {                                            \
+      if (!a.asym) return launch_sym16<DK, CC>(a, BV, stages, st);             \
+    }                                                                          \
     if (stages & 1) {                                                          \
       e = launch_ut<T, DK, CC>(a, st);                                         \
       if (e != hipSuccess) return e;                                           \
