@@ -292,63 +292,90 @@ __global__ __launch_bounds__(256) void dp_prep_kernel(FwdArgs p) {
 
 // ---------------------------------------------------------------------------
 // dp_chain_kernel: the sequential part, one workgroup per (head, BV columns).
-
-// Block-major tile reads.  `base` already holds the lane part of the address
-// (see lane_row / lane_tr), so every tile offset is an immediate.
 //
-// A operand of a 32-deep step from rows: lane (n = l & 15, g = l >> 4) needs
-// columns 32t + 4g + e and 32t + 16 + 4g + e of row `row0 + n`: blocks
-// 4t + (g >> 1) and 4t + 2 + (g >> 1), 8-byte half (g & 1).
+// LDS tile layout.  A tile of R rows and W columns arrives block-major (W/8
+// blocks of R x 16 bytes).  In LDS (a) the rows of logically odd blocks are
+// permuted, row r in slot r ^ 8, and (b) when W is a multiple of 32 the blocks
+// of each group of four are stored in the order 0, 2, 1, 3.  With (b) the two
+// 8-byte halves of an MFMA A fragment (columns 32t + 4g.. and 32t + 16 + 4g..)
+// sit exactly one block apart, so one ds_read2_b64 fetches a fragment into
+// consecutive registers.
+
+// physical position of logical block q in a region of W columns (an involution)
+__host__ __device__ constexpr int blk_pos(int q, int W) {
+  return (W % 32 == 0) ? ((q & ~3) | ((q & 1) << 1) | ((q >> 1) & 1)) : q;
+}
+
+// Lane part of a row read (A fragment of a 32- or 16-deep step): lane
+// (n = l & 15, g = l >> 4) reads row row0 + n, logical blocks 4t + (g >> 1)
+// (and 4t + 2 + (g >> 1)), 8-byte half (g & 1).
+template <int W>
 __device__ __forceinline__ int lane_row(int rows) {
   const int l = threadIdx.x & 63, n = l & 15, g = l >> 4, hi = g >> 1;
-  return hi * rows * 16 + (n ^ (8 * hi)) * 16 + 8 * (g & 1);
+  return blk_pos(hi, W) * rows * 16 + (n ^ (8 * hi)) * 16 + 8 * (g & 1);
 }
-// Transposed A operand (ds_read_b64_tr_b16): source lane i = 4e + a of
-// group g points at row j0 + 4g + e, columns d0 + 4a .. d0 + 4a + 3, i.e.
-// block d0 / 8 + (a >> 1), 8-byte half (a & 1).
+// Lane part of a transposed read (ds_read_b64_tr_b16): source lane i = 4e + a
+// of group g points at row j0 + 4g + e, columns d0 + 4a .. d0 + 4a + 3, i.e.
+// logical block d0 / 8 + (a >> 1), 8-byte half (a & 1).
+template <int W>
 __device__ __forceinline__ int lane_tr(int rows) {
   const int l = threadIdx.x & 63, i = l & 15, g = l >> 4, e = i >> 2, a = i & 3, hi = a >> 1;
-  return hi * rows * 16 + ((4 * g + e) ^ (8 * hi)) * 16 + 8 * (a & 1);
+  return blk_pos(hi, W) * rows * 16 + ((4 * g + e) ^ (8 * hi)) * 16 + 8 * (a & 1);
+}
+// block offset (immediate part) of logical block pair base 2 * dt (d0 = 16 dt)
+template <int W>
+__host__ __device__ constexpr int tr_block(int dt) {
+  return (W % 32 == 0) ? 4 * (dt >> 1) + (dt & 1) : 2 * dt;
 }
 
-template <int ROWS>
-__device__ __forceinline__ f16x8_t blk_a32(const unsigned char* base, int row0, int t) {
-  const unsigned char* p = base + row0 * 16 + 4 * t * ROWS * 16;
-  return cat8(*reinterpret_cast<const f16x4_t*>(p), *reinterpret_cast<const f16x4_t*>(p + 2 * ROWS * 16));
-}
-template <int ROWS>
-__device__ __forceinline__ f16x4_t blk_a16(const unsigned char* base, int row0, int k0) {
-  return *reinterpret_cast<const f16x4_t*>(base + row0 * 16 + (k0 / 8) * ROWS * 16);
-}
-template <int ROWS>
-__device__ __forceinline__ s16x4_t blk_t16_raw(const unsigned char* base, int d0, int j0) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(base + (d0 / 8) * ROWS * 16 + j0 * 16));
-}
-template <int ROWS>
-__device__ __forceinline__ f16x4_t blk_t16(const unsigned char* base, int d0, int j0) {
-  return __builtin_bit_cast(f16x4_t, blk_t16_raw<ROWS>(base, d0, j0));
-}
+// A fragments of a 16 x K operand from block-major rows (K = W of the region).
+template <int ROWS, int K>
+struct RowFrags {
+  f16x8_t f[K / 32 > 0 ? K / 32 : 1];
+  f16x4_t r;  // the last 16 of the contraction when K % 32 == 16
+  // `off`: LDS byte offset of this 16-row tile (lane part included).  It is
+  // made opaque so that the two halves of each fragment -- one block apart --
+  // are the closest loads on their base register and pair into ds_read2_b64.
+  __device__ __forceinline__ void load(const unsigned char* lds, uint32_t off) {
+    asm volatile("" : "+v"(off));
+    const unsigned char* base = lds + off;
+#pragma unroll
+    for (int t = 0; t < K / 32; ++t) {
+      const unsigned char* p = base + 4 * t * ROWS * 16;
+      f[t] = cat8(*reinterpret_cast<const f16x4_t*>(p), *reinterpret_cast<const f16x4_t*>(p + ROWS * 16));
+    }
+    if constexpr (K % 32 == 16) r = *reinterpret_cast<const f16x4_t*>(base + ((K - 16) / 8) * ROWS * 16);
+  }
+  __device__ __forceinline__ f32x4_t mma(f32x4_t acc, const f16x4_t* b) const {
+#pragma unroll
+    for (int t = 0; t < K / 32; ++t) acc = mfma32h(f[t], cat8(b[2 * t], b[2 * t + 1]), acc);
+    if constexpr (K % 32 == 16) acc = mfma16h(r, b[K / 16 - 1], acc);
+    return acc;
+  }
+};
 
-// acc += A (16 x K from block-major rows row0..row0+15) * B (register tiles)
-template <int ROWS, int K>
-__device__ __forceinline__ f32x4_t mm_blk(f32x4_t acc, const unsigned char* base, int row0, const f16x4_t* b) {
-  static_assert(K % 16 == 0, "K");
+// A fragments of the transpose (16 x K) of block-major rows 0..K-1, columns
+// d0..d0+15 of a region W columns wide.
+template <int ROWS, int W, int K>
+struct TrFrags {
+  f16x8_t f[K / 32 > 0 ? K / 32 : 1];
+  f16x4_t r;
+  __device__ __forceinline__ static f16x4_t rd(const unsigned char* p) {
+    return __builtin_bit_cast(f16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p));
+  }
+  __device__ __forceinline__ void load(const unsigned char* base, int dt) {
+    const unsigned char* p = base + tr_block<W>(dt) * ROWS * 16;
 #pragma unroll
-  for (int t = 0; t < K / 32; ++t) acc = mfma32h(blk_a32<ROWS>(base, row0, t), cat8(b[2 * t], b[2 * t + 1]), acc);
-  if constexpr (K % 32 == 16) acc = mfma16h(blk_a16<ROWS>(base, row0, K - 16), b[K / 16 - 1], acc);
-  return acc;
-}
-// acc += A (16 x K: transpose of block-major rows 0..K-1, columns d0..d0+15) * B
-template <int ROWS, int K>
-__device__ __forceinline__ f32x4_t mm_blk_t(f32x4_t acc, const unsigned char* base, int d0, const f16x4_t* b) {
-  static_assert(K % 16 == 0, "K");
+    for (int t = 0; t < K / 32; ++t) f[t] = cat8(rd(p + 32 * t * 16), rd(p + (32 * t + 16) * 16));
+    if constexpr (K % 32 == 16) r = rd(p + (K - 16) * 16);
+  }
+  __device__ __forceinline__ f32x4_t mma(f32x4_t acc, const f16x4_t* b) const {
 #pragma unroll
-  for (int t = 0; t < K / 32; ++t)
-    acc = mfma32h(cat8(blk_t16<ROWS>(base, d0, 32 * t), blk_t16<ROWS>(base, d0, 32 * t + 16)),
-                  cat8(b[2 * t], b[2 * t + 1]), acc);
-  if constexpr (K % 32 == 16) acc = mfma16h(blk_t16<ROWS>(base, d0, K - 16), b[K / 16 - 1], acc);
-  return acc;
-}
+    for (int t = 0; t < K / 32; ++t) acc = mfma32h(f[t], cat8(b[2 * t], b[2 * t + 1]), acc);
+    if constexpr (K % 32 == 16) acc = mfma16h(r, b[K / 16 - 1], acc);
+    return acc;
+  }
+};
 
 __device__ __forceinline__ void dma16(const void* src, unsigned char* lds_dst) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
@@ -359,9 +386,12 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+// keep the scheduler from moving instructions across this point
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
-template <int DK, int C, int NWC, int NRT>
-__global__ __launch_bounds__(64 * (NWC + 1)) void dp_chain_kernel(FwdArgs p) {
+template <int DK, int C, int NWC, int NRT, bool GATED>
+__global__ __launch_bounds__(64 * (NWC + 1)) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void dp_chain_kernel(FwdArgs p) {
   constexpr int RT = 16 * NRT, BV = 16 * NWC;
   constexpr int NCT = C / 16, NDT = DK / 16;
   constexpr Chunk16Layout W = chunk16_layout(DK, C, RT);
@@ -390,23 +420,25 @@ __global__ __launch_bounds__(64 * (NWC + 1)) void dp_chain_kernel(FwdArgs p) {
 
   if (wave == NWC) {
     // ================================================================ copy wave
-    // Source offset of each lane in each copy of the chunk block: the odd
-    // blocks of every tile region get their rows permuted (r -> r ^ 8).
+    // Source offset of each lane in each copy of the chunk block: LDS slot
+    // (physical block, row slot) of a tile region holds logical block
+    // blk_pos(physical) and row slot ^ 8 for odd logical blocks.
     int soff[NIB];
 #pragma unroll
     for (int m = 0; m < NIB; ++m) {
       const int o = 1024 * m + 16 * lane;
       int src = o;
-      auto region = [&](int start, int rows, int bytes) {
-        if (o >= start && o < start + bytes) {
-          const int rel = o - start, blk = rel / (rows * 16), r = (rel / 16) % rows;
-          src = start + blk * rows * 16 + (r ^ (8 * (blk & 1))) * 16;
+      auto region = [&](int start, int rows, int cols) {
+        if (o >= start && o < start + rows * cols * 2) {
+          const int rel = o - start, pb = rel / (rows * 16), rs = (rel / 16) % rows;
+          const int q = blk_pos(pb, cols);
+          src = start + q * rows * 16 + (rs ^ (8 * (q & 1))) * 16;
         }
       };
-      region(W.oT, C, C * C * 2);
-      region(W.oK, C, C * DK * 2);
-      region(W.oQ, RT, RT * DK * 2);
-      region(W.oP, RT, RT * C * 2);
+      region(W.oT, C, C);
+      region(W.oK, C, DK);
+      region(W.oQ, RT, DK);
+      region(W.oP, RT, C);
       soff[m] = src;
     }
     const bf16_t* vp = static_cast<const bf16_t*>(p.v) + v0;
@@ -417,16 +449,17 @@ __global__ __launch_bounds__(64 * (NWC + 1)) void dp_chain_kernel(FwdArgs p) {
 #pragma unroll
       for (int m = 0; m < NIB; ++m)
         if (1024 * m + 16 * lane < W.bytes) dma16(src + soff[m], st + 1024 * m);
-      // value tile: block q = columns v0 + 8q.., rows = sub-steps (odd blocks permuted)
+      // value tile: logical block q = columns v0 + 8q.., rows = sub-steps
 #pragma unroll
       for (int m = 0; m < NIV; ++m) {
         const int o = 1024 * m + 16 * lane;
-        const int blk = o / (C * 16), r = (o / 16) % C;
-        int s = c * C + (r ^ (8 * (blk & 1)));
+        const int pb = o / (C * 16), rs = (o / 16) % C;
+        const int q = blk_pos(pb, BV);
+        int s = c * C + (rs ^ (8 * (q & 1)));
         s = s < p.N ? s : p.N - 1;  // rows past the end: any valid row (their beta is 0)
         const int t = fastdiv(s, p.nh_magic, p.nh_shift);
         const long long row = (tok0 + (long long)t * p.H) * p.n_h + (s - t * p.n_h);
-        if (lane < VPI) dma16(vp + row * p.dv + 8 * blk, st + W.bytes + 1024 * m);
+        if (lane < VPI) dma16(vp + row * p.dv + 8 * q, st + W.bytes + 1024 * m);
       }
     };
     if (nc > 0) {
@@ -454,7 +487,8 @@ __global__ __launch_bounds__(64 * (NWC + 1)) void dp_chain_kernel(FwdArgs p) {
   // ==================================================================== consumers
   const int col = lane & 15, grp = lane >> 4;
   const int vw = 16 * wave;  // this wavefront's columns inside the block
-  const int lrC = lane_row(C), lrR = lane_row(RT), ltC = lane_tr(C);
+  const int lrT = lane_row<C>(C), lrK = lane_row<DK>(C), lrQ = lane_row<DK>(RT), lrP = lane_row<C>(RT);
+  const int ltK = lane_tr<DK>(C), ltV = lane_tr<BV>(C);
   f32x4_t hacc[NDT];
   f16x4_t hq[NDT];
 #pragma unroll
@@ -466,59 +500,87 @@ __global__ __launch_bounds__(64 * (NWC + 1)) void dp_chain_kernel(FwdArgs p) {
     }
     hq[dt] = to_h4(hacc[dt]);
   }
-  const bool gated = p.g != nullptr;
   if (nc > 0) block_sync_lds();  // X(0)
   for (int c = 0; c < nc; ++c) {
-    const unsigned char* st = smem + (c % kChainStages) * STAGE;
-    const unsigned char* aK = st + W.oK + lrC;
-    const unsigned char* tK = st + W.oK + ltC;
-    const unsigned char* aT = st + W.oT + lrC;
-    const unsigned char* aQ = st + W.oQ + lrR;
-    const unsigned char* aP = st + W.oP + lrR;
-    const unsigned char* tV = st + W.bytes + ltC;
+    const uint32_t so = (uint32_t)((c % kChainStages) * STAGE);
+    const unsigned char* st = smem + so;
     const float* sEG = reinterpret_cast<const float*>(st + W.oS + W.oEG);
     const float* sEL = reinterpret_cast<const float*>(st + W.oS + W.oEL);
     const float* sEGL = reinterpret_cast<const float*>(st + W.oS + W.oEGL);
     const long long* sOff = reinterpret_cast<const long long*>(st + W.oS + W.oOff);
 
+    // ---- operands of X and Up, all issued before the first product
+    RowFrags<C, DK> fk[NCT];
+    RowFrags<C, C> ft[NCT];
+    s16x4_t vr[NCT];
+    f32x4_t eg[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      fk[ct].load(smem, so + W.oK + lrK + ct * 256);
+      vr[ct] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4_t*)(st + W.bytes + ltV + tr_block<BV>(wave) * C * 16 + ct * 16 * 16));
+      eg[ct] = *reinterpret_cast<const f32x4_t*>(sEG + ct * 16 + 4 * grp);
+    }
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) ft[ct].load(smem, so + W.oT + lrT + ct * 256);
+    sched_fence();
+
     // ---- X = V - diag(e^G) (Kn H)
     f16x4_t xq[NCT];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mm_blk<C, DK>(acc, aK, ct * 16, hq);
-      const f32x4_t eg = *reinterpret_cast<const f32x4_t*>(sEG + ct * 16 + 4 * grp);
-      const s16x4_t vr = blk_t16_raw<C>(tV, vw, ct * 16);  // V[16 ct + 4 grp + e][vw + col], bf16
+      const f32x4_t acc = fk[ct].mma(f32x4_t{0.f, 0.f, 0.f, 0.f}, hq);
       f32x4_t x;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = __uint_as_float((uint32_t)(uint16_t)vr[e] << 16) - eg[e] * acc[e];
+      for (int e = 0; e < 4; ++e) x[e] = __uint_as_float((uint32_t)(uint16_t)vr[ct][e] << 16) - eg[ct][e] * acc[e];
       xq[ct] = to_h4(x);
     }
+    // operands of the readout, issued while X and Up are computed
+    RowFrags<RT, DK> fq[NRT];
+    RowFrags<RT, C> fp[NRT];
+    f32x4_t egl[NRT];
+    long long off[NRT][4];
+#pragma unroll
+    for (int it = 0; it < NRT; ++it) {
+      fq[it].load(smem, so + W.oQ + lrQ + it * 256);
+      fp[it].load(smem, so + W.oP + lrP + it * 256);
+      egl[it] = *reinterpret_cast<const f32x4_t*>(sEGL + it * 16 + 4 * grp);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) off[it][e] = sOff[it * 16 + 4 * grp + e];
+    }
+    f32x4_t el[NCT];
+    if constexpr (GATED) {
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) el[ct] = *reinterpret_cast<const f32x4_t*>(sEL + ct * 16 + 4 * grp);
+    }
+    sched_fence();
+
     // ---- Up = (T diag(beta)) X;  Us = diag(e^{G_last - G}) Up
     f16x4_t uq[NCT], usq[NCT];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mm_blk<C, C>(acc, aT, ct * 16, xq);
+      const f32x4_t acc = ft[ct].mma(f32x4_t{0.f, 0.f, 0.f, 0.f}, xq);
       uq[ct] = to_h4(acc);
-      if (gated) {
-        const f32x4_t el = *reinterpret_cast<const f32x4_t*>(sEL + ct * 16 + 4 * grp);
-        usq[ct] = to_h4(acc * el);
-      } else {
+      if constexpr (GATED)
+        usq[ct] = to_h4(acc * el[ct]);
+      else
         usq[ct] = uq[ct];
-      }
     }
+    // operands of the state update, issued while the readout is computed
+    TrFrags<C, DK, C> fkt[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) fkt[dt].load(st + W.oK + ltK, dt);
+    sched_fence();
+
     // ---- O = diag(e^{G_loc}) Q H + P Up for the readout rows, written out
 #pragma unroll
     for (int it = 0; it < NRT; ++it) {
-      f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-      z = mm_blk<RT, DK>(z, aQ, it * 16, hq);
-      const f32x4_t egl = *reinterpret_cast<const f32x4_t*>(sEGL + it * 16 + 4 * grp);
-      z = z * egl;
-      z = mm_blk<RT, C>(z, aP, it * 16, uq);
+      f32x4_t z = fq[it].mma(f32x4_t{0.f, 0.f, 0.f, 0.f}, hq);
+      z = z * egl[it];
+      z = fp[it].mma(z, uq);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const long long o = sOff[it * 16 + 4 * grp + e];
+        const long long o = off[it][e];
         if (o >= 0) {
           if (p.out_f32)
             static_cast<float*>(p.out)[o + v0 + vw + col] = z[e];
@@ -531,8 +593,8 @@ __global__ __launch_bounds__(64 * (NWC + 1)) void dp_chain_kernel(FwdArgs p) {
     const float dec = sEG[C - 1];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      if (gated) hacc[dt] = hacc[dt] * dec;
-      hacc[dt] = mm_blk_t<C, C>(hacc[dt], tK, dt * 16, usq);
+      if constexpr (GATED) hacc[dt] = hacc[dt] * dec;
+      hacc[dt] = fkt[dt].mma(hacc[dt], usq);
       hq[dt] = to_h4(hacc[dt]);
     }
     if (c + 1 < nc) block_sync_lds();  // X(c + 1)

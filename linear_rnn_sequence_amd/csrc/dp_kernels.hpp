@@ -1190,14 +1190,19 @@ hipError_t launch_prep(const FwdArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int DK, int C, int NWC, int NRT>
-hipError_t launch_chain(const FwdArgs& a, hipStream_t st) {
-  static const bool attr = allow_big_lds(reinterpret_cast<const void*>(&dp_chain_kernel<DK, C, NWC, NRT>));
+template <int DK, int C, int NWC, int NRT, bool GATED>
+hipError_t launch_chain_g(const FwdArgs& a, hipStream_t st) {
+  static const bool attr = allow_big_lds(reinterpret_cast<const void*>(&dp_chain_kernel<DK, C, NWC, NRT, GATED>));
   (void)attr;
   const long long nwg = (long long)a.B * a.H * a.nvb;
-  hipLaunchKernelGGL((dp_chain_kernel<DK, C, NWC, NRT>), dim3((unsigned)nwg), dim3(64 * (NWC + 1)),
+  hipLaunchKernelGGL((dp_chain_kernel<DK, C, NWC, NRT, GATED>), dim3((unsigned)nwg), dim3(64 * (NWC + 1)),
                      chain_lds_bytes(DK, C, 16 * NRT, 16 * NWC), st, a);
   return hipGetLastError();
+}
+
+template <int DK, int C, int NWC, int NRT>
+hipError_t launch_chain(const FwdArgs& a, hipStream_t st) {
+  return a.g != nullptr ? launch_chain_g<DK, C, NWC, NRT, true>(a, st) : launch_chain_g<DK, C, NWC, NRT, false>(a, st);
 }
 
 template <int DK, int C, int NRT>
