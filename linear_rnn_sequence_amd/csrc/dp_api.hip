@@ -64,11 +64,16 @@ int readout_rows(int C, int n_h) {
 
 // bf16: one operand block per chunk (dp_prep_kernel's output); it also covers
 // the T / (1/|k|, G) layout the write-key path uses.  fp32: T and (1/|k|, G).
+size_t ws_blocks_bytes(const Shape& s) {
+  const dp::Chunk16Layout W = dp::chunk16_layout(s.dk, s.chunk, readout_rows(s.chunk, s.n_h));
+  return align_up((size_t)s.B * s.H * num_chunks(s) * W.bytes, kWsAlign);
+}
+
+// One fp32 slot per lane of every scan wavefront (at most dv / 16 per head).
+size_t ws_sink_bytes(const Shape& s) { return align_up((size_t)s.B * s.H * (s.dv / 16) * 64 * 4, kWsAlign); }
+
 size_t ws_total(const Shape& s, int elem) {
-  if (elem == 2) {
-    const dp::Chunk16Layout W = dp::chunk16_layout(s.dk, s.chunk, readout_rows(s.chunk, s.n_h));
-    return align_up((size_t)s.B * s.H * num_chunks(s) * W.bytes, kWsAlign);
-  }
+  if (elem == 2) return ws_blocks_bytes(s) + ws_sink_bytes(s);
   return ws_t_bytes(s, elem) + (size_t)s.B * s.H * num_chunks(s) * s.chunk * sizeof(float2);
 }
 
@@ -265,6 +270,7 @@ int fwd_impl(int elem, const void* q, const void* k, const void* kt, const void*
   a.fstate = final_state;
   a.wsT = workspace;
   a.wsS = reinterpret_cast<float2*>(static_cast<char*>(workspace) + ws_t_bytes(s, elem));
+  if (elem == 2) a.sink = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws_blocks_bytes(s));
   a.N = L * n_h;
   a.B = B;
   a.H = H;

@@ -66,11 +66,16 @@ __host__ __device__ constexpr int chain_lds_bytes(int DK, int C, int RT, int BV)
   return kChainStages * chain_stage_bytes(DK, C, RT, BV);
 }
 
-// LDS of dp_prep_kernel: fp16 key and query rows, fp32 M and T, beta / G /
-// scalars, readout locations and the partial-sum tiles of the blocked inverse.
+// LDS of dp_prep_kernel.  Region 0 holds the fp16 key and query rows while
+// M and the scores are formed, then fp32 T and the partial-sum tiles of the
+// blocked inverse; after it come fp32 M, beta, G and the readout locations.
+__host__ __device__ constexpr int prep_region0_bytes(int DK, int C, int RT) {
+  return (C * (DK + 8) * 2 + RT * (DK + 8) * 2) > (C * (C + 4) * 4 + 4 * 16 * 17 * 4)
+             ? (C * (DK + 8) * 2 + RT * (DK + 8) * 2)
+             : (C * (C + 4) * 4 + 4 * 16 * 17 * 4);
+}
 __host__ __device__ constexpr int prep_lds_bytes(int DK, int C, int RT) {
-  return C * (DK + 8) * 2 + RT * (DK + 8) * 2 + 2 * C * (C + 4) * 4 + 2 * C * 4 + RT * 4 +
-         4 * 16 * 17 * 4;
+  return prep_region0_bytes(DK, C, RT) + C * (C + 4) * 4 + 2 * C * 4 + RT * 4;
 }
 
 // ---------------------------------------------------------------------------
@@ -87,14 +92,14 @@ __global__ __launch_bounds__(256) void dp_prep_kernel(FwdArgs p) {
   static_assert(TPR <= 64 && 64 % TPR == 0, "row group must fit in a wavefront");
 
   extern __shared__ __align__(16) unsigned char smem[];
-  f16_t* sK = reinterpret_cast<f16_t*>(smem);
+  f16_t* sK = reinterpret_cast<f16_t*>(smem);  // region 0, until M and P are formed
   f16_t* sQ = sK + C * LDK;
-  float* sA = reinterpret_cast<float*>(sQ + RT * LDK);
-  float* sTf = sA + C * LDA;
-  float* sB = sTf + C * LDA;
+  float* sTf = reinterpret_cast<float*>(smem);  // region 0, from the inverse on
+  float* sSc = sTf + C * LDA;
+  float* sA = reinterpret_cast<float*>(smem + prep_region0_bytes(DK, C, RT));
+  float* sB = sA + C * LDA;
   float* sG = sB + C;
   int* sLoc = reinterpret_cast<int*>(sG + C);
-  float* sSc = reinterpret_cast<float*>(sLoc + RT);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const long long chunk = blockIdx.x;
@@ -210,7 +215,7 @@ __global__ __launch_bounds__(256) void dp_prep_kernel(FwdArgs p) {
     for (int e = 0; e < 4; ++e) {
       const int ii = ti * 16 + 4 * (lane >> 4) + e;
       float val = 0.f;
-      if (jj < ii) val = sB[ii] * expf(sG[ii] - sG[jj]) * acc[e];
+      if (jj < ii) val = sB[ii] * (p.g != nullptr ? expf(sG[ii] - sG[jj]) : 1.f) * acc[e];
       sA[ii * LDA + jj] = val;
     }
   }
@@ -489,6 +494,8 @@ void dp_chain_kernel(FwdArgs p) {
   const int vw = 16 * wave;  // this wavefront's columns inside the block
   const int lrT = lane_row<C>(C), lrK = lane_row<DK>(C), lrQ = lane_row<DK>(RT), lrP = lane_row<C>(RT);
   const int ltK = lane_tr<DK>(C), ltV = lane_tr<BV>(C);
+  const int ocol = v0 + vw + col;  // output column of this lane
+  float* const sink = p.sink + ((long long)f * NWC + wave) * 64 + lane;
   f32x4_t hacc[NDT];
   f16x4_t hq[NDT];
 #pragma unroll
@@ -509,11 +516,11 @@ void dp_chain_kernel(FwdArgs p) {
     const float* sEGL = reinterpret_cast<const float*>(st + W.oS + W.oEGL);
     const long long* sOff = reinterpret_cast<const long long*>(st + W.oS + W.oOff);
 
-    // ---- operands of X and Up, all issued before the first product
+    // ---- operands of X and of the readout's Q H, all issued before the first product
     RowFrags<C, DK> fk[NCT];
-    RowFrags<C, C> ft[NCT];
+    RowFrags<RT, DK> fq[NRT];
     s16x4_t vr[NCT];
-    f32x4_t eg[NCT];
+    f32x4_t eg[NCT], egl[NRT];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       fk[ct].load(smem, so + W.oK + lrK + ct * 256);
@@ -522,11 +529,18 @@ void dp_chain_kernel(FwdArgs p) {
       eg[ct] = *reinterpret_cast<const f32x4_t*>(sEG + ct * 16 + 4 * grp);
     }
 #pragma unroll
+    for (int it = 0; it < NRT; ++it) {
+      fq[it].load(smem, so + W.oQ + lrQ + it * 256);
+      egl[it] = *reinterpret_cast<const f32x4_t*>(sEGL + it * 16 + 4 * grp);
+    }
+    RowFrags<C, C> ft[NCT];
+#pragma unroll
     for (int ct = 0; ct < NCT; ++ct) ft[ct].load(smem, so + W.oT + lrT + ct * 256);
     sched_fence();
 
-    // ---- X = V - diag(e^G) (Kn H)
+    // ---- X = V - diag(e^G) (Kn H);  Z = diag(e^{G_loc}) Q H  (both read H)
     f16x4_t xq[NCT];
+    f32x4_t z[NRT];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       const f32x4_t acc = fk[ct].mma(f32x4_t{0.f, 0.f, 0.f, 0.f}, hq);
@@ -535,16 +549,14 @@ void dp_chain_kernel(FwdArgs p) {
       for (int e = 0; e < 4; ++e) x[e] = __uint_as_float((uint32_t)(uint16_t)vr[ct][e] << 16) - eg[ct][e] * acc[e];
       xq[ct] = to_h4(x);
     }
-    // operands of the readout, issued while X and Up are computed
-    RowFrags<RT, DK> fq[NRT];
+#pragma unroll
+    for (int it = 0; it < NRT; ++it) z[it] = fq[it].mma(f32x4_t{0.f, 0.f, 0.f, 0.f}, hq) * egl[it];
+    // operands of the readout's P Up, issued while X and Up are computed
     RowFrags<RT, C> fp[NRT];
-    f32x4_t egl[NRT];
     long long off[NRT][4];
 #pragma unroll
     for (int it = 0; it < NRT; ++it) {
-      fq[it].load(smem, so + W.oQ + lrQ + it * 256);
       fp[it].load(smem, so + W.oP + lrP + it * 256);
-      egl[it] = *reinterpret_cast<const f32x4_t*>(sEGL + it * 16 + 4 * grp);
 #pragma unroll
       for (int e = 0; e < 4; ++e) off[it][e] = sOff[it * 16 + 4 * grp + e];
     }
@@ -572,31 +584,32 @@ void dp_chain_kernel(FwdArgs p) {
     for (int dt = 0; dt < NDT; ++dt) fkt[dt].load(st + W.oK + ltK, dt);
     sched_fence();
 
-    // ---- O = diag(e^{G_loc}) Q H + P Up for the readout rows, written out
-#pragma unroll
-    for (int it = 0; it < NRT; ++it) {
-      f32x4_t z = fq[it].mma(f32x4_t{0.f, 0.f, 0.f, 0.f}, hq);
-      z = z * egl[it];
-      z = fp[it].mma(z, uq);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const long long o = off[it][e];
-        if (o >= 0) {
-          if (p.out_f32)
-            static_cast<float*>(p.out)[o + v0 + vw + col] = z[e];
-          else
-            static_cast<bf16_t*>(p.out)[o + v0 + vw + col] = __builtin_bit_cast(bf16_t, (__bf16)z[e]);
-        }
-      }
-    }
-    // ---- H = e^{G_last} H + Kn^T Us
+    // ---- H = e^{G_last} H + Kn^T Us;  O = Z + P Up for the readout rows, written
+    //      out (rows of missing readouts go to this lane's slot of the sink)
     const float dec = sEG[C - 1];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       if constexpr (GATED) hacc[dt] = hacc[dt] * dec;
       hacc[dt] = fkt[dt].mma(hacc[dt], usq);
-      hq[dt] = to_h4(hacc[dt]);
     }
+#pragma unroll
+    for (int it = 0; it < NRT; ++it) z[it] = fp[it].mma(z[it], uq);
+    if (p.out_f32) {
+#pragma unroll
+      for (int it = 0; it < NRT; ++it)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          *(off[it][e] >= 0 ? static_cast<float*>(p.out) + off[it][e] + ocol : sink) = z[it][e];
+    } else {
+#pragma unroll
+      for (int it = 0; it < NRT; ++it)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          *(off[it][e] >= 0 ? static_cast<bf16_t*>(p.out) + off[it][e] + ocol : reinterpret_cast<bf16_t*>(sink)) =
+              __builtin_bit_cast(bf16_t, (__bf16)z[it][e]);
+    }
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) hq[dt] = to_h4(hacc[dt]);
     if (c + 1 < nc) block_sync_lds();  // X(c + 1)
   }
 

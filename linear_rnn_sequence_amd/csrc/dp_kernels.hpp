@@ -69,6 +69,7 @@ struct FwdArgs {
   float* fstate;    // nullptr: final state not returned
   void* wsT;        // [B*H*nc][C][C]: T diag(beta), operand type (fp16 / fp32)
   float2* wsS;      // [B*H*nc][C]: (1/|k|, G)
+  float* sink;      // one slot per scan lane for outputs of rows that are not read out
   int N;            // L * n_h sub-steps per head
   int B, H, L, n_h, dv, nc, RT, nvb, asym;
   int out_f32;      // 1: out is fp32 whatever the input type
