@@ -31,9 +31,26 @@
 // are instruction immediates.
 #pragma once
 
+#include <utility>
+
 #include "dp_device.hpp"
 
 namespace dp {
+
+// Operands that are only read by rows (T diag(beta), Q, P) use, when their
+// width W is a multiple of 32, the "fragment" layout: the 16-byte granule
+// (t, g) of a row holds columns 32t + 4g .. 32t + 4g + 3 and 32t + 16 + 4g ..
+// 32t + 16 + 4g + 3 -- exactly the eight values one lane of group g feeds a
+// 32-deep MFMA step -- and granule (t, g) of all rows forms block 4t + g.  A
+// fragment is then one 16-byte read, and 16 lanes read 256 contiguous bytes.
+// The keys (read by rows and transposed) stay in plain blocks of 8 columns.
+__host__ __device__ constexpr bool frag_layout(int W) { return W % 32 == 0; }
+// byte offset, inside a row's granules, of column c (fragment layout)
+__host__ __device__ constexpr int frag_col_byte(int c) {
+  return ((c >> 4) & 1) * 8 + (c & 3) * 2;
+}
+// block index of column c (fragment layout)
+__host__ __device__ constexpr int frag_col_block(int c) { return 4 * (c >> 5) + ((c & 15) >> 2); }
 
 // Byte offsets of one chunk's operand block (workspace and LDS stage alike).
 struct Chunk16Layout {
@@ -202,7 +219,14 @@ __global__ __launch_bounds__(256) void dp_prep_kernel(FwdArgs p) {
   }
   for (int idx = tid; idx < QV; idx += 256) {
     const int q = idx / RT, i = idx % RT;
-    st16(wsc + W.oQ + (q * RT + i) * 16, ld16(sQ + i * LDK + q * 8));
+    if constexpr (frag_layout(DK)) {  // block q = 4t + g: columns 32t + 4g.. and 32t + 16 + 4g..
+      const int c0 = 32 * (q >> 2) + 4 * (q & 3);
+      const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(sQ + i * LDK + c0);
+      const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(sQ + i * LDK + c0 + 16);
+      st16(wsc + W.oQ + (q * RT + i) * 16, u32x4_t{lo[0], lo[1], hi[0], hi[1]});
+    } else {
+      st16(wsc + W.oQ + (q * RT + i) * 16, ld16(sQ + i * LDK + q * 8));
+    }
   }
 
   // 5. M = strict_tril(diag(beta) (E o Kn Kn^T)) on MFMA (lower tiles only)
@@ -236,8 +260,9 @@ __global__ __launch_bounds__(256) void dp_prep_kernel(FwdArgs p) {
       const int j = j0 + e;
       pv[e] = (j <= loc) ? acc[e] * (p.g != nullptr ? expf(gl - sG[j]) : 1.f) : 0.f;
     }
-    st4(reinterpret_cast<f16_t*>(wsc + W.oP + ((j0 >> 3) * RT + i) * 16 + (j0 & 7) * 2), pv[0], pv[1], pv[2],
-        pv[3]);
+    const int pblk = frag_layout(C) ? frag_col_block(j0) : (j0 >> 3);
+    const int pbyte = frag_layout(C) ? frag_col_byte(j0) : (j0 & 7) * 2;
+    st4(reinterpret_cast<f16_t*>(wsc + W.oP + (pblk * RT + i) * 16 + pbyte), pv[0], pv[1], pv[2], pv[3]);
   }
   __syncthreads();
 
@@ -288,7 +313,7 @@ __global__ __launch_bounds__(256) void dp_prep_kernel(FwdArgs p) {
     float f[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int j = q * 8 + e;
+      const int j = frag_layout(C) ? 32 * (q >> 2) + 4 * (q & 3) + (e & 3) + 16 * (e >> 2) : q * 8 + e;
       f[e] = ((j >> 4) > (i >> 4)) ? 0.f : sTf[i * LDA + j] * sB[j];
     }
     st_vec16(reinterpret_cast<f16_t*>(wsc + W.oT + (q * C + i) * 16), f);
@@ -334,22 +359,29 @@ __host__ __device__ constexpr int tr_block(int dt) {
 }
 
 // A fragments of a 16 x K operand from block-major rows (K = W of the region).
-template <int ROWS, int K>
+template <int ROWS, int K, bool FRAG>
 struct RowFrags {
   f16x8_t f[K / 32 > 0 ? K / 32 : 1];
   f16x4_t r;  // the last 16 of the contraction when K % 32 == 16
-  // `off`: LDS byte offset of this 16-row tile (lane part included).  It is
-  // made opaque so that the two halves of each fragment -- one block apart --
-  // are the closest loads on their base register and pair into ds_read2_b64.
+  // `off`: LDS byte offset of this 16-row tile, lane part included (lane_frag
+  // for the fragment layout, lane_row otherwise).  In the plain layout the two
+  // halves of a fragment are one block apart; each half gets its own opaque
+  // base so that they stay two ds_read_b64 (a paired ds_read2 of this pattern
+  // is bank-conflicted four ways).
   __device__ __forceinline__ void load(const unsigned char* lds, uint32_t off) {
-    asm volatile("" : "+v"(off));
-    const unsigned char* base = lds + off;
+    if constexpr (FRAG) {
+      asm volatile("" : "+v"(off));
 #pragma unroll
-    for (int t = 0; t < K / 32; ++t) {
-      const unsigned char* p = base + 4 * t * ROWS * 16;
-      f[t] = cat8(*reinterpret_cast<const f16x4_t*>(p), *reinterpret_cast<const f16x4_t*>(p + ROWS * 16));
+      for (int t = 0; t < K / 32; ++t) f[t] = *reinterpret_cast<const f16x8_t*>(lds + off + 4 * t * ROWS * 16);
+    } else {
+      uint32_t off1 = off + ROWS * 16;
+      asm volatile("" : "+v"(off), "+v"(off1));
+#pragma unroll
+      for (int t = 0; t < K / 32; ++t)
+        f[t] = cat8(*reinterpret_cast<const f16x4_t*>(lds + off + 4 * t * ROWS * 16),
+                    *reinterpret_cast<const f16x4_t*>(lds + off1 + 4 * t * ROWS * 16));
+      if constexpr (K % 32 == 16) r = *reinterpret_cast<const f16x4_t*>(lds + off + ((K - 16) / 8) * ROWS * 16);
     }
-    if constexpr (K % 32 == 16) r = *reinterpret_cast<const f16x4_t*>(base + ((K - 16) / 8) * ROWS * 16);
   }
   __device__ __forceinline__ f32x4_t mma(f32x4_t acc, const f16x4_t* b) const {
 #pragma unroll
@@ -358,6 +390,11 @@ struct RowFrags {
     return acc;
   }
 };
+// Lane part of a row read in the fragment layout: lane (n, g) reads row n of block g.
+__device__ __forceinline__ int lane_frag(int rows) {
+  const int l = threadIdx.x & 63;
+  return (l >> 4) * rows * 16 + (l & 15) * 16;
+}
 
 // A fragments of the transpose (16 x K) of block-major rows 0..K-1, columns
 // d0..d0+15 of a region W columns wide.
@@ -394,8 +431,31 @@ __device__ __forceinline__ void wait_vmcnt() {
 // keep the scheduler from moving instructions across this point
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
+// f(std::integral_constant<int, I>{}) for I = 0 .. N-1, each with a compile-time index
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (N > 0) static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Step schedule of the pipelined chain body (see dp_chain_kernel): phase
+// starts S2, S3, S4 and end NS; a tile conversion for step k runs in
+// iteration min(k + LA + DL, next phase start + LA).
+template <int S2, int S3, int S4, int NS, int LA, int DL>
+__host__ __device__ constexpr int chain_conv_iter(int k) {
+  const int nxt = k < S2 ? S2 : (k < S3 ? S3 : (k < S4 ? S4 : NS));
+  return (k + LA + DL) < (nxt + LA) ? (k + LA + DL) : (nxt + LA);
+}
+
+// Copy wavefronts per dp_chain_kernel workgroup: one wavefront issues about one
+// 1 KB direct-to-LDS copy per ~60 cycles, so the copies of a chunk are split.
+constexpr int kChainCopyWaves = 2;
+
 template <int DK, int C, int NWC, int NRT, bool GATED>
-__global__ __launch_bounds__(64 * (NWC + 1)) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(64 * (NWC + kChainCopyWaves)) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void dp_chain_kernel(FwdArgs p) {
   constexpr int RT = 16 * NRT, BV = 16 * NWC;
   constexpr int NCT = C / 16, NDT = DK / 16;
@@ -406,7 +466,11 @@ void dp_chain_kernel(FwdArgs p) {
   constexpr int NIV = VB / 1024 > 0 ? VB / 1024 : 1;  // copies per value tile
   constexpr int VPI = VB >= 1024 ? 64 : VB / 16;      // lanes per value copy
   constexpr int NI = NIB + NIV;
-  static_assert(NI < 64, "copies per chunk exceed the vmcnt range");
+  constexpr int NCW = kChainCopyWaves;
+  // copies of copy wavefront w: indices m = w, w + NCW, .. of the NI copies
+  constexpr int NI0 = (NI + NCW - 1) / NCW, NI1 = NI / NCW;
+  static_assert(NCW == 2, "two copy wavefronts");
+  static_assert(NI0 < 64, "copies per chunk exceed the vmcnt range");
   static_assert(VB % 16 == 0 && (VB < 1024 || VB % 1024 == 0), "value tile");
 
   extern __shared__ __align__(16) unsigned char smem[];
@@ -423,25 +487,32 @@ void dp_chain_kernel(FwdArgs p) {
   const int nc = p.nc;
   const unsigned char* wsh = static_cast<const unsigned char*>(p.wsT) + (long long)bh * nc * W.bytes;
 
-  if (wave == NWC) {
-    // ================================================================ copy wave
-    // Source offset of each lane in each copy of the chunk block: LDS slot
-    // (physical block, row slot) of a tile region holds logical block
-    // blk_pos(physical) and row slot ^ 8 for odd logical blocks.
+  if (wave >= NWC) {
+    // =============================================================== copy waves
+    // Source offset of each lane in each copy of the chunk block: in the
+    // plain-layout tiles, LDS slot (physical block, row slot) holds logical
+    // block blk_pos(physical) and row slot ^ 8 for odd logical blocks; the
+    // fragment-layout tiles and the scalars are copied as they are.
+    const int cw = wave - NWC;
     int soff[NIB];
 #pragma unroll
     for (int m = 0; m < NIB; ++m) {
       const int o = 1024 * m + 16 * lane;
       int src = o;
       auto region = [&](int start, int rows, int cols) {
-        if (o >= start && o < start + rows * cols * 2) {
+        if (!frag_layout(cols) && o >= start && o < start + rows * cols * 2) {
           const int rel = o - start, pb = rel / (rows * 16), rs = (rel / 16) % rows;
           const int q = blk_pos(pb, cols);
           src = start + q * rows * 16 + (rs ^ (8 * (q & 1))) * 16;
         }
       };
       region(W.oT, C, C);
-      region(W.oK, C, DK);
+      // the keys keep the plain layout whatever their width (they are also read transposed)
+      if (o >= W.oK && o < W.oK + C * DK * 2) {
+        const int rel = o - W.oK, pb = rel / (C * 16), rs = (rel / 16) % C;
+        const int q = blk_pos(pb, DK);
+        src = W.oK + q * C * 16 + (rs ^ (8 * (q & 1))) * 16;
+      }
       region(W.oQ, RT, DK);
       region(W.oP, RT, C);
       soff[m] = src;
@@ -453,10 +524,11 @@ void dp_chain_kernel(FwdArgs p) {
       const unsigned char* src = wsh + (long long)c * W.bytes;
 #pragma unroll
       for (int m = 0; m < NIB; ++m)
-        if (1024 * m + 16 * lane < W.bytes) dma16(src + soff[m], st + 1024 * m);
+        if (m % NCW == cw && 1024 * m + 16 * lane < W.bytes) dma16(src + soff[m], st + 1024 * m);
       // value tile: logical block q = columns v0 + 8q.., rows = sub-steps
 #pragma unroll
       for (int m = 0; m < NIV; ++m) {
+        if ((NIB + m) % NCW != cw) continue;
         const int o = 1024 * m + 16 * lane;
         const int pb = o / (C * 16), rs = (o / 16) % C;
         const int q = blk_pos(pb, BV);
@@ -467,11 +539,18 @@ void dp_chain_kernel(FwdArgs p) {
         if (lane < VPI) dma16(vp + row * p.dv + 8 * q, st + W.bytes + 1024 * m);
       }
     };
+    // wait until this wavefront's copies of the previous chunk have landed
+    auto wait_prev = [&]() {
+      if (cw == 0)
+        wait_vmcnt<NI0>();
+      else
+        wait_vmcnt<NI1>();
+    };
     if (nc > 0) {
       issue(0);
       if (nc > 1) {
         issue(1);
-        wait_vmcnt<NI>();
+        wait_prev();
       } else {
         wait_vmcnt<0>();
       }
@@ -480,7 +559,7 @@ void dp_chain_kernel(FwdArgs p) {
     for (int c = 0; c + 1 < nc; ++c) {
       if (c + 2 < nc) {
         issue(c + 2);  // into the stage chunk c - 1 used
-        wait_vmcnt<NI>();  // chunk c + 1 has landed
+        wait_prev();   // chunk c + 1 has landed
       } else {
         wait_vmcnt<0>();
       }
@@ -492,7 +571,10 @@ void dp_chain_kernel(FwdArgs p) {
   // ==================================================================== consumers
   const int col = lane & 15, grp = lane >> 4;
   const int vw = 16 * wave;  // this wavefront's columns inside the block
-  const int lrT = lane_row<C>(C), lrK = lane_row<DK>(C), lrQ = lane_row<DK>(RT), lrP = lane_row<C>(RT);
+  const int lrK = lane_row<DK>(C);
+  const int lrT = frag_layout(C) ? lane_frag(C) : lane_row<C>(C);
+  const int lrQ = frag_layout(DK) ? lane_frag(RT) : lane_row<DK>(RT);
+  const int lrP = frag_layout(C) ? lane_frag(RT) : lane_row<C>(RT);
   const int ltK = lane_tr<DK>(C), ltV = lane_tr<BV>(C);
   const int ocol = v0 + vw + col;  // output column of this lane
   float* const sink = p.sink + ((long long)f * NWC + wave) * 64 + lane;
@@ -507,6 +589,171 @@ void dp_chain_kernel(FwdArgs p) {
     }
     hq[dt] = to_h4(hacc[dt]);
   }
+  if constexpr (DK % 32 == 0 && C % 32 == 0) {
+    // Software-pipelined chunk body.  The MFMA steps of a chunk run in a fixed
+    // order -- Kn H (X), Q H (readout), T X (Up), P Up (readout), Kn^T Us
+    // (state) -- and the A fragment of step i is read LA steps ahead.  The
+    // tile conversions that feed later products run DL steps after the MFMA
+    // that completes the tile, or at the start of the product that needs
+    // them, whichever comes first.  The state's fp16 copy holds -H (the
+    // readout scale carries the sign back), so X = V + e^G (Kn (-H)).
+    constexpr int KST = DK / 32, CST = C / 32;
+    constexpr int S1 = NCT * KST, S2 = S1 + NRT * KST, S3 = S2 + NCT * CST, S4 = S3 + NRT * CST;
+    constexpr int NS = S4 + NDT * CST;
+    constexpr int LA = 6, DL = 4;
+    f16x4_t hqn[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) hqn[dt] = to_h4(-hacc[dt]);
+    if (nc > 0) block_sync_lds();  // X(0)
+    for (int c = 0; c < nc; ++c) {
+      const uint32_t so = (uint32_t)((c % kChainStages) * STAGE);
+      const unsigned char* st = smem + so;
+      const float* sEG = reinterpret_cast<const float*>(st + W.oS + W.oEG);
+      const float* sEL = reinterpret_cast<const float*>(st + W.oS + W.oEL);
+      const float* sEGL = reinterpret_cast<const float*>(st + W.oS + W.oEGL);
+      const long long* sOff = reinterpret_cast<const long long*>(st + W.oS + W.oOff);
+      // per-tile LDS offsets, opaque so that fragment halves pair on their own base
+      uint32_t oK[NCT], oK1[NCT], oT[NCT], oQ[NRT], oP[NRT];
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        oK[ct] = so + W.oK + lrK + ct * 256;
+        oK1[ct] = oK[ct] + C * 16;  // second half of each key fragment: one block on
+        oT[ct] = so + W.oT + lrT + ct * 256;
+        asm volatile("" : "+v"(oK[ct]), "+v"(oK1[ct]), "+v"(oT[ct]));
+      }
+#pragma unroll
+      for (int it = 0; it < NRT; ++it) {
+        oQ[it] = so + W.oQ + lrQ + it * 256;
+        oP[it] = so + W.oP + lrP + it * 256;
+        asm volatile("" : "+v"(oQ[it]), "+v"(oP[it]));
+      }
+      // small operands
+      f32x4_t vf[NCT], eg[NCT], el[NCT], negl[NRT];
+      long long off[NRT][4];
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        // V[16 ct + 4 grp + e][vw + col] (bf16) in accumulator layout
+        const s16x4_t vr = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_t*)(st + W.bytes + ltV + tr_block<BV>(wave) * C * 16 + ct * 16 * 16));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vf[ct][e] = __uint_as_float((uint32_t)(uint16_t)vr[e] << 16);
+        if constexpr (GATED) {
+          eg[ct] = *reinterpret_cast<const f32x4_t*>(sEG + ct * 16 + 4 * grp);
+          el[ct] = *reinterpret_cast<const f32x4_t*>(sEL + ct * 16 + 4 * grp);
+        }
+      }
+#pragma unroll
+      for (int it = 0; it < NRT; ++it) {
+        negl[it] = -*reinterpret_cast<const f32x4_t*>(sEGL + it * 16 + 4 * grp);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) off[it][e] = sOff[it * 16 + 4 * grp + e];
+      }
+      const float dec = sEG[C - 1];
+
+      f16x8_t ring[LA];
+      f32x4_t accX[NCT], accU[NCT], z[NRT];
+      f16x4_t xq[NCT], uq[NCT], usq[NCT];
+      auto load_frag = [&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        f16x8_t fr;
+        if constexpr (i < S1) {
+          constexpr int ko = 4 * (i % KST) * C * 16;
+          fr = cat8(*reinterpret_cast<const f16x4_t*>(smem + oK[i / KST] + ko),
+                    *reinterpret_cast<const f16x4_t*>(smem + oK1[i / KST] + ko));
+        } else if constexpr (i < S2) {
+          constexpr int j = i - S1;
+          fr = *reinterpret_cast<const f16x8_t*>(smem + oQ[j / KST] + 4 * (j % KST) * RT * 16);
+        } else if constexpr (i < S3) {
+          constexpr int j = i - S2;
+          fr = *reinterpret_cast<const f16x8_t*>(smem + oT[j / CST] + 4 * (j % CST) * C * 16);
+        } else if constexpr (i < S4) {
+          constexpr int j = i - S3;
+          fr = *reinterpret_cast<const f16x8_t*>(smem + oP[j / CST] + 4 * (j % CST) * RT * 16);
+        } else {
+          constexpr int j = i - S4;
+          const unsigned char* q = st + W.oK + ltK + tr_block<DK>(j / CST) * C * 16 + 32 * (j % CST) * 16;
+          fr = cat8(__builtin_bit_cast(f16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)q)),
+                    __builtin_bit_cast(f16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(q + 256))));
+        }
+        ring[i % LA] = fr;
+      };
+      auto mfma_step = [&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        const f16x8_t a = ring[i % LA];
+        if constexpr (i < S1) {
+          constexpr int ct = i / KST, t = i % KST;
+          accX[ct] = mfma32h(a, cat8(hqn[2 * t], hqn[2 * t + 1]), t == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : accX[ct]);
+        } else if constexpr (i < S2) {
+          constexpr int j = i - S1, it = j / KST, t = j % KST;
+          z[it] = mfma32h(a, cat8(hqn[2 * t], hqn[2 * t + 1]), t == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : z[it]);
+        } else if constexpr (i < S3) {
+          constexpr int j = i - S2, ct = j / CST, t = j % CST;
+          accU[ct] = mfma32h(a, cat8(xq[2 * t], xq[2 * t + 1]), t == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : accU[ct]);
+        } else if constexpr (i < S4) {
+          constexpr int j = i - S3, it = j / CST, t = j % CST;
+          z[it] = mfma32h(a, cat8(uq[2 * t], uq[2 * t + 1]), z[it]);
+        } else {
+          constexpr int j = i - S4, dt = j / CST, t = j % CST;
+          if constexpr (GATED && t == 0) hacc[dt] = hacc[dt] * dec;
+          hacc[dt] = mfma32h(a, cat8(usq[2 * t], usq[2 * t + 1]), hacc[dt]);
+        }
+      };
+      auto conv = [&](auto kc) {
+        constexpr int k = decltype(kc)::value;
+        if constexpr (k < S1) {
+          if constexpr (k % KST == KST - 1) {
+            constexpr int ct = k / KST;
+            if constexpr (GATED)
+              xq[ct] = to_h4(vf[ct] + eg[ct] * accX[ct]);  // accX = -Kn H
+            else
+              xq[ct] = to_h4(vf[ct] + accX[ct]);
+          }
+        } else if constexpr (k < S2) {
+          if constexpr ((k - S1) % KST == KST - 1) z[(k - S1) / KST] = z[(k - S1) / KST] * negl[(k - S1) / KST];
+        } else if constexpr (k < S3) {
+          if constexpr ((k - S2) % CST == CST - 1) {
+            constexpr int ct = (k - S2) / CST;
+            uq[ct] = to_h4(accU[ct]);
+            if constexpr (GATED)
+              usq[ct] = to_h4(accU[ct] * el[ct]);
+            else
+              usq[ct] = uq[ct];
+          }
+        } else if constexpr (k < S4) {
+          if constexpr ((k - S3) % CST == CST - 1) {
+            constexpr int it = (k - S3) / CST;
+            // rows of missing readouts go to this lane's slot of the sink
+            if (p.out_f32) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                *(off[it][e] >= 0 ? static_cast<float*>(p.out) + off[it][e] + ocol : sink) = z[it][e];
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                *(off[it][e] >= 0 ? static_cast<bf16_t*>(p.out) + off[it][e] + ocol : reinterpret_cast<bf16_t*>(sink)) =
+                    __builtin_bit_cast(bf16_t, (__bf16)z[it][e]);
+            }
+          }
+        } else {
+          if constexpr ((k - S4) % CST == CST - 1) hqn[(k - S4) / CST] = to_h4(-hacc[(k - S4) / CST]);
+        }
+      };
+      static_for<NS + LA + DL>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        // conversions due in this iteration: steps k in [i - LA - DL, i - LA]
+        static_for<DL + 1>([&](auto wc) {
+          constexpr int k = i - LA - DL + decltype(wc)::value;
+          if constexpr (k >= 0 && k < NS) {
+            if constexpr (chain_conv_iter<S2, S3, S4, NS, LA, DL>(k) == i) conv(std::integral_constant<int, k>{});
+          }
+        });
+        if constexpr (i >= LA && i - LA < NS) mfma_step(std::integral_constant<int, i - LA>{});
+        if constexpr (i < NS) load_frag(std::integral_constant<int, i>{});
+        sched_fence();
+      });
+      if (c + 1 < nc) block_sync_lds();  // X(c + 1)
+    }
+  } else {
   if (nc > 0) block_sync_lds();  // X(0)
   for (int c = 0; c < nc; ++c) {
     const uint32_t so = (uint32_t)((c % kChainStages) * STAGE);
@@ -517,8 +764,8 @@ void dp_chain_kernel(FwdArgs p) {
     const long long* sOff = reinterpret_cast<const long long*>(st + W.oS + W.oOff);
 
     // ---- operands of X and of the readout's Q H, all issued before the first product
-    RowFrags<C, DK> fk[NCT];
-    RowFrags<RT, DK> fq[NRT];
+    RowFrags<C, DK, false> fk[NCT];
+    RowFrags<RT, DK, frag_layout(DK)> fq[NRT];
     s16x4_t vr[NCT];
     f32x4_t eg[NCT], egl[NRT];
 #pragma unroll
@@ -533,7 +780,7 @@ void dp_chain_kernel(FwdArgs p) {
       fq[it].load(smem, so + W.oQ + lrQ + it * 256);
       egl[it] = *reinterpret_cast<const f32x4_t*>(sEGL + it * 16 + 4 * grp);
     }
-    RowFrags<C, C> ft[NCT];
+    RowFrags<C, C, frag_layout(C)> ft[NCT];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) ft[ct].load(smem, so + W.oT + lrT + ct * 256);
     sched_fence();
@@ -552,7 +799,7 @@ void dp_chain_kernel(FwdArgs p) {
 #pragma unroll
     for (int it = 0; it < NRT; ++it) z[it] = fq[it].mma(f32x4_t{0.f, 0.f, 0.f, 0.f}, hq) * egl[it];
     // operands of the readout's P Up, issued while X and Up are computed
-    RowFrags<RT, C> fp[NRT];
+    RowFrags<RT, C, frag_layout(C)> fp[NRT];
     long long off[NRT][4];
 #pragma unroll
     for (int it = 0; it < NRT; ++it) {
@@ -611,6 +858,8 @@ void dp_chain_kernel(FwdArgs p) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) hq[dt] = to_h4(hacc[dt]);
     if (c + 1 < nc) block_sync_lds();  // X(c + 1)
+  }
+
   }
 
   if (p.fstate != nullptr) {

@@ -1196,7 +1196,7 @@ hipError_t launch_chain_g(const FwdArgs& a, hipStream_t st) {
   static const bool attr = allow_big_lds(reinterpret_cast<const void*>(&dp_chain_kernel<DK, C, NWC, NRT, GATED>));
   (void)attr;
   const long long nwg = (long long)a.B * a.H * a.nvb;
-  hipLaunchKernelGGL((dp_chain_kernel<DK, C, NWC, NRT, GATED>), dim3((unsigned)nwg), dim3(64 * (NWC + 1)),
+  hipLaunchKernelGGL((dp_chain_kernel<DK, C, NWC, NRT, GATED>), dim3((unsigned)nwg), dim3(64 * (NWC + kChainCopyWaves)),
                      chain_lds_bytes(DK, C, 16 * NRT, 16 * NWC), st, a);
   return hipGetLastError();
 }
