@@ -419,8 +419,13 @@ struct TrFrags {
   }
 };
 
-__device__ __forceinline__ void dma16(const void* src, unsigned char* lds_dst) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
+// One direct-to-LDS copy: each lane moves 16 bytes from `src` to LDS byte
+// address lds + 16 * lane.  Written as inline assembly: completion is tracked
+// by the caller's explicit vmcnt waits (the compiler's own tracking of the
+// builtin inserts a full vmcnt(0) wait whenever it reuses an address register,
+// which would serialize the copy pipeline).
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
 }
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding)
 template <int N>
@@ -519,52 +524,60 @@ void dp_chain_kernel(FwdArgs p) {
     }
     const bf16_t* vp = static_cast<const bf16_t*>(p.v) + v0;
     const long long tok0 = (long long)b * p.L * p.H + h;
-    auto issue = [&](int c) {
-      unsigned char* st = smem + (c % kChainStages) * STAGE;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)smem;  // LDS byte address of the ring
+    // copies of chunk c issued by copy wavefront CW: index m = CW, CW + NCW, ..
+    auto issue = [&](auto cwc, int c) {
+      constexpr int CW = decltype(cwc)::value;
+      const uint32_t st = lds0 + (uint32_t)((c % kChainStages) * STAGE);
       const unsigned char* src = wsh + (long long)c * W.bytes;
-#pragma unroll
-      for (int m = 0; m < NIB; ++m)
-        if (m % NCW == cw && 1024 * m + 16 * lane < W.bytes) dma16(src + soff[m], st + 1024 * m);
+      static_for<NIB>([&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        if constexpr (m % NCW == CW) {
+          if (1024 * m + 16 * lane < W.bytes) dma16(src + soff[m], st + 1024 * m);
+        }
+      });
       // value tile: logical block q = columns v0 + 8q.., rows = sub-steps
-#pragma unroll
-      for (int m = 0; m < NIV; ++m) {
-        if ((NIB + m) % NCW != cw) continue;
-        const int o = 1024 * m + 16 * lane;
-        const int pb = o / (C * 16), rs = (o / 16) % C;
-        const int q = blk_pos(pb, BV);
-        int s = c * C + (rs ^ (8 * (q & 1)));
-        s = s < p.N ? s : p.N - 1;  // rows past the end: any valid row (their beta is 0)
-        const int t = fastdiv(s, p.nh_magic, p.nh_shift);
-        const long long row = (tok0 + (long long)t * p.H) * p.n_h + (s - t * p.n_h);
-        if (lane < VPI) dma16(vp + row * p.dv + 8 * q, st + W.bytes + 1024 * m);
+      static_for<NIV>([&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        if constexpr ((NIB + m) % NCW == CW) {
+          const int o = 1024 * m + 16 * lane;
+          const int pb = o / (C * 16), rs = (o / 16) % C;
+          const int q = blk_pos(pb, BV);
+          int s = c * C + (rs ^ (8 * (q & 1)));
+          s = s < p.N ? s : p.N - 1;  // rows past the end: any valid row (their beta is 0)
+          const int t = fastdiv(s, p.nh_magic, p.nh_shift);
+          const long long row = (tok0 + (long long)t * p.H) * p.n_h + (s - t * p.n_h);
+          if (lane < VPI) dma16(vp + row * p.dv + 8 * q, st + W.bytes + 1024 * m);
+        }
+      });
+    };
+    auto run = [&](auto cwc) {
+      constexpr int CW = decltype(cwc)::value;
+      constexpr int NMINE = CW == 0 ? NI0 : NI1;  // copies per chunk of this wavefront
+      if (nc > 0) {
+        issue(cwc, 0);
+        if (nc > 1) {
+          issue(cwc, 1);
+          wait_vmcnt<NMINE>();
+        } else {
+          wait_vmcnt<0>();
+        }
+        block_sync_lds();  // X(0)
+      }
+      for (int c = 0; c + 1 < nc; ++c) {
+        if (c + 2 < nc) {
+          issue(cwc, c + 2);  // into the stage chunk c - 1 used
+          wait_vmcnt<NMINE>();  // chunk c + 1 has landed
+        } else {
+          wait_vmcnt<0>();
+        }
+        block_sync_lds();  // X(c + 1)
       }
     };
-    // wait until this wavefront's copies of the previous chunk have landed
-    auto wait_prev = [&]() {
-      if (cw == 0)
-        wait_vmcnt<NI0>();
-      else
-        wait_vmcnt<NI1>();
-    };
-    if (nc > 0) {
-      issue(0);
-      if (nc > 1) {
-        issue(1);
-        wait_prev();
-      } else {
-        wait_vmcnt<0>();
-      }
-      block_sync_lds();  // X(0)
-    }
-    for (int c = 0; c + 1 < nc; ++c) {
-      if (c + 2 < nc) {
-        issue(c + 2);  // into the stage chunk c - 1 used
-        wait_prev();   // chunk c + 1 has landed
-      } else {
-        wait_vmcnt<0>();
-      }
-      block_sync_lds();  // X(c + 1)
-    }
+    if (cw == 0)
+      run(std::integral_constant<int, 0>{});
+    else
+      run(std::integral_constant<int, 1>{});
     return;
   }
 
