@@ -40,6 +40,7 @@ def parse():
     ap.add_argument("--also", default="c3b",
                     help="comma-separated extra workloads timed in the same run ('' = none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode-step timing")
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU sample (0: auto)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run device-to-device copies of BYTES (counter calibration)")
@@ -228,6 +229,56 @@ def time_gpu(w, steps, warmup):
                 pre_ms=pre_ms, plan=plan, inputs=inp)
 
 
+def decode_bytes(B, H, n_h, dk, dv, elem=2):
+    """Algorithmic bytes of one decode step: the fp32 state read and written,
+    plus q, k, v (elem bytes each), beta and out per head."""
+    return B * H * (2 * dk * dv * 4 + (n_h * (dk + dv) + dk + dv) * elem + n_h * 4)
+
+
+def time_decode(B, H, n_h, dk, dv, tokens=128, reps=5):
+    """Recurrent decode: `tokens` consecutive one-token launches on a resident
+    state (the pages' protocol decodes 128 tokens after a prefill), timed with
+    HIP events on the launch stream; best of `reps` runs."""
+    import torch
+
+    import linear_rnn_sequence_amd as dp
+    from linear_rnn_sequence_amd.inputs import WORKLOADS, make
+
+    dev = torch.device("cuda:0")
+    w = WORKLOADS["c3"].scaled(B=B, H=H, L=tokens, n_h=n_h, dk=dk, dv=dv)
+    inp = make(w)
+    toks = [{n: inp[n][:, t].contiguous().to(dev) for n in ("q", "k", "v", "beta")}
+            for t in range(tokens)]
+    state = torch.zeros(B, H, dk, dv, dtype=torch.float32, device=dev)
+    out = torch.empty(B, H, dv, dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def run():
+        for x in toks:
+            dp.decode(x["q"], x["k"], x["v"], x["beta"], state, out=out, stream=stream)
+
+    run()
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    us = 1e3 * best / tokens
+    nbytes = decode_bytes(B, H, n_h, dk, dv)
+    return {"workload": f"decode: B={B} H={H} n_h={n_h} dk={dk} dv={dv} bf16, fp32 state, "
+                        f"{tokens} one-token launches",
+            "us_per_token": us, "tokens_per_s": B * 1e6 / us,
+            "roofline": {"kernel": "dp_decode_kernel", "bound": "hbm",
+                         "achieved": nbytes / (us * 1e3), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": nbytes / (us * 1e3) / HBM_PEAK_GBS,
+                         "alg_bytes_per_launch": nbytes}}
+
+
 # ---------------------------------------------------------------- CPU baseline
 
 def cpu_baseline(w, inp, nheads, min_seconds=10.0, max_pass_seconds=30.0, max_passes=100):
@@ -387,6 +438,10 @@ def main():
         del r2
     if also:
         line["also"] = also
+    if not a.no_decode:
+        # the pages' decode protocol (batch 1) and a serving-size batch, head shape of c3
+        line["decode"] = {"b1": time_decode(1, 16, 3, 128, 128),
+                          "b64": time_decode(64, 16, 3, 128, 128)}
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, r["inputs"], a.cpu_heads)
     else:

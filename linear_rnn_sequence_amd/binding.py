@@ -23,6 +23,7 @@ EXPORTS = (
     "dp_fwd_f32", "dp_fwd_bf16", "dp_fwd_wk_f32", "dp_fwd_wk_bf16",
     "dp_fwd_ex_f32", "dp_fwd_ex_bf16",
     "dp_osdn_precond_f32", "dp_osdn_precond_bf16",
+    "dp_decode_f32", "dp_decode_bf16",
 )
 
 _lib = None
@@ -68,6 +69,10 @@ def load() -> ctypes.CDLL:
         for name in ("dp_osdn_precond_f32", "dp_osdn_precond_bf16"):
             getattr(lib, name).restype = _I
             getattr(lib, name).argtypes = pre
+        dec = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _P]
+        for name in ("dp_decode_f32", "dp_decode_bf16"):
+            getattr(lib, name).restype = _I
+            getattr(lib, name).argtypes = dec
         _lib = lib
     return _lib
 
@@ -212,3 +217,41 @@ def osdn_precond(k, beta, *, eta: float = 3e-3, dmin: float = 0.5, dmax: float =
             _stream(stream))
     _check(rc, f"dp_osdn_precond_{suf}")
     return kt, d_state
+
+
+def decode(q, k, v, beta, state, g=None, *, kt=None, out=None, out_dtype=None, stream=None):
+    """One recurrent decode step through libdp, updating `state` in place.
+
+    q [B,H,dk], k [B,H,n_h,dk], v [B,H,n_h,dv] (float32 or bfloat16, one
+    dtype), beta [B,H,n_h] f32, g [B,H] f32 or None, kt (write keys, shape of
+    k) or None, state [B,H,dk,dv] f32 (H_{t-1} in, H_t out).  Returns out
+    [B,H,dv] in the input dtype or out_dtype (torch.float32).
+    """
+    if q.dim() != 3 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("expected q[B,H,dk], k[B,H,n_h,dk], v[B,H,n_h,dv]")
+    B, H, dk = q.shape
+    n_h, dv = k.shape[2], v.shape[3]
+    dev, dt = q.device, q.dtype
+    suf = _suffix(dt)
+    _need(k, "k", dt, (B, H, n_h, dk), dev)
+    _need(kt, "kt", dt, (B, H, n_h, dk), dev)
+    _need(v, "v", dt, (B, H, n_h, dv), dev)
+    _need(beta, "beta", torch.float32, (B, H, n_h), dev)
+    _need(g, "g", torch.float32, (B, H), dev)
+    _need(state, "state", torch.float32, (B, H, dk, dv), dev)
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    if out is not None and out_dtype is None:
+        out_dtype = out.dtype
+    odt = dt if out_dtype is None else out_dtype
+    if odt not in (dt, torch.float32):
+        raise TypeError(f"out_dtype must be {dt} or torch.float32")
+    if out is None:
+        out = torch.empty(B, H, dv, dtype=odt, device=dev)
+    _need(out, "out", odt, (B, H, dv), dev)
+    flags = OUT_F32 if (odt == torch.float32 and dt != torch.float32) else 0
+    fn = getattr(load(), f"dp_decode_{suf}")
+    rc = fn(_ptr(q), _ptr(k), _ptr(kt), _ptr(v), _ptr(beta), _ptr(g), n_h, B, H, dk, dv,
+            _ptr(out), _ptr(state), flags, _stream(stream))
+    _check(rc, f"dp_decode_{suf}")
+    return out

@@ -294,6 +294,54 @@ int fwd_impl(int elem, const void* q, const void* k, const void* kt, const void*
   return e == hipSuccess ? DP_OK : DP_EHIP;
 }
 
+hipError_t dispatch_decode(int elem, int dk, const dp::DecodeArgs& a, hipStream_t st) {
+  if (elem == 4) {
+    switch (dk) {
+      case 16: return dp_launch_decode_f32_16(a, st);
+      case 32: return dp_launch_decode_f32_32(a, st);
+      case 64: return dp_launch_decode_f32_64(a, st);
+      case 128: return dp_launch_decode_f32_128(a, st);
+    }
+  } else {
+    switch (dk) {
+      case 16: return dp_launch_decode_bf16_16(a, st);
+      case 32: return dp_launch_decode_bf16_32(a, st);
+      case 64: return dp_launch_decode_bf16_64(a, st);
+      case 128: return dp_launch_decode_bf16_128(a, st);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+int decode_impl(int elem, const void* q, const void* k, const void* kt, const void* v,
+                const float* beta, const float* g, int n_h, int B, int H, int dk, int dv,
+                void* out, float* state, int flags, dp_stream stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || beta == nullptr || out == nullptr ||
+      state == nullptr)
+    return DP_EINVAL;
+  if (n_h <= 0 || B <= 0 || H <= 0 || dk <= 0 || dv <= 0) return DP_EINVAL;
+  if ((flags & ~DP_OUT_F32) != 0) return DP_EINVAL;
+  if (!dim_ok(dk) || !dim_ok(dv)) return DP_ENOTSUP;
+  if (n_h > 64) return DP_ENOTSUP;
+  if ((long long)B * H * 8 > (long long)INT_MAX) return DP_ENOTSUP;  // grid size
+  dp::DecodeArgs a;
+  a.q = q;
+  a.k = k;
+  a.kt = kt;
+  a.v = v;
+  a.beta = beta;
+  a.g = g;
+  a.out = out;
+  a.state = state;
+  a.B = B;
+  a.H = H;
+  a.n_h = n_h;
+  a.dv = dv;
+  a.out_f32 = (elem == 4 || (flags & DP_OUT_F32) != 0) ? 1 : 0;
+  const hipError_t e = dispatch_decode(elem, dk, a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DP_OK : DP_EHIP;
+}
+
 int precond_impl(int elem, const void* k, const float* beta, int B, int H, int L, int dk,
                  float eta, float dmin, float dmax, float eps, float* d_state, void* kt,
                  dp_stream stream) {
@@ -431,6 +479,18 @@ int dp_osdn_precond_bf16(const void* k, const float* beta, int B, int H, int L, 
                          float eta, float dmin, float dmax, float eps, float* d_state,
                          void* kt, dp_stream stream) {
   return precond_impl(2, k, beta, B, H, L, dk, eta, dmin, dmax, eps, d_state, kt, stream);
+}
+
+int dp_decode_f32(const float* q, const float* k, const float* kt, const float* v,
+                  const float* beta, const float* g, int n_h, int B, int H, int dk, int dv,
+                  float* out, float* state, int flags, dp_stream stream) {
+  return decode_impl(4, q, k, kt, v, beta, g, n_h, B, H, dk, dv, out, state, flags, stream);
+}
+
+int dp_decode_bf16(const void* q, const void* k, const void* kt, const void* v,
+                   const float* beta, const float* g, int n_h, int B, int H, int dk, int dv,
+                   void* out, float* state, int flags, dp_stream stream) {
+  return decode_impl(2, q, k, kt, v, beta, g, n_h, B, H, dk, dv, out, state, flags, stream);
 }
 
 }  // extern "C"

@@ -1093,6 +1093,7 @@ inline bool allow_big_lds(const void* fn) {
 }  // namespace dp
 
 #include "dp_fwd16.hpp"
+#include "dp_decode.hpp"
 
 namespace dp {
 
@@ -1273,7 +1274,8 @@ hipError_t launch_precond_dk(const PrecondArgs& a, hipStream_t st) {
 #define DP_DECLARE_LAUNCHERS(TNAME, DK)                                                        \
   hipError_t dp_launch_fwd_##TNAME##_##DK(const dp::FwdArgs& a, int C, int BV, int lds_scan,   \
                                           int stages, hipStream_t st);                         \
-  hipError_t dp_launch_precond_##TNAME##_##DK(const dp::PrecondArgs& a, hipStream_t st);
+  hipError_t dp_launch_precond_##TNAME##_##DK(const dp::PrecondArgs& a, hipStream_t st);   \
+  hipError_t dp_launch_decode_##TNAME##_##DK(const dp::DecodeArgs& a, hipStream_t st);
 
 #define DP_DEFINE_LAUNCHERS(T, TNAME, DK)                                                      \
   hipError_t dp_launch_fwd_##TNAME##_##DK(const dp::FwdArgs& a, int C, int BV, int lds_scan,   \
@@ -1282,4 +1284,7 @@ hipError_t launch_precond_dk(const PrecondArgs& a, hipStream_t st) {
   }                                                                                            \
   hipError_t dp_launch_precond_##TNAME##_##DK(const dp::PrecondArgs& a, hipStream_t st) {      \
     return dp::launch_precond_dk<T, DK>(a, st);                                                \
+  }                                                                                            \
+  hipError_t dp_launch_decode_##TNAME##_##DK(const dp::DecodeArgs& a, hipStream_t st) {        \
+    return dp::launch_decode_dk<T, DK>(a, st);                                                 \
   }

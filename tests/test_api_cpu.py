@@ -174,3 +174,41 @@ def test_binding_rejects_bad_tensors_on_cpu():
         dp.fwd(q.double(), k, v, beta)
     with pytest.raises(ValueError):
         dp.fwd(q, k[:, :3], v, beta)
+
+
+@pytest.mark.parametrize("suffix", ["bf16", "f32"])
+def test_decode_validation_errors_before_hip(lib, suffix):
+    E = dp.binding
+    f = getattr(lib, f"dp_decode_{suffix}")
+
+    def call(q=FAKE, k=FAKE, kt=None, v=FAKE, beta=FAKE, g=None, n_h=2, B=1, H=1, dk=16, dv=16,
+             out=FAKE, state=FAKE, flags=0):
+        return f(q, k, kt, v, beta, g, n_h, B, H, dk, dv, out, state, flags, None)
+
+    assert call(q=None) == E.DP_EINVAL
+    assert call(k=None) == E.DP_EINVAL
+    assert call(v=None) == E.DP_EINVAL
+    assert call(beta=None) == E.DP_EINVAL
+    assert call(out=None) == E.DP_EINVAL
+    assert call(state=None) == E.DP_EINVAL
+    assert call(n_h=0) == E.DP_EINVAL
+    assert call(B=0) == E.DP_EINVAL
+    assert call(flags=8) == E.DP_EINVAL
+    assert call(dk=24) == E.DP_ENOTSUP
+    assert call(dv=256) == E.DP_ENOTSUP
+    assert call(n_h=65) == E.DP_ENOTSUP
+
+
+def test_decode_binding_rejects_bad_tensors_on_cpu():
+    import torch
+    q = torch.zeros(2, 3, 16)
+    k = torch.zeros(2, 3, 2, 16)
+    v = torch.zeros(2, 3, 2, 16)
+    beta = torch.zeros(2, 3, 2)
+    st = torch.zeros(2, 3, 16, 16)
+    with pytest.raises(TypeError):
+        dp.decode(q, k, v, beta, st.double())
+    with pytest.raises(ValueError):
+        dp.decode(q, k, v[:, :2], beta, st)
+    with pytest.raises(ValueError):
+        dp.decode(q, k, v, beta, st.transpose(2, 3))

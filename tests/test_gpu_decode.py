@@ -1,0 +1,154 @@
+"""GPU parity of the recurrent decode step (one token's n_h sub-steps against a
+resident fp32 state) with the fp64 oracle.
+
+The oracle is the sequential forward itself: one decode step from state S is
+its one-token forward with initial state S, and a prefill of L0 tokens
+followed by decode steps is its forward over the whole sequence.  Errors are
+max|x_gpu - x_oracle| / RMS(x_oracle) per tensor, bounded by 1e-4 (fp32
+inputs) and 2e-2 (bf16 inputs and outputs).
+"""
+import numpy as np
+import pytest
+import torch
+
+import linear_rnn_sequence_amd as dp
+import oracle
+from linear_rnn_sequence_amd.inputs import WORKLOADS, make
+from parity import TOL, f64, gpu_forward, rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    dp.load()  # raises when libdp.so is missing: no silent fallback
+
+
+def token(inp, name, t):
+    """Token t of a token-major [B, L, H, ...] input as a contiguous [B, H, ...] tensor."""
+    x = inp[name]
+    return None if x is None else x[:, t].contiguous()
+
+
+def decode_token(inp, t, state, kt=None, out_dtype=None):
+    """One GPU decode step on token t of `inp` (state on the device, updated in place)."""
+    dev = lambda x: None if x is None else x.cuda()
+    out = dp.decode(dev(token(inp, "q", t)), dev(token(inp, "k", t)), dev(token(inp, "v", t)),
+                    dev(token(inp, "beta", t)), state, g=dev(token(inp, "g", t)),
+                    kt=None if kt is None else dev(kt[:, t].contiguous()), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return out
+
+
+def check(pairs, tol, label):
+    for name, (x, ref) in pairs.items():
+        e = rel_err(x, ref)
+        say(f"  {label} {name}: err {e:.3e} (tol {tol:.0e})")
+        assert np.all(np.isfinite(x)), f"{label} {name}: non-finite values"
+        assert e <= tol, f"{label} {name}: err {e:.3e} > {tol}"
+
+
+# (workload, overrides): head dims 16..128, n_h 1..4, gate, asymmetric write key
+STEP = [
+    ("c1", dict(B=2, H=3)),
+    ("c2", dict(B=3, H=5, n_h=4, dv=32)),
+    ("c3", dict(B=2, H=4)),
+    ("c4", dict(B=2, H=3, dk=32, dv=128)),
+    ("c5", dict(B=2, H=3, n_h=2, dk=64, dv=16)),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("name,kw", STEP, ids=[f"{n}-{i}" for i, (n, _) in enumerate(STEP)])
+def test_decode_step_matches_oracle(name, kw, dtype):
+    w = WORKLOADS[name].scaled(L=1, dtype=dtype, **kw)
+    say(f"case decode-step {name} {kw} dtype={dtype} n_h={w.n_h} dk={w.dk} dv={w.dv}")
+    inp = make(w)
+    gen = torch.Generator().manual_seed(7)
+    s0 = torch.randn(w.B, w.H, w.dk, w.dv, generator=gen) * 0.3
+    kt = None
+    if w.asym:  # any write keys will do for one step: the keys scaled per coordinate
+        dscale = 0.5 + 1.5 * torch.rand(w.dk, generator=gen)
+        kt = (inp["k"].float() * dscale).to(inp["k"].dtype).contiguous()
+    st = s0.clone().cuda()
+    out = decode_token(inp, 0, st, kt=kt, out_dtype=torch.float32 if w.out_f32 else None)
+    oo, fo = oracle.fwd(inp["q"], inp["k"], inp["v"], inp["beta"], g=inp["g"], kt=kt, h0=s0)
+    check(dict(out=(f64(out), oo[:, 0]), state=(f64(st), fo)), TOL[dtype], f"{name}/{dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("name", ["c3", "c4", "c5"])
+def test_prefill_then_decode(name, dtype):
+    """Chunkwise prefill of L0 tokens, then one decode launch per token: every
+    decoded output and the final state equal the oracle's forward over the
+    whole sequence."""
+    L0, K = 157, 12
+    w = WORKLOADS[name].scaled(B=1, H=3, L=L0 + K, dtype=dtype)
+    say(f"case prefill+decode {name} dtype={dtype} L0={L0} K={K} n_h={w.n_h}")
+    inp = make(w)
+    kt = None
+    if w.asym:
+        kt1, _ = oracle.precond(inp["k"][:, :, :, 0, :].contiguous(), inp["beta"][..., 0].contiguous())
+        kt = torch.from_numpy(kt1).to(inp["k"].dtype)[:, :, :, None, :].contiguous()
+    pre = {n: (x[:, :L0].contiguous() if isinstance(x, torch.Tensor) and n not in ("h0",) else x)
+           for n, x in inp.items()}
+    _, st = gpu_forward(pre, kt=None if kt is None else kt[:, :L0].contiguous())
+    odt = torch.float32 if w.out_f32 else None
+    outs = [decode_token(inp, L0 + i, st, kt=kt, out_dtype=odt) for i in range(K)]
+    oo, fo = oracle.fwd(inp["q"], inp["k"], inp["v"], inp["beta"], g=inp["g"], kt=kt, h0=inp["h0"])
+    got = torch.stack([o.cpu() for o in outs], dim=1)
+    check(dict(out=(f64(got), oo[:, L0:]), state=(f64(st), fo)), TOL[dtype], f"{name}/{dtype}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_gate_zero_and_beta_zero(dtype):
+    """g = 0 erases the state before the sub-steps; beta = 0 sub-steps are
+    identities, so the readout is H^T q of the gated state alone."""
+    w = WORKLOADS["c4"].scaled(B=1, H=4, L=1, dk=64, dv=64, dtype=dtype)
+    inp = make(w)
+    inp["g"][0, 0, :2] = 0.0
+    inp["beta"][0, 0, 2:] = 0.0
+    s0 = torch.randn(1, 4, 64, 64, generator=torch.Generator().manual_seed(3))
+    st = s0.clone().cuda()
+    out = decode_token(inp, 0, st, out_dtype=torch.float32)
+    oo, fo = oracle.fwd(inp["q"], inp["k"], inp["v"], inp["beta"], g=inp["g"], h0=s0)
+    check(dict(out=(f64(out), oo[:, 0]), state=(f64(st), fo)), TOL[dtype], f"gate0/{dtype}")
+    # heads 2 and 3: no update at all, the state is only scaled by g
+    g = inp["g"][0, 0, 2:].view(2, 1, 1)
+    assert torch.allclose(st[0, 2:].cpu(), s0[0, 2:] * g, rtol=1e-6, atol=1e-7)
+
+
+def test_decode_max_sub_steps():
+    """n_h = 64 (the largest supported), fp32."""
+    w = WORKLOADS["c2"].scaled(B=1, H=2, L=1, n_h=64, dk=128, dv=64, dtype="f32")
+    inp = make(w)
+    s0 = torch.randn(1, 2, 128, 64, generator=torch.Generator().manual_seed(5)) * 0.1
+    st = s0.clone().cuda()
+    out = decode_token(inp, 0, st)
+    oo, fo = oracle.fwd(inp["q"], inp["k"], inp["v"], inp["beta"], h0=s0)
+    check(dict(out=(f64(out), oo[:, 0]), state=(f64(st), fo)), TOL["f32"], "nh64")
+
+
+def test_decode_full_size_batch():
+    """A serving-size batch (B=64, H=16, dk=dv=128, n_h=3, bf16) in one launch,
+    checked on every head against the oracle."""
+    w = WORKLOADS["c3"].scaled(B=64, L=1)
+    inp = make(w)
+    s0 = torch.randn(w.B, w.H, w.dk, w.dv, generator=torch.Generator().manual_seed(11)) * 0.2
+    st = s0.clone().cuda()
+    out = decode_token(inp, 0, st)
+    oo, fo = oracle.fwd(inp["q"], inp["k"], inp["v"], inp["beta"], h0=s0)
+    check(dict(out=(f64(out), oo[:, 0]), state=(f64(st), fo)), TOL["bf16"], "B64")
+
+
+def test_decode_errors():
+    q = torch.zeros(1, 1, 24, device="cuda")
+    k = torch.zeros(1, 1, 1, 24, device="cuda")
+    v = torch.zeros(1, 1, 1, 16, device="cuda")
+    b = torch.zeros(1, 1, 1, device="cuda")
+    s = torch.zeros(1, 1, 24, 16, device="cuda")
+    with pytest.raises(dp.DPError) as ei:
+        dp.decode(q, k, v, b, s)  # dk = 24 is not supported
+    assert ei.value.code == -2
