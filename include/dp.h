@@ -80,9 +80,13 @@ const char* dp_status_str(int status);
  * Workspace bytes needed by dp_fwd_* / dp_fwd_wk_* for these sizes.
  * elem_bytes: 4 for the f32 path, 2 for the bf16 path.  Writes *bytes and
  * returns DP_OK, or a negative status (sizes validated as for dp_fwd_*).
- * The workspace holds, per chunk of every head, the matrix T*diag(beta)
- * (chunk x chunk, type T) and two floats per sub-step (1/|k| and the
- * chunk-local cumulative log-gate).
+ * The workspace holds, per chunk of every head: on the fp32 path and the
+ * bf16 write-key path, the matrix T*diag(beta) (chunk x chunk) and two floats
+ * per sub-step (1/|k| and the chunk-local cumulative log-gate); on the bf16
+ * symmetric path, one operand block (T*diag(beta), the unit keys, the readout
+ * queries and their masked scores in fp16, then the per-sub-step decay
+ * factors and the readout rows' output offsets), plus one float per lane of
+ * the chunk-scan launch.
  */
 int dp_fwd_workspace_size(int n_h, int B, int H, int L, int dk, int dv, int chunk,
                           int elem_bytes, size_t* bytes);
@@ -92,7 +96,7 @@ int dp_fwd_workspace_size(int n_h, int B, int H, int L, int dk, int dv, int chun
  * tuning; nothing is launched).  asym: 0 symmetric, 1 write-key variant.
  * info[0] = BV, the value columns per scan workgroup (16, 32 or 64)
  * info[1] = scan workgroups (B*H*dv/BV), info[2] = UT workgroups (chunks),
- * info[3] = scan LDS bytes, info[4] = UT LDS bytes, info[5] = readout rows
+ * info[3] = scan LDS bytes, info[4] = prep / UT LDS bytes, info[5] = readout rows
  * per chunk (padded to 16).  Returns DP_OK or a validation status.
  */
 int dp_fwd_launch_info(int n_h, int B, int H, int L, int dk, int dv, int chunk, int elem_bytes,
@@ -186,6 +190,28 @@ int dp_osdn_precond_f32(const float* k, const float* beta, int B, int H, int L, 
 int dp_osdn_precond_bf16(const void* k, const float* beta, int B, int H, int L, int dk,
                          float eta, float dmin, float dmax, float eps, float* d_state,
                          void* kt, dp_stream stream);
+
+/*
+ * Phase-1 variants (OSDN notes sec. 2.6 and sec. 2.7), same scan and layouts:
+ *   r      [B, L, H] f32  APF retention gate of d (sec. 2.6, Sec.4.4), or NULL
+ *                         (= 1, exactly dp_osdn_precond_*):
+ *                           d_{t+1} = P[ r_t d_t + step(d_t) ]
+ *                         the step is computed from d_t before the retention;
+ *   flags  0, or DP_PRECOND_BETA_FREE: the beta-free step of the 1.3B
+ *          configuration (sec. 2.7, App.B/C), eta (1 - <d_t, s>) / max(|k|^2, eps) s,
+ *          i.e. the step above with b = 1 (the forward's write still uses beta);
+ *   P      the box [dmin, dmax]; here dmin may be <= 0 and the bounds may be
+ *          -inf / +inf (no projection), as long as dmin <= dmax.
+ * Errors: as dp_osdn_precond_*, plus DP_EINVAL for an unknown flag.
+ */
+#define DP_PRECOND_BETA_FREE 1
+
+int dp_osdn_precond_ex_f32(const float* k, const float* beta, const float* r, int flags, int B,
+                           int H, int L, int dk, float eta, float dmin, float dmax, float eps,
+                           float* d_state, float* kt, dp_stream stream);
+int dp_osdn_precond_ex_bf16(const void* k, const float* beta, const float* r, int flags, int B,
+                            int H, int L, int dk, float eta, float dmin, float dmax, float eps,
+                            float* d_state, void* kt, dp_stream stream);
 
 /*
  * One recurrent decode step (DeltaProduct notes sec. 2.2 Eq.(3) and the

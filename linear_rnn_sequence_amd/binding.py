@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(HERE, "libdp.so")
 
 DP_OK, DP_EINVAL, DP_ENOTSUP, DP_EWORKSPACE, DP_EHIP = 0, -1, -2, -3, -4
 STAGE_UT, STAGE_SCAN, STAGE_ALL, OUT_F32 = 1, 2, 3, 4
+PRECOND_BETA_FREE = 1
 
 # every symbol include/dp.h declares
 EXPORTS = (
@@ -24,6 +25,7 @@ EXPORTS = (
     "dp_fwd_ex_f32", "dp_fwd_ex_bf16",
     "dp_osdn_precond_f32", "dp_osdn_precond_bf16",
     "dp_decode_f32", "dp_decode_bf16",
+    "dp_osdn_precond_ex_f32", "dp_osdn_precond_ex_bf16",
 )
 
 _lib = None
@@ -69,6 +71,10 @@ def load() -> ctypes.CDLL:
         for name in ("dp_osdn_precond_f32", "dp_osdn_precond_bf16"):
             getattr(lib, name).restype = _I
             getattr(lib, name).argtypes = pre
+        pre_ex = [_P, _P, _P, _I, _I, _I, _I, _I, _F, _F, _F, _F, _P, _P, _P]
+        for name in ("dp_osdn_precond_ex_f32", "dp_osdn_precond_ex_bf16"):
+            getattr(lib, name).restype = _I
+            getattr(lib, name).argtypes = pre_ex
         dec = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _P]
         for name in ("dp_decode_f32", "dp_decode_bf16"):
             getattr(lib, name).restype = _I
@@ -192,11 +198,14 @@ def fwd(q, k, v, beta, g=None, *, chunk: int = 64, h0=None, kt=None, out=None,
 
 
 def osdn_precond(k, beta, *, eta: float = 3e-3, dmin: float = 0.5, dmax: float = 2.0,
-                 eps: float = 1e-6, d_state=None, kt=None, stream=None):
+                 eps: float = 1e-6, d_state=None, kt=None, r=None, beta_aware: bool = True,
+                 stream=None):
     """OSDN phase 1 through libdp: k [B,L,H,dk], beta [B,L,H] f32.
 
     d_state [B,H,dk] f32 is d_1 on entry (default ones) and d_{L+1} on return.
-    Returns (kt [B,L,H,dk], d_state).
+    r [B,L,H] f32: optional APF retention of d; beta_aware=False: the beta-free
+    phase-1 step.  Either one selects dp_osdn_precond_ex_* (whose box may be
+    open: dmin = -inf, dmax = inf).  Returns (kt [B,L,H,dk], d_state).
     """
     if k.dim() != 4:
         raise ValueError("expected k[B,L,H,dk]")
@@ -204,6 +213,7 @@ def osdn_precond(k, beta, *, eta: float = 3e-3, dmin: float = 0.5, dmax: float =
     dev, dt = k.device, k.dtype
     suf = _suffix(dt)
     _need(beta, "beta", torch.float32, (B, L, H), dev)
+    _need(r, "r", torch.float32, (B, L, H), dev)
     if not k.is_contiguous():
         raise ValueError("k must be contiguous")
     if d_state is None:
@@ -212,10 +222,17 @@ def osdn_precond(k, beta, *, eta: float = 3e-3, dmin: float = 0.5, dmax: float =
     if kt is None:
         kt = torch.empty(B, L, H, dk, dtype=dt, device=dev)
     _need(kt, "kt", dt, (B, L, H, dk), dev)
-    fn = getattr(load(), f"dp_osdn_precond_{suf}")
-    rc = fn(_ptr(k), _ptr(beta), B, H, L, dk, eta, dmin, dmax, eps, _ptr(d_state), _ptr(kt),
-            _stream(stream))
-    _check(rc, f"dp_osdn_precond_{suf}")
+    lib = load()
+    if r is None and beta_aware:
+        fn, name = getattr(lib, f"dp_osdn_precond_{suf}"), f"dp_osdn_precond_{suf}"
+        rc = fn(_ptr(k), _ptr(beta), B, H, L, dk, eta, dmin, dmax, eps, _ptr(d_state), _ptr(kt),
+                _stream(stream))
+    else:
+        fn, name = getattr(lib, f"dp_osdn_precond_ex_{suf}"), f"dp_osdn_precond_ex_{suf}"
+        flags = 0 if beta_aware else PRECOND_BETA_FREE
+        rc = fn(_ptr(k), _ptr(beta), _ptr(r), flags, B, H, L, dk, eta, dmin, dmax, eps,
+                _ptr(d_state), _ptr(kt), _stream(stream))
+    _check(rc, name)
     return kt, d_state
 
 

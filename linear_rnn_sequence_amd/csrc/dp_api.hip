@@ -342,23 +342,27 @@ int decode_impl(int elem, const void* q, const void* k, const void* kt, const vo
   return e == hipSuccess ? DP_OK : DP_EHIP;
 }
 
-int precond_impl(int elem, const void* k, const float* beta, int B, int H, int L, int dk,
-                 float eta, float dmin, float dmax, float eps, float* d_state, void* kt,
-                 dp_stream stream) {
+int precond_impl(int elem, const void* k, const float* beta, const float* ret, int flags,
+                 int B, int H, int L, int dk, float eta, float dmin, float dmax, float eps,
+                 float* d_state, void* kt, bool open_box, dp_stream stream) {
   if (k == nullptr || beta == nullptr || d_state == nullptr || kt == nullptr) return DP_EINVAL;
   if (B <= 0 || H <= 0 || L < 0) return DP_EINVAL;
+  if ((flags & ~DP_PRECOND_BETA_FREE) != 0) return DP_EINVAL;
   if (!dim_ok(dk)) return DP_ENOTSUP;
-  if (!(eps > 0.f) || !(dmin > 0.f) || !(dmin <= dmax) || !(eta == eta)) return DP_EINVAL;
+  if (!(eps > 0.f) || !(dmin <= dmax) || !(eta == eta)) return DP_EINVAL;
+  if (!open_box && !(dmin > 0.f)) return DP_EINVAL;
   if ((long long)B * H * (long long)L > (long long)1 << 40) return DP_ENOTSUP;
   if (L == 0) return DP_OK;
   dp::PrecondArgs a;
   a.k = k;
   a.beta = beta;
+  a.ret = ret;
   a.d = d_state;
   a.kt = kt;
   a.B = B;
   a.H = H;
   a.L = L;
+  a.beta_aware = (flags & DP_PRECOND_BETA_FREE) ? 0 : 1;
   a.eta = eta;
   a.dmin = dmin;
   a.dmax = dmax;
@@ -472,13 +476,29 @@ int dp_fwd_ex_bf16(const void* q, const void* k, const void* kt, const void* v,
 int dp_osdn_precond_f32(const float* k, const float* beta, int B, int H, int L, int dk,
                         float eta, float dmin, float dmax, float eps, float* d_state,
                         float* kt, dp_stream stream) {
-  return precond_impl(4, k, beta, B, H, L, dk, eta, dmin, dmax, eps, d_state, kt, stream);
+  return precond_impl(4, k, beta, nullptr, 0, B, H, L, dk, eta, dmin, dmax, eps, d_state, kt,
+                      false, stream);
 }
 
 int dp_osdn_precond_bf16(const void* k, const float* beta, int B, int H, int L, int dk,
                          float eta, float dmin, float dmax, float eps, float* d_state,
                          void* kt, dp_stream stream) {
-  return precond_impl(2, k, beta, B, H, L, dk, eta, dmin, dmax, eps, d_state, kt, stream);
+  return precond_impl(2, k, beta, nullptr, 0, B, H, L, dk, eta, dmin, dmax, eps, d_state, kt,
+                      false, stream);
+}
+
+int dp_osdn_precond_ex_f32(const float* k, const float* beta, const float* r, int flags, int B,
+                           int H, int L, int dk, float eta, float dmin, float dmax, float eps,
+                           float* d_state, float* kt, dp_stream stream) {
+  return precond_impl(4, k, beta, r, flags, B, H, L, dk, eta, dmin, dmax, eps, d_state, kt, true,
+                      stream);
+}
+
+int dp_osdn_precond_ex_bf16(const void* k, const float* beta, const float* r, int flags, int B,
+                            int H, int L, int dk, float eta, float dmin, float dmax, float eps,
+                            float* d_state, void* kt, dp_stream stream) {
+  return precond_impl(2, k, beta, r, flags, B, H, L, dk, eta, dmin, dmax, eps, d_state, kt, true,
+                      stream);
 }
 
 int dp_decode_f32(const float* q, const float* k, const float* kt, const float* v,

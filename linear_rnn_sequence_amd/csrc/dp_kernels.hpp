@@ -82,9 +82,11 @@ struct FwdArgs {
 struct PrecondArgs {
   const void* k;
   const float* beta;
+  const float* ret;  // [B, L, H] retention of d (APF), or nullptr
   float* d;
   void* kt;
   int B, H, L;
+  int beta_aware;    // 0: the beta-free phase-1 step
   float eta, dmin, dmax, eps;
 };
 
@@ -988,7 +990,10 @@ __global__ __launch_bounds__(64 * (NWC + NWP)) void dp_scan16_kernel(FwdArgs p) 
 }
 
 // ---------------------------------------------------------------------------
-// dp_precond_kernel: OSDN phase 1 (OSDN notes sec. 2.3-2.4, Alg.1).
+// dp_precond_kernel: OSDN phase 1 (OSDN notes sec. 2.3-2.4, Alg.1), with the
+// optional APF retention of d (sec. 2.6: d_{t+1} = P[r_t d_t + step]) and the
+// beta-free step of the 1.3B configuration (sec. 2.7: beta taken as 1 in the
+// phase-1 step only).
 // One wavefront holds 4 heads, 16 lanes per head, DK/16 coordinates per lane;
 // each head is a sequential scan over its L tokens.  Tokens are fetched PF at
 // a time, one block ahead of the block being processed.
@@ -1011,28 +1016,30 @@ __global__ __launch_bounds__(64) void dp_precond_kernel(PrecondArgs p) {
   for (int e = 0; e < EPL; ++e) d[e] = p.d[bh * DK + sl * EPL + e];
 
   auto tok_of = [&](int t) { return ((long long)b * p.L + t) * p.H + h; };
-  auto load_tok = [&](int t, float* kv, float& bv) {
+  auto load_tok = [&](int t, float* kv, float& bv, float& rv) {
     if (t < p.L) {
       const long long tok = tok_of(t);
       const T* src = kp + tok * DK + sl * EPL;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) kv[e] = to_f32(src[e]);
       bv = p.beta[tok];
+      rv = p.ret != nullptr ? p.ret[tok] : 1.f;
     } else {
 #pragma unroll
       for (int e = 0; e < EPL; ++e) kv[e] = 0.f;
       bv = 0.f;
+      rv = 1.f;
     }
   };
 
-  float kc[PF][EPL], bc[PF];
+  float kc[PF][EPL], bc[PF], rc[PF];
 #pragma unroll
-  for (int i = 0; i < PF; ++i) load_tok(i, kc[i], bc[i]);
+  for (int i = 0; i < PF; ++i) load_tok(i, kc[i], bc[i], rc[i]);
 
   for (int t0 = 0; t0 < p.L; t0 += PF) {
-    float kn[PF][EPL], bn[PF];
+    float kn[PF][EPL], bn[PF], rn[PF];
 #pragma unroll
-    for (int i = 0; i < PF; ++i) load_tok(t0 + PF + i, kn[i], bn[i]);
+    for (int i = 0; i < PF; ++i) load_tok(t0 + PF + i, kn[i], bn[i], rn[i]);
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
       const int t = t0 + i;
@@ -1059,16 +1066,18 @@ __global__ __launch_bounds__(64) void dp_precond_kernel(PrecondArgs p) {
         }
         ds = group_sum<16>(ds);
         ns = group_sum<16>(ns);
-        const float bt = clamp_keep_nan(bc[i], 0.f, 2.f);
+        const float bt = p.beta_aware ? clamp_keep_nan(bc[i], 0.f, 2.f) : 1.f;
         const float a = bt * ds;
         const float coef = p.eta * bt * (1.f - a) / fmaxf(ns, p.eps);
+        // retention scales d_t (exactly 1 without the gate), the step uses d_t
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) d[e] = clamp_keep_nan(fmaf(coef, s[e], d[e]), p.dmin, p.dmax);
+        for (int e = 0; e < EPL; ++e) d[e] = clamp_keep_nan(fmaf(coef, s[e], rc[i] * d[e]), p.dmin, p.dmax);
       }
     }
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
       bc[i] = bn[i];
+      rc[i] = rn[i];
 #pragma unroll
       for (int e = 0; e < EPL; ++e) kc[i][e] = kn[i][e];
     }

@@ -157,3 +157,12 @@ def select_state(t: torch.Tensor, heads, H: int) -> torch.Tensor:
         b, h = divmod(int(bh), H)
         parts.append(t[b:b + 1, h:h + 1])
     return torch.cat(parts, dim=1).contiguous()
+
+
+def retention(B: int, L: int, H: int, seed: int, bias: float = 3.0) -> torch.Tensor:
+    """Per-token, per-head retention values in (0, 1) for the preconditioner
+    (the APF gate is a sigmoid of a learned projection; here sigmoid(N(0,1) +
+    bias), so values sit near sigmoid(bias) ~ 0.95) -> ``[B, L, H]`` fp32."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(seed)
+    return torch.sigmoid(torch.randn(B, L, H, generator=gen, dtype=torch.float32) + bias)

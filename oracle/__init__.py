@@ -49,6 +49,11 @@ def _load():
                                        ctypes.c_int, ctypes.c_double, ctypes.c_double,
                                        ctypes.c_double, ctypes.c_double, _D, _D,
                                        ctypes.c_int]
+        lib.oracle_precond_ex.restype = ctypes.c_int
+        lib.oracle_precond_ex.argtypes = [_D, _D, _D, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                                          ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                                          _D, _D, ctypes.c_int]
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         _LIB = lib
@@ -130,22 +135,29 @@ def fwd_heads(q, k, v, beta, heads, g=None, kt=None, h0=None, nthreads=0):
     return out, fs
 
 
-def precond(k, beta, eta=3e-3, dmin=0.5, dmax=2.0, eps=1e-6, d0=None, nthreads=0):
+def precond(k, beta, eta=3e-3, dmin=0.5, dmax=2.0, eps=1e-6, d0=None, nthreads=0, r=None,
+            beta_aware=True):
     """OSDN phase 1 over ``k [B,L,H,dk]`` (raw keys) and ``beta [B,L,H]``.
 
-    Returns ``(kt [B,L,H,dk], d_final [B,H,dk])``; ``d0`` defaults to ones.
+    ``r [B,L,H]`` is the optional APF retention gate on d; ``beta_aware=False``
+    takes the beta-free phase-1 step.  Returns ``(kt [B,L,H,dk], d_final
+    [B,H,dk])``; ``d0`` defaults to ones.
     """
     k = _f64(k)
     beta = _f64(beta)
     if k.ndim != 4 or beta.shape != k.shape[:3]:
         raise ValueError("expected k[B,L,H,dk] and beta[B,L,H]")
     B, L, H, dk = k.shape
+    r = None if r is None else _f64(r)
+    if r is not None and r.shape != beta.shape:
+        raise ValueError("r must be [B,L,H]")
     d = np.ones((B, H, dk), np.float64) if d0 is None else _f64(d0).copy()
     if d.shape != (B, H, dk):
         raise ValueError("d0 must be [B,H,dk]")
     kt = np.zeros((B, L, H, dk), np.float64)
-    rc = _load().oracle_precond(_ptr(k), _ptr(beta), B, H, L, dk, float(eta), float(dmin),
-                                float(dmax), float(eps), _ptr(d), _ptr(kt), int(nthreads))
+    rc = _load().oracle_precond_ex(_ptr(k), _ptr(beta), _ptr(r), int(bool(beta_aware)), B, H, L,
+                                   dk, float(eta), float(dmin), float(dmax), float(eps), _ptr(d),
+                                   _ptr(kt), int(nthreads))
     if rc != 0:
-        raise RuntimeError(f"oracle_precond failed ({rc})")
+        raise RuntimeError(f"oracle_precond_ex failed ({rc})")
     return kt, d

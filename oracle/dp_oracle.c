@@ -226,10 +226,20 @@ int oracle_fwd_heads(const double* q, const double* k, const double* kt, const d
  * rule as the forward; beta [B, L, H] is clamped to [0, 2] as in the forward.
  * d_state [B, H, dk]: d_1 on entry, d_{L+1} on exit.  kt_out [B, L, H, dk]:
  * the write keys d_t * k_t, emitted BEFORE d is updated.
+ *
+ * Two variants the pages describe ride on the same scan:
+ *   - ret [B, L, H] (NULL: none): the APF retention gate r_t of [OSDN]
+ *     sec. 2.6 (Sec.4.4), which scales d_t inside the projection,
+ *     d_{t+1} = P[r_t d_t + step]; the step itself still uses d_t;
+ *   - beta_aware = 0: the beta-free phase-1 step of the 1.3B configuration
+ *     ([OSDN] sec. 2.7, App.B/C), eta (1 - <d_t, s_t>) s_t, i.e. the
+ *     beta-aware step with beta replaced by 1 (the division by
+ *     max(|k|^2, eps) is 1 for unit keys and is kept).
+ * The box [dmin, dmax] is the projection; dmin = -inf, dmax = +inf drop it.
  */
-int oracle_precond(const double* k, const double* beta, int B, int H, int L, int dk,
-                   double eta, double dmin, double dmax, double eps, double* d_state,
-                   double* kt_out, int nthreads)
+int oracle_precond_ex(const double* k, const double* beta, const double* ret, int beta_aware,
+                      int B, int H, int L, int dk, double eta, double dmin, double dmax,
+                      double eps, double* d_state, double* kt_out, int nthreads)
 {
     if (!k || !beta || !d_state || !kt_out) return -1;
     if (B < 0 || H < 0 || L < 0 || dk < 1) return -1;
@@ -253,6 +263,10 @@ int oracle_precond(const double* k, const double* beta, int B, int H, int L, int
             const size_t tok = ((size_t)b * L + t) * H + h;
             unit_key(k + tok * dk, dk, kh);
             const double bt = clampd(beta[tok], 0.0, 2.0);
+            /* the beta of the phase-1 step: the clamped beta, or 1 (beta-free) */
+            const double bu = beta_aware ? bt : 1.0;
+            /* retention of d_t (APF); 1 without the gate */
+            const double rt = ret ? ret[tok] : 1.0;
             /* emit the write key with the current d_t */
             double* ko = kt_out + tok * dk;
             for (int r = 0; r < dk; ++r) ko[r] = d[r] * kh[r];
@@ -263,13 +277,22 @@ int oracle_precond(const double* k, const double* beta, int B, int H, int L, int
                 n += s;
                 ds += d[r] * s;
             }
-            const double a = bt * ds;
+            const double a = bu * ds;
             const double nb = n > eps ? n : eps;
-            const double coef = eta * bt * (1.0 - a) / nb;
-            /* projected step onto the box [dmin, dmax]^dk */
-            for (int r = 0; r < dk; ++r) d[r] = clampd(d[r] + coef * (kh[r] * kh[r]), dmin, dmax);
+            const double coef = eta * bu * (1.0 - a) / nb;
+            /* retained d_t plus the step, projected onto the box [dmin, dmax]^dk */
+            for (int r = 0; r < dk; ++r) d[r] = clampd(rt * d[r] + coef * (kh[r] * kh[r]), dmin, dmax);
         }
         free(kh);
     }
     return bad ? -2 : 0;
+}
+
+/* The phase-1 scan as [OSDN] Alg.1 states it: no retention, beta-aware step. */
+int oracle_precond(const double* k, const double* beta, int B, int H, int L, int dk,
+                   double eta, double dmin, double dmax, double eps, double* d_state,
+                   double* kt_out, int nthreads)
+{
+    return oracle_precond_ex(k, beta, NULL, 1, B, H, L, dk, eta, dmin, dmax, eps, d_state,
+                             kt_out, nthreads);
 }

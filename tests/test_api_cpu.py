@@ -212,3 +212,23 @@ def test_decode_binding_rejects_bad_tensors_on_cpu():
         dp.decode(q, k, v[:, :2], beta, st)
     with pytest.raises(ValueError):
         dp.decode(q, k, v, beta, st.transpose(2, 3))
+
+
+def test_precond_ex_validation_errors_before_hip(lib):
+    E = dp.binding
+    f = lib.dp_osdn_precond_ex_f32
+
+    def call(k=FAKE, beta=FAKE, r=None, flags=0, B=1, H=1, L=4, dk=16, eta=3e-3, dmin=0.5,
+             dmax=2.0, eps=1e-6, d=FAKE, kt=FAKE):
+        return f(k, beta, r, flags, B, H, L, dk, eta, dmin, dmax, eps, d, kt, None)
+
+    assert call(k=None) == E.DP_EINVAL
+    assert call(flags=2) == E.DP_EINVAL
+    assert call(dmin=2.0, dmax=1.0) == E.DP_EINVAL
+    assert call(dmin=float("nan")) == E.DP_EINVAL
+    assert call(eps=0.0) == E.DP_EINVAL
+    assert call(dk=40) == E.DP_ENOTSUP
+    # the open box is allowed here (and only here)
+    assert call(L=0, dmin=float("-inf"), dmax=float("inf"), flags=1) == E.DP_OK
+    assert lib.dp_osdn_precond_f32(FAKE, FAKE, 1, 1, 0, 16, 3e-3, float("-inf"), 2.0, 1e-6,
+                                   FAKE, FAKE, None) == E.DP_EINVAL

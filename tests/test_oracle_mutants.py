@@ -38,17 +38,23 @@ MUTANTS = {
         "                for (size_t x = 0; x < (size_t)dk * dv; ++x) S[x] *= gt;\n            }"),
     "readout_before_last_substep": ("        /* o = H^T q after the token's last sub-step */",
                                     "        if (0) /* moved */"),
-    "phase1_missing_beta_in_a": ("const double a = bt * ds;", "const double a = ds;"),
+    "phase1_missing_beta_in_a": ("const double a = bu * ds;", "const double a = ds;"),
     "phase1_emit_after_update": (
         "            for (int r = 0; r < dk; ++r) ko[r] = d[r] * kh[r];\n",
         "            double* ko_late = ko;\n"),
-    "phase1_no_projection": ("d[r] = clampd(d[r] + coef * (kh[r] * kh[r]), dmin, dmax);",
-                             "d[r] = d[r] + coef * (kh[r] * kh[r]);"),
+    "phase1_no_projection": ("d[r] = clampd(rt * d[r] + coef * (kh[r] * kh[r]), dmin, dmax);",
+                             "d[r] = rt * d[r] + coef * (kh[r] * kh[r]);"),
+    "phase1_retention_ignored": ("const double rt = ret ? ret[tok] : 1.0;", "const double rt = 1.0;"),
+    "phase1_retention_on_the_step": (
+        "d[r] = clampd(rt * d[r] + coef * (kh[r] * kh[r]), dmin, dmax);",
+        "d[r] = clampd(rt * (d[r] + coef * (kh[r] * kh[r])), dmin, dmax);"),
+    "phase1_beta_free_keeps_beta": ("const double bu = beta_aware ? bt : 1.0;",
+                                    "const double bu = bt;"),
 }
 
 _EMIT_LATE = (
-    "            for (int r = 0; r < dk; ++r) d[r] = clampd(d[r] + coef * (kh[r] * kh[r]), dmin, dmax);\n",
-    "            for (int r = 0; r < dk; ++r) d[r] = clampd(d[r] + coef * (kh[r] * kh[r]), dmin, dmax);\n"
+    "            for (int r = 0; r < dk; ++r) d[r] = clampd(rt * d[r] + coef * (kh[r] * kh[r]), dmin, dmax);\n",
+    "            for (int r = 0; r < dk; ++r) d[r] = clampd(rt * d[r] + coef * (kh[r] * kh[r]), dmin, dmax);\n"
     "            for (int r = 0; r < dk; ++r) ko_late[r] = d[r] * kh[r];\n")
 
 _READOUT_FIX = (

@@ -533,3 +533,61 @@ def test_phase1_fixed_point_and_box_invariant():
     ratio = kt / np.where(np.abs(kh) > 1e-9, kh, np.nan)
     assert np.nanmin(ratio) >= 0.5 - 1e-12 and np.nanmax(ratio) <= 2 + 1e-12
     assert np.min(d) >= 0.5 and np.max(d) <= 2.0
+
+
+# ---------------------------------------------------------------- [OSDN] phase-1 variants
+
+
+def test_phase1_retention_closed_form():
+    """[OSDN] sec. 2.6 (APF, Sec.4.4): the retention gate scales d_t, the step still uses
+    d_t.  k = e1, constant beta and r: d_{t+1,1} = (r - eta b^2) d_t + eta b, so
+    d_{t,1} = d* + (r - eta b^2)^(t-1) (1 - d*), d* = eta b / (1 - r + eta b^2), while
+    inside the box; the other coordinates only decay, d_t = r^(t-1), until the
+    projection's floor dmin holds them (the gate does not reset d to 1)."""
+    eta, b, r, dk, L = 0.05, 0.9, 0.97, 3, 60
+    k = np.zeros((1, L, 1, dk))
+    k[..., 0] = 0.7
+    kt, d = oracle.precond(k, np.full((1, L, 1), b), eta=eta, r=np.full((1, L, 1), r))
+    t = np.arange(1, L + 1)
+    ds = eta * b / (1 - r + eta * b * b)
+    assert 0.5 < ds < 2.0
+    np.testing.assert_allclose(kt[0, :, 0, 0], ds + (r - eta * b * b) ** (t - 1) * (1 - ds),
+                               rtol=0, atol=1e-13)
+    np.testing.assert_allclose(d[0, 0, 0], ds + (r - eta * b * b) ** L * (1 - ds), atol=1e-13)
+    # coordinates with s = 0: pure decay, then the floor (the emitted key is 0 there)
+    np.testing.assert_allclose(d[0, 0, 1:], max(r ** L, 0.5), atol=0)
+    for T in (5, 20, 40):
+        _, dT = oracle.precond(k[:, :T], np.full((1, T, 1), b), eta=eta, r=np.full((1, T, 1), r))
+        np.testing.assert_allclose(dT[0, 0, 1:], max(r ** T, 0.5), rtol=1e-14, atol=0)
+    # r = 1 is exactly the gate-free scan
+    kt1, d1 = oracle.precond(k, np.full((1, L, 1), b), eta=eta, r=np.ones((1, L, 1)))
+    kt0, d0 = oracle.precond(k, np.full((1, L, 1), b), eta=eta)
+    assert np.array_equal(kt1, kt0) and np.array_equal(d1, d0)
+
+
+def test_phase1_beta_free_closed_form():
+    """[OSDN] sec. 2.7 (App.B/C, the 1.3B configuration): the phase-1 step carries no
+    beta, d_{t+1} = d_t + eta (1 - <d_t, k^2>) k^2 for unit keys.  With k = e1 the first
+    coordinate follows d_t = 1 + (1 - eta)^(t-1) (d_1 - 1) whatever beta is; with the box
+    dropped (dmin = -inf, dmax = inf) and a retention r it follows the affine map
+    d_{t+1} = (r - eta) d_t + eta below the old floor."""
+    rng = np.random.default_rng(21)
+    eta, dk, L = 0.08, 4, 50
+    k = np.zeros((1, L, 1, dk))
+    k[..., 0] = 3.0
+    beta = rng.uniform(0.05, 1.95, (1, L, 1))
+    d0 = np.full((1, 1, dk), 0.6)
+    kt, d = oracle.precond(k, beta, eta=eta, d0=d0, beta_aware=False)
+    t = np.arange(1, L + 1)
+    np.testing.assert_allclose(kt[0, :, 0, 0], 1 + (1 - eta) ** (t - 1) * (0.6 - 1), atol=1e-13)
+    np.testing.assert_allclose(d[0, 0, 1:], 0.6, atol=0)
+    # the beta-aware scan on the same input moves differently
+    kta, _ = oracle.precond(k, beta, eta=eta, d0=d0)
+    assert np.max(np.abs(kta - kt)) > 1e-3
+    # no box, retention 0.9: fixed point eta / (1 - r + eta) = 0.444.. < 0.5
+    r = 0.9
+    kt2, d2 = oracle.precond(k, beta, eta=eta, d0=d0, beta_aware=False, dmin=-np.inf,
+                             dmax=np.inf, r=np.full((1, L, 1), r))
+    fp = eta / (1 - r + eta)
+    np.testing.assert_allclose(kt2[0, :, 0, 0], fp + (r - eta) ** (t - 1) * (0.6 - fp), atol=1e-13)
+    np.testing.assert_allclose(d2[0, 0, 1:], 0.6 * r ** L, rtol=1e-13)
