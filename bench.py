@@ -34,8 +34,10 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the GPU's clocks ramp up over the first ~50 forwards of a cold run (~0.5 ms
+    # each at c3); 100 warm-up steps put the timed steps in the steady state
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="c3", help="c1, c2, c3, c3b, c4 or c5")
     ap.add_argument("--also", default="c3b",
                     help="comma-separated extra workloads timed in the same run ('' = none)")

@@ -44,6 +44,8 @@ int check_shape(const Shape& s) {
   const long long nc = (N + s.chunk - 1) / s.chunk;
   if ((long long)s.B * s.H * nc > (long long)INT_MAX) return DP_ENOTSUP;  // grid size
   if ((long long)s.B * s.H * 8 > (long long)INT_MAX) return DP_ENOTSUP;
+  // byte offsets within a chunk's readout rows are 32-bit: 64 rows x H dv x 4 bytes
+  if ((long long)s.H * s.dv * 64 * 4 > (long long)INT_MAX) return DP_ENOTSUP;
   return DP_OK;
 }
 

@@ -459,6 +459,10 @@ __host__ __device__ constexpr int chain_conv_iter(int k) {
 // 1 KB direct-to-LDS copy per ~60 cycles, so the copies of a chunk are split.
 constexpr int kChainCopyWaves = 2;
 
+// Third descriptor word of a raw (stride 0) gfx9 buffer resource: 32-bit data
+// format; the hardware then bounds each access by the resource's byte size.
+constexpr int kBufferDword3 = 0x00020000;
+
 template <int DK, int C, int NWC, int NRT, bool GATED>
 __global__ __launch_bounds__(64 * (NWC + kChainCopyWaves)) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void dp_chain_kernel(FwdArgs p) {
@@ -613,7 +617,20 @@ void dp_chain_kernel(FwdArgs p) {
     constexpr int KST = DK / 32, CST = C / 32;
     constexpr int S1 = NCT * KST, S2 = S1 + NRT * KST, S3 = S2 + NCT * CST, S4 = S3 + NRT * CST;
     constexpr int NS = S4 + NDT * CST;
-    constexpr int LA = 6, DL = 4;
+    constexpr int LA = 8, DL = 4;
+    // Readout row i of a chunk is token t0 + i: consecutive tokens, H dv
+    // elements apart in out.  Each chunk stores through a buffer resource
+    // based at its first row and bounded by its nrd rows, so this lane's
+    // element of row 16 it + 4 grp + e sits at a byte offset that is the
+    // same for every chunk, and the padding rows (from nrd on) fall outside
+    // the bound, where the hardware drops the store.
+    const int HD = p.H * p.dv;
+    const int es = p.out_f32 ? 4 : 2;
+    int voff[NRT][4];
+#pragma unroll
+    for (int it = 0; it < NRT; ++it)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) voff[it][e] = ((16 * it + 4 * grp + e) * HD + ocol) * es;
     f16x4_t hqn[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) hqn[dt] = to_h4(-hacc[dt]);
@@ -624,7 +641,12 @@ void dp_chain_kernel(FwdArgs p) {
       const float* sEG = reinterpret_cast<const float*>(st + W.oS + W.oEG);
       const float* sEL = reinterpret_cast<const float*>(st + W.oS + W.oEL);
       const float* sEGL = reinterpret_cast<const float*>(st + W.oS + W.oEGL);
-      const long long* sOff = reinterpret_cast<const long long*>(st + W.oS + W.oOff);
+      // readout rows i < nrd are the tokens t0 + i (uniform, scalar unit)
+      const int t0 = fastdiv(c * C, p.nh_magic, p.nh_shift);
+      const int nrd = fastdiv(min(c * C + C, p.N), p.nh_magic, p.nh_shift) - t0;
+      const long long rowbase = (((long long)b * p.L + t0) * p.H + h) * p.dv;
+      const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+          static_cast<char*>(p.out) + rowbase * es, 0, nrd * HD * es, kBufferDword3);
       // per-tile LDS offsets, opaque so that fragment halves pair on their own base
       uint32_t oK[NCT], oK1[NCT], oT[NCT], oQ[NRT], oP[NRT];
 #pragma unroll
@@ -642,7 +664,6 @@ void dp_chain_kernel(FwdArgs p) {
       }
       // small operands
       f32x4_t vf[NCT], eg[NCT], el[NCT], negl[NRT];
-      long long off[NRT][4];
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         // V[16 ct + 4 grp + e][vw + col] (bf16) in accumulator layout
@@ -658,8 +679,6 @@ void dp_chain_kernel(FwdArgs p) {
 #pragma unroll
       for (int it = 0; it < NRT; ++it) {
         negl[it] = -*reinterpret_cast<const f32x4_t*>(sEGL + it * 16 + 4 * grp);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) off[it][e] = sOff[it * 16 + 4 * grp + e];
       }
       const float dec = sEG[C - 1];
 
@@ -735,16 +754,16 @@ void dp_chain_kernel(FwdArgs p) {
         } else if constexpr (k < S4) {
           if constexpr ((k - S3) % CST == CST - 1) {
             constexpr int it = (k - S3) / CST;
-            // rows of missing readouts go to this lane's slot of the sink
+            // rows from nrd on are padding: out of the resource's bound, dropped
             if (p.out_f32) {
 #pragma unroll
               for (int e = 0; e < 4; ++e)
-                *(off[it][e] >= 0 ? static_cast<float*>(p.out) + off[it][e] + ocol : sink) = z[it][e];
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(z[it][e]), orsrc, voff[it][e], 0, 0);
             } else {
 #pragma unroll
               for (int e = 0; e < 4; ++e)
-                *(off[it][e] >= 0 ? static_cast<bf16_t*>(p.out) + off[it][e] + ocol : reinterpret_cast<bf16_t*>(sink)) =
-                    __builtin_bit_cast(bf16_t, (__bf16)z[it][e]);
+                __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (__bf16)z[it][e]), orsrc,
+                                                      voff[it][e], 0, 0);
             }
           }
         } else {
