@@ -86,13 +86,21 @@ __host__ __device__ constexpr int chain_lds_bytes(int DK, int C, int RT, int BV)
 // LDS of dp_prep_kernel.  Region 0 holds the fp16 key and query rows while
 // M and the scores are formed, then fp32 T and the partial-sum tiles of the
 // blocked inverse; after it come fp32 M, beta, G and the readout locations.
+// M is kept as its lower-triangular 16 x 16 blocks only (block (i, j), j <= i,
+// at index i (i + 1) / 2 + j, rows kPrepLdm floats apart), which keeps four
+// workgroups resident per CU at dk = 128, chunk 64.
+constexpr int kPrepLdm = 20;  // 20 n mod 64 is distinct for n < 16: conflict-free row reads
+__host__ __device__ constexpr int prep_mblock(int i, int j) { return i * (i + 1) / 2 + j; }
 __host__ __device__ constexpr int prep_region0_bytes(int DK, int C, int RT) {
   return (C * (DK + 8) * 2 + RT * (DK + 8) * 2) > (C * (C + 4) * 4 + 4 * 16 * 17 * 4)
              ? (C * (DK + 8) * 2 + RT * (DK + 8) * 2)
              : (C * (C + 4) * 4 + 4 * 16 * 17 * 4);
 }
+__host__ __device__ constexpr int prep_m_bytes(int C) {
+  return (C / 16) * (C / 16 + 1) / 2 * 16 * kPrepLdm * 4;
+}
 __host__ __device__ constexpr int prep_lds_bytes(int DK, int C, int RT) {
-  return prep_region0_bytes(DK, C, RT) + C * (C + 4) * 4 + 2 * C * 4 + RT * 4;
+  return prep_region0_bytes(DK, C, RT) + prep_m_bytes(C) + 2 * C * 4 + RT * 4;
 }
 
 // ---------------------------------------------------------------------------
@@ -114,7 +122,7 @@ __global__ __launch_bounds__(256) void dp_prep_kernel(FwdArgs p) {
   float* sTf = reinterpret_cast<float*>(smem);  // region 0, from the inverse on
   float* sSc = sTf + C * LDA;
   float* sA = reinterpret_cast<float*>(smem + prep_region0_bytes(DK, C, RT));
-  float* sB = sA + C * LDA;
+  float* sB = sA + prep_m_bytes(C) / 4;
   float* sG = sB + C;
   int* sLoc = reinterpret_cast<int*>(sG + C);
 
@@ -229,18 +237,21 @@ __global__ __launch_bounds__(256) void dp_prep_kernel(FwdArgs p) {
     }
   }
 
-  // 5. M = strict_tril(diag(beta) (E o Kn Kn^T)) on MFMA (lower tiles only)
-  for (int tile = wave; tile < NT * NT; tile += 4) {
-    const int ti = tile / NT, tj = tile % NT;
+  // 5. M = strict_tril(diag(beta) (E o Kn Kn^T)) on MFMA, lower blocks only
+  for (int tile = wave; tile < NT * (NT + 1) / 2; tile += 4) {
+    int ti = 0;
+    while (prep_mblock(ti + 1, 0) <= tile) ++ti;
+    const int tj = tile - prep_mblock(ti, 0);
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    if (tj <= ti) acc = mm_ll<DK>(acc, sK, LDK, ti * 16 + (lane & 15), sK, LDK, tj * 16 + (lane & 15));
+    acc = mm_ll<DK>(acc, sK, LDK, ti * 16 + (lane & 15), sK, LDK, tj * 16 + (lane & 15));
     const int jj = tj * 16 + (lane & 15);
+    float* mb = sA + tile * 16 * kPrepLdm;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int ii = ti * 16 + 4 * (lane >> 4) + e;
       float val = 0.f;
       if (jj < ii) val = sB[ii] * (p.g != nullptr ? expf(sG[ii] - sG[jj]) : 1.f) * acc[e];
-      sA[ii * LDA + jj] = val;
+      mb[(4 * (lane >> 4) + e) * kPrepLdm + (lane & 15)] = val;
     }
   }
   // 6. masked, decayed scores of the readout rows:  P[i][j] = (q_i . kn_j)
@@ -277,7 +288,7 @@ __global__ __launch_bounds__(256) void dp_prep_kernel(FwdArgs p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float acc = (i == cc) ? 1.f : 0.f;
-        const float* ar = sA + (gb * 16 + i) * LDA + gb * 16;
+        const float* ar = sA + (prep_mblock(gb, gb) * 16 + i) * kPrepLdm;
 #pragma unroll
         for (int j = 0; j < i; ++j) acc = fmaf(-ar[j], t[j], acc);
         t[i] = acc;
@@ -294,7 +305,8 @@ __global__ __launch_bounds__(256) void dp_prep_kernel(FwdArgs p) {
     if (i < NT) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
       for (int kb = j; kb < i; ++kb)
-        acc = mm_tile_tb<float, 16>(acc, sA + i * 16 * LDA + kb * 16, LDA, 0, sTf + kb * 16 * LDA + j * 16, LDA, 0);
+        acc = mm_tile_tb<float, 16>(acc, sA + prep_mblock(i, kb) * 16 * kPrepLdm, kPrepLdm, 0,
+                                    sTf + kb * 16 * LDA + j * 16, LDA, 0);
 #pragma unroll
       for (int e = 0; e < 4; ++e) sS[(4 * (lane >> 4) + e) * 17 + (lane & 15)] = acc[e];
     }
