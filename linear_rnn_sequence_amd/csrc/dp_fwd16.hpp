@@ -52,6 +52,19 @@ __host__ __device__ constexpr int frag_col_byte(int c) {
 // block index of column c (fragment layout)
 __host__ __device__ constexpr int frag_col_block(int c) { return 4 * (c >> 5) + ((c & 15) >> 2); }
 
+// T diag(beta) is block lower-triangular.  When the chunk scan runs its
+// pipelined body (dk and chunk multiples of 32) and the chunk has more than
+// one 32-column tile, the fragment-layout blocks of column tile t keep only
+// rows 32 t .. C-1 (the rows above are zero): block 4t + g then starts at
+// t_block_byte(C, t) + g (C - 32 t) 16 and row i sits (i - 32 t) 16 bytes in.
+__host__ __device__ constexpr bool t_trimmed(int DK, int C) { return DK % 32 == 0 && C % 32 == 0 && C > 32; }
+__host__ __device__ constexpr int t_block_byte(int C, int t) {
+  return 4 * 16 * (t * C - 16 * t * (t - 1));  // sum over t' < t of 4 (C - 32 t') 16
+}
+__host__ __device__ constexpr int t_bytes(int DK, int C) {
+  return t_trimmed(DK, C) ? t_block_byte(C, C / 32) : C * C * 2;
+}
+
 // Byte offsets of one chunk's operand block (workspace and LDS stage alike).
 struct Chunk16Layout {
   int oT, oK, oQ, oP, oS;  // T diag(beta), Kn, readout Q, scores P, scalars
@@ -62,7 +75,7 @@ struct Chunk16Layout {
 __host__ __device__ constexpr Chunk16Layout chunk16_layout(int DK, int C, int RT) {
   Chunk16Layout L{};
   L.oT = 0;
-  L.oK = L.oT + C * C * 2;
+  L.oK = L.oT + t_bytes(DK, C);
   L.oQ = L.oK + C * DK * 2;
   L.oP = L.oQ + RT * DK * 2;
   L.oS = L.oP + RT * C * 2;
@@ -319,16 +332,25 @@ __global__ __launch_bounds__(256) void dp_prep_kernel(FwdArgs p) {
     }
     __syncthreads();
   }
-  // 8. T diag(beta) (upper tiles zero) to the workspace, block-major
-  for (int idx = tid; idx < C * C / 8; idx += 256) {
-    const int q = idx / C, i = idx % C;
+  // 8. T diag(beta) to the workspace, block-major (upper tiles zero, or left
+  //    out in the trimmed layout: granule idx is then tile t's block g, row i)
+  constexpr bool TRIM = t_trimmed(DK, C);
+  for (int idx = tid; idx < t_bytes(DK, C) / 16; idx += 256) {
+    int q = idx / C, i = idx % C;
+    if constexpr (TRIM) {
+      int t = 0;
+      while (t + 1 < C / 32 && idx >= t_block_byte(C, t + 1) / 16) ++t;
+      const int rel = idx - t_block_byte(C, t) / 16, rows = C - 32 * t;
+      q = 4 * t + rel / rows;
+      i = 32 * t + rel % rows;
+    }
     float f[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int j = frag_layout(C) ? 32 * (q >> 2) + 4 * (q & 3) + (e & 3) + 16 * (e >> 2) : q * 8 + e;
       f[e] = ((j >> 4) > (i >> 4)) ? 0.f : sTf[i * LDA + j] * sB[j];
     }
-    st_vec16(reinterpret_cast<f16_t*>(wsc + W.oT + (q * C + i) * 16), f);
+    st_vec16(reinterpret_cast<f16_t*>(wsc + W.oT + idx * 16), f);
   }
 }
 
@@ -624,12 +646,15 @@ void dp_chain_kernel(FwdArgs p) {
     // (state) -- and the A fragment of step i is read LA steps ahead.  The
     // tile conversions that feed later products run DL steps after the MFMA
     // that completes the tile, or at the start of the product that needs
-    // them, whichever comes first.  The state's fp16 copy holds -H (the
-    // readout scale carries the sign back), so X = V + e^G (Kn (-H)).
+    // them, whichever comes first; each converted tile is pinned where it is
+    // made (an empty asm), so the compiler cannot sink the state's
+    // conversions past the chunk's barrier.
     constexpr int KST = DK / 32, CST = C / 32;
     constexpr int S1 = NCT * KST, S2 = S1 + NRT * KST, S3 = S2 + NCT * CST, S4 = S3 + NRT * CST;
     constexpr int NS = S4 + NDT * CST;
     constexpr int LA = 8, DL = 4;
+    constexpr bool TRIM = t_trimmed(DK, C);
+    constexpr int TS = TRIM ? 32 : 0;  // first stored row of T tile t is TS t
     // Readout row i of a chunk is token t0 + i: consecutive tokens, H dv
     // elements apart in out.  Each chunk stores through a buffer resource
     // based at its first row and bounded by its nrd rows, so this lane's
@@ -645,7 +670,7 @@ void dp_chain_kernel(FwdArgs p) {
       for (int e = 0; e < 4; ++e) voff[it][e] = ((16 * it + 4 * grp + e) * HD + ocol) * es;
     f16x4_t hqn[NDT];
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) hqn[dt] = to_h4(-hacc[dt]);
+    for (int dt = 0; dt < NDT; ++dt) hqn[dt] = to_h4(hacc[dt]);
     if (nc > 0) block_sync_lds();  // X(0)
     for (int c = 0; c < nc; ++c) {
       const uint32_t so = (uint32_t)((c % kChainStages) * STAGE);
@@ -660,13 +685,19 @@ void dp_chain_kernel(FwdArgs p) {
       const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
           static_cast<char*>(p.out) + rowbase * es, 0, nrd * HD * es, kBufferDword3);
       // per-tile LDS offsets, opaque so that fragment halves pair on their own base
-      uint32_t oK[NCT], oK1[NCT], oT[NCT], oQ[NRT], oP[NRT];
+      uint32_t oK[NCT], oK1[NCT], oT[CST], oQ[NRT], oP[NRT];
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         oK[ct] = so + W.oK + lrK + ct * 256;
         oK1[ct] = oK[ct] + C * 16;  // second half of each key fragment: one block on
-        oT[ct] = so + W.oT + lrT + ct * 256;
-        asm volatile("" : "+v"(oK[ct]), "+v"(oK1[ct]), "+v"(oT[ct]));
+        asm volatile("" : "+v"(oK[ct]), "+v"(oK1[ct]));
+      }
+      // T diag(beta): one base per 32-column tile t (rows from 32 t on when trimmed)
+#pragma unroll
+      for (int t = 0; t < CST; ++t) {
+        oT[t] = so + W.oT + (TRIM ? t_block_byte(C, t) : 4 * t * C * 16) + (lane >> 4) * (C - TS * t) * 16 +
+                (lane & 15) * 16;
+        asm volatile("" : "+v"(oT[t]));
       }
 #pragma unroll
       for (int it = 0; it < NRT; ++it) {
@@ -675,7 +706,7 @@ void dp_chain_kernel(FwdArgs p) {
         asm volatile("" : "+v"(oQ[it]), "+v"(oP[it]));
       }
       // small operands
-      f32x4_t vf[NCT], eg[NCT], el[NCT], negl[NRT];
+      f32x4_t vf[NCT], eg[NCT], el[NCT], egl[NRT];
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         // V[16 ct + 4 grp + e][vw + col] (bf16) in accumulator layout
@@ -690,7 +721,7 @@ void dp_chain_kernel(FwdArgs p) {
       }
 #pragma unroll
       for (int it = 0; it < NRT; ++it) {
-        negl[it] = -*reinterpret_cast<const f32x4_t*>(sEGL + it * 16 + 4 * grp);
+        egl[it] = *reinterpret_cast<const f32x4_t*>(sEGL + it * 16 + 4 * grp);
       }
       const float dec = sEG[C - 1];
 
@@ -699,6 +730,9 @@ void dp_chain_kernel(FwdArgs p) {
       f16x4_t xq[NCT], uq[NCT], usq[NCT];
       auto load_frag = [&](auto ic) {
         constexpr int i = decltype(ic)::value;
+        if constexpr (i >= S2 && i < S3 && TRIM && (i - S2) / CST < 2 * ((i - S2) % CST)) {
+          return;  // zero tile of T diag(beta): no read, no product
+        }
         f16x8_t fr;
         if constexpr (i < S1) {
           constexpr int ko = 4 * (i % KST) * C * 16;
@@ -709,7 +743,8 @@ void dp_chain_kernel(FwdArgs p) {
           fr = *reinterpret_cast<const f16x8_t*>(smem + oQ[j / KST] + 4 * (j % KST) * RT * 16);
         } else if constexpr (i < S3) {
           constexpr int j = i - S2;
-          fr = *reinterpret_cast<const f16x8_t*>(smem + oT[j / CST] + 4 * (j % CST) * C * 16);
+          constexpr int ct = j / CST, t = j % CST;
+          fr = *reinterpret_cast<const f16x8_t*>(smem + oT[t] + (16 * ct - TS * t) * 16);
         } else if constexpr (i < S4) {
           constexpr int j = i - S3;
           fr = *reinterpret_cast<const f16x8_t*>(smem + oP[j / CST] + 4 * (j % CST) * RT * 16);
@@ -732,7 +767,8 @@ void dp_chain_kernel(FwdArgs p) {
           z[it] = mfma32h(a, cat8(hqn[2 * t], hqn[2 * t + 1]), t == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : z[it]);
         } else if constexpr (i < S3) {
           constexpr int j = i - S2, ct = j / CST, t = j % CST;
-          accU[ct] = mfma32h(a, cat8(xq[2 * t], xq[2 * t + 1]), t == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : accU[ct]);
+          if constexpr (!(TRIM && ct < 2 * t))
+            accU[ct] = mfma32h(a, cat8(xq[2 * t], xq[2 * t + 1]), t == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : accU[ct]);
         } else if constexpr (i < S4) {
           constexpr int j = i - S3, it = j / CST, t = j % CST;
           z[it] = mfma32h(a, cat8(uq[2 * t], uq[2 * t + 1]), z[it]);
@@ -748,20 +784,24 @@ void dp_chain_kernel(FwdArgs p) {
           if constexpr (k % KST == KST - 1) {
             constexpr int ct = k / KST;
             if constexpr (GATED)
-              xq[ct] = to_h4(vf[ct] + eg[ct] * accX[ct]);  // accX = -Kn H
+              xq[ct] = to_h4(vf[ct] - eg[ct] * accX[ct]);  // accX = Kn H
             else
-              xq[ct] = to_h4(vf[ct] + accX[ct]);
+              xq[ct] = to_h4(vf[ct] - accX[ct]);
+            asm volatile("" : "+v"(xq[ct]));
           }
         } else if constexpr (k < S2) {
-          if constexpr ((k - S1) % KST == KST - 1) z[(k - S1) / KST] = z[(k - S1) / KST] * negl[(k - S1) / KST];
+          if constexpr ((k - S1) % KST == KST - 1) z[(k - S1) / KST] = z[(k - S1) / KST] * egl[(k - S1) / KST];
         } else if constexpr (k < S3) {
           if constexpr ((k - S2) % CST == CST - 1) {
             constexpr int ct = (k - S2) / CST;
             uq[ct] = to_h4(accU[ct]);
-            if constexpr (GATED)
+            asm volatile("" : "+v"(uq[ct]));
+            if constexpr (GATED) {
               usq[ct] = to_h4(accU[ct] * el[ct]);
-            else
+              asm volatile("" : "+v"(usq[ct]));
+            } else {
               usq[ct] = uq[ct];
+            }
           }
         } else if constexpr (k < S4) {
           if constexpr ((k - S3) % CST == CST - 1) {
@@ -779,7 +819,10 @@ void dp_chain_kernel(FwdArgs p) {
             }
           }
         } else {
-          if constexpr ((k - S4) % CST == CST - 1) hqn[(k - S4) / CST] = to_h4(-hacc[(k - S4) / CST]);
+          if constexpr ((k - S4) % CST == CST - 1) {
+            hqn[(k - S4) / CST] = to_h4(hacc[(k - S4) / CST]);
+            asm volatile("" : "+v"(hqn[(k - S4) / CST]));
+          }
         }
       };
       static_for<NS + LA + DL>([&](auto ic) {
