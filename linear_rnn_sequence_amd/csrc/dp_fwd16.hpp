@@ -18,7 +18,7 @@
 // dp_chain_kernel then only runs the recurrence: NWC consumer wavefronts keep
 // their 16 value columns of the fp32 state in registers, and one copy
 // wavefront streams each chunk's operands (and the values) into a ring of
-// LDS stages with global_load_lds_dwordx4, two chunks ahead.
+// LDS stages with global_load_lds_dwordx4, two or three chunks ahead.
 //
 // Tile layout ("block-major"): a tile of R rows and W fp16 columns is stored
 // as W/8 blocks of R x 16 bytes (block q holds columns 8q..8q+7 of every row).
@@ -88,12 +88,15 @@ __host__ __device__ constexpr Chunk16Layout chunk16_layout(int DK, int C, int RT
 }
 
 // LDS of dp_chain_kernel: kStages copies of (chunk block, value tile).
-constexpr int kChainStages = 3;
+// Four stages (three chunks in flight) when they fit the 160 KB of LDS, else three.
 __host__ __device__ constexpr int chain_stage_bytes(int DK, int C, int RT, int BV) {
   return chunk16_layout(DK, C, RT).bytes + C * BV * 2;
 }
+__host__ __device__ constexpr int chain_stages(int DK, int C, int RT, int BV) {
+  return 4 * chain_stage_bytes(DK, C, RT, BV) <= 160 * 1024 ? 4 : 3;
+}
 __host__ __device__ constexpr int chain_lds_bytes(int DK, int C, int RT, int BV) {
-  return kChainStages * chain_stage_bytes(DK, C, RT, BV);
+  return chain_stages(DK, C, RT, BV) * chain_stage_bytes(DK, C, RT, BV);
 }
 
 // LDS of dp_prep_kernel.  Region 0 holds the fp16 key and query rows while
@@ -503,6 +506,7 @@ void dp_chain_kernel(FwdArgs p) {
   constexpr int RT = 16 * NRT, BV = 16 * NWC;
   constexpr int NCT = C / 16, NDT = DK / 16;
   constexpr Chunk16Layout W = chunk16_layout(DK, C, RT);
+  constexpr int STG = chain_stages(DK, C, RT, BV);    // LDS ring stages
   constexpr int VB = C * BV * 2;                      // value tile bytes
   constexpr int STAGE = W.bytes + VB;
   constexpr int NIB = (W.bytes + 1023) / 1024;        // copies per chunk block
@@ -513,7 +517,7 @@ void dp_chain_kernel(FwdArgs p) {
   // copies of copy wavefront w: indices m = w, w + NCW, .. of the NI copies
   constexpr int NI0 = (NI + NCW - 1) / NCW, NI1 = NI / NCW;
   static_assert(NCW == 2, "two copy wavefronts");
-  static_assert(NI0 < 64, "copies per chunk exceed the vmcnt range");
+  static_assert((STG - 2) * NI0 < 64, "copies in flight exceed the vmcnt range");
   static_assert(VB % 16 == 0 && (VB < 1024 || VB % 1024 == 0), "value tile");
 
   extern __shared__ __align__(16) unsigned char smem[];
@@ -566,7 +570,7 @@ void dp_chain_kernel(FwdArgs p) {
     // copies of chunk c issued by copy wavefront CW: index m = CW, CW + NCW, ..
     auto issue = [&](auto cwc, int c) {
       constexpr int CW = decltype(cwc)::value;
-      const uint32_t st = lds0 + (uint32_t)((c % kChainStages) * STAGE);
+      const uint32_t st = lds0 + (uint32_t)((c % STG) * STAGE);
       const unsigned char* src = wsh + (long long)c * W.bytes;
       static_for<NIB>([&](auto mc) {
         constexpr int m = decltype(mc)::value;
@@ -592,24 +596,27 @@ void dp_chain_kernel(FwdArgs p) {
     auto run = [&](auto cwc) {
       constexpr int CW = decltype(cwc)::value;
       constexpr int NMINE = CW == 0 ? NI0 : NI1;  // copies per chunk of this wavefront
-      if (nc > 0) {
-        issue(cwc, 0);
-        if (nc > 1) {
-          issue(cwc, 1);
+      // wait until at most `ahead` chunks' copies of this wavefront are in flight
+      auto wait_ahead = [&](int ahead) {
+        if (ahead >= 2) {
+          wait_vmcnt<(STG > 3 ? 2 : 1) * NMINE>();
+        } else if (ahead == 1) {
           wait_vmcnt<NMINE>();
         } else {
           wait_vmcnt<0>();
         }
-        block_sync_lds();  // X(0)
+      };
+      const int pre = nc < STG - 1 ? nc : STG - 1;  // chunks 0 .. STG-2 up front
+      for (int j = 0; j < pre; ++j) issue(cwc, j);
+      if (nc > 0) {
+        wait_ahead(pre - 1);  // chunk 0 has landed
+        block_sync_lds();     // X(0)
       }
       for (int c = 0; c + 1 < nc; ++c) {
-        if (c + 2 < nc) {
-          issue(cwc, c + 2);  // into the stage chunk c - 1 used
-          wait_vmcnt<NMINE>();  // chunk c + 1 has landed
-        } else {
-          wait_vmcnt<0>();
-        }
-        block_sync_lds();  // X(c + 1)
+        if (c + STG - 1 < nc) issue(cwc, c + STG - 1);  // into the stage chunk c - 1 used
+        const int last = c + STG - 1 < nc ? c + STG - 1 : nc - 1;
+        wait_ahead(last - (c + 1));  // chunk c + 1 has landed
+        block_sync_lds();            // X(c + 1)
       }
     };
     if (cw == 0)
@@ -673,7 +680,7 @@ void dp_chain_kernel(FwdArgs p) {
     for (int dt = 0; dt < NDT; ++dt) hqn[dt] = to_h4(hacc[dt]);
     if (nc > 0) block_sync_lds();  // X(0)
     for (int c = 0; c < nc; ++c) {
-      const uint32_t so = (uint32_t)((c % kChainStages) * STAGE);
+      const uint32_t so = (uint32_t)((c % STG) * STAGE);
       const unsigned char* st = smem + so;
       const float* sEG = reinterpret_cast<const float*>(st + W.oS + W.oEG);
       const float* sEL = reinterpret_cast<const float*>(st + W.oS + W.oEL);
@@ -843,7 +850,7 @@ void dp_chain_kernel(FwdArgs p) {
   } else {
   if (nc > 0) block_sync_lds();  // X(0)
   for (int c = 0; c < nc; ++c) {
-    const uint32_t so = (uint32_t)((c % kChainStages) * STAGE);
+    const uint32_t so = (uint32_t)((c % STG) * STAGE);
     const unsigned char* st = smem + so;
     const float* sEG = reinterpret_cast<const float*>(st + W.oS + W.oEG);
     const float* sEL = reinterpret_cast<const float*>(st + W.oS + W.oEL);
