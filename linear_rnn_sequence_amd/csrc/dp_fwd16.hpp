@@ -95,6 +95,13 @@ __host__ __device__ constexpr int chain_stage_bytes(int DK, int C, int RT, int B
 __host__ __device__ constexpr int chain_stages(int DK, int C, int RT, int BV) {
   return 4 * chain_stage_bytes(DK, C, RT, BV) <= 160 * 1024 ? 4 : 3;
 }
+// Lookahead (in MFMA steps) of the pipelined chunk body.
+constexpr int kLookahead = 8;
+// Pipelined body (dk and chunk multiples of 32), four stages, and the first
+// kLookahead steps are key fragments (C/16 key tiles of dk/32 steps each).
+__host__ __device__ constexpr bool chain_early(int DK, int C, int STG) {
+  return DK % 32 == 0 && C % 32 == 0 && STG == 4 && (C / 16) * (DK / 32) >= kLookahead;
+}
 __host__ __device__ constexpr int chain_lds_bytes(int DK, int C, int RT, int BV) {
   return chain_stages(DK, C, RT, BV) * chain_stage_bytes(DK, C, RT, BV);
 }
@@ -507,6 +514,10 @@ void dp_chain_kernel(FwdArgs p) {
   constexpr int NCT = C / 16, NDT = DK / 16;
   constexpr Chunk16Layout W = chunk16_layout(DK, C, RT);
   constexpr int STG = chain_stages(DK, C, RT, BV);    // LDS ring stages
+  // With four stages and a pipelined body whose first kLookahead steps are
+  // key fragments, the consumers read the next chunk's first operands while
+  // finishing the current one, so each chunk must land one chunk earlier.
+  constexpr bool EARLY = chain_early(DK, C, STG);
   constexpr int VB = C * BV * 2;                      // value tile bytes
   constexpr int STAGE = W.bytes + VB;
   constexpr int NIB = (W.bytes + 1023) / 1024;        // copies per chunk block
@@ -606,17 +617,21 @@ void dp_chain_kernel(FwdArgs p) {
           wait_vmcnt<0>();
         }
       };
+      // at X(c) chunk c has landed, and chunk c + 1 too when EARLY
+      constexpr int LEAD = EARLY ? 1 : 0;
       const int pre = nc < STG - 1 ? nc : STG - 1;  // chunks 0 .. STG-2 up front
       for (int j = 0; j < pre; ++j) issue(cwc, j);
       if (nc > 0) {
-        wait_ahead(pre - 1);  // chunk 0 has landed
-        block_sync_lds();     // X(0)
+        const int a0 = pre - 1 - LEAD;
+        wait_ahead(a0 > 0 ? a0 : 0);
+        block_sync_lds();  // X(0)
       }
       for (int c = 0; c + 1 < nc; ++c) {
         if (c + STG - 1 < nc) issue(cwc, c + STG - 1);  // into the stage chunk c - 1 used
         const int last = c + STG - 1 < nc ? c + STG - 1 : nc - 1;
-        wait_ahead(last - (c + 1));  // chunk c + 1 has landed
-        block_sync_lds();            // X(c + 1)
+        const int a = last - (c + 1 + LEAD);
+        wait_ahead(a > 0 ? a : 0);
+        block_sync_lds();  // X(c + 1)
       }
     };
     if (cw == 0)
@@ -659,7 +674,7 @@ void dp_chain_kernel(FwdArgs p) {
     constexpr int KST = DK / 32, CST = C / 32;
     constexpr int S1 = NCT * KST, S2 = S1 + NRT * KST, S3 = S2 + NCT * CST, S4 = S3 + NRT * CST;
     constexpr int NS = S4 + NDT * CST;
-    constexpr int LA = 8, DL = 4;
+    constexpr int LA = kLookahead, DL = 4;
     constexpr bool TRIM = t_trimmed(DK, C);
     constexpr int TS = TRIM ? 32 : 0;  // first stored row of T tile t is TS t
     // Readout row i of a chunk is token t0 + i: consecutive tokens, H dv
@@ -670,21 +685,79 @@ void dp_chain_kernel(FwdArgs p) {
     // the bound, where the hardware drops the store.
     const int HD = p.H * p.dv;
     const int es = p.out_f32 ? 4 : 2;
-    int voff[NRT][4];
+    int voff[NRT][4], voff4[NRT];
 #pragma unroll
-    for (int it = 0; it < NRT; ++it)
+    for (int it = 0; it < NRT; ++it) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) voff[it][e] = ((16 * it + 4 * grp + e) * HD + ocol) * es;
+      // after the quad transpose (bf16): row 16 it + 4 grp + (col & 3), columns from ocol - (col & 3)
+      voff4[it] = ((16 * it + 4 * grp + (col & 3)) * HD + ocol - (col & 3)) * 2;
+    }
+    // byte selector of the second transpose step: even lanes keep their low
+    // halves and take the partner's low halves above them, odd lanes the highs
+    const uint32_t qsel = (lane & 1) ? 0x03020706u : 0x05040100u;
     f16x4_t hqn[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) hqn[dt] = to_h4(hacc[dt]);
-    if (nc > 0) block_sync_lds();  // X(0)
-    for (int c = 0; c < nc; ++c) {
-      const uint32_t so = (uint32_t)((c % STG) * STAGE);
+    // step list padded to a multiple of LA: the next chunk's step k then lands
+    // in ring slot k % LA, the slot its MFMA reads
+    constexpr int NSP = EARLY ? (NS + LA - 1) / LA * LA : NS;
+    static_assert(!EARLY || (S1 >= LA && LA % KST == 0), "early fragments must be key fragments");
+    f32x4_t vf[NCT], eg[NCT], el[NCT], egl[NRT];
+    float dec = 1.f;
+    f16x8_t ring[LA];
+    // the first LA fragments of the next chunk, read during this one (EARLY): a
+    // loop-carried array of its own, written once per chunk, so that the
+    // compiler keeps it in place across the back edge
+    f16x8_t pre[EARLY ? LA : 1];
+    // per-chunk small operands of the chunk in stage byte offset `so`
+    auto load_small = [&](uint32_t so) {
       const unsigned char* st = smem + so;
       const float* sEG = reinterpret_cast<const float*>(st + W.oS + W.oEG);
       const float* sEL = reinterpret_cast<const float*>(st + W.oS + W.oEL);
       const float* sEGL = reinterpret_cast<const float*>(st + W.oS + W.oEGL);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        // V[16 ct + 4 grp + e][vw + col] (bf16) in accumulator layout
+        const s16x4_t vr = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4_t*)(st + W.bytes + ltV + tr_block<BV>(wave) * C * 16 + ct * 16 * 16));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vf[ct][e] = __uint_as_float((uint32_t)(uint16_t)vr[e] << 16);
+        if constexpr (GATED) {
+          eg[ct] = *reinterpret_cast<const f32x4_t*>(sEG + ct * 16 + 4 * grp);
+          el[ct] = *reinterpret_cast<const f32x4_t*>(sEL + ct * 16 + 4 * grp);
+        }
+      }
+#pragma unroll
+      for (int it = 0; it < NRT; ++it) egl[it] = *reinterpret_cast<const f32x4_t*>(sEGL + it * 16 + 4 * grp);
+      if constexpr (GATED) dec = sEG[C - 1];
+    };
+    // key fragment k (< LA) of the chunk whose key tiles start at ok / ok1
+    auto key_frag = [&](const uint32_t* ok, const uint32_t* ok1, auto kc) {
+      constexpr int k = decltype(kc)::value;
+      constexpr int ko = 4 * (k % KST) * C * 16;
+      pre[k] = cat8(*reinterpret_cast<const f16x4_t*>(smem + ok[k / KST] + ko),
+                    *reinterpret_cast<const f16x4_t*>(smem + ok1[k / KST] + ko));
+    };
+    if (nc > 0) block_sync_lds();  // X(0)
+    if constexpr (EARLY) {
+      if (nc > 0) {  // chunk 0's small operands and first LA fragments (stage 0)
+        uint32_t ok[LA / KST], ok1[LA / KST];
+#pragma unroll
+        for (int ct = 0; ct < LA / KST; ++ct) {
+          ok[ct] = W.oK + lrK + ct * 256;
+          ok1[ct] = ok[ct] + C * 16;
+          asm volatile("" : "+v"(ok[ct]), "+v"(ok1[ct]));
+        }
+        load_small(0);
+        static_for<LA>([&](auto kc) { key_frag(ok, ok1, kc); });
+      }
+    }
+    for (int c = 0; c < nc; ++c) {
+      const uint32_t so = (uint32_t)((c % STG) * STAGE);
+      const unsigned char* st = smem + so;
+      // stage of the next chunk (this one's again after the last: the reads are then unused)
+      const uint32_t son = (uint32_t)(((c + 1 < nc ? c + 1 : c) % STG) * STAGE);
       // readout rows i < nrd are the tokens t0 + i (uniform, scalar unit)
       const int t0 = fastdiv(c * C, p.nh_magic, p.nh_shift);
       const int nrd = fastdiv(min(c * C + C, p.N), p.nh_magic, p.nh_shift) - t0;
@@ -712,27 +785,19 @@ void dp_chain_kernel(FwdArgs p) {
         oP[it] = so + W.oP + lrP + it * 256;
         asm volatile("" : "+v"(oQ[it]), "+v"(oP[it]));
       }
-      // small operands
-      f32x4_t vf[NCT], eg[NCT], el[NCT], egl[NRT];
+      // the next chunk's first key tiles (EARLY)
+      uint32_t okn[EARLY ? LA / KST : 1], ok1n[EARLY ? LA / KST : 1];
+      if constexpr (EARLY) {
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        // V[16 ct + 4 grp + e][vw + col] (bf16) in accumulator layout
-        const s16x4_t vr = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4_t*)(st + W.bytes + ltV + tr_block<BV>(wave) * C * 16 + ct * 16 * 16));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vf[ct][e] = __uint_as_float((uint32_t)(uint16_t)vr[e] << 16);
-        if constexpr (GATED) {
-          eg[ct] = *reinterpret_cast<const f32x4_t*>(sEG + ct * 16 + 4 * grp);
-          el[ct] = *reinterpret_cast<const f32x4_t*>(sEL + ct * 16 + 4 * grp);
+        for (int ct = 0; ct < LA / KST; ++ct) {
+          okn[ct] = son + W.oK + lrK + ct * 256;
+          ok1n[ct] = okn[ct] + C * 16;
+          asm volatile("" : "+v"(okn[ct]), "+v"(ok1n[ct]));
         }
+      } else {
+        load_small(so);
       }
-#pragma unroll
-      for (int it = 0; it < NRT; ++it) {
-        egl[it] = *reinterpret_cast<const f32x4_t*>(sEGL + it * 16 + 4 * grp);
-      }
-      const float dec = sEG[C - 1];
 
-      f16x8_t ring[LA];
       f32x4_t accX[NCT], accU[NCT], z[NRT];
       f16x4_t xq[NCT], uq[NCT], usq[NCT];
       auto load_frag = [&](auto ic) {
@@ -765,7 +830,11 @@ void dp_chain_kernel(FwdArgs p) {
       };
       auto mfma_step = [&](auto ic) {
         constexpr int i = decltype(ic)::value;
-        const f16x8_t a = ring[i % LA];
+        f16x8_t a;
+        if constexpr (EARLY && i < LA)
+          a = pre[i];
+        else
+          a = ring[i % LA];
         if constexpr (i < S1) {
           constexpr int ct = i / KST, t = i % KST;
           accX[ct] = mfma32h(a, cat8(hqn[2 * t], hqn[2 * t + 1]), t == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : accX[ct]);
@@ -811,20 +880,7 @@ void dp_chain_kernel(FwdArgs p) {
             }
           }
         } else if constexpr (k < S4) {
-          if constexpr ((k - S3) % CST == CST - 1) {
-            constexpr int it = (k - S3) / CST;
-            // rows from nrd on are padding: out of the resource's bound, dropped
-            if (p.out_f32) {
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(z[it][e]), orsrc, voff[it][e], 0, 0);
-            } else {
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (__bf16)z[it][e]), orsrc,
-                                                      voff[it][e], 0, 0);
-            }
-          }
+          // the readout tiles are stored after the chunk's last product (below)
         } else {
           if constexpr ((k - S4) % CST == CST - 1) {
             hqn[(k - S4) / CST] = to_h4(hacc[(k - S4) / CST]);
@@ -832,7 +888,7 @@ void dp_chain_kernel(FwdArgs p) {
           }
         }
       };
-      static_for<NS + LA + DL>([&](auto ic) {
+      static_for<NSP + LA + DL>([&](auto ic) {
         constexpr int i = decltype(ic)::value;
         // conversions due in this iteration: steps k in [i - LA - DL, i - LA]
         static_for<DL + 1>([&](auto wc) {
@@ -842,9 +898,46 @@ void dp_chain_kernel(FwdArgs p) {
           }
         });
         if constexpr (i >= LA && i - LA < NS) mfma_step(std::integral_constant<int, i - LA>{});
-        if constexpr (i < NS) load_frag(std::integral_constant<int, i>{});
+        if constexpr (EARLY) {
+          // steps 0 .. LA-1 were read during the previous chunk
+          if constexpr (i >= LA && i < NS) load_frag(std::integral_constant<int, i>{});
+          if constexpr (i >= NSP && i < NSP + LA) key_frag(okn, ok1n, std::integral_constant<int, i - NSP>{});
+          if constexpr (i == NS + LA) load_small(son);  // past this chunk's last use of them
+        } else {
+          if constexpr (i < NS) load_frag(std::integral_constant<int, i>{});
+        }
         sched_fence();
       });
+      // Readout rows, stored once the chunk's products are issued: the copy
+      // wavefronts' transfers of a later chunk, issued after the previous
+      // barrier, have left the vector-memory path by now, so the stores do not
+      // queue behind them.  Rows from nrd on are padding: out of the
+      // resource's bound, dropped.
+#pragma unroll
+      for (int it = 0; it < NRT; ++it) {
+        if (p.out_f32) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(z[it][e]), orsrc, voff[it][e], 0, 0);
+        } else {
+          // bf16: transpose each quad of lanes' 4 x 4 values (lane 4q + a of a
+          // group holds rows 4g + e of column 4q + a; afterwards row 4g + a of
+          // columns 4q .. 4q + 3), so one 8-byte store per lane writes the tile
+          uint32_t p0 = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{z[it][0], z[it][1]}, bf16x2_t));
+          uint32_t p1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{z[it][2], z[it][3]}, bf16x2_t));
+          const uint32_t x0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)p0, 0x4E, 0xF, 0xF, false);  // lane ^ 2
+          const uint32_t x1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)p1, 0x4E, 0xF, 0xF, false);
+          if (lane & 2)
+            p0 = x1;
+          else
+            p1 = x0;
+          const uint32_t y0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)p0, 0xB1, 0xF, 0xF, false);  // lane ^ 1
+          const uint32_t y1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)p1, 0xB1, 0xF, 0xF, false);
+          p0 = __builtin_amdgcn_perm(y0, p0, qsel);
+          p1 = __builtin_amdgcn_perm(y1, p1, qsel);
+          __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{p0, p1}, orsrc, voff4[it], 0, 0);
+        }
+      }
       if (c + 1 < nc) block_sync_lds();  // X(c + 1)
     }
   } else {
