@@ -114,13 +114,17 @@ __host__ __device__ constexpr int chain_lds_bytes(int DK, int C, int RT, int BV)
 // workgroups resident per CU at dk = 128, chunk 64.
 constexpr int kPrepLdm = 20;  // 20 n mod 64 is distinct for n < 16: conflict-free row reads
 __host__ __device__ constexpr int prep_mblock(int i, int j) { return i * (i + 1) / 2 + j; }
-__host__ __device__ constexpr int prep_region0_bytes(int DK, int C, int RT) {
-  return (C * (DK + 8) * 2 + RT * (DK + 8) * 2) > (C * (C + 4) * 4 + 4 * 16 * 17 * 4)
-             ? (C * (DK + 8) * 2 + RT * (DK + 8) * 2)
-             : (C * (C + 4) * 4 + 4 * 16 * 17 * 4);
-}
 __host__ __device__ constexpr int prep_m_bytes(int C) {
   return (C / 16) * (C / 16 + 1) / 2 * 16 * kPrepLdm * 4;
+}
+// With dk a multiple of 32 the readout queries never touch LDS: each
+// wavefront loads its MFMA fragments of them straight into registers (and
+// writes them to the operand block from there).  T is kept packed like M.
+__host__ __device__ constexpr bool prep_q_in_regs(int DK) { return DK % 32 == 0; }
+__host__ __device__ constexpr int prep_region0_bytes(int DK, int C, int RT) {
+  return (C * (DK + 8) * 2 + (prep_q_in_regs(DK) ? 0 : RT * (DK + 8) * 2)) > (prep_m_bytes(C) + 4 * 16 * 17 * 4)
+             ? (C * (DK + 8) * 2 + (prep_q_in_regs(DK) ? 0 : RT * (DK + 8) * 2))
+             : (prep_m_bytes(C) + 4 * 16 * 17 * 4);
 }
 __host__ __device__ constexpr int prep_lds_bytes(int DK, int C, int RT) {
   return prep_region0_bytes(DK, C, RT) + prep_m_bytes(C) + 2 * C * 4 + RT * 4;
@@ -129,10 +133,10 @@ __host__ __device__ constexpr int prep_lds_bytes(int DK, int C, int RT) {
 // ---------------------------------------------------------------------------
 // dp_prep_kernel: one chunk per workgroup.
 template <int DK, int C, int NRT>
-__global__ __launch_bounds__(256) void dp_prep_kernel(FwdArgs p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void dp_prep_kernel(FwdArgs p) {
   constexpr int RT = 16 * NRT;
   constexpr int TPR = DK / 8;  // 16-byte granules per key row
-  constexpr int LDK = DK + 8, LDA = C + 4;
+  constexpr int LDK = DK + 8;
   constexpr int NT = C / 16;
   constexpr int KV = C * TPR, KIT = (KV + 255) / 256;
   constexpr int QV = RT * TPR, QIT = (QV + 255) / 256;
@@ -142,8 +146,8 @@ __global__ __launch_bounds__(256) void dp_prep_kernel(FwdArgs p) {
   extern __shared__ __align__(16) unsigned char smem[];
   f16_t* sK = reinterpret_cast<f16_t*>(smem);  // region 0, until M and P are formed
   f16_t* sQ = sK + C * LDK;
-  float* sTf = reinterpret_cast<float*>(smem);  // region 0, from the inverse on
-  float* sSc = sTf + C * LDA;
+  float* sTf = reinterpret_cast<float*>(smem);  // region 0, from the inverse on (packed blocks)
+  float* sSc = sTf + prep_m_bytes(C) / 4;
   float* sA = reinterpret_cast<float*>(smem + prep_region0_bytes(DK, C, RT));
   float* sB = sA + prep_m_bytes(C) / 4;
   float* sG = sB + C;
@@ -161,6 +165,8 @@ __global__ __launch_bounds__(256) void dp_prep_kernel(FwdArgs p) {
   unsigned char* wsc = static_cast<unsigned char*>(p.wsT) + chunk * W.bytes;
 
   // 1. global loads: key rows, readout query rows, beta, gate
+  constexpr bool QREG = prep_q_in_regs(DK);
+  constexpr int QKS = DK / 32;  // 32-deep steps of a query fragment row
   u32x4_t rk[KIT], rq[QIT];
 #pragma unroll
   for (int it = 0; it < KIT; ++it) {
@@ -169,17 +175,6 @@ __global__ __launch_bounds__(256) void dp_prep_kernel(FwdArgs p) {
     const int s = s0 + r;
     rk[it] = u32x4_t{0u, 0u, 0u, 0u};
     if (idx < KV && s < p.N) rk[it] = ld16(kp + sub_row(p, s, b, h) * DK + cg * 8);
-  }
-#pragma unroll
-  for (int it = 0; it < QIT; ++it) {
-    const int idx = tid + it * 256;
-    const int i = idx / TPR, cg = idx % TPR;
-    const int s = r0 + i * n_h;
-    rq[it] = u32x4_t{0u, 0u, 0u, 0u};
-    if (idx < QV && s < s0 + C && s < p.N) {
-      const long long tk = tok0 + (long long)fastdiv(s, p.nh_magic, p.nh_shift) * p.H;
-      rq[it] = ld16(qp + tk * DK + cg * 8);
-    }
   }
   float braw = 0.f, lam = 0.f;
   if (tid < C && s0 + tid < p.N) {
@@ -207,13 +202,61 @@ __global__ __launch_bounds__(256) void dp_prep_kernel(FwdArgs p) {
     for (int e = 0; e < 8; ++e) f[e] *= rinv;
     if (idx < KV) st_vec16(sK + r * LDK + cg * 8, f);
   }
+  // queries, loaded once the key rows are in LDS (fewer registers live at once).
+  // QREG: the fragment (row 16 it + n, step t) of lane (n, g) -- columns
+  // 32 t + 4 g .. + 3 and 32 t + 16 + 4 g .. + 3 -- as raw bf16
+  u32x4_t qr[QREG ? NRT : 1][QREG ? QKS : 1];
+  if constexpr (QREG) {
 #pragma unroll
-  for (int it = 0; it < QIT; ++it) {
-    const int idx = tid + it * 256;
-    const int i = idx / TPR, cg = idx % TPR;
-    float f[8];
-    unpack16(rq[it], f, bf16_t{});
-    if (idx < QV) st_vec16(sQ + i * LDK + cg * 8, f);
+    for (int it = 0; it < NRT; ++it) {
+      const int i = it * 16 + (lane & 15);
+      const int s = r0 + i * n_h;
+      const bool ok = s < s0 + C && s < p.N;
+      const long long tk = tok0 + (long long)fastdiv(ok ? s : s0, p.nh_magic, p.nh_shift) * p.H;
+#pragma unroll
+      for (int t = 0; t < QKS; ++t) {
+        qr[it][t] = u32x4_t{0u, 0u, 0u, 0u};
+        if (ok) {
+          const bf16_t* src = qp + tk * DK + 32 * t + 4 * (lane >> 4);
+          const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(src);
+          const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(src + 16);
+          qr[it][t] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int it = 0; it < QIT; ++it) {
+      const int idx = tid + it * 256;
+      const int i = idx / TPR, cg = idx % TPR;
+      const int s = r0 + i * n_h;
+      rq[it] = u32x4_t{0u, 0u, 0u, 0u};
+      if (idx < QV && s < s0 + C && s < p.N) {
+        const long long tk = tok0 + (long long)fastdiv(s, p.nh_magic, p.nh_shift) * p.H;
+        rq[it] = ld16(qp + tk * DK + cg * 8);
+      }
+    }
+  }
+  f16x8_t qf[QREG ? NRT : 1][QREG ? QKS : 1];  // QREG: fp16 query fragments
+  if constexpr (QREG) {
+#pragma unroll
+    for (int it = 0; it < NRT; ++it)
+#pragma unroll
+      for (int t = 0; t < QKS; ++t) {
+        float f[8];
+        unpack16(qr[it][t], f, bf16_t{});
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[it][t][e] = (f16_t)f[e];
+      }
+  } else {
+#pragma unroll
+    for (int it = 0; it < QIT; ++it) {
+      const int idx = tid + it * 256;
+      const int i = idx / TPR, cg = idx % TPR;
+      float f[8];
+      unpack16(rq[it], f, bf16_t{});
+      if (idx < QV) st_vec16(sQ + i * LDK + cg * 8, f);
+    }
   }
 
   // 3. beta range, cumulative log-gate and the per-chunk scalars (wave 0)
@@ -248,19 +291,62 @@ __global__ __launch_bounds__(256) void dp_prep_kernel(FwdArgs p) {
     const int q = idx / C, r = idx % C;
     st16(wsc + W.oK + (q * C + r) * 16, ld16(sK + r * LDK + q * 8));
   }
-  for (int idx = tid; idx < QV; idx += 256) {
-    const int q = idx / RT, i = idx % RT;
-    if constexpr (frag_layout(DK)) {  // block q = 4t + g: columns 32t + 4g.. and 32t + 16 + 4g..
-      const int c0 = 32 * (q >> 2) + 4 * (q & 3);
-      const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(sQ + i * LDK + c0);
-      const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(sQ + i * LDK + c0 + 16);
-      st16(wsc + W.oQ + (q * RT + i) * 16, u32x4_t{lo[0], lo[1], hi[0], hi[1]});
-    } else {
+  if constexpr (QREG) {
+    // fragment layout: block 4 t + g holds lane (n, g)'s fragment of step t, row 16 it + n
+#pragma unroll
+    for (int t = 0; t < QKS; ++t) {
+      if ((t & 3) != wave) continue;  // every wavefront holds every fragment: wave t % 4 writes step t
+#pragma unroll
+      for (int it = 0; it < NRT; ++it)
+        st16(wsc + W.oQ + ((4 * t + (lane >> 4)) * RT + it * 16 + (lane & 15)) * 16,
+             __builtin_bit_cast(u32x4_t, qf[it][t]));
+    }
+  } else {
+    for (int idx = tid; idx < QV; idx += 256) {
+      const int q = idx / RT, i = idx % RT;
       st16(wsc + W.oQ + (q * RT + i) * 16, ld16(sQ + i * LDK + q * 8));
     }
   }
 
-  // 5. M = strict_tril(diag(beta) (E o Kn Kn^T)) on MFMA, lower blocks only
+  // 5. masked, decayed scores of the readout rows:  P[i][j] = (q_i . kn_j)
+  //    e^{G_loc(i) - G_j} for j <= loc(i).  Computed transposed (lane: four
+  //    consecutive j of one i) and stored block-major in 8-byte pieces.
+  auto p_tile = [&](int it, int jt, f32x4_t acc) {
+    const int i = it * 16 + (lane & 15);
+    const int loc = sLoc[i];
+    const int j0 = jt * 16 + 4 * (lane >> 4);
+    const float gl = loc >= 0 ? sG[loc] : 0.f;
+    float pv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = j0 + e;
+      pv[e] = (j <= loc) ? acc[e] * (p.g != nullptr ? expf(gl - sG[j]) : 1.f) : 0.f;
+    }
+    const int pblk = frag_layout(C) ? frag_col_block(j0) : (j0 >> 3);
+    const int pbyte = frag_layout(C) ? frag_col_byte(j0) : (j0 & 7) * 2;
+    st4(reinterpret_cast<f16_t*>(wsc + W.oP + (pblk * RT + i) * 16 + pbyte), pv[0], pv[1], pv[2], pv[3]);
+  };
+  if constexpr (QREG) {
+    // the query fragments are registers: the row tile it is a compile-time index
+#pragma unroll
+    for (int it = 0; it < NRT; ++it) {
+      for (int jt = wave; jt < NT; jt += 4) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < QKS; ++t)
+          acc = mfma32h(lds_a32(sK, LDK, jt * 16 + (lane & 15), 32 * t), qf[it][t], acc);
+        p_tile(it, jt, acc);
+      }
+    }
+  } else {
+    for (int tile = wave; tile < NRT * NT; tile += 4) {
+      const int it = tile / NT, jt = tile % NT;
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mm_ll<DK>(acc, sK, LDK, jt * 16 + (lane & 15), sQ, LDK, it * 16 + (lane & 15));
+      p_tile(it, jt, acc);
+    }
+  }
+  // 6. M = strict_tril(diag(beta) (E o Kn Kn^T)) on MFMA, lower blocks only
   for (int tile = wave; tile < NT * (NT + 1) / 2; tile += 4) {
     int ti = 0;
     while (prep_mblock(ti + 1, 0) <= tile) ++ti;
@@ -276,27 +362,6 @@ __global__ __launch_bounds__(256) void dp_prep_kernel(FwdArgs p) {
       if (jj < ii) val = sB[ii] * (p.g != nullptr ? expf(sG[ii] - sG[jj]) : 1.f) * acc[e];
       mb[(4 * (lane >> 4) + e) * kPrepLdm + (lane & 15)] = val;
     }
-  }
-  // 6. masked, decayed scores of the readout rows:  P[i][j] = (q_i . kn_j)
-  //    e^{G_loc(i) - G_j} for j <= loc(i).  Computed transposed (lane: four
-  //    consecutive j of one i) and stored block-major in 8-byte pieces.
-  for (int tile = wave; tile < NRT * NT; tile += 4) {
-    const int it = tile / NT, jt = tile % NT;
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    acc = mm_ll<DK>(acc, sK, LDK, jt * 16 + (lane & 15), sQ, LDK, it * 16 + (lane & 15));
-    const int i = it * 16 + (lane & 15);
-    const int loc = sLoc[i];
-    const int j0 = jt * 16 + 4 * (lane >> 4);
-    const float gl = loc >= 0 ? sG[loc] : 0.f;
-    float pv[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int j = j0 + e;
-      pv[e] = (j <= loc) ? acc[e] * (p.g != nullptr ? expf(gl - sG[j]) : 1.f) : 0.f;
-    }
-    const int pblk = frag_layout(C) ? frag_col_block(j0) : (j0 >> 3);
-    const int pbyte = frag_layout(C) ? frag_col_byte(j0) : (j0 & 7) * 2;
-    st4(reinterpret_cast<f16_t*>(wsc + W.oP + (pblk * RT + i) * 16 + pbyte), pv[0], pv[1], pv[2], pv[3]);
   }
   __syncthreads();
 
@@ -317,7 +382,7 @@ __global__ __launch_bounds__(256) void dp_prep_kernel(FwdArgs p) {
         t[i] = acc;
       }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sTf[(gb * 16 + i) * LDA + gb * 16 + cc] = t[i];
+      for (int i = 0; i < 16; ++i) sTf[(prep_mblock(gb, gb) * 16 + i) * kPrepLdm + cc] = t[i];
     }
   }
   __syncthreads();
@@ -329,16 +394,17 @@ __global__ __launch_bounds__(256) void dp_prep_kernel(FwdArgs p) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
       for (int kb = j; kb < i; ++kb)
         acc = mm_tile_tb<float, 16>(acc, sA + prep_mblock(i, kb) * 16 * kPrepLdm, kPrepLdm, 0,
-                                    sTf + kb * 16 * LDA + j * 16, LDA, 0);
+                                    sTf + prep_mblock(kb, j) * 16 * kPrepLdm, kPrepLdm, 0);
 #pragma unroll
       for (int e = 0; e < 4; ++e) sS[(4 * (lane >> 4) + e) * 17 + (lane & 15)] = acc[e];
     }
     __syncthreads();
     if (i < NT) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mm_tile_tb<float, 16>(acc, sTf + i * 16 * LDA + i * 16, LDA, 0, sS, 17, 0);
+      acc = mm_tile_tb<float, 16>(acc, sTf + prep_mblock(i, i) * 16 * kPrepLdm, kPrepLdm, 0, sS, 17, 0);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sTf[(i * 16 + 4 * (lane >> 4) + e) * LDA + j * 16 + (lane & 15)] = -acc[e];
+      for (int e = 0; e < 4; ++e)
+        sTf[(prep_mblock(i, j) * 16 + 4 * (lane >> 4) + e) * kPrepLdm + (lane & 15)] = -acc[e];
     }
     __syncthreads();
   }
@@ -358,7 +424,8 @@ __global__ __launch_bounds__(256) void dp_prep_kernel(FwdArgs p) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int j = frag_layout(C) ? 32 * (q >> 2) + 4 * (q & 3) + (e & 3) + 16 * (e >> 2) : q * 8 + e;
-      f[e] = ((j >> 4) > (i >> 4)) ? 0.f : sTf[i * LDA + j] * sB[j];
+      f[e] = ((j >> 4) > (i >> 4)) ? 0.f
+                                   : sTf[(prep_mblock(i >> 4, j >> 4) * 16 + (i & 15)) * kPrepLdm + (j & 15)] * sB[j];
     }
     st_vec16(reinterpret_cast<f16_t*>(wsc + W.oT + idx * 16), f);
   }
