@@ -214,6 +214,33 @@ int dp_osdn_precond_ex_bf16(const void* k, const float* beta, const float* r, in
                             float* d_state, void* kt, dp_stream stream);
 
 /*
+ * Packed variable-length sequences, bf16 with symmetric keys (DeltaProduct
+ * notes sec. 2.2, 2.6, 4.1): nseq independent sequences packed along one
+ * token axis, sequence d being tokens cu_seqlens[d] .. cu_seqlens[d+1]-1.  Each
+ * sequence starts from its own initial state and is chunked on its own (no
+ * chunk straddles two sequences), so every result equals dp_fwd_bf16 run on
+ * that sequence alone.
+ *   q [T, H, dk], k [T, H, n_h, dk], v [T, H, n_h, dv]   bf16
+ *   beta [T, H, n_h], g [T, H] or NULL                   f32
+ *   cu_seqlens [nseq + 1] int32, DEVICE memory: 0 = cu[0] <= cu[1] <= ..
+ *              <= cu[nseq] = T.  Offsets that break this are not read as
+ *              sequences: every sequence is then treated as empty (out is not
+ *              written, final_state receives h0).
+ *   out [T, H, dv] bf16 (float32 with DP_OUT_F32)
+ *   h0, final_state [nseq, H, dk, dv] f32, each nullable (as in dp_fwd_*)
+ *   workspace: dp_fwd_varlen_workspace_size() bytes, 256-byte aligned
+ *   flags: stage bits as for dp_fwd_ex_* (DP_STAGE_SCAN alone needs a
+ *          workspace filled by DP_STAGE_UT for the same inputs) | DP_OUT_F32
+ * Errors: as dp_fwd_ex_bf16; nseq < 1 or T < 0 is DP_EINVAL.
+ */
+int dp_fwd_varlen_workspace_size(int n_h, int nseq, int H, int T, int dk, int dv, int chunk,
+                                 size_t* bytes);
+int dp_fwd_varlen_bf16(const void* q, const void* k, const void* v, const float* beta,
+                       const float* g, const int* cu_seqlens, int nseq, int n_h, int H, int T,
+                       int dk, int dv, int chunk, void* out, float* final_state, const float* h0,
+                       void* workspace, size_t workspace_bytes, int flags, dp_stream stream);
+
+/*
  * One recurrent decode step (DeltaProduct notes sec. 2.2 Eq.(3) and the
  * per-token pseudocode of sec. 2.6; OSDN notes sec. 2.2 Eqs.(2)/(5) for kt):
  * every head applies ONE token's n_h sub-steps to its resident state and

@@ -26,6 +26,7 @@ EXPORTS = (
     "dp_osdn_precond_f32", "dp_osdn_precond_bf16",
     "dp_decode_f32", "dp_decode_bf16",
     "dp_osdn_precond_ex_f32", "dp_osdn_precond_ex_bf16",
+    "dp_fwd_varlen_workspace_size", "dp_fwd_varlen_bf16",
 )
 
 _lib = None
@@ -75,6 +76,11 @@ def load() -> ctypes.CDLL:
         for name in ("dp_osdn_precond_ex_f32", "dp_osdn_precond_ex_bf16"):
             getattr(lib, name).restype = _I
             getattr(lib, name).argtypes = pre_ex
+        lib.dp_fwd_varlen_workspace_size.restype = _I
+        lib.dp_fwd_varlen_workspace_size.argtypes = [_I] * 7 + [ctypes.POINTER(ctypes.c_size_t)]
+        lib.dp_fwd_varlen_bf16.restype = _I
+        lib.dp_fwd_varlen_bf16.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P,
+                                           _P, _P, ctypes.c_size_t, _I, _P]
         dec = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _P]
         for name in ("dp_decode_f32", "dp_decode_bf16"):
             getattr(lib, name).restype = _I
@@ -272,3 +278,62 @@ def decode(q, k, v, beta, state, g=None, *, kt=None, out=None, out_dtype=None, s
             _ptr(out), _ptr(state), flags, _stream(stream))
     _check(rc, f"dp_decode_{suf}")
     return out
+
+
+def varlen_workspace_size(n_h, nseq, H, T, dk, dv, chunk) -> int:
+    """Bytes of device workspace dp_fwd_varlen_bf16 needs."""
+    n = ctypes.c_size_t(0)
+    _check(load().dp_fwd_varlen_workspace_size(n_h, nseq, H, T, dk, dv, chunk, ctypes.byref(n)),
+           "dp_fwd_varlen_workspace_size")
+    return n.value
+
+
+def fwd_varlen(q, k, v, beta, cu_seqlens, g=None, *, chunk: int = 64, h0=None, out=None,
+               final_state=None, return_state: bool = True, workspace=None,
+               stages: int = STAGE_ALL, out_dtype=None, stream=None):
+    """Packed variable-length forward (bf16, symmetric keys) through libdp.
+
+    q [T,H,dk], k [T,H,n_h,dk], v [T,H,n_h,dv] bfloat16, beta [T,H,n_h] f32,
+    g [T,H] f32 or None, cu_seqlens [nseq+1] int32 on the device, h0
+    [nseq,H,dk,dv] f32 or None.  Returns (out [T,H,dv], final_state).
+    """
+    if q.dim() != 3 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("expected q[T,H,dk], k[T,H,n_h,dk], v[T,H,n_h,dv]")
+    T, H, dk = q.shape
+    n_h, dv = k.shape[2], v.shape[3]
+    dev, dt = q.device, q.dtype
+    if dt != torch.bfloat16:
+        raise TypeError("fwd_varlen takes bfloat16 q, k, v")
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be [nseq + 1]")
+    nseq = cu_seqlens.numel() - 1
+    _need(cu_seqlens, "cu_seqlens", torch.int32, (nseq + 1,), dev)
+    _need(k, "k", dt, (T, H, n_h, dk), dev)
+    _need(v, "v", dt, (T, H, n_h, dv), dev)
+    _need(beta, "beta", torch.float32, (T, H, n_h), dev)
+    _need(g, "g", torch.float32, (T, H), dev)
+    _need(h0, "h0", torch.float32, (nseq, H, dk, dv), dev)
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    if out is not None and out_dtype is None:
+        out_dtype = out.dtype
+    odt = dt if out_dtype is None else out_dtype
+    if odt not in (dt, torch.float32):
+        raise TypeError(f"out_dtype must be {dt} or torch.float32")
+    flags = stages | (OUT_F32 if odt == torch.float32 else 0)
+    if out is None:
+        out = torch.empty(T, H, dv, dtype=odt, device=dev)
+    _need(out, "out", odt, (T, H, dv), dev)
+    if final_state is None and return_state:
+        final_state = torch.empty(nseq, H, dk, dv, dtype=torch.float32, device=dev)
+    _need(final_state, "final_state", torch.float32, (nseq, H, dk, dv), dev)
+    if workspace is None:
+        nbytes = varlen_workspace_size(n_h, nseq, H, T, dk, dv, chunk)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    rc = load().dp_fwd_varlen_bf16(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(cu_seqlens),
+                                   nseq, n_h, H, T, dk, dv, chunk, _ptr(out), _ptr(final_state),
+                                   _ptr(h0), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), flags,
+                                   _stream(stream))
+    _check(rc, "dp_fwd_varlen_bf16")
+    return out, final_state

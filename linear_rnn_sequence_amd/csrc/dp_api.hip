@@ -296,6 +296,93 @@ int fwd_impl(int elem, const void* q, const void* k, const void* kt, const void*
   return e == hipSuccess ? DP_OK : DP_EHIP;
 }
 
+// Packed variable-length sequences (bf16, symmetric keys).  The operand blocks
+// are sized for the worst case over all splits of T tokens into nseq sequences,
+// H (ceil(T n_h / C) + nseq) blocks; then the per-sequence first chunks
+// (nseq + 1 ints) and the sink.
+struct VarShape {
+  int n_h, nseq, H, T, dk, dv, chunk;
+};
+
+int check_varlen(const VarShape& v) {
+  if (v.n_h <= 0 || v.nseq <= 0 || v.H <= 0 || v.T < 0 || v.dk <= 0 || v.dv <= 0 || v.chunk <= 0)
+    return DP_EINVAL;
+  const Shape s{v.n_h, v.nseq, v.H, 0, v.dk, v.dv, v.chunk};
+  const int rc = check_shape(s);
+  if (rc != DP_OK) return rc;
+  const long long N = (long long)v.T * v.n_h;
+  if (N > (long long)INT_MAX - 64) return DP_ENOTSUP;
+  const long long nwork = (long long)v.H * ((N + v.chunk - 1) / v.chunk + v.nseq);
+  if (nwork > (long long)INT_MAX) return DP_ENOTSUP;
+  return DP_OK;
+}
+
+long long varlen_nwork(const VarShape& v) {
+  const long long N = (long long)v.T * v.n_h;
+  return (long long)v.H * ((N + v.chunk - 1) / v.chunk + v.nseq);
+}
+
+size_t varlen_blocks_bytes(const VarShape& v) {
+  const dp::Chunk16Layout W = dp::chunk16_layout(v.dk, v.chunk, readout_rows(v.chunk, v.n_h));
+  return align_up((size_t)varlen_nwork(v) * W.bytes, kWsAlign);
+}
+size_t varlen_cbase_bytes(const VarShape& v) { return align_up((size_t)(v.nseq + 1) * 4, kWsAlign); }
+size_t varlen_ws_total(const VarShape& v) {
+  return varlen_blocks_bytes(v) + varlen_cbase_bytes(v) +
+         align_up((size_t)v.nseq * v.H * (v.dv / 16) * 64 * 4, kWsAlign);
+}
+
+int varlen_impl(const void* q, const void* k, const void* v, const float* beta, const float* g,
+                const int* cu_seqlens, int nseq, int n_h, int H, int T, int dk, int dv, int chunk,
+                void* out, float* final_state, const float* h0, void* workspace,
+                size_t workspace_bytes, int flags, dp_stream stream) {
+  const VarShape vs{n_h, nseq, H, T, dk, dv, chunk};
+  int rc = check_varlen(vs);
+  if (rc != DP_OK) return rc;
+  if ((flags & ~(DP_STAGE_ALL | DP_OUT_F32)) != 0) return DP_EINVAL;
+  const int stages = flags & DP_STAGE_ALL;
+  if (stages == 0) return DP_EINVAL;
+  if (cu_seqlens == nullptr) return DP_EINVAL;
+  if (T > 0 && (q == nullptr || k == nullptr || v == nullptr || beta == nullptr || out == nullptr))
+    return DP_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return DP_EINVAL;
+  const size_t need = varlen_ws_total(vs);
+  if (workspace_bytes < need || workspace == nullptr) return DP_EWORKSPACE;
+  if (((uintptr_t)workspace & (kWsAlign - 1)) != 0) return DP_EWORKSPACE;
+
+  dp::FwdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.beta = beta;
+  a.g = g;
+  a.h0 = h0;
+  a.out = out;
+  a.fstate = final_state;
+  a.wsT = workspace;
+  a.cu = cu_seqlens;
+  a.cbase = reinterpret_cast<int*>(static_cast<char*>(workspace) + varlen_blocks_bytes(vs));
+  a.sink = reinterpret_cast<float*>(static_cast<char*>(workspace) + varlen_blocks_bytes(vs) +
+                                    varlen_cbase_bytes(vs));
+  a.nwork = (int)varlen_nwork(vs);
+  a.B = nseq;
+  a.H = H;
+  a.L = T;  // total tokens (the chunk-offset kernel checks cu[nseq] == T)
+  a.n_h = n_h;
+  a.dv = dv;
+  a.RT = readout_rows(chunk, n_h);
+  a.asym = 0;
+  a.out_f32 = (flags & DP_OUT_F32) != 0 ? 1 : 0;
+  fastdiv_magic(n_h, &a.nh_magic, &a.nh_shift);
+
+  int BV = 0, lds = 0;
+  rc = plan(a, 2, dk, chunk, &BV, &lds);
+  if (rc != DP_OK) return rc;
+  const hipError_t e = dispatch_fwd(2, dk, a, chunk, BV, lds, stages, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DP_OK : DP_EHIP;
+}
+
 hipError_t dispatch_decode(int elem, int dk, const dp::DecodeArgs& a, hipStream_t st) {
   if (elem == 4) {
     switch (dk) {
@@ -501,6 +588,24 @@ int dp_osdn_precond_ex_bf16(const void* k, const float* beta, const float* r, in
                             float* d_state, void* kt, dp_stream stream) {
   return precond_impl(2, k, beta, r, flags, B, H, L, dk, eta, dmin, dmax, eps, d_state, kt, true,
                       stream);
+}
+
+int dp_fwd_varlen_workspace_size(int n_h, int nseq, int H, int T, int dk, int dv, int chunk,
+                                 size_t* bytes) {
+  if (bytes == nullptr) return DP_EINVAL;
+  const VarShape vs{n_h, nseq, H, T, dk, dv, chunk};
+  const int rc = check_varlen(vs);
+  if (rc != DP_OK) return rc;
+  *bytes = varlen_ws_total(vs);
+  return DP_OK;
+}
+
+int dp_fwd_varlen_bf16(const void* q, const void* k, const void* v, const float* beta,
+                       const float* g, const int* cu_seqlens, int nseq, int n_h, int H, int T,
+                       int dk, int dv, int chunk, void* out, float* final_state, const float* h0,
+                       void* workspace, size_t workspace_bytes, int flags, dp_stream stream) {
+  return varlen_impl(q, k, v, beta, g, cu_seqlens, nseq, n_h, H, T, dk, dv, chunk, out, final_state,
+                     h0, workspace, workspace_bytes, flags, stream);
 }
 
 int dp_decode_f32(const float* q, const float* k, const float* kt, const float* v,

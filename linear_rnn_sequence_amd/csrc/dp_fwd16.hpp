@@ -154,12 +154,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void d
   int* sLoc = reinterpret_cast<int*>(sG + C);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const long long chunk = blockIdx.x;
-  const int bh = (int)(chunk / p.nc), c = (int)(chunk % p.nc);
-  const int b = bh / p.H, h = bh % p.H;
+  const long long chunk = blockIdx.x;  // operand block index
+  int b, h, c;
+  if (p.cu == nullptr) {
+    const int bh = (int)(chunk / p.nc);
+    c = (int)(chunk % p.nc);
+    b = bh / p.H;
+    h = bh % p.H;
+  } else {
+    // sequence d owns blocks cbase[d] H .. cbase[d+1] H - 1 (head-major inside)
+    if (chunk >= (long long)p.cbase[p.B] * p.H) return;  // past the last block: nothing to do
+    int lo = 0, hi = p.B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((long long)p.cbase[mid] * p.H <= chunk) lo = mid; else hi = mid - 1;
+    }
+    b = lo;
+    const int ncd = p.cbase[b + 1] - p.cbase[b];
+    const int rel = (int)(chunk - (long long)p.cbase[b] * p.H);
+    h = rel / ncd;
+    c = rel % ncd;
+  }
+  const SeqGeom sg = seq_geom(p, b, h, C);
+  const int N = sg.N;
   const int s0 = c * C, n_h = p.n_h;
   const int r0 = s0 + (n_h - 1 - (s0 - fastdiv(s0, p.nh_magic, p.nh_shift) * n_h));  // first readout
-  const long long tok0 = (long long)b * p.L * p.H + h;  // token (b, 0, h)
+  const long long tok0 = sg.tok * p.H + h;  // token (sequence start, head h)
   const bf16_t* kp = static_cast<const bf16_t*>(p.k);
   const bf16_t* qp = static_cast<const bf16_t*>(p.q);
   unsigned char* wsc = static_cast<unsigned char*>(p.wsT) + chunk * W.bytes;
@@ -174,10 +194,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void d
     const int r = idx / TPR, cg = idx % TPR;
     const int s = s0 + r;
     rk[it] = u32x4_t{0u, 0u, 0u, 0u};
-    if (idx < KV && s < p.N) rk[it] = ld16(kp + sub_row(p, s, b, h) * DK + cg * 8);
+    if (idx < KV && s < N) {
+      const int t = fastdiv(s, p.nh_magic, p.nh_shift);
+      rk[it] = ld16(kp + ((tok0 + (long long)t * p.H) * n_h + (s - t * n_h)) * DK + cg * 8);
+    }
   }
   float braw = 0.f, lam = 0.f;
-  if (tid < C && s0 + tid < p.N) {
+  if (tid < C && s0 + tid < N) {
     const int s = s0 + tid;
     const int t = fastdiv(s, p.nh_magic, p.nh_shift);
     const int j = s - t * n_h;
@@ -211,7 +234,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void d
     for (int it = 0; it < NRT; ++it) {
       const int i = it * 16 + (lane & 15);
       const int s = r0 + i * n_h;
-      const bool ok = s < s0 + C && s < p.N;
+      const bool ok = s < s0 + C && s < N;
       const long long tk = tok0 + (long long)fastdiv(ok ? s : s0, p.nh_magic, p.nh_shift) * p.H;
 #pragma unroll
       for (int t = 0; t < QKS; ++t) {
@@ -231,7 +254,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void d
       const int i = idx / TPR, cg = idx % TPR;
       const int s = r0 + i * n_h;
       rq[it] = u32x4_t{0u, 0u, 0u, 0u};
-      if (idx < QV && s < s0 + C && s < p.N) {
+      if (idx < QV && s < s0 + C && s < N) {
         const long long tk = tok0 + (long long)fastdiv(s, p.nh_magic, p.nh_shift) * p.H;
         rq[it] = ld16(qp + tk * DK + cg * 8);
       }
@@ -274,7 +297,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void d
       sEL[lane] = expf(Gl - G);
     }
     const int s = r0 + lane * n_h;
-    const bool ok = lane < RT && s < s0 + C && s < p.N;
+    const bool ok = lane < RT && s < s0 + C && s < N;
     const int loc = ok ? s - s0 : 0;
     const float Gloc = __shfl(G, loc, 64);
     if (lane < RT) {
@@ -609,8 +632,9 @@ void dp_chain_kernel(FwdArgs p) {
   const int bh = f / p.nvb, vb = f % p.nvb;
   const int b = bh / p.H, h = bh % p.H;
   const int v0 = vb * BV;
-  const int nc = p.nc;
-  const unsigned char* wsh = static_cast<const unsigned char*>(p.wsT) + (long long)bh * nc * W.bytes;
+  const SeqGeom sg = seq_geom(p, b, h, C);
+  const int nc = sg.nc, N = sg.N;
+  const unsigned char* wsh = static_cast<const unsigned char*>(p.wsT) + sg.blk0 * W.bytes;
 
   if (wave >= NWC) {
     // =============================================================== copy waves
@@ -643,7 +667,7 @@ void dp_chain_kernel(FwdArgs p) {
       soff[m] = src;
     }
     const bf16_t* vp = static_cast<const bf16_t*>(p.v) + v0;
-    const long long tok0 = (long long)b * p.L * p.H + h;
+    const long long tok0 = sg.tok * p.H + h;
     const uint32_t lds0 = (uint32_t)(uintptr_t)smem;  // LDS byte address of the ring
     // copies of chunk c issued by copy wavefront CW: index m = CW, CW + NCW, ..
     auto issue = [&](auto cwc, int c) {
@@ -664,7 +688,7 @@ void dp_chain_kernel(FwdArgs p) {
           const int pb = o / (C * 16), rs = (o / 16) % C;
           const int q = blk_pos(pb, BV);
           int s = c * C + (rs ^ (8 * (q & 1)));
-          s = s < p.N ? s : p.N - 1;  // rows past the end: any valid row (their beta is 0)
+          s = s < N ? s : N - 1;  // rows past the end: any valid row (their beta is 0)
           const int t = fastdiv(s, p.nh_magic, p.nh_shift);
           const long long row = (tok0 + (long long)t * p.H) * p.n_h + (s - t * p.n_h);
           if (lane < VPI) dma16(vp + row * p.dv + 8 * q, st + W.bytes + 1024 * m);
@@ -827,8 +851,8 @@ void dp_chain_kernel(FwdArgs p) {
       const uint32_t son = (uint32_t)(((c + 1 < nc ? c + 1 : c) % STG) * STAGE);
       // readout rows i < nrd are the tokens t0 + i (uniform, scalar unit)
       const int t0 = fastdiv(c * C, p.nh_magic, p.nh_shift);
-      const int nrd = fastdiv(min(c * C + C, p.N), p.nh_magic, p.nh_shift) - t0;
-      const long long rowbase = (((long long)b * p.L + t0) * p.H + h) * p.dv;
+      const int nrd = fastdiv(min(c * C + C, N), p.nh_magic, p.nh_shift) - t0;
+      const long long rowbase = ((sg.tok + t0) * p.H + h) * p.dv;
       const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
           static_cast<char*>(p.out) + rowbase * es, 0, nrd * HD * es, kBufferDword3);
       // per-tile LDS offsets, opaque so that fragment halves pair on their own base

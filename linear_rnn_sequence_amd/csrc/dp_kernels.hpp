@@ -73,6 +73,13 @@ struct FwdArgs {
   int N;            // L * n_h sub-steps per head
   int B, H, L, n_h, dv, nc, RT, nvb, asym;
   int out_f32;      // 1: out is fp32 whatever the input type
+  // Packed variable-length sequences (bf16 symmetric path): sequence d is
+  // tokens cu[d] .. cu[d+1]-1 of a [T, H, ...] batch, with its own state; B is
+  // then the number of sequences and cbase[d] the first chunk of sequence d
+  // (workspace, filled on the device).  cu == nullptr: B sequences of L tokens.
+  const int* cu;
+  int* cbase;
+  int nwork;        // prep work items (varlen: an upper bound; extra items exit)
   uint32_t nh_magic;  // s / n_h == fastdiv(s, nh_magic, nh_shift) for 0 <= s < 2^31
   int nh_shift;
   // dp_scan_kernel LDS byte offsets
@@ -91,6 +98,32 @@ struct PrecondArgs {
 };
 
 __host__ __device__ constexpr int align16(int x) { return (x + 15) & ~15; }
+
+// Geometry of sequence d of head h: token offset of its first token, sub-steps,
+// chunks and the index of its first operand block (blocks are sequence-major,
+// then head, then chunk).
+struct SeqGeom {
+  long long tok;
+  int N, nc;
+  long long blk0;
+};
+__device__ __forceinline__ SeqGeom seq_geom(const FwdArgs& p, int d, int h, int C) {
+  SeqGeom g;
+  if (p.cu == nullptr) {
+    g.tok = (long long)d * p.L;
+    g.N = p.N;
+    g.nc = p.nc;
+    g.blk0 = ((long long)d * p.H + h) * p.nc;
+  } else {
+    // the chunk count comes from cbase, which is all zero for malformed offsets:
+    // such a sequence then has no chunk and nothing of it is read
+    g.nc = p.cbase[d + 1] - p.cbase[d];
+    g.tok = g.nc > 0 ? p.cu[d] : 0;
+    g.N = g.nc > 0 ? (p.cu[d + 1] - p.cu[d]) * p.n_h : 0;
+    g.blk0 = (long long)p.cbase[d] * p.H + (long long)h * g.nc;
+  }
+  return g;
+}
 
 // Row of sub-step s of head (b, h) in a [B, L, H, n_h, *] tensor:
 // ((b L + t) H + h) n_h + j with t = s / n_h, j = s % n_h.
@@ -1089,6 +1122,52 @@ __global__ __launch_bounds__(64) void dp_precond_kernel(PrecondArgs p) {
 }
 
 // ---------------------------------------------------------------------------
+// dp_varlen_chunks_kernel: first chunk of every packed sequence,
+//   cbase[d] = sum over d' < d of ceil((cu[d'+1] - cu[d']) n_h / C),  d = 0 .. nseq,
+// in one workgroup (each thread a contiguous run of sequences, then a scan of
+// the run totals).  Offsets that are not 0 = cu[0] <= cu[1] <= .. <= cu[nseq]
+// = T make every sequence empty (cbase all zero): nothing is then read or
+// written beyond the initial state.
+template <int C>
+__global__ __launch_bounds__(256) void dp_varlen_chunks_kernel(const int* cu, int nseq, int n_h, int T, int* cbase) {
+  __shared__ long long run[256];
+  __shared__ int bad;
+  const int tid = threadIdx.x;
+  const int per = (nseq + 255) / 256;
+  const int lo = tid * per < nseq ? tid * per : nseq;
+  const int hi = lo + per < nseq ? lo + per : nseq;
+  if (tid == 0) bad = (cu[0] != 0 || cu[nseq] != T) ? 1 : 0;
+  __syncthreads();
+  long long sum = 0;
+  int mybad = 0;
+  for (int d = lo; d < hi; ++d) {
+    const int len = cu[d + 1] - cu[d];
+    if (len < 0) mybad = 1;
+    sum += ((long long)(len > 0 ? len : 0) * n_h + C - 1) / C;
+  }
+  if (mybad) atomicOr(&bad, 1);
+  run[tid] = sum;
+  __syncthreads();
+  if (tid == 0) {
+    long long acc = 0;
+    for (int i = 0; i < 256; ++i) {
+      const long long x = run[i];
+      run[i] = acc;
+      acc += x;
+    }
+  }
+  __syncthreads();
+  long long acc = run[tid];
+  const bool ok = bad == 0;
+  for (int d = lo; d < hi; ++d) {
+    cbase[d] = ok ? (int)acc : 0;
+    const int len = cu[d + 1] - cu[d];
+    acc += ((long long)(len > 0 ? len : 0) * n_h + C - 1) / C;
+  }
+  if (tid == 255) cbase[nseq] = ok ? (int)acc : 0;
+}
+
+// ---------------------------------------------------------------------------
 // Host-side launchers (instantiated per element type and key dimension).
 
 // Raise a kernel's dynamic-LDS limit to the gfx950 maximum (best effort: a
@@ -1195,7 +1274,13 @@ template <int DK, int C, int NRT>
 hipError_t launch_prep(const FwdArgs& a, hipStream_t st) {
   static const bool attr = allow_big_lds(reinterpret_cast<const void*>(&dp_prep_kernel<DK, C, NRT>));
   (void)attr;
-  const long long nchunks = (long long)a.B * a.H * a.nc;
+  if (a.cu != nullptr) {
+    hipLaunchKernelGGL((dp_varlen_chunks_kernel<C>), dim3(1), dim3(256), 0, st, a.cu, a.B, a.n_h, a.L, a.cbase);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const long long nchunks = a.cu != nullptr ? (long long)a.nwork : (long long)a.B * a.H * a.nc;
+  if (nchunks == 0) return hipSuccess;
   hipLaunchKernelGGL((dp_prep_kernel<DK, C, NRT>), dim3((unsigned)nchunks), dim3(256),
                      prep_lds_bytes(DK, C, 16 * NRT), st, a);
   return hipGetLastError();

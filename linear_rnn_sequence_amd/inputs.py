@@ -166,3 +166,22 @@ def retention(B: int, L: int, H: int, seed: int, bias: float = 3.0) -> torch.Ten
     gen = torch.Generator(device="cpu")
     gen.manual_seed(seed)
     return torch.sigmoid(torch.randn(B, L, H, generator=gen, dtype=torch.float32) + bias)
+
+
+def packed_lengths(T: int, seed: int, median: float = 400.0, sigma: float = 1.0,
+                   lmax: int = 8192) -> list:
+    """Document lengths that pack exactly T tokens: log-normal draws (median
+    `median`, log-sd `sigma`) clipped to [1, lmax], the last one cut to fit.
+    The pages pack training text into fixed-size token tensors with the state
+    reset at document boundaries but give no length distribution; this is a
+    stand-in with a realistic spread of short and long documents."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(seed)
+    out, total = [], 0
+    while total < T:
+        x = float(torch.exp(torch.randn(1, generator=gen) * sigma).item()) * median
+        n = max(1, min(lmax, int(round(x))))
+        n = min(n, T - total)
+        out.append(n)
+        total += n
+    return out

@@ -238,3 +238,42 @@ def test_precond_ex_validation_errors_before_hip(lib):
     assert call(L=0, dmin=float("-inf"), dmax=float("inf"), flags=1) == E.DP_OK
     assert lib.dp_osdn_precond_f32(FAKE, FAKE, 1, 1, 0, 16, 3e-3, float("-inf"), 2.0, 1e-6,
                                    FAKE, FAKE, None) == E.DP_EINVAL
+
+
+def test_varlen_validation_errors_before_hip(lib):
+    E = dp.binding
+    f = lib.dp_fwd_varlen_bf16
+
+    def call(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, g=None, cu=FAKE, nseq=2, n_h=2, H=1, T=8, dk=16,
+             dv=16, chunk=16, out=FAKE, fs=None, h0=None, wsp=FAKE, wsb=1 << 30, flags=3):
+        return f(q, k, v, beta, g, cu, nseq, n_h, H, T, dk, dv, chunk, out, fs, h0, wsp, wsb, flags,
+                 None)
+
+    assert call(cu=None) == E.DP_EINVAL
+    assert call(nseq=0) == E.DP_EINVAL
+    assert call(T=-1) == E.DP_EINVAL
+    assert call(q=None) == E.DP_EINVAL
+    assert call(q=FAKE + 8) == E.DP_EINVAL
+    assert call(flags=0) == E.DP_EINVAL
+    assert call(flags=8 | 3) == E.DP_EINVAL
+    assert call(dk=24) == E.DP_ENOTSUP
+    assert call(chunk=8) == E.DP_ENOTSUP
+    assert call(wsb=16) == E.DP_EWORKSPACE
+    assert call(wsp=FAKE + 16) == E.DP_EWORKSPACE
+
+
+def test_varlen_workspace_size(lib):
+    n = SZ(0)
+    # 3 heads, 1000 tokens, n_h 3, chunk 64: blocks for 3 (ceil(3000 / 64) + 5) chunks,
+    # then 6 ints of chunk offsets and the sink (5 x 3 x 8 wavefront slots)
+    assert lib.dp_fwd_varlen_workspace_size(3, 5, 3, 1000, 128, 128, 64, ctypes.byref(n)) == 0
+    blocks = -(-3 * (47 + 5) * bf16_chunk_block(128, 64, 3) // 256) * 256
+    assert n.value == blocks + 256 + -(-5 * 3 * 8 * 64 * 4 // 256) * 256
+    assert lib.dp_fwd_varlen_workspace_size(3, 0, 3, 1000, 128, 128, 64, ctypes.byref(n)) == \
+        dp.binding.DP_EINVAL
+
+
+def test_packed_lengths_cover_the_batch_exactly():
+    from linear_rnn_sequence_amd.inputs import packed_lengths
+    ls = packed_lengths(65536, seed=5)
+    assert sum(ls) == 65536 and min(ls) >= 1 and max(ls) <= 8192 and len(ls) > 20
