@@ -43,6 +43,7 @@ def parse():
                     help="comma-separated extra workloads timed in the same run ('' = none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step timing")
+    ap.add_argument("--no-varlen", action="store_true", help="skip the packed variable-length timing")
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU sample (0: auto)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run device-to-device copies of BYTES (counter calibration)")
@@ -281,6 +282,45 @@ def time_decode(B, H, n_h, dk, dv, tokens=128, reps=5):
                          "alg_bytes_per_launch": nbytes}}
 
 
+def time_varlen(steps, warmup, T=65536):
+    """Packed variable-length forward: T tokens of log-normal document lengths
+    (H=16, dk=dv=128, n_h=2, bf16), each document its own sequence and state."""
+    import itertools
+
+    import torch
+
+    import linear_rnn_sequence_amd as dp
+    from linear_rnn_sequence_amd.inputs import WORKLOADS, make, packed_lengths
+
+    dev = torch.device("cuda:0")
+    w = WORKLOADS["c3b"]
+    lengths = packed_lengths(T, seed=11)
+    inp = make(w.scaled(B=1, L=T))
+    d = {n: inp[n][0].contiguous().to(dev) for n in ("q", "k", "v", "beta")}
+    cu = torch.tensor([0] + list(itertools.accumulate(lengths)), dtype=torch.int32, device=dev)
+    nseq = len(lengths)
+    ws = torch.empty(dp.varlen_workspace_size(w.n_h, nseq, w.H, T, w.dk, w.dv, w.chunk),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty(T, w.H, w.dv, dtype=torch.bfloat16, device=dev)
+    fs = torch.empty(nseq, w.H, w.dk, w.dv, dtype=torch.float32, device=dev)
+
+    def step():
+        dp.fwd_varlen(d["q"], d["k"], d["v"], d["beta"], cu, chunk=w.chunk, out=out, final_state=fs,
+                      workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = 1e3 * (time.perf_counter() - t0) / steps
+    return {"workload": f"varlen: {nseq} packed documents, T={T} tokens, H={w.H} n_h={w.n_h} "
+                        f"dk={w.dk} dv={w.dv} chunk={w.chunk} bf16",
+            "value": T / (ms / 1e3), "unit": "tokens/s", "ms_per_step": ms}
+
+
 # ---------------------------------------------------------------- CPU baseline
 
 def cpu_baseline(w, inp, nheads, min_seconds=10.0, max_pass_seconds=30.0, max_passes=100):
@@ -440,6 +480,8 @@ def main():
         del r2
     if also:
         line["also"] = also
+    if not a.no_varlen:
+        line["varlen"] = time_varlen(a.steps, a.warmup)
     if not a.no_decode:
         # the pages' decode protocol (batch 1) and a serving-size batch, head shape of c3
         line["decode"] = {"b1": time_decode(1, 16, 3, 128, 128),
