@@ -844,50 +844,51 @@ void dp_chain_kernel(FwdArgs p) {
         static_for<LA>([&](auto kc) { key_frag(ok, ok1, kc); });
       }
     }
-    for (int c = 0; c < nc; ++c) {
-      const uint32_t so = (uint32_t)((c % STG) * STAGE);
-      const unsigned char* st = smem + so;
-      // stage of the next chunk (this one's again after the last: the reads are then unused)
-      const uint32_t son = (uint32_t)(((c + 1 < nc ? c + 1 : c) % STG) * STAGE);
-      // readout rows i < nrd are the tokens t0 + i (uniform, scalar unit)
-      const int t0 = fastdiv(c * C, p.nh_magic, p.nh_shift);
-      const int nrd = fastdiv(min(c * C + C, N), p.nh_magic, p.nh_shift) - t0;
-      const long long rowbase = ((sg.tok + t0) * p.H + h) * p.dv;
-      const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
-          static_cast<char*>(p.out) + rowbase * es, 0, nrd * HD * es, kBufferDword3);
-      // per-tile LDS offsets, opaque so that fragment halves pair on their own base
-      uint32_t oK[NCT], oK1[NCT], oT[CST], oQ[NRT], oP[NRT];
+    // Per-chunk context: LDS offsets of the chunk's stage (opaque, so that the
+    // two halves of a key fragment keep their own bases) and its readout rows.
+    // The context of chunk c + 1 is built while chunk c runs, so that little
+    // is left between the chunk barrier and the next products.
+    struct ChunkCtx {
+      uint32_t so, oK[NCT], oK1[NCT], oT[CST], oQ[NRT], oP[NRT];
+      int t0, nrd;  // readout rows i < nrd are the tokens t0 + i
+    };
+    auto make_ctx = [&](int cc) __attribute__((always_inline)) {
+      ChunkCtx x;
+      x.so = (uint32_t)((cc % STG) * STAGE);
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
-        oK[ct] = so + W.oK + lrK + ct * 256;
-        oK1[ct] = oK[ct] + C * 16;  // second half of each key fragment: one block on
-        asm volatile("" : "+v"(oK[ct]), "+v"(oK1[ct]));
+        x.oK[ct] = x.so + W.oK + lrK + ct * 256;
+        x.oK1[ct] = x.oK[ct] + C * 16;  // second half of each key fragment: one block on
+        asm volatile("" : "+v"(x.oK[ct]), "+v"(x.oK1[ct]));
       }
       // T diag(beta): one base per 32-column tile t (rows from 32 t on when trimmed)
 #pragma unroll
       for (int t = 0; t < CST; ++t) {
-        oT[t] = so + W.oT + (TRIM ? t_block_byte(C, t) : 4 * t * C * 16) + (lane >> 4) * (C - TS * t) * 16 +
-                (lane & 15) * 16;
-        asm volatile("" : "+v"(oT[t]));
+        x.oT[t] = x.so + W.oT + (TRIM ? t_block_byte(C, t) : 4 * t * C * 16) + (lane >> 4) * (C - TS * t) * 16 +
+                  (lane & 15) * 16;
+        asm volatile("" : "+v"(x.oT[t]));
       }
 #pragma unroll
       for (int it = 0; it < NRT; ++it) {
-        oQ[it] = so + W.oQ + lrQ + it * 256;
-        oP[it] = so + W.oP + lrP + it * 256;
-        asm volatile("" : "+v"(oQ[it]), "+v"(oP[it]));
+        x.oQ[it] = x.so + W.oQ + lrQ + it * 256;
+        x.oP[it] = x.so + W.oP + lrP + it * 256;
+        asm volatile("" : "+v"(x.oQ[it]), "+v"(x.oP[it]));
       }
-      // the next chunk's first key tiles (EARLY)
-      uint32_t okn[EARLY ? LA / KST : 1], ok1n[EARLY ? LA / KST : 1];
-      if constexpr (EARLY) {
-#pragma unroll
-        for (int ct = 0; ct < LA / KST; ++ct) {
-          okn[ct] = son + W.oK + lrK + ct * 256;
-          ok1n[ct] = okn[ct] + C * 16;
-          asm volatile("" : "+v"(okn[ct]), "+v"(ok1n[ct]));
-        }
-      } else {
-        load_small(so);
-      }
+      x.t0 = fastdiv(cc * C, p.nh_magic, p.nh_shift);
+      x.nrd = fastdiv(min(cc * C + C, N), p.nh_magic, p.nh_shift) - x.t0;
+      return x;
+    };
+    ChunkCtx cur = make_ctx(0);
+    for (int c = 0; c < nc; ++c) {
+      const uint32_t so = cur.so;
+      const unsigned char* st = smem + so;
+      const uint32_t *oK = cur.oK, *oK1 = cur.oK1, *oT = cur.oT, *oQ = cur.oQ, *oP = cur.oP;
+      const long long rowbase = ((sg.tok + cur.t0) * p.H + h) * p.dv;
+      const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+          static_cast<char*>(p.out) + rowbase * es, 0, cur.nrd * HD * es, kBufferDword3);
+      // the next chunk's context (this chunk's again after the last: its reads are then unused)
+      ChunkCtx nxt;
+      if constexpr (!EARLY) load_small(so);
 
       f32x4_t accX[NCT], accU[NCT], z[NRT];
       f16x4_t xq[NCT], uq[NCT], usq[NCT];
@@ -989,11 +990,12 @@ void dp_chain_kernel(FwdArgs p) {
           }
         });
         if constexpr (i >= LA && i - LA < NS) mfma_step(std::integral_constant<int, i - LA>{});
+        if constexpr (i == LA + 2) nxt = make_ctx(c + 1 < nc ? c + 1 : c);
         if constexpr (EARLY) {
           // steps 0 .. LA-1 were read during the previous chunk
           if constexpr (i >= LA && i < NS) load_frag(std::integral_constant<int, i>{});
-          if constexpr (i >= NSP && i < NSP + LA) key_frag(okn, ok1n, std::integral_constant<int, i - NSP>{});
-          if constexpr (i == NS + LA) load_small(son);  // past this chunk's last use of them
+          if constexpr (i >= NSP && i < NSP + LA) key_frag(nxt.oK, nxt.oK1, std::integral_constant<int, i - NSP>{});
+          if constexpr (i == NS + LA) load_small(nxt.so);  // past this chunk's last use of them
         } else {
           if constexpr (i < NS) load_frag(std::integral_constant<int, i>{});
         }
@@ -1030,6 +1032,7 @@ void dp_chain_kernel(FwdArgs p) {
         }
       }
       if (c + 1 < nc) block_sync_lds();  // X(c + 1)
+      cur = nxt;
     }
   } else {
   if (nc > 0) block_sync_lds();  // X(0)
