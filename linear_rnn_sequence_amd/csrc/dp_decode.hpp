@@ -18,7 +18,7 @@
 // is laid out for that stream.
 //
 // Layout of work: a workgroup owns one head and CW consecutive value columns
-// (CW = min(dv, 64)); each of its 256 threads holds one column of RP
+// (CW = min(dv, 64)); each of its 256 or 512 threads holds one column of RP
 // consecutive state rows in registers, so every load and store of a row of
 // the state is one contiguous CW * 4-byte segment per wavefront.  The column
 // sums H^T k and H^T q reduce the threads' row partials through LDS (one
@@ -39,18 +39,21 @@ struct DecodeArgs {
   int B, H, n_h, dv, out_f32;
 };
 
-constexpr int kDecodeThreads = 256;
+// Threads per workgroup: 512 where the head slice holds at least 512 state
+// elements (16 rows of a column per thread at dk = 128, CW = 64), else 256.
+__host__ __device__ constexpr int decode_threads(int dk, int cw) { return dk * cw >= 512 ? 512 : 256; }
 
 // LDS floats of dp_decode_kernel: read keys and write keys (n_h x DK each),
 // q (DK), the block's value columns (n_h x CW), 1/|k| and beta (n_h each),
-// two reduction buffers (NRG x CW each).
+// two reduction buffers (one float per thread each).
 __host__ __device__ constexpr int decode_lds_floats(int dk, int cw, int n_h, int asym) {
-  return n_h * dk * (1 + asym) + dk + n_h * cw + 2 * n_h + 2 * (kDecodeThreads / cw) * cw;
+  return n_h * dk * (1 + asym) + dk + n_h * cw + 2 * n_h + 2 * decode_threads(dk, cw);
 }
 
 template <typename T, int DK, int CW>
-__global__ __launch_bounds__(kDecodeThreads) void dp_decode_kernel(DecodeArgs p) {
-  constexpr int NRG = kDecodeThreads / CW;  // row groups
+__global__ __launch_bounds__(512) void dp_decode_kernel(DecodeArgs p) {
+  constexpr int NTH = decode_threads(DK, CW);
+  constexpr int NRG = NTH / CW;  // row groups
   constexpr int RP = DK / NRG;              // state rows per thread
   static_assert(RP >= 1 && DK % NRG == 0, "row split");
   extern __shared__ float dsm[];
@@ -77,22 +80,22 @@ __global__ __launch_bounds__(kDecodeThreads) void dp_decode_kernel(DecodeArgs p)
   for (int i = 0; i < RP; ++i) hs[i] = st[(long long)i * p.dv];
 
   const T* kp = static_cast<const T*>(p.k) + bh * n_h * DK;
-  for (int x = tid; x < n_h * DK; x += kDecodeThreads) sK[x] = to_f32(kp[x]);
+  for (int x = tid; x < n_h * DK; x += NTH) sK[x] = to_f32(kp[x]);
   if (asym) {
     const T* wp = static_cast<const T*>(p.kt) + bh * n_h * DK;
-    for (int x = tid; x < n_h * DK; x += kDecodeThreads) sW[x] = to_f32(wp[x]);
+    for (int x = tid; x < n_h * DK; x += NTH) sW[x] = to_f32(wp[x]);
   }
   const T* qp = static_cast<const T*>(p.q) + bh * DK;
-  for (int x = tid; x < DK; x += kDecodeThreads) sQ[x] = to_f32(qp[x]);
+  for (int x = tid; x < DK; x += NTH) sQ[x] = to_f32(qp[x]);
   const T* vp = static_cast<const T*>(p.v) + bh * n_h * p.dv + (col - cl);
-  for (int x = tid; x < n_h * CW; x += kDecodeThreads) sV[x] = to_f32(vp[(long long)(x / CW) * p.dv + x % CW]);
-  for (int j = tid; j < n_h; j += kDecodeThreads) sB[j] = fminf(fmaxf(p.beta[bh * n_h + j], 0.f), 2.f);
+  for (int x = tid; x < n_h * CW; x += NTH) sV[x] = to_f32(vp[(long long)(x / CW) * p.dv + x % CW]);
+  for (int j = tid; j < n_h; j += NTH) sB[j] = fminf(fmaxf(p.beta[bh * n_h + j], 0.f), 2.f);
   const float gt = p.g != nullptr ? p.g[bh] : 1.f;
   block_sync_lds();
 
   // key norms: wavefront w takes sub-steps w, w + 4, ...
   const int wave = tid >> 6, lane = tid & 63;
-  for (int j = wave; j < n_h; j += kDecodeThreads / 64) {
+  for (int j = wave; j < n_h; j += NTH / 64) {
     float s = 0.f;
     for (int x = lane; x < DK; x += 64) s = fmaf(sK[j * DK + x], sK[j * DK + x], s);
 #pragma unroll
@@ -157,7 +160,8 @@ hipError_t launch_decode_cw(const DecodeArgs& a, hipStream_t st) {
   static const bool attr = allow_big_lds(reinterpret_cast<const void*>(&dp_decode_kernel<T, DK, CW>));
   (void)attr;
   const int lds = 4 * decode_lds_floats(DK, CW, a.n_h, a.kt != nullptr ? 1 : 0);
-  hipLaunchKernelGGL((dp_decode_kernel<T, DK, CW>), dim3((unsigned)blocks), dim3(kDecodeThreads), lds, st, a);
+  hipLaunchKernelGGL((dp_decode_kernel<T, DK, CW>), dim3((unsigned)blocks), dim3(decode_threads(DK, CW)), lds, st,
+                     a);
   return hipGetLastError();
 }
 
