@@ -36,11 +36,11 @@ def _load():
             _build.build()
         lib = ctypes.CDLL(_build.LIB)
         lib.oracle_fwd.restype = ctypes.c_int
-        lib.oracle_fwd.argtypes = [_D, _D, _D, _D, _D, _D, ctypes.c_int, ctypes.c_int,
+        lib.oracle_fwd.argtypes = [_D, _D, _D, _D, _D, _D, _D, ctypes.c_int, ctypes.c_int,
                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                    _D, _D, _D, ctypes.c_int]
         lib.oracle_fwd_heads.restype = ctypes.c_int
-        lib.oracle_fwd_heads.argtypes = [_D, _D, _D, _D, _D, _D, ctypes.c_int, ctypes.c_int,
+        lib.oracle_fwd_heads.argtypes = [_D, _D, _D, _D, _D, _D, _D, ctypes.c_int, ctypes.c_int,
                                          ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                          ctypes.c_int, _D, _LP, ctypes.c_int, _D, _D,
                                          ctypes.c_int]
@@ -80,7 +80,7 @@ def num_threads() -> int:
     return _load().oracle_num_threads()
 
 
-def _shapes(q, k, v, beta, g, kt, h0):
+def _shapes(q, k, v, beta, g, kt, h0, ga=None):
     if q.ndim != 4 or k.ndim != 5 or v.ndim != 5 or beta.ndim != 4:
         raise ValueError("expected q[B,L,H,dk], k[B,L,H,n_h,dk], v[B,L,H,n_h,dv], beta[B,L,H,n_h]")
     B, L, H, dk = q.shape
@@ -94,41 +94,44 @@ def _shapes(q, k, v, beta, g, kt, h0):
         raise ValueError("g must be [B,L,H]")
     if kt is not None and kt.shape != k.shape:
         raise ValueError("kt must have the shape of k")
+    if ga is not None and ga.shape != (B, L, H, dk):
+        raise ValueError("ga must be [B,L,H,dk]")
     if h0 is not None and h0.shape != (B, H, dk, dv):
         raise ValueError("h0 must be [B,H,dk,dv]")
     return B, L, H, n_h, dk, dv
 
 
-def fwd(q, k, v, beta, g=None, kt=None, h0=None, nthreads=0):
+def fwd(q, k, v, beta, g=None, kt=None, h0=None, nthreads=0, ga=None):
     """Sequential fp64 forward over every head.
 
+    ``ga [B,L,H,dk]``: optional per-key-channel gate (the KDA host).
     Returns ``(out [B,L,H,dv], final_state [B,H,dk,dv])`` as float64 arrays.
     """
-    q, k, v, beta, g, kt, h0 = (_f64(a) for a in (q, k, v, beta, g, kt, h0))
-    B, L, H, n_h, dk, dv = _shapes(q, k, v, beta, g, kt, h0)
+    q, k, v, beta, g, kt, h0, ga = (_f64(a) for a in (q, k, v, beta, g, kt, h0, ga))
+    B, L, H, n_h, dk, dv = _shapes(q, k, v, beta, g, kt, h0, ga)
     out = np.zeros((B, L, H, dv), np.float64)
     fs = np.zeros((B, H, dk, dv), np.float64)
-    rc = _load().oracle_fwd(_ptr(q), _ptr(k), _ptr(kt), _ptr(v), _ptr(beta), _ptr(g), n_h, B,
-                            H, L, dk, dv, _ptr(h0), _ptr(out), _ptr(fs), int(nthreads))
+    rc = _load().oracle_fwd(_ptr(q), _ptr(k), _ptr(kt), _ptr(v), _ptr(beta), _ptr(g), _ptr(ga),
+                            n_h, B, H, L, dk, dv, _ptr(h0), _ptr(out), _ptr(fs), int(nthreads))
     if rc != 0:
         raise RuntimeError(f"oracle_fwd failed ({rc})")
     return out, fs
 
 
-def fwd_heads(q, k, v, beta, heads, g=None, kt=None, h0=None, nthreads=0):
+def fwd_heads(q, k, v, beta, heads, g=None, kt=None, h0=None, nthreads=0, ga=None):
     """Forward for the listed flattened heads ``b*H + h`` only.
 
     Returns compact ``(out [n,L,dv], final_state [n,dk,dv])``; each head is
     computed exactly as :func:`fwd` computes it.
     """
-    q, k, v, beta, g, kt, h0 = (_f64(a) for a in (q, k, v, beta, g, kt, h0))
-    B, L, H, n_h, dk, dv = _shapes(q, k, v, beta, g, kt, h0)
+    q, k, v, beta, g, kt, h0, ga = (_f64(a) for a in (q, k, v, beta, g, kt, h0, ga))
+    B, L, H, n_h, dk, dv = _shapes(q, k, v, beta, g, kt, h0, ga)
     hs = np.ascontiguousarray(np.asarray(heads, dtype=np.int64))
     n = hs.size
     out = np.zeros((n, L, dv), np.float64)
     fs = np.zeros((n, dk, dv), np.float64)
     rc = _load().oracle_fwd_heads(_ptr(q), _ptr(k), _ptr(kt), _ptr(v), _ptr(beta), _ptr(g),
-                                  n_h, B, H, L, dk, dv, _ptr(h0), hs.ctypes.data_as(_LP), n,
+                                  _ptr(ga), n_h, B, H, L, dk, dv, _ptr(h0), hs.ctypes.data_as(_LP), n,
                                   _ptr(out), _ptr(fs), int(nthreads))
     if rc != 0:
         raise RuntimeError(f"oracle_fwd_heads failed ({rc})")

@@ -86,13 +86,16 @@ int oracle_num_threads(void)
 
 /*
  * One head (b, h) of the sequential DeltaProduct forward ([DP] sec. 2.2
- * Eq.(3), sec. 2.6), with an optional asymmetric write key ([OSDN] sec. 2.2).
+ * Eq.(3), sec. 2.6), with an optional asymmetric write key ([OSDN] sec. 2.2)
+ * and an optional per-key-channel gate ga [B, L, H, dk] (the KDA host of
+ * [OSDN] sec. 2.7: H <- Diag(alpha_t) H before the token's sub-steps, so the
+ * residual and the write see the decayed state).
  * out_h points at this head's first output row; consecutive tokens are
  * out_stride doubles apart.  S (dk*dv), kh (dk) and e (dv) are scratch.
  */
 static void run_head(const double* q, const double* k, const double* kt, const double* v,
-                     const double* beta, const double* g, int n_h, long b, long h, int H,
-                     int L, int dk, int dv, const double* h0_h, double* out_h,
+                     const double* beta, const double* g, const double* ga, int n_h, long b,
+                     long h, int H, int L, int dk, int dv, const double* h0_h, double* out_h,
                      size_t out_stride, double* fs_h, double* S, double* kh, double* e)
 {
     if (h0_h)
@@ -102,6 +105,12 @@ static void run_head(const double* q, const double* k, const double* kt, const d
 
     for (long t = 0; t < L; ++t) {
         const size_t tok = ((size_t)b * L + t) * H + h; /* (b, t, h) */
+        if (ga) {
+            /* Diag(alpha_t) H: row r of the state (key channel r) scales by alpha_t[r] */
+            const double* al = ga + tok * dk;
+            for (int r = 0; r < dk; ++r)
+                for (int c = 0; c < dv; ++c) S[(size_t)r * dv + c] *= al[r];
+        }
         if (g) {
             /* H_{i,0} = g_i H_{i-1}: once per token, before its sub-steps */
             const double gt = g[tok];
@@ -145,7 +154,7 @@ static void run_head(const double* q, const double* k, const double* kt, const d
  * bad arguments, -2 when scratch memory could not be allocated.
  */
 static int fwd_impl(const double* q, const double* k, const double* kt, const double* v,
-                    const double* beta, const double* g, int n_h, int B, int H, int L,
+                    const double* beta, const double* g, const double* ga, int n_h, int B, int H, int L,
                     int dk, int dv, const double* h0, const long* heads, int nsel,
                     double* out, double* final_state, int nthreads)
 {
@@ -189,7 +198,7 @@ static int fwd_impl(const double* q, const double* k, const double* kt, const do
             out_stride = (size_t)H * dv;
             fs_h = final_state ? final_state + (size_t)bh * dk * dv : NULL;
         }
-        run_head(q, k, kt, v, beta, g, n_h, b, h, H, L, dk, dv, h0_h, out_h, out_stride,
+        run_head(q, k, kt, v, beta, g, ga, n_h, b, h, H, L, dk, dv, h0_h, out_h, out_stride,
                  fs_h, S, kh, e);
         free(S); free(kh); free(e);
     }
@@ -198,11 +207,11 @@ static int fwd_impl(const double* q, const double* k, const double* kt, const do
 
 /* Full forward over all heads.  nthreads <= 0: OpenMP default. */
 int oracle_fwd(const double* q, const double* k, const double* kt, const double* v,
-               const double* beta, const double* g, int n_h, int B, int H, int L,
-               int dk, int dv, const double* h0, double* out, double* final_state,
+               const double* beta, const double* g, const double* ga, int n_h, int B, int H,
+               int L, int dk, int dv, const double* h0, double* out, double* final_state,
                int nthreads)
 {
-    return fwd_impl(q, k, kt, v, beta, g, n_h, B, H, L, dk, dv, h0, NULL, 0, out,
+    return fwd_impl(q, k, kt, v, beta, g, ga, n_h, B, H, L, dk, dv, h0, NULL, 0, out,
                     final_state, nthreads);
 }
 
@@ -211,12 +220,12 @@ int oracle_fwd(const double* q, const double* k, const double* kt, const double*
  * listed head is computed exactly as oracle_fwd computes it; outputs compact.
  */
 int oracle_fwd_heads(const double* q, const double* k, const double* kt, const double* v,
-                     const double* beta, const double* g, int n_h, int B, int H, int L,
-                     int dk, int dv, const double* h0, const long* heads, int nsel,
+                     const double* beta, const double* g, const double* ga, int n_h, int B,
+                     int H, int L, int dk, int dv, const double* h0, const long* heads, int nsel,
                      double* out, double* final_state, int nthreads)
 {
     if (!heads) return -1;
-    return fwd_impl(q, k, kt, v, beta, g, n_h, B, H, L, dk, dv, h0, heads, nsel, out,
+    return fwd_impl(q, k, kt, v, beta, g, ga, n_h, B, H, L, dk, dv, h0, heads, nsel, out,
                     final_state, nthreads);
 }
 

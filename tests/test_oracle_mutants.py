@@ -50,6 +50,10 @@ MUTANTS = {
         "d[r] = clampd(rt * (d[r] + coef * (kh[r] * kh[r])), dmin, dmax);"),
     "phase1_beta_free_keeps_beta": ("const double bu = beta_aware ? bt : 1.0;",
                                     "const double bu = bt;"),
+    "channel_gate_on_columns": ("for (int c = 0; c < dv; ++c) S[(size_t)r * dv + c] *= al[r];",
+                                "for (int c = 0; c < dv; ++c) S[(size_t)r * dv + c] *= al[c % dk];"),
+    "channel_gate_ignored": ("for (int c = 0; c < dv; ++c) S[(size_t)r * dv + c] *= al[r];",
+                             "for (int c = 0; c < dv; ++c) S[(size_t)r * dv + c] *= 1.0;"),
 }
 
 _EMIT_LATE = (

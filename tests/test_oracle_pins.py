@@ -591,3 +591,67 @@ def test_phase1_beta_free_closed_form():
     fp = eta / (1 - r + eta)
     np.testing.assert_allclose(kt2[0, :, 0, 0], fp + (r - eta) ** (t - 1) * (0.6 - fp), atol=1e-13)
     np.testing.assert_allclose(d2[0, 0, 1:], 0.6 * r ** L, rtol=1e-13)
+
+
+# ---------------------------------------------------------------- [OSDN] KDA host: per-channel gate
+
+
+def test_channel_gate_without_writes_is_a_diagonal_decay():
+    """[OSDN] sec. 2.7: the KDA host decays the state per key channel, H <- Diag(alpha_t) H,
+    before the token's update.  With beta = 0 nothing is written, so H_t =
+    Diag(prod_{s <= t} alpha_s) H_0 row by row, and out_t = H_t^T q_t."""
+    rng = np.random.default_rng(31)
+    B, L, H, n_h, dk, dv = 1, 7, 2, 2, 5, 3
+    q = rng.standard_normal((B, L, H, dk))
+    k = rng.standard_normal((B, L, H, n_h, dk))
+    v = rng.standard_normal((B, L, H, n_h, dv))
+    beta = np.zeros((B, L, H, n_h))
+    ga = rng.uniform(0.2, 1.0, (B, L, H, dk))
+    h0 = rng.standard_normal((B, H, dk, dv))
+    out, fs = oracle.fwd(q, k, v, beta, ga=ga, h0=h0)
+    decay = np.cumprod(ga, axis=1)  # [B, L, H, dk]
+    for t in range(L):
+        Ht = decay[0, t][:, :, None] * h0[0]  # [H, dk, dv]
+        np.testing.assert_allclose(out[0, t], np.einsum("hkv,hk->hv", Ht, q[0, t]), atol=1e-13)
+    np.testing.assert_allclose(fs[0], decay[0, -1][:, :, None] * h0[0], atol=1e-14)
+
+
+def test_channel_gate_kda_step_closed_form():
+    """[OSDN] sec. 2.7: H_1 = (I - b kt k^T) Diag(alpha) H_0 + b kt v^T.  With k = e_1,
+    kt = c e_1 and b = 1, row 0 becomes (1 - c) alpha_0 H_0[0] + c v and every other row
+    r is alpha_r H_0[r]: the decay acts on rows (key channels), before the write."""
+    rng = np.random.default_rng(32)
+    dk, dv, c = 4, 3, 0.7
+    h0 = rng.standard_normal((1, 1, dk, dv))
+    alpha = np.array([0.9, 0.5, 0.25, 0.8])
+    v = rng.standard_normal(dv)
+    k = np.zeros((1, 1, 1, 1, dk))
+    k[..., 0] = 2.0  # normalised inside to e_1
+    kt = np.zeros_like(k)
+    kt[..., 0] = c
+    q = rng.standard_normal((1, 1, 1, dk))
+    _, fs = oracle.fwd(q, k, v.reshape(1, 1, 1, 1, dv), np.ones((1, 1, 1, 1)), kt=kt, h0=h0,
+                       ga=alpha.reshape(1, 1, 1, dk))
+    want = alpha[:, None] * h0[0, 0]
+    want[0] = (1 - c) * alpha[0] * h0[0, 0, 0] + c * v
+    np.testing.assert_allclose(fs[0, 0], want, atol=1e-14)
+
+
+def test_uniform_channel_gate_is_the_scalar_gate():
+    """A per-channel gate equal in every channel is the scalar gate of [DP] sec. 2.6, and
+    the two compose by product."""
+    rng = np.random.default_rng(33)
+    B, L, H, n_h, dk, dv = 2, 9, 2, 3, 6, 4
+    q = rng.standard_normal((B, L, H, dk))
+    k = rng.standard_normal((B, L, H, n_h, dk))
+    v = rng.standard_normal((B, L, H, n_h, dv))
+    beta = rng.uniform(0, 2, (B, L, H, n_h))
+    g = rng.uniform(0.3, 1.0, (B, L, H))
+    o1, f1 = oracle.fwd(q, k, v, beta, g=g)
+    o2, f2 = oracle.fwd(q, k, v, beta, ga=np.repeat(g[..., None], dk, axis=-1))
+    np.testing.assert_allclose(o2, o1, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(f2, f1, rtol=1e-12, atol=1e-13)
+    g2 = rng.uniform(0.3, 1.0, (B, L, H))
+    o3, _ = oracle.fwd(q, k, v, beta, g=g, ga=np.repeat(g2[..., None], dk, axis=-1))
+    o4, _ = oracle.fwd(q, k, v, beta, g=g * g2)
+    np.testing.assert_allclose(o3, o4, rtol=1e-12, atol=1e-13)
