@@ -242,10 +242,12 @@ int dp_fwd_varlen_bf16(const void* q, const void* k, const void* v, const float*
 
 /*
  * One recurrent decode step (DeltaProduct notes sec. 2.2 Eq.(3) and the
- * per-token pseudocode of sec. 2.6; OSDN notes sec. 2.2 Eqs.(2)/(5) for kt):
- * every head applies ONE token's n_h sub-steps to its resident state and
- * reads it out, exactly as one token of dp_fwd_* / dp_fwd_wk_*:
- *   H <- g H (gated only);  for j < n_h: H <- H + clamp(b_j,0,2) w_j (v_j - H^T kn_j)^T;
+ * per-token pseudocode of sec. 2.6; OSDN notes sec. 2.2 Eqs.(2)/(5) for kt,
+ * sec. 2.7 for the KDA host's per-key-channel gate): every head applies ONE
+ * token's n_h sub-steps to its resident state and reads it out, exactly as
+ * one token of dp_fwd_* / dp_fwd_wk_* (with ga == NULL):
+ *   H <- g H;  H <- Diag(ga) H  (each when given);
+ *   for j < n_h: H <- H + clamp(b_j,0,2) w_j (v_j - H^T kn_j)^T;
  *   out = H^T q,
  * kn_j = k_j / max(|k_j|_2, 1e-6), w_j = kn_j (kt == NULL) or kt_j as given.
  * The per-token tensors are the forward's with L = 1:
@@ -256,6 +258,8 @@ int dp_fwd_varlen_bf16(const void* q, const void* k, const void* v, const float*
  *   beta [B, H, n_h]       f32
  *   g    [B, H]            f32   or NULL (no gate); the state is multiplied
  *                                by g as given
+ *   ga   [B, H, dk]        f32   or NULL: per-key-channel gate alpha (KDA
+ *                                host), state row r multiplied by ga[r]
  *   out  [B, H, dv]          T   written (float32 with DP_OUT_F32; the _f32
  *                                entry point always writes float32)
  *   state [B, H, dk, dv]   f32   in/out: H_{t-1} on entry, H_t on exit (the
@@ -267,11 +271,11 @@ int dp_fwd_varlen_bf16(const void* q, const void* k, const void* v, const float*
  * DP_ENOTSUP (dk or dv outside {16, 32, 64, 128}, n_h > 64), DP_EHIP.
  */
 int dp_decode_f32(const float* q, const float* k, const float* kt, const float* v,
-                  const float* beta, const float* g, int n_h, int B, int H, int dk, int dv,
-                  float* out, float* state, int flags, dp_stream stream);
+                  const float* beta, const float* g, const float* ga, int n_h, int B, int H,
+                  int dk, int dv, float* out, float* state, int flags, dp_stream stream);
 int dp_decode_bf16(const void* q, const void* k, const void* kt, const void* v,
-                   const float* beta, const float* g, int n_h, int B, int H, int dk, int dv,
-                   void* out, float* state, int flags, dp_stream stream);
+                   const float* beta, const float* g, const float* ga, int n_h, int B, int H,
+                   int dk, int dv, void* out, float* state, int flags, dp_stream stream);
 
 #ifdef __cplusplus
 }

@@ -81,7 +81,7 @@ def load() -> ctypes.CDLL:
         lib.dp_fwd_varlen_bf16.restype = _I
         lib.dp_fwd_varlen_bf16.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P,
                                            _P, _P, ctypes.c_size_t, _I, _P]
-        dec = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _P]
+        dec = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _P]
         for name in ("dp_decode_f32", "dp_decode_bf16"):
             getattr(lib, name).restype = _I
             getattr(lib, name).argtypes = dec
@@ -242,13 +242,15 @@ def osdn_precond(k, beta, *, eta: float = 3e-3, dmin: float = 0.5, dmax: float =
     return kt, d_state
 
 
-def decode(q, k, v, beta, state, g=None, *, kt=None, out=None, out_dtype=None, stream=None):
+def decode(q, k, v, beta, state, g=None, *, kt=None, ga=None, out=None, out_dtype=None,
+           stream=None):
     """One recurrent decode step through libdp, updating `state` in place.
 
     q [B,H,dk], k [B,H,n_h,dk], v [B,H,n_h,dv] (float32 or bfloat16, one
-    dtype), beta [B,H,n_h] f32, g [B,H] f32 or None, kt (write keys, shape of
-    k) or None, state [B,H,dk,dv] f32 (H_{t-1} in, H_t out).  Returns out
-    [B,H,dv] in the input dtype or out_dtype (torch.float32).
+    dtype), beta [B,H,n_h] f32, g [B,H] f32 or None, ga [B,H,dk] f32 (the
+    per-key-channel gate) or None, kt (write keys, shape of k) or None, state
+    [B,H,dk,dv] f32 (H_{t-1} in, H_t out).  Returns out [B,H,dv] in the input
+    dtype or out_dtype (torch.float32).
     """
     if q.dim() != 3 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("expected q[B,H,dk], k[B,H,n_h,dk], v[B,H,n_h,dv]")
@@ -261,6 +263,7 @@ def decode(q, k, v, beta, state, g=None, *, kt=None, out=None, out_dtype=None, s
     _need(v, "v", dt, (B, H, n_h, dv), dev)
     _need(beta, "beta", torch.float32, (B, H, n_h), dev)
     _need(g, "g", torch.float32, (B, H), dev)
+    _need(ga, "ga", torch.float32, (B, H, dk), dev)
     _need(state, "state", torch.float32, (B, H, dk, dv), dev)
     if not q.is_contiguous():
         raise ValueError("q must be contiguous")
@@ -274,8 +277,8 @@ def decode(q, k, v, beta, state, g=None, *, kt=None, out=None, out_dtype=None, s
     _need(out, "out", odt, (B, H, dv), dev)
     flags = OUT_F32 if (odt == torch.float32 and dt != torch.float32) else 0
     fn = getattr(load(), f"dp_decode_{suf}")
-    rc = fn(_ptr(q), _ptr(k), _ptr(kt), _ptr(v), _ptr(beta), _ptr(g), n_h, B, H, dk, dv,
-            _ptr(out), _ptr(state), flags, _stream(stream))
+    rc = fn(_ptr(q), _ptr(k), _ptr(kt), _ptr(v), _ptr(beta), _ptr(g), _ptr(ga), n_h, B, H, dk,
+            dv, _ptr(out), _ptr(state), flags, _stream(stream))
     _check(rc, f"dp_decode_{suf}")
     return out
 

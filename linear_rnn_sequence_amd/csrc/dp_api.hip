@@ -403,8 +403,8 @@ hipError_t dispatch_decode(int elem, int dk, const dp::DecodeArgs& a, hipStream_
 }
 
 int decode_impl(int elem, const void* q, const void* k, const void* kt, const void* v,
-                const float* beta, const float* g, int n_h, int B, int H, int dk, int dv,
-                void* out, float* state, int flags, dp_stream stream) {
+                const float* beta, const float* g, const float* ga, int n_h, int B, int H, int dk,
+                int dv, void* out, float* state, int flags, dp_stream stream) {
   if (q == nullptr || k == nullptr || v == nullptr || beta == nullptr || out == nullptr ||
       state == nullptr)
     return DP_EINVAL;
@@ -420,6 +420,7 @@ int decode_impl(int elem, const void* q, const void* k, const void* kt, const vo
   a.v = v;
   a.beta = beta;
   a.g = g;
+  a.ga = ga;
   a.out = out;
   a.state = state;
   a.B = B;
@@ -609,15 +610,15 @@ int dp_fwd_varlen_bf16(const void* q, const void* k, const void* v, const float*
 }
 
 int dp_decode_f32(const float* q, const float* k, const float* kt, const float* v,
-                  const float* beta, const float* g, int n_h, int B, int H, int dk, int dv,
-                  float* out, float* state, int flags, dp_stream stream) {
-  return decode_impl(4, q, k, kt, v, beta, g, n_h, B, H, dk, dv, out, state, flags, stream);
+                  const float* beta, const float* g, const float* ga, int n_h, int B, int H,
+                  int dk, int dv, float* out, float* state, int flags, dp_stream stream) {
+  return decode_impl(4, q, k, kt, v, beta, g, ga, n_h, B, H, dk, dv, out, state, flags, stream);
 }
 
 int dp_decode_bf16(const void* q, const void* k, const void* kt, const void* v,
-                   const float* beta, const float* g, int n_h, int B, int H, int dk, int dv,
-                   void* out, float* state, int flags, dp_stream stream) {
-  return decode_impl(2, q, k, kt, v, beta, g, n_h, B, H, dk, dv, out, state, flags, stream);
+                   const float* beta, const float* g, const float* ga, int n_h, int B, int H,
+                   int dk, int dv, void* out, float* state, int flags, dp_stream stream) {
+  return decode_impl(2, q, k, kt, v, beta, g, ga, n_h, B, H, dk, dv, out, state, flags, stream);
 }
 
 }  // extern "C"

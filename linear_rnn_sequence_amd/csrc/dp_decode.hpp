@@ -5,9 +5,10 @@
 // (DeltaProduct study notes, arXiv 2502.10297v7: sec. 2.2 Eq.(3), the
 // per-token pseudocode of sec. 2.6 with its optional gate, applied once
 // before the first sub-step; the asymmetric write key of the OSDN study
-// notes, arXiv 2605.13473v1, sec. 2.2 Eqs.(2)/(5)):
+// notes, arXiv 2605.13473v1, sec. 2.2 Eqs.(2)/(5), and its KDA host's
+// per-key-channel decay, sec. 2.7):
 //
-//   H <- g H                                   (gated only)
+//   H <- g H, H <- Diag(alpha) H               (when the gates are given)
 //   for j < n_h:  e = v_j - H^T kn_j,   H <- H + clamp(b_j, 0, 2) kw_j e^T
 //   o = H^T q
 //
@@ -34,6 +35,7 @@ struct DecodeArgs {
   const void* v;    // [B, H, n_h, dv]   T
   const float* beta;  // [B, H, n_h]
   const float* g;     // [B, H] or nullptr
+  const float* ga;    // [B, H, dk] per-key-channel gate or nullptr
   void* out;          // [B, H, dv]      T, or fp32 when out_f32
   float* state;       // [B, H, dk, dv]  in/out
   int B, H, n_h, dv, out_f32;
@@ -106,6 +108,11 @@ __global__ __launch_bounds__(512) void dp_decode_kernel(DecodeArgs p) {
   if (p.g != nullptr) {
 #pragma unroll
     for (int i = 0; i < RP; ++i) hs[i] *= gt;
+  }
+  if (p.ga != nullptr) {  // Diag(alpha) H: state row r scales by alpha[r]
+    const float* al = p.ga + bh * DK + rg * RP;
+#pragma unroll
+    for (int i = 0; i < RP; ++i) hs[i] *= al[i];
   }
   block_sync_lds();
 

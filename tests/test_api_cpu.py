@@ -187,9 +187,9 @@ def test_decode_validation_errors_before_hip(lib, suffix):
     E = dp.binding
     f = getattr(lib, f"dp_decode_{suffix}")
 
-    def call(q=FAKE, k=FAKE, kt=None, v=FAKE, beta=FAKE, g=None, n_h=2, B=1, H=1, dk=16, dv=16,
-             out=FAKE, state=FAKE, flags=0):
-        return f(q, k, kt, v, beta, g, n_h, B, H, dk, dv, out, state, flags, None)
+    def call(q=FAKE, k=FAKE, kt=None, v=FAKE, beta=FAKE, g=None, ga=None, n_h=2, B=1, H=1, dk=16,
+             dv=16, out=FAKE, state=FAKE, flags=0):
+        return f(q, k, kt, v, beta, g, ga, n_h, B, H, dk, dv, out, state, flags, None)
 
     assert call(q=None) == E.DP_EINVAL
     assert call(k=None) == E.DP_EINVAL

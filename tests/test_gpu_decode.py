@@ -152,3 +152,28 @@ def test_decode_errors():
     with pytest.raises(dp.DPError) as ei:
         dp.decode(q, k, v, b, s)  # dk = 24 is not supported
     assert ei.value.code == -2
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_channel_gate_kda_host(dtype):
+    """The KDA host of OSDN (notes sec. 2.7): a per-key-channel gate alpha_t decays the
+    state's rows before the update, with the OSDN write keys.  Twenty consecutive
+    decode launches from a random state against the oracle's forward over those tokens."""
+    L = 20
+    w = WORKLOADS["c5"].scaled(B=2, H=3, L=L, dk=64, dv=64, dtype=dtype)
+    inp = make(w)
+    gen = torch.Generator().manual_seed(41)
+    ga = 0.6 + 0.4 * torch.rand(w.B, L, w.H, w.dk, generator=gen)
+    kt1, _ = oracle.precond(inp["k"][:, :, :, 0, :].contiguous(), inp["beta"][..., 0].contiguous())
+    kt = torch.from_numpy(kt1).to(inp["k"].dtype)[:, :, :, None, :].contiguous()
+    s0 = torch.randn(w.B, w.H, w.dk, w.dv, generator=gen) * 0.3
+    st = s0.clone().cuda()
+    outs = []
+    for t in range(L):
+        dev = lambda x: None if x is None else x[:, t].contiguous().cuda()
+        outs.append(dp.decode(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["beta"]), st,
+                              kt=dev(kt), ga=dev(ga), out_dtype=torch.float32))
+    torch.cuda.synchronize()
+    oo, fo = oracle.fwd(inp["q"], inp["k"], inp["v"], inp["beta"], kt=kt, h0=s0, ga=ga)
+    got = torch.stack([o.cpu() for o in outs], dim=1)
+    check(dict(out=(f64(got), oo), state=(f64(st), fo)), TOL[dtype], f"kda/{dtype}")
