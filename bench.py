@@ -10,7 +10,9 @@ scan first.  Prints ONE JSON line on stdout; diagnostics go to stderr.
 
 Per-kernel durations come from HIP events recorded on the launch stream
 around every launch inside the timed region.  The CPU baseline is the fp64
-oracle on a bounded sample of heads of the same workload, on this host.
+oracle on a bounded sample of heads of the same workload, on this host.  The
+same line also carries a packed variable-length batch (`varlen`) and the
+one-token decode step at batch 1 and 64 (`decode`), each with its own figures.
 """
 import argparse
 import json

@@ -16,9 +16,11 @@
 // readout queries Q, the masked and decayed scores P, and per-chunk scalars
 // (e^G, e^{G_last - G}, e^{G_loc} and the output offset of each readout row).
 // dp_chain_kernel then only runs the recurrence: NWC consumer wavefronts keep
-// their 16 value columns of the fp32 state in registers, and one copy
-// wavefront streams each chunk's operands (and the values) into a ring of
+// their 16 value columns of the fp32 state in registers, and two copy
+// wavefronts stream each chunk's operands (and the values) into a ring of
 // LDS stages with global_load_lds_dwordx4, two or three chunks ahead.
+// Packed variable-length batches run the same two kernels: every sequence is
+// chunked from its own first sub-step (SeqGeom), so no chunk spans two.
 //
 // Tile layout ("block-major"): a tile of R rows and W fp16 columns is stored
 // as W/8 blocks of R x 16 bytes (block q holds columns 8q..8q+7 of every row).

@@ -18,7 +18,9 @@
 // Up is computed as (T diag(beta)) (V - diag(e^G) Kn H0), which needs the
 // state only through one C x dk x BV product per chunk.
 //
-// Two launches:
+// Kernel pairs: the bf16 forward with symmetric keys runs dp_prep_kernel and
+// dp_chain_kernel (dp_fwd16.hpp); the fp32 forward and the bf16 write-key
+// forward run these two launches:
 //   dp_ut_kernel    one workgroup per chunk (all chunks in parallel): gathers
 //                   the chunk's sub-steps straight from the token-major
 //                   tensors (the interleave is pure addressing), normalises
@@ -30,7 +32,10 @@
 //                   in MFMA accumulators; per chunk it computes Up, the
 //                   readout rows and the state update on MFMA; at the end it
 //                   writes the final state.
-// A third kernel, dp_precond_kernel, is the OSDN phase-1 scan.
+//   (dp_scan16_kernel is the bf16 form of the scan, for the write-key path.)
+// dp_precond_kernel is the OSDN phase-1 scan, dp_decode_kernel (dp_decode.hpp)
+// the one-token decode step, dp_varlen_chunks_kernel the first chunk of every
+// packed sequence.
 //
 // Precision: on the bf16 path the inputs are bf16, every accumulation and the
 // carried state are fp32, and the MFMA operands that are computed (T diag(beta),
