@@ -582,6 +582,15 @@ __device__ __forceinline__ void static_for(F&& f) {
   if constexpr (N > 0) static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
+// Order of the MFMA steps inside one product of the pipelined chain body: step
+// j of a product with `ntile` output tiles and `nk` 32-deep contraction steps
+// works on tile step_tile(j) and contraction step step_k(j).  The contraction
+// step is outermost, so consecutive MFMAs accumulate into different tiles and
+// none waits for the result of the one before it; a tile is complete at its
+// last contraction step.
+__host__ __device__ constexpr int step_tile(int j, int ntile) { return j % ntile; }
+__host__ __device__ constexpr int step_k(int j, int ntile) { return j / ntile; }
+
 // Step schedule of the pipelined chain body (see dp_chain_kernel): phase
 // starts S2, S3, S4 and end NS; a tile conversion for step k runs in
 // iteration min(k + LA + DL, next phase start + LA).
@@ -795,7 +804,7 @@ void dp_chain_kernel(FwdArgs p) {
     // step list padded to a multiple of LA: the next chunk's step k then lands
     // in ring slot k % LA, the slot its MFMA reads
     constexpr int NSP = EARLY ? (NS + LA - 1) / LA * LA : NS;
-    static_assert(!EARLY || (S1 >= LA && LA % KST == 0), "early fragments must be key fragments");
+    static_assert(!EARLY || S1 >= LA, "early fragments must be key fragments");
     f32x4_t vf[NCT], eg[NCT], el[NCT], egl[NRT];
     float dec = 1.f;
     f16x8_t ring[LA];
@@ -828,16 +837,16 @@ void dp_chain_kernel(FwdArgs p) {
     // key fragment k (< LA) of the chunk whose key tiles start at ok / ok1
     auto key_frag = [&](const uint32_t* ok, const uint32_t* ok1, auto kc) {
       constexpr int k = decltype(kc)::value;
-      constexpr int ko = 4 * (k % KST) * C * 16;
-      pre[k] = cat8(*reinterpret_cast<const f16x4_t*>(smem + ok[k / KST] + ko),
-                    *reinterpret_cast<const f16x4_t*>(smem + ok1[k / KST] + ko));
+      constexpr int ct = step_tile(k, NCT), ko = 4 * step_k(k, NCT) * C * 16;
+      pre[k] = cat8(*reinterpret_cast<const f16x4_t*>(smem + ok[ct] + ko),
+                    *reinterpret_cast<const f16x4_t*>(smem + ok1[ct] + ko));
     };
     if (nc > 0) block_sync_lds();  // X(0)
     if constexpr (EARLY) {
       if (nc > 0) {  // chunk 0's small operands and first LA fragments (stage 0)
-        uint32_t ok[LA / KST], ok1[LA / KST];
+        uint32_t ok[NCT], ok1[NCT];
 #pragma unroll
-        for (int ct = 0; ct < LA / KST; ++ct) {
+        for (int ct = 0; ct < NCT; ++ct) {
           ok[ct] = W.oK + lrK + ct * 256;
           ok1[ct] = ok[ct] + C * 16;
           asm volatile("" : "+v"(ok[ct]), "+v"(ok1[ct]));
@@ -896,27 +905,28 @@ void dp_chain_kernel(FwdArgs p) {
       f16x4_t xq[NCT], uq[NCT], usq[NCT];
       auto load_frag = [&](auto ic) {
         constexpr int i = decltype(ic)::value;
-        if constexpr (i >= S2 && i < S3 && TRIM && (i - S2) / CST < 2 * ((i - S2) % CST)) {
+        if constexpr (i >= S2 && i < S3 && TRIM && step_tile(i - S2, NCT) < 2 * step_k(i - S2, NCT)) {
           return;  // zero tile of T diag(beta): no read, no product
         }
         f16x8_t fr;
         if constexpr (i < S1) {
-          constexpr int ko = 4 * (i % KST) * C * 16;
-          fr = cat8(*reinterpret_cast<const f16x4_t*>(smem + oK[i / KST] + ko),
-                    *reinterpret_cast<const f16x4_t*>(smem + oK1[i / KST] + ko));
+          constexpr int ct = step_tile(i, NCT), ko = 4 * step_k(i, NCT) * C * 16;
+          fr = cat8(*reinterpret_cast<const f16x4_t*>(smem + oK[ct] + ko),
+                    *reinterpret_cast<const f16x4_t*>(smem + oK1[ct] + ko));
         } else if constexpr (i < S2) {
           constexpr int j = i - S1;
-          fr = *reinterpret_cast<const f16x8_t*>(smem + oQ[j / KST] + 4 * (j % KST) * RT * 16);
+          fr = *reinterpret_cast<const f16x8_t*>(smem + oQ[step_tile(j, NRT)] + 4 * step_k(j, NRT) * RT * 16);
         } else if constexpr (i < S3) {
           constexpr int j = i - S2;
-          constexpr int ct = j / CST, t = j % CST;
+          constexpr int ct = step_tile(j, NCT), t = step_k(j, NCT);
           fr = *reinterpret_cast<const f16x8_t*>(smem + oT[t] + (16 * ct - TS * t) * 16);
         } else if constexpr (i < S4) {
           constexpr int j = i - S3;
-          fr = *reinterpret_cast<const f16x8_t*>(smem + oP[j / CST] + 4 * (j % CST) * RT * 16);
+          fr = *reinterpret_cast<const f16x8_t*>(smem + oP[step_tile(j, NRT)] + 4 * step_k(j, NRT) * RT * 16);
         } else {
           constexpr int j = i - S4;
-          const unsigned char* q = st + W.oK + ltK + tr_block<DK>(j / CST) * C * 16 + 32 * (j % CST) * 16;
+          const unsigned char* q =
+              st + W.oK + ltK + tr_block<DK>(step_tile(j, NDT)) * C * 16 + 32 * step_k(j, NDT) * 16;
           fr = cat8(__builtin_bit_cast(f16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)q)),
                     __builtin_bit_cast(f16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(q + 256))));
         }
@@ -930,20 +940,20 @@ void dp_chain_kernel(FwdArgs p) {
         else
           a = ring[i % LA];
         if constexpr (i < S1) {
-          constexpr int ct = i / KST, t = i % KST;
+          constexpr int ct = step_tile(i, NCT), t = step_k(i, NCT);
           accX[ct] = mfma32h(a, cat8(hqn[2 * t], hqn[2 * t + 1]), t == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : accX[ct]);
         } else if constexpr (i < S2) {
-          constexpr int j = i - S1, it = j / KST, t = j % KST;
+          constexpr int j = i - S1, it = step_tile(j, NRT), t = step_k(j, NRT);
           z[it] = mfma32h(a, cat8(hqn[2 * t], hqn[2 * t + 1]), t == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : z[it]);
         } else if constexpr (i < S3) {
-          constexpr int j = i - S2, ct = j / CST, t = j % CST;
+          constexpr int j = i - S2, ct = step_tile(j, NCT), t = step_k(j, NCT);
           if constexpr (!(TRIM && ct < 2 * t))
             accU[ct] = mfma32h(a, cat8(xq[2 * t], xq[2 * t + 1]), t == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : accU[ct]);
         } else if constexpr (i < S4) {
-          constexpr int j = i - S3, it = j / CST, t = j % CST;
+          constexpr int j = i - S3, it = step_tile(j, NRT), t = step_k(j, NRT);
           z[it] = mfma32h(a, cat8(uq[2 * t], uq[2 * t + 1]), z[it]);
         } else {
-          constexpr int j = i - S4, dt = j / CST, t = j % CST;
+          constexpr int j = i - S4, dt = step_tile(j, NDT), t = step_k(j, NDT);
           if constexpr (GATED && t == 0) hacc[dt] = hacc[dt] * dec;
           hacc[dt] = mfma32h(a, cat8(usq[2 * t], usq[2 * t + 1]), hacc[dt]);
         }
@@ -951,8 +961,8 @@ void dp_chain_kernel(FwdArgs p) {
       auto conv = [&](auto kc) {
         constexpr int k = decltype(kc)::value;
         if constexpr (k < S1) {
-          if constexpr (k % KST == KST - 1) {
-            constexpr int ct = k / KST;
+          if constexpr (step_k(k, NCT) == KST - 1) {
+            constexpr int ct = step_tile(k, NCT);
             if constexpr (GATED)
               xq[ct] = to_h4(vf[ct] - eg[ct] * accX[ct]);  // accX = Kn H
             else
@@ -960,10 +970,13 @@ void dp_chain_kernel(FwdArgs p) {
             asm volatile("" : "+v"(xq[ct]));
           }
         } else if constexpr (k < S2) {
-          if constexpr ((k - S1) % KST == KST - 1) z[(k - S1) / KST] = z[(k - S1) / KST] * egl[(k - S1) / KST];
+          if constexpr (step_k(k - S1, NRT) == KST - 1) {
+            constexpr int it = step_tile(k - S1, NRT);
+            z[it] = z[it] * egl[it];
+          }
         } else if constexpr (k < S3) {
-          if constexpr ((k - S2) % CST == CST - 1) {
-            constexpr int ct = (k - S2) / CST;
+          if constexpr (step_k(k - S2, NCT) == CST - 1) {
+            constexpr int ct = step_tile(k - S2, NCT);
             uq[ct] = to_h4(accU[ct]);
             asm volatile("" : "+v"(uq[ct]));
             if constexpr (GATED) {
@@ -976,9 +989,10 @@ void dp_chain_kernel(FwdArgs p) {
         } else if constexpr (k < S4) {
           // the readout tiles are stored after the chunk's last product (below)
         } else {
-          if constexpr ((k - S4) % CST == CST - 1) {
-            hqn[(k - S4) / CST] = to_h4(hacc[(k - S4) / CST]);
-            asm volatile("" : "+v"(hqn[(k - S4) / CST]));
+          if constexpr (step_k(k - S4, NDT) == CST - 1) {
+            constexpr int dt = step_tile(k - S4, NDT);
+            hqn[dt] = to_h4(hacc[dt]);
+            asm volatile("" : "+v"(hqn[dt]));
           }
         }
       };
