@@ -13,6 +13,8 @@ contiguous float64 and calls it through ctypes.  Sources, by page title:
   generalized-Householder sub-steps), sec. 2.6 (per-token gate applied before
   the sub-steps; readout H^T q), sec. 4.1 / Sec.5.1 (only each token's last
   sub-step is read out).
+* the gradient of that forward w.r.t. all of its inputs, by reverse-mode
+  differentiation of the same sequential definition (``bwd``).
 * "OSDN: Improving Delta Rule with Provable Online Preconditioning in Linear
   Attention" -- sec. 2.2 Eqs.(2)/(5) (asymmetric write key), sec. 2.4 Alg.1
   (phase-1 preconditioner, emit-then-update).
@@ -54,6 +56,15 @@ def _load():
                                           ctypes.c_int, ctypes.c_int, ctypes.c_double,
                                           ctypes.c_double, ctypes.c_double, ctypes.c_double,
                                           _D, _D, ctypes.c_int]
+        lib.oracle_bwd.restype = ctypes.c_int
+        lib.oracle_bwd.argtypes = [_D, _D, _D, _D, _D, _D, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   _D, _D, _D, _D, _D, _D, _D, _D, _D, _D, ctypes.c_int]
+        lib.oracle_bwd_heads.restype = ctypes.c_int
+        lib.oracle_bwd_heads.argtypes = [_D, _D, _D, _D, _D, _D, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         _D, _D, _D, _LP, ctypes.c_int, _D, _D, _D, _D, _D, _D,
+                                         _D, ctypes.c_int]
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         _LIB = lib
@@ -164,3 +175,64 @@ def precond(k, beta, eta=3e-3, dmin=0.5, dmax=2.0, eps=1e-6, d0=None, nthreads=0
     if rc != 0:
         raise RuntimeError(f"oracle_precond_ex failed ({rc})")
     return kt, d
+
+
+def _bwd_args(q, k, v, beta, dout, g, kt, h0, dfinal):
+    q, k, v, beta, dout, g, kt, h0, dfinal = (_f64(a) for a in (q, k, v, beta, dout, g, kt, h0,
+                                                                  dfinal))
+    B, L, H, n_h, dk, dv = _shapes(q, k, v, beta, g, kt, h0)
+    if dout.shape != (B, L, H, dv):
+        raise ValueError("dout must be [B,L,H,dv]")
+    if dfinal is not None and dfinal.shape != (B, H, dk, dv):
+        raise ValueError("dfinal must be [B,H,dk,dv]")
+    return (q, k, v, beta, dout, g, kt, h0, dfinal), (B, L, H, n_h, dk, dv)
+
+
+def bwd(q, k, v, beta, dout, g=None, kt=None, h0=None, dfinal=None, nthreads=0):
+    """Gradient of the sequential fp64 forward, for a loss with gradient
+    ``dout [B,L,H,dv]`` on the outputs and ``dfinal [B,H,dk,dv]`` (None: zero)
+    on the final state.
+
+    Returns a dict of float64 arrays in the inputs' layouts: ``q, k, v, beta,
+    h0`` always, ``g`` when a gate is given, ``kt`` when write keys are given.
+    """
+    (q, k, v, beta, dout, g, kt, h0, dfinal), (B, L, H, n_h, dk, dv) = _bwd_args(
+        q, k, v, beta, dout, g, kt, h0, dfinal)
+    r = dict(q=np.zeros((B, L, H, dk)), k=np.zeros((B, L, H, n_h, dk)),
+             v=np.zeros((B, L, H, n_h, dv)), beta=np.zeros((B, L, H, n_h)),
+             h0=np.zeros((B, H, dk, dv)))
+    if g is not None:
+        r["g"] = np.zeros((B, L, H))
+    if kt is not None:
+        r["kt"] = np.zeros((B, L, H, n_h, dk))
+    rc = _load().oracle_bwd(_ptr(q), _ptr(k), _ptr(kt), _ptr(v), _ptr(beta), _ptr(g), n_h, B, H,
+                            L, dk, dv, _ptr(h0), _ptr(dout), _ptr(dfinal), _ptr(r["q"]),
+                            _ptr(r["k"]), _ptr(r.get("kt")), _ptr(r["v"]), _ptr(r["beta"]),
+                            _ptr(r.get("g")), _ptr(r["h0"]), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_bwd failed ({rc})")
+    return r
+
+
+def bwd_heads(q, k, v, beta, dout, heads, g=None, kt=None, h0=None, dfinal=None, nthreads=0):
+    """:func:`bwd` for the listed flattened heads ``b*H + h`` only; gradients
+    compact per head: ``q [n,L,dk]``, ``k``/``kt [n,L,n_h,dk]``, ``v
+    [n,L,n_h,dv]``, ``beta [n,L,n_h]``, ``g [n,L]``, ``h0 [n,dk,dv]``."""
+    (q, k, v, beta, dout, g, kt, h0, dfinal), (B, L, H, n_h, dk, dv) = _bwd_args(
+        q, k, v, beta, dout, g, kt, h0, dfinal)
+    hs = np.ascontiguousarray(np.asarray(heads, dtype=np.int64))
+    n = hs.size
+    r = dict(q=np.zeros((n, L, dk)), k=np.zeros((n, L, n_h, dk)), v=np.zeros((n, L, n_h, dv)),
+             beta=np.zeros((n, L, n_h)), h0=np.zeros((n, dk, dv)))
+    if g is not None:
+        r["g"] = np.zeros((n, L))
+    if kt is not None:
+        r["kt"] = np.zeros((n, L, n_h, dk))
+    rc = _load().oracle_bwd_heads(_ptr(q), _ptr(k), _ptr(kt), _ptr(v), _ptr(beta), _ptr(g), n_h,
+                                  B, H, L, dk, dv, _ptr(h0), _ptr(dout), _ptr(dfinal),
+                                  hs.ctypes.data_as(_LP), n, _ptr(r["q"]), _ptr(r["k"]),
+                                  _ptr(r.get("kt")), _ptr(r["v"]), _ptr(r["beta"]),
+                                  _ptr(r.get("g")), _ptr(r["h0"]), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_bwd_heads failed ({rc})")
+    return r

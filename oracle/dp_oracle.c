@@ -1,6 +1,6 @@
 /*
  * dp_oracle.c -- slow, plain fp64 CPU oracle for the DeltaProduct forward
- * recurrence and the OSDN phase-1 preconditioner scan.
+ * recurrence, its gradient, and the OSDN phase-1 preconditioner scan.
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
  * call this file; only the tests, the smoke check and the benchmark's CPU
@@ -304,4 +304,250 @@ int oracle_precond(const double* k, const double* beta, int B, int H, int L, int
 {
     return oracle_precond_ex(k, beta, NULL, 1, B, H, L, dk, eta, dmin, dmax, eps, d_state,
                              kt_out, nthreads);
+}
+
+/*
+ * ------------------------------------------------------------------------
+ * Gradient of the forward (reverse mode, one sub-step at a time).
+ *
+ * For a scalar loss with dout = dLoss/dout [B, L, H, dv] and dfinal =
+ * dLoss/dfinal_state [B, H, dk, dv] (NULL: zero), this returns the gradients
+ * w.r.t. every input of the forward above, by differentiating its
+ * sequential definition step by step, last token first:
+ *   readout o = H^T q:          dq = H dout,  dH += q dout^T
+ *   sub-step H' = H + bt w e^T with e = v - H^T kh:
+ *                               de = bt dH'^T w      (this is dv)
+ *                               dbt = w^T dH' e,  dw = bt dH' e
+ *                               dkh = -H de (+ dw when w = kh)
+ *                               dH = dH' - kh de^T
+ *   unit key kh = k / max(|k|, 1e-6):
+ *                               dk = (dkh - kh <kh, dkh>) / |k|   (|k| > 1e-6)
+ *                               dk = dkh / 1e-6                   (otherwise)
+ *   beta clamp to [0, 2]:       dbeta = dbt where 0 <= beta <= 2, else 0
+ *   gate H_0 = g H_prev:        dg = <dH_0, H_prev>,  dH_prev = g dH_0
+ * and dh0 = dH after the first token.  The derivative of the clamp at its
+ * end points is taken as 1 (the gradient passes at beta = 0 and beta = 2).
+ * The per-channel gate of the forward is not differentiated here.
+ *
+ * heads == NULL: every head, gradients in the layouts of the inputs:
+ *   dq [B,L,H,dk], dk [B,L,H,n_h,dk], dkt [B,L,H,n_h,dk] (when kt),
+ *   dv [B,L,H,n_h,dv], dbeta [B,L,H,n_h], dg [B,L,H] (when g),
+ *   dh0 [B,H,dk,dv].
+ * heads != NULL: the listed heads only, compact: dq [n,L,dk], dk and dkt
+ *   [n,L,n_h,dk], dv [n,L,n_h,dv], dbeta [n,L,n_h], dg [n,L], dh0 [n,dk,dv].
+ * dkt, dg and dh0 may be NULL (not returned).  Returns 0, -1 on bad
+ * arguments, -2 when scratch memory could not be allocated.
+ */
+static int bwd_impl(const double* q, const double* k, const double* kt, const double* v,
+                    const double* beta, const double* g, int n_h, int B, int H, int L, int dk,
+                    int dv, const double* h0, const double* dout, const double* dfinal,
+                    const long* heads, int nsel, double* dq, double* dkr, double* dkt,
+                    double* dvv, double* dbeta, double* dg, double* dh0, int nthreads)
+{
+    if (!q || !k || !v || !beta || !dout || !dq || !dkr || !dvv || !dbeta) return -1;
+    if (n_h < 1 || B < 0 || H < 0 || L < 0 || dk < 1 || dv < 1) return -1;
+    const long nbh = (long)B * H;
+    const long nrun = heads ? nsel : nbh;
+    if (heads) {
+        if (nsel < 0) return -1;
+        for (long i = 0; i < nsel; ++i)
+            if (heads[i] < 0 || heads[i] >= nbh) return -1;
+    }
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#else
+    (void)nthreads;
+#endif
+    const size_t DS = (size_t)dk * dv;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads) reduction(| : bad)
+    for (long i = 0; i < nrun; ++i) {
+        const long bh = heads ? heads[i] : i;
+        const long b = bh / H, h = bh % H;
+        /* Hpre[t]: the state before token t's gate; Hs[j]: before sub-step j of one token */
+        double* Hpre = (double*)malloc(sizeof(double) * DS * (size_t)(L > 0 ? L : 1));
+        double* Hs = (double*)malloc(sizeof(double) * DS * (size_t)(n_h + 1));
+        double* dH = (double*)malloc(sizeof(double) * DS);
+        double* kh = (double*)malloc(sizeof(double) * (size_t)dk * n_h);
+        double* e = (double*)malloc(sizeof(double) * (size_t)dv * n_h);
+        double* de = (double*)malloc(sizeof(double) * (size_t)dv);
+        double* dkh = (double*)malloc(sizeof(double) * (size_t)dk);
+        if (!Hpre || !Hs || !dH || !kh || !e || !de || !dkh) {
+            free(Hpre); free(Hs); free(dH); free(kh); free(e); free(de); free(dkh);
+            bad |= 1;
+            continue;
+        }
+        /* output addressing: element (t, [j,] x) of this head */
+        size_t oq, sq, ok, sk, ov, sv, ob, sb, og, sg;
+        if (heads) {
+            oq = (size_t)i * L * dk;          sq = (size_t)dk;
+            ok = (size_t)i * L * n_h * dk;    sk = (size_t)n_h * dk;
+            ov = (size_t)i * L * n_h * dv;    sv = (size_t)n_h * dv;
+            ob = (size_t)i * L * n_h;         sb = (size_t)n_h;
+            og = (size_t)i * L;               sg = 1;
+        } else {
+            const size_t tok0 = (size_t)b * L * H + h;
+            oq = tok0 * dk;                   sq = (size_t)H * dk;
+            ok = tok0 * n_h * dk;             sk = (size_t)H * n_h * dk;
+            ov = tok0 * n_h * dv;             sv = (size_t)H * n_h * dv;
+            ob = tok0 * n_h;                  sb = (size_t)H * n_h;
+            og = tok0;                        sg = (size_t)H;
+        }
+        const size_t odh = (size_t)(heads ? i : bh) * DS;
+
+        /* forward, keeping the state before each token's gate */
+        double* S = Hs; /* running state */
+        if (h0)
+            memcpy(S, h0 + (size_t)bh * DS, sizeof(double) * DS);
+        else
+            memset(S, 0, sizeof(double) * DS);
+        for (long t = 0; t < L; ++t) {
+            const size_t tok = ((size_t)b * L + t) * H + h;
+            memcpy(Hpre + (size_t)t * DS, S, sizeof(double) * DS);
+            if (g)
+                for (size_t x = 0; x < DS; ++x) S[x] *= g[tok];
+            for (int j = 0; j < n_h; ++j) {
+                const size_t sub = tok * n_h + j;
+                unit_key(k + sub * dk, dk, kh);
+                const double bt = clampd(beta[sub], 0.0, 2.0);
+                const double* w = kt ? kt + sub * dk : kh;
+                for (int c = 0; c < dv; ++c) {
+                    double acc = 0.0;
+                    for (int r = 0; r < dk; ++r) acc += S[(size_t)r * dv + c] * kh[r];
+                    e[c] = v[sub * dv + c] - acc;
+                }
+                for (int r = 0; r < dk; ++r)
+                    for (int c = 0; c < dv; ++c) S[(size_t)r * dv + c] += bt * w[r] * e[c];
+            }
+        }
+
+        /* reverse sweep */
+        if (dfinal)
+            memcpy(dH, dfinal + (size_t)bh * DS, sizeof(double) * DS);
+        else
+            memset(dH, 0, sizeof(double) * DS);
+        for (long t = L - 1; t >= 0; --t) {
+            const size_t tok = ((size_t)b * L + t) * H + h;
+            /* recompute this token: Hs[j] is the state before sub-step j, Hs[n_h] after the last */
+            memcpy(Hs, Hpre + (size_t)t * DS, sizeof(double) * DS);
+            if (g)
+                for (size_t x = 0; x < DS; ++x) Hs[x] *= g[tok];
+            for (int j = 0; j < n_h; ++j) {
+                const size_t sub = tok * n_h + j;
+                const double* Sj = Hs + (size_t)j * DS;
+                double* Sn = Hs + (size_t)(j + 1) * DS;
+                double* khj = kh + (size_t)j * dk;
+                double* ej = e + (size_t)j * dv;
+                unit_key(k + sub * dk, dk, khj);
+                const double bt = clampd(beta[sub], 0.0, 2.0);
+                const double* w = kt ? kt + sub * dk : khj;
+                for (int c = 0; c < dv; ++c) {
+                    double acc = 0.0;
+                    for (int r = 0; r < dk; ++r) acc += Sj[(size_t)r * dv + c] * khj[r];
+                    ej[c] = v[sub * dv + c] - acc;
+                }
+                for (int r = 0; r < dk; ++r)
+                    for (int c = 0; c < dv; ++c)
+                        Sn[(size_t)r * dv + c] = Sj[(size_t)r * dv + c] + bt * w[r] * ej[c];
+            }
+            /* readout o = H^T q after the last sub-step */
+            const double* qq = q + tok * dk;
+            const double* Hl = Hs + (size_t)n_h * DS;
+            const double* dO = dout + tok * dv;
+            double* dqt = dq + oq + (size_t)t * sq;
+            for (int r = 0; r < dk; ++r) {
+                double acc = 0.0;
+                for (int c = 0; c < dv; ++c) acc += Hl[(size_t)r * dv + c] * dO[c];
+                dqt[r] = acc;
+            }
+            for (int r = 0; r < dk; ++r)
+                for (int c = 0; c < dv; ++c) dH[(size_t)r * dv + c] += qq[r] * dO[c];
+            /* sub-steps, last first */
+            for (int j = n_h - 1; j >= 0; --j) {
+                const size_t sub = tok * n_h + j;
+                const double* Sj = Hs + (size_t)j * DS;
+                const double* khj = kh + (size_t)j * dk;
+                const double* ej = e + (size_t)j * dv;
+                const double braw = beta[sub];
+                const double bt = clampd(braw, 0.0, 2.0);
+                const double* w = kt ? kt + sub * dk : khj;
+                /* de = bt dH^T w */
+                for (int c = 0; c < dv; ++c) {
+                    double acc = 0.0;
+                    for (int r = 0; r < dk; ++r) acc += w[r] * dH[(size_t)r * dv + c];
+                    de[c] = bt * acc;
+                }
+                /* dbt = w^T dH e;  dw = bt dH e */
+                double dbt = 0.0;
+                double* dktj = dkt ? dkt + ok + (size_t)t * sk + (size_t)j * dk : NULL;
+                for (int r = 0; r < dk; ++r) {
+                    double acc = 0.0;
+                    for (int c = 0; c < dv; ++c) acc += dH[(size_t)r * dv + c] * ej[c];
+                    dbt += w[r] * acc;
+                    /* dkh = -H de, plus dw when the write key is the read key */
+                    double dr = 0.0;
+                    for (int c = 0; c < dv; ++c) dr -= Sj[(size_t)r * dv + c] * de[c];
+                    if (kt) {
+                        if (dktj) dktj[r] = bt * acc;
+                    } else {
+                        dr += bt * acc;
+                    }
+                    dkh[r] = dr;
+                }
+                /* dv = de */
+                double* dvj = dvv + ov + (size_t)t * sv + (size_t)j * dv;
+                for (int c = 0; c < dv; ++c) dvj[c] = de[c];
+                /* dbeta through the clamp */
+                dbeta[ob + (size_t)t * sb + j] = (braw >= 0.0 && braw <= 2.0) ? dbt : 0.0;
+                /* dk through the normalisation */
+                const double* kr = k + sub * dk;
+                double n2 = 0.0;
+                for (int r = 0; r < dk; ++r) n2 += kr[r] * kr[r];
+                const double nrm = sqrt(n2);
+                double* dkj = dkr + ok + (size_t)t * sk + (size_t)j * dk;
+                if (nrm > ORACLE_KEY_EPS) {
+                    double p = 0.0;
+                    for (int r = 0; r < dk; ++r) p += khj[r] * dkh[r];
+                    for (int r = 0; r < dk; ++r) dkj[r] = (dkh[r] - khj[r] * p) / nrm;
+                } else {
+                    for (int r = 0; r < dk; ++r) dkj[r] = dkh[r] / ORACLE_KEY_EPS;
+                }
+                /* dH before the sub-step: dH - kh de^T */
+                for (int r = 0; r < dk; ++r)
+                    for (int c = 0; c < dv; ++c) dH[(size_t)r * dv + c] -= khj[r] * de[c];
+            }
+            /* gate: H_0 = g H_prev */
+            if (g) {
+                const double* Hp = Hpre + (size_t)t * DS;
+                double acc = 0.0;
+                for (size_t x = 0; x < DS; ++x) acc += dH[x] * Hp[x];
+                if (dg) dg[og + (size_t)t * sg] = acc;
+                for (size_t x = 0; x < DS; ++x) dH[x] *= g[tok];
+            }
+        }
+        if (dh0) memcpy(dh0 + odh, dH, sizeof(double) * DS);
+        free(Hpre); free(Hs); free(dH); free(kh); free(e); free(de); free(dkh);
+    }
+    return bad ? -2 : 0;
+}
+
+int oracle_bwd(const double* q, const double* k, const double* kt, const double* v,
+               const double* beta, const double* g, int n_h, int B, int H, int L, int dk, int dv,
+               const double* h0, const double* dout, const double* dfinal, double* dq,
+               double* dk_out, double* dkt, double* dv_out, double* dbeta, double* dg,
+               double* dh0, int nthreads)
+{
+    return bwd_impl(q, k, kt, v, beta, g, n_h, B, H, L, dk, dv, h0, dout, dfinal, NULL, 0, dq,
+                    dk_out, dkt, dv_out, dbeta, dg, dh0, nthreads);
+}
+
+int oracle_bwd_heads(const double* q, const double* k, const double* kt, const double* v,
+                     const double* beta, const double* g, int n_h, int B, int H, int L, int dk,
+                     int dv, const double* h0, const double* dout, const double* dfinal,
+                     const long* heads, int nsel, double* dq, double* dk_out, double* dkt,
+                     double* dv_out, double* dbeta, double* dg, double* dh0, int nthreads)
+{
+    if (!heads) return -1;
+    return bwd_impl(q, k, kt, v, beta, g, n_h, B, H, L, dk, dv, h0, dout, dfinal, heads, nsel,
+                    dq, dk_out, dkt, dv_out, dbeta, dg, dh0, nthreads);
 }

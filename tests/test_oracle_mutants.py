@@ -56,6 +56,22 @@ MUTANTS = {
                              "for (int c = 0; c < dv; ++c) S[(size_t)r * dv + c] *= 1.0;"),
 }
 
+# mistakes in the gradient, caught by tests/test_oracle_bwd_pins.py
+BWD_MUTANTS = {
+    "bwd_drop_state_term_in_dk": ("dr -= Sj[(size_t)r * dv + c] * de[c];", "dr -= 0.0 * de[c];"),
+    "bwd_state_grad_sign": ("dH[(size_t)r * dv + c] -= khj[r] * de[c];",
+                            "dH[(size_t)r * dv + c] += khj[r] * de[c];"),
+    "bwd_gate_grad_on_gated_state": ("for (size_t x = 0; x < DS; ++x) acc += dH[x] * Hp[x];",
+                                     "for (size_t x = 0; x < DS; ++x) acc += dH[x] * Hs[x];"),
+    "bwd_dq_from_earlier_state": ("const double* Hl = Hs + (size_t)n_h * DS;",
+                                  "const double* Hl = Hs + (size_t)(n_h - 1) * DS;"),
+    "bwd_norm_projection_dropped": ("dkj[r] = (dkh[r] - khj[r] * p) / nrm;", "dkj[r] = dkh[r] / nrm;"),
+    "bwd_dbeta_ignores_clamp": ("(braw >= 0.0 && braw <= 2.0) ? dbt : 0.0", "dbt"),
+    "bwd_write_grad_missing_beta": ("dr += bt * acc;", "dr += acc;"),
+    "bwd_gate_not_applied_to_state_grad": ("for (size_t x = 0; x < DS; ++x) dH[x] *= g[tok];",
+                                           "for (size_t x = 0; x < DS; ++x) dH[x] *= 1.0;"),
+}
+
 _EMIT_LATE = (
     "            for (int r = 0; r < dk; ++r) d[r] = clampd(rt * d[r] + coef * (kh[r] * kh[r]), dmin, dmax);\n",
     "            for (int r = 0; r < dk; ++r) d[r] = clampd(rt * d[r] + coef * (kh[r] * kh[r]), dmin, dmax);\n"
@@ -67,6 +83,10 @@ _READOUT_FIX = (
 
 
 def _mutate(src, name):
+    if name in BWD_MUTANTS:
+        a, b = BWD_MUTANTS[name]
+        assert src.count(a) == 1, name
+        return src.replace(a, b)
     a, b = MUTANTS[name]
     assert src.count(a) >= 1, name
     s = src.replace(a, b)
@@ -88,8 +108,9 @@ def _mutate(src, name):
     return s
 
 
-@pytest.mark.parametrize("name", sorted(MUTANTS))
+@pytest.mark.parametrize("name", sorted(MUTANTS) + sorted(BWD_MUTANTS))
 def test_pins_catch_planted_mistake(name, tmp_path):
+    pins = "test_oracle_bwd_pins.py" if name in BWD_MUTANTS else "test_oracle_pins.py"
     src = open(os.path.join(ROOT, "oracle", "dp_oracle.c")).read()
     mut = _mutate(src, name)
     assert mut != src
@@ -103,7 +124,7 @@ def test_pins_catch_planted_mistake(name, tmp_path):
                     str(tmp_path / "oracle" / "dp_oracle.c"), "-o",
                     str(tmp_path / "oracle" / "liboracle.so"), "-lm"], check=True)
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
-                        "--rootdir", str(tmp_path), str(tmp_path / "tests" / "test_oracle_pins.py")],
+                        "--rootdir", str(tmp_path), str(tmp_path / "tests" / pins)],
                        capture_output=True, text=True, cwd=str(tmp_path), timeout=600)
     assert "passed" in r.stdout or "failed" in r.stdout, r.stdout + r.stderr
     assert r.returncode != 0, f"mutant {name} survived every pin:\n{r.stdout[-2000:]}"
