@@ -277,6 +277,47 @@ int dp_decode_bf16(const void* q, const void* k, const void* kt, const void* v,
                    const float* beta, const float* g, const float* ga, int n_h, int B, int H,
                    int dk, int dv, void* out, float* state, int flags, dp_stream stream);
 
+/*
+ * Gradient of the symmetric forward (dp_fwd_f32 / dp_fwd_bf16 without write
+ * keys) w.r.t. all of its inputs: the reverse-mode derivative of the
+ * recurrence of DeltaProduct notes sec. 2.2 Eq.(3) with the gate and readout
+ * of sec. 2.6 over the expanded sequence of sec. 4.1, computed in the
+ * chunkwise form of the OSDN notes sec. 2.5 / App.A.2.  For a loss with
+ * gradient dout on out and dfinal on final_state it returns
+ *   dq    [B, L, H, dk]        f32   written
+ *   dk_out [B, L, H, n_h, dk]  f32   written: w.r.t. the RAW keys (through
+ *                                    k / max(|k|_2, 1e-6))
+ *   dv_out [B, L, H, n_h, dv]  f32   written
+ *   dbeta [B, L, H, n_h]       f32   written: w.r.t. the raw beta; zero where
+ *                                    beta lies outside [0, 2] (the clamp)
+ *   dg    [B, L, H]            f32   written when g is given, else untouched;
+ *                                    may be NULL.  Zero where g < FLT_MIN (the
+ *                                    forward uses log(max(g, FLT_MIN)))
+ *   dh0   [B, H, dk, dv]       f32   written, or NULL (not returned); the
+ *                                    gradient w.r.t. h0 (zero h0 when NULL)
+ * The inputs are the forward's (q, k, v, beta, g, h0 with the same layouts
+ * and types; T = float or bf16 by suffix), plus
+ *   dout   [B, L, H, dv]   T     gradient on out
+ *   dfinal [B, H, dk, dv]  f32   gradient on final_state, or NULL (zero)
+ * The backward recomputes the forward's chunk states itself: nothing from a
+ * forward call is needed.  workspace: dp_bwd_workspace_size() bytes,
+ * 256-byte aligned, caller-owned (T and the key scalars per 32-sub-step
+ * chunk, the chunk-start states and their gradients, all fp32: about
+ * 2 dk dv 4 B per 32 sub-steps per head).  All arithmetic is fp32.
+ * Errors: DP_EINVAL (null required pointer, sizes <= 0), DP_ENOTSUP (dk or
+ * dv outside {16, 32, 64, 128}, n_h > 64, sizes past the 32-bit index
+ * limits), DP_EWORKSPACE, DP_EHIP.
+ */
+int dp_bwd_workspace_size(int n_h, int B, int H, int L, int dk, int dv, size_t* bytes);
+int dp_bwd_f32(const float* q, const float* k, const float* v, const float* beta, const float* g,
+               const float* h0, const float* dout, const float* dfinal, int n_h, int B, int H,
+               int L, int dk, int dv, float* dq, float* dk_out, float* dv_out, float* dbeta,
+               float* dg, float* dh0, void* workspace, size_t workspace_bytes, dp_stream stream);
+int dp_bwd_bf16(const void* q, const void* k, const void* v, const float* beta, const float* g,
+                const float* h0, const void* dout, const float* dfinal, int n_h, int B, int H,
+                int L, int dk, int dv, float* dq, float* dk_out, float* dv_out, float* dbeta,
+                float* dg, float* dh0, void* workspace, size_t workspace_bytes, dp_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -27,6 +27,7 @@ EXPORTS = (
     "dp_decode_f32", "dp_decode_bf16",
     "dp_osdn_precond_ex_f32", "dp_osdn_precond_ex_bf16",
     "dp_fwd_varlen_workspace_size", "dp_fwd_varlen_bf16",
+    "dp_bwd_workspace_size", "dp_bwd_f32", "dp_bwd_bf16",
 )
 
 _lib = None
@@ -85,6 +86,12 @@ def load() -> ctypes.CDLL:
         for name in ("dp_decode_f32", "dp_decode_bf16"):
             getattr(lib, name).restype = _I
             getattr(lib, name).argtypes = dec
+        lib.dp_bwd_workspace_size.restype = _I
+        lib.dp_bwd_workspace_size.argtypes = [_I] * 6 + [ctypes.POINTER(ctypes.c_size_t)]
+        bwd = [_P] * 8 + [_I] * 6 + [_P] * 7 + [ctypes.c_size_t, _P]
+        for name in ("dp_bwd_f32", "dp_bwd_bf16"):
+            getattr(lib, name).restype = _I
+            getattr(lib, name).argtypes = bwd
         _lib = lib
     return _lib
 
@@ -340,3 +347,57 @@ def fwd_varlen(q, k, v, beta, cu_seqlens, g=None, *, chunk: int = 64, h0=None, o
                                    _stream(stream))
     _check(rc, "dp_fwd_varlen_bf16")
     return out, final_state
+
+
+def bwd_workspace_size(n_h, B, H, L, dk, dv) -> int:
+    """Workspace bytes of :func:`bwd` (dp_bwd_workspace_size)."""
+    n = ctypes.c_size_t(0)
+    _check(load().dp_bwd_workspace_size(n_h, B, H, L, dk, dv, ctypes.byref(n)),
+           "dp_bwd_workspace_size")
+    return n.value
+
+
+def bwd(q, k, v, beta, dout, g=None, *, h0=None, dfinal=None, workspace=None, grads=None,
+        stream=None) -> dict:
+    """Gradient of the symmetric forward through libdp (dp_bwd_f32 / dp_bwd_bf16).
+
+    Inputs as :func:`fwd` (q, k, v and dout in one dtype, float32 or
+    bfloat16), dout [B,L,H,dv] the gradient on out and dfinal [B,H,dk,dv] f32
+    (or None) the gradient on the final state.  Returns a dict of float32
+    gradients ``q, k, v, beta, h0`` and ``g`` when a gate is given; ``grads``
+    may hold preallocated tensors under those names.
+    """
+    if q.dim() != 4 or k.dim() != 5 or v.dim() != 5:
+        raise ValueError("expected q[B,L,H,dk], k[B,L,H,n_h,dk], v[B,L,H,n_h,dv]")
+    B, L, H, dk = q.shape
+    n_h, dv = k.shape[3], v.shape[4]
+    dev, dt = q.device, q.dtype
+    suf = _suffix(dt)
+    _need(k, "k", dt, (B, L, H, n_h, dk), dev)
+    _need(v, "v", dt, (B, L, H, n_h, dv), dev)
+    _need(dout, "dout", dt, (B, L, H, dv), dev)
+    _need(beta, "beta", torch.float32, (B, L, H, n_h), dev)
+    _need(g, "g", torch.float32, (B, L, H), dev)
+    _need(h0, "h0", torch.float32, (B, H, dk, dv), dev)
+    _need(dfinal, "dfinal", torch.float32, (B, H, dk, dv), dev)
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    shapes = dict(q=(B, L, H, dk), k=(B, L, H, n_h, dk), v=(B, L, H, n_h, dv), beta=(B, L, H, n_h),
+                  h0=(B, H, dk, dv))
+    if g is not None:
+        shapes["g"] = (B, L, H)
+    out = dict(grads or {})
+    for n, shp in shapes.items():
+        if n not in out:
+            out[n] = torch.empty(shp, dtype=torch.float32, device=dev)
+        _need(out[n], "grad " + n, torch.float32, shp, dev)
+    if workspace is None:
+        nbytes = bwd_workspace_size(n_h, B, H, L, dk, dv)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    fn = getattr(load(), f"dp_bwd_{suf}")
+    rc = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(h0), _ptr(dout), _ptr(dfinal),
+            n_h, B, H, L, dk, dv, _ptr(out["q"]), _ptr(out["k"]), _ptr(out["v"]), _ptr(out["beta"]),
+            _ptr(out.get("g")), _ptr(out["h0"]), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc, f"dp_bwd_{suf}")
+    return out

@@ -9,6 +9,7 @@
 #include <string.h>
 
 #include "dp.h"
+#include "dp_bwd.hpp"
 #include "dp_kernels.hpp"
 
 DP_DECLARE_LAUNCHERS(f32, 16)
@@ -19,6 +20,14 @@ DP_DECLARE_LAUNCHERS(bf16, 16)
 DP_DECLARE_LAUNCHERS(bf16, 32)
 DP_DECLARE_LAUNCHERS(bf16, 64)
 DP_DECLARE_LAUNCHERS(bf16, 128)
+DP_DECLARE_BWD_LAUNCHER(f32, 16)
+DP_DECLARE_BWD_LAUNCHER(f32, 32)
+DP_DECLARE_BWD_LAUNCHER(f32, 64)
+DP_DECLARE_BWD_LAUNCHER(f32, 128)
+DP_DECLARE_BWD_LAUNCHER(bf16, 16)
+DP_DECLARE_BWD_LAUNCHER(bf16, 32)
+DP_DECLARE_BWD_LAUNCHER(bf16, 64)
+DP_DECLARE_BWD_LAUNCHER(bf16, 128)
 
 namespace {
 
@@ -461,6 +470,113 @@ int precond_impl(int elem, const void* k, const float* beta, const float* ret, i
   return e == hipSuccess ? DP_OK : DP_EHIP;
 }
 
+// Backward: fixed chunk of kBwdChunk sub-steps.  Workspace: T (fp32) and
+// (1/|k|, G) per chunk, the chunk-start states, the chunk-end state
+// gradients and the pseudo-value gradients.
+struct BwdWs {
+  size_t t, s, hs, dhe, dup, total;
+};
+
+BwdWs bwd_ws(const Shape& s) {
+  const size_t nch = (size_t)s.B * s.H * num_chunks(s);
+  BwdWs w;
+  w.t = align_up(nch * s.chunk * s.chunk * 4, kWsAlign);
+  w.s = align_up(nch * s.chunk * sizeof(float2), kWsAlign);
+  w.hs = align_up(nch * s.dk * s.dv * 4, kWsAlign);
+  w.dhe = w.hs;
+  w.dup = align_up(nch * s.chunk * s.dv * 4, kWsAlign);
+  w.total = w.t + w.s + w.hs + w.dhe + w.dup;
+  return w;
+}
+
+hipError_t dispatch_bwd(int elem, int dk, const dp::FwdArgs& fa, const dp::BwdArgs& a, hipStream_t st) {
+  if (elem == 4) {
+    switch (dk) {
+      case 16: return dp_launch_bwd_f32_16(fa, a, st);
+      case 32: return dp_launch_bwd_f32_32(fa, a, st);
+      case 64: return dp_launch_bwd_f32_64(fa, a, st);
+      case 128: return dp_launch_bwd_f32_128(fa, a, st);
+    }
+  } else {
+    switch (dk) {
+      case 16: return dp_launch_bwd_bf16_16(fa, a, st);
+      case 32: return dp_launch_bwd_bf16_32(fa, a, st);
+      case 64: return dp_launch_bwd_bf16_64(fa, a, st);
+      case 128: return dp_launch_bwd_bf16_128(fa, a, st);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+int bwd_impl(int elem, const void* q, const void* k, const void* v, const float* beta,
+             const float* g, const float* h0, const void* dout, const float* dfinal, int n_h,
+             int B, int H, int L, int dk, int dv, float* dq, float* dk_out, float* dv_out,
+             float* dbeta, float* dg, float* dh0, void* workspace, size_t workspace_bytes,
+             dp_stream stream) {
+  const Shape s{n_h, B, H, L, dk, dv, dp::kBwdChunk};
+  int rc = check_shape(s);
+  if (rc != DP_OK) return rc;
+  if (L > 0 && (q == nullptr || k == nullptr || v == nullptr || beta == nullptr || dout == nullptr ||
+                dq == nullptr || dk_out == nullptr || dv_out == nullptr || dbeta == nullptr))
+    return DP_EINVAL;
+  const BwdWs w = bwd_ws(s);
+  if (workspace_bytes < w.total || workspace == nullptr) return DP_EWORKSPACE;
+  if (((uintptr_t)workspace & (kWsAlign - 1)) != 0) return DP_EWORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+
+  dp::FwdArgs fa;
+  memset(&fa, 0, sizeof(fa));
+  fa.k = k;
+  fa.beta = beta;
+  fa.g = g;
+  fa.wsT = ws;
+  fa.wsS = reinterpret_cast<float2*>(ws + w.t);
+  fa.N = L * n_h;
+  fa.B = B;
+  fa.H = H;
+  fa.L = L;
+  fa.n_h = n_h;
+  fa.dv = dv;
+  fa.nc = num_chunks(s);
+  fastdiv_magic(n_h, &fa.nh_magic, &fa.nh_shift);
+
+  dp::BwdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.beta = beta;
+  a.g = g;
+  a.h0 = h0;
+  a.dout = dout;
+  a.dfinal = dfinal;
+  a.wsT = reinterpret_cast<const float*>(ws);
+  a.wsS = fa.wsS;
+  a.hs = reinterpret_cast<float*>(ws + w.t + w.s);
+  a.dhe = reinterpret_cast<float*>(ws + w.t + w.s + w.hs);
+  a.dup = reinterpret_cast<float*>(ws + w.t + w.s + w.hs + w.dhe);
+  a.dq = dq;
+  a.dk = dk_out;
+  a.dv = dv_out;
+  a.dbeta = dbeta;
+  a.dg = g != nullptr ? dg : nullptr;
+  a.dh0 = dh0;
+  a.N = fa.N;
+  a.B = B;
+  a.H = H;
+  a.L = L;
+  a.n_h = n_h;
+  a.dvd = dv;
+  a.nc = fa.nc;
+  a.RT = readout_rows(dp::kBwdChunk, n_h);
+  a.nvb = dv / dp::kBwdBV;
+  a.nh_magic = fa.nh_magic;
+  a.nh_shift = fa.nh_shift;
+  if (a.RT != 16 && a.RT != 32) return DP_ENOTSUP;
+  const hipError_t e = dispatch_bwd(elem, dk, fa, a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DP_OK : DP_EHIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -619,6 +735,31 @@ int dp_decode_bf16(const void* q, const void* k, const void* kt, const void* v,
                    const float* beta, const float* g, const float* ga, int n_h, int B, int H,
                    int dk, int dv, void* out, float* state, int flags, dp_stream stream) {
   return decode_impl(2, q, k, kt, v, beta, g, ga, n_h, B, H, dk, dv, out, state, flags, stream);
+}
+
+int dp_bwd_workspace_size(int n_h, int B, int H, int L, int dk, int dv, size_t* bytes) {
+  if (bytes == nullptr) return DP_EINVAL;
+  const Shape s{n_h, B, H, L, dk, dv, dp::kBwdChunk};
+  const int rc = check_shape(s);
+  if (rc != DP_OK) return rc;
+  *bytes = bwd_ws(s).total;
+  return DP_OK;
+}
+
+int dp_bwd_f32(const float* q, const float* k, const float* v, const float* beta, const float* g,
+               const float* h0, const float* dout, const float* dfinal, int n_h, int B, int H,
+               int L, int dk, int dv, float* dq, float* dk_out, float* dv_out, float* dbeta,
+               float* dg, float* dh0, void* workspace, size_t workspace_bytes, dp_stream stream) {
+  return bwd_impl(4, q, k, v, beta, g, h0, dout, dfinal, n_h, B, H, L, dk, dv, dq, dk_out, dv_out,
+                  dbeta, dg, dh0, workspace, workspace_bytes, stream);
+}
+
+int dp_bwd_bf16(const void* q, const void* k, const void* v, const float* beta, const float* g,
+                const float* h0, const void* dout, const float* dfinal, int n_h, int B, int H,
+                int L, int dk, int dv, float* dq, float* dk_out, float* dv_out, float* dbeta,
+                float* dg, float* dh0, void* workspace, size_t workspace_bytes, dp_stream stream) {
+  return bwd_impl(2, q, k, v, beta, g, h0, dout, dfinal, n_h, B, H, L, dk, dv, dq, dk_out, dv_out,
+                  dbeta, dg, dh0, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

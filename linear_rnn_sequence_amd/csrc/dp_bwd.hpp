@@ -1,0 +1,786 @@
+// dp_bwd.hpp -- gfx950 kernels of the chunkwise DeltaProduct backward.
+//
+// The gradient of the forward of the DeltaProduct study notes (arXiv
+// 2502.10297v7: sec. 2.2 Eq.(3) sub-steps, sec. 2.6 gate and readout, sec. 4.1
+// the expanded sequence) w.r.t. q, the raw keys, v, the raw beta, the gate
+// and the initial state, for symmetric keys.  It is the reverse-mode
+// derivative of the chunkwise form (OSDN study notes, arXiv 2605.13473v1,
+// sec. 2.5 / App.A.2, with the chunk-local log-gate G).  Per chunk, with the
+// chunk-start state H0, Tb = T diag(beta):
+//
+//   X  = V - diag(e^G) K H0             Up = Tb X
+//   H1 = e^{G_C} H0 + K^T diag(e^{G_C - G}) Up
+//   O  = diag(e^{G_l}) Q H0 + P Up,      P_rj = e^{G_l - G_j} q_r.k_j  (j <= l)
+//
+// (l the readout sub-step of row r).  Given dH1 and dO, reverse mode gives
+//
+//   dUp = diag(e^{G_C - G}) K dH1 + P^T dO          dX = Tb^T dUp  (= dV)
+//   dH0 = e^{G_C} dH1 + Q^T diag(e^{G_l}) dO - K^T diag(e^G) dX
+//   dTb = dUp X^T,  dT = dTb diag(beta),  dM = -T^T dT T^T  (strictly lower)
+//
+// and the key, query, beta and log-gate terms collected in
+// dp_bwd_chunk_kernel.  Four launches:
+//   dp_ut_kernel<.., float, false>  T (fp32) and (1/|k|, G) per chunk
+//   dp_bwd_states_kernel   sequential over chunks per (head, value block):
+//                          the forward's chunk-start states H0 -> workspace
+//   dp_bwd_dstate_kernel   sequential over chunks in reverse: dH1 and dUp
+//                          of every chunk -> workspace, dH0 of chunk 0 -> dh0
+//   dp_bwd_chunk_kernel    one workgroup per chunk, all in parallel: dq, dk,
+//                          dv, dbeta, dg from H0, dH1, dUp and the chunk
+// All arithmetic is fp32 (fp32 MFMA, 16x16x4), whatever the input type.
+#pragma once
+
+#include "dp_kernels.hpp"
+
+namespace dp {
+
+constexpr int kBwdChunk = 32;  // sub-steps per chunk of the backward
+constexpr int kBwdBV = 16;     // value columns per block
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* beta;
+  const float* g;       // nullptr: no gate
+  const float* h0;      // nullptr: zero initial state
+  const void* dout;     // [B, L, H, dv], input type
+  const float* dfinal;  // [B, H, dk, dv] or nullptr (zero)
+  const float* wsT;     // [B*H*nc][C][C] T (fp32)
+  const float2* wsS;    // [B*H*nc][C] (1/|k|, G)
+  float* hs;            // [B*H*nc][dk][dv] chunk-start states
+  float* dhe;           // [B*H*nc][dk][dv] gradients of the chunk-end states
+  float* dup;           // [B*H*nc][C][dv] gradients of the pseudo-values
+  float* dq;            // [B, L, H, dk]
+  float* dk;            // [B, L, H, n_h, dk]
+  float* dv;            // [B, L, H, n_h, dv]
+  float* dbeta;         // [B, L, H, n_h]
+  float* dg;            // [B, L, H] or nullptr
+  float* dh0;           // [B, H, dk, dv] or nullptr
+  int N, B, H, L, n_h, dvd, nc, RT, nvb;
+  uint32_t nh_magic;
+  int nh_shift;
+};
+
+// acc += A * B, A read transposed (element (m, k) at a[k * lda + ra + m]) and
+// B read k-major (element (k, n) at b[k * ldb + rb + n]).
+template <int K>
+__device__ __forceinline__ f32x4_t mm_tile_tt(f32x4_t acc, const float* a, int lda, int ra, const float* b,
+                                              int ldb, int rb) {
+  using M = Mfma<float>;
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += M::KS) acc = M::mma(M::load_t(a, lda, ra, k0), M::load_t(b, ldb, rb, k0), acc);
+  return acc;
+}
+
+// Sum over the 16 lanes of one lane group (one accumulator row of a tile).
+__device__ __forceinline__ float sum16(float x) {
+  x += __shfl_xor(x, 8);
+  x += __shfl_xor(x, 4);
+  x += __shfl_xor(x, 2);
+  x += __shfl_xor(x, 1);
+  return x;
+}
+// Sum over the 4 lane groups (one accumulator column of a tile, per e).
+__device__ __forceinline__ float sum_groups(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+// Per-chunk indexing shared by the backward kernels: row of each sub-step in
+// the [B, L, H, n_h, *] tensors (-1 past the end), token of each readout row
+// (-1 when the row is empty) and its sub-step within the chunk.
+struct BwdChunkMeta {
+  long long* row;  // [C]
+  long long* tok;  // [RT]
+  int* loc;        // [RT]
+};
+
+template <int C>
+__device__ __forceinline__ void bwd_index_chunk(const BwdArgs& p, int b, int h, int c, int RT,
+                                                const BwdChunkMeta& m) {
+  const int tid = threadIdx.x;
+  const int s0 = c * C;
+  const long long tok0 = (long long)b * p.L * p.H + h;
+  if (tid < C) {
+    const int s = s0 + tid;
+    long long row = -1;
+    if (s < p.N) {
+      const int t = fastdiv(s, p.nh_magic, p.nh_shift);
+      row = (tok0 + (long long)t * p.H) * p.n_h + (s - t * p.n_h);
+    }
+    m.row[tid] = row;
+  }
+  if (tid < RT) {
+    const int r0 = s0 + (p.n_h - 1 - (s0 - fastdiv(s0, p.nh_magic, p.nh_shift) * p.n_h));
+    const int s = r0 + tid * p.n_h;
+    const bool ok = s < s0 + C && s < p.N;
+    m.tok[tid] = ok ? tok0 + (long long)fastdiv(s, p.nh_magic, p.nh_shift) * p.H : -1;
+    m.loc[tid] = ok ? s - s0 : -1;
+  }
+}
+
+// Unit keys of the chunk (fp32, zero past the end) into sK[C][LDK].
+template <typename T, int DK, int C, int LDK>
+__device__ __forceinline__ void bwd_load_keys(const BwdArgs& p, const long long* row, const float* rinv,
+                                              float* sK) {
+  const T* kp = static_cast<const T*>(p.k);
+  for (int idx = threadIdx.x; idx < C * DK; idx += blockDim.x) {
+    const int r = idx / DK, d = idx % DK;
+    const long long rw = row[r];
+    sK[r * LDK + d] = rw >= 0 ? to_f32(kp[rw * DK + d]) * rinv[r] : 0.f;
+  }
+}
+
+// Readout queries of the chunk (zero for empty rows) into sQ[RT][LDK].
+template <typename T, int DK, int LDK>
+__device__ __forceinline__ void bwd_load_queries(const BwdArgs& p, const long long* tok, int RT, float* sQ) {
+  const T* qp = static_cast<const T*>(p.q);
+  for (int idx = threadIdx.x; idx < RT * DK; idx += blockDim.x) {
+    const int r = idx / DK, d = idx % DK;
+    const long long tk = tok[r];
+    sQ[r * LDK + d] = tk >= 0 ? to_f32(qp[tk * DK + d]) : 0.f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dp_bwd_states_kernel: the forward's chunk-start states, one workgroup per
+// (head, block of BV value columns), sequential over the chunks.  The state
+// lives in LDS (fp32); each wavefront updates the tiles it owns.
+template <typename T, int DK, int C, int BV>
+__global__ __launch_bounds__(256) void dp_bwd_states_kernel(BwdArgs p) {
+  constexpr int LDK = DK + 4, LDC = C + 4, LDB = BV + 4;
+  constexpr int NCT = C / 16, NDT = DK / 16, NVT = BV / 16;
+  __shared__ float sK[C * LDK], sT[C * LDC], sH[DK * LDB], sXb[C * LDB], sU[C * LDB], sV[C * LDB];
+  __shared__ float sB[C], sEG[C], sEL[C], sRinv[C];
+  __shared__ long long sRow[C];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  const int bh = blockIdx.x / p.nvb, vb = blockIdx.x % p.nvb;
+  const int b = bh / p.H, h = bh % p.H;
+  const int v0 = vb * BV;
+  const T* vp = static_cast<const T*>(p.v);
+
+  for (int idx = tid; idx < DK * BV; idx += 256) {
+    const int d = idx / BV, n = idx % BV;
+    sH[d * LDB + n] = p.h0 != nullptr ? p.h0[((long long)bh * DK + d) * p.dvd + v0 + n] : 0.f;
+  }
+  for (int c = 0; c < p.nc; ++c) {
+    const long long chunk = (long long)bh * p.nc + c;
+    __syncthreads();  // the previous chunk is done with every buffer
+    if (tid < C) {
+      const int s = c * C + tid;
+      long long row = -1;
+      if (s < p.N) {
+        const int t = fastdiv(s, p.nh_magic, p.nh_shift);
+        row = (((long long)b * p.L + t) * p.H + h) * p.n_h + (s - t * p.n_h);
+      }
+      sRow[tid] = row;
+      const float2 sc = p.wsS[chunk * C + tid];
+      const float gl = p.wsS[chunk * C + C - 1].y;
+      sRinv[tid] = sc.x;
+      sEG[tid] = expf(sc.y);
+      sEL[tid] = expf(gl - sc.y);
+      sB[tid] = row >= 0 ? clamp_keep_nan(p.beta[row], 0.f, 2.f) : 0.f;
+    }
+    // the state at the chunk start
+    float* hdst = p.hs + chunk * DK * p.dvd + v0;
+    for (int idx = tid; idx < DK * BV; idx += 256) {
+      const int d = idx / BV, n = idx % BV;
+      hdst[(long long)d * p.dvd + n] = sH[d * LDB + n];
+    }
+    __syncthreads();
+    bwd_load_keys<T, DK, C, LDK>(p, sRow, sRinv, sK);
+    const float* tsrc = p.wsT + chunk * C * C;
+    for (int idx = tid; idx < C * C; idx += 256) sT[(idx / C) * LDC + idx % C] = tsrc[idx];
+    for (int idx = tid; idx < C * BV; idx += 256) {
+      const int r = idx / BV, n = idx % BV;
+      const long long rw = sRow[r];
+      sV[r * LDB + n] = rw >= 0 ? to_f32(vp[rw * p.dvd + v0 + n]) : 0.f;
+    }
+    __syncthreads();
+    // beta X = beta (V - diag(e^G) K H0)
+    for (int tile = wave; tile < NCT * NVT; tile += 4) {
+      const int ct = tile / NVT, nt = tile % NVT;
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mm_tile_tb<float, DK>(acc, sK, LDK, ct * 16, sH, LDB, nt * 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = ct * 16 + 4 * grp + e, n = nt * 16 + col;
+        sXb[r * LDB + n] = sB[r] * (sV[r * LDB + n] - sEG[r] * acc[e]);
+      }
+    }
+    __syncthreads();
+    // diag(e^{G_C - G}) Up, Up = T (beta X)
+    for (int tile = wave; tile < NCT * NVT; tile += 4) {
+      const int ct = tile / NVT, nt = tile % NVT;
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mm_tile_tb<float, C>(acc, sT, LDC, ct * 16, sXb, LDB, nt * 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = ct * 16 + 4 * grp + e;
+        sU[r * LDB + nt * 16 + col] = sEL[r] * acc[e];
+      }
+    }
+    __syncthreads();
+    // H = e^{G_C} H + K^T (diag(e^{G_C - G}) Up): each wavefront its own tiles
+    const float egl = sEG[C - 1];
+    for (int tile = wave; tile < NDT * NVT; tile += 4) {
+      const int dt = tile / NVT, nt = tile % NVT;
+      f32x4_t acc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = egl * sH[(dt * 16 + 4 * grp + e) * LDB + nt * 16 + col];
+      acc = mm_tile_tt<C>(acc, sK, LDK, dt * 16, sU, LDB, nt * 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sH[(dt * 16 + 4 * grp + e) * LDB + nt * 16 + col] = acc[e];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dp_bwd_dstate_kernel: the reverse chunk scan of the state gradient, one
+// workgroup per (head, block of BV value columns), chunks last to first.
+// Writes dH1 (the gradient of each chunk's end state) and dUp per chunk, and
+// the gradient of the initial state.
+template <typename T, int DK, int C, int BV, int NRT>
+__global__ __launch_bounds__(256) void dp_bwd_dstate_kernel(BwdArgs p) {
+  constexpr int RT = 16 * NRT;
+  constexpr int LDK = DK + 4, LDC = C + 4, LDB = BV + 4;
+  constexpr int NCT = C / 16, NDT = DK / 16, NVT = BV / 16;
+  __shared__ float sK[C * LDK], sQ[RT * LDK], sT[C * LDC], sP[RT * LDC];
+  __shared__ float sdH[DK * LDB], sdO[RT * LDB], sdOe[RT * LDB], sdUp[C * LDB], sdX[C * LDB];
+  __shared__ float sB[C], sG[C], sEG[C], sEL[C], sRinv[C];
+  __shared__ long long sRow[C], sTok[RT];
+  __shared__ int sLoc[RT];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  const int bh = blockIdx.x / p.nvb, vb = blockIdx.x % p.nvb;
+  const int b = bh / p.H, h = bh % p.H;
+  const int v0 = vb * BV;
+  const T* dop = static_cast<const T*>(p.dout);
+  const BwdChunkMeta meta{sRow, sTok, sLoc};
+
+  for (int idx = tid; idx < DK * BV; idx += 256) {
+    const int d = idx / BV, n = idx % BV;
+    sdH[d * LDB + n] = p.dfinal != nullptr ? p.dfinal[((long long)bh * DK + d) * p.dvd + v0 + n] : 0.f;
+  }
+  for (int c = p.nc - 1; c >= 0; --c) {
+    const long long chunk = (long long)bh * p.nc + c;
+    __syncthreads();  // the previous chunk is done with every buffer
+    bwd_index_chunk<C>(p, b, h, c, RT, meta);
+    if (tid < C) {
+      const float2 sc = p.wsS[chunk * C + tid];
+      const float gl = p.wsS[chunk * C + C - 1].y;
+      sRinv[tid] = sc.x;
+      sG[tid] = sc.y;
+      sEG[tid] = expf(sc.y);
+      sEL[tid] = expf(gl - sc.y);
+    }
+    // the gradient of the chunk's end state
+    float* ddst = p.dhe + chunk * DK * p.dvd + v0;
+    for (int idx = tid; idx < DK * BV; idx += 256) {
+      const int d = idx / BV, n = idx % BV;
+      ddst[(long long)d * p.dvd + n] = sdH[d * LDB + n];
+    }
+    __syncthreads();
+    if (tid < C) sB[tid] = sRow[tid] >= 0 ? clamp_keep_nan(p.beta[sRow[tid]], 0.f, 2.f) : 0.f;
+    bwd_load_keys<T, DK, C, LDK>(p, sRow, sRinv, sK);
+    bwd_load_queries<T, DK, LDK>(p, sTok, RT, sQ);
+    const float* tsrc = p.wsT + chunk * C * C;
+    for (int idx = tid; idx < C * C; idx += 256) sT[(idx / C) * LDC + idx % C] = tsrc[idx];
+    for (int idx = tid; idx < RT * BV; idx += 256) {
+      const int r = idx / BV, n = idx % BV;
+      const long long tk = sTok[r];
+      const float x = tk >= 0 ? to_f32(dop[tk * p.dvd + v0 + n]) : 0.f;
+      sdO[r * LDB + n] = x;
+      sdOe[r * LDB + n] = tk >= 0 ? expf(sG[sLoc[r]]) * x : 0.f;
+    }
+    __syncthreads();
+    // P = masked, gated scores (RT x C)
+    for (int tile = wave; tile < NRT * NCT; tile += 4) {
+      const int rt = tile / NCT, ct = tile % NCT;
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mm_tile<float, DK>(acc, sQ, LDK, rt * 16, sK, LDK, ct * 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = rt * 16 + 4 * grp + e, j = ct * 16 + col;
+        const int l = sLoc[r];
+        sP[r * LDC + j] = (l >= 0 && j <= l) ? acc[e] * expf(sG[l] - sG[j]) : 0.f;
+      }
+    }
+    __syncthreads();
+    // dUp = diag(e^{G_C - G}) K dH1 + P^T dO
+    for (int tile = wave; tile < NCT * NVT; tile += 4) {
+      const int ct = tile / NVT, nt = tile % NVT;
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
+      acc = mm_tile_tb<float, DK>(acc, sK, LDK, ct * 16, sdH, LDB, nt * 16);
+      acc2 = mm_tile_tt<RT>(acc2, sP, LDC, ct * 16, sdO, LDB, nt * 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = ct * 16 + 4 * grp + e, n = nt * 16 + col;
+        const float du = sEL[j] * acc[e] + acc2[e];
+        sdUp[j * LDB + n] = du;
+        p.dup[(chunk * C + j) * p.dvd + v0 + n] = du;
+      }
+    }
+    __syncthreads();
+    // diag(e^G) dX,  dX = Tb^T dUp = diag(beta) T^T dUp
+    for (int tile = wave; tile < NCT * NVT; tile += 4) {
+      const int ct = tile / NVT, nt = tile % NVT;
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mm_tile_tt<C>(acc, sT, LDC, ct * 16, sdUp, LDB, nt * 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = ct * 16 + 4 * grp + e;
+        sdX[j * LDB + nt * 16 + col] = sEG[j] * sB[j] * acc[e];
+      }
+    }
+    __syncthreads();
+    // dH0 = e^{G_C} dH1 + Q^T diag(e^{G_l}) dO - K^T diag(e^G) dX
+    const float egl = sEG[C - 1];
+    for (int tile = wave; tile < NDT * NVT; tile += 4) {
+      const int dt = tile / NVT, nt = tile % NVT;
+      f32x4_t acc, acc2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = egl * sdH[(dt * 16 + 4 * grp + e) * LDB + nt * 16 + col];
+      acc = mm_tile_tt<RT>(acc, sQ, LDK, dt * 16, sdOe, LDB, nt * 16);
+      acc2 = mm_tile_tt<C>(acc2, sK, LDK, dt * 16, sdX, LDB, nt * 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sdH[(dt * 16 + 4 * grp + e) * LDB + nt * 16 + col] = acc[e] - acc2[e];
+    }
+  }
+  __syncthreads();
+  if (p.dh0 != nullptr) {
+    for (int idx = tid; idx < DK * BV; idx += 256) {
+      const int d = idx / BV, n = idx % BV;
+      p.dh0[((long long)bh * DK + d) * p.dvd + v0 + n] = sdH[d * LDB + n];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dp_bwd_chunk_kernel: the per-chunk gradients, one workgroup per chunk.
+//
+// The value columns are taken in blocks of 16: each block's X, Up and dX are
+// formed in LDS and folded into register accumulators (fixed tile ownership
+// per wavefront) of
+//   dXH = dX H0^T (C x DK)   Y = Up dH1^T (C x DK)   A = dO H0^T (RT x DK)
+//   dP = dO Up^T (RT x C)    dTb = dUp X^T (C x C)   <dH1, H0>
+// after which the key, query, beta and log-gate gradients follow:
+//   dq_r  = e^{G_l} A_r + sum_j Gm_rj k_j,     Gm_rj = e^{G_l - G_j} dP_rj (j <= l)
+//   dkn   = -diag(e^G) dXH + diag(e^{G_C - G}) Y + Gm^T Q + Z K + Z^T K
+//   Z_ij  = F_ij beta_i e^{G_i - G_j},  F = strict_tril(-T^T (dTb diag(beta)) T^T)
+//   dbeta_j = sum_i dTb_ij T_ij + sum_i' F_ji' e^{G_j - G_i'} S_ji'   (S = K K^T)
+//   dG    = the gate terms of each product, then dlog g = reverse cumsum of dG
+// and finally the key normalisation, the beta clamp and the log of the gate.
+template <int DK, int C, int RT>
+__host__ __device__ constexpr int bwd_chunk_lds_floats() {
+  return C * (DK + 4) + RT * (DK + 4) + 3 * C * (C + 4) + RT * (C + 4) + 2 * DK * 20 + 6 * C * 20 +
+         RT * 20 + 8 * C;
+}
+template <int DK, int C, int RT>
+__host__ __device__ constexpr int bwd_chunk_lds_bytes() {
+  return bwd_chunk_lds_floats<DK, C, RT>() * 4 + C * 8 + RT * 12;
+}
+
+template <typename T, int DK, int C, int NRT>
+__global__ __launch_bounds__(256) void dp_bwd_chunk_kernel(BwdArgs p) {
+  constexpr int BV = 16;
+  constexpr int RT = 16 * NRT;
+  constexpr int LDK = DK + 4, LDC = C + 4, LDB = BV + 4;
+  constexpr int NCT = C / 16, NDT = DK / 16;
+  constexpr int NKD = NCT * NDT, KPW = (NKD + 3) / 4;  // C x DK tiles
+  constexpr int NQD = NRT * NDT, QPW = (NQD + 3) / 4;  // RT x DK tiles
+  constexpr int NCC = NCT * NCT, NRC = NRT * NCT;
+  static_assert(NCC <= 4 && NRC <= 4 && 2 * NCT <= 4, "one C x C and one RT x C tile per wavefront");
+
+  extern __shared__ __align__(16) float smf[];
+  float* sK = smf;                   // C x LDK unit keys
+  float* sQ = sK + C * LDK;          // RT x LDK readout queries
+  float* sT = sQ + RT * LDK;         // C x LDC  T
+  float* sA = sT + C * LDC;          // C x LDC  dT, then Z
+  float* sW = sA + C * LDC;          // C x LDC  T^T dT
+  float* sGm = sW + C * LDC;         // RT x LDC gated, masked dP
+  float* sH0 = sGm + RT * LDC;       // DK x LDB
+  float* sdHe = sH0 + DK * LDB;      // DK x LDB
+  float* sV = sdHe + DK * LDB;       // C x LDB
+  float* sdUp = sV + C * LDB;
+  float* sX = sdUp + C * LDB;
+  float* sXb = sX + C * LDB;         // beta X
+  float* sUp = sXb + C * LDB;
+  float* sdX = sUp + C * LDB;
+  float* sdO = sdX + C * LDB;        // RT x LDB
+  float* sB = sdO + RT * LDB;        // C scalars each
+  float* sG = sB + C;
+  float* sEG = sG + C;
+  float* sEL = sEG + C;
+  float* sRinv = sEL + C;
+  float* sDB = sRinv + C;            // dbeta accumulator
+  float* sDG = sDB + C;              // dG accumulator
+  float* sRD = sDG + C;              // k . dkn per row
+  long long* sRow = reinterpret_cast<long long*>(sRD + C);
+  long long* sTok = sRow + C;
+  int* sLoc = reinterpret_cast<int*>(sTok + RT);
+  static_assert(BV + 4 == 20 && bwd_chunk_lds_floats<DK, C, RT>() ==
+                    C * LDK + RT * LDK + 3 * C * LDC + RT * LDC + 2 * DK * LDB + 6 * C * LDB + RT * LDB + 8 * C,
+                "LDS layout");
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  const long long chunk = blockIdx.x;
+  const int bh = (int)(chunk / p.nc), c = (int)(chunk % p.nc);
+  const int b = bh / p.H, h = bh % p.H;
+  const T* vp = static_cast<const T*>(p.v);
+  const T* dop = static_cast<const T*>(p.dout);
+  const BwdChunkMeta meta{sRow, sTok, sLoc};
+
+  bwd_index_chunk<C>(p, b, h, c, RT, meta);
+  if (tid < C) {
+    const float2 sc = p.wsS[chunk * C + tid];
+    sRinv[tid] = sc.x;
+    sG[tid] = sc.y;
+    sDB[tid] = 0.f;
+    sDG[tid] = 0.f;
+    sRD[tid] = 0.f;
+  }
+  __syncthreads();
+  if (tid < C) {
+    sB[tid] = sRow[tid] >= 0 ? clamp_keep_nan(p.beta[sRow[tid]], 0.f, 2.f) : 0.f;
+    sEG[tid] = expf(sG[tid]);
+    sEL[tid] = expf(sG[C - 1] - sG[tid]);
+  }
+  bwd_load_keys<T, DK, C, LDK>(p, sRow, sRinv, sK);
+  bwd_load_queries<T, DK, LDK>(p, sTok, RT, sQ);
+  {
+    const float* tsrc = p.wsT + chunk * C * C;
+    for (int idx = tid; idx < C * C; idx += 256) sT[(idx / C) * LDC + idx % C] = tsrc[idx];
+  }
+  __syncthreads();
+
+  // S = K K^T (tile `wave`) and Q K^T (tile `wave` when < NRC), kept in registers
+  const int cit = wave / NCT, cjt = wave % NCT;  // the C x C tile of this wavefront
+  const int rrt = wave / NCT, rct = wave % NCT;  // the RT x C tile of this wavefront
+  f32x4_t accS = {0.f, 0.f, 0.f, 0.f}, accQK = {0.f, 0.f, 0.f, 0.f};
+  if (wave < NCC) accS = mm_tile<float, DK>(accS, sK, LDK, cit * 16, sK, LDK, cjt * 16);
+  if (wave < NRC) accQK = mm_tile<float, DK>(accQK, sQ, LDK, rrt * 16, sK, LDK, rct * 16);
+
+  f32x4_t aXH[KPW], aY[KPW], aA[QPW];
+  f32x4_t aP = {0.f, 0.f, 0.f, 0.f}, aTb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < KPW; ++u) aXH[u] = aY[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < QPW; ++u) aA[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float hdot = 0.f;
+
+  const float* hsrc = p.hs + chunk * DK * p.dvd;
+  const float* dhsrc = p.dhe + chunk * DK * p.dvd;
+  const float* dusrc = p.dup + chunk * C * p.dvd;
+  for (int vb = 0; vb < p.nvb; ++vb) {
+    const int v0 = vb * BV;
+    for (int idx = tid; idx < DK * BV; idx += 256) {
+      const int d = idx / BV, n = idx % BV;
+      const float a = hsrc[(long long)d * p.dvd + v0 + n], e = dhsrc[(long long)d * p.dvd + v0 + n];
+      sH0[d * LDB + n] = a;
+      sdHe[d * LDB + n] = e;
+      hdot = fmaf(a, e, hdot);
+    }
+    for (int idx = tid; idx < C * BV; idx += 256) {
+      const int r = idx / BV, n = idx % BV;
+      const long long rw = sRow[r];
+      sV[r * LDB + n] = rw >= 0 ? to_f32(vp[rw * p.dvd + v0 + n]) : 0.f;
+      sdUp[r * LDB + n] = dusrc[(long long)r * p.dvd + v0 + n];
+    }
+    for (int idx = tid; idx < RT * BV; idx += 256) {
+      const int r = idx / BV, n = idx % BV;
+      const long long tk = sTok[r];
+      sdO[r * LDB + n] = tk >= 0 ? to_f32(dop[tk * p.dvd + v0 + n]) : 0.f;
+    }
+    __syncthreads();
+    if (wave < NCT) {
+      // X = V - diag(e^G) K H0
+      const int ct = wave;
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mm_tile_tb<float, DK>(acc, sK, LDK, ct * 16, sH0, LDB, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = ct * 16 + 4 * grp + e;
+        const float x = sV[r * LDB + col] - sEG[r] * acc[e];
+        sX[r * LDB + col] = x;
+        sXb[r * LDB + col] = sB[r] * x;
+      }
+    } else if (wave < 2 * NCT) {
+      // dX = diag(beta) T^T dUp, which is dv
+      const int ct = wave - NCT;
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mm_tile_tt<C>(acc, sT, LDC, ct * 16, sdUp, LDB, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = ct * 16 + 4 * grp + e;
+        const float dx = sB[j] * acc[e];
+        sdX[j * LDB + col] = dx;
+        if (sRow[j] >= 0) p.dv[sRow[j] * p.dvd + v0 + col] = dx;
+      }
+    }
+    __syncthreads();
+    if (wave < NCT) {
+      // Up = T (beta X)
+      const int ct = wave;
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mm_tile_tb<float, C>(acc, sT, LDC, ct * 16, sXb, LDB, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sUp[(ct * 16 + 4 * grp + e) * LDB + col] = acc[e];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < KPW; ++u) {
+      const int tile = wave + 4 * u;
+      if (tile < NKD) {
+        const int ct = tile / NDT, dt = tile % NDT;
+        aXH[u] = mm_tile<float, BV>(aXH[u], sdX, LDB, ct * 16, sH0, LDB, dt * 16);
+        aY[u] = mm_tile<float, BV>(aY[u], sUp, LDB, ct * 16, sdHe, LDB, dt * 16);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < QPW; ++u) {
+      const int tile = wave + 4 * u;
+      if (tile < NQD) {
+        const int rt = tile / NDT, dt = tile % NDT;
+        aA[u] = mm_tile<float, BV>(aA[u], sdO, LDB, rt * 16, sH0, LDB, dt * 16);
+      }
+    }
+    if (wave < NRC) aP = mm_tile<float, BV>(aP, sdO, LDB, rrt * 16, sUp, LDB, rct * 16);
+    if (wave < NCC) aTb = mm_tile<float, BV>(aTb, sdUp, LDB, cit * 16, sX, LDB, cjt * 16);
+    __syncthreads();  // the next block overwrites the block buffers
+  }
+
+  // <dH1, H0>: block sum into the gate gradient of the chunk's last sub-step
+  hdot = sum16(hdot);
+  hdot += __shfl_xor(hdot, 16);
+  hdot += __shfl_xor(hdot, 32);
+  if (lane == 0) atomicAdd(&sDG[C - 1], sEG[C - 1] * hdot);
+
+  // dT = dTb diag(beta) -> sA;  dbeta_j += sum_i dTb_ij T_ij
+  if (wave < NCC) {
+    const int j = cjt * 16 + col;
+    float cs = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = cit * 16 + 4 * grp + e;
+      cs = fmaf(aTb[e], sT[i * LDC + j], cs);
+      sA[i * LDC + j] = aTb[e] * sB[j];
+    }
+    cs = sum_groups(cs);
+    if (grp == 0) atomicAdd(&sDB[j], cs);
+  }
+  __syncthreads();
+  // T^T dT -> sW
+  if (wave < NCC) {
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    acc = mm_tile_tt<C>(acc, sT, LDC, cit * 16, sA, LDC, cjt * 16);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sW[(cit * 16 + 4 * grp + e) * LDC + cjt * 16 + col] = acc[e];
+  }
+  __syncthreads();
+  // F = -(T^T dT) T^T (strictly lower); the M terms of dbeta and dG; Z -> sA
+  if (wave < NCC) {
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    acc = mm_tile<float, C>(acc, sW, LDC, cit * 16, sT, LDC, cjt * 16);
+    const int j = cjt * 16 + col;
+    float csum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = cit * 16 + 4 * grp + e;
+      const bool ok = j < i && sRow[i] >= 0;
+      const float ex = ok ? expf(sG[i] - sG[j]) : 0.f;
+      const float fm = ok ? -acc[e] * ex : 0.f;  // F_ij e^{G_i - G_j}
+      const float z = fm * sB[i];
+      const float zs = z * accS[e];
+      const float rb = sum16(fm * accS[e]);
+      const float rg = sum16(zs);
+      if (col == 0) {
+        atomicAdd(&sDB[i], rb);
+        atomicAdd(&sDG[i], rg);
+      }
+      csum += zs;
+      sA[i * LDC + j] = z;
+    }
+    csum = sum_groups(csum);
+    if (grp == 0) atomicAdd(&sDG[j], -csum);
+  }
+  // Gm = e^{G_l - G_j} dP (j <= l); the score terms of dG
+  if (wave < NRC) {
+    const int j = rct * 16 + col;
+    float csum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = rrt * 16 + 4 * grp + e;
+      const int l = sLoc[r];
+      const bool ok = l >= 0 && j <= l;
+      const float gm = ok ? aP[e] * expf(sG[l] - sG[j]) : 0.f;
+      const float pr = gm * accQK[e];
+      const float rs = sum16(pr);
+      if (col == 0 && l >= 0) atomicAdd(&sDG[l], rs);
+      csum += pr;
+      sGm[r * LDC + j] = gm;
+    }
+    csum = sum_groups(csum);
+    if (grp == 0) atomicAdd(&sDG[j], -csum);
+  }
+  __syncthreads();
+  // dq = diag(e^{G_l}) A + Gm K;  dG_l += e^{G_l} q_r . A_r
+  float* dqp = p.dq;
+#pragma unroll
+  for (int u = 0; u < QPW; ++u) {
+    const int tile = wave + 4 * u;
+    if (tile < NQD) {
+      const int rt = tile / NDT, dt = tile % NDT;
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mm_tile_tb<float, C>(acc, sGm, LDC, rt * 16, sK, LDK, dt * 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = rt * 16 + 4 * grp + e, d = dt * 16 + col;
+        const int l = sLoc[r];
+        const float el = l >= 0 ? sEG[l] : 0.f;
+        const float a = aA[u][e];
+        const float qd = sum16(sQ[r * LDK + d] * a * el);
+        if (l >= 0) {
+          dqp[sTok[r] * DK + d] = el * a + acc[e];
+          if (col == 0) atomicAdd(&sDG[l], qd);
+        }
+      }
+    }
+  }
+  // dkn = -diag(e^G) dXH + diag(e^{G_C - G}) Y + Gm^T Q + Z K + Z^T K, and its gate terms
+  f32x4_t dkn[KPW];
+  float glast = 0.f;
+#pragma unroll
+  for (int u = 0; u < KPW; ++u) {
+    const int tile = wave + 4 * u;
+    dkn[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (tile < NKD) {
+      const int ct = tile / NDT, dt = tile % NDT;
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mm_tile_tt<RT>(acc, sGm, LDC, ct * 16, sQ, LDK, dt * 16);
+      acc = mm_tile_tb<float, C>(acc, sA, LDC, ct * 16, sK, LDK, dt * 16);
+      acc = mm_tile_tt<C>(acc, sA, LDC, ct * 16, sK, LDK, dt * 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = ct * 16 + 4 * grp + e, d = dt * 16 + col;
+        const float kv = sK[j * LDK + d];
+        const float xh = aXH[u][e], y = aY[u][e];
+        const float dk = acc[e] - sEG[j] * xh + sEL[j] * y;
+        dkn[u][e] = dk;
+        const float gj = sum16(-sEG[j] * kv * xh - sEL[j] * kv * y);
+        const float rd = sum16(kv * dk);
+        glast = fmaf(sEL[j], kv * y, glast);
+        if (col == 0) {
+          atomicAdd(&sDG[j], gj);
+          atomicAdd(&sRD[j], rd);
+        }
+      }
+    }
+  }
+  glast = sum16(glast);
+  glast += __shfl_xor(glast, 16);
+  glast += __shfl_xor(glast, 32);
+  if (lane == 0) atomicAdd(&sDG[C - 1], glast);
+  __syncthreads();
+  // raw-key gradient through k / max(|k|, 1e-6)
+  const float rclamp = 1.f / 1e-6f;
+#pragma unroll
+  for (int u = 0; u < KPW; ++u) {
+    const int tile = wave + 4 * u;
+    if (tile < NKD) {
+      const int ct = tile / NDT, dt = tile % NDT;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = ct * 16 + 4 * grp + e, d = dt * 16 + col;
+        const long long rw = sRow[j];
+        if (rw >= 0) {
+          const float ri = sRinv[j];
+          const float proj = ri < rclamp ? sK[j * LDK + d] * sRD[j] : 0.f;
+          p.dk[rw * DK + d] = ri * (dkn[u][e] - proj);
+        }
+      }
+    }
+  }
+  // dbeta through the clamp; dlog g = reverse cumsum of dG over the chunk
+  if (wave == 0) {
+    const int i = lane;
+    float x = (i < C) ? sDG[i] : 0.f;
+    // suffix sum over lanes i .. C-1
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_down(x, off);
+      if (i + off < 64) x += y;
+    }
+    if (i < C && sRow[i] >= 0) {
+      const long long rw = sRow[i];
+      const float braw = p.beta[rw];
+      p.dbeta[rw] = (braw >= 0.f && braw <= 2.f) ? sDB[i] : 0.f;
+      if (p.g != nullptr && p.dg != nullptr && (rw % p.n_h) == 0) {
+        const long long tk = rw / p.n_h;
+        const float gv = p.g[tk];
+        p.dg[tk] = gv >= FLT_MIN ? x / gv : 0.f;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launch of the four kernels.
+template <typename T, int DK>
+hipError_t launch_bwd_dk(const FwdArgs& fa, const BwdArgs& a, hipStream_t st) {
+  constexpr int C = kBwdChunk, BV = kBwdBV;
+  const long long nchunks = (long long)a.B * a.H * a.nc;
+  if (nchunks > 0) {
+    const int lds = ut_lds_bytes((int)sizeof(T), DK, C, 0);
+    static const bool attr = allow_big_lds(reinterpret_cast<const void*>(&dp_ut_kernel<T, DK, C, float, false>));
+    (void)attr;
+    hipLaunchKernelGGL((dp_ut_kernel<T, DK, C, float, false>), dim3((unsigned)nchunks), dim3(kThreads), lds, st, fa);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((dp_bwd_states_kernel<T, DK, C, BV>), dim3((unsigned)(a.B * a.H * a.nvb)), dim3(256), 0, st, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const unsigned nwg = (unsigned)(a.B * a.H * a.nvb);
+  if (nwg > 0) {
+    if (a.RT == 16)
+      hipLaunchKernelGGL((dp_bwd_dstate_kernel<T, DK, C, BV, 1>), dim3(nwg), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((dp_bwd_dstate_kernel<T, DK, C, BV, 2>), dim3(nwg), dim3(256), 0, st, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (nchunks > 0) {
+    if (a.RT == 16) {
+      static const bool attr = allow_big_lds(reinterpret_cast<const void*>(&dp_bwd_chunk_kernel<T, DK, C, 1>));
+      (void)attr;
+      constexpr int lds = bwd_chunk_lds_bytes<DK, C, 16>();
+      hipLaunchKernelGGL((dp_bwd_chunk_kernel<T, DK, C, 1>), dim3((unsigned)nchunks), dim3(256), lds, st, a);
+    } else {
+      static const bool attr = allow_big_lds(reinterpret_cast<const void*>(&dp_bwd_chunk_kernel<T, DK, C, 2>));
+      (void)attr;
+      constexpr int lds = bwd_chunk_lds_bytes<DK, C, 32>();
+      hipLaunchKernelGGL((dp_bwd_chunk_kernel<T, DK, C, 2>), dim3((unsigned)nchunks), dim3(256), lds, st, a);
+    }
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+}  // namespace dp
+
+#define DP_DEFINE_BWD_LAUNCHER(T, TNAME, DK)                                                     \
+  hipError_t dp_launch_bwd_##TNAME##_##DK(const dp::FwdArgs& fa, const dp::BwdArgs& a, hipStream_t st) { \
+    return dp::launch_bwd_dk<T, DK>(fa, a, st);                                                  \
+  }
+#define DP_DECLARE_BWD_LAUNCHER(TNAME, DK) \
+  hipError_t dp_launch_bwd_##TNAME##_##DK(const dp::FwdArgs& fa, const dp::BwdArgs& a, hipStream_t st);

@@ -147,9 +147,11 @@ __host__ __device__ constexpr int ut_lds_bytes(int elem, int DK, int C, int asym
 
 // ---------------------------------------------------------------------------
 // dp_ut_kernel: per-chunk prep + UT transform.
-template <typename T, int DK, int C>
+// WT is the workspace type of T's output and TB selects T diag(beta) (the
+// forward's operand) or T itself (the backward, which also needs T alone).
+template <typename T, int DK, int C, typename WT = typename OpType<T>::type, bool TB = true>
 __global__ __launch_bounds__(kThreads) void dp_ut_kernel(FwdArgs p) {
-  using OT = typename OpType<T>::type;
+  using OT = WT;
   constexpr int VE = Vec<T>::N;
   constexpr int LDK = DK + VE;  // 16-byte row pad
   constexpr int LDA = C + 4;
@@ -293,7 +295,7 @@ __global__ __launch_bounds__(kThreads) void dp_ut_kernel(FwdArgs p) {
     }
     block_sync_lds();
   }
-  // 6. T diag(beta) -> workspace in the operand type, 8 columns per store
+  // 6. T diag(beta) (or T) -> workspace in the operand type, 8 columns per store
   //    (upper tiles are zero)
   {
     OT* wt = static_cast<OT*>(p.wsT) + chunk * C * C;
@@ -304,7 +306,7 @@ __global__ __launch_bounds__(kThreads) void dp_ut_kernel(FwdArgs p) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int j = j0 + e;
-        f[e] = ((j >> 4) > (i >> 4)) ? 0.f : sTf[i * LDA + j] * sB[j];
+        f[e] = ((j >> 4) > (i >> 4)) ? 0.f : sTf[i * LDA + j] * (TB ? sB[j] : 1.f);
       }
       if constexpr (sizeof(OT) == 2) {
         st_vec16(wt + i * C + j0, f);

@@ -129,6 +129,17 @@ def make(w: Workload, seed: Optional[int] = None) -> dict:
     }
 
 
+def make_grads(w: Workload, seed: Optional[int] = None, final: bool = True) -> dict:
+    """Seeded output gradients for a backward of workload ``w``: ``dout
+    [B,L,H,dv]`` (standard normal, in the workload's dtype) and ``dfinal
+    [B,H,dk,dv]`` (f32, or None when ``final`` is False)."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed((w.seed if seed is None else seed) + 1000)
+    dout = torch.randn(w.B, w.L, w.H, w.dv, generator=gen, dtype=torch.float32)
+    dfinal = torch.randn(w.B, w.H, w.dk, w.dv, generator=gen, dtype=torch.float32) if final else None
+    return {"dout": dout.to(torch_dtype(w.dtype)).contiguous(), "dfinal": dfinal}
+
+
 # ------------------------------------------------------------------ head sampling
 # Heads (b, h) are independent, so a large workload can be checked or timed on
 # a sample of heads.  These helpers only index; they compute nothing.
