@@ -11,8 +11,10 @@ scan first.  Prints ONE JSON line on stdout; diagnostics go to stderr.
 Per-kernel durations come from HIP events recorded on the launch stream
 around every launch inside the timed region.  The CPU baseline is the fp64
 oracle on a bounded sample of heads of the same workload, on this host.  The
-same line also carries a packed variable-length batch (`varlen`) and the
-one-token decode step at batch 1 and 64 (`decode`), each with its own figures.
+same line also carries a packed variable-length batch (`varlen`), the
+one-token decode step at batch 1 and 64 (`decode`), the chunkwise backward on
+the default workload's shape (`bwd`), each with its own figures, and what the
+GPU sustains on a plain copy and a library GEMM (`ceilings`).
 """
 import argparse
 import json
@@ -46,6 +48,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step timing")
     ap.add_argument("--no-varlen", action="store_true", help="skip the packed variable-length timing")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the backward timing")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the copy / GEMM ceiling measurements")
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU sample (0: auto)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run device-to-device copies of BYTES (counter calibration)")
@@ -323,6 +328,78 @@ def time_varlen(steps, warmup, T=65536):
             "value": T / (ms / 1e3), "unit": "tokens/s", "ms_per_step": ms}
 
 
+def time_bwd(w, steps, warmup):
+    """Chunkwise backward (dp_bwd_*) on the forward workload ``w``'s shape:
+    gradients w.r.t. q, k, v, beta (and g, h0) for a seeded output gradient,
+    with inputs, gradients and workspace resident in HBM."""
+    import torch
+
+    import linear_rnn_sequence_amd as dp
+    from linear_rnn_sequence_amd.inputs import make, make_grads
+
+    dev = torch.device("cuda:0")
+    inp = make(w)
+    gr = make_grads(w)
+    d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    dout = gr["dout"].to(dev)
+    dfinal = gr["dfinal"].to(dev)
+    ws = torch.empty(dp.bwd_workspace_size(w.n_h, w.B, w.H, w.L, w.dk, w.dv), dtype=torch.uint8, device=dev)
+    grads = dp.bwd(d["q"], d["k"], d["v"], d["beta"], dout, d["g"], h0=d["h0"], dfinal=dfinal, workspace=ws)
+
+    def step():
+        dp.bwd(d["q"], d["k"], d["v"], d["beta"], dout, d["g"], h0=d["h0"], dfinal=dfinal, workspace=ws,
+               grads=grads)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"workload": f"backward of {describe(w)}; fp32 arithmetic, 32-sub-step chunks",
+            "value": w.B * w.L / (ms / 1e3), "unit": "tokens/s", "ms_per_step": ms,
+            "workspace_bytes": ws.numel()}
+
+
+def measure_ceilings():
+    """What this GPU sustains on plain library work, next to the published
+    peaks: a 1 GiB device-to-device copy (read + write bytes / time) and an
+    8192^3 bf16 GEMM (torch.matmul)."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    out = {}
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(20):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    out["d2d_copy_gbs"] = 2 * src.numel() * 4 * 20 / (e0.elapsed_time(e1) * 1e6)
+    del src, dst
+    n = 8192
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    for _ in range(5):
+        c = a @ b
+    e0.record()
+    for _ in range(20):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    out["bf16_gemm_tflops"] = 2 * n ** 3 * 20 / (e0.elapsed_time(e1) * 1e9)
+    del a, b, c
+    return out
+
+
 # ---------------------------------------------------------------- CPU baseline
 
 def cpu_baseline(w, inp, nheads, min_seconds=10.0, max_pass_seconds=30.0, max_passes=100):
@@ -488,6 +565,10 @@ def main():
         # the pages' decode protocol (batch 1) and a serving-size batch, head shape of c3
         line["decode"] = {"b1": time_decode(1, 16, 3, 128, 128),
                           "b64": time_decode(64, 16, 3, 128, 128)}
+    if not a.no_bwd:
+        line["bwd"] = time_bwd(w, max(5, a.steps // 10), max(3, a.warmup // 10))
+    if not a.no_ceilings:
+        line["ceilings"] = measure_ceilings()
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, r["inputs"], a.cpu_heads)
     else:
