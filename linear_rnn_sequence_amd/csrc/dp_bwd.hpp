@@ -145,6 +145,93 @@ __device__ __forceinline__ void bwd_load_queries(const BwdArgs& p, const long lo
 }
 
 // ---------------------------------------------------------------------------
+// Software pipelining of the two sequential kernels.  While a chunk is
+// computed from LDS, every thread already holds its slice of the next
+// chunk's operands in registers (loaded with the widest aligned loads); after
+// the chunk's last barrier it writes them to LDS.  One thread per C/256 of a
+// sub-step row: thread t covers row t / TPR, elements (t % TPR) * E ..
+
+// E consecutive stored elements of T, read with loads as wide as their
+// alignment allows (E * sizeof(T) bytes, at most 16 at a time).
+template <typename T, int E>
+struct RawSlice {
+  T v[E];
+  __device__ __forceinline__ void load(const T* src) {
+    constexpr int NB = E * (int)sizeof(T);
+    constexpr int AL = NB >= 16 ? 16 : NB;
+    __builtin_memcpy(v, __builtin_assume_aligned(src, AL), NB);
+  }
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] = T{};
+  }
+  __device__ __forceinline__ float operator[](int i) const { return to_f32(v[i]); }
+};
+
+// Row of sub-step s of head (b, h) in the [B, L, H, n_h, *] tensors, or -1 past the end.
+__device__ __forceinline__ long long bwd_row(const BwdArgs& p, int b, int h, int s) {
+  if (s >= p.N) return -1;
+  const int t = fastdiv(s, p.nh_magic, p.nh_shift);
+  return (((long long)b * p.L + t) * p.H + h) * p.n_h + (s - t * p.n_h);
+}
+
+// Readout row rr of chunk c: its token's row in the [B, L, H, *] tensors and
+// its sub-step inside the chunk, or (-1, -1) when the chunk has no such row.
+__device__ __forceinline__ void bwd_readout(const BwdArgs& p, int b, int h, int c, int C, int rr, long long* tok,
+                                            int* loc) {
+  const int s0 = c * C;
+  const int r0 = s0 + (p.n_h - 1 - (s0 - fastdiv(s0, p.nh_magic, p.nh_shift) * p.n_h));
+  const int s = r0 + rr * p.n_h;
+  const bool ok = s < s0 + C && s < p.N;
+  *tok = ok ? ((long long)b * p.L + fastdiv(s, p.nh_magic, p.nh_shift)) * p.H + h : -1;
+  *loc = ok ? s - s0 : -1;
+}
+
+// The operands every sequential kernel needs per chunk: the thread's slice of
+// the unit keys (with 1/|k| of its row), its four entries of T, and for
+// threads t < C the scalars of sub-step t (beta, G, G of the chunk's last).
+template <typename T, int DK, int C>
+struct BwdChunkCommon {
+  static constexpr int TPR = 256 / C;  // threads per sub-step row
+  static constexpr int EK = DK / TPR;  // key elements per thread
+  static_assert(C * C == 4 * 256 && EK >= 1 && DK % TPR == 0, "32-sub-step chunks, 256 threads");
+  RawSlice<T, EK> k;
+  float rinv;  // 1/|k| of the key row (0 past the end)
+  float4 t;    // T entries 4 tid .. 4 tid + 3
+  float beta, g, gl;
+  __device__ __forceinline__ void load(const BwdArgs& p, int b, int h, int c, long long chunk) {
+    const int tid = threadIdx.x;
+    const long long row = bwd_row(p, b, h, c * C + tid / TPR);
+    if (row >= 0) {
+      k.load(static_cast<const T*>(p.k) + row * DK + (tid % TPR) * EK);
+      rinv = p.wsS[chunk * C + tid / TPR].x;
+    } else {
+      k.zero();
+      rinv = 0.f;
+    }
+    t = *reinterpret_cast<const float4*>(p.wsT + chunk * C * C + 4 * tid);
+    if (tid < C) {
+      const long long rs = bwd_row(p, b, h, c * C + tid);
+      beta = rs >= 0 ? clamp_keep_nan(p.beta[rs], 0.f, 2.f) : 0.f;
+      g = p.wsS[chunk * C + tid].y;
+      gl = p.wsS[chunk * C + C - 1].y;
+    }
+  }
+  template <int LDK, int LDC>
+  __device__ __forceinline__ void commit(float* sK, float* sT) const {
+    const int tid = threadIdx.x;
+    float* kd = sK + (tid / TPR) * LDK + (tid % TPR) * EK;
+#pragma unroll
+    for (int i = 0; i < EK; ++i) kd[i] = k[i] * rinv;
+    float* td = sT + ((4 * tid) / C) * LDC + (4 * tid) % C;
+    td[0] = t.x;
+    td[1] = t.y;
+    td[2] = t.z;
+    td[3] = t.w;
+  }
+};
+
+// ---------------------------------------------------------------------------
 // dp_bwd_states_kernel: the forward's chunk-start states, one workgroup per
 // (head, block of BV value columns), sequential over the chunks.  The state
 // lives in LDS (fp32); each wavefront updates the tiles it owns.
@@ -152,9 +239,11 @@ template <typename T, int DK, int C, int BV>
 __global__ __launch_bounds__(256) void dp_bwd_states_kernel(BwdArgs p) {
   constexpr int LDK = DK + 4, LDC = C + 4, LDB = BV + 4;
   constexpr int NCT = C / 16, NDT = DK / 16, NVT = BV / 16;
+  using Common = BwdChunkCommon<T, DK, C>;
+  constexpr int TPR = Common::TPR, EV = BV / TPR;
+  static_assert(EV >= 1 && BV % TPR == 0, "value slice");
   __shared__ float sK[C * LDK], sT[C * LDC], sH[DK * LDB], sXb[C * LDB], sU[C * LDB], sV[C * LDB];
-  __shared__ float sB[C], sEG[C], sEL[C], sRinv[C];
-  __shared__ long long sRow[C];
+  __shared__ float sB[C], sEG[C], sEL[C];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -164,27 +253,37 @@ __global__ __launch_bounds__(256) void dp_bwd_states_kernel(BwdArgs p) {
   const int v0 = vb * BV;
   const T* vp = static_cast<const T*>(p.v);
 
+  // the next chunk's operands, in registers
+  Common nx;
+  RawSlice<T, EV> nv;
+  auto prefetch = [&](int c) {
+    const long long chunk = (long long)bh * p.nc + c;
+    nx.load(p, b, h, c, chunk);
+    const long long row = bwd_row(p, b, h, c * C + tid / TPR);
+    if (row >= 0)
+      nv.load(vp + row * p.dvd + v0 + (tid % TPR) * EV);
+    else
+      nv.zero();
+  };
+
   for (int idx = tid; idx < DK * BV; idx += 256) {
     const int d = idx / BV, n = idx % BV;
     sH[d * LDB + n] = p.h0 != nullptr ? p.h0[((long long)bh * DK + d) * p.dvd + v0 + n] : 0.f;
   }
+  if (p.nc > 0) prefetch(0);
   for (int c = 0; c < p.nc; ++c) {
     const long long chunk = (long long)bh * p.nc + c;
     __syncthreads();  // the previous chunk is done with every buffer
+    nx.template commit<LDK, LDC>(sK, sT);
+    {
+      float* vd = sV + (tid / TPR) * LDB + (tid % TPR) * EV;
+#pragma unroll
+      for (int i = 0; i < EV; ++i) vd[i] = nv[i];
+    }
     if (tid < C) {
-      const int s = c * C + tid;
-      long long row = -1;
-      if (s < p.N) {
-        const int t = fastdiv(s, p.nh_magic, p.nh_shift);
-        row = (((long long)b * p.L + t) * p.H + h) * p.n_h + (s - t * p.n_h);
-      }
-      sRow[tid] = row;
-      const float2 sc = p.wsS[chunk * C + tid];
-      const float gl = p.wsS[chunk * C + C - 1].y;
-      sRinv[tid] = sc.x;
-      sEG[tid] = expf(sc.y);
-      sEL[tid] = expf(gl - sc.y);
-      sB[tid] = row >= 0 ? clamp_keep_nan(p.beta[row], 0.f, 2.f) : 0.f;
+      sB[tid] = nx.beta;
+      sEG[tid] = expf(nx.g);
+      sEL[tid] = expf(nx.gl - nx.g);
     }
     // the state at the chunk start
     float* hdst = p.hs + chunk * DK * p.dvd + v0;
@@ -193,15 +292,7 @@ __global__ __launch_bounds__(256) void dp_bwd_states_kernel(BwdArgs p) {
       hdst[(long long)d * p.dvd + n] = sH[d * LDB + n];
     }
     __syncthreads();
-    bwd_load_keys<T, DK, C, LDK>(p, sRow, sRinv, sK);
-    const float* tsrc = p.wsT + chunk * C * C;
-    for (int idx = tid; idx < C * C; idx += 256) sT[(idx / C) * LDC + idx % C] = tsrc[idx];
-    for (int idx = tid; idx < C * BV; idx += 256) {
-      const int r = idx / BV, n = idx % BV;
-      const long long rw = sRow[r];
-      sV[r * LDB + n] = rw >= 0 ? to_f32(vp[rw * p.dvd + v0 + n]) : 0.f;
-    }
-    __syncthreads();
+    if (c + 1 < p.nc) prefetch(c + 1);  // lands while this chunk is computed
     // beta X = beta (V - diag(e^G) K H0)
     for (int tile = wave; tile < NCT * NVT; tile += 4) {
       const int ct = tile / NVT, nt = tile % NVT;
@@ -250,10 +341,12 @@ __global__ __launch_bounds__(256) void dp_bwd_dstate_kernel(BwdArgs p) {
   constexpr int RT = 16 * NRT;
   constexpr int LDK = DK + 4, LDC = C + 4, LDB = BV + 4;
   constexpr int NCT = C / 16, NDT = DK / 16, NVT = BV / 16;
+  using Common = BwdChunkCommon<T, DK, C>;
+  constexpr int TPQ = 256 / RT, EQ = DK / TPQ, EO = BV / TPQ;  // per readout row
+  static_assert(EQ >= 1 && EO >= 1 && DK % TPQ == 0 && BV % TPQ == 0, "readout slices");
   __shared__ float sK[C * LDK], sQ[RT * LDK], sT[C * LDC], sP[RT * LDC];
   __shared__ float sdH[DK * LDB], sdO[RT * LDB], sdOe[RT * LDB], sdUp[C * LDB], sdX[C * LDB];
-  __shared__ float sB[C], sG[C], sEG[C], sEL[C], sRinv[C];
-  __shared__ long long sRow[C], sTok[RT];
+  __shared__ float sB[C], sG[C], sEG[C], sEL[C];
   __shared__ int sLoc[RT];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -263,23 +356,56 @@ __global__ __launch_bounds__(256) void dp_bwd_dstate_kernel(BwdArgs p) {
   const int b = bh / p.H, h = bh % p.H;
   const int v0 = vb * BV;
   const T* dop = static_cast<const T*>(p.dout);
-  const BwdChunkMeta meta{sRow, sTok, sLoc};
+  const T* qp = static_cast<const T*>(p.q);
+
+  // the next chunk's operands, in registers
+  Common nx;
+  RawSlice<T, EQ> nq;
+  RawSlice<T, EO> no;
+  int nloc;
+  float neg;  // e^{G} at the readout row's sub-step
+  auto prefetch = [&](int c) {
+    const long long chunk = (long long)bh * p.nc + c;
+    nx.load(p, b, h, c, chunk);
+    long long tok;
+    bwd_readout(p, b, h, c, C, tid / TPQ, &tok, &nloc);
+    if (tok >= 0) {
+      nq.load(qp + tok * DK + (tid % TPQ) * EQ);
+      no.load(dop + tok * p.dvd + v0 + (tid % TPQ) * EO);
+      neg = p.wsS[chunk * C + nloc].y;
+    } else {
+      nq.zero();
+      no.zero();
+      neg = 0.f;
+    }
+  };
 
   for (int idx = tid; idx < DK * BV; idx += 256) {
     const int d = idx / BV, n = idx % BV;
     sdH[d * LDB + n] = p.dfinal != nullptr ? p.dfinal[((long long)bh * DK + d) * p.dvd + v0 + n] : 0.f;
   }
+  if (p.nc > 0) prefetch(p.nc - 1);
   for (int c = p.nc - 1; c >= 0; --c) {
     const long long chunk = (long long)bh * p.nc + c;
     __syncthreads();  // the previous chunk is done with every buffer
-    bwd_index_chunk<C>(p, b, h, c, RT, meta);
+    nx.template commit<LDK, LDC>(sK, sT);
+    {
+      const int rr = tid / TPQ, q0 = (tid % TPQ) * EQ, o0 = (tid % TPQ) * EO;
+#pragma unroll
+      for (int i = 0; i < EQ; ++i) sQ[rr * LDK + q0 + i] = nq[i];
+      const float e = nloc >= 0 ? expf(neg) : 0.f;
+#pragma unroll
+      for (int i = 0; i < EO; ++i) {
+        sdO[rr * LDB + o0 + i] = no[i];
+        sdOe[rr * LDB + o0 + i] = e * no[i];
+      }
+      if (tid % TPQ == 0) sLoc[rr] = nloc;
+    }
     if (tid < C) {
-      const float2 sc = p.wsS[chunk * C + tid];
-      const float gl = p.wsS[chunk * C + C - 1].y;
-      sRinv[tid] = sc.x;
-      sG[tid] = sc.y;
-      sEG[tid] = expf(sc.y);
-      sEL[tid] = expf(gl - sc.y);
+      sB[tid] = nx.beta;
+      sG[tid] = nx.g;
+      sEG[tid] = expf(nx.g);
+      sEL[tid] = expf(nx.gl - nx.g);
     }
     // the gradient of the chunk's end state
     float* ddst = p.dhe + chunk * DK * p.dvd + v0;
@@ -288,19 +414,7 @@ __global__ __launch_bounds__(256) void dp_bwd_dstate_kernel(BwdArgs p) {
       ddst[(long long)d * p.dvd + n] = sdH[d * LDB + n];
     }
     __syncthreads();
-    if (tid < C) sB[tid] = sRow[tid] >= 0 ? clamp_keep_nan(p.beta[sRow[tid]], 0.f, 2.f) : 0.f;
-    bwd_load_keys<T, DK, C, LDK>(p, sRow, sRinv, sK);
-    bwd_load_queries<T, DK, LDK>(p, sTok, RT, sQ);
-    const float* tsrc = p.wsT + chunk * C * C;
-    for (int idx = tid; idx < C * C; idx += 256) sT[(idx / C) * LDC + idx % C] = tsrc[idx];
-    for (int idx = tid; idx < RT * BV; idx += 256) {
-      const int r = idx / BV, n = idx % BV;
-      const long long tk = sTok[r];
-      const float x = tk >= 0 ? to_f32(dop[tk * p.dvd + v0 + n]) : 0.f;
-      sdO[r * LDB + n] = x;
-      sdOe[r * LDB + n] = tk >= 0 ? expf(sG[sLoc[r]]) * x : 0.f;
-    }
-    __syncthreads();
+    if (c > 0) prefetch(c - 1);  // lands while this chunk is computed
     // P = masked, gated scores (RT x C)
     for (int tile = wave; tile < NRT * NCT; tile += 4) {
       const int rt = tile / NCT, ct = tile % NCT;
