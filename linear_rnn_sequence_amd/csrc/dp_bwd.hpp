@@ -121,29 +121,6 @@ __device__ __forceinline__ void bwd_index_chunk(const BwdArgs& p, int b, int h, 
   }
 }
 
-// Unit keys of the chunk (fp32, zero past the end) into sK[C][LDK].
-template <typename T, int DK, int C, int LDK>
-__device__ __forceinline__ void bwd_load_keys(const BwdArgs& p, const long long* row, const float* rinv,
-                                              float* sK) {
-  const T* kp = static_cast<const T*>(p.k);
-  for (int idx = threadIdx.x; idx < C * DK; idx += blockDim.x) {
-    const int r = idx / DK, d = idx % DK;
-    const long long rw = row[r];
-    sK[r * LDK + d] = rw >= 0 ? to_f32(kp[rw * DK + d]) * rinv[r] : 0.f;
-  }
-}
-
-// Readout queries of the chunk (zero for empty rows) into sQ[RT][LDK].
-template <typename T, int DK, int LDK>
-__device__ __forceinline__ void bwd_load_queries(const BwdArgs& p, const long long* tok, int RT, float* sQ) {
-  const T* qp = static_cast<const T*>(p.q);
-  for (int idx = threadIdx.x; idx < RT * DK; idx += blockDim.x) {
-    const int r = idx / DK, d = idx % DK;
-    const long long tk = tok[r];
-    sQ[r * LDK + d] = tk >= 0 ? to_f32(qp[tk * DK + d]) : 0.f;
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Software pipelining of the two sequential kernels.  While a chunk is
 // computed from LDS, every thread already holds its slice of the next
@@ -253,37 +230,41 @@ __global__ __launch_bounds__(256) void dp_bwd_states_kernel(BwdArgs p) {
   const int v0 = vb * BV;
   const T* vp = static_cast<const T*>(p.v);
 
-  // the next chunk's operands, in registers
-  Common nx;
-  RawSlice<T, EV> nv;
-  auto prefetch = [&](int c) {
+  // the operands of the next two chunks, in registers (two buffers, used alternately)
+  struct Next {
+    Common x;
+    RawSlice<T, EV> v;
+  };
+  Next nb0, nb1;
+  auto prefetch = [&](Next& nx, int c) {
     const long long chunk = (long long)bh * p.nc + c;
-    nx.load(p, b, h, c, chunk);
+    nx.x.load(p, b, h, c, chunk);
     const long long row = bwd_row(p, b, h, c * C + tid / TPR);
     if (row >= 0)
-      nv.load(vp + row * p.dvd + v0 + (tid % TPR) * EV);
+      nx.v.load(vp + row * p.dvd + v0 + (tid % TPR) * EV);
     else
-      nv.zero();
+      nx.v.zero();
   };
 
   for (int idx = tid; idx < DK * BV; idx += 256) {
     const int d = idx / BV, n = idx % BV;
     sH[d * LDB + n] = p.h0 != nullptr ? p.h0[((long long)bh * DK + d) * p.dvd + v0 + n] : 0.f;
   }
-  if (p.nc > 0) prefetch(0);
-  for (int c = 0; c < p.nc; ++c) {
+  if (p.nc > 0) prefetch(nb0, 0);
+  if (p.nc > 1) prefetch(nb1, 1);
+  auto body = [&](Next& nx, int c) {
     const long long chunk = (long long)bh * p.nc + c;
     __syncthreads();  // the previous chunk is done with every buffer
-    nx.template commit<LDK, LDC>(sK, sT);
+    nx.x.template commit<LDK, LDC>(sK, sT);
     {
       float* vd = sV + (tid / TPR) * LDB + (tid % TPR) * EV;
 #pragma unroll
-      for (int i = 0; i < EV; ++i) vd[i] = nv[i];
+      for (int i = 0; i < EV; ++i) vd[i] = nx.v[i];
     }
     if (tid < C) {
-      sB[tid] = nx.beta;
-      sEG[tid] = expf(nx.g);
-      sEL[tid] = expf(nx.gl - nx.g);
+      sB[tid] = nx.x.beta;
+      sEG[tid] = expf(nx.x.g);
+      sEL[tid] = expf(nx.x.gl - nx.x.g);
     }
     // the state at the chunk start
     float* hdst = p.hs + chunk * DK * p.dvd + v0;
@@ -292,7 +273,7 @@ __global__ __launch_bounds__(256) void dp_bwd_states_kernel(BwdArgs p) {
       hdst[(long long)d * p.dvd + n] = sH[d * LDB + n];
     }
     __syncthreads();
-    if (c + 1 < p.nc) prefetch(c + 1);  // lands while this chunk is computed
+    if (c + 2 < p.nc) prefetch(nx, c + 2);  // lands while the next two chunks are computed
     // beta X = beta (V - diag(e^G) K H0)
     for (int tile = wave; tile < NCT * NVT; tile += 4) {
       const int ct = tile / NVT, nt = tile % NVT;
@@ -328,6 +309,10 @@ __global__ __launch_bounds__(256) void dp_bwd_states_kernel(BwdArgs p) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) sH[(dt * 16 + 4 * grp + e) * LDB + nt * 16 + col] = acc[e];
     }
+  };
+  for (int c = 0; c < p.nc; c += 2) {
+    body(nb0, c);
+    if (c + 1 < p.nc) body(nb1, c + 1);
   }
 }
 
@@ -358,25 +343,28 @@ __global__ __launch_bounds__(256) void dp_bwd_dstate_kernel(BwdArgs p) {
   const T* dop = static_cast<const T*>(p.dout);
   const T* qp = static_cast<const T*>(p.q);
 
-  // the next chunk's operands, in registers
-  Common nx;
-  RawSlice<T, EQ> nq;
-  RawSlice<T, EO> no;
-  int nloc;
-  float neg;  // e^{G} at the readout row's sub-step
-  auto prefetch = [&](int c) {
+  // the operands of the next two chunks, in registers (two buffers, used alternately)
+  struct Next {
+    Common x;
+    RawSlice<T, EQ> q;
+    RawSlice<T, EO> o;
+    int loc;
+    float g;  // G at the readout row's sub-step
+  };
+  Next nb0, nb1;
+  auto prefetch = [&](Next& nx, int c) {
     const long long chunk = (long long)bh * p.nc + c;
-    nx.load(p, b, h, c, chunk);
+    nx.x.load(p, b, h, c, chunk);
     long long tok;
-    bwd_readout(p, b, h, c, C, tid / TPQ, &tok, &nloc);
+    bwd_readout(p, b, h, c, C, tid / TPQ, &tok, &nx.loc);
     if (tok >= 0) {
-      nq.load(qp + tok * DK + (tid % TPQ) * EQ);
-      no.load(dop + tok * p.dvd + v0 + (tid % TPQ) * EO);
-      neg = p.wsS[chunk * C + nloc].y;
+      nx.q.load(qp + tok * DK + (tid % TPQ) * EQ);
+      nx.o.load(dop + tok * p.dvd + v0 + (tid % TPQ) * EO);
+      nx.g = p.wsS[chunk * C + nx.loc].y;
     } else {
-      nq.zero();
-      no.zero();
-      neg = 0.f;
+      nx.q.zero();
+      nx.o.zero();
+      nx.g = 0.f;
     }
   };
 
@@ -384,28 +372,29 @@ __global__ __launch_bounds__(256) void dp_bwd_dstate_kernel(BwdArgs p) {
     const int d = idx / BV, n = idx % BV;
     sdH[d * LDB + n] = p.dfinal != nullptr ? p.dfinal[((long long)bh * DK + d) * p.dvd + v0 + n] : 0.f;
   }
-  if (p.nc > 0) prefetch(p.nc - 1);
-  for (int c = p.nc - 1; c >= 0; --c) {
+  if (p.nc > 0) prefetch(nb0, p.nc - 1);
+  if (p.nc > 1) prefetch(nb1, p.nc - 2);
+  auto body = [&](Next& nx, int c) {
     const long long chunk = (long long)bh * p.nc + c;
     __syncthreads();  // the previous chunk is done with every buffer
-    nx.template commit<LDK, LDC>(sK, sT);
+    nx.x.template commit<LDK, LDC>(sK, sT);
     {
       const int rr = tid / TPQ, q0 = (tid % TPQ) * EQ, o0 = (tid % TPQ) * EO;
 #pragma unroll
-      for (int i = 0; i < EQ; ++i) sQ[rr * LDK + q0 + i] = nq[i];
-      const float e = nloc >= 0 ? expf(neg) : 0.f;
+      for (int i = 0; i < EQ; ++i) sQ[rr * LDK + q0 + i] = nx.q[i];
+      const float e = nx.loc >= 0 ? expf(nx.g) : 0.f;
 #pragma unroll
       for (int i = 0; i < EO; ++i) {
-        sdO[rr * LDB + o0 + i] = no[i];
-        sdOe[rr * LDB + o0 + i] = e * no[i];
+        sdO[rr * LDB + o0 + i] = nx.o[i];
+        sdOe[rr * LDB + o0 + i] = e * nx.o[i];
       }
-      if (tid % TPQ == 0) sLoc[rr] = nloc;
+      if (tid % TPQ == 0) sLoc[rr] = nx.loc;
     }
     if (tid < C) {
-      sB[tid] = nx.beta;
-      sG[tid] = nx.g;
-      sEG[tid] = expf(nx.g);
-      sEL[tid] = expf(nx.gl - nx.g);
+      sB[tid] = nx.x.beta;
+      sG[tid] = nx.x.g;
+      sEG[tid] = expf(nx.x.g);
+      sEL[tid] = expf(nx.x.gl - nx.x.g);
     }
     // the gradient of the chunk's end state
     float* ddst = p.dhe + chunk * DK * p.dvd + v0;
@@ -414,7 +403,7 @@ __global__ __launch_bounds__(256) void dp_bwd_dstate_kernel(BwdArgs p) {
       ddst[(long long)d * p.dvd + n] = sdH[d * LDB + n];
     }
     __syncthreads();
-    if (c > 0) prefetch(c - 1);  // lands while this chunk is computed
+    if (c > 1) prefetch(nx, c - 2);  // lands while the next two chunks are computed
     // P = masked, gated scores (RT x C)
     for (int tile = wave; tile < NRT * NCT; tile += 4) {
       const int rt = tile / NCT, ct = tile % NCT;
@@ -467,6 +456,10 @@ __global__ __launch_bounds__(256) void dp_bwd_dstate_kernel(BwdArgs p) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) sdH[(dt * 16 + 4 * grp + e) * LDB + nt * 16 + col] = acc[e] - acc2[e];
     }
+  };
+  for (int c = p.nc - 1; c >= 0; c -= 2) {
+    body(nb0, c);
+    if (c > 0) body(nb1, c - 1);
   }
   __syncthreads();
   if (p.dh0 != nullptr) {
@@ -553,6 +546,51 @@ __global__ __launch_bounds__(256) void dp_bwd_chunk_kernel(BwdArgs p) {
   const T* vp = static_cast<const T*>(p.v);
   const T* dop = static_cast<const T*>(p.dout);
   const BwdChunkMeta meta{sRow, sTok, sLoc};
+  const float* hsrc = p.hs + chunk * DK * p.dvd;
+  const float* dhsrc = p.dhe + chunk * DK * p.dvd;
+  const float* dusrc = p.dup + chunk * C * p.dvd;
+  // The next value block's operands, in registers: thread t holds EH
+  // consecutive columns of row t / TPH of H0 and dH1, EV of sub-step row
+  // t / TPR of V and dUp, and EO of readout row t / TPQ of dO.
+  constexpr int TPH = 256 / DK, EH = BV / TPH;
+  constexpr int TPR = 256 / C, EV = BV / TPR;
+  constexpr int TPQ = 256 / RT, EO = BV / TPQ;
+  static_assert(EH >= 1 && EV >= 1 && EO >= 1, "block slices");
+  const int hd = tid / TPH, hn = (tid % TPH) * EH;
+  const int vr = tid / TPR, vn = (tid % TPR) * EV;
+  const int orr = tid / TPQ, on = (tid % TPQ) * EO;
+  const long long vrow = bwd_row(p, b, h, c * C + vr);
+  long long otok;
+  int oloc;
+  bwd_readout(p, b, h, c, C, orr, &otok, &oloc);
+  RawSlice<float, EH> nh0, ndh;
+  RawSlice<T, EV> nv;
+  RawSlice<float, EV> ndu;
+  RawSlice<T, EO> ndo;
+  auto prefetch = [&](int vb) {
+    const int v0 = vb * BV;
+    nh0.load(hsrc + (long long)hd * p.dvd + v0 + hn);
+    ndh.load(dhsrc + (long long)hd * p.dvd + v0 + hn);
+    ndu.load(dusrc + (long long)vr * p.dvd + v0 + vn);
+    if (vrow >= 0)
+      nv.load(vp + vrow * p.dvd + v0 + vn);
+    else
+      nv.zero();
+    if (otok >= 0)
+      ndo.load(dop + otok * p.dvd + v0 + on);
+    else
+      ndo.zero();
+  };
+  // the chunk's keys, T and readout queries, then value block 0, all issued up front
+  BwdChunkCommon<T, DK, C> cx;
+  cx.load(p, b, h, c, chunk);
+  constexpr int EQ = DK / TPQ;
+  RawSlice<T, EQ> cq;
+  if (otok >= 0)
+    cq.load(static_cast<const T*>(p.q) + otok * DK + (tid % TPQ) * EQ);
+  else
+    cq.zero();
+  if (p.nvb > 0) prefetch(0);  // lands while the chunk's scores are formed
 
   bwd_index_chunk<C>(p, b, h, c, RT, meta);
   if (tid < C) {
@@ -565,16 +603,13 @@ __global__ __launch_bounds__(256) void dp_bwd_chunk_kernel(BwdArgs p) {
   }
   __syncthreads();
   if (tid < C) {
-    sB[tid] = sRow[tid] >= 0 ? clamp_keep_nan(p.beta[sRow[tid]], 0.f, 2.f) : 0.f;
+    sB[tid] = cx.beta;
     sEG[tid] = expf(sG[tid]);
     sEL[tid] = expf(sG[C - 1] - sG[tid]);
   }
-  bwd_load_keys<T, DK, C, LDK>(p, sRow, sRinv, sK);
-  bwd_load_queries<T, DK, LDK>(p, sTok, RT, sQ);
-  {
-    const float* tsrc = p.wsT + chunk * C * C;
-    for (int idx = tid; idx < C * C; idx += 256) sT[(idx / C) * LDC + idx % C] = tsrc[idx];
-  }
+  cx.template commit<LDK, LDC>(sK, sT);
+#pragma unroll
+  for (int i = 0; i < EQ; ++i) sQ[orr * LDK + (tid % TPQ) * EQ + i] = cq[i];
   __syncthreads();
 
   // S = K K^T (tile `wave`) and Q K^T (tile `wave` when < NRC), kept in registers
@@ -586,36 +621,30 @@ __global__ __launch_bounds__(256) void dp_bwd_chunk_kernel(BwdArgs p) {
 
   f32x4_t aXH[KPW], aY[KPW], aA[QPW];
   f32x4_t aP = {0.f, 0.f, 0.f, 0.f}, aTb = {0.f, 0.f, 0.f, 0.f};
+  static_assert(BV == 16, "16-column value blocks");
 #pragma unroll
   for (int u = 0; u < KPW; ++u) aXH[u] = aY[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int u = 0; u < QPW; ++u) aA[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float hdot = 0.f;
 
-  const float* hsrc = p.hs + chunk * DK * p.dvd;
-  const float* dhsrc = p.dhe + chunk * DK * p.dvd;
-  const float* dusrc = p.dup + chunk * C * p.dvd;
   for (int vb = 0; vb < p.nvb; ++vb) {
     const int v0 = vb * BV;
-    for (int idx = tid; idx < DK * BV; idx += 256) {
-      const int d = idx / BV, n = idx % BV;
-      const float a = hsrc[(long long)d * p.dvd + v0 + n], e = dhsrc[(long long)d * p.dvd + v0 + n];
-      sH0[d * LDB + n] = a;
-      sdHe[d * LDB + n] = e;
-      hdot = fmaf(a, e, hdot);
+#pragma unroll
+    for (int i = 0; i < EH; ++i) {
+      sH0[hd * LDB + hn + i] = nh0[i];
+      sdHe[hd * LDB + hn + i] = ndh[i];
+      hdot = fmaf(nh0[i], ndh[i], hdot);
     }
-    for (int idx = tid; idx < C * BV; idx += 256) {
-      const int r = idx / BV, n = idx % BV;
-      const long long rw = sRow[r];
-      sV[r * LDB + n] = rw >= 0 ? to_f32(vp[rw * p.dvd + v0 + n]) : 0.f;
-      sdUp[r * LDB + n] = dusrc[(long long)r * p.dvd + v0 + n];
+#pragma unroll
+    for (int i = 0; i < EV; ++i) {
+      sV[vr * LDB + vn + i] = nv[i];
+      sdUp[vr * LDB + vn + i] = ndu[i];
     }
-    for (int idx = tid; idx < RT * BV; idx += 256) {
-      const int r = idx / BV, n = idx % BV;
-      const long long tk = sTok[r];
-      sdO[r * LDB + n] = tk >= 0 ? to_f32(dop[tk * p.dvd + v0 + n]) : 0.f;
-    }
+#pragma unroll
+    for (int i = 0; i < EO; ++i) sdO[orr * LDB + on + i] = ndo[i];
     __syncthreads();
+    if (vb + 1 < p.nvb) prefetch(vb + 1);  // lands while this block is computed
     if (wave < NCT) {
       // X = V - diag(e^G) K H0
       const int ct = wave;
