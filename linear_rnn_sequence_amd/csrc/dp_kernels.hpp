@@ -46,6 +46,8 @@
 
 #include <float.h>
 
+#include <type_traits>
+
 #include "dp_device.hpp"
 
 namespace dp {
@@ -1034,93 +1036,157 @@ __global__ __launch_bounds__(64 * (NWC + NWP)) void dp_scan16_kernel(FwdArgs p) 
 // optional APF retention of d (sec. 2.6: d_{t+1} = P[r_t d_t + step]) and the
 // beta-free step of the 1.3B configuration (sec. 2.7: beta taken as 1 in the
 // phase-1 step only).
-// One wavefront holds 4 heads, 16 lanes per head, DK/16 coordinates per lane;
-// each head is a sequential scan over its L tokens.  Tokens are fetched PF at
-// a time, one block ahead of the block being processed.
+// A head's dk coordinates are spread over LPH = min(dk, 64) lanes (dk/LPH
+// each), 64/LPH heads per wavefront; each head is a sequential scan over its
+// L tokens.  Tokens come in blocks of PF, loaded one block ahead.  The part of
+// a token that does not depend on d -- the key norm, the unit key kh,
+// s = kh o kh, its sum and the step factor eta beta / max(sum s, eps) -- runs
+// LAH tokens ahead of the sequential part, which is <d, s> (one head sum),
+// the update of d and the store of the write key d o kh.
+
+// Sum over the LPH lanes of a head (LPH = 16, 32 or 64): within each DPP row
+// (lane ^ 1, lane ^ 2, the mirrored quad, the mirrored half), then across row
+// pairs and halves by permlane swaps.  Every lane of the head ends with the
+// same value.
+template <int LPH>
+__device__ __forceinline__ float head_sum(float x) {
+  static_assert(LPH == 16 || LPH == 32 || LPH == 64, "lanes per head");
+  auto dpp_add = [](float v, auto ctrl) {
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), decltype(ctrl)::value, 0xF, 0xF, true));
+  };
+  x = dpp_add(x, std::integral_constant<int, 0xB1>{});   // quad_perm [1, 0, 3, 2]
+  x = dpp_add(x, std::integral_constant<int, 0x4E>{});   // quad_perm [2, 3, 0, 1]
+  x = dpp_add(x, std::integral_constant<int, 0x141>{});  // row_half_mirror
+  x = dpp_add(x, std::integral_constant<int, 0x140>{});  // row_mirror
+  if constexpr (LPH >= 32) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  if constexpr (LPH == 64) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  return x;
+}
+
+// clamp to [lo, hi]; NaN stays NaN
+__device__ __forceinline__ float med3_keep_nan(float x, float lo, float hi) {
+  return x != x ? x : __builtin_amdgcn_fmed3f(x, lo, hi);
+}
+
 template <typename T, int DK>
 __global__ __launch_bounds__(64) void dp_precond_kernel(PrecondArgs p) {
-  constexpr int EPL = DK / 16;  // coordinates per lane
-  constexpr int PF = 8;         // tokens per prefetch block
+  constexpr int LPH = DK < 64 ? DK : 64;  // lanes per head
+  constexpr int EPL = DK / LPH;           // coordinates per lane (1 or 2)
+  constexpr int HPW = 64 / LPH;           // heads per wavefront
+  constexpr int PF = 32;                  // tokens per block
+  constexpr int LAH = 3, NSL = LAH + 1;   // look-ahead of the d-independent part
+  static_assert(EPL == 1 || EPL == 2, "coordinates per lane");
   const int lane = threadIdx.x & 63;
-  const int sl = lane & 15;
+  const int sl = lane % LPH;
   const long long nbh = (long long)p.B * p.H;
-  const long long bh_raw = (long long)blockIdx.x * 4 + (lane >> 4);
+  const long long bh_raw = (long long)blockIdx.x * HPW + lane / LPH;
   const bool active = bh_raw < nbh;
   const long long bh = active ? bh_raw : 0;
   const int b = (int)(bh / p.H), h = (int)(bh % p.H);
-  const T* kp = static_cast<const T*>(p.k);
-  T* ktp = static_cast<T*>(p.kt);
+  // token t of this head: row ((b L + t) H + h) of the token-major tensors
+  const long long row0 = (long long)b * p.L * p.H + h;
+  const T* kp = static_cast<const T*>(p.k) + row0 * DK + sl * EPL;
+  T* ktp = static_cast<T*>(p.kt) + row0 * DK + sl * EPL;
+  const float* bp = p.beta + row0;
+  const float* rp = p.ret != nullptr ? p.ret + row0 : nullptr;
+  const long long kstride = (long long)p.H * DK;
 
   float d[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) d[e] = p.d[bh * DK + sl * EPL + e];
 
-  auto tok_of = [&](int t) { return ((long long)b * p.L + t) * p.H + h; };
-  auto load_tok = [&](int t, float* kv, float& bv, float& rv) {
-    if (t < p.L) {
-      const long long tok = tok_of(t);
-      const T* src = kp + tok * DK + sl * EPL;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) kv[e] = to_f32(src[e]);
-      bv = p.beta[tok];
-      rv = p.ret != nullptr ? p.ret[tok] : 1.f;
-    } else {
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) kv[e] = 0.f;
-      bv = 0.f;
-      rv = 1.f;
-    }
+  // raw key slice, beta and retention of the tokens of one block
+  struct Raw {
+    T k[PF][EPL];
+    float beta[PF], ret[PF];
   };
-
-  float kc[PF][EPL], bc[PF], rc[PF];
-#pragma unroll
-  for (int i = 0; i < PF; ++i) load_tok(i, kc[i], bc[i], rc[i]);
-
-  for (int t0 = 0; t0 < p.L; t0 += PF) {
-    float kn[PF][EPL], bn[PF], rn[PF];
-#pragma unroll
-    for (int i = 0; i < PF; ++i) load_tok(t0 + PF + i, kn[i], bn[i], rn[i]);
+  auto load_block = [&](int t0, Raw& r) {
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
       const int t = t0 + i;
       if (t < p.L) {
-        float n2 = 0.f;
+        __builtin_memcpy(r.k[i], __builtin_assume_aligned(kp + t * kstride, EPL * sizeof(T)), EPL * sizeof(T));
+        r.beta[i] = bp[(long long)t * p.H];
+        r.ret[i] = rp != nullptr ? rp[(long long)t * p.H] : 1.f;
+      } else {
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) n2 = fmaf(kc[i][e], kc[i][e], n2);
-        n2 = group_sum<16>(n2);
-        const float r = 1.f / fmaxf(sqrtf(n2), 1e-6f);
-        float kh[EPL], s[EPL];
-        float ds = 0.f, ns = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          kh[e] = kc[i][e] * r;
-          s[e] = kh[e] * kh[e];
-          ds = fmaf(d[e], s[e], ds);
-          ns += s[e];
-        }
-        // emit the write key with the current d_t
-        if (active) {
-          T* dst = ktp + tok_of(t) * DK + sl * EPL;
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) dst[e] = from_f32<T>(d[e] * kh[e]);
-        }
-        ds = group_sum<16>(ds);
-        ns = group_sum<16>(ns);
-        const float bt = p.beta_aware ? clamp_keep_nan(bc[i], 0.f, 2.f) : 1.f;
-        const float a = bt * ds;
-        const float coef = p.eta * bt * (1.f - a) / fmaxf(ns, p.eps);
-        // retention scales d_t (exactly 1 without the gate), the step uses d_t
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) d[e] = clamp_keep_nan(fmaf(coef, s[e], rc[i] * d[e]), p.dmin, p.dmax);
+        for (int e = 0; e < EPL; ++e) r.k[i][e] = T{};
+        r.beta[i] = 0.f;
+        r.ret[i] = 1.f;
       }
     }
+  };
+  // write key d o kh of token t (EPL values, stored together)
+  auto store_kt = [&](int t, const float* kh) {
+    T o[EPL];
+    if constexpr (sizeof(T) == 2 && EPL == 2) {
+      const bf16x2_t v = __builtin_convertvector(f32x2_t{d[0] * kh[0], d[1] * kh[1]}, bf16x2_t);
+      __builtin_memcpy(o, &v, 4);
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[e] = from_f32<T>(d[e] * kh[e]);
+    }
+    __builtin_memcpy(__builtin_assume_aligned(ktp + t * kstride, EPL * sizeof(T)), o, EPL * sizeof(T));
+  };
+
+  Raw cur, nxt;
+  // FULL: every token of the block is below L (no per-token checks)
+  auto run_block = [&](auto fullc, int t0) {
+    constexpr bool FULL = decltype(fullc)::value;
+    float kh[NSL][EPL], s[NSL][EPL], w[NSL], bt[NSL];
+    auto prep_tok = [&](int i) {
+      const int q = i % NSL;
+      float n2 = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) n2 = fmaf(to_f32(cur.k[i][e]), to_f32(cur.k[i][e]), n2);
+      n2 = head_sum<LPH>(n2);
+      const float r = __builtin_amdgcn_rsqf(fmaxf(n2, 1e-12f));  // 1 / max(|k|, 1e-6)
+      float ns = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        kh[q][e] = to_f32(cur.k[i][e]) * r;
+        s[q][e] = kh[q][e] * kh[q][e];
+        ns += s[q][e];
+      }
+      ns = head_sum<LPH>(ns);
+      bt[q] = p.beta_aware ? clamp_keep_nan(cur.beta[i], 0.f, 2.f) : 1.f;
+      w[q] = p.eta * bt[q] * __builtin_amdgcn_rcpf(fmaxf(ns, p.eps));
+    };
+#pragma unroll
+    for (int i = 0; i < LAH; ++i) prep_tok(i);
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
-      bc[i] = bn[i];
-      rc[i] = rn[i];
+      if (i + LAH < PF) prep_tok(i + LAH);
+      const int q = i % NSL;
+      const int t = t0 + i;
+      if (FULL || t < p.L) {
+        float ds = 0.f;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) kc[i][e] = kn[i][e];
+        for (int e = 0; e < EPL; ++e) ds = fmaf(d[e], s[q][e], ds);
+        ds = head_sum<LPH>(ds);
+        // emit the write key with the current d_t
+        if (active) store_kt(t, kh[q]);
+        const float coef = w[q] * (1.f - bt[q] * ds);
+        // retention scales d_t (exactly 1 without the gate), the step uses d_t
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) d[e] = med3_keep_nan(fmaf(coef, s[q][e], cur.ret[i] * d[e]), p.dmin, p.dmax);
+      }
     }
+  };
+  load_block(0, cur);
+  for (int t0 = 0; t0 < p.L; t0 += PF) {
+    if (t0 + PF < p.L) load_block(t0 + PF, nxt);
+    if (t0 + PF <= p.L)
+      run_block(std::true_type{}, t0);
+    else
+      run_block(std::false_type{}, t0);
+    cur = nxt;
   }
   if (active) {
 #pragma unroll
@@ -1363,7 +1429,8 @@ hipError_t launch_fwd_dk(const FwdArgs& a, int C, int BV, int lds_scan, int stag
 template <typename T, int DK>
 hipError_t launch_precond_dk(const PrecondArgs& a, hipStream_t st) {
   const long long nbh = (long long)a.B * a.H;
-  const unsigned blocks = (unsigned)((nbh + 3) / 4);
+  constexpr int HPW = 64 / (DK < 64 ? DK : 64);  // heads per wavefront
+  const unsigned blocks = (unsigned)((nbh + HPW - 1) / HPW);
   hipLaunchKernelGGL((dp_precond_kernel<T, DK>), dim3(blocks), dim3(64), 0, st, a);
   return hipGetLastError();
 }
