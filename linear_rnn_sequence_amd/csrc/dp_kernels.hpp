@@ -1101,6 +1101,116 @@ __global__ __launch_bounds__(64) void dp_precond_kernel(PrecondArgs p) {
 #pragma unroll
   for (int e = 0; e < EPL; ++e) d[e] = p.d[bh * DK + sl * EPL + e];
 
+  // write key d o kh of token t (EPL values, stored together)
+  auto store_kt = [&](int t, const float* kh) {
+    T o[EPL];
+    if constexpr (sizeof(T) == 2 && EPL == 2) {
+      const bf16x2_t v = __builtin_convertvector(f32x2_t{d[0] * kh[0], d[1] * kh[1]}, bf16x2_t);
+      __builtin_memcpy(o, &v, 4);
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[e] = from_f32<T>(d[e] * kh[e]);
+    }
+    __builtin_memcpy(__builtin_assume_aligned(ktp + t * kstride, EPL * sizeof(T)), o, EPL * sizeof(T));
+  };
+
+  if constexpr (LPH == 64) {
+    // One head per wavefront.  Lane j also owns token t0 + j of the block: it
+    // loads that token's whole key row, beta and retention one block ahead
+    // and forms the token's scalars (1/max(|k|, 1e-6), the step factor, the
+    // clamped beta); the sequential part reads them with v_readlane.
+    constexpr int PB = sizeof(T) == 2 ? 64 : 32;  // tokens per block
+    constexpr int RB = DK * (int)sizeof(T);       // bytes per key row
+    static_assert(RB % 16 == 0, "key rows in 16-byte pieces");
+    const T* krow = static_cast<const T*>(p.k) + row0 * DK;
+    uint4 rowraw[RB / 16];
+    float bnx = 0.f, rnx = 1.f;
+    auto load_rows = [&](int t0) {
+      const int t = t0 + lane;
+      if (lane < PB && t < p.L) {
+        const uint4* src = reinterpret_cast<const uint4*>(krow + t * kstride);
+#pragma unroll
+        for (int q = 0; q < RB / 16; ++q) rowraw[q] = src[q];
+        bnx = bp[(long long)t * p.H];
+        rnx = rp != nullptr ? rp[(long long)t * p.H] : 1.f;
+      } else {
+#pragma unroll
+        for (int q = 0; q < RB / 16; ++q) rowraw[q] = uint4{0u, 0u, 0u, 0u};
+        bnx = 0.f;
+        rnx = 1.f;
+      }
+    };
+    T sc[PB][EPL], sn[PB][EPL];  // this lane's coordinates of every token, current and next block
+    auto load_slices = [&](int t0, T (&sv)[PB][EPL]) {
+#pragma unroll
+      for (int i = 0; i < PB; ++i) {
+        if (t0 + i < p.L)
+          __builtin_memcpy(sv[i], __builtin_assume_aligned(kp + (t0 + i) * kstride, EPL * sizeof(T)), EPL * sizeof(T));
+        else
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) sv[i][e] = T{};
+      }
+    };
+    float rv, wv, btv, rtv;  // this lane's token scalars (current block)
+    auto token_scalars = [&]() {
+      const T* kv = reinterpret_cast<const T*>(rowraw);
+      float n4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < DK; ++e) n4[e & 3] = fmaf(to_f32(kv[e]), to_f32(kv[e]), n4[e & 3]);
+      const float n2 = (n4[0] + n4[1]) + (n4[2] + n4[3]);
+      rv = __builtin_amdgcn_rsqf(fmaxf(n2, 1e-12f));  // 1 / max(|k|, 1e-6)
+      const float ns = n2 * rv * rv;                  // |kh|^2
+      btv = p.beta_aware ? clamp_keep_nan(bnx, 0.f, 2.f) : 1.f;
+      wv = p.eta * btv * __builtin_amdgcn_rcpf(fmaxf(ns, p.eps));
+      rtv = rnx;
+    };
+    auto lane_val = [](float x, int i) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), i)); };
+    auto run_block = [&](auto fullc, int t0) {
+      constexpr bool FULL = decltype(fullc)::value;
+#pragma unroll
+      for (int i = 0; i < PB; ++i) {
+        const int t = t0 + i;
+        if (FULL || t < p.L) {
+          const float r = lane_val(rv, i), w = lane_val(wv, i), bt = lane_val(btv, i), rt = lane_val(rtv, i);
+          float kh[EPL], sq[EPL], ds = 0.f;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) {
+            kh[e] = to_f32(sc[i][e]) * r;
+            sq[e] = kh[e] * kh[e];
+            ds = fmaf(d[e], sq[e], ds);
+          }
+          ds = head_sum<LPH>(ds);
+          if (active) store_kt(t, kh);
+          const float coef = w * (1.f - bt * ds);
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) d[e] = med3_keep_nan(fmaf(coef, sq[e], rt * d[e]), p.dmin, p.dmax);
+        }
+      }
+    };
+    load_rows(0);
+    load_slices(0, sc);
+    for (int t0 = 0; t0 < p.L; t0 += PB) {
+      token_scalars();
+      if (t0 + PB < p.L) {
+        load_rows(t0 + PB);
+        load_slices(t0 + PB, sn);
+      }
+      if (t0 + PB <= p.L)
+        run_block(std::true_type{}, t0);
+      else
+        run_block(std::false_type{}, t0);
+#pragma unroll
+      for (int i = 0; i < PB; ++i)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) sc[i][e] = sn[i][e];
+    }
+    if (active) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) p.d[bh * DK + sl * EPL + e] = d[e];
+    }
+    return;
+  }
+
   // raw key slice, beta and retention of the tokens of one block
   struct Raw {
     T k[PF][EPL];
@@ -1122,19 +1232,6 @@ __global__ __launch_bounds__(64) void dp_precond_kernel(PrecondArgs p) {
       }
     }
   };
-  // write key d o kh of token t (EPL values, stored together)
-  auto store_kt = [&](int t, const float* kh) {
-    T o[EPL];
-    if constexpr (sizeof(T) == 2 && EPL == 2) {
-      const bf16x2_t v = __builtin_convertvector(f32x2_t{d[0] * kh[0], d[1] * kh[1]}, bf16x2_t);
-      __builtin_memcpy(o, &v, 4);
-    } else {
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) o[e] = from_f32<T>(d[e] * kh[e]);
-    }
-    __builtin_memcpy(__builtin_assume_aligned(ktp + t * kstride, EPL * sizeof(T)), o, EPL * sizeof(T));
-  };
-
   Raw cur, nxt;
   // FULL: every token of the block is below L (no per-token checks)
   auto run_block = [&](auto fullc, int t0) {
