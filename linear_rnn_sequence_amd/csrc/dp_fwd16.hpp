@@ -621,7 +621,12 @@ void dp_chain_kernel(FwdArgs p) {
   constexpr bool EARLY = chain_early(DK, C, STG);
   constexpr int VB = C * BV * 2;                      // value tile bytes
   constexpr int STAGE = W.bytes + VB;
-  constexpr int NIB = (W.bytes + 1023) / 1024;        // copies per chunk block
+  // Bytes of each block the scan reads: the ungated pipelined body needs none
+  // of the per-chunk scalars at the block's end (its decay factors are all 1
+  // and it bounds the readout rows itself), so its copies stop before them.
+  constexpr bool PIPE = DK % 32 == 0 && C % 32 == 0;
+  constexpr int CB = (PIPE && !GATED) ? W.oS : W.bytes;
+  constexpr int NIB = (CB + 1023) / 1024;             // copies per chunk block
   constexpr int NIV = VB / 1024 > 0 ? VB / 1024 : 1;  // copies per value tile
   constexpr int VPI = VB >= 1024 ? 64 : VB / 16;      // lanes per value copy
   constexpr int NI = NIB + NIV;
@@ -688,7 +693,7 @@ void dp_chain_kernel(FwdArgs p) {
       static_for<NIB>([&](auto mc) {
         constexpr int m = decltype(mc)::value;
         if constexpr (m % NCW == CW) {
-          if (1024 * m + 16 * lane < W.bytes) dma16(src + soff[m], st + 1024 * m);
+          if (1024 * m + 16 * lane < CB) dma16(src + soff[m], st + 1024 * m);
         }
       });
       // value tile: logical block q = columns v0 + 8q.., rows = sub-steps
@@ -831,7 +836,9 @@ void dp_chain_kernel(FwdArgs p) {
         }
       }
 #pragma unroll
-      for (int it = 0; it < NRT; ++it) egl[it] = *reinterpret_cast<const f32x4_t*>(sEGL + it * 16 + 4 * grp);
+      for (int it = 0; it < NRT; ++it) {
+        if constexpr (GATED) egl[it] = *reinterpret_cast<const f32x4_t*>(sEGL + it * 16 + 4 * grp);
+      }
       if constexpr (GATED) dec = sEG[C - 1];
     };
     // key fragment k (< LA) of the chunk whose key tiles start at ok / ok1
@@ -972,7 +979,7 @@ void dp_chain_kernel(FwdArgs p) {
         } else if constexpr (k < S2) {
           if constexpr (step_k(k - S1, NRT) == KST - 1) {
             constexpr int it = step_tile(k - S1, NRT);
-            z[it] = z[it] * egl[it];
+            if constexpr (GATED) z[it] = z[it] * egl[it];  // e^{G_loc} = 1 without a gate
           }
         } else if constexpr (k < S3) {
           if constexpr (step_k(k - S2, NCT) == CST - 1) {
