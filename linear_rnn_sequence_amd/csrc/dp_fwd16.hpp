@@ -660,6 +660,11 @@ void dp_chain_kernel(FwdArgs p) {
     // fragment-layout tiles and the scalars are copied as they are.
     const int cw = wave - NWC;
     int soff[NIB];
+    // Readout rows past ceil(C / n_h), the most any chunk has, are padding in
+    // the Q and P tiles: their lanes copy nothing (the LDS rows keep whatever
+    // they held; they only ever feed output rows that are never stored).
+    const int rmax = (C + p.n_h - 1) / p.n_h;
+    bool keep[NIB];
 #pragma unroll
     for (int m = 0; m < NIB; ++m) {
       const int o = 1024 * m + 16 * lane;
@@ -681,6 +686,10 @@ void dp_chain_kernel(FwdArgs p) {
       region(W.oQ, RT, DK);
       region(W.oP, RT, C);
       soff[m] = src;
+      keep[m] = true;
+      // (fragment-layout tiles are copied as they are: LDS row = tile row)
+      if (frag_layout(DK) && o >= W.oQ && o < W.oQ + RT * DK * 2 && ((o - W.oQ) / 16) % RT >= rmax) keep[m] = false;
+      if (frag_layout(C) && o >= W.oP && o < W.oP + RT * C * 2 && ((o - W.oP) / 16) % RT >= rmax) keep[m] = false;
     }
     const bf16_t* vp = static_cast<const bf16_t*>(p.v) + v0;
     const long long tok0 = sg.tok * p.H + h;
@@ -693,7 +702,7 @@ void dp_chain_kernel(FwdArgs p) {
       static_for<NIB>([&](auto mc) {
         constexpr int m = decltype(mc)::value;
         if constexpr (m % NCW == CW) {
-          if (1024 * m + 16 * lane < CB) dma16(src + soff[m], st + 1024 * m);
+          if (1024 * m + 16 * lane < CB && keep[m]) dma16(src + soff[m], st + 1024 * m);
         }
       });
       // value tile: logical block q = columns v0 + 8q.., rows = sub-steps
