@@ -314,7 +314,8 @@ def test_errors_surface_as_exceptions():
 
 # ------------------------------------------------------------------ phase 1 alone
 
-@pytest.mark.parametrize("dtype,dk", [("f32", 16), ("bf16", 64), ("bf16", 128), ("f32", 128)])
+@pytest.mark.parametrize("dtype,dk", [("f32", 16), ("bf16", 32), ("f32", 32), ("bf16", 64), ("bf16", 128),
+                                      ("f32", 128)])
 def test_precond_parity(dtype, dk):
     w = WORKLOADS["c5"].scaled(B=2, H=5, L=301, dk=dk, dv=dk, dtype=dtype)
     inp = make(w)
@@ -326,3 +327,21 @@ def test_precond_parity(dtype, dk):
     kto, do = oracle.precond(k1, b1, eta=0.05)
     check(dict(kt=(f64(ktg), kto), d=(f64(dg), do)), TOL[dtype], "precond")
     assert float(dg.min()) >= 0.5 and float(dg.max()) <= 2.0
+
+
+# the scan works in blocks of 64 tokens (bf16) or 32 (fp32) at dk >= 64 and in
+# blocks of 16 / 8 with 16 or 32 lanes per head below: sequences shorter than,
+# equal to and one past a block, and an odd number of heads per wavefront
+@pytest.mark.parametrize("dtype,dk,B,H,L", [("bf16", 128, 1, 3, 1), ("bf16", 128, 2, 1, 7), ("bf16", 128, 1, 2, 64),
+                                            ("bf16", 128, 1, 2, 65), ("f32", 128, 1, 2, 33), ("f32", 64, 3, 1, 32),
+                                            ("bf16", 32, 1, 3, 17), ("f32", 16, 1, 5, 9), ("bf16", 16, 2, 3, 16)])
+def test_precond_block_edges(dtype, dk, B, H, L):
+    w = WORKLOADS["c5"].scaled(B=B, H=H, L=L, dk=dk, dv=dk, dtype=dtype)
+    inp = make(w)
+    k1 = inp["k"][:, :, :, 0, :].contiguous()
+    b1 = inp["beta"][..., 0].contiguous()
+    say(f"case precond edges {dtype} dk={dk} B={B} H={H} L={L}")
+    ktg, dg = dp.osdn_precond(k1.cuda(), b1.cuda(), eta=0.05)
+    torch.cuda.synchronize()
+    kto, do = oracle.precond(k1, b1, eta=0.05)
+    check(dict(kt=(f64(ktg), kto), d=(f64(dg), do)), TOL[dtype], "precond edges")
