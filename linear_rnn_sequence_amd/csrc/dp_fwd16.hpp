@@ -211,6 +211,48 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void d
     if (p.g != nullptr && j == 0) lam = logf(fmaxf(p.g[tok], FLT_MIN));
   }
 
+  // queries: loaded with the keys (one memory round trip per chunk) when
+  // their fragments fit the registers (up to two row tiles), else once the
+  // key rows are in LDS (fewer registers live at once).
+  // QREG: the fragment (row 16 it + n, step t) of lane (n, g) -- columns
+  // 32 t + 4 g .. + 3 and 32 t + 16 + 4 g .. + 3 -- as raw bf16
+  constexpr bool QEARLY = NRT <= 2;
+  u32x4_t qr[QREG ? NRT : 1][QREG ? QKS : 1];
+  auto load_queries = [&]() {
+    if constexpr (QREG) {
+#pragma unroll
+      for (int it = 0; it < NRT; ++it) {
+        const int i = it * 16 + (lane & 15);
+        const int s = r0 + i * n_h;
+        const bool ok = s < s0 + C && s < N;
+        const long long tk = tok0 + (long long)fastdiv(ok ? s : s0, p.nh_magic, p.nh_shift) * p.H;
+#pragma unroll
+        for (int t = 0; t < QKS; ++t) {
+          qr[it][t] = u32x4_t{0u, 0u, 0u, 0u};
+          if (ok) {
+            const bf16_t* src = qp + tk * DK + 32 * t + 4 * (lane >> 4);
+            const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(src);
+            const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(src + 16);
+            qr[it][t] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int it = 0; it < QIT; ++it) {
+        const int idx = tid + it * 256;
+        const int i = idx / TPR, cg = idx % TPR;
+        const int s = r0 + i * n_h;
+        rq[it] = u32x4_t{0u, 0u, 0u, 0u};
+        if (idx < QV && s < s0 + C && s < N) {
+          const long long tk = tok0 + (long long)fastdiv(s, p.nh_magic, p.nh_shift) * p.H;
+          rq[it] = ld16(qp + tk * DK + cg * 8);
+        }
+      }
+    }
+  };
+  if constexpr (QEARLY) load_queries();
+
   // 2. unit keys (row norms by a TPR-lane reduction) and queries, as fp16 rows
 #pragma unroll
   for (int it = 0; it < KIT; ++it) {
@@ -227,41 +269,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void d
     for (int e = 0; e < 8; ++e) f[e] *= rinv;
     if (idx < KV) st_vec16(sK + r * LDK + cg * 8, f);
   }
-  // queries, loaded once the key rows are in LDS (fewer registers live at once).
-  // QREG: the fragment (row 16 it + n, step t) of lane (n, g) -- columns
-  // 32 t + 4 g .. + 3 and 32 t + 16 + 4 g .. + 3 -- as raw bf16
-  u32x4_t qr[QREG ? NRT : 1][QREG ? QKS : 1];
-  if constexpr (QREG) {
-#pragma unroll
-    for (int it = 0; it < NRT; ++it) {
-      const int i = it * 16 + (lane & 15);
-      const int s = r0 + i * n_h;
-      const bool ok = s < s0 + C && s < N;
-      const long long tk = tok0 + (long long)fastdiv(ok ? s : s0, p.nh_magic, p.nh_shift) * p.H;
-#pragma unroll
-      for (int t = 0; t < QKS; ++t) {
-        qr[it][t] = u32x4_t{0u, 0u, 0u, 0u};
-        if (ok) {
-          const bf16_t* src = qp + tk * DK + 32 * t + 4 * (lane >> 4);
-          const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(src);
-          const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(src + 16);
-          qr[it][t] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-        }
-      }
-    }
-  } else {
-#pragma unroll
-    for (int it = 0; it < QIT; ++it) {
-      const int idx = tid + it * 256;
-      const int i = idx / TPR, cg = idx % TPR;
-      const int s = r0 + i * n_h;
-      rq[it] = u32x4_t{0u, 0u, 0u, 0u};
-      if (idx < QV && s < s0 + C && s < N) {
-        const long long tk = tok0 + (long long)fastdiv(s, p.nh_magic, p.nh_shift) * p.H;
-        rq[it] = ld16(qp + tk * DK + cg * 8);
-      }
-    }
-  }
+  if constexpr (!QEARLY) load_queries();
   f16x8_t qf[QREG ? NRT : 1][QREG ? QKS : 1];  // QREG: fp16 query fragments
   if constexpr (QREG) {
 #pragma unroll
