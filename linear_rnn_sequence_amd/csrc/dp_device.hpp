@@ -8,6 +8,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace dp {
 
 using bf16_t = uint16_t;  // bfloat16 storage (raw bits)
@@ -360,6 +362,22 @@ template <int W>
 __device__ __forceinline__ float group_sum(float x) {
 #pragma unroll
   for (int m = W / 2; m >= 1; m >>= 1) x += __shfl_xor(x, m, W);
+  return x;
+}
+
+// Sum over aligned groups of W consecutive lanes (W = 2, 4, 8 or 16: inside
+// one DPP row) by DPP: lane ^ 1, lane ^ 2, the mirrored quad, the mirrored
+// half.  Every lane of a group ends with the same value.
+template <int W>
+__device__ __forceinline__ float dpp_group_sum(float x) {
+  static_assert(W == 2 || W == 4 || W == 8 || W == 16, "group within a DPP row");
+  auto add = [](float v, auto ctrl) {
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), decltype(ctrl)::value, 0xF, 0xF, true));
+  };
+  x = add(x, std::integral_constant<int, 0xB1>{});                     // quad_perm [1, 0, 3, 2]
+  if constexpr (W >= 4) x = add(x, std::integral_constant<int, 0x4E>{});   // quad_perm [2, 3, 0, 1]
+  if constexpr (W >= 8) x = add(x, std::integral_constant<int, 0x141>{});  // row_half_mirror
+  if constexpr (W >= 16) x = add(x, std::integral_constant<int, 0x140>{}); // row_mirror
   return x;
 }
 

@@ -263,7 +263,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void d
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss = fmaf(f[e], f[e], ss);
-    ss = group_sum<TPR>(ss);
+    ss = dpp_group_sum<TPR>(ss);
     const float rinv = 1.f / fmaxf(sqrtf(ss), 1e-6f);
 #pragma unroll
     for (int e = 0; e < 8; ++e) f[e] *= rinv;
@@ -294,7 +294,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void d
 
   // 3. beta range, cumulative log-gate and the per-chunk scalars (wave 0)
   if (wave == 0) {
-    const float G = wave_inclusive_scan(lam);
+    const float G = p.g != nullptr ? wave_inclusive_scan(lam) : 0.f;  // no gate: all zero
     const float Gl = __shfl(G, C - 1, 64);
     float* sEG = reinterpret_cast<float*>(wsc + W.oS + W.oEG);
     float* sEL = reinterpret_cast<float*>(wsc + W.oS + W.oEL);
