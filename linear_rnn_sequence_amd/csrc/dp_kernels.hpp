@@ -222,12 +222,15 @@ __global__ __launch_bounds__(kThreads) void dp_ut_kernel(FwdArgs p) {
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < VE; ++e) ss = fmaf(f[e], f[e], ss);
-    ss = group_sum<TPR>(ss);
+    if constexpr (TPR <= 16)
+      ss = dpp_group_sum<TPR>(ss);  // inside one DPP row
+    else
+      ss = group_sum<TPR>(ss);
     if (idx < KV && cg == 0) sR[r] = (s0 + r < p.N) ? 1.f / fmaxf(sqrtf(ss), 1e-6f) : 0.f;
   }
   // 3. beta range and chunk-local cumulative log-gate (C <= 64: wave 0)
   if (wave == 0) {
-    const float G = wave_inclusive_scan(lam);
+    const float G = p.g != nullptr ? wave_inclusive_scan(lam) : 0.f;  // no gate: all zero
     if (lane < C) {
       sB[lane] = clamp_keep_nan(braw, 0.f, 2.f);
       sG[lane] = G;
