@@ -64,6 +64,7 @@ SMALL = [
     ("c3b", dict(B=1, H=2, L=161)),
     ("c4", dict(B=2, H=2, L=300)),
     ("c5", dict(B=2, H=3, L=257)),
+    ("c4", dict(B=1, H=2, L=130, n_h=3)),  # gated, h0, 22 readout rows of 32 per chunk
 ]
 
 
@@ -268,6 +269,8 @@ EDGE = [
     dict(B=2, H=1, L=29, n_h=5, dk=32, dv=64, chunk=64),     # n_h = 5: 13 readouts / chunk
     dict(B=1, H=2, L=9, n_h=17, dk=16, dv=32, chunk=16),     # n_h > chunk
     dict(B=1, H=1, L=64, n_h=2, dk=64, dv=32, chunk=16),     # exact multiple of chunk
+    dict(B=1, H=2, L=45, n_h=3, dk=64, dv=64, chunk=32),     # 11 readouts in a 16-row tile
+    dict(B=2, H=1, L=37, n_h=7, dk=128, dv=32, chunk=64),    # 10 readouts in a 16-row tile
 ]
 
 
