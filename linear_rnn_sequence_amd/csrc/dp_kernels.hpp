@@ -1104,6 +1104,18 @@ __global__ __launch_bounds__(64) void dp_precond_kernel(PrecondArgs p) {
 #pragma unroll
   for (int e = 0; e < EPL; ++e) d[e] = p.d[bh * DK + sl * EPL + e];
 
+  // write key d o kh (EPL values, stored together) at dst
+  auto store_kt_at = [&](T* dst, const float* kh) {
+    T o[EPL];
+    if constexpr (sizeof(T) == 2 && EPL == 2) {
+      const bf16x2_t v = __builtin_convertvector(f32x2_t{d[0] * kh[0], d[1] * kh[1]}, bf16x2_t);
+      __builtin_memcpy(o, &v, 4);
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[e] = from_f32<T>(d[e] * kh[e]);
+    }
+    __builtin_memcpy(__builtin_assume_aligned(dst, EPL * sizeof(T)), o, EPL * sizeof(T));
+  };
   // write key d o kh of token t (EPL values, stored together)
   auto store_kt = [&](int t, const float* kh) {
     T o[EPL];
@@ -1154,7 +1166,7 @@ __global__ __launch_bounds__(64) void dp_precond_kernel(PrecondArgs p) {
           for (int e = 0; e < EPL; ++e) sv[i][e] = T{};
       }
     };
-    float rv, wv, btv, rtv;  // this lane's token scalars (current block)
+    float rv, wv, bwv, rtv;  // this lane's token scalars (current block): 1/|k|, w, beta w, r
     auto token_scalars = [&]() {
       const T* kv = reinterpret_cast<const T*>(rowraw);
       float n4[4] = {0.f, 0.f, 0.f, 0.f};
@@ -1163,18 +1175,21 @@ __global__ __launch_bounds__(64) void dp_precond_kernel(PrecondArgs p) {
       const float n2 = (n4[0] + n4[1]) + (n4[2] + n4[3]);
       rv = __builtin_amdgcn_rsqf(fmaxf(n2, 1e-12f));  // 1 / max(|k|, 1e-6)
       const float ns = n2 * rv * rv;                  // |kh|^2
-      btv = p.beta_aware ? clamp_keep_nan(bnx, 0.f, 2.f) : 1.f;
-      wv = p.eta * btv * __builtin_amdgcn_rcpf(fmaxf(ns, p.eps));
+      const float bt = p.beta_aware ? clamp_keep_nan(bnx, 0.f, 2.f) : 1.f;
+      wv = p.eta * bt * __builtin_amdgcn_rcpf(fmaxf(ns, p.eps));
+      bwv = bt * wv;  // coef = w (1 - beta <d, s>) = w - (beta w) <d, s>
       rtv = rnx;
     };
     auto lane_val = [](float x, int i) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), i)); };
-    auto run_block = [&](auto fullc, int t0) {
-      constexpr bool FULL = decltype(fullc)::value;
+    // RET: a retention gate is given (else r = 1 and d is not rescaled)
+    auto run_block = [&](auto fullc, auto retc, int t0) {
+      constexpr bool FULL = decltype(fullc)::value, RET = decltype(retc)::value;
+      T* kto = ktp + t0 * kstride;  // write key of token t0 + i at kto + i kstride
 #pragma unroll
       for (int i = 0; i < PB; ++i) {
         const int t = t0 + i;
         if (FULL || t < p.L) {
-          const float r = lane_val(rv, i), w = lane_val(wv, i), bt = lane_val(btv, i), rt = lane_val(rtv, i);
+          const float r = lane_val(rv, i), w = lane_val(wv, i), bw = lane_val(bwv, i);
           float kh[EPL], sq[EPL], ds = 0.f;
 #pragma unroll
           for (int e = 0; e < EPL; ++e) {
@@ -1183,10 +1198,17 @@ __global__ __launch_bounds__(64) void dp_precond_kernel(PrecondArgs p) {
             ds = fmaf(d[e], sq[e], ds);
           }
           ds = head_sum<LPH>(ds);
-          if (active) store_kt(t, kh);
-          const float coef = w * (1.f - bt * ds);
+          if (active) store_kt_at(kto, kh);
+          kto += kstride;
+          const float coef = fmaf(-bw, ds, w);
+          if constexpr (RET) {
+            const float rt = lane_val(rtv, i);
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) d[e] = med3_keep_nan(fmaf(coef, sq[e], rt * d[e]), p.dmin, p.dmax);
+            for (int e = 0; e < EPL; ++e) d[e] = med3_keep_nan(fmaf(coef, sq[e], rt * d[e]), p.dmin, p.dmax);
+          } else {
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) d[e] = med3_keep_nan(fmaf(coef, sq[e], d[e]), p.dmin, p.dmax);
+          }
         }
       }
     };
@@ -1198,10 +1220,18 @@ __global__ __launch_bounds__(64) void dp_precond_kernel(PrecondArgs p) {
         load_rows(t0 + PB);
         load_slices(t0 + PB, sn);
       }
-      if (t0 + PB <= p.L)
-        run_block(std::true_type{}, t0);
-      else
-        run_block(std::false_type{}, t0);
+      const bool full = t0 + PB <= p.L;
+      if (rp != nullptr) {
+        if (full)
+          run_block(std::true_type{}, std::true_type{}, t0);
+        else
+          run_block(std::false_type{}, std::true_type{}, t0);
+      } else {
+        if (full)
+          run_block(std::true_type{}, std::false_type{}, t0);
+        else
+          run_block(std::false_type{}, std::false_type{}, t0);
+      }
 #pragma unroll
       for (int i = 0; i < PB; ++i)
 #pragma unroll
