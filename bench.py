@@ -72,12 +72,16 @@ def copy_probe(nbytes):
 
 
 def source_digest():
-    """sha256 over the kernel sources (csrc/*.hip, *.hpp), in name order."""
+    """sha256 over the forward kernels' sources (csrc/*.hip, *.hpp, in name
+    order, without the backward and decode files, which they do not use)."""
     import glob
     import hashlib
 
     hsh = hashlib.sha256()
     for f in sorted(glob.glob(os.path.join(ROOT, "linear_rnn_sequence_amd", "csrc", "*"))):
+        base = os.path.basename(f)
+        if base.startswith(("dp_bwd", "dp_decode")):
+            continue
         if f.endswith((".hip", ".hpp")):
             hsh.update(os.path.basename(f).encode())
             with open(f, "rb") as fh:
