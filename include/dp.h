@@ -213,6 +213,35 @@ int dp_osdn_precond_ex_bf16(const void* k, const float* beta, const float* r, in
                             int H, int L, int dk, float eta, float dmin, float dmax, float eps,
                             float* d_state, void* kt, dp_stream stream);
 
+/* OSDN phase 1 and the write-key forward in one call, pipelined over token
+ * segments (OSDN notes sec. 2.4 Alg. 1 for phase 1, sec. 2.5 for phase 2; the
+ * DeltaProduct notes sec. 2.2 and 2.6 for the recurrence, with n_h = 1).
+ * Computes exactly what dp_osdn_precond_bf16 followed by dp_fwd_wk_bf16 with
+ * the emitted write keys computes (the same kernels, the same chunks), but the
+ * sequence is cut into `segments` runs of whole chunks: while the forward of
+ * one run proceeds on a second stream of the device, phase 1 already scans the
+ * next run on `stream`.  On return `stream` waits for both.
+ *   q [B,L,H,dk], k [B,L,H,dk] (raw read keys), v [B,L,H,dv]  bf16
+ *   beta [B,L,H] f32;  h0 [B,H,dk,dv] f32 or NULL (zero)
+ *   eta, dmin, dmax, eps: the phase-1 constants (3e-3, 0.5, 2, 1e-6)
+ *   d_state [B,H,dk] f32 in/out: d_1 on entry, d_{L+1} on exit
+ *   kt [B,L,H,dk] bf16 written: the write keys d_t o kh_t
+ *   out [B,L,H,dv] bf16 written;  final_state [B,H,dk,dv] f32 written (the
+ *   state passes through it between runs: it must not be NULL when the call
+ *   makes more than one run, and may alias h0)
+ *   workspace: dp_osdn_fwd_workspace_size() bytes (one run's forward), 256-byte aligned
+ *   segments: 1 .. 16 (runs of ceil(ceil(L / segments) / chunk) chunks)
+ * Calls on one device must not overlap in time: they share the second stream.
+ * Errors: those of the two calls it replaces; DP_EINVAL for segments outside
+ * 1 .. 16 or a NULL final_state with several runs; DP_EHIP when the second
+ * stream cannot be made. */
+int dp_osdn_fwd_workspace_size(int B, int H, int L, int dk, int dv, int chunk, int segments,
+                               size_t* bytes);
+int dp_osdn_fwd_bf16(const void* q, const void* k, const void* v, const float* beta, const float* h0,
+                     int B, int H, int L, int dk, int dv, int chunk, float eta, float dmin, float dmax,
+                     float eps, float* d_state, void* kt, void* out, float* final_state, void* workspace,
+                     size_t workspace_bytes, int segments, dp_stream stream);
+
 /*
  * Packed variable-length sequences, bf16 with symmetric keys (DeltaProduct
  * notes sec. 2.2, 2.6, 4.1): nseq independent sequences packed along one

@@ -28,6 +28,7 @@ EXPORTS = (
     "dp_osdn_precond_ex_f32", "dp_osdn_precond_ex_bf16",
     "dp_fwd_varlen_workspace_size", "dp_fwd_varlen_bf16",
     "dp_bwd_workspace_size", "dp_bwd_f32", "dp_bwd_bf16",
+    "dp_osdn_fwd_workspace_size", "dp_osdn_fwd_bf16",
 )
 
 _lib = None
@@ -92,6 +93,11 @@ def load() -> ctypes.CDLL:
         for name in ("dp_bwd_f32", "dp_bwd_bf16"):
             getattr(lib, name).restype = _I
             getattr(lib, name).argtypes = bwd
+        lib.dp_osdn_fwd_workspace_size.restype = _I
+        lib.dp_osdn_fwd_workspace_size.argtypes = [_I] * 7 + [ctypes.POINTER(ctypes.c_size_t)]
+        lib.dp_osdn_fwd_bf16.restype = _I
+        lib.dp_osdn_fwd_bf16.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _F, _F, _P, _P,
+                                         _P, _P, _P, ctypes.c_size_t, _I, _P]
         _lib = lib
     return _lib
 
@@ -247,6 +253,55 @@ def osdn_precond(k, beta, *, eta: float = 3e-3, dmin: float = 0.5, dmax: float =
                 _ptr(d_state), _ptr(kt), _stream(stream))
     _check(rc, name)
     return kt, d_state
+
+
+def osdn_fwd_workspace_size(B, H, L, dk, dv, chunk, segments) -> int:
+    """Workspace bytes of :func:`osdn_fwd` (dp_osdn_fwd_workspace_size)."""
+    n = ctypes.c_size_t(0)
+    _check(load().dp_osdn_fwd_workspace_size(B, H, L, dk, dv, chunk, segments, ctypes.byref(n)),
+           "dp_osdn_fwd_workspace_size")
+    return n.value
+
+
+def osdn_fwd(q, k, v, beta, *, h0=None, chunk: int = 64, segments: int = 4, eta: float = 3e-3,
+             dmin: float = 0.5, dmax: float = 2.0, eps: float = 1e-6, d_state=None, kt=None, out=None,
+             final_state=None, workspace=None, stream=None):
+    """OSDN phase 1 and the write-key forward in one call (dp_osdn_fwd_bf16),
+    pipelined over `segments` token runs: q, k [B,L,H,dk], v [B,L,H,dv] bf16,
+    beta [B,L,H] f32.  d_state [B,H,dk] is d_1 on entry (default ones).
+    Returns (out [B,L,H,dv], final_state [B,H,dk,dv], kt [B,L,H,dk], d_state)."""
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("expected q[B,L,H,dk], k[B,L,H,dk], v[B,L,H,dv]")
+    B, L, H, dk = q.shape
+    dv = v.shape[3]
+    dev = q.device
+    for t, n, shp in ((q, "q", (B, L, H, dk)), (k, "k", (B, L, H, dk)), (v, "v", (B, L, H, dv))):
+        _need(t, n, torch.bfloat16, shp, dev)
+        if not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous")
+    _need(beta, "beta", torch.float32, (B, L, H), dev)
+    _need(h0, "h0", torch.float32, (B, H, dk, dv), dev)
+    if d_state is None:
+        d_state = torch.ones(B, H, dk, dtype=torch.float32, device=dev)
+    _need(d_state, "d_state", torch.float32, (B, H, dk), dev)
+    if kt is None:
+        kt = torch.empty(B, L, H, dk, dtype=torch.bfloat16, device=dev)
+    _need(kt, "kt", torch.bfloat16, (B, L, H, dk), dev)
+    if out is None:
+        out = torch.empty(B, L, H, dv, dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, (B, L, H, dv), dev)
+    if final_state is None:
+        final_state = torch.empty(B, H, dk, dv, dtype=torch.float32, device=dev)
+    _need(final_state, "final_state", torch.float32, (B, H, dk, dv), dev)
+    if workspace is None:
+        nbytes = osdn_fwd_workspace_size(B, H, L, dk, dv, chunk, segments)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    rc = load().dp_osdn_fwd_bf16(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(h0), B, H, L, dk, dv, chunk,
+                                 eta, dmin, dmax, eps, _ptr(d_state), _ptr(kt), _ptr(out), _ptr(final_state),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(), segments,
+                                 _stream(stream))
+    _check(rc, "dp_osdn_fwd_bf16")
+    return out, final_state, kt, d_state
 
 
 def decode(q, k, v, beta, state, g=None, *, kt=None, ga=None, out=None, out_dtype=None,

@@ -3,6 +3,7 @@
 // Every entry point validates its arguments on the host before touching the
 // HIP runtime, then enqueues the kernels of dp_kernels.hpp on the caller's
 // stream and returns.  The library allocates nothing and keeps no state.
+#include <mutex>
 #include <limits.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -249,10 +250,12 @@ hipError_t dispatch_precond(int elem, int dk, const dp::PrecondArgs& a, hipStrea
   return hipErrorInvalidValue;
 }
 
+// Ls, t0: the call covers tokens t0 .. t0 + L - 1 of sequences Ls tokens long
+// (0, 0: the whole sequences).
 int fwd_impl(int elem, const void* q, const void* k, const void* kt, const void* v,
              const float* beta, const float* g, int n_h, int B, int H, int L, int dk, int dv,
              int chunk, void* out, float* final_state, const float* h0, void* workspace,
-             size_t workspace_bytes, int flags, dp_stream stream) {
+             size_t workspace_bytes, int flags, dp_stream stream, int Ls = 0, int t0 = 0) {
   const Shape s{n_h, B, H, L, dk, dv, chunk};
   int rc = check_shape(s);
   if (rc != DP_OK) return rc;
@@ -292,6 +295,8 @@ int fwd_impl(int elem, const void* q, const void* k, const void* kt, const void*
   a.RT = readout_rows(chunk, n_h);
   a.asym = kt != nullptr ? 1 : 0;
   a.out_f32 = (elem == 4 || (flags & DP_OUT_F32) != 0) ? 1 : 0;
+  a.Ls = Ls;
+  a.t0 = t0;
   fastdiv_magic(n_h, &a.nh_magic, &a.nh_shift);
 
   int BV = 0, lds = 0;
@@ -443,7 +448,7 @@ int decode_impl(int elem, const void* q, const void* k, const void* kt, const vo
 
 int precond_impl(int elem, const void* k, const float* beta, const float* ret, int flags,
                  int B, int H, int L, int dk, float eta, float dmin, float dmax, float eps,
-                 float* d_state, void* kt, bool open_box, dp_stream stream) {
+                 float* d_state, void* kt, bool open_box, dp_stream stream, int Ls = 0, int t0 = 0) {
   if (k == nullptr || beta == nullptr || d_state == nullptr || kt == nullptr) return DP_EINVAL;
   if (B <= 0 || H <= 0 || L < 0) return DP_EINVAL;
   if ((flags & ~DP_PRECOND_BETA_FREE) != 0) return DP_EINVAL;
@@ -466,8 +471,47 @@ int precond_impl(int elem, const void* k, const float* beta, const float* ret, i
   a.dmin = dmin;
   a.dmax = dmax;
   a.eps = eps;
+  a.Ls = Ls;
+  a.t0 = t0;
   const hipError_t e = dispatch_precond(elem, dk, a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DP_OK : DP_EHIP;
+}
+
+// Write-key forward with its phase 1, pipelined over token segments.  Each
+// segment is a whole number of chunks (n_h = 1: a chunk is C tokens), so the
+// chunks are those of the unsegmented forward.  Phase 1 runs on the caller's
+// stream and phase 2 on a second stream of the device (created once, default
+// priority), ordered by one event per segment.
+constexpr int kMaxSegments = 16;
+constexpr int kMaxDevices = 64;
+
+int seg_len(int L, int chunk, int segments) {
+  const int per = (L + segments - 1) / segments;
+  const int len = (per + chunk - 1) / chunk * chunk;
+  return len > 0 ? len : chunk;
+}
+
+struct SegRes {
+  hipStream_t st2 = nullptr;
+  hipEvent_t ev[kMaxSegments + 1] = {};
+  bool ready = false;
+};
+
+// the second stream and events of the current device, or nullptr on failure
+SegRes* seg_res() {
+  static SegRes res[kMaxDevices];
+  static std::mutex mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  SegRes& r = res[dev];
+  if (!r.ready) {
+    if (hipStreamCreateWithFlags(&r.st2, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    for (int i = 0; i <= kMaxSegments; ++i)
+      if (hipEventCreateWithFlags(&r.ev[i], hipEventDisableTiming) != hipSuccess) return nullptr;
+    r.ready = true;
+  }
+  return &r;
 }
 
 // Backward: fixed chunk of kBwdChunk sub-steps.  Workspace: T (fp32) and
@@ -705,6 +749,54 @@ int dp_osdn_precond_ex_bf16(const void* k, const float* beta, const float* r, in
                             float* d_state, void* kt, dp_stream stream) {
   return precond_impl(2, k, beta, r, flags, B, H, L, dk, eta, dmin, dmax, eps, d_state, kt, true,
                       stream);
+}
+
+int dp_osdn_fwd_workspace_size(int B, int H, int L, int dk, int dv, int chunk, int segments,
+                               size_t* bytes) {
+  if (bytes == nullptr || segments < 1 || segments > kMaxSegments || chunk <= 0 || L < 0) return DP_EINVAL;
+  const Shape s{1, B, H, seg_len(L, chunk, segments), dk, dv, chunk};
+  const int rc = check_shape(s);
+  if (rc != DP_OK) return rc;
+  *bytes = ws_total(s, 2);
+  return DP_OK;
+}
+
+int dp_osdn_fwd_bf16(const void* q, const void* k, const void* v, const float* beta, const float* h0,
+                     int B, int H, int L, int dk, int dv, int chunk, float eta, float dmin, float dmax,
+                     float eps, float* d_state, void* kt, void* out, float* final_state, void* workspace,
+                     size_t workspace_bytes, int segments, dp_stream stream) {
+  if (segments < 1 || segments > kMaxSegments || chunk <= 0 || L < 0) return DP_EINVAL;
+  const int len = seg_len(L, chunk, segments);
+  const int nseg = L > 0 ? (L + len - 1) / len : 0;
+  const Shape s{1, B, H, len, dk, dv, chunk};
+  int rc = check_shape(s);
+  if (rc != DP_OK) return rc;
+  if (nseg > 1 && final_state == nullptr) return DP_EINVAL;  // the state passes through it
+  if (L > 0 && (q == nullptr || k == nullptr || v == nullptr || beta == nullptr || out == nullptr ||
+                kt == nullptr || d_state == nullptr))
+    return DP_EINVAL;
+  const size_t need = ws_total(s, 2);
+  if (workspace_bytes < need || (need > 0 && workspace == nullptr)) return DP_EWORKSPACE;
+  if (nseg == 0) return fwd_impl(2, q, k, k, v, beta, nullptr, 1, B, H, 0, dk, dv, chunk, out, final_state,
+                                 h0, workspace, workspace_bytes, DP_STAGE_ALL, stream);
+  SegRes* r = seg_res();
+  if (r == nullptr) return DP_EHIP;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  for (int sg = 0; sg < nseg; ++sg) {
+    const int t0 = sg * len, n = L - t0 < len ? L - t0 : len;
+    rc = precond_impl(2, k, beta, nullptr, 0, B, H, n, dk, eta, dmin, dmax, eps, d_state, kt, false,
+                      stream, L, t0);
+    if (rc != DP_OK) return rc;
+    if (hipEventRecord(r->ev[sg], st) != hipSuccess || hipStreamWaitEvent(r->st2, r->ev[sg], 0) != hipSuccess)
+      return DP_EHIP;
+    rc = fwd_impl(2, q, k, kt, v, beta, nullptr, 1, B, H, n, dk, dv, chunk, out, final_state,
+                  sg == 0 ? h0 : final_state, workspace, workspace_bytes, DP_STAGE_ALL, r->st2, L, t0);
+    if (rc != DP_OK) return rc;
+  }
+  if (hipEventRecord(r->ev[kMaxSegments], r->st2) != hipSuccess ||
+      hipStreamWaitEvent(st, r->ev[kMaxSegments], 0) != hipSuccess)
+    return DP_EHIP;
+  return DP_OK;
 }
 
 int dp_fwd_varlen_workspace_size(int n_h, int nseq, int H, int T, int dk, int dv, int chunk,

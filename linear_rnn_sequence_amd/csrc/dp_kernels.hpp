@@ -89,9 +89,19 @@ struct FwdArgs {
   int nwork;        // prep work items (varlen: an upper bound; extra items exit)
   uint32_t nh_magic;  // s / n_h == fastdiv(s, nh_magic, nh_shift) for 0 <= s < 2^31
   int nh_shift;
+  // A call on tokens t0 .. t0 + L - 1 of sequences Ls tokens long (the UT and
+  // scan kernels of the fixed-length paths): token t of batch row b is row
+  // (b Ls + t0 + t) of the token-major tensors.  Ls = 0: Ls = L, t0 = 0.
+  int Ls = 0, t0 = 0;
   // dp_scan_kernel LDS byte offsets
   int oK, oKt, oQ, oT, oHt, oXt, oUo, oUs, oP, oV, oG, oEG, oEL, oLoc, oRow, oTok;
 };
+
+// First token row of batch row b (see FwdArgs::Ls).
+template <typename A>
+__host__ __device__ __forceinline__ long long tok_base(const A& p, int b) {
+  return (long long)b * (p.Ls > 0 ? p.Ls : p.L) + p.t0;
+}
 
 struct PrecondArgs {
   const void* k;
@@ -102,6 +112,7 @@ struct PrecondArgs {
   int B, H, L;
   int beta_aware;    // 0: the beta-free phase-1 step
   float eta, dmin, dmax, eps;
+  int Ls = 0, t0 = 0;  // a call on tokens t0 .. t0 + L - 1 of Ls-token sequences (0: Ls = L)
 };
 
 __host__ __device__ constexpr int align16(int x) { return (x + 15) & ~15; }
@@ -137,7 +148,7 @@ __device__ __forceinline__ SeqGeom seq_geom(const FwdArgs& p, int d, int h, int 
 __device__ __forceinline__ long long sub_row(const FwdArgs& p, int s, int b, int h) {
   const int t = fastdiv(s, p.nh_magic, p.nh_shift);
   const int j = s - t * p.n_h;
-  return (((long long)b * p.L + t) * p.H + h) * p.n_h + j;
+  return ((tok_base(p, b) + t) * p.H + h) * p.n_h + j;
 }
 
 // LDS bytes of dp_ut_kernel: K (and Kw) rows, fp32 M, 3 scalar vectors,
@@ -203,7 +214,7 @@ __global__ __launch_bounds__(kThreads) void dp_ut_kernel(FwdArgs p) {
     const int s = s0 + tid;
     const int t = fastdiv(s, p.nh_magic, p.nh_shift);
     const int j = s - t * p.n_h;
-    const long long tok = ((long long)b * p.L + t) * p.H + h;
+    const long long tok = (tok_base(p, b) + t) * p.H + h;
     braw = p.beta[tok * p.n_h + j];
     first = (j == 0);
     if (p.g != nullptr && first) lam = logf(fmaxf(p.g[tok], FLT_MIN));
@@ -396,7 +407,7 @@ __global__ __launch_bounds__(kThreads) void dp_scan_kernel(FwdArgs p) {
   const T* qp = static_cast<const T*>(p.q);
   const OT* wsT = static_cast<const OT*>(p.wsT) + (long long)bh * nc * C * C;
   const float2* wsS = p.wsS + (long long)bh * nc * C;
-  const long long tok0 = (long long)b * p.L * p.H + h;  // token (b, 0, h)
+  const long long tok0 = tok_base(p, b) * p.H + h;  // token (b, 0, h)
 
   // row indices of chunk c's sub-steps / readout tokens into buffer c & 1
   auto index_chunk = [&](int c) {
@@ -752,7 +763,7 @@ __global__ __launch_bounds__(64 * (NWC + NWP)) void dp_scan16_kernel(FwdArgs p) 
   const int b = bh / p.H, h = bh % p.H;
   const int v0 = vb * BV;  // first value column of the workgroup
   const int n_h = p.n_h, nc = p.nc;
-  const long long tok0 = (long long)b * p.L * p.H + h;  // token (b, 0, h)
+  const long long tok0 = tok_base(p, b) * p.H + h;  // token (b, 0, h)
   auto first_readout = [&](int s0) { return s0 + (n_h - 1 - (s0 - fastdiv(s0, p.nh_magic, p.nh_shift) * n_h)); };
   auto buffer = [&](int c) { return smem + (c & 1) * Lo.buf; };
 
@@ -1093,7 +1104,7 @@ __global__ __launch_bounds__(64) void dp_precond_kernel(PrecondArgs p) {
   const long long bh = active ? bh_raw : 0;
   const int b = (int)(bh / p.H), h = (int)(bh % p.H);
   // token t of this head: row ((b L + t) H + h) of the token-major tensors
-  const long long row0 = (long long)b * p.L * p.H + h;
+  const long long row0 = tok_base(p, b) * p.H + h;
   const T* kp = static_cast<const T*>(p.k) + row0 * DK + sl * EPL;
   T* ktp = static_cast<T*>(p.kt) + row0 * DK + sl * EPL;
   const float* bp = p.beta + row0;

@@ -1,0 +1,86 @@
+"""GPU checks of the pipelined write-key forward (dp_osdn_fwd_bf16).
+
+It runs the same kernels on the same chunks as OSDN phase 1 followed by the
+write-key forward, cut into token runs (the state and d pass between runs in
+fp32), so its results must equal the two-call path bit for bit; one case is also
+checked against the fp64 oracle.
+"""
+import pytest
+import torch
+
+import linear_rnn_sequence_amd as dp
+import oracle
+from linear_rnn_sequence_amd.inputs import WORKLOADS, make
+from parity import TOL, f64, rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    dp.load()  # raises when libdp.so is missing: no silent fallback
+
+
+def two_calls(q, k1, v1, b1, h0, chunk):
+    kt, d = dp.osdn_precond(k1, b1)
+    out, fs = dp.fwd(q, k1.unsqueeze(3), v1.unsqueeze(3), b1.unsqueeze(3), chunk=chunk, h0=h0,
+                     kt=kt.unsqueeze(3))
+    return out, fs, kt, d
+
+
+def inputs(B, H, L, dk, dv, with_h0=False):
+    w = WORKLOADS["c5"].scaled(B=B, H=H, L=L, dk=dk, dv=dv)
+    inp = make(w)
+    dev = torch.device("cuda:0")
+    q = inp["q"].to(dev)
+    k1 = inp["k"][:, :, :, 0, :].contiguous().to(dev)
+    v1 = inp["v"][:, :, :, 0, :].contiguous().to(dev)
+    b1 = inp["beta"][..., 0].contiguous().to(dev)
+    h0 = (0.1 * torch.randn(B, H, dk, dv, generator=torch.Generator().manual_seed(5))).to(dev) if with_h0 else None
+    return q, k1, v1, b1, h0
+
+
+CASES = [  # B, H, L, dk, dv, chunk, segments, h0
+    (2, 3, 300, 128, 128, 64, 1, False),
+    (2, 3, 300, 128, 128, 64, 2, False),
+    (2, 3, 300, 128, 128, 64, 4, True),
+    (1, 2, 300, 128, 128, 64, 16, False),  # more runs asked for than chunks
+    (1, 2, 50, 128, 64, 64, 4, False),     # shorter than one chunk
+    (2, 1, 257, 64, 32, 32, 3, True),
+]
+
+
+@pytest.mark.parametrize("B,H,L,dk,dv,chunk,segments,with_h0", CASES)
+def test_pipelined_equals_two_calls(B, H, L, dk, dv, chunk, segments, with_h0):
+    say(f"case osdn_fwd B={B} H={H} L={L} dk={dk} dv={dv} C={chunk} segments={segments} h0={with_h0}")
+    q, k1, v1, b1, h0 = inputs(B, H, L, dk, dv, with_h0)
+    ref = two_calls(q, k1, v1, b1, h0, chunk)
+    got = dp.osdn_fwd(q, k1, v1, b1, h0=h0, chunk=chunk, segments=segments)
+    torch.cuda.synchronize()
+    for name, x, r in zip(("out", "final_state", "kt", "d"), got, ref):
+        assert torch.equal(x, r), f"{name} differs from the two-call path"
+
+
+def test_pipelined_matches_oracle():
+    B, H, L, dk, dv = 2, 2, 200, 128, 128
+    say(f"case osdn_fwd vs oracle B={B} H={H} L={L}")
+    q, k1, v1, b1, _ = inputs(B, H, L, dk, dv)
+    out, fs, kt, d = dp.osdn_fwd(q, k1, v1, b1, segments=3)
+    torch.cuda.synchronize()
+    kto, do = oracle.precond(k1.cpu(), b1.cpu())
+    oo, fo = oracle.fwd(q.cpu(), k1.cpu().unsqueeze(3), v1.cpu().unsqueeze(3), b1.cpu().unsqueeze(3),
+                        kt=kto[:, :, :, None, :])
+    for name, x, r in (("out", out, oo), ("final_state", fs, fo), ("kt", kt, kto), ("d", d, do)):
+        e = rel_err(f64(x), r)
+        say(f"  {name}: err {e:.3e}")
+        assert e <= TOL["bf16"], f"{name}: err {e:.3e}"
+
+
+def test_argument_errors():
+    q, k1, v1, b1, _ = inputs(1, 1, 130, 128, 128)
+    with pytest.raises(dp.DPError):
+        dp.osdn_fwd(q, k1, v1, b1, segments=0)
+    with pytest.raises(dp.DPError):
+        dp.osdn_fwd(q, k1, v1, b1, segments=17)
