@@ -496,6 +496,14 @@ __device__ __forceinline__ int lane_tr(int rows) {
   const int l = threadIdx.x & 63, i = l & 15, g = l >> 4, e = i >> 2, a = i & 3, hi = a >> 1;
   return blk_pos(hi, W) * rows * 16 + ((4 * g + e) ^ (8 * hi)) * 16 + 8 * (a & 1);
 }
+// Lane part of a transposed read of a row-major tile W columns wide (W * 2
+// bytes per row): source lane i = 4e + a of group g points at row 4g + e,
+// columns 4a .. 4a + 3 (plus the tile's row and column offsets).
+template <int W>
+__device__ __forceinline__ int lane_tr_rows() {
+  const int l = threadIdx.x & 63, i = l & 15, g = l >> 4, e = i >> 2, a = i & 3;
+  return ((4 * g + e) * W + 4 * a) * 2;
+}
 // block offset (immediate part) of logical block pair base 2 * dt (d0 = 16 dt)
 template <int W>
 __host__ __device__ constexpr int tr_block(int dt) {
@@ -713,18 +721,18 @@ void dp_chain_kernel(FwdArgs p) {
           if (1024 * m + 16 * lane < CB && keep[m]) dma16(src + soff[m], st + 1024 * m);
         }
       });
-      // value tile: logical block q = columns v0 + 8q.., rows = sub-steps
+      // value tile, row-major (BV * 2 bytes per sub-step): each copy moves
+      // whole runs of BV columns of consecutive sub-steps
       static_for<NIV>([&](auto mc) {
         constexpr int m = decltype(mc)::value;
         if constexpr ((NIB + m) % NCW == CW) {
           const int o = 1024 * m + 16 * lane;
-          const int pb = o / (C * 16), rs = (o / 16) % C;
-          const int q = blk_pos(pb, BV);
-          int s = c * C + (rs ^ (8 * (q & 1)));
+          const int r = o / (BV * 2), cv = (o % (BV * 2)) / 2;  // tile row, first column
+          int s = c * C + r;
           s = s < N ? s : N - 1;  // rows past the end: any valid row (their beta is 0)
           const int t = fastdiv(s, p.nh_magic, p.nh_shift);
           const long long row = (tok0 + (long long)t * p.H) * p.n_h + (s - t * p.n_h);
-          if (lane < VPI) dma16(vp + row * p.dv + 8 * q, st + W.bytes + 1024 * m);
+          if (lane < VPI) dma16(vp + row * p.dv + cv, st + W.bytes + 1024 * m);
         }
       });
     };
@@ -772,7 +780,7 @@ void dp_chain_kernel(FwdArgs p) {
   const int lrT = frag_layout(C) ? lane_frag(C) : lane_row<C>(C);
   const int lrQ = frag_layout(DK) ? lane_frag(RT) : lane_row<DK>(RT);
   const int lrP = frag_layout(C) ? lane_frag(RT) : lane_row<C>(RT);
-  const int ltK = lane_tr<DK>(C), ltV = lane_tr<BV>(C);
+  const int ltK = lane_tr<DK>(C), ltV = lane_tr_rows<BV>();
   const int ocol = v0 + vw + col;  // output column of this lane
   float* const sink = p.sink + ((long long)f * NWC + wave) * 64 + lane;
   f32x4_t hacc[NDT];
@@ -844,7 +852,7 @@ void dp_chain_kernel(FwdArgs p) {
       for (int ct = 0; ct < NCT; ++ct) {
         // V[16 ct + 4 grp + e][vw + col] (bf16) in accumulator layout
         const s16x4_t vr = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_s16x4_t*)(st + W.bytes + ltV + tr_block<BV>(wave) * C * 16 + ct * 16 * 16));
+            (lds_s16x4_t*)(st + W.bytes + ltV + (16 * ct * BV + 16 * wave) * 2));
 #pragma unroll
         for (int e = 0; e < 4; ++e) vf[ct][e] = __uint_as_float((uint32_t)(uint16_t)vr[e] << 16);
         if constexpr (GATED) {
@@ -1093,7 +1101,7 @@ void dp_chain_kernel(FwdArgs p) {
     for (int ct = 0; ct < NCT; ++ct) {
       fk[ct].load(smem, so + W.oK + lrK + ct * 256);
       vr[ct] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4_t*)(st + W.bytes + ltV + tr_block<BV>(wave) * C * 16 + ct * 16 * 16));
+          (lds_s16x4_t*)(st + W.bytes + ltV + (16 * ct * BV + 16 * wave) * 2));
       eg[ct] = *reinterpret_cast<const f32x4_t*>(sEG + ct * 16 + 4 * grp);
     }
 #pragma unroll
