@@ -473,7 +473,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void d
 // of each group of four are stored in the order 0, 2, 1, 3.  With (b) the two
 // 8-byte halves of an MFMA A fragment (columns 32t + 4g.. and 32t + 16 + 4g..)
 // sit exactly one block apart, so one ds_read2_b64 fetches a fragment into
-// consecutive registers.
+// consecutive registers.  The value tile is the exception: it is row-major
+// (BV columns per sub-step), so that each direct-to-LDS copy moves whole rows.
 
 // physical position of logical block q in a region of W columns (an involution)
 __host__ __device__ constexpr int blk_pos(int q, int W) {
