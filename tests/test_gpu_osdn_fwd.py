@@ -49,6 +49,8 @@ CASES = [  # B, H, L, dk, dv, chunk, segments, h0
     (1, 2, 300, 128, 128, 64, 16, False),  # more runs asked for than chunks
     (1, 2, 50, 128, 64, 64, 4, False),     # shorter than one chunk
     (2, 1, 257, 64, 32, 32, 3, True),
+    (1, 3, 130, 32, 32, 32, 2, False),     # dk = 32: two heads per phase-1 wavefront
+    (1, 2, 100, 16, 16, 16, 5, True),      # dk = 16, chunk 16
 ]
 
 
