@@ -112,12 +112,17 @@ __host__ __device__ constexpr int chain_lds_bytes(int DK, int C, int RT, int BV)
 // M and the scores are formed, then fp32 T and the partial-sum tiles of the
 // blocked inverse; after it come fp32 M, beta, G and the readout locations.
 // M is kept as its lower-triangular 16 x 16 blocks only (block (i, j), j <= i,
-// at index i (i + 1) / 2 + j, rows kPrepLdm floats apart), which keeps four
-// workgroups resident per CU at dk = 128, chunk 64.
+// at index i (i + 1) / 2 + j, rows kPrepLdm floats apart, blocks kPrepBlk
+// floats apart), which keeps five workgroups resident per CU at dk = 128,
+// chunk 64.
 constexpr int kPrepLdm = 20;  // 20 n mod 64 is distinct for n < 16: conflict-free row reads
+// 8 floats of padding per block: the diagonal blocks 0, 2, 5, 9 that the four
+// lane groups of the forward substitution read in step start on banks 0, 16,
+// 40 and 8 (with 320 they would all start on bank 0: a 4-way conflict)
+constexpr int kPrepBlk = 16 * kPrepLdm + 8;
 __host__ __device__ constexpr int prep_mblock(int i, int j) { return i * (i + 1) / 2 + j; }
 __host__ __device__ constexpr int prep_m_bytes(int C) {
-  return (C / 16) * (C / 16 + 1) / 2 * 16 * kPrepLdm * 4;
+  return (C / 16) * (C / 16 + 1) / 2 * kPrepBlk * 4;
 }
 // With dk a multiple of 32 the readout queries never touch LDS: each
 // wavefront loads its MFMA fragments of them straight into registers (and
@@ -387,7 +392,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void d
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     acc = mm_ll<DK>(acc, sK, LDK, ti * 16 + (lane & 15), sK, LDK, tj * 16 + (lane & 15));
     const int jj = tj * 16 + (lane & 15);
-    float* mb = sA + tile * 16 * kPrepLdm;
+    float* mb = sA + tile * kPrepBlk;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int ii = ti * 16 + 4 * (lane >> 4) + e;
@@ -409,13 +414,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void d
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float acc = (i == cc) ? 1.f : 0.f;
-        const float* ar = sA + (prep_mblock(gb, gb) * 16 + i) * kPrepLdm;
+        const float* ar = sA + prep_mblock(gb, gb) * kPrepBlk + i * kPrepLdm;
 #pragma unroll
         for (int j = 0; j < i; ++j) acc = fmaf(-ar[j], t[j], acc);
         t[i] = acc;
       }
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sTf[(prep_mblock(gb, gb) * 16 + i) * kPrepLdm + cc] = t[i];
+      for (int i = 0; i < 16; ++i) sTf[prep_mblock(gb, gb) * kPrepBlk + i * kPrepLdm + cc] = t[i];
     }
   }
   __syncthreads();
@@ -426,18 +431,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void d
     if (i < NT) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
       for (int kb = j; kb < i; ++kb)
-        acc = mm_tile_tb<float, 16>(acc, sA + prep_mblock(i, kb) * 16 * kPrepLdm, kPrepLdm, 0,
-                                    sTf + prep_mblock(kb, j) * 16 * kPrepLdm, kPrepLdm, 0);
+        acc = mm_tile_tb<float, 16>(acc, sA + prep_mblock(i, kb) * kPrepBlk, kPrepLdm, 0,
+                                    sTf + prep_mblock(kb, j) * kPrepBlk, kPrepLdm, 0);
 #pragma unroll
       for (int e = 0; e < 4; ++e) sS[(4 * (lane >> 4) + e) * 17 + (lane & 15)] = acc[e];
     }
     __syncthreads();
     if (i < NT) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mm_tile_tb<float, 16>(acc, sTf + prep_mblock(i, i) * 16 * kPrepLdm, kPrepLdm, 0, sS, 17, 0);
+      acc = mm_tile_tb<float, 16>(acc, sTf + prep_mblock(i, i) * kPrepBlk, kPrepLdm, 0, sS, 17, 0);
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        sTf[(prep_mblock(i, j) * 16 + 4 * (lane >> 4) + e) * kPrepLdm + (lane & 15)] = -acc[e];
+        sTf[prep_mblock(i, j) * kPrepBlk + (4 * (lane >> 4) + e) * kPrepLdm + (lane & 15)] = -acc[e];
     }
     __syncthreads();
   }
@@ -458,7 +463,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void d
     for (int e = 0; e < 8; ++e) {
       const int j = frag_layout(C) ? 32 * (q >> 2) + 4 * (q & 3) + (e & 3) + 16 * (e >> 2) : q * 8 + e;
       f[e] = ((j >> 4) > (i >> 4)) ? 0.f
-                                   : sTf[(prep_mblock(i >> 4, j >> 4) * 16 + (i & 15)) * kPrepLdm + (j & 15)] * sB[j];
+                                   : sTf[prep_mblock(i >> 4, j >> 4) * kPrepBlk + (i & 15) * kPrepLdm + (j & 15)] * sB[j];
     }
     st_vec16(reinterpret_cast<f16_t*>(wsc + W.oT + idx * 16), f);
   }
