@@ -458,12 +458,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void d
       q = 4 * t + rel / rows;
       i = 32 * t + rel % rows;
     }
+    // The reads are unconditional: for any row block ib and column block jb
+    // below C/16, prep_mblock(ib, jb) stays inside the packed lower blocks, so
+    // an upper block reads a stored block and the select drops it.  The
+    // compiler then fetches four adjacent columns per 16-byte read, one LDS
+    // round trip per granule (a guarded read waits once per element).
     float f[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int j = frag_layout(C) ? 32 * (q >> 2) + 4 * (q & 3) + (e & 3) + 16 * (e >> 2) : q * 8 + e;
-      f[e] = ((j >> 4) > (i >> 4)) ? 0.f
-                                   : sTf[prep_mblock(i >> 4, j >> 4) * kPrepBlk + (i & 15) * kPrepLdm + (j & 15)] * sB[j];
+      const float tv = sTf[prep_mblock(i >> 4, j >> 4) * kPrepBlk + (i & 15) * kPrepLdm + (j & 15)] * sB[j];
+      f[e] = ((j >> 4) > (i >> 4)) ? 0.f : tv;
     }
     st_vec16(reinterpret_cast<f16_t*>(wsc + W.oT + idx * 16), f);
   }
