@@ -318,11 +318,15 @@ __global__ __launch_bounds__(kThreads) void dp_ut_kernel(FwdArgs p) {
     constexpr int NV8 = C * C / 8;
     for (int v8 = tid; v8 < NV8; v8 += kThreads) {
       const int i = v8 / (C / 8), j0 = (v8 % (C / 8)) * 8;
+      // unconditional reads (T is a full C x LDA matrix in LDS) and a select:
+      // the compiler then fetches the eight values in 16-byte reads with one
+      // wait, where a guarded read waits once per element
       float f[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int j = j0 + e;
-        f[e] = ((j >> 4) > (i >> 4)) ? 0.f : sTf[i * LDA + j] * (TB ? sB[j] : 1.f);
+        const float tv = sTf[i * LDA + j] * (TB ? sB[j] : 1.f);
+        f[e] = ((j >> 4) > (i >> 4)) ? 0.f : tv;
       }
       if constexpr (sizeof(OT) == 2) {
         st_vec16(wt + i * C + j0, f);
