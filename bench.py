@@ -43,6 +43,12 @@ def parse():
     # each at c3); 100 warm-up steps put the timed steps in the steady state
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--settle", type=float, default=1.0, metavar="SECONDS",
+                    help="untimed steps for at least this long before the warm-up, so that the "
+                         "timed steps run at settled clocks (reported in the line; 0 = none)")
+    ap.add_argument("--no-other-path", action="store_true",
+                    help="skip timing the bf16 symmetric-key workload on the path the library "
+                         "does not pick by default (fused kernel or prep / chain pair)")
     ap.add_argument("--workload", default="c3", help="c1, c2, c3, c3b, c4 or c5")
     ap.add_argument("--also", default="c3b",
                     help="comma-separated extra workloads timed in the same run ('' = none)")
@@ -154,8 +160,14 @@ def recurrent_flops(w):
     return w.B * w.L * w.H * per_tok
 
 
+def fused_possible(w):
+    """Can this workload run the single fused kernel (DP_FWD_FUSED)?"""
+    return w.dtype == "bf16" and not w.asym and w.dk % 32 == 0 and w.chunk % 32 == 0
+
+
 def kernel_names(w):
-    """(prep / UT kernel, scan kernel) names of the path a workload runs on."""
+    """(prep / UT kernel, scan kernel) names of the two-launch path a workload
+    runs on; the fused path is the one kernel dp_fused_kernel."""
     if w.dtype == "bf16" and not w.asym:
         return "dp_prep_kernel", "dp_chain_kernel"
     if w.dtype == "bf16":
@@ -163,8 +175,26 @@ def kernel_names(w):
     return "dp_ut_kernel", "dp_scan_kernel"
 
 
+def fused_issued_flops(w, plan):
+    """MFMA flops dp_fused_kernel issues per forward (tile-padded).  Every
+    workgroup of a head builds the chunk's operands itself: the Gram matrix's
+    lower 16 x 16 tiles (bf16), the readout scores (fp16) and the two
+    off-diagonal T blocks as split-fp16 products (two 32-deep steps per
+    product, two products per 32-row half); the consumers, per 16 value
+    columns: Kn H, Q H, the three 32 x 32 solve steps per half pair, P Up and
+    the state update."""
+    C, dk, dv, BV, RT = w.chunk, w.dk, w.dv, plan["BV"], plan["readout_rows"]
+    nc = -(-(w.L * w.n_h) // C)
+    NT, CH = C // 16, C // 32
+    prod = (NT * (NT + 1) // 2) * 2 * 16 * 16 * dk + 2 * RT * C * dk + CH * 2 * 2 * 2 * 16 * 16 * 32
+    solve = (2 + 4 * (CH - 1)) * 2 * 16 * 16 * 32
+    cons16 = 2 * 16 * (C * dk + RT * dk + RT * C + dk * C) + solve
+    heads = w.B * w.H
+    return heads * nc * ((dv // BV) * prod + (dv // 16) * cons16)
+
+
 def issued_flops(w, plan):
-    """MFMA flops the two kernels actually issue (tile-padded), per forward."""
+    """MFMA flops the two kernels of the two-launch path issue (tile-padded), per forward."""
     C, dk, dv, BV, RT = w.chunk, w.dk, w.dv, plan["BV"], plan["readout_rows"]
     N = w.L * w.n_h
     nc = -(-N // C)
@@ -183,7 +213,29 @@ def issued_flops(w, plan):
 
 # ---------------------------------------------------------------- GPU timing
 
-def time_gpu(w, steps, warmup):
+def settle_clocks(step, seconds):
+    """Run untimed steps for at least `seconds` of wall time: a cold MI355X
+    raises its clocks over the first ~50 forwards, and a short warm-up would
+    time that ramp.  Returns (steps run, seconds)."""
+    import torch
+
+    if seconds <= 0:
+        return 0, 0.0
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+        n += 10
+    return n, time.perf_counter() - t0
+
+
+def time_gpu(w, steps, warmup, settle=0.0, path="auto"):
+    """Time `steps` forwards of workload w on the path the library picks by
+    default (path="auto"), or on the one named ("split", "fused").  The fused
+    kernel runs as one call; the two-kernel paths (prep / chain for bf16
+    symmetric keys, UT / scan otherwise) as two staged calls, so that each
+    kernel is timed on its own."""
     import torch
 
     import linear_rnn_sequence_amd as dp
@@ -196,7 +248,9 @@ def time_gpu(w, steps, warmup):
     d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
     dt = d["q"].dtype
     plan = dp.launch_info(w.n_h, w.B, w.H, w.L, w.dk, w.dv, w.chunk, dt, asym=w.asym)
-    ws = dp.alloc_workspace(w.n_h, w.B, w.H, w.L, w.dk, w.dv, w.chunk, dt, dev)
+    # launch_info reports the default call's plan (no UT workgroups: the fused kernel)
+    fused = path == "fused" or (path == "auto" and plan["ut_wgs"] == 0)
+    ws = None if fused else dp.alloc_workspace(w.n_h, w.B, w.H, w.L, w.dk, w.dv, w.chunk, dt, dev)
     out = torch.empty(w.B, w.L, w.H, w.dv, dtype=inp["out_dtype"], device=dev)
     fs = torch.empty(w.B, w.H, w.dk, w.dv, dtype=torch.float32, device=dev)
     k1 = b1 = kt = dstate = d1 = None
@@ -207,6 +261,7 @@ def time_gpu(w, steps, warmup):
         d1 = torch.ones(w.B, w.H, w.dk, dtype=torch.float32, device=dev)
         dstate = torch.empty_like(d1)
     args = (d["q"], d["k"], d["v"], d["beta"], d["g"])
+    split_flag = "split" if fused_possible(w) else "auto"
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
@@ -218,15 +273,21 @@ def time_gpu(w, steps, warmup):
         kk = None if kt is None else kt.unsqueeze(3)
         if ev is not None:
             ev[1].record(stream)
-        dp.fwd(*args, chunk=w.chunk, h0=d["h0"], kt=kk, out=out, final_state=fs, workspace=ws,
-               stages=dp.STAGE_UT)
-        if ev is not None:
-            ev[2].record(stream)
-        dp.fwd(*args, chunk=w.chunk, h0=d["h0"], kt=kk, out=out, final_state=fs, workspace=ws,
-               stages=dp.STAGE_SCAN)
+        if fused:
+            dp.fwd(*args, chunk=w.chunk, h0=d["h0"], kt=kk, out=out, final_state=fs, path="fused")
+            if ev is not None:
+                ev[2].record(stream)
+        else:
+            dp.fwd(*args, chunk=w.chunk, h0=d["h0"], kt=kk, out=out, final_state=fs, workspace=ws,
+                   stages=dp.STAGE_UT, path=split_flag)
+            if ev is not None:
+                ev[2].record(stream)
+            dp.fwd(*args, chunk=w.chunk, h0=d["h0"], kt=kk, out=out, final_state=fs, workspace=ws,
+                   stages=dp.STAGE_SCAN, path=split_flag)
         if ev is not None:
             ev[3].record(stream)
 
+    settled = settle_clocks(step, settle)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -241,7 +302,7 @@ def time_gpu(w, steps, warmup):
     scan_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / steps
     pre_ms = (sum(e[0].elapsed_time(e[1]) for e in evs) / steps) if w.asym else 0.0
     res = dict(elapsed=elapsed, ms_per_step=1e3 * elapsed / steps, ut_ms=ut_ms, scan_ms=scan_ms,
-               pre_ms=pre_ms, plan=plan, inputs=inp)
+               pre_ms=pre_ms, plan=plan, inputs=inp, fused=fused, settled=settled)
     if w.asym:
         # the same step as one pipelined call (phase 1 of a token run overlaps the
         # forward of the previous run); the per-kernel times above are the two-call path's
@@ -531,30 +592,40 @@ def main():
     from linear_rnn_sequence_amd.inputs import WORKLOADS
 
     w = WORKLOADS[a.workload]
-    r = time_gpu(w, a.steps, a.warmup)
+    r = time_gpu(w, a.steps, a.warmup, settle=a.settle)
     tokens = w.B * w.L
     value = tokens / (r["ms_per_step"] / 1e3)
     cf = chunk_flops(w)
     rf = recurrent_flops(w)
-    ut_issued, scan_issued = issued_flops(w, r["plan"])
     ab = alg_bytes(w)
     peak_mfma = FP32_PEAK_TFLOPS if w.dtype == "f32" else BF16_PEAK_TFLOPS
-    ut_name, scan_name = kernel_names(w)
-    kernels = {
-        ut_name: {"ms": r["ut_ms"], "issued_tflops": ut_issued / (r["ut_ms"] * 1e9),
-                  "workgroups": r["plan"]["ut_wgs"]},
-        scan_name: {"ms": r["scan_ms"], "issued_tflops": scan_issued / (r["scan_ms"] * 1e9),
-                    "workgroups": r["plan"]["scan_wgs"], "value_columns": r["plan"]["BV"]},
-    }
+    if r["fused"]:
+        fi = fused_issued_flops(w, r["plan"])
+        kernels = {"dp_fused_kernel": {"ms": r["ut_ms"], "issued_tflops": fi / (r["ut_ms"] * 1e9),
+                                       "issued_frac": fi / (r["ut_ms"] * 1e9) / peak_mfma,
+                                       "workgroups": r["plan"]["scan_wgs"],
+                                       "value_columns": r["plan"]["BV"]}}
+    else:
+        ut_issued, scan_issued = issued_flops(w, r["plan"])
+        ut_name, scan_name = kernel_names(w)
+        kernels = {
+            ut_name: {"ms": r["ut_ms"], "issued_tflops": ut_issued / (r["ut_ms"] * 1e9),
+                      "workgroups": r["plan"]["ut_wgs"]},
+            scan_name: {"ms": r["scan_ms"], "issued_tflops": scan_issued / (r["scan_ms"] * 1e9),
+                        "workgroups": r["plan"]["scan_wgs"], "value_columns": r["plan"]["BV"]},
+        }
     if w.asym:
         kernels["dp_precond_kernel"] = {"ms": r["pre_ms"],
                                         "gbs": precond_bytes(w) / (r["pre_ms"] * 1e6)}
 
-    # dominant kernel: the chunk scan streams every input and output of the forward
+    # dominant kernel and its own algorithmic bytes: the fused kernel (or, on the
+    # two-launch paths, the scan) reads every input and writes every output of
+    # the forward once; phase 1 reads k and beta and writes kt
     dom = max(kernels, key=lambda k: kernels[k]["ms"])
     dom_ms = kernels[dom]["ms"]
     dom_bytes = ab if dom != "dp_precond_kernel" else precond_bytes(w)
     achieved = dom_bytes / (dom_ms * 1e6)
+    step_bytes = ab + (precond_bytes(w) if w.asym else 0)
     line = {
         "metric": METRIC,
         "value": value,
@@ -578,8 +649,30 @@ def main():
         "kernels": kernels,
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(w.name, dom), "alg_bytes_per_launch": dom_bytes},
+                     "traffic": measured_traffic(w.name, dom), "alg_bytes_per_launch": dom_bytes,
+                     "step_achieved": step_bytes / (r["ms_per_step"] * 1e6),
+                     "step_frac": step_bytes / (r["ms_per_step"] * 1e6) / HBM_PEAK_GBS,
+                     "note": "achieved: the kernel's own algorithmic bytes over its event-timed "
+                             "duration; step_*: the whole step's algorithmic bytes over ms_per_step"},
+        "clock_settle": {"steps": r["settled"][0], "seconds": r["settled"][1],
+                         "note": "untimed steps run before the warm-up so that the timed steps see "
+                                 "settled clocks"},
     }
+    if fused_possible(w) and not a.no_other_path:
+        other = "split" if r["fused"] else "fused"
+        rs = time_gpu(w, a.steps, a.warmup, settle=min(a.settle, 0.3), path=other)
+        if other == "split":
+            line["other_path"] = {"path": "split (DP_FWD_SPLIT)", "ms_per_step": rs["ms_per_step"],
+                                  "dp_prep_kernel_ms": rs["ut_ms"], "dp_chain_kernel_ms": rs["scan_ms"],
+                                  "note": "the same workload on the two-kernel path: operand blocks "
+                                          "written to HBM by the prep kernel"}
+        else:
+            line["other_path"] = {"path": "fused (DP_FWD_FUSED)", "ms_per_step": rs["ms_per_step"],
+                                  "dp_fused_kernel_ms": rs["ut_ms"],
+                                  "note": "the same workload on the single fused kernel: every "
+                                          "value-column workgroup of a head builds the chunk's "
+                                          "operands itself"}
+        del rs
     if w.asym:
         line["pipeline"] = {"call": "dp_osdn_fwd_bf16", "segments": r["segments"],
                             "two_call_ms_per_step": r["two_call_ms_per_step"],
@@ -587,12 +680,15 @@ def main():
     also = {}
     for name in [x for x in a.also.split(",") if x and x != a.workload]:
         w2 = WORKLOADS[name]
-        r2 = time_gpu(w2, a.steps, a.warmup)
+        r2 = time_gpu(w2, a.steps, a.warmup, settle=min(a.settle, 0.3))
         also[name] = {"workload": describe(w2),
                       "value": w2.B * w2.L / (r2["ms_per_step"] / 1e3), "unit": "tokens/s",
                       "ms_per_step": r2["ms_per_step"],
-                      "mfma_tflops": chunk_flops(w2) / (r2["ms_per_step"] * 1e9),
-                      "ut_ms": r2["ut_ms"], "scan_ms": r2["scan_ms"]}
+                      "mfma_tflops": chunk_flops(w2) / (r2["ms_per_step"] * 1e9)}
+        if r2["fused"]:
+            also[name]["dp_fused_kernel_ms"] = r2["ut_ms"]
+        else:
+            also[name]["ut_ms"], also[name]["scan_ms"] = r2["ut_ms"], r2["scan_ms"]
         del r2
     if also:
         line["also"] = also

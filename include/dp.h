@@ -95,7 +95,8 @@ int dp_fwd_workspace_size(int n_h, int B, int H, int L, int dk, int dv, int chun
  * Launch plan the forward would use for these sizes (for measurement and
  * tuning; nothing is launched).  asym: 0 symmetric, 1 write-key variant.
  * info[0] = BV, the value columns per scan workgroup (16, 32 or 64)
- * info[1] = scan workgroups (B*H*dv/BV), info[2] = UT workgroups (chunks),
+ * info[1] = scan (or fused) workgroups (B*H*dv/BV), info[2] = UT workgroups
+ * (chunks; 0 when the default call runs the fused kernel),
  * info[3] = scan LDS bytes, info[4] = prep / UT LDS bytes, info[5] = readout rows
  * per chunk (padded to 16).  Returns DP_OK or a validation status.
  */
@@ -154,13 +155,33 @@ int dp_fwd_wk_bf16(const void* q, const void* k, const void* kt, const void* v,
  *   DP_STAGE_SCAN  run the chunk-scan launch (reads the workspace; writes out
  *                  and final_state)
  *   DP_OUT_F32     write `out` as float32 [B, L, H, dv] instead of T (bf16
- *                  path only; the fp32 path always writes float32)
- * At least one stage bit must be set.  DP_STAGE_UT then DP_STAGE_SCAN with
- * the same arguments is exactly one DP_STAGE_ALL call; DP_STAGE_SCAN alone
- * requires a workspace filled by DP_STAGE_UT for the same k, kt, beta, g
- * and sizes.  The stages exist for measurement and inspection.
+ *                  path only; the fp32 path always writes float32).  With bf16
+ *                  out the output carries the bf16 rounding of every element
+ *                  (relative 2^-9) on top of the fp32 accumulation: at long
+ *                  sequences with large state norms (L = 16384, H = 8) that
+ *                  rounding reaches ~2.5e-2 of max|out|, so callers that need
+ *                  the tighter figure ask for fp32 out
+ *   DP_FWD_SPLIT   symmetric bf16 keys: run the two-kernel path (a prep kernel
+ *                  writes each chunk's operand blocks to the workspace, a chain
+ *                  kernel reads them)
+ *   DP_FWD_FUSED   symmetric bf16 keys, dk and chunk multiples of 32, both
+ *                  stages: run the single fused kernel (each workgroup builds
+ *                  its chunk's operands in LDS; no workspace is read or written,
+ *                  and `workspace` may be NULL with workspace_bytes 0).
+ *                  DP_ENOTSUP where those conditions do not hold
+ * At least one stage bit must be set; DP_FWD_SPLIT with DP_FWD_FUSED is
+ * DP_EINVAL.  Without either, symmetric bf16 keys take the fused kernel where
+ * one workgroup holds all dv columns of a head (dv <= 32, dk and chunk
+ * multiples of 32, both stages) and the two-kernel path elsewhere; the
+ * workspace from dp_fwd_workspace_size covers both.  Both paths compute the
+ * same forward to within their rounding.  DP_STAGE_UT then DP_STAGE_SCAN with
+ * the same arguments is exactly one DP_STAGE_ALL call on the two-kernel path;
+ * DP_STAGE_SCAN alone requires a workspace filled by DP_STAGE_UT for the same
+ * k, kt, beta, g and sizes.  The stages exist for measurement and inspection.
  */
 #define DP_OUT_F32 4
+#define DP_FWD_SPLIT 8
+#define DP_FWD_FUSED 16
 
 int dp_fwd_ex_f32(const float* q, const float* k, const float* kt, const float* v,
                   const float* beta, const float* g, int n_h, int B, int H, int L, int dk,

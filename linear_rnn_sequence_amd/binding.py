@@ -15,7 +15,14 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdp.so")
 
 DP_OK, DP_EINVAL, DP_ENOTSUP, DP_EWORKSPACE, DP_EHIP = 0, -1, -2, -3, -4
-STAGE_UT, STAGE_SCAN, STAGE_ALL, OUT_F32 = 1, 2, 3, 4
+STAGE_UT, STAGE_SCAN, STAGE_ALL, OUT_F32, FWD_SPLIT, FWD_FUSED = 1, 2, 3, 4, 8, 16
+_PATH_FLAGS = {"auto": 0, "split": FWD_SPLIT, "fused": FWD_FUSED}
+
+
+def _path_flag(path):
+    if path not in _PATH_FLAGS:
+        raise ValueError(f"path must be one of {sorted(_PATH_FLAGS)}, not {path!r}")
+    return _PATH_FLAGS[path]
 PRECOND_BETA_FREE = 1
 
 # every symbol include/dp.h declares
@@ -170,14 +177,16 @@ def alloc_workspace(n_h, B, H, L, dk, dv, chunk, dtype, device) -> torch.Tensor:
 
 def fwd(q, k, v, beta, g=None, *, chunk: int = 64, h0=None, kt=None, out=None,
         final_state=None, return_state: bool = True, workspace=None,
-        stages: int = STAGE_ALL, out_dtype=None,
+        stages: int = STAGE_ALL, out_dtype=None, path: str = "auto",
         stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """DeltaProduct forward through libdp.
 
     q [B,L,H,dk], k [B,L,H,n_h,dk], v [B,L,H,n_h,dv] (float32 or bfloat16, one
     dtype), beta [B,L,H,n_h] f32, g [B,L,H] f32 or None, h0 [B,H,dk,dv] f32 or
     None, kt (write keys, shape of k) or None.  out_dtype: the input dtype
-    (default) or torch.float32.  Returns (out, final_state); final_state is
+    (default) or torch.float32.  path (bf16 symmetric keys): "auto" lets the
+    library choose, "split" runs the chunk-prep / chain kernel pair, "fused"
+    the single fused kernel (same results up to rounding).  Returns (out, final_state); final_state is
     None when return_state is False and none was passed.
     """
     if q.dim() != 4 or k.dim() != 5 or v.dim() != 5:
@@ -199,7 +208,7 @@ def fwd(q, k, v, beta, g=None, *, chunk: int = 64, h0=None, kt=None, out=None,
     odt = dt if out_dtype is None else out_dtype
     if odt not in (dt, torch.float32):
         raise TypeError(f"out_dtype must be {dt} or torch.float32")
-    flags = stages | (OUT_F32 if odt == torch.float32 else 0)
+    flags = stages | (OUT_F32 if odt == torch.float32 else 0) | _path_flag(path)
     if out is None:
         out = torch.empty(B, L, H, dv, dtype=odt, device=dev)
     _need(out, "out", odt, (B, L, H, dv), dev)
@@ -355,12 +364,12 @@ def varlen_workspace_size(n_h, nseq, H, T, dk, dv, chunk) -> int:
 
 def fwd_varlen(q, k, v, beta, cu_seqlens, g=None, *, chunk: int = 64, h0=None, out=None,
                final_state=None, return_state: bool = True, workspace=None,
-               stages: int = STAGE_ALL, out_dtype=None, stream=None):
+               stages: int = STAGE_ALL, out_dtype=None, path: str = "auto", stream=None):
     """Packed variable-length forward (bf16, symmetric keys) through libdp.
 
     q [T,H,dk], k [T,H,n_h,dk], v [T,H,n_h,dv] bfloat16, beta [T,H,n_h] f32,
     g [T,H] f32 or None, cu_seqlens [nseq+1] int32 on the device, h0
-    [nseq,H,dk,dv] f32 or None.  Returns (out [T,H,dv], final_state).
+    [nseq,H,dk,dv] f32 or None.  path as for fwd.  Returns (out [T,H,dv], final_state).
     """
     if q.dim() != 3 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("expected q[T,H,dk], k[T,H,n_h,dk], v[T,H,n_h,dv]")
@@ -385,7 +394,7 @@ def fwd_varlen(q, k, v, beta, cu_seqlens, g=None, *, chunk: int = 64, h0=None, o
     odt = dt if out_dtype is None else out_dtype
     if odt not in (dt, torch.float32):
         raise TypeError(f"out_dtype must be {dt} or torch.float32")
-    flags = stages | (OUT_F32 if odt == torch.float32 else 0)
+    flags = stages | (OUT_F32 if odt == torch.float32 else 0) | _path_flag(path)
     if out is None:
         out = torch.empty(T, H, dv, dtype=odt, device=dev)
     _need(out, "out", odt, (T, H, dv), dev)

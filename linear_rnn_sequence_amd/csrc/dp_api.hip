@@ -171,8 +171,46 @@ int pick_bv16(int BH, int dv) {
   return 16;
 }
 
-// Choose BV and fill the scan layout of `a` (a.RT and a.asym must be set).
+// Can this call run the fused kernel?  bf16, symmetric keys, dk and chunk
+// multiples of 32 and both stages in one call.
+bool fused_possible(int elem, bool asym, int dk, int chunk, int flags) {
+  return elem == 2 && !asym && dp::fused_ok(dk, chunk) && (flags & DP_STAGE_ALL) == DP_STAGE_ALL;
+}
+
+// Does it?  Each workgroup of the fused kernel builds its chunk's operands
+// itself, so a head split over several workgroups (value-column blocks) builds
+// them once per block; the prep / chain pair builds them once per chunk and
+// is faster there.  The fused kernel is the default only where one workgroup
+// holds all dv columns of a head (dv <= 32); DP_FWD_SPLIT and DP_FWD_FUSED
+// override the choice.
+bool use_fused(int elem, bool asym, int dk, int dv, int chunk, int flags) {
+  if (!fused_possible(elem, asym, dk, chunk, flags) || (flags & DP_FWD_SPLIT) != 0) return false;
+  return (flags & DP_FWD_FUSED) != 0 || dv <= 32;
+}
+
+// Flag checks shared by the forward entry points: known bits, one stage at
+// least, not both path overrides, and a forced fused path only where it exists.
+int check_fwd_flags(int elem, bool asym, int dk, int chunk, int flags) {
+  if ((flags & ~(DP_STAGE_ALL | DP_OUT_F32 | DP_FWD_SPLIT | DP_FWD_FUSED)) != 0) return DP_EINVAL;
+  if ((flags & DP_STAGE_ALL) == 0) return DP_EINVAL;
+  if ((flags & DP_FWD_SPLIT) != 0 && (flags & DP_FWD_FUSED) != 0) return DP_EINVAL;
+  if ((flags & DP_FWD_FUSED) != 0 && !fused_possible(elem, asym, dk, chunk, flags)) return DP_ENOTSUP;
+  return DP_OK;
+}
+
+// Choose BV and fill the scan layout of `a` (a.RT, a.asym and a.fused must be set).
 int plan(dp::FwdArgs& a, int elem, int dk, int chunk, int* BV_out, int* lds_out) {
+  if (a.fused) {
+    // one or two consumer wavefronts: all of dv up to 32 columns in one workgroup
+    int BV = a.dv <= 32 ? a.dv : pick_bv16(a.B * a.H, a.dv);
+    if (BV > 32) BV = 32;
+    while (dp::fused_layout(dk, chunk, a.RT, BV).bytes > kMaxLds && BV > 16) BV >>= 1;
+    if (dp::fused_layout(dk, chunk, a.RT, BV).bytes > kMaxLds) return DP_ENOTSUP;
+    a.nvb = a.dv / BV;
+    *BV_out = BV;
+    *lds_out = dp::fused_layout(dk, chunk, a.RT, BV).bytes;
+    return DP_OK;
+  }
   if (elem == 2 && !a.asym) {
     int BV = pick_bv16(a.B * a.H, a.dv);
     while (dp::chain_lds_bytes(dk, chunk, a.RT, BV) > kMaxLds && BV > 16) BV >>= 1;
@@ -259,17 +297,18 @@ int fwd_impl(int elem, const void* q, const void* k, const void* kt, const void*
   const Shape s{n_h, B, H, L, dk, dv, chunk};
   int rc = check_shape(s);
   if (rc != DP_OK) return rc;
-  if ((flags & ~(DP_STAGE_ALL | DP_OUT_F32)) != 0) return DP_EINVAL;
+  rc = check_fwd_flags(elem, kt != nullptr, dk, chunk, flags);
+  if (rc != DP_OK) return rc;
   const int stages = flags & DP_STAGE_ALL;
-  if (stages == 0) return DP_EINVAL;
   // with L == 0 the per-token tensors are empty and may be null
   if (L > 0 && (q == nullptr || k == nullptr || v == nullptr || beta == nullptr || out == nullptr))
     return DP_EINVAL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (kt != nullptr && !aligned16(kt)))
     return DP_EINVAL;
-  const size_t need = ws_total(s, elem);
+  const bool fused = use_fused(elem, kt != nullptr, dk, dv, chunk, flags);
+  const size_t need = fused ? 0 : ws_total(s, elem);
   if (workspace_bytes < need || (need > 0 && workspace == nullptr)) return DP_EWORKSPACE;
-  if (((uintptr_t)workspace & (kWsAlign - 1)) != 0) return DP_EWORKSPACE;
+  if (need > 0 && ((uintptr_t)workspace & (kWsAlign - 1)) != 0) return DP_EWORKSPACE;
 
   dp::FwdArgs a;
   memset(&a, 0, sizeof(a));
@@ -282,9 +321,11 @@ int fwd_impl(int elem, const void* q, const void* k, const void* kt, const void*
   a.h0 = h0;
   a.out = out;
   a.fstate = final_state;
-  a.wsT = workspace;
-  a.wsS = reinterpret_cast<float2*>(static_cast<char*>(workspace) + ws_t_bytes(s, elem));
-  if (elem == 2) a.sink = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws_blocks_bytes(s));
+  if (!fused) {
+    a.wsT = workspace;
+    a.wsS = reinterpret_cast<float2*>(static_cast<char*>(workspace) + ws_t_bytes(s, elem));
+    if (elem == 2) a.sink = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws_blocks_bytes(s));
+  }
   a.N = L * n_h;
   a.B = B;
   a.H = H;
@@ -297,6 +338,7 @@ int fwd_impl(int elem, const void* q, const void* k, const void* kt, const void*
   a.out_f32 = (elem == 4 || (flags & DP_OUT_F32) != 0) ? 1 : 0;
   a.Ls = Ls;
   a.t0 = t0;
+  a.fused = fused ? 1 : 0;
   fastdiv_magic(n_h, &a.nh_magic, &a.nh_shift);
 
   int BV = 0, lds = 0;
@@ -345,6 +387,8 @@ size_t varlen_ws_total(const VarShape& v) {
   return varlen_blocks_bytes(v) + varlen_cbase_bytes(v) +
          align_up((size_t)v.nseq * v.H * (v.dv / 16) * 64 * 4, kWsAlign);
 }
+// the fused kernel needs only the per-sequence first chunks
+size_t varlen_ws_need(const VarShape& v, bool fused) { return fused ? varlen_cbase_bytes(v) : varlen_ws_total(v); }
 
 int varlen_impl(const void* q, const void* k, const void* v, const float* beta, const float* g,
                 const int* cu_seqlens, int nseq, int n_h, int H, int T, int dk, int dv, int chunk,
@@ -353,14 +397,15 @@ int varlen_impl(const void* q, const void* k, const void* v, const float* beta, 
   const VarShape vs{n_h, nseq, H, T, dk, dv, chunk};
   int rc = check_varlen(vs);
   if (rc != DP_OK) return rc;
-  if ((flags & ~(DP_STAGE_ALL | DP_OUT_F32)) != 0) return DP_EINVAL;
+  rc = check_fwd_flags(2, false, dk, chunk, flags);
+  if (rc != DP_OK) return rc;
   const int stages = flags & DP_STAGE_ALL;
-  if (stages == 0) return DP_EINVAL;
   if (cu_seqlens == nullptr) return DP_EINVAL;
   if (T > 0 && (q == nullptr || k == nullptr || v == nullptr || beta == nullptr || out == nullptr))
     return DP_EINVAL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return DP_EINVAL;
-  const size_t need = varlen_ws_total(vs);
+  const bool fused = use_fused(2, false, dk, dv, chunk, flags);
+  const size_t need = varlen_ws_need(vs, fused);
   if (workspace_bytes < need || workspace == nullptr) return DP_EWORKSPACE;
   if (((uintptr_t)workspace & (kWsAlign - 1)) != 0) return DP_EWORKSPACE;
 
@@ -374,11 +419,16 @@ int varlen_impl(const void* q, const void* k, const void* v, const float* beta, 
   a.h0 = h0;
   a.out = out;
   a.fstate = final_state;
-  a.wsT = workspace;
   a.cu = cu_seqlens;
-  a.cbase = reinterpret_cast<int*>(static_cast<char*>(workspace) + varlen_blocks_bytes(vs));
-  a.sink = reinterpret_cast<float*>(static_cast<char*>(workspace) + varlen_blocks_bytes(vs) +
-                                    varlen_cbase_bytes(vs));
+  if (fused) {
+    a.cbase = static_cast<int*>(workspace);
+  } else {
+    a.wsT = workspace;
+    a.cbase = reinterpret_cast<int*>(static_cast<char*>(workspace) + varlen_blocks_bytes(vs));
+    a.sink = reinterpret_cast<float*>(static_cast<char*>(workspace) + varlen_blocks_bytes(vs) +
+                                      varlen_cbase_bytes(vs));
+  }
+  a.fused = fused ? 1 : 0;
   a.nwork = (int)varlen_nwork(vs);
   a.B = nseq;
   a.H = H;
@@ -661,14 +711,15 @@ int dp_fwd_launch_info(int n_h, int B, int H, int L, int dk, int dv, int chunk, 
   a.dv = dv;
   a.RT = readout_rows(chunk, n_h);
   a.asym = asym;
+  a.fused = use_fused(elem_bytes, asym != 0, dk, dv, chunk, DP_STAGE_ALL) ? 1 : 0;
   int BV = 0, lds = 0;
   const int prc = plan(a, elem_bytes, dk, chunk, &BV, &lds);
   if (prc != DP_OK) return prc;
   info[0] = BV;
   info[1] = B * H * a.nvb;
-  info[2] = B * H * num_chunks(s);
+  info[2] = a.fused ? 0 : B * H * num_chunks(s);
   info[3] = lds;
-  info[4] = (elem_bytes == 2 && !asym) ? dp::prep_lds_bytes(dk, chunk, a.RT) : ut_lds(elem_bytes, dk, chunk, asym);
+  info[4] = a.fused ? 0 : (elem_bytes == 2 && !asym) ? dp::prep_lds_bytes(dk, chunk, a.RT) : ut_lds(elem_bytes, dk, chunk, asym);
   info[5] = a.RT;
   return DP_OK;
 }

@@ -93,6 +93,9 @@ struct FwdArgs {
   // scan kernels of the fixed-length paths): token t of batch row b is row
   // (b Ls + t0 + t) of the token-major tensors.  Ls = 0: Ls = L, t0 = 0.
   int Ls = 0, t0 = 0;
+  // bf16 with symmetric keys: 1 runs the single fused kernel (dp_fused.hpp),
+  // 0 the chunk-prep kernel then the chain kernel with operand blocks in HBM
+  int fused = 0;
   // dp_scan_kernel LDS byte offsets
   int oK, oKt, oQ, oT, oHt, oXt, oUo, oUs, oP, oV, oG, oEG, oEL, oLoc, oRow, oTok;
 };
@@ -1399,6 +1402,7 @@ inline bool allow_big_lds(const void* fn) {
 }  // namespace dp
 
 #include "dp_fwd16.hpp"
+#include "dp_fused.hpp"
 #include "dp_decode.hpp"
 
 namespace dp {
@@ -1521,6 +1525,14 @@ hipError_t launch_chain(const FwdArgs& a, hipStream_t st) {
 
 template <int DK, int C, int NRT>
 hipError_t launch_sym16_nrt(const FwdArgs& a, int BV, int stages, hipStream_t st) {
+  if (a.fused) {
+    if (a.cu != nullptr) {  // packed sequences: per-sequence chunk counts first
+      hipLaunchKernelGGL((dp_varlen_chunks_kernel<C>), dim3(1), dim3(256), 0, st, a.cu, a.B, a.n_h, a.L, a.cbase);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    return launch_fused<DK, C, NRT>(a, BV, st);
+  }
   if (stages & 1) {
     const hipError_t e = launch_prep<DK, C, NRT>(a, st);
     if (e != hipSuccess) return e;

@@ -137,7 +137,14 @@ def test_fwd_validation_errors_before_hip(lib, suffix):
     assert fwd_call(lib, suffix, n_h=100) == E.DP_ENOTSUP
     assert fwd_call(lib, suffix, stages=0) == E.DP_EINVAL
     assert fwd_call(lib, suffix, stages=4) == E.DP_EINVAL            # no stage bit
-    assert fwd_call(lib, suffix, stages=8 | 3) == E.DP_EINVAL        # unknown flag
+    assert fwd_call(lib, suffix, stages=32 | 3) == E.DP_EINVAL       # unknown flag
+    assert fwd_call(lib, suffix, stages=8 | 16 | 3) == E.DP_EINVAL   # both path overrides
+    # the fused kernel exists for bf16, symmetric keys, dk and chunk multiples of 32, both stages
+    assert fwd_call(lib, suffix, stages=16 | 3) == E.DP_ENOTSUP
+    assert fwd_call(lib, suffix, stages=16 | 1, dk=32, chunk=32) == E.DP_ENOTSUP
+    assert fwd_call(lib, suffix, stages=16 | 3, dk=32, chunk=32, kt=FAKE) == E.DP_ENOTSUP
+    if suffix == "f32":
+        assert fwd_call(lib, suffix, stages=16 | 3, dk=32, chunk=32) == E.DP_ENOTSUP
     assert fwd_call(lib, suffix, wsb=16) == E.DP_EWORKSPACE           # too small
     assert fwd_call(lib, suffix, wsp=None) == E.DP_EWORKSPACE         # missing
     assert fwd_call(lib, suffix, wsp=FAKE + 16) == E.DP_EWORKSPACE    # misaligned
@@ -255,7 +262,9 @@ def test_varlen_validation_errors_before_hip(lib):
     assert call(q=None) == E.DP_EINVAL
     assert call(q=FAKE + 8) == E.DP_EINVAL
     assert call(flags=0) == E.DP_EINVAL
-    assert call(flags=8 | 3) == E.DP_EINVAL
+    assert call(flags=32 | 3) == E.DP_EINVAL
+    assert call(flags=8 | 16 | 3) == E.DP_EINVAL
+    assert call(flags=16 | 3) == E.DP_ENOTSUP    # dk 16: no fused kernel
     assert call(dk=24) == E.DP_ENOTSUP
     assert call(chunk=8) == E.DP_ENOTSUP
     assert call(wsb=16) == E.DP_EWORKSPACE
@@ -277,3 +286,20 @@ def test_packed_lengths_cover_the_batch_exactly():
     from linear_rnn_sequence_amd.inputs import packed_lengths
     ls = packed_lengths(65536, seed=5)
     assert sum(ls) == 65536 and min(ls) >= 1 and max(ls) <= 8192 and len(ls) > 20
+
+
+def test_launch_info_reports_the_default_path(lib):
+    """Symmetric bf16 keys take the fused kernel (no UT workgroups, one workgroup
+    per head) where dv <= 32, and the prep / chain pair where a head's dv columns
+    would span several workgroups; fp32 and write keys always take two kernels."""
+    info = (ctypes.c_int * 6)()
+    assert lib.dp_fwd_launch_info(2, 8, 32, 2048, 128, 32, 64, 2, 0, info) == 0
+    assert info[2] == 0 and info[0] == 32 and info[1] == 8 * 32
+    assert lib.dp_fwd_launch_info(2, 1, 4, 256, 64, 16, 32, 2, 0, info) == 0
+    assert info[2] == 0 and info[0] == 16 and info[1] == 4
+    assert lib.dp_fwd_launch_info(3, 8, 16, 4096, 128, 128, 64, 2, 0, info) == 0
+    assert info[2] > 0 and info[1] == 8 * 16 * (128 // info[0])
+    assert lib.dp_fwd_launch_info(2, 8, 32, 2048, 128, 32, 64, 4, 0, info) == 0
+    assert info[2] > 0
+    assert lib.dp_fwd_launch_info(2, 8, 32, 2048, 128, 32, 64, 2, 1, info) == 0
+    assert info[2] > 0

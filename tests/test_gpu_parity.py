@@ -152,6 +152,10 @@ def test_resume_split_equals_single_call(dtype):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_staged_equals_single_launch_and_is_deterministic(dtype):
+    """The default call is deterministic; the two-launch path (prep / UT kernel,
+    then the scan) run as two staged calls equals the same path in one call.
+    On the bf16 path with symmetric keys the fused kernel is a different
+    summation order: it is checked against the oracle."""
     w = WORKLOADS["c3"].scaled(B=1, H=3, L=123, dtype=dtype)
     inp = make(w)
     d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
@@ -159,11 +163,49 @@ def test_staged_equals_single_launch_and_is_deterministic(dtype):
     args = (d["q"], d["k"], d["v"], d["beta"], d["g"])
     o_all, f_all = dp.fwd(*args, chunk=w.chunk, workspace=ws)
     o_all2, f_all2 = dp.fwd(*args, chunk=w.chunk, workspace=ws)
+    o_sp, f_sp = dp.fwd(*args, chunk=w.chunk, workspace=ws, path="split")
+    o_fu = f_fu = None
+    if dtype == "bf16":
+        o_fu, f_fu = dp.fwd(*args, chunk=w.chunk, workspace=ws, path="fused")
     dp.fwd(*args, chunk=w.chunk, workspace=ws, stages=dp.STAGE_UT)
     o_st, f_st = dp.fwd(*args, chunk=w.chunk, workspace=ws, stages=dp.STAGE_SCAN)
     torch.cuda.synchronize()
     assert torch.equal(o_all, o_all2) and torch.equal(f_all, f_all2)
-    assert torch.equal(o_all, o_st) and torch.equal(f_all, f_st)
+    assert torch.equal(o_sp, o_st) and torch.equal(f_sp, f_st)
+    oo, fo = oracle.fwd(inp["q"], inp["k"], inp["v"], inp["beta"], g=inp["g"], h0=inp["h0"])
+    res = dict(out=(f64(o_all), oo), fs=(f64(f_all), fo), out_split=(f64(o_sp), oo), fs_split=(f64(f_sp), fo))
+    if o_fu is not None:
+        res.update(out_fused=(f64(o_fu), oo), fs_fused=(f64(f_fu), fo))
+    check(res, TOL[dtype], f"staged/{dtype}")
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("c2", dict(B=2, H=3, L=203)), ("c3", dict(B=1, H=3, L=150)), ("c3b", dict(B=2, H=2, L=161)),
+    ("c4", dict(B=2, H=2, L=300)), ("c3", dict(B=1, H=2, L=150, n_h=1)), ("c3", dict(B=1, H=2, L=99, n_h=5)),
+    ("c4", dict(B=1, H=3, L=200, dk=32, dv=64)), ("c4", dict(B=1, H=2, L=200, dk=128, dv=32, chunk=32)),
+    ("c3", dict(B=1, H=2, L=77, dk=64, dv=16, chunk=32, n_h=1)),
+])
+def test_fused_and_split_paths_agree(name, kw):
+    """The fused kernel (DP_FWD_FUSED) and the prep / chain pair (DP_FWD_SPLIT)
+    are two schedules of the same chunk form: both meet the bound against the
+    oracle, across head dims 32..128, chunk 32 and 64, n_h 1..5, gate and h0,
+    and the default call equals one of them bit for bit."""
+    w = WORKLOADS[name].scaled(**kw)
+    say(f"case fused-vs-split {name} {kw}")
+    inp = make(w)
+    d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    odt = inp.get("out_dtype")
+    res = {}
+    for path in ("fused", "split", "auto"):
+        o, f = dp.fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], chunk=w.chunk, h0=d["h0"],
+                      out_dtype=odt, path=path)
+        torch.cuda.synchronize()
+        res[path] = (f64(o), f64(f))
+    auto = "fused" if w.dv <= 32 else "split"
+    assert np.array_equal(res["auto"][0], res[auto][0]) and np.array_equal(res["auto"][1], res[auto][1])
+    oo, fo = oracle.fwd(inp["q"], inp["k"], inp["v"], inp["beta"], g=inp["g"], h0=inp["h0"])
+    check(dict(out=(res["fused"][0], oo), fs=(res["fused"][1], fo), out_split=(res["split"][0], oo),
+               fs_split=(res["split"][1], fo)), TOL["bf16"], f"{name}")
 
 
 def test_out_f32_flag_is_the_unrounded_output():
@@ -308,9 +350,13 @@ def test_errors_surface_as_exceptions():
     w = WORKLOADS["c2"].scaled(B=1, H=1, L=8)
     d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in make(w).items()}
     tiny = torch.empty(16, dtype=torch.uint8, device="cuda")
+    # the two-kernel path keeps its operand blocks in the workspace
     with pytest.raises(dp.DPError) as ei:
-        dp.fwd(d["q"], d["k"], d["v"], d["beta"], chunk=64, workspace=tiny)
+        dp.fwd(d["q"], d["k"], d["v"], d["beta"], chunk=64, workspace=tiny, path="split")
     assert ei.value.code == dp.binding.DP_EWORKSPACE
+    # the fused kernel needs none
+    dp.fwd(d["q"], d["k"], d["v"], d["beta"], chunk=64, workspace=tiny, path="fused")
+    torch.cuda.synchronize()
     with pytest.raises(dp.DPError):
         dp.fwd(d["q"], d["k"], d["v"], d["beta"], chunk=48)
 
