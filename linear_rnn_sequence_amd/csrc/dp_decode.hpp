@@ -91,7 +91,7 @@ __global__ __launch_bounds__(512) void dp_decode_kernel(DecodeArgs p) {
   for (int x = tid; x < DK; x += NTH) sQ[x] = to_f32(qp[x]);
   const T* vp = static_cast<const T*>(p.v) + bh * n_h * p.dv + (col - cl);
   for (int x = tid; x < n_h * CW; x += NTH) sV[x] = to_f32(vp[(long long)(x / CW) * p.dv + x % CW]);
-  for (int j = tid; j < n_h; j += NTH) sB[j] = fminf(fmaxf(p.beta[bh * n_h + j], 0.f), 2.f);
+  for (int j = tid; j < n_h; j += NTH) sB[j] = clamp_keep_nan(p.beta[bh * n_h + j], 0.f, 2.f);
   const float gt = p.g != nullptr ? p.g[bh] : 1.f;
   block_sync_lds();
 

@@ -120,6 +120,25 @@ def test_decode_gate_zero_and_beta_zero(dtype):
     assert torch.allclose(st[0, 2:].cpu(), s0[0, 2:] * g, rtol=1e-6, atol=1e-7)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_nan_beta_propagates(dtype):
+    """A NaN beta is not clamped away: the head it belongs to ends with a NaN
+    state and output (the oracle's clamp keeps it too), the other heads are
+    untouched by it and match the oracle."""
+    w = WORKLOADS["c3"].scaled(B=1, H=4, L=1, dk=64, dv=64, dtype=dtype)
+    inp = make(w)
+    inp["beta"][0, 0, 1, 0] = float("nan")
+    s0 = torch.randn(1, 4, 64, 64, generator=torch.Generator().manual_seed(4)) * 0.2
+    st = s0.clone().cuda()
+    out = decode_token(inp, 0, st, out_dtype=torch.float32)
+    assert torch.isnan(out[0, 1]).all() and torch.isnan(st[0, 1]).all()
+    oo, fo = oracle.fwd(inp["q"], inp["k"], inp["v"], inp["beta"], h0=s0)
+    assert np.isnan(fo[0, 1]).all()
+    keep = [0, 2, 3]
+    check(dict(out=(f64(out)[:, keep], oo[:, 0][:, keep]), state=(f64(st)[:, keep], fo[:, keep])),
+          TOL[dtype], f"nan-beta/{dtype}")
+
+
 def test_decode_max_sub_steps():
     """n_h = 64 (the largest supported), fp32."""
     w = WORKLOADS["c2"].scaled(B=1, H=2, L=1, n_h=64, dk=128, dv=64, dtype="f32")
