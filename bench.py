@@ -312,11 +312,12 @@ def time_gpu(w, steps, warmup, settle=0.0, path="auto"):
                           dtype=torch.uint8, device=dev)
         fs2 = torch.empty_like(fs)
         out2 = torch.empty_like(out)
+        pipe = dp.Pipeline()
 
         def pstep():
             dstate.copy_(d1)
             dp.osdn_fwd(q, kk, vv, b1, chunk=w.chunk, segments=S, d_state=dstate, kt=kt, out=out2,
-                        final_state=fs2, workspace=pws)
+                        final_state=fs2, workspace=pws, pipeline=pipe)
 
         for _ in range(warmup):
             pstep()
@@ -326,6 +327,7 @@ def time_gpu(w, steps, warmup, settle=0.0, path="auto"):
             pstep()
         torch.cuda.synchronize()
         pel = time.perf_counter() - t0
+        pipe.close()
         res["two_call_ms_per_step"] = res["ms_per_step"]
         res["elapsed"], res["ms_per_step"], res["segments"] = pel, 1e3 * pel / steps, S
     return res

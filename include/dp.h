@@ -234,14 +234,31 @@ int dp_osdn_precond_ex_bf16(const void* k, const float* beta, const float* r, in
                             int H, int L, int dk, float eta, float dmin, float dmax, float eps,
                             float* d_state, void* kt, dp_stream stream);
 
+/*
+ * Pipeline handle for dp_osdn_fwd_bf16: a second stream on one device (non-
+ * blocking, default priority) and the events that order it against the
+ * caller's stream.  dp_pipeline_create makes one on the current device and
+ * returns DP_OK, DP_EINVAL for a NULL `out`, or DP_EHIP (nothing is then
+ * left allocated).  The caller owns it: dp_pipeline_destroy waits for the
+ * work enqueued on its stream, then releases it (NULL is a no-op).  Calls
+ * that use one handle are serialised on its stream and may come from several
+ * host threads (each call holds the handle for its enqueue sequence); calls
+ * that should overlap in time use handles of their own.
+ */
+typedef struct dp_pipeline_s* dp_pipeline;
+int dp_pipeline_create(dp_pipeline* out);
+int dp_pipeline_destroy(dp_pipeline pipe);
+
 /* OSDN phase 1 and the write-key forward in one call, pipelined over token
  * segments (OSDN notes sec. 2.4 Alg. 1 for phase 1, sec. 2.5 for phase 2; the
  * DeltaProduct notes sec. 2.2 and 2.6 for the recurrence, with n_h = 1).
  * Computes exactly what dp_osdn_precond_bf16 followed by dp_fwd_wk_bf16 with
  * the emitted write keys computes (the same kernels, the same chunks), but the
  * sequence is cut into `segments` runs of whole chunks: while the forward of
- * one run proceeds on a second stream of the device, phase 1 already scans the
- * next run on `stream`.  On return `stream` waits for both.
+ * one run proceeds on the second stream of `pipe`, phase 1 already scans the
+ * next run on `stream`, and `stream` waits for both at the end.  With pipe ==
+ * NULL the runs go one after another on `stream` (no overlap; the same
+ * results bit for bit).
  *   q [B,L,H,dk], k [B,L,H,dk] (raw read keys), v [B,L,H,dv]  bf16
  *   beta [B,L,H] f32;  h0 [B,H,dk,dv] f32 or NULL (zero)
  *   eta, dmin, dmax, eps: the phase-1 constants (3e-3, 0.5, 2, 1e-6)
@@ -252,16 +269,19 @@ int dp_osdn_precond_ex_bf16(const void* k, const float* beta, const float* r, in
  *   makes more than one run, and may alias h0)
  *   workspace: dp_osdn_fwd_workspace_size() bytes (one run's forward), 256-byte aligned
  *   segments: 1 .. 16 (runs of ceil(ceil(L / segments) / chunk) chunks)
- * Calls on one device must not overlap in time: they share the second stream.
- * Errors: those of the two calls it replaces; DP_EINVAL for segments outside
- * 1 .. 16 or a NULL final_state with several runs; DP_EHIP when the second
- * stream cannot be made. */
+ *   pipe: a handle from dp_pipeline_create on the current device, or NULL
+ * Every argument of every run is checked before the first run is enqueued:
+ * on failure nothing is enqueued and d_state, kt, out and final_state are
+ * untouched.  Errors: those of the two calls it replaces; DP_EINVAL for
+ * segments outside 1 .. 16, a NULL final_state with several runs, or a
+ * handle made on another device; DP_EHIP when a HIP call fails (runs already
+ * enqueued then stay enqueued). */
 int dp_osdn_fwd_workspace_size(int B, int H, int L, int dk, int dv, int chunk, int segments,
                                size_t* bytes);
 int dp_osdn_fwd_bf16(const void* q, const void* k, const void* v, const float* beta, const float* h0,
                      int B, int H, int L, int dk, int dv, int chunk, float eta, float dmin, float dmax,
                      float eps, float* d_state, void* kt, void* out, float* final_state, void* workspace,
-                     size_t workspace_bytes, int segments, dp_stream stream);
+                     size_t workspace_bytes, int segments, dp_pipeline pipe, dp_stream stream);
 
 /*
  * Packed variable-length sequences, bf16 with symmetric keys (DeltaProduct

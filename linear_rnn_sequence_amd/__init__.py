@@ -1,7 +1,7 @@
 """MI355X-native (gfx950) DeltaProduct forward: hand-written HIP kernels
 behind a C ABI (include/dp.h, libdp.so), with a thin ctypes binding."""
 from .binding import (  # noqa: F401
-    DPError, EXPORTS, STAGE_ALL, STAGE_SCAN, STAGE_UT, alloc_workspace, bwd, bwd_workspace_size, decode, fwd,
+    DPError, EXPORTS, Pipeline, STAGE_ALL, STAGE_SCAN, STAGE_UT, alloc_workspace, bwd, bwd_workspace_size, decode, fwd,
     fwd_varlen, launch_info, load,
     osdn_fwd, osdn_fwd_workspace_size, osdn_precond, status_str, varlen_workspace_size, workspace_size,
 )

@@ -35,7 +35,7 @@ EXPORTS = (
     "dp_osdn_precond_ex_f32", "dp_osdn_precond_ex_bf16",
     "dp_fwd_varlen_workspace_size", "dp_fwd_varlen_bf16",
     "dp_bwd_workspace_size", "dp_bwd_f32", "dp_bwd_bf16",
-    "dp_osdn_fwd_workspace_size", "dp_osdn_fwd_bf16",
+    "dp_osdn_fwd_workspace_size", "dp_osdn_fwd_bf16", "dp_pipeline_create", "dp_pipeline_destroy",
 )
 
 _lib = None
@@ -104,7 +104,11 @@ def load() -> ctypes.CDLL:
         lib.dp_osdn_fwd_workspace_size.argtypes = [_I] * 7 + [ctypes.POINTER(ctypes.c_size_t)]
         lib.dp_osdn_fwd_bf16.restype = _I
         lib.dp_osdn_fwd_bf16.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _F, _F, _F, _P, _P,
-                                         _P, _P, _P, ctypes.c_size_t, _I, _P]
+                                         _P, _P, _P, ctypes.c_size_t, _I, _P, _P]
+        lib.dp_pipeline_create.restype = _I
+        lib.dp_pipeline_create.argtypes = [ctypes.POINTER(_P)]
+        lib.dp_pipeline_destroy.restype = _I
+        lib.dp_pipeline_destroy.argtypes = [_P]
         _lib = lib
     return _lib
 
@@ -272,12 +276,40 @@ def osdn_fwd_workspace_size(B, H, L, dk, dv, chunk, segments) -> int:
     return n.value
 
 
+class Pipeline:
+    """A dp_pipeline: the second stream and events that let :func:`osdn_fwd`
+    overlap phase 1 of one token run with the forward of the previous one.
+    Made on the current device; released by close() or when collected."""
+
+    def __init__(self):
+        h = _P()
+        _check(load().dp_pipeline_create(ctypes.byref(h)), "dp_pipeline_create")
+        self._h = h
+
+    @property
+    def handle(self):
+        return self._h
+
+    def close(self):
+        if self._h is not None and self._h.value is not None:
+            h, self._h = self._h, None
+            _check(load().dp_pipeline_destroy(h), "dp_pipeline_destroy")
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
 def osdn_fwd(q, k, v, beta, *, h0=None, chunk: int = 64, segments: int = 4, eta: float = 3e-3,
              dmin: float = 0.5, dmax: float = 2.0, eps: float = 1e-6, d_state=None, kt=None, out=None,
-             final_state=None, workspace=None, stream=None):
+             final_state=None, workspace=None, pipeline: Optional[Pipeline] = None, stream=None):
     """OSDN phase 1 and the write-key forward in one call (dp_osdn_fwd_bf16),
-    pipelined over `segments` token runs: q, k [B,L,H,dk], v [B,L,H,dv] bf16,
-    beta [B,L,H] f32.  d_state [B,H,dk] is d_1 on entry (default ones).
+    cut into `segments` token runs: q, k [B,L,H,dk], v [B,L,H,dv] bf16,
+    beta [B,L,H] f32.  d_state [B,H,dk] is d_1 on entry (default ones).  With a
+    :class:`Pipeline` the runs overlap (phase 1 of a run beside the forward of
+    the previous one); without one they run in order on `stream`.
     Returns (out [B,L,H,dv], final_state [B,H,dk,dv], kt [B,L,H,dk], d_state)."""
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("expected q[B,L,H,dk], k[B,L,H,dk], v[B,L,H,dv]")
@@ -308,7 +340,7 @@ def osdn_fwd(q, k, v, beta, *, h0=None, chunk: int = 64, segments: int = 4, eta:
     rc = load().dp_osdn_fwd_bf16(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(h0), B, H, L, dk, dv, chunk,
                                  eta, dmin, dmax, eps, _ptr(d_state), _ptr(kt), _ptr(out), _ptr(final_state),
                                  _ptr(workspace), workspace.numel() * workspace.element_size(), segments,
-                                 _stream(stream))
+                                 None if pipeline is None else pipeline.handle, _stream(stream))
     _check(rc, "dp_osdn_fwd_bf16")
     return out, final_state, kt, d_state
 

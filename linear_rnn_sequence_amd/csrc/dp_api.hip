@@ -2,8 +2,10 @@
 //
 // Every entry point validates its arguments on the host before touching the
 // HIP runtime, then enqueues the kernels of dp_kernels.hpp on the caller's
-// stream and returns.  The library allocates nothing and keeps no state.
+// stream and returns.  The library allocates no device memory for a call and
+// keeps no state between calls (a dp_pipeline is the caller's object).
 #include <mutex>
+#include <new>
 #include <limits.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -289,11 +291,12 @@ hipError_t dispatch_precond(int elem, int dk, const dp::PrecondArgs& a, hipStrea
 }
 
 // Ls, t0: the call covers tokens t0 .. t0 + L - 1 of sequences Ls tokens long
-// (0, 0: the whole sequences).
+// (0, 0: the whole sequences).  dry: validate and plan only, enqueue nothing.
 int fwd_impl(int elem, const void* q, const void* k, const void* kt, const void* v,
              const float* beta, const float* g, int n_h, int B, int H, int L, int dk, int dv,
              int chunk, void* out, float* final_state, const float* h0, void* workspace,
-             size_t workspace_bytes, int flags, dp_stream stream, int Ls = 0, int t0 = 0) {
+             size_t workspace_bytes, int flags, dp_stream stream, int Ls = 0, int t0 = 0,
+             bool dry = false) {
   const Shape s{n_h, B, H, L, dk, dv, chunk};
   int rc = check_shape(s);
   if (rc != DP_OK) return rc;
@@ -343,7 +346,7 @@ int fwd_impl(int elem, const void* q, const void* k, const void* kt, const void*
 
   int BV = 0, lds = 0;
   rc = plan(a, elem, dk, chunk, &BV, &lds);
-  if (rc != DP_OK) return rc;
+  if (rc != DP_OK || dry) return rc;
 
   int run = stages;
   if (a.nc == 0) run &= ~DP_STAGE_UT;  // nothing to transform; the scan copies h0
@@ -498,7 +501,8 @@ int decode_impl(int elem, const void* q, const void* k, const void* kt, const vo
 
 int precond_impl(int elem, const void* k, const float* beta, const float* ret, int flags,
                  int B, int H, int L, int dk, float eta, float dmin, float dmax, float eps,
-                 float* d_state, void* kt, bool open_box, dp_stream stream, int Ls = 0, int t0 = 0) {
+                 float* d_state, void* kt, bool open_box, dp_stream stream, int Ls = 0, int t0 = 0,
+                 bool dry = false) {
   if (k == nullptr || beta == nullptr || d_state == nullptr || kt == nullptr) return DP_EINVAL;
   if (B <= 0 || H <= 0 || L < 0) return DP_EINVAL;
   if ((flags & ~DP_PRECOND_BETA_FREE) != 0) return DP_EINVAL;
@@ -506,7 +510,7 @@ int precond_impl(int elem, const void* k, const float* beta, const float* ret, i
   if (!(eps > 0.f) || !(dmin <= dmax) || !(eta == eta)) return DP_EINVAL;
   if (!open_box && !(dmin > 0.f)) return DP_EINVAL;
   if ((long long)B * H * (long long)L > (long long)1 << 40) return DP_ENOTSUP;
-  if (L == 0) return DP_OK;
+  if (L == 0 || dry) return DP_OK;
   dp::PrecondArgs a;
   a.k = k;
   a.beta = beta;
@@ -530,10 +534,9 @@ int precond_impl(int elem, const void* k, const float* beta, const float* ret, i
 // Write-key forward with its phase 1, pipelined over token segments.  Each
 // segment is a whole number of chunks (n_h = 1: a chunk is C tokens), so the
 // chunks are those of the unsegmented forward.  Phase 1 runs on the caller's
-// stream and phase 2 on a second stream of the device (created once, default
-// priority), ordered by one event per segment.
+// stream and phase 2 on the stream of a caller-owned dp_pipeline, ordered by
+// one event per segment.
 constexpr int kMaxSegments = 16;
-constexpr int kMaxDevices = 64;
 
 int seg_len(int L, int chunk, int segments) {
   const int per = (L + segments - 1) / segments;
@@ -541,27 +544,22 @@ int seg_len(int L, int chunk, int segments) {
   return len > 0 ? len : chunk;
 }
 
-struct SegRes {
+}  // namespace
+
+struct dp_pipeline_s {
+  int device = -1;
   hipStream_t st2 = nullptr;
   hipEvent_t ev[kMaxSegments + 1] = {};
-  bool ready = false;
+  std::mutex mu;  // held by a call for its whole enqueue sequence
 };
 
-// the second stream and events of the current device, or nullptr on failure
-SegRes* seg_res() {
-  static SegRes res[kMaxDevices];
-  static std::mutex mu;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-  std::lock_guard<std::mutex> lock(mu);
-  SegRes& r = res[dev];
-  if (!r.ready) {
-    if (hipStreamCreateWithFlags(&r.st2, hipStreamNonBlocking) != hipSuccess) return nullptr;
-    for (int i = 0; i <= kMaxSegments; ++i)
-      if (hipEventCreateWithFlags(&r.ev[i], hipEventDisableTiming) != hipSuccess) return nullptr;
-    r.ready = true;
-  }
-  return &r;
+namespace {
+
+void release_pipeline(dp_pipeline p) {
+  for (int i = 0; i <= kMaxSegments; ++i)
+    if (p->ev[i] != nullptr) (void)hipEventDestroy(p->ev[i]);
+  if (p->st2 != nullptr) (void)hipStreamDestroy(p->st2);
+  delete p;
 }
 
 // Backward: fixed chunk of kBwdChunk sub-steps.  Workspace: T (fp32) and
@@ -812,10 +810,34 @@ int dp_osdn_fwd_workspace_size(int B, int H, int L, int dk, int dv, int chunk, i
   return DP_OK;
 }
 
+int dp_pipeline_create(dp_pipeline* out) {
+  if (out == nullptr) return DP_EINVAL;
+  *out = nullptr;
+  dp_pipeline p = new (std::nothrow) dp_pipeline_s;
+  if (p == nullptr) return DP_EHIP;
+  bool ok = hipGetDevice(&p->device) == hipSuccess &&
+            hipStreamCreateWithFlags(&p->st2, hipStreamNonBlocking) == hipSuccess;
+  for (int i = 0; ok && i <= kMaxSegments; ++i)
+    ok = hipEventCreateWithFlags(&p->ev[i], hipEventDisableTiming) == hipSuccess;
+  if (!ok) {
+    release_pipeline(p);
+    return DP_EHIP;
+  }
+  *out = p;
+  return DP_OK;
+}
+
+int dp_pipeline_destroy(dp_pipeline pipe) {
+  if (pipe == nullptr) return DP_OK;
+  const hipError_t e = hipStreamSynchronize(pipe->st2);
+  release_pipeline(pipe);
+  return e == hipSuccess ? DP_OK : DP_EHIP;
+}
+
 int dp_osdn_fwd_bf16(const void* q, const void* k, const void* v, const float* beta, const float* h0,
                      int B, int H, int L, int dk, int dv, int chunk, float eta, float dmin, float dmax,
                      float eps, float* d_state, void* kt, void* out, float* final_state, void* workspace,
-                     size_t workspace_bytes, int segments, dp_stream stream) {
+                     size_t workspace_bytes, int segments, dp_pipeline pipe, dp_stream stream) {
   if (segments < 1 || segments > kMaxSegments || chunk <= 0 || L < 0) return DP_EINVAL;
   const int len = seg_len(L, chunk, segments);
   const int nseg = L > 0 ? (L + len - 1) / len : 0;
@@ -830,22 +852,38 @@ int dp_osdn_fwd_bf16(const void* q, const void* k, const void* v, const float* b
   if (workspace_bytes < need || (need > 0 && workspace == nullptr)) return DP_EWORKSPACE;
   if (nseg == 0) return fwd_impl(2, q, k, k, v, beta, nullptr, 1, B, H, 0, dk, dv, chunk, out, final_state,
                                  h0, workspace, workspace_bytes, DP_STAGE_ALL, stream);
-  SegRes* r = seg_res();
-  if (r == nullptr) return DP_EHIP;
+  // Check every run before enqueueing the first.  The runs differ only in
+  // their token count (len, the last one at most len) and offset: a full run
+  // passes the same shape, pointer, workspace and plan checks as each of them.
+  rc = precond_impl(2, k, beta, nullptr, 0, B, H, len, dk, eta, dmin, dmax, eps, d_state, kt, false,
+                    stream, L, 0, true);
+  if (rc != DP_OK) return rc;
+  rc = fwd_impl(2, q, k, kt, v, beta, nullptr, 1, B, H, len, dk, dv, chunk, out, final_state, h0,
+                workspace, workspace_bytes, DP_STAGE_ALL, stream, L, 0, true);
+  if (rc != DP_OK) return rc;
+  std::unique_lock<std::mutex> hold;
+  if (pipe != nullptr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return DP_EHIP;
+    if (dev != pipe->device) return DP_EINVAL;
+    hold = std::unique_lock<std::mutex>(pipe->mu);
+  }
   hipStream_t st = static_cast<hipStream_t>(stream);
+  hipStream_t st2 = pipe != nullptr ? pipe->st2 : st;
   for (int sg = 0; sg < nseg; ++sg) {
     const int t0 = sg * len, n = L - t0 < len ? L - t0 : len;
     rc = precond_impl(2, k, beta, nullptr, 0, B, H, n, dk, eta, dmin, dmax, eps, d_state, kt, false,
                       stream, L, t0);
     if (rc != DP_OK) return rc;
-    if (hipEventRecord(r->ev[sg], st) != hipSuccess || hipStreamWaitEvent(r->st2, r->ev[sg], 0) != hipSuccess)
+    if (pipe != nullptr && (hipEventRecord(pipe->ev[sg], st) != hipSuccess ||
+                            hipStreamWaitEvent(st2, pipe->ev[sg], 0) != hipSuccess))
       return DP_EHIP;
     rc = fwd_impl(2, q, k, kt, v, beta, nullptr, 1, B, H, n, dk, dv, chunk, out, final_state,
-                  sg == 0 ? h0 : final_state, workspace, workspace_bytes, DP_STAGE_ALL, r->st2, L, t0);
+                  sg == 0 ? h0 : final_state, workspace, workspace_bytes, DP_STAGE_ALL, st2, L, t0);
     if (rc != DP_OK) return rc;
   }
-  if (hipEventRecord(r->ev[kMaxSegments], r->st2) != hipSuccess ||
-      hipStreamWaitEvent(st, r->ev[kMaxSegments], 0) != hipSuccess)
+  if (pipe != nullptr && (hipEventRecord(pipe->ev[kMaxSegments], st2) != hipSuccess ||
+                          hipStreamWaitEvent(st, pipe->ev[kMaxSegments], 0) != hipSuccess))
     return DP_EHIP;
   return DP_OK;
 }

@@ -303,3 +303,38 @@ def test_launch_info_reports_the_default_path(lib):
     assert info[2] > 0
     assert lib.dp_fwd_launch_info(2, 8, 32, 2048, 128, 32, 64, 2, 1, info) == 0
     assert info[2] > 0
+
+
+def test_osdn_fwd_checks_every_run_before_the_first(lib):
+    """dp_osdn_fwd_bf16 validates what each run's phase 1 and forward would
+    check before it enqueues anything: with no GPU here, a failure found only
+    after the first run's phase 1 had been enqueued would surface as DP_EHIP
+    (a HIP launch on a machine without a device), not as the status below.
+    So on a failed call d_state, kt, out and final_state are never written."""
+    E = dp.binding
+    f = lib.dp_osdn_fwd_bf16
+
+    def call(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, h0=None, B=1, H=2, L=300, dk=128, dv=128, chunk=64,
+             eta=3e-3, dmin=0.5, dmax=2.0, eps=1e-6, d=FAKE, kt=FAKE, out=FAKE, fs=FAKE, wsp=FAKE,
+             wsb=1 << 30, segments=4, pipe=None):
+        return f(q, k, v, beta, h0, B, H, L, dk, dv, chunk, eta, dmin, dmax, eps, d, kt, out, fs, wsp,
+                 wsb, segments, pipe, None)
+
+    assert call(v=FAKE + 2) == E.DP_EINVAL      # read by the forward only
+    assert call(q=FAKE + 8) == E.DP_EINVAL
+    assert call(kt=FAKE + 4) == E.DP_EINVAL
+    assert call(dmin=0.0) == E.DP_EINVAL        # phase-1 box must be positive here
+    assert call(eps=0.0) == E.DP_EINVAL
+    assert call(dmin=3.0) == E.DP_EINVAL        # dmin > dmax
+    assert call(fs=None) == E.DP_EINVAL         # the state passes through it between runs
+    assert call(d=None) == E.DP_EINVAL
+    assert call(wsb=16) == E.DP_EWORKSPACE
+    assert call(segments=0) == E.DP_EINVAL
+    assert call(segments=17) == E.DP_EINVAL
+    assert call(dk=24) == E.DP_ENOTSUP
+
+
+def test_pipeline_handle_arguments(lib):
+    E = dp.binding
+    assert lib.dp_pipeline_create(None) == E.DP_EINVAL
+    assert lib.dp_pipeline_destroy(None) == E.DP_OK

@@ -59,18 +59,83 @@ def test_pipelined_equals_two_calls(B, H, L, dk, dv, chunk, segments, with_h0):
     say(f"case osdn_fwd B={B} H={H} L={L} dk={dk} dv={dv} C={chunk} segments={segments} h0={with_h0}")
     q, k1, v1, b1, h0 = inputs(B, H, L, dk, dv, with_h0)
     ref = two_calls(q, k1, v1, b1, h0, chunk)
-    got = dp.osdn_fwd(q, k1, v1, b1, h0=h0, chunk=chunk, segments=segments)
+    pipe = dp.Pipeline()
+    got = dp.osdn_fwd(q, k1, v1, b1, h0=h0, chunk=chunk, segments=segments, pipeline=pipe)
+    seq = dp.osdn_fwd(q, k1, v1, b1, h0=h0, chunk=chunk, segments=segments)
     torch.cuda.synchronize()
-    for name, x, r in zip(("out", "final_state", "kt", "d"), got, ref):
-        assert torch.equal(x, r), f"{name} differs from the two-call path"
+    pipe.close()
+    for name, x, y, r in zip(("out", "final_state", "kt", "d"), got, seq, ref):
+        assert torch.equal(x, r), f"{name} (pipelined) differs from the two-call path"
+        assert torch.equal(y, r), f"{name} (runs in order, no pipeline) differs from the two-call path"
+
+
+def test_one_pipeline_serves_calls_from_two_threads():
+    """A handle may be shared: each call holds it for its enqueue sequence, so
+    calls from two host threads on their own streams give the two-call results."""
+    import threading
+
+    B, H, L, dk, dv = 1, 2, 300, 128, 128
+    q, k1, v1, b1, _ = inputs(B, H, L, dk, dv)
+    ref = two_calls(q, k1, v1, b1, None, 64)
+    torch.cuda.synchronize()
+    pipe = dp.Pipeline()
+    results = [None, None]
+
+    def run(i):
+        st = torch.cuda.Stream()
+        with torch.cuda.stream(st):
+            for _ in range(3):
+                r = dp.osdn_fwd(q, k1, v1, b1, segments=4, pipeline=pipe, stream=st)
+            st.synchronize()
+            results[i] = r
+
+    ts = [threading.Thread(target=run, args=(i,)) for i in range(2)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    torch.cuda.synchronize()
+    pipe.close()
+    for got in results:
+        for name, x, r in zip(("out", "final_state", "kt", "d"), got, ref):
+            assert torch.equal(x, r), f"{name} differs from the two-call path"
+
+
+def test_failed_call_leaves_outputs_untouched():
+    """Every run is checked before the first is enqueued: a misaligned v (which
+    only the forward of a run reads) fails the call with d, kt, out and the
+    final state as they were."""
+    B, H, L, dk, dv = 1, 2, 300, 128, 128
+    q, k1, v1, b1, _ = inputs(B, H, L, dk, dv)
+    raw = torch.empty(v1.numel() + 1, dtype=v1.dtype, device=v1.device)
+    v_mis = raw[1:].view(v1.shape)
+    v_mis.copy_(v1)
+    assert v_mis.is_contiguous() and v_mis.data_ptr() % 16 != 0
+    d = torch.full((B, H, dk), 1.25, device=q.device)
+    kt = torch.full((B, L, H, dk), 3.0, dtype=torch.bfloat16, device=q.device)
+    out = torch.full((B, L, H, dv), -2.0, dtype=torch.bfloat16, device=q.device)
+    fs = torch.full((B, H, dk, dv), 7.0, device=q.device)
+    snap = [t.clone() for t in (d, kt, out, fs)]
+    pipe = dp.Pipeline()
+    for p in (pipe, None):
+        with pytest.raises(dp.DPError) as ei:
+            dp.osdn_fwd(q, k1, v_mis, b1, segments=4, d_state=d, kt=kt, out=out, final_state=fs,
+                        pipeline=p)
+        assert ei.value.code == dp.binding.DP_EINVAL
+    torch.cuda.synchronize()
+    pipe.close()
+    for t, s in zip((d, kt, out, fs), snap):
+        assert torch.equal(t, s)
 
 
 def test_pipelined_matches_oracle():
     B, H, L, dk, dv = 2, 2, 200, 128, 128
     say(f"case osdn_fwd vs oracle B={B} H={H} L={L}")
     q, k1, v1, b1, _ = inputs(B, H, L, dk, dv)
-    out, fs, kt, d = dp.osdn_fwd(q, k1, v1, b1, segments=3)
+    pipe = dp.Pipeline()
+    out, fs, kt, d = dp.osdn_fwd(q, k1, v1, b1, segments=3, pipeline=pipe)
     torch.cuda.synchronize()
+    pipe.close()
     kto, do = oracle.precond(k1.cpu(), b1.cpu())
     oo, fo = oracle.fwd(q.cpu(), k1.cpu().unsqueeze(3), v1.cpu().unsqueeze(3), b1.cpu().unsqueeze(3),
                         kt=kto[:, :, :, None, :])
