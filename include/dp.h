@@ -36,8 +36,9 @@
  *     and the call returns DP_OK without waiting for it.
  *   - Inputs are read-only and must not overlap out, final_state or the
  *     workspace.  When L == 0 the per-token tensors are empty and may be NULL.  h0 and final_state MAY be the same buffer (in-place resume).
- *   - The library keeps no global state: calls on different streams may run
- *     concurrently as long as their buffers are disjoint.
+ *   - The library keeps no global state, with one stated exception (the
+ *     fixed scratch array of dp_fwd_varlen_noalloc_bf16): calls on different
+ *     streams may run concurrently as long as their buffers are disjoint.
  *   - NaN and Inf in the inputs propagate; nothing is silently repaired.
  *   - Precision: the state and every accumulation are fp32.  On the bf16
  *     path the computed MFMA operands (normalised keys, queries, write keys,
@@ -63,7 +64,8 @@ typedef enum {
     DP_EINVAL = -1,     /* null required pointer, bad size, misaligned pointer */
     DP_ENOTSUP = -2,    /* dk/dv/chunk/n_h outside the supported set */
     DP_EWORKSPACE = -3, /* workspace missing or smaller than dp_fwd_workspace_size */
-    DP_EHIP = -4        /* a HIP launch or runtime call failed */
+    DP_EHIP = -4,       /* a HIP launch or runtime call failed */
+    DP_ESCRATCH = -5    /* beyond the fixed scratch of dp_fwd_varlen_noalloc_bf16 */
 } dp_status;
 
 typedef void* dp_stream; /* hipStream_t */
@@ -309,6 +311,29 @@ int dp_fwd_varlen_bf16(const void* q, const void* k, const void* v, const float*
                        const float* g, const int* cu_seqlens, int nseq, int n_h, int H, int T,
                        int dk, int dv, int chunk, void* out, float* final_state, const float* h0,
                        void* workspace, size_t workspace_bytes, int flags, dp_stream stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * dp_fwd_varlen_bf16 with DP_FWD_FUSED, without a workspace.  The fused
+ * kernel's only scratch, the per-sequence chunk-offset table (nseq + 1 ints),
+ * lives in a fixed array inside the library: (DP_NOALLOC_MAX_SEQS + 1) ints =
+ * 256 KiB on every device the library runs on, held until the process ends.
+ * The call allocates nothing.  Arguments as for dp_fwd_varlen_bf16, with
+ *   flags: 0 or DP_OUT_F32 (both stages always run)
+ * Results equal dp_fwd_varlen_bf16 with DP_FWD_FUSED bit for bit.  Nothing in
+ * the array needs clearing: each call writes all nseq + 1 entries before its
+ * forward reads them.  Calls on one device share the array: two calls that
+ * overlap in time there (other streams, other threads) race, and their
+ * results are undefined; the caller serialises them.
+ * Errors: as dp_fwd_varlen_bf16; DP_ESCRATCH when nseq > DP_NOALLOC_MAX_SEQS;
+ * DP_ENOTSUP when dk or chunk is not a multiple of 32 (no fused kernel).
+ */
+#define DP_NOALLOC_MAX_SEQS 65535
+int dp_fwd_varlen_noalloc_bf16(const void* q, const void* k, const void* v, const float* beta,
+                               const float* g, const int* cu_seqlens, int nseq, int n_h, int H,
+                               int T, int dk, int dv, int chunk, void* out, float* final_state,
+                               const float* h0, int flags, dp_stream stream);
 
 /*
  * One recurrent decode step (DeltaProduct notes sec. 2.2 Eq.(3) and the

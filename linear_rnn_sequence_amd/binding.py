@@ -14,7 +14,8 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdp.so")
 
-DP_OK, DP_EINVAL, DP_ENOTSUP, DP_EWORKSPACE, DP_EHIP = 0, -1, -2, -3, -4
+DP_OK, DP_EINVAL, DP_ENOTSUP, DP_EWORKSPACE, DP_EHIP, DP_ESCRATCH = 0, -1, -2, -3, -4, -5
+NOALLOC_MAX_SEQS = 65535
 STAGE_UT, STAGE_SCAN, STAGE_ALL, OUT_F32, FWD_SPLIT, FWD_FUSED = 1, 2, 3, 4, 8, 16
 _PATH_FLAGS = {"auto": 0, "split": FWD_SPLIT, "fused": FWD_FUSED}
 
@@ -36,6 +37,7 @@ EXPORTS = (
     "dp_fwd_varlen_workspace_size", "dp_fwd_varlen_bf16",
     "dp_bwd_workspace_size", "dp_bwd_f32", "dp_bwd_bf16",
     "dp_osdn_fwd_workspace_size", "dp_osdn_fwd_bf16", "dp_pipeline_create", "dp_pipeline_destroy",
+    "dp_fwd_varlen_noalloc_bf16",
 )
 
 _lib = None
@@ -90,6 +92,9 @@ def load() -> ctypes.CDLL:
         lib.dp_fwd_varlen_bf16.restype = _I
         lib.dp_fwd_varlen_bf16.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P,
                                            _P, _P, ctypes.c_size_t, _I, _P]
+        lib.dp_fwd_varlen_noalloc_bf16.restype = _I
+        lib.dp_fwd_varlen_noalloc_bf16.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P,
+                                                   _P, _P, _I, _P]
         dec = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _P]
         for name in ("dp_decode_f32", "dp_decode_bf16"):
             getattr(lib, name).restype = _I
@@ -442,6 +447,44 @@ def fwd_varlen(q, k, v, beta, cu_seqlens, g=None, *, chunk: int = 64, h0=None, o
                                    workspace.numel() * workspace.element_size(), flags,
                                    _stream(stream))
     _check(rc, "dp_fwd_varlen_bf16")
+    return out, final_state
+
+
+def fwd_varlen_noalloc(q, k, v, beta, cu_seqlens, out, g=None, *, chunk: int = 64, h0=None,
+                       final_state=None, stream=None):
+    """The packed forward with no device allocation (dp_fwd_varlen_noalloc_bf16):
+    the fused kernel, its chunk-offset table in the library's fixed scratch.
+    Arguments as for :func:`fwd_varlen`, but `out` (bf16 or float32) must be
+    given and nothing is allocated here either; final_state may be None.  At
+    most NOALLOC_MAX_SEQS sequences; calls that overlap in time on one device
+    race (they share the scratch)."""
+    if q.dim() != 3 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("expected q[T,H,dk], k[T,H,n_h,dk], v[T,H,n_h,dv]")
+    T, H, dk = q.shape
+    n_h, dv = k.shape[2], v.shape[3]
+    dev, dt = q.device, q.dtype
+    if dt != torch.bfloat16:
+        raise TypeError("fwd_varlen_noalloc takes bfloat16 q, k, v")
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be [nseq + 1]")
+    nseq = cu_seqlens.numel() - 1
+    _need(cu_seqlens, "cu_seqlens", torch.int32, (nseq + 1,), dev)
+    _need(k, "k", dt, (T, H, n_h, dk), dev)
+    _need(v, "v", dt, (T, H, n_h, dv), dev)
+    _need(beta, "beta", torch.float32, (T, H, n_h), dev)
+    _need(g, "g", torch.float32, (T, H), dev)
+    _need(h0, "h0", torch.float32, (nseq, H, dk, dv), dev)
+    _need(final_state, "final_state", torch.float32, (nseq, H, dk, dv), dev)
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    if out is None or out.dtype not in (dt, torch.float32):
+        raise TypeError("out must be a bfloat16 or float32 tensor [T, H, dv]")
+    _need(out, "out", out.dtype, (T, H, dv), dev)
+    flags = OUT_F32 if out.dtype == torch.float32 else 0
+    rc = load().dp_fwd_varlen_noalloc_bf16(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(cu_seqlens),
+                                           nseq, n_h, H, T, dk, dv, chunk, _ptr(out), _ptr(final_state),
+                                           _ptr(h0), flags, _stream(stream))
+    _check(rc, "dp_fwd_varlen_noalloc_bf16")
     return out, final_state
 
 

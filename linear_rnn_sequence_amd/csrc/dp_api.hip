@@ -3,7 +3,8 @@
 // Every entry point validates its arguments on the host before touching the
 // HIP runtime, then enqueues the kernels of dp_kernels.hpp on the caller's
 // stream and returns.  The library allocates no device memory for a call and
-// keeps no state between calls (a dp_pipeline is the caller's object).
+// keeps no state between calls (a dp_pipeline is the caller's object), except
+// the fixed `scratch` array of the no-alloc packed forward.
 #include <mutex>
 #include <new>
 #include <limits.h>
@@ -31,6 +32,11 @@ DP_DECLARE_BWD_LAUNCHER(bf16, 16)
 DP_DECLARE_BWD_LAUNCHER(bf16, 32)
 DP_DECLARE_BWD_LAUNCHER(bf16, 64)
 DP_DECLARE_BWD_LAUNCHER(bf16, 128)
+
+// Chunk-offset table of the no-alloc packed forward (dp_fwd_varlen_noalloc_bf16).
+constexpr int kScratchInts = DP_NOALLOC_MAX_SEQS + 1;
+static_assert(kScratchInts % 64 == 0, "scratch is a whole number of 256-byte blocks");
+static __device__ __align__(256) int scratch[kScratchInts];
 
 namespace {
 
@@ -393,10 +399,13 @@ size_t varlen_ws_total(const VarShape& v) {
 // the fused kernel needs only the per-sequence first chunks
 size_t varlen_ws_need(const VarShape& v, bool fused) { return fused ? varlen_cbase_bytes(v) : varlen_ws_total(v); }
 
+// table: when not NULL, the fused kernel's chunk-offset table lives there (at
+// least nseq + 1 ints) and no workspace is used.  dry: validate and plan only.
 int varlen_impl(const void* q, const void* k, const void* v, const float* beta, const float* g,
                 const int* cu_seqlens, int nseq, int n_h, int H, int T, int dk, int dv, int chunk,
                 void* out, float* final_state, const float* h0, void* workspace,
-                size_t workspace_bytes, int flags, dp_stream stream) {
+                size_t workspace_bytes, int flags, dp_stream stream, int* table = nullptr,
+                bool dry = false) {
   const VarShape vs{n_h, nseq, H, T, dk, dv, chunk};
   int rc = check_varlen(vs);
   if (rc != DP_OK) return rc;
@@ -408,9 +417,13 @@ int varlen_impl(const void* q, const void* k, const void* v, const float* beta, 
     return DP_EINVAL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return DP_EINVAL;
   const bool fused = use_fused(2, false, dk, dv, chunk, flags);
-  const size_t need = varlen_ws_need(vs, fused);
-  if (workspace_bytes < need || workspace == nullptr) return DP_EWORKSPACE;
-  if (((uintptr_t)workspace & (kWsAlign - 1)) != 0) return DP_EWORKSPACE;
+  if (table != nullptr) {
+    if (!fused) return DP_ENOTSUP;  // only the fused kernel runs on the table alone
+  } else {
+    const size_t need = varlen_ws_need(vs, fused);
+    if (workspace_bytes < need || workspace == nullptr) return DP_EWORKSPACE;
+    if (((uintptr_t)workspace & (kWsAlign - 1)) != 0) return DP_EWORKSPACE;
+  }
 
   dp::FwdArgs a;
   memset(&a, 0, sizeof(a));
@@ -424,7 +437,7 @@ int varlen_impl(const void* q, const void* k, const void* v, const float* beta, 
   a.fstate = final_state;
   a.cu = cu_seqlens;
   if (fused) {
-    a.cbase = static_cast<int*>(workspace);
+    a.cbase = table != nullptr ? table : static_cast<int*>(workspace);
   } else {
     a.wsT = workspace;
     a.cbase = reinterpret_cast<int*>(static_cast<char*>(workspace) + varlen_blocks_bytes(vs));
@@ -445,9 +458,31 @@ int varlen_impl(const void* q, const void* k, const void* v, const float* beta, 
 
   int BV = 0, lds = 0;
   rc = plan(a, 2, dk, chunk, &BV, &lds);
-  if (rc != DP_OK) return rc;
+  if (rc != DP_OK || dry) return rc;
   const hipError_t e = dispatch_fwd(2, dk, a, chunk, BV, lds, stages, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DP_OK : DP_EHIP;
+}
+
+// The no-alloc packed forward keeps its chunk-offset table in `scratch`, one
+// copy per device, held until the process ends.  In host code `scratch` names
+// a host-side stand-in: its device address on each device comes from
+// hipGetSymbolAddress, looked up once per device with that device current,
+// and only that address is handed to kernels.
+constexpr int kMaxScratchDevices = 64;
+
+// device address of this device's `scratch`, or nullptr when the lookup fails
+int* scratch_on_current_device() {
+  static std::mutex mu;
+  static int* addr[kMaxScratchDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+    addr[dev] = static_cast<int*>(p);
+  }
+  return addr[dev];
 }
 
 hipError_t dispatch_decode(int elem, int dk, const dp::DecodeArgs& a, hipStream_t st) {
@@ -680,6 +715,7 @@ const char* dp_status_str(int status) {
     case DP_ENOTSUP: return "DP_ENOTSUP: unsupported shape (dk/dv/chunk/n_h)";
     case DP_EWORKSPACE: return "DP_EWORKSPACE: workspace missing, misaligned or too small";
     case DP_EHIP: return "DP_EHIP: HIP launch or runtime error";
+    case DP_ESCRATCH: return "DP_ESCRATCH: more sequences than the no-alloc entry point's fixed scratch holds";
     default: return "unknown dp status";
   }
 }
@@ -904,6 +940,25 @@ int dp_fwd_varlen_bf16(const void* q, const void* k, const void* v, const float*
                        void* workspace, size_t workspace_bytes, int flags, dp_stream stream) {
   return varlen_impl(q, k, v, beta, g, cu_seqlens, nseq, n_h, H, T, dk, dv, chunk, out, final_state,
                      h0, workspace, workspace_bytes, flags, stream);
+}
+
+int dp_fwd_varlen_noalloc_bf16(const void* q, const void* k, const void* v, const float* beta,
+                               const float* g, const int* cu_seqlens, int nseq, int n_h, int H,
+                               int T, int dk, int dv, int chunk, void* out, float* final_state,
+                               const float* h0, int flags, dp_stream stream) {
+  if ((flags & ~DP_OUT_F32) != 0) return DP_EINVAL;
+  if (nseq > DP_NOALLOC_MAX_SEQS) return DP_ESCRATCH;
+  const int f = DP_STAGE_ALL | DP_FWD_FUSED | flags;
+  // every check first, before any HIP call; the table address only marks the
+  // table-only form here and is not read
+  int* const mark = reinterpret_cast<int*>(kWsAlign);
+  int rc = varlen_impl(q, k, v, beta, g, cu_seqlens, nseq, n_h, H, T, dk, dv, chunk, out,
+                       final_state, h0, nullptr, 0, f, stream, mark, true);
+  if (rc != DP_OK) return rc;
+  int* const table = scratch_on_current_device();
+  if (table == nullptr) return DP_EHIP;
+  return varlen_impl(q, k, v, beta, g, cu_seqlens, nseq, n_h, H, T, dk, dv, chunk, out, final_state,
+                     h0, nullptr, 0, f, stream, table, false);
 }
 
 int dp_decode_f32(const float* q, const float* k, const float* kt, const float* v,

@@ -49,7 +49,7 @@ def test_library_is_gfx950_and_loads_on_cpu(lib):
 
 
 def test_status_strings(lib):
-    for code in (0, -1, -2, -3, -4):
+    for code in (0, -1, -2, -3, -4, -5):
         assert dp.status_str(code).startswith("DP_")
     assert "unknown" in dp.status_str(7)
 
@@ -338,3 +338,24 @@ def test_pipeline_handle_arguments(lib):
     E = dp.binding
     assert lib.dp_pipeline_create(None) == E.DP_EINVAL
     assert lib.dp_pipeline_destroy(None) == E.DP_OK
+
+
+def test_noalloc_varlen_validation_before_hip(lib):
+    """dp_fwd_varlen_noalloc_bf16 rejects what it cannot run before any HIP
+    call (including the lookup of its scratch array's device address)."""
+    E = dp.binding
+    f = lib.dp_fwd_varlen_noalloc_bf16
+
+    def call(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, g=None, cu=FAKE, nseq=2, n_h=2, H=1, T=8, dk=32,
+             dv=16, chunk=32, out=FAKE, fs=None, h0=None, flags=0):
+        return f(q, k, v, beta, g, cu, nseq, n_h, H, T, dk, dv, chunk, out, fs, h0, flags, None)
+
+    assert call(nseq=E.NOALLOC_MAX_SEQS + 1) == E.DP_ESCRATCH
+    assert call(flags=1) == E.DP_EINVAL          # stage bits are not taken: both always run
+    assert call(flags=8) == E.DP_EINVAL
+    assert call(dk=16) == E.DP_ENOTSUP           # no fused kernel for dk 16
+    assert call(chunk=16) == E.DP_ENOTSUP
+    assert call(cu=None) == E.DP_EINVAL
+    assert call(nseq=0) == E.DP_EINVAL
+    assert call(q=FAKE + 8) == E.DP_EINVAL
+    assert "scratch" in dp.status_str(E.DP_ESCRATCH)
