@@ -78,9 +78,10 @@ def copy_probe(nbytes):
     print(json.dumps({"copy_probe_bytes": n * 4, "copies": 3}), flush=True)
 
 
-def source_digest():
-    """sha256 over the forward kernels' sources (csrc/*.hip, *.hpp, in name
-    order, without the backward and decode files, which they do not use)."""
+def source_digest(kernel=None):
+    """sha256 over the sources a forward kernel is built from (csrc/*.hip,
+    *.hpp, in name order, without the backward and decode files, and without
+    the fused kernel's header unless `kernel` is the fused kernel)."""
     import glob
     import hashlib
 
@@ -88,6 +89,8 @@ def source_digest():
     for f in sorted(glob.glob(os.path.join(ROOT, "linear_rnn_sequence_amd", "csrc", "*"))):
         base = os.path.basename(f)
         if base.startswith(("dp_bwd", "dp_decode")):
+            continue
+        if base == "dp_fused.hpp" and kernel != "dp_fused_kernel":
             continue
         if f.endswith((".hip", ".hpp")):
             hsh.update(os.path.basename(f).encode())
@@ -104,7 +107,7 @@ def measured_traffic(workload, kernel):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_sha256") != source_digest():
+    if rec.get("source_sha256") != source_digest(kernel):
         return None
     return rec.get("bytes_per_launch")
 
@@ -168,7 +171,7 @@ def fused_possible(w):
 def kernel_names(w):
     """(prep / UT kernel, scan kernel) names of the two-launch path a workload
     runs on; the fused path is the one kernel dp_fused_kernel."""
-    if w.dtype == "bf16" and not w.asym:
+    if w.dtype == "bf16" and (not w.asym or (w.dk % 32 == 0 and w.chunk % 32 == 0)):
         return "dp_prep_kernel", "dp_chain_kernel"
     if w.dtype == "bf16":
         return "dp_ut_kernel", "dp_scan16_kernel"

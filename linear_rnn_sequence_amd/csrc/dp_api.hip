@@ -82,10 +82,14 @@ int readout_rows(int C, int n_h) {
   return r >= C ? C : ((r + 15) / 16) * 16;
 }
 
-// bf16: one operand block per chunk (dp_prep_kernel's output); it also covers
-// the T / (1/|k|, G) layout the write-key path uses.  fp32: T and (1/|k|, G).
+// bf16: one operand block per chunk (dp_prep_kernel's output), sized for the
+// write-key form where that runs on the same kernels (its block adds the write
+// keys), so that one workspace size serves dp_fwd_* and dp_fwd_wk_*; it also
+// covers the T / (1/|k|, G) layout of the other write-key shapes.  fp32: T
+// and (1/|k|, G).
 size_t ws_blocks_bytes(const Shape& s) {
-  const dp::Chunk16Layout W = dp::chunk16_layout(s.dk, s.chunk, readout_rows(s.chunk, s.n_h));
+  const bool asym = dp::chain_asym_ok(s.dk, s.chunk);
+  const dp::Chunk16Layout W = dp::chunk16_layout(s.dk, s.chunk, readout_rows(s.chunk, s.n_h), asym);
   return align_up((size_t)s.B * s.H * num_chunks(s) * W.bytes, kWsAlign);
 }
 
@@ -219,14 +223,15 @@ int plan(dp::FwdArgs& a, int elem, int dk, int chunk, int* BV_out, int* lds_out)
     *lds_out = dp::fused_layout(dk, chunk, a.RT, BV).bytes;
     return DP_OK;
   }
-  if (elem == 2 && !a.asym) {
+  if (elem == 2 && (!a.asym || dp::chain_asym_ok(dk, chunk))) {
+    const bool asym = a.asym != 0;
     int BV = pick_bv16(a.B * a.H, a.dv);
-    while (dp::chain_lds_bytes(dk, chunk, a.RT, BV) > kMaxLds && BV > 16) BV >>= 1;
-    if (dp::chain_lds_bytes(dk, chunk, a.RT, BV) > kMaxLds) return DP_ENOTSUP;
-    if (dp::prep_lds_bytes(dk, chunk, a.RT) > kMaxLds) return DP_ENOTSUP;
+    while (dp::chain_lds_bytes(dk, chunk, a.RT, BV, asym) > kMaxLds && BV > 16) BV >>= 1;
+    if (dp::chain_lds_bytes(dk, chunk, a.RT, BV, asym) > kMaxLds) return DP_ENOTSUP;
+    if (dp::prep_lds_bytes(dk, chunk, a.RT, asym) > kMaxLds) return DP_ENOTSUP;
     a.nvb = a.dv / BV;
     *BV_out = BV;
-    *lds_out = dp::chain_lds_bytes(dk, chunk, a.RT, BV);
+    *lds_out = dp::chain_lds_bytes(dk, chunk, a.RT, BV, asym);
     return DP_OK;
   }
   if (elem == 2) {
@@ -753,7 +758,9 @@ int dp_fwd_launch_info(int n_h, int B, int H, int L, int dk, int dv, int chunk, 
   info[1] = B * H * a.nvb;
   info[2] = a.fused ? 0 : B * H * num_chunks(s);
   info[3] = lds;
-  info[4] = a.fused ? 0 : (elem_bytes == 2 && !asym) ? dp::prep_lds_bytes(dk, chunk, a.RT) : ut_lds(elem_bytes, dk, chunk, asym);
+  info[4] = a.fused                                               ? 0
+            : (elem_bytes == 2 && (!asym || dp::chain_asym_ok(dk, chunk))) ? dp::prep_lds_bytes(dk, chunk, a.RT, asym != 0)
+                                                                    : ut_lds(elem_bytes, dk, chunk, asym);
   info[5] = a.RT;
   return DP_OK;
 }

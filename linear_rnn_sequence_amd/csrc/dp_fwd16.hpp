@@ -68,17 +68,20 @@ __host__ __device__ constexpr int t_bytes(int DK, int C) {
 }
 
 // Byte offsets of one chunk's operand block (workspace and LDS stage alike).
+// With a separate write key (asym) the block also holds the write keys Kw,
+// which the state update reads transposed in place of Kn.
 struct Chunk16Layout {
-  int oT, oK, oQ, oP, oS;  // T diag(beta), Kn, readout Q, scores P, scalars
-  int oEG, oEL, oEGL, oOff;  // scalars (relative to oS)
-  int bytes;                 // whole block, a multiple of 16
+  int oT, oK, oKW, oQ, oP, oS;  // T diag(beta), Kn, Kw (= oK when symmetric), readout Q, scores P, scalars
+  int oEG, oEL, oEGL, oOff;     // scalars (relative to oS)
+  int bytes;                    // whole block, a multiple of 16
 };
 
-__host__ __device__ constexpr Chunk16Layout chunk16_layout(int DK, int C, int RT) {
+__host__ __device__ constexpr Chunk16Layout chunk16_layout(int DK, int C, int RT, bool asym = false) {
   Chunk16Layout L{};
   L.oT = 0;
   L.oK = L.oT + t_bytes(DK, C);
-  L.oQ = L.oK + C * DK * 2;
+  L.oKW = asym ? L.oK + C * DK * 2 : L.oK;
+  L.oQ = L.oKW + C * DK * 2;
   L.oP = L.oQ + RT * DK * 2;
   L.oS = L.oP + RT * C * 2;
   L.oEG = 0;
@@ -90,12 +93,15 @@ __host__ __device__ constexpr Chunk16Layout chunk16_layout(int DK, int C, int RT
 }
 
 // LDS of dp_chain_kernel: kStages copies of (chunk block, value tile).
-// Four stages (three chunks in flight) when they fit the 160 KB of LDS, else three.
-__host__ __device__ constexpr int chain_stage_bytes(int DK, int C, int RT, int BV) {
-  return chunk16_layout(DK, C, RT).bytes + C * BV * 2;
+// Four stages (three chunks in flight) when they fit the 160 KB of LDS, else
+// three, else two (the write-key block at one readout per sub-step).
+__host__ __device__ constexpr int chain_stage_bytes(int DK, int C, int RT, int BV, bool asym = false) {
+  return chunk16_layout(DK, C, RT, asym).bytes + C * BV * 2;
 }
-__host__ __device__ constexpr int chain_stages(int DK, int C, int RT, int BV) {
-  return 4 * chain_stage_bytes(DK, C, RT, BV) <= 160 * 1024 ? 4 : 3;
+__host__ __device__ constexpr int chain_stages(int DK, int C, int RT, int BV, bool asym = false) {
+  return 4 * chain_stage_bytes(DK, C, RT, BV, asym) <= 160 * 1024   ? 4
+         : 3 * chain_stage_bytes(DK, C, RT, BV, asym) <= 160 * 1024 ? 3
+                                                                     : 2;
 }
 // Lookahead (in MFMA steps) of the pipelined chunk body.
 constexpr int kLookahead = 8;
@@ -104,9 +110,12 @@ constexpr int kLookahead = 8;
 __host__ __device__ constexpr bool chain_early(int DK, int C, int STG) {
   return DK % 32 == 0 && C % 32 == 0 && STG == 4 && (C / 16) * (DK / 32) >= kLookahead;
 }
-__host__ __device__ constexpr int chain_lds_bytes(int DK, int C, int RT, int BV) {
-  return chain_stages(DK, C, RT, BV) * chain_stage_bytes(DK, C, RT, BV);
+__host__ __device__ constexpr int chain_lds_bytes(int DK, int C, int RT, int BV, bool asym = false) {
+  return chain_stages(DK, C, RT, BV, asym) * chain_stage_bytes(DK, C, RT, BV, asym);
 }
+// The write-key form runs on the prep / chain pair only with the chain's
+// pipelined body (dk and chunk multiples of 32).
+__host__ __device__ constexpr bool chain_asym_ok(int DK, int C) { return DK % 32 == 0 && C % 32 == 0; }
 
 // LDS of dp_prep_kernel.  Region 0 holds the fp16 key and query rows while
 // M and the scores are formed, then fp32 T and the partial-sum tiles of the
@@ -128,18 +137,24 @@ __host__ __device__ constexpr int prep_m_bytes(int C) {
 // wavefront loads its MFMA fragments of them straight into registers (and
 // writes them to the operand block from there).  T is kept packed like M.
 __host__ __device__ constexpr bool prep_q_in_regs(int DK) { return DK % 32 == 0; }
-__host__ __device__ constexpr int prep_region0_bytes(int DK, int C, int RT) {
-  return (C * (DK + 8) * 2 + (prep_q_in_regs(DK) ? 0 : RT * (DK + 8) * 2)) > (prep_m_bytes(C) + 4 * 16 * 17 * 4)
-             ? (C * (DK + 8) * 2 + (prep_q_in_regs(DK) ? 0 : RT * (DK + 8) * 2))
-             : (prep_m_bytes(C) + 4 * 16 * 17 * 4);
+// With write keys, region 0 also holds their fp16 rows (after the query rows).
+__host__ __device__ constexpr int prep_rows_bytes(int DK, int C, int RT, bool asym) {
+  return C * (DK + 8) * 2 + (prep_q_in_regs(DK) ? 0 : RT * (DK + 8) * 2) + (asym ? C * (DK + 8) * 2 : 0);
 }
-__host__ __device__ constexpr int prep_lds_bytes(int DK, int C, int RT) {
-  return prep_region0_bytes(DK, C, RT) + prep_m_bytes(C) + 2 * C * 4 + RT * 4;
+__host__ __device__ constexpr int prep_region0_bytes(int DK, int C, int RT, bool asym = false) {
+  return prep_rows_bytes(DK, C, RT, asym) > (prep_m_bytes(C) + 4 * 16 * 17 * 4) ? prep_rows_bytes(DK, C, RT, asym)
+                                                                               : (prep_m_bytes(C) + 4 * 16 * 17 * 4);
+}
+__host__ __device__ constexpr int prep_lds_bytes(int DK, int C, int RT, bool asym = false) {
+  return prep_region0_bytes(DK, C, RT, asym) + prep_m_bytes(C) + 2 * C * 4 + RT * 4;
 }
 
 // ---------------------------------------------------------------------------
-// dp_prep_kernel: one chunk per workgroup.
-template <int DK, int C, int NRT>
+// dp_prep_kernel: one chunk per workgroup.  ASYM: the write keys kt are
+// given (used as they are): M pairs the read keys Kn (rows) with the write
+// keys (columns), the scores pair the queries with the write keys, and the
+// block carries the write keys for the chain's state update.
+template <int DK, int C, int NRT, bool ASYM = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void dp_prep_kernel(FwdArgs p) {
   constexpr int RT = 16 * NRT;
   constexpr int TPR = DK / 8;  // 16-byte granules per key row
@@ -147,15 +162,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void d
   constexpr int NT = C / 16;
   constexpr int KV = C * TPR, KIT = (KV + 255) / 256;
   constexpr int QV = RT * TPR, QIT = (QV + 255) / 256;
-  constexpr Chunk16Layout W = chunk16_layout(DK, C, RT);
+  constexpr Chunk16Layout W = chunk16_layout(DK, C, RT, ASYM);
   static_assert(TPR <= 64 && 64 % TPR == 0, "row group must fit in a wavefront");
 
   extern __shared__ __align__(16) unsigned char smem[];
   f16_t* sK = reinterpret_cast<f16_t*>(smem);  // region 0, until M and P are formed
   f16_t* sQ = sK + C * LDK;
+  // write-key rows (fp16, as given); the read keys stand in for them when symmetric
+  f16_t* sKW = ASYM ? sQ + (prep_q_in_regs(DK) ? 0 : RT * LDK) : sK;
   float* sTf = reinterpret_cast<float*>(smem);  // region 0, from the inverse on (packed blocks)
   float* sSc = sTf + prep_m_bytes(C) / 4;
-  float* sA = reinterpret_cast<float*>(smem + prep_region0_bytes(DK, C, RT));
+  float* sA = reinterpret_cast<float*>(smem + prep_region0_bytes(DK, C, RT, ASYM));
   float* sB = sA + prep_m_bytes(C) / 4;
   float* sG = sB + C;
   int* sLoc = reinterpret_cast<int*>(sG + C);
@@ -188,22 +205,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void d
   const int r0 = s0 + (n_h - 1 - (s0 - fastdiv(s0, p.nh_magic, p.nh_shift) * n_h));  // first readout
   const long long tok0 = sg.tok * p.H + h;  // token (sequence start, head h)
   const bf16_t* kp = static_cast<const bf16_t*>(p.k);
+  const bf16_t* kwp = static_cast<const bf16_t*>(p.kt);
   const bf16_t* qp = static_cast<const bf16_t*>(p.q);
   unsigned char* wsc = static_cast<unsigned char*>(p.wsT) + chunk * W.bytes;
 
   // 1. global loads: key rows, readout query rows, beta, gate
   constexpr bool QREG = prep_q_in_regs(DK);
   constexpr int QKS = DK / 32;  // 32-deep steps of a query fragment row
-  u32x4_t rk[KIT], rq[QIT];
+  u32x4_t rk[KIT], rq[QIT], rkw[ASYM ? KIT : 1];
 #pragma unroll
   for (int it = 0; it < KIT; ++it) {
     const int idx = tid + it * 256;
     const int r = idx / TPR, cg = idx % TPR;
     const int s = s0 + r;
     rk[it] = u32x4_t{0u, 0u, 0u, 0u};
+    if constexpr (ASYM) rkw[it] = u32x4_t{0u, 0u, 0u, 0u};
     if (idx < KV && s < N) {
       const int t = fastdiv(s, p.nh_magic, p.nh_shift);
-      rk[it] = ld16(kp + ((tok0 + (long long)t * p.H) * n_h + (s - t * n_h)) * DK + cg * 8);
+      const long long row = ((tok0 + (long long)t * p.H) * n_h + (s - t * n_h)) * DK + cg * 8;
+      rk[it] = ld16(kp + row);
+      if constexpr (ASYM) rkw[it] = ld16(kwp + row);
     }
   }
   float braw = 0.f, lam = 0.f;
@@ -273,6 +294,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void d
 #pragma unroll
     for (int e = 0; e < 8; ++e) f[e] *= rinv;
     if (idx < KV) st_vec16(sK + r * LDK + cg * 8, f);
+    if constexpr (ASYM) {
+      unpack16(rkw[it], f, bf16_t{});
+      if (idx < KV) st_vec16(sKW + r * LDK + cg * 8, f);
+    }
   }
   if constexpr (!QEARLY) load_queries();
   f16x8_t qf[QREG ? NRT : 1][QREG ? QKS : 1];  // QREG: fp16 query fragments
@@ -328,6 +353,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void d
   for (int idx = tid; idx < KV; idx += 256) {
     const int q = idx / C, r = idx % C;
     st16(wsc + W.oK + (q * C + r) * 16, ld16(sK + r * LDK + q * 8));
+    if constexpr (ASYM) st16(wsc + W.oKW + (q * C + r) * 16, ld16(sKW + r * LDK + q * 8));
   }
   if constexpr (QREG) {
     // fragment layout: block 4 t + g holds lane (n, g)'s fragment of step t, row 16 it + n
@@ -372,7 +398,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void d
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < QKS; ++t)
-          acc = mfma32h(lds_a32(sK, LDK, jt * 16 + (lane & 15), 32 * t), qf[it][t], acc);
+          acc = mfma32h(lds_a32(sKW, LDK, jt * 16 + (lane & 15), 32 * t), qf[it][t], acc);
         p_tile(it, jt, acc);
       }
     }
@@ -380,7 +406,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void d
     for (int tile = wave; tile < NRT * NT; tile += 4) {
       const int it = tile / NT, jt = tile % NT;
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mm_ll<DK>(acc, sK, LDK, jt * 16 + (lane & 15), sQ, LDK, it * 16 + (lane & 15));
+      acc = mm_ll<DK>(acc, sKW, LDK, jt * 16 + (lane & 15), sQ, LDK, it * 16 + (lane & 15));
       p_tile(it, jt, acc);
     }
   }
@@ -390,7 +416,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void d
     while (prep_mblock(ti + 1, 0) <= tile) ++ti;
     const int tj = tile - prep_mblock(ti, 0);
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    acc = mm_ll<DK>(acc, sK, LDK, ti * 16 + (lane & 15), sK, LDK, tj * 16 + (lane & 15));
+    acc = mm_ll<DK>(acc, sK, LDK, ti * 16 + (lane & 15), sKW, LDK, tj * 16 + (lane & 15));
     const int jj = tj * 16 + (lane & 15);
     float* mb = sA + tile * kPrepBlk;
 #pragma unroll
@@ -635,13 +661,15 @@ constexpr int kChainCopyWaves = 2;
 // format; the hardware then bounds each access by the resource's byte size.
 constexpr int kBufferDword3 = 0x00020000;
 
-template <int DK, int C, int NWC, int NRT, bool GATED>
+// ASYM: the state update reads the block's write keys (transposed) where the
+// symmetric form reads Kn; everything else is the same.
+template <int DK, int C, int NWC, int NRT, bool GATED, bool ASYM = false>
 __global__ __launch_bounds__(64 * (NWC + kChainCopyWaves)) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void dp_chain_kernel(FwdArgs p) {
   constexpr int RT = 16 * NRT, BV = 16 * NWC;
   constexpr int NCT = C / 16, NDT = DK / 16;
-  constexpr Chunk16Layout W = chunk16_layout(DK, C, RT);
-  constexpr int STG = chain_stages(DK, C, RT, BV);    // LDS ring stages
+  constexpr Chunk16Layout W = chunk16_layout(DK, C, RT, ASYM);
+  constexpr int STG = chain_stages(DK, C, RT, BV, ASYM);  // LDS ring stages
   // With four stages and a pipelined body whose first kLookahead steps are
   // key fragments, the consumers read the next chunk's first operands while
   // finishing the current one, so each chunk must land one chunk earlier.
@@ -652,6 +680,7 @@ void dp_chain_kernel(FwdArgs p) {
   // of the per-chunk scalars at the block's end (its decay factors are all 1
   // and it bounds the readout rows itself), so its copies stop before them.
   constexpr bool PIPE = DK % 32 == 0 && C % 32 == 0;
+  static_assert(!ASYM || PIPE, "the write-key form runs on the pipelined body only");
   constexpr int CB = (PIPE && !GATED) ? W.oS : W.bytes;
   constexpr int NIB = (CB + 1023) / 1024;             // copies per chunk block
   constexpr int NIV = VB / 1024 > 0 ? VB / 1024 : 1;  // copies per value tile
@@ -704,12 +733,17 @@ void dp_chain_kernel(FwdArgs p) {
         }
       };
       region(W.oT, C, C);
-      // the keys keep the plain layout whatever their width (they are also read transposed)
-      if (o >= W.oK && o < W.oK + C * DK * 2) {
-        const int rel = o - W.oK, pb = rel / (C * 16), rs = (rel / 16) % C;
-        const int q = blk_pos(pb, DK);
-        src = W.oK + q * C * 16 + (rs ^ (8 * (q & 1))) * 16;
-      }
+      // the keys keep the plain layout whatever their width (they are also read
+      // transposed); so do the write keys
+      auto keys = [&](int start) {
+        if (o >= start && o < start + C * DK * 2) {
+          const int rel = o - start, pb = rel / (C * 16), rs = (rel / 16) % C;
+          const int q = blk_pos(pb, DK);
+          src = start + q * C * 16 + (rs ^ (8 * (q & 1))) * 16;
+        }
+      };
+      keys(W.oK);
+      if constexpr (ASYM) keys(W.oKW);
       region(W.oQ, RT, DK);
       region(W.oP, RT, C);
       soff[m] = src;
@@ -969,7 +1003,7 @@ void dp_chain_kernel(FwdArgs p) {
         } else {
           constexpr int j = i - S4;
           const unsigned char* q =
-              st + W.oK + ltK + tr_block<DK>(step_tile(j, NDT)) * C * 16 + 32 * step_k(j, NDT) * 16;
+              st + W.oKW + ltK + tr_block<DK>(step_tile(j, NDT)) * C * 16 + 32 * step_k(j, NDT) * 16;
           fr = cat8(__builtin_bit_cast(f16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)q)),
                     __builtin_bit_cast(f16x4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(q + 256))));
         }

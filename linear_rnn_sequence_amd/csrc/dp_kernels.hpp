@@ -131,7 +131,7 @@ struct SeqGeom {
 __device__ __forceinline__ SeqGeom seq_geom(const FwdArgs& p, int d, int h, int C) {
   SeqGeom g;
   if (p.cu == nullptr) {
-    g.tok = (long long)d * p.L;
+    g.tok = tok_base(p, d);  // a token run (FwdArgs::Ls, t0) starts t0 tokens into its sequence
     g.N = p.N;
     g.nc = p.nc;
     g.blk0 = ((long long)d * p.H + h) * p.nc;
@@ -1491,10 +1491,11 @@ hipError_t launch_scan_any(const FwdArgs& a, int BV, int lds, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
-// bf16 with symmetric keys: dp_prep_kernel then dp_chain_kernel.
-template <int DK, int C, int NRT>
+// bf16: dp_prep_kernel then dp_chain_kernel (symmetric keys, or write keys
+// with dk and chunk multiples of 32).
+template <int DK, int C, int NRT, bool ASYM>
 hipError_t launch_prep(const FwdArgs& a, hipStream_t st) {
-  static const bool attr = allow_big_lds(reinterpret_cast<const void*>(&dp_prep_kernel<DK, C, NRT>));
+  static const bool attr = allow_big_lds(reinterpret_cast<const void*>(&dp_prep_kernel<DK, C, NRT, ASYM>));
   (void)attr;
   if (a.cu != nullptr) {
     hipLaunchKernelGGL((dp_varlen_chunks_kernel<C>), dim3(1), dim3(256), 0, st, a.cu, a.B, a.n_h, a.L, a.cbase);
@@ -1503,29 +1504,31 @@ hipError_t launch_prep(const FwdArgs& a, hipStream_t st) {
   }
   const long long nchunks = a.cu != nullptr ? (long long)a.nwork : (long long)a.B * a.H * a.nc;
   if (nchunks == 0) return hipSuccess;
-  hipLaunchKernelGGL((dp_prep_kernel<DK, C, NRT>), dim3((unsigned)nchunks), dim3(256),
-                     prep_lds_bytes(DK, C, 16 * NRT), st, a);
+  hipLaunchKernelGGL((dp_prep_kernel<DK, C, NRT, ASYM>), dim3((unsigned)nchunks), dim3(256),
+                     prep_lds_bytes(DK, C, 16 * NRT, ASYM), st, a);
   return hipGetLastError();
 }
 
-template <int DK, int C, int NWC, int NRT, bool GATED>
+template <int DK, int C, int NWC, int NRT, bool GATED, bool ASYM>
 hipError_t launch_chain_g(const FwdArgs& a, hipStream_t st) {
-  static const bool attr = allow_big_lds(reinterpret_cast<const void*>(&dp_chain_kernel<DK, C, NWC, NRT, GATED>));
+  static const bool attr =
+      allow_big_lds(reinterpret_cast<const void*>(&dp_chain_kernel<DK, C, NWC, NRT, GATED, ASYM>));
   (void)attr;
   const long long nwg = (long long)a.B * a.H * a.nvb;
-  hipLaunchKernelGGL((dp_chain_kernel<DK, C, NWC, NRT, GATED>), dim3((unsigned)nwg), dim3(64 * (NWC + kChainCopyWaves)),
-                     chain_lds_bytes(DK, C, 16 * NRT, 16 * NWC), st, a);
+  hipLaunchKernelGGL((dp_chain_kernel<DK, C, NWC, NRT, GATED, ASYM>), dim3((unsigned)nwg),
+                     dim3(64 * (NWC + kChainCopyWaves)), chain_lds_bytes(DK, C, 16 * NRT, 16 * NWC, ASYM), st, a);
   return hipGetLastError();
 }
 
-template <int DK, int C, int NWC, int NRT>
+template <int DK, int C, int NWC, int NRT, bool ASYM>
 hipError_t launch_chain(const FwdArgs& a, hipStream_t st) {
-  return a.g != nullptr ? launch_chain_g<DK, C, NWC, NRT, true>(a, st) : launch_chain_g<DK, C, NWC, NRT, false>(a, st);
+  return a.g != nullptr ? launch_chain_g<DK, C, NWC, NRT, true, ASYM>(a, st)
+                        : launch_chain_g<DK, C, NWC, NRT, false, ASYM>(a, st);
 }
 
-template <int DK, int C, int NRT>
-hipError_t launch_sym16_nrt(const FwdArgs& a, int BV, int stages, hipStream_t st) {
-  if (a.fused) {
+template <int DK, int C, int NRT, bool ASYM>
+hipError_t launch_pair16_nrt(const FwdArgs& a, int BV, int stages, hipStream_t st) {
+  if (!ASYM && a.fused) {
     if (a.cu != nullptr) {  // packed sequences: per-sequence chunk counts first
       hipLaunchKernelGGL((dp_varlen_chunks_kernel<C>), dim3(1), dim3(256), 0, st, a.cu, a.B, a.n_h, a.L, a.cbase);
       const hipError_t e = hipGetLastError();
@@ -1534,27 +1537,27 @@ hipError_t launch_sym16_nrt(const FwdArgs& a, int BV, int stages, hipStream_t st
     return launch_fused<DK, C, NRT>(a, BV, st);
   }
   if (stages & 1) {
-    const hipError_t e = launch_prep<DK, C, NRT>(a, st);
+    const hipError_t e = launch_prep<DK, C, NRT, ASYM>(a, st);
     if (e != hipSuccess) return e;
   }
   if (stages & 2) {
     switch (BV) {
-      case 16: return launch_chain<DK, C, 1, NRT>(a, st);
-      case 32: return launch_chain<DK, C, 2, NRT>(a, st);
-      case 64: return launch_chain<DK, C, 4, NRT>(a, st);
+      case 16: return launch_chain<DK, C, 1, NRT, ASYM>(a, st);
+      case 32: return launch_chain<DK, C, 2, NRT, ASYM>(a, st);
+      case 64: return launch_chain<DK, C, 4, NRT, ASYM>(a, st);
       default: return hipErrorInvalidValue;
     }
   }
   return hipSuccess;
 }
 
-template <int DK, int C>
-hipError_t launch_sym16(const FwdArgs& a, int BV, int stages, hipStream_t st) {
+template <int DK, int C, bool ASYM>
+hipError_t launch_pair16(const FwdArgs& a, int BV, int stages, hipStream_t st) {
   switch (a.RT / 16) {
-    case 1: return launch_sym16_nrt<DK, C, 1>(a, BV, stages, st);
-    case 2: if constexpr (C >= 32) return launch_sym16_nrt<DK, C, 2>(a, BV, stages, st); break;
-    case 3: if constexpr (C >= 64) return launch_sym16_nrt<DK, C, 3>(a, BV, stages, st); break;
-    case 4: if constexpr (C >= 64) return launch_sym16_nrt<DK, C, 4>(a, BV, stages, st); break;
+    case 1: return launch_pair16_nrt<DK, C, 1, ASYM>(a, BV, stages, st);
+    case 2: if constexpr (C >= 32) return launch_pair16_nrt<DK, C, 2, ASYM>(a, BV, stages, st); break;
+    case 3: if constexpr (C >= 64) return launch_pair16_nrt<DK, C, 3, ASYM>(a, BV, stages, st); break;
+    case 4: if constexpr (C >= 64) return launch_pair16_nrt<DK, C, 4, ASYM>(a, BV, stages, st); break;
   }
   return hipErrorInvalidValue;
 }
@@ -1565,7 +1568,9 @@ hipError_t launch_fwd_dk(const FwdArgs& a, int C, int BV, int lds_scan, int stag
 #define DP_CASE_C(CC)                                                          \
   case CC:                                                                     \
     if constexpr (sizeof(T) == 2) {                                            \
-      if (!a.asym) return launch_sym16<DK, CC>(a, BV, stages, st);             \
+      if (!a.asym) return launch_pair16<DK, CC, false>(a, BV, stages, st);     \
+      if constexpr (chain_asym_ok(DK, CC))                                     \
+        return launch_pair16<DK, CC, true>(a, BV, stages, st);                 \
     }                                                                          \
     if (stages & 1) {                                                          \
       e = launch_ut<T, DK, CC>(a, st);                                         \

@@ -170,6 +170,19 @@ def select_state(t: torch.Tensor, heads, H: int) -> torch.Tensor:
     return torch.cat(parts, dim=1).contiguous()
 
 
+def write_keys(w: Workload, seed: int) -> torch.Tensor:
+    """Seeded write keys for the write-key forward, [B, L, H, n_h, dk] in the
+    path dtype: a random direction N(0,1)/sqrt(dk) per sub-step times a
+    per-channel factor drawn uniformly from [0.5, 2] per (b, h) -- the shape
+    and range of the phase-1 write keys d * kn, without running phase 1."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(seed)
+    B, L, H, n_h, dk = w.B, w.L, w.H, w.n_h, w.dk
+    kt = torch.randn(B, L, H, n_h, dk, generator=gen, dtype=torch.float32) / dk ** 0.5
+    d = 0.5 + 1.5 * torch.rand(B, 1, H, 1, dk, generator=gen, dtype=torch.float32)
+    return (kt * d).to(torch_dtype(w.dtype)).contiguous()
+
+
 def retention(B: int, L: int, H: int, seed: int, bias: float = 3.0) -> torch.Tensor:
     """Per-token, per-head retention values in (0, 1) for the preconditioner
     (the APF gate is a sigmoid of a learned projection; here sigmoid(N(0,1) +

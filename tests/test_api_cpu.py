@@ -63,13 +63,14 @@ def ws(n_h, B, H, L, dk, dv, chunk, elem):
     return rc, out.value
 
 
-def bf16_chunk_block(dk, C, n_h):
+def bf16_chunk_block(dk, C, n_h, write_keys=False):
     """Bytes of one chunk's operand block on the bf16 path: T diag(beta), unit
-    keys (C x dk), readout queries (RT x dk), scores (RT x C), all fp16, then
-    e^G, e^{G_last - G} (C floats each), e^{G_loc} (RT floats) and the output
-    offsets (RT int64, 8-byte aligned); RT = ceil(C / n_h) in 16s.  T diag(beta)
-    is C x C, except that with dk and C multiples of 32 and C > 32 its 32-column
-    tile t keeps only rows 32 t .. C-1 (the rows above are zero)."""
+    keys (C x dk), the write keys (C x dk, write-key form only), readout queries
+    (RT x dk), scores (RT x C), all fp16, then e^G, e^{G_last - G} (C floats
+    each), e^{G_loc} (RT floats) and the output offsets (RT int64, 8-byte
+    aligned); RT = ceil(C / n_h) in 16s.  T diag(beta) is C x C, except that
+    with dk and C multiples of 32 and C > 32 its 32-column tile t keeps only
+    rows 32 t .. C-1 (the rows above are zero)."""
     r = -(-C // n_h)
     RT = C if r >= C else -(-r // 16) * 16
     scal = (8 * C + 4 * RT + 7) // 8 * 8 + 8 * RT
@@ -77,16 +78,21 @@ def bf16_chunk_block(dk, C, n_h):
         t_elems = sum(32 * (C - 32 * t) for t in range(C // 32))
     else:
         t_elems = C * C
-    return 2 * (t_elems + C * dk + RT * dk + RT * C) + (scal + 15) // 16 * 16
+    kw = C * dk if write_keys else 0
+    return 2 * (t_elems + C * dk + kw + RT * dk + RT * C) + (scal + 15) // 16 * 16
 
 
 def test_workspace_size_formula(lib):
+    """One size serves the symmetric and the write-key forward: where the
+    write-key form runs on the prep / chain pair (dk and chunk multiples of 32)
+    the blocks are sized with the write keys."""
     rc, n = ws(3, 4, 16, 4096, 128, 128, 64, 2)
     assert rc == 0
     nc = 4096 * 3 // 64
     assert bf16_chunk_block(128, 64, 3) == 35712
+    assert bf16_chunk_block(128, 64, 3, write_keys=True) == 35712 + 64 * 128 * 2
     sink = 4 * 16 * (128 // 16) * 64 * 4  # one fp32 slot per lane of every scan wavefront
-    assert n == -(-4 * 16 * nc * 35712 // 256) * 256 + sink
+    assert n == -(-4 * 16 * nc * (35712 + 16384) // 256) * 256 + sink
     rc, n = ws(2, 1, 1, 33, 16, 16, 16, 2)  # ragged: 66 sub-steps -> 5 chunks
     assert rc == 0 and n == -(-5 * bf16_chunk_block(16, 16, 2) // 256) * 256 + 256
     rc, n = ws(2, 1, 1, 33, 16, 16, 16, 4)  # ragged: 66 sub-steps -> 5 chunks

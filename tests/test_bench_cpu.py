@@ -81,8 +81,13 @@ def test_traffic_record_is_dropped_when_the_kernels_change(tmp_path, monkeypatch
     prof.mkdir()
     (prof / "traffic_k_w.json").write_text(json.dumps(rec))
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    monkeypatch.setattr(bench, "source_digest", lambda: "abc")
+    monkeypatch.setattr(bench, "source_digest", lambda kernel=None: "abc")
     assert bench.measured_traffic("w", "k") == 123.0
-    monkeypatch.setattr(bench, "source_digest", lambda: "def")
+    monkeypatch.setattr(bench, "source_digest", lambda kernel=None: "def")
     assert bench.measured_traffic("w", "k") is None
     assert bench.measured_traffic("w", "missing") is None
+
+
+def test_fused_header_only_enters_the_fused_kernels_digest():
+    assert bench.source_digest("dp_chain_kernel") == bench.source_digest("dp_prep_kernel")
+    assert bench.source_digest("dp_fused_kernel") != bench.source_digest("dp_chain_kernel")
