@@ -1148,10 +1148,12 @@ __global__ __launch_bounds__(64) void dp_precond_kernel(PrecondArgs p) {
   };
 
   if constexpr (LPH == 64) {
-    // One head per wavefront.  Lane j also owns token t0 + j of the block: it
+    // One head per wavefront (the grid has one per head: every lane is active).
+    // Lane j also owns token t0 + j of the block: it
     // loads that token's whole key row, beta and retention one block ahead
     // and forms the token's scalars (1/max(|k|, 1e-6), the step factor, the
     // clamped beta); the sequential part reads them with v_readlane.
+    if (!active) return;
     constexpr int PB = sizeof(T) == 2 ? 64 : 32;  // tokens per block
     constexpr int RB = DK * (int)sizeof(T);       // bytes per key row
     static_assert(RB % 16 == 0, "key rows in 16-byte pieces");
@@ -1216,7 +1218,7 @@ __global__ __launch_bounds__(64) void dp_precond_kernel(PrecondArgs p) {
             ds = fmaf(d[e], sq[e], ds);
           }
           ds = head_sum<LPH>(ds);
-          if (active) store_kt_at(kto, kh);
+          store_kt_at(kto, kh);
           kto += kstride;
           const float coef = fmaf(-bw, ds, w);
           if constexpr (RET) {
@@ -1255,10 +1257,8 @@ __global__ __launch_bounds__(64) void dp_precond_kernel(PrecondArgs p) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) sc[i][e] = sn[i][e];
     }
-    if (active) {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) p.d[bh * DK + sl * EPL + e] = d[e];
-    }
+    for (int e = 0; e < EPL; ++e) p.d[bh * DK + sl * EPL + e] = d[e];
     return;
   }
 

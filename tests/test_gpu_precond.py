@@ -132,3 +132,33 @@ def test_precond_variants_full_size_sampled_heads():
                              r=select_heads(r, heads, w.H), beta_aware=False)
     check_phase1(select_heads(ktg.cpu(), heads, w.H), kto, select_state(dg.cpu(), heads, w.H), do,
                  "bf16", "full-c5-variant")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_precond_clamps_and_nans_inside_full_blocks(dtype):
+    """The dk >= 64 scan runs each full block of tokens speculatively (no
+    coordinate clamped) and falls back to the exact step when a clamp or a NaN
+    shows up.  With eta = 0.5 the box [0.5, 2] binds inside full blocks, and a
+    NaN beta in the middle of a block of one head must poison that head from
+    the next token on exactly as the oracle's clamp (which keeps NaN) does,
+    while the other heads meet the bound.  With eta = 0.5 and the box [0.9,
+    1.1] the clean heads first clamp at tokens 74 and 95, inside full blocks,
+    and clamp on most tokens after that."""
+    w = WORKLOADS["c5"].scaled(B=1, H=3, L=256, dk=128, dv=128, dtype=dtype)
+    inp = make(w)
+    k1 = inp["k"][:, :, :, 0, :].contiguous()
+    b1 = inp["beta"][..., 0].contiguous().clone()
+    b1[0, 100, 1] = float("nan")
+    say(f"case precond clamps/NaN {dtype}")
+    ktg, dg = dp.osdn_precond(k1.cuda(), b1.cuda(), eta=0.5, dmin=0.9, dmax=1.1)
+    torch.cuda.synchronize()
+    kto, do = oracle.precond(k1, b1, eta=0.5, dmin=0.9, dmax=1.1)
+    g, o = f64(ktg), kto
+    assert np.array_equal(np.isnan(g), np.isnan(o)), "NaN positions of the write keys differ"
+    assert np.array_equal(np.isnan(f64(dg)), np.isnan(do))
+    assert np.isnan(o[0, 101:, 1]).all() and not np.isnan(o[0, :101, 1]).any()
+    keep = [0, 2]
+    check_phase1(ktg[:, :, keep], kto[:, :, keep], dg[:, keep], do[:, keep], dtype, "clamps")
+    # the box binds: some coordinates of the clean heads end on a bound
+    dd = do[:, keep]
+    assert (np.abs(dd - 0.9) < 1e-9).any() or (np.abs(dd - 1.1) < 1e-9).any()
