@@ -99,17 +99,32 @@ def source_digest(kernel=None):
     return hsh.hexdigest()
 
 
-def measured_traffic(workload, kernel):
-    """HBM bytes per launch of `kernel` for `workload` from the committed counter
-    summary, or None when there is none or the kernel sources changed since."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+def counter_record(kind, workload, kernel):
+    """The committed counter record profiles/<kind>_<kernel>_<workload>.json,
+    or None when there is none or the kernel's sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"{kind}_{kernel}_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
     if rec.get("source_sha256") != source_digest(kernel):
         return None
-    return rec.get("bytes_per_launch")
+    return rec
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` for `workload` from the committed counter
+    summary, or None when there is none or the kernel sources changed since."""
+    rec = counter_record("traffic", workload, kernel)
+    return None if rec is None else rec.get("bytes_per_launch")
+
+
+def measured_mfma_busy(workload, kernel):
+    """Fraction of the chip's SIMD cycles the MFMA units were busy during
+    `kernel` (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE / 8 XCDs x 1024
+    SIMDs), from the committed counter record, or None."""
+    rec = counter_record("mfma", workload, kernel)
+    return None if rec is None else rec.get("mfma_busy_frac")
 
 
 # ---------------------------------------------------------------- accounting
@@ -212,6 +227,20 @@ def issued_flops(w, plan):
         return heads * nc * ut, heads * nc * per16 * (dv // 16)
     scan = 2 * (C * BV * dk + C * RT * dk + RT * BV * dk + C * C * BV + RT * C * BV + dk * C * BV)
     return heads * nc * ut, heads * nc * scan * (dv // BV)
+
+
+def roofline_fields(kernel, kernel_ms, kernel_bytes, step_bytes, step_ms, traffic):
+    """The line's roofline object: the dominant kernel's algorithmic bytes over
+    its event-timed duration against the HBM peak, and the whole step's
+    algorithmic bytes over ms_per_step beside it."""
+    achieved = kernel_bytes / (kernel_ms * 1e6)
+    step = step_bytes / (step_ms * 1e6)
+    return {"kernel": kernel, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+            "alg_bytes_per_launch": kernel_bytes, "step_achieved": step,
+            "step_frac": step / HBM_PEAK_GBS,
+            "note": "achieved: the kernel's own algorithmic bytes over its event-timed "
+                    "duration; step_*: the whole step's algorithmic bytes over ms_per_step"}
 
 
 # ---------------------------------------------------------------- GPU timing
@@ -518,6 +547,15 @@ def cpu_baseline(w, inp, nheads, min_seconds=10.0, max_pass_seconds=30.0, max_pa
 
     threads = oracle.num_threads()
     total = w.B * w.H
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
 
     def prepare(heads):
         sub = {k: (None if inp[k] is None else select_heads(inp[k], heads, w.H))
@@ -529,14 +567,14 @@ def cpu_baseline(w, inp, nheads, min_seconds=10.0, max_pass_seconds=30.0, max_pa
                                            .to(torch.float64).numpy()))
         return conv
 
-    def one_pass(c):
+    def one_pass(c, nthreads=0):
         t0 = time.perf_counter()
         if w.asym:
-            kt, _ = oracle.precond(c["k"][:, :, :, 0, :], c["beta"][..., 0])
+            kt, _ = oracle.precond(c["k"][:, :, :, 0, :], c["beta"][..., 0], nthreads=nthreads)
             oracle.fwd(c["q"], c["k"], c["v"], c["beta"], g=c["g"], kt=kt[:, :, :, None, :],
-                       h0=c["h0"])
+                       h0=c["h0"], nthreads=nthreads)
         else:
-            oracle.fwd(c["q"], c["k"], c["v"], c["beta"], g=c["g"], h0=c["h0"])
+            oracle.fwd(c["q"], c["k"], c["v"], c["beta"], g=c["g"], h0=c["h0"], nthreads=nthreads)
         return time.perf_counter() - t0
 
     if nheads:
@@ -561,11 +599,22 @@ def cpu_baseline(w, inp, nheads, min_seconds=10.0, max_pass_seconds=30.0, max_pa
     value = len(heads) * w.L / w.H / t   # whole-workload tokens/s at this rate
     what = ("the whole workload" if len(heads) == total
             else f"{len(heads)} of {total} heads (b,h)")
+    # the same oracle on one thread, on a few heads (about two seconds)
+    few = sampled_heads(w.B, w.H, min(total, 2))
+    c1 = prepare(few)
+    t1s, t_start = [], time.perf_counter()
+    while not t1s or (time.perf_counter() - t_start < 2.0 and len(t1s) < 5):
+        t1s.append(one_pass(c1, nthreads=1))
+    t1 = statistics.median(t1s)
     return {"value": value, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{what} of {w.name}, full L={w.L}, all {w.n_h} sub-steps per token"
                       f"{', phase 1 included' if w.asym else ''}; fp64 sequential recurrence; "
                       f"median of {len(times)} passes ({sum(times):.1f}s wall) on {threads} threads",
-            "seconds_per_pass": t}
+            "seconds_per_pass": t, "cpu_model": model,
+            "one_thread": {"value": len(few) * w.L / w.H / t1, "unit": "tokens/s",
+                           "sample": f"{len(few)} heads of {w.name}, full L, median of {len(t1s)} passes "
+                                     f"on 1 thread",
+                           "speedup_of_cores": value / (len(few) * w.L / w.H / t1)}}
 
 
 # ---------------------------------------------------------------- main
@@ -608,6 +657,7 @@ def main():
         fi = fused_issued_flops(w, r["plan"])
         kernels = {"dp_fused_kernel": {"ms": r["ut_ms"], "issued_tflops": fi / (r["ut_ms"] * 1e9),
                                        "issued_frac": fi / (r["ut_ms"] * 1e9) / peak_mfma,
+                                       "mfma_busy_counter": measured_mfma_busy(w.name, "dp_fused_kernel"),
                                        "workgroups": r["plan"]["scan_wgs"],
                                        "value_columns": r["plan"]["BV"]}}
     else:
@@ -615,8 +665,12 @@ def main():
         ut_name, scan_name = kernel_names(w)
         kernels = {
             ut_name: {"ms": r["ut_ms"], "issued_tflops": ut_issued / (r["ut_ms"] * 1e9),
+                      "issued_frac": ut_issued / (r["ut_ms"] * 1e9) / peak_mfma,
+                      "mfma_busy_counter": measured_mfma_busy(w.name, ut_name),
                       "workgroups": r["plan"]["ut_wgs"]},
             scan_name: {"ms": r["scan_ms"], "issued_tflops": scan_issued / (r["scan_ms"] * 1e9),
+                        "issued_frac": scan_issued / (r["scan_ms"] * 1e9) / peak_mfma,
+                        "mfma_busy_counter": measured_mfma_busy(w.name, scan_name),
                         "workgroups": r["plan"]["scan_wgs"], "value_columns": r["plan"]["BV"]},
         }
     if w.asym:
@@ -629,7 +683,6 @@ def main():
     dom = max(kernels, key=lambda k: kernels[k]["ms"])
     dom_ms = kernels[dom]["ms"]
     dom_bytes = ab if dom != "dp_precond_kernel" else precond_bytes(w)
-    achieved = dom_bytes / (dom_ms * 1e6)
     step_bytes = ab + (precond_bytes(w) if w.asym else 0)
     line = {
         "metric": METRIC,
@@ -652,13 +705,8 @@ def main():
         "recurrent_tflops": rf / (r["ms_per_step"] * 1e9),
         "alg_gbs": ab / (r["ms_per_step"] * 1e6),
         "kernels": kernels,
-        "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(w.name, dom), "alg_bytes_per_launch": dom_bytes,
-                     "step_achieved": step_bytes / (r["ms_per_step"] * 1e6),
-                     "step_frac": step_bytes / (r["ms_per_step"] * 1e6) / HBM_PEAK_GBS,
-                     "note": "achieved: the kernel's own algorithmic bytes over its event-timed "
-                             "duration; step_*: the whole step's algorithmic bytes over ms_per_step"},
+        "roofline": roofline_fields(dom, dom_ms, dom_bytes, step_bytes, r["ms_per_step"],
+                                    measured_traffic(w.name, dom)),
         "clock_settle": {"steps": r["settled"][0], "seconds": r["settled"][1],
                          "note": "untimed steps run before the warm-up so that the timed steps see "
                                  "settled clocks"},

@@ -91,3 +91,64 @@ def test_traffic_record_is_dropped_when_the_kernels_change(tmp_path, monkeypatch
 def test_fused_header_only_enters_the_fused_kernels_digest():
     assert bench.source_digest("dp_chain_kernel") == bench.source_digest("dp_prep_kernel")
     assert bench.source_digest("dp_fused_kernel") != bench.source_digest("dp_chain_kernel")
+
+
+def test_issued_flops_of_the_pair_c3():
+    """Per chunk: the prep forms the 10 lower 16 x 16 Gram blocks over dk (fp16),
+    the blocked fp32 inverse ((NT - dist)(dist + 1) 16^3 products per level)
+    and the readout scores (RT x C x dk); the chain, per 16 value columns, Kn H,
+    T X, Q H, P Up and the state update."""
+    w = WORKLOADS["c3"]
+    C, dk, RT = 64, 128, 32
+    nc = w.B * w.H * (w.L * w.n_h // C)
+    gram = 10 * 16 * 16 * dk * 2
+    inverse = sum((4 - dist) * (dist + 1) * 16 ** 3 * 2 for dist in range(1, 4))
+    scores = 2 * RT * C * dk
+    per16 = 2 * 16 * (C * dk + C * C + RT * dk + RT * C + dk * C)
+    prep, chain = bench.issued_flops(w, {"BV": 32, "readout_rows": RT})
+    assert prep == nc * (gram + inverse + scores)
+    assert chain == nc * per16 * (128 // 16)
+
+
+def test_issued_flops_of_the_fused_kernel():
+    """Every workgroup of a head builds its chunk's operands: the Gram's lower
+    tiles, the scores, two split-fp16 off-diagonal T products per 32-row half;
+    the consumers run Kn H, Q H, the solve steps, P Up and the state update."""
+    w = WORKLOADS["c3"].scaled(B=1, H=2, L=64, n_h=2, dk=64, dv=32)
+    C, dk, dv, BV, RT = 64, 64, 32, 32, 32
+    nc = 2
+    prod = 10 * 2 * 16 * 16 * dk + 2 * RT * C * dk + 2 * 2 * 2 * 2 * 16 * 16 * 32
+    solve = (2 + 4) * 2 * 16 * 16 * 32
+    cons16 = 2 * 16 * (C * dk + RT * dk + RT * C + dk * C) + solve
+    expect = 2 * nc * ((dv // BV) * prod + (dv // 16) * cons16)
+    assert bench.fused_issued_flops(w, {"BV": BV, "readout_rows": RT}) == expect
+
+
+def test_roofline_fields():
+    r = bench.roofline_fields("k", 0.2, 544e6, 600e6, 0.35, None)
+    assert r["achieved"] == pytest.approx(544e6 / 0.2e6)
+    assert r["frac"] == pytest.approx(544e6 / 0.2e6 / 8000)
+    assert r["step_achieved"] == pytest.approx(600e6 / 0.35e6)
+    assert r["step_frac"] == pytest.approx(600e6 / 0.35e6 / 8000)
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0 and r["traffic"] is None
+
+
+def test_mfma_record_is_read_only_for_the_current_sources(tmp_path, monkeypatch):
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    (prof / "mfma_k_w.json").write_text(json.dumps({"source_sha256": "abc", "mfma_busy_frac": 0.164}))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "source_digest", lambda kernel=None: "abc")
+    assert bench.measured_mfma_busy("w", "k") == 0.164
+    monkeypatch.setattr(bench, "source_digest", lambda kernel=None: "def")
+    assert bench.measured_mfma_busy("w", "k") is None
+
+
+def test_cpu_baseline_reports_cores_model_and_one_thread():
+    """The oracle timed on this host on a tiny workload: the fields the line carries."""
+    from linear_rnn_sequence_amd.inputs import make
+    w = WORKLOADS["c1"].scaled(B=2, H=2, L=32)
+    r = bench.cpu_baseline(w, make(w), 0, min_seconds=0.05)
+    assert r["kind"] == "oracle" and r["unit"] == "tokens/s" and r["cores"] >= 1
+    assert r["value"] > 0 and r["one_thread"]["value"] > 0
+    assert "cpu_model" in r
