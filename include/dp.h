@@ -152,7 +152,16 @@ int dp_fwd_wk_bf16(const void* q, const void* k, const void* kt, const void* v,
 
 /*
  * General form of the forward: kt may be NULL (symmetric, as dp_fwd_*) or a
- * write-key tensor (as dp_fwd_wk_*), and `flags` is an OR of
+ * write-key tensor (as dp_fwd_wk_*); ga may be NULL or the per-key-channel
+ * gate of the KDA host (OSDN notes sec. 2.7):
+ *   ga    [B, L, H, dk]         f32   alpha_t in (0, 1]: before token t's
+ *                                     sub-steps, state row (key channel) c is
+ *                                     multiplied by ga[t][c] (then by g[t])
+ * With ga the forward runs the UT and scan kernels for either input type
+ * (fp32 arithmetic on the fp32 path, fp16 operands on the bf16 path, as
+ * elsewhere): each decay factor is formed for its own pair of sub-steps and is
+ * at most 1, so no channel's decay can overflow an operand.  A gate of 0 is
+ * taken as FLT_MIN.  `flags` is an OR of
  *   DP_STAGE_UT    run the per-chunk prep + UT launch (fills the workspace)
  *   DP_STAGE_SCAN  run the chunk-scan launch (reads the workspace; writes out
  *                  and final_state)
@@ -166,7 +175,7 @@ int dp_fwd_wk_bf16(const void* q, const void* k, const void* kt, const void* v,
  *   DP_FWD_SPLIT   symmetric bf16 keys: run the two-kernel path (a prep kernel
  *                  writes each chunk's operand blocks to the workspace, a chain
  *                  kernel reads them)
- *   DP_FWD_FUSED   symmetric bf16 keys, dk and chunk multiples of 32, both
+ *   DP_FWD_FUSED   symmetric bf16 keys, no ga, dk and chunk multiples of 32, both
  *                  stages: run the single fused kernel (each workgroup builds
  *                  its chunk's operands in LDS; no workspace is read or written,
  *                  and `workspace` may be NULL with workspace_bytes 0).
@@ -186,12 +195,12 @@ int dp_fwd_wk_bf16(const void* q, const void* k, const void* kt, const void* v,
 #define DP_FWD_FUSED 16
 
 int dp_fwd_ex_f32(const float* q, const float* k, const float* kt, const float* v,
-                  const float* beta, const float* g, int n_h, int B, int H, int L, int dk,
-                  int dv, int chunk, float* out, float* final_state, const float* h0,
+                  const float* beta, const float* g, const float* ga, int n_h, int B, int H, int L,
+                  int dk, int dv, int chunk, float* out, float* final_state, const float* h0,
                   void* workspace, size_t workspace_bytes, int flags, dp_stream stream);
 int dp_fwd_ex_bf16(const void* q, const void* k, const void* kt, const void* v,
-                   const float* beta, const float* g, int n_h, int B, int H, int L, int dk,
-                   int dv, int chunk, void* out, float* final_state, const float* h0,
+                   const float* beta, const float* g, const float* ga, int n_h, int B, int H, int L,
+                   int dk, int dv, int chunk, void* out, float* final_state, const float* h0,
                    void* workspace, size_t workspace_bytes, int flags, dp_stream stream);
 
 /*

@@ -74,7 +74,7 @@ def load() -> ctypes.CDLL:
         for name in ("dp_fwd_wk_f32", "dp_fwd_wk_bf16"):
             getattr(lib, name).restype = _I
             getattr(lib, name).argtypes = wk_args
-        ex = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P,
+        ex = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P,
               ctypes.c_size_t, _I, _P]
         for name in ("dp_fwd_ex_f32", "dp_fwd_ex_bf16"):
             getattr(lib, name).restype = _I
@@ -184,7 +184,7 @@ def alloc_workspace(n_h, B, H, L, dk, dv, chunk, dtype, device) -> torch.Tensor:
     return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
 
 
-def fwd(q, k, v, beta, g=None, *, chunk: int = 64, h0=None, kt=None, out=None,
+def fwd(q, k, v, beta, g=None, *, chunk: int = 64, h0=None, kt=None, ga=None, out=None,
         final_state=None, return_state: bool = True, workspace=None,
         stages: int = STAGE_ALL, out_dtype=None, path: str = "auto",
         stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
@@ -192,7 +192,8 @@ def fwd(q, k, v, beta, g=None, *, chunk: int = 64, h0=None, kt=None, out=None,
 
     q [B,L,H,dk], k [B,L,H,n_h,dk], v [B,L,H,n_h,dv] (float32 or bfloat16, one
     dtype), beta [B,L,H,n_h] f32, g [B,L,H] f32 or None, h0 [B,H,dk,dv] f32 or
-    None, kt (write keys, shape of k) or None.  out_dtype: the input dtype
+    None, kt (write keys, shape of k) or None, ga [B,L,H,dk] f32 (the per-key-
+    channel gate of the KDA host) or None.  out_dtype: the input dtype
     (default) or torch.float32.  path (bf16 symmetric keys): "auto" lets the
     library choose, "split" runs the chunk-prep / chain kernel pair, "fused"
     the single fused kernel (same results up to rounding).  Returns (out, final_state); final_state is
@@ -209,6 +210,7 @@ def fwd(q, k, v, beta, g=None, *, chunk: int = 64, h0=None, kt=None, out=None,
     _need(v, "v", dt, (B, L, H, n_h, dv), dev)
     _need(beta, "beta", torch.float32, (B, L, H, n_h), dev)
     _need(g, "g", torch.float32, (B, L, H), dev)
+    _need(ga, "ga", torch.float32, (B, L, H, dk), dev)
     _need(h0, "h0", torch.float32, (B, H, dk, dv), dev)
     if not q.is_contiguous():
         raise ValueError("q must be contiguous")
@@ -227,7 +229,7 @@ def fwd(q, k, v, beta, g=None, *, chunk: int = 64, h0=None, kt=None, out=None,
     if workspace is None:
         workspace = alloc_workspace(n_h, B, H, L, dk, dv, chunk, dt, dev)
     fn = getattr(load(), f"dp_fwd_ex_{suf}")
-    rc = fn(_ptr(q), _ptr(k), _ptr(kt), _ptr(v), _ptr(beta), _ptr(g), n_h, B, H, L, dk, dv,
+    rc = fn(_ptr(q), _ptr(k), _ptr(kt), _ptr(v), _ptr(beta), _ptr(g), _ptr(ga), n_h, B, H, L, dk, dv,
             chunk, _ptr(out), _ptr(final_state), _ptr(h0), _ptr(workspace),
             workspace.numel() * workspace.element_size(), flags, _stream(stream))
     _check(rc, f"dp_fwd_ex_{suf}")

@@ -96,9 +96,18 @@ size_t ws_blocks_bytes(const Shape& s) {
 // One fp32 slot per lane of every scan wavefront (at most dv / 16 per head).
 size_t ws_sink_bytes(const Shape& s) { return align_up((size_t)s.B * s.H * (s.dv / 16) * 64 * 4, kWsAlign); }
 
+// The per-channel-gate form (UT / scan kernels) keeps T, the per-sub-step
+// scalars and the readout scores (RT x C) per chunk.
+size_t ws_s_bytes(const Shape& s) { return align_up((size_t)s.B * s.H * num_chunks(s) * s.chunk * sizeof(float2), kWsAlign); }
+size_t ws_cg_bytes(const Shape& s, int elem) {
+  return ws_t_bytes(s, elem) + ws_s_bytes(s) +
+         align_up((size_t)s.B * s.H * num_chunks(s) * readout_rows(s.chunk, s.n_h) * s.chunk * elem, kWsAlign);
+}
+
 size_t ws_total(const Shape& s, int elem) {
-  if (elem == 2) return ws_blocks_bytes(s) + ws_sink_bytes(s);
-  return ws_t_bytes(s, elem) + (size_t)s.B * s.H * num_chunks(s) * s.chunk * sizeof(float2);
+  const size_t cg = ws_cg_bytes(s, elem);
+  size_t base = elem == 2 ? ws_blocks_bytes(s) + ws_sink_bytes(s) : ws_t_bytes(s, elem) + ws_s_bytes(s);
+  return base > cg ? base : cg;
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -127,8 +136,9 @@ int scan_layout(dp::FwdArgs& a, int elem, int DK, int C, int BV) {
     off += a16(bytes);
     return o;
   };
+  const bool cg = a.ga != nullptr;
   a.oK = take(C * LDK * elem);
-  a.oKt = a.asym ? take(C * LDK * elem) : a.oK;
+  a.oKt = (a.asym || cg) ? take(C * LDK * elem) : a.oK;
   // the readout queries are dead after the first phase of a chunk and Up / Us
   // are written after it: they share one region
   const int q_bytes = a.RT * LDK * elem, u_bytes = a16(BV * LDC * elem);
@@ -146,10 +156,11 @@ int scan_layout(dp::FwdArgs& a, int elem, int DK, int C, int BV) {
   a.oLoc = take(a.RT * 4);
   a.oRow = take(2 * C * 8);
   a.oTok = take(2 * a.RT * 8);
+  a.oDec = cg ? take(DK * 4) : 0;
   return off;
 }
 
-int ut_lds(int elem, int DK, int C, int asym) { return dp::ut_lds_bytes(elem, DK, C, asym); }
+int ut_lds(int elem, int DK, int C, int asym, int cg = 0) { return dp::ut_lds_bytes(elem, DK, C, asym, cg); }
 
 // Value-block width of the scan: the widest BV (fewer redundant key-side
 // products per head) that still gives at least one workgroup per CU
@@ -210,8 +221,22 @@ int check_fwd_flags(int elem, bool asym, int dk, int chunk, int flags) {
   return DP_OK;
 }
 
-// Choose BV and fill the scan layout of `a` (a.RT, a.asym and a.fused must be set).
+// Choose BV and fill the scan layout of `a` (a.RT, a.asym, a.fused and a.ga must be set).
 int plan(dp::FwdArgs& a, int elem, int dk, int chunk, int* BV_out, int* lds_out) {
+  if (a.ga != nullptr) {  // per-channel gate: the UT / scan kernels for either input type
+    int BV = pick_bv(a.B * a.H, a.dv);
+    int lds = 0;
+    for (;; BV >>= 1) {
+      if (BV < 16) return DP_ENOTSUP;
+      lds = scan_layout(a, elem, dk, chunk, BV);
+      if (lds <= kMaxLds) break;
+    }
+    if (ut_lds(elem, dk, chunk, a.asym, 1) > kMaxLds) return DP_ENOTSUP;
+    a.nvb = a.dv / BV;
+    *BV_out = BV;
+    *lds_out = lds;
+    return DP_OK;
+  }
   if (a.fused) {
     // one or two consumer wavefronts: all of dv up to 32 columns in one workgroup
     int BV = a.dv <= 32 ? a.dv : pick_bv16(a.B * a.H, a.dv);
@@ -307,7 +332,7 @@ int fwd_impl(int elem, const void* q, const void* k, const void* kt, const void*
              const float* beta, const float* g, int n_h, int B, int H, int L, int dk, int dv,
              int chunk, void* out, float* final_state, const float* h0, void* workspace,
              size_t workspace_bytes, int flags, dp_stream stream, int Ls = 0, int t0 = 0,
-             bool dry = false) {
+             bool dry = false, const float* ga = nullptr) {
   const Shape s{n_h, B, H, L, dk, dv, chunk};
   int rc = check_shape(s);
   if (rc != DP_OK) return rc;
@@ -319,7 +344,8 @@ int fwd_impl(int elem, const void* q, const void* k, const void* kt, const void*
     return DP_EINVAL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || (kt != nullptr && !aligned16(kt)))
     return DP_EINVAL;
-  const bool fused = use_fused(elem, kt != nullptr, dk, dv, chunk, flags);
+  if (ga != nullptr && (flags & DP_FWD_FUSED) != 0) return DP_ENOTSUP;  // the fused kernel has no channel gate
+  const bool fused = ga == nullptr && use_fused(elem, kt != nullptr, dk, dv, chunk, flags);
   const size_t need = fused ? 0 : ws_total(s, elem);
   if (workspace_bytes < need || (need > 0 && workspace == nullptr)) return DP_EWORKSPACE;
   if (need > 0 && ((uintptr_t)workspace & (kWsAlign - 1)) != 0) return DP_EWORKSPACE;
@@ -339,7 +365,9 @@ int fwd_impl(int elem, const void* q, const void* k, const void* kt, const void*
     a.wsT = workspace;
     a.wsS = reinterpret_cast<float2*>(static_cast<char*>(workspace) + ws_t_bytes(s, elem));
     if (elem == 2) a.sink = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws_blocks_bytes(s));
+    if (ga != nullptr) a.wsP = static_cast<char*>(workspace) + ws_t_bytes(s, elem) + ws_s_bytes(s);
   }
+  a.ga = ga;
   a.N = L * n_h;
   a.B = B;
   a.H = H;
@@ -800,19 +828,19 @@ int dp_fwd_wk_bf16(const void* q, const void* k, const void* kt, const void* v,
 }
 
 int dp_fwd_ex_f32(const float* q, const float* k, const float* kt, const float* v,
-                  const float* beta, const float* g, int n_h, int B, int H, int L, int dk,
-                  int dv, int chunk, float* out, float* final_state, const float* h0,
+                  const float* beta, const float* g, const float* ga, int n_h, int B, int H, int L,
+                  int dk, int dv, int chunk, float* out, float* final_state, const float* h0,
                   void* workspace, size_t workspace_bytes, int flags, dp_stream stream) {
   return fwd_impl(4, q, k, kt, v, beta, g, n_h, B, H, L, dk, dv, chunk, out, final_state, h0,
-                  workspace, workspace_bytes, flags, stream);
+                  workspace, workspace_bytes, flags, stream, 0, 0, false, ga);
 }
 
 int dp_fwd_ex_bf16(const void* q, const void* k, const void* kt, const void* v,
-                   const float* beta, const float* g, int n_h, int B, int H, int L, int dk,
-                   int dv, int chunk, void* out, float* final_state, const float* h0,
+                   const float* beta, const float* g, const float* ga, int n_h, int B, int H, int L,
+                   int dk, int dv, int chunk, void* out, float* final_state, const float* h0,
                    void* workspace, size_t workspace_bytes, int flags, dp_stream stream) {
   return fwd_impl(2, q, k, kt, v, beta, g, n_h, B, H, L, dk, dv, chunk, out, final_state, h0,
-                  workspace, workspace_bytes, flags, stream);
+                  workspace, workspace_bytes, flags, stream, 0, 0, false, ga);
 }
 
 int dp_osdn_precond_f32(const float* k, const float* beta, int B, int H, int L, int dk,

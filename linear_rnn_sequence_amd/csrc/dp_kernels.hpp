@@ -96,8 +96,12 @@ struct FwdArgs {
   // bf16 with symmetric keys: 1 runs the single fused kernel (dp_fused.hpp),
   // 0 the chunk-prep kernel then the chain kernel with operand blocks in HBM
   int fused = 0;
-  // dp_scan_kernel LDS byte offsets
-  int oK, oKt, oQ, oT, oHt, oXt, oUo, oUs, oP, oV, oG, oEG, oEL, oLoc, oRow, oTok;
+  // per-key-channel gate alpha [B, L, H, dk] (the KDA host) or nullptr; with it
+  // the UT kernel also writes each chunk's readout scores to wsP (RT x C)
+  const float* ga = nullptr;
+  void* wsP = nullptr;
+  // dp_scan_kernel LDS byte offsets (oDec: the per-channel state decay, dk floats)
+  int oK, oKt, oQ, oT, oHt, oXt, oUo, oUs, oP, oV, oG, oEG, oEL, oLoc, oRow, oTok, oDec;
 };
 
 // First token row of batch row b (see FwdArgs::Ls).
@@ -155,17 +159,31 @@ __device__ __forceinline__ long long sub_row(const FwdArgs& p, int s, int b, int
 }
 
 // LDS bytes of dp_ut_kernel: K (and Kw) rows, fp32 M, 3 scalar vectors,
-// fp32 T and the per-wave partial-sum tiles of the blocked inverse.
-__host__ __device__ constexpr int ut_lds_bytes(int elem, int DK, int C, int asym) {
-  return align16((asym ? 2 : 1) * C * (DK + 16 / elem) * elem) + align16(C * (C + 4) * 4) +
-         3 * C * 4 + C * (C + 4) * 4 + 4 * 16 * 17 * 4;
+// fp32 T and the per-wave partial-sum tiles of the blocked inverse; with a
+// per-channel gate (cg) both key regions and the cumulative log-gates G
+// (C x (dk + 4) fp32).
+__host__ __device__ constexpr int ut_gam_ld(int DK) { return DK + 4; }
+__host__ __device__ constexpr int ut_lds_bytes(int elem, int DK, int C, int asym, int cg = 0) {
+  return align16((asym || cg ? 2 : 1) * C * (DK + 16 / elem) * elem) + align16(C * (C + 4) * 4) +
+         3 * C * 4 + C * (C + 4) * 4 + 4 * 16 * 17 * 4 + (cg ? C * ut_gam_ld(DK) * 4 : 0);
 }
 
 // ---------------------------------------------------------------------------
 // dp_ut_kernel: per-chunk prep + UT transform.
 // WT is the workspace type of T's output and TB selects T diag(beta) (the
 // forward's operand) or T itself (the backward, which also needs T alone).
-template <typename T, int DK, int C, typename WT = typename OpType<T>::type, bool TB = true>
+//
+// CG: a per-key-channel gate alpha (the KDA host of the OSDN notes, sec. 2.7:
+// H <- Diag(alpha_t) H before a token's sub-steps).  With G_s the chunk-local
+// cumulative log-gate of each key channel (the scalar gate folded in), a chunk
+// is the ungated write-key form for the read keys e^{G_s} o kn_s and the write
+// keys e^{-G_s} o w_s, so that
+//   M_ij = beta_i sum_c kn_i[c] w_j[c] e^{G_i[c] - G_j[c]}          (j < i)
+//   P_rj = sum_c q_r[c] w_j[c] e^{G_loc(r)[c] - G_j[c]}             (j <= loc(r))
+// Every factor is e^{G_a - G_b} with a >= b, at most 1: each entry is summed
+// pair by pair with its own factors, so no scaling can overflow however fast a
+// channel decays.  The scores go to wsP for the scan.
+template <typename T, int DK, int C, typename WT = typename OpType<T>::type, bool TB = true, bool CG = false>
 __global__ __launch_bounds__(kThreads) void dp_ut_kernel(FwdArgs p) {
   using OT = WT;
   constexpr int VE = Vec<T>::N;
@@ -181,12 +199,14 @@ __global__ __launch_bounds__(kThreads) void dp_ut_kernel(FwdArgs p) {
   T* sK = reinterpret_cast<T*>(smem);
   T* sKt = sK + C * LDK;
   const T* sKw = p.asym ? sKt : sK;
-  float* sA = reinterpret_cast<float*>(smem + align16((p.asym ? 2 : 1) * C * LDK * (int)sizeof(T)));
+  float* sA = reinterpret_cast<float*>(smem + align16((p.asym || CG ? 2 : 1) * C * LDK * (int)sizeof(T)));
   float* sR = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(sA) + align16(C * LDA * 4));
   float* sB = sR + C;
   float* sG = sB + C;
   float* sTf = sG + C;         // C x LDA fp32: T
   float* sSc = sTf + C * LDA;  // 4 x 16 x 17 fp32: per-wave partial sums
+  float* sGam = sSc + 4 * 16 * 17;  // CG: C x ut_gam_ld(DK) fp32, cumulative log-gates
+  constexpr int LDG = ut_gam_ld(DK);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const long long chunk = blockIdx.x;
@@ -230,6 +250,7 @@ __global__ __launch_bounds__(kThreads) void dp_ut_kernel(FwdArgs p) {
     if (idx < KV) {
       st16(sK + r * LDK + cg * VE, rk[it]);
       if (p.asym) st16(sKt + r * LDK + cg * VE, rkt[it]);
+      else if (CG) st16(sKt + r * LDK + cg * VE, rk[it]);  // write keys: the keys (normalised below)
     }
     float f[VE];
     unpack16(rk[it], f, T{});
@@ -250,9 +271,83 @@ __global__ __launch_bounds__(kThreads) void dp_ut_kernel(FwdArgs p) {
       sG[lane] = G;
     }
   }
+  if constexpr (CG) {
+    // cumulative log-gate of each key channel over the chunk's sub-steps: the
+    // gates act at a token's first sub-step (log alpha_t + log g_t there, 0 on
+    // the others and past the end)
+    if (tid < DK) {
+      const float* gap = p.ga;
+      float acc = 0.f;
+      for (int r = 0; r < C; ++r) {
+        const int s = s0 + r;
+        if (s < p.N) {
+          const int t = fastdiv(s, p.nh_magic, p.nh_shift);
+          if (s == t * p.n_h) {
+            const long long tok = (tok_base(p, b) + t) * p.H + h;
+            acc += logf(fmaxf(gap[tok * DK + tid], FLT_MIN));
+            if (p.g != nullptr) acc += logf(fmaxf(p.g[tok], FLT_MIN));
+          }
+        }
+        sGam[r * LDG + tid] = acc;
+      }
+    }
+  }
   block_sync_lds();
-  if (tid < C) p.wsS[chunk * C + tid] = make_float2(sR[tid], sG[tid]);
+  if (tid < C) p.wsS[chunk * C + tid] = make_float2(sR[tid], CG ? 0.f : sG[tid]);
 
+  if constexpr (CG) {
+    // 4'. M_ij (j < i), pair by pair over the key channels; symmetric keys are
+    //     normalised here (sR), write keys used as given
+    constexpr int NPAIR = C * (C - 1) / 2;
+    for (int pr = tid; pr < C * C; pr += kThreads) sA[(pr / C) * LDA + pr % C] = 0.f;
+    block_sync_lds();
+    for (int pr = tid; pr < NPAIR; pr += kThreads) {
+      int i = (int)((1.f + sqrtf(1.f + 8.f * (float)pr)) * 0.5f);
+      while (i * (i - 1) / 2 > pr) --i;
+      while ((i + 1) * i / 2 <= pr) ++i;
+      const int j = pr - i * (i - 1) / 2;
+      float acc = 0.f;
+#pragma unroll 4
+      for (int c = 0; c < DK; ++c)
+        acc = fmaf(to_f32(sK[i * LDK + c]) * to_f32(sKt[j * LDK + c]), __expf(sGam[i * LDG + c] - sGam[j * LDG + c]),
+                   acc);
+      sA[i * LDA + j] = sB[i] * sR[i] * (p.asym ? 1.f : sR[j]) * acc;
+    }
+    block_sync_lds();
+    // 4''. readout scores P_rj (j <= loc(r)) to wsP; the query rows take the
+    //      key rows' place (the keys are done)
+    const int n_h = p.n_h;
+    const int r0 = s0 + (n_h - 1 - (s0 - fastdiv(s0, p.nh_magic, p.nh_shift) * n_h));
+    const int RT = p.RT;
+    const T* qp = static_cast<const T*>(p.q);
+    for (int idx = tid; idx < RT * TPR; idx += kThreads) {
+      const int r = idx / TPR, cg = idx % TPR;
+      const int s = r0 + r * n_h;
+      u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
+      if (s < s0 + C && s < p.N) {
+        const long long tok = (tok_base(p, b) + fastdiv(s, p.nh_magic, p.nh_shift)) * p.H + h;
+        v = ld16(qp + tok * DK + cg * VE);
+      }
+      st16(sK + r * LDK + cg * VE, v);
+    }
+    block_sync_lds();
+    OT* wp = static_cast<OT*>(p.wsP) + chunk * RT * C;
+    for (int e = tid; e < RT * C; e += kThreads) {
+      const int r = e / C, j = e % C;
+      const int s = r0 + r * n_h;
+      const int loc = (s < s0 + C && s < p.N) ? s - s0 : -1;
+      float acc = 0.f;
+      if (j <= loc) {
+        const float rw = p.asym ? 1.f : sR[j];
+#pragma unroll 4
+        for (int c = 0; c < DK; ++c)
+          acc = fmaf(to_f32(sK[r * LDK + c]) * to_f32(sKt[j * LDK + c]),
+                     __expf(sGam[loc * LDG + c] - sGam[j * LDG + c]), acc);
+        acc *= rw;
+      }
+      wp[e] = from_f32<OT>(acc);
+    }
+  } else {
   // 4. M = strict_tril(diag(beta) (E o Kn Kw^T)) on MFMA (lower tiles only)
   for (int tile = wave; tile < NT * NT; tile += 4) {
     const int ti = tile / NT, tj = tile % NT;
@@ -267,6 +362,7 @@ __global__ __launch_bounds__(kThreads) void dp_ut_kernel(FwdArgs p) {
       if (jj < ii) val = sB[ii] * sR[ii] * rw * expf(sG[ii] - sG[jj]) * acc[e];
       sA[ii * LDA + jj] = val;
     }
+  }
   }
   block_sync_lds();
 
@@ -351,7 +447,13 @@ __global__ __launch_bounds__(kThreads) void dp_ut_kernel(FwdArgs p) {
 // committed), so no wait is forced before the compute.  Row indices of the
 // next chunk's sub-steps and readout tokens are computed once per chunk into
 // LDS.  All barriers order LDS only.  NRT = readout-row tiles per chunk.
-template <typename T, int DK, int C, int BV, int NRT>
+//
+// CG (per-key-channel gate, see dp_ut_kernel): the scores come from the UT
+// kernel (wsP); after a chunk is committed, each key channel's thread walks the
+// chunk's sub-steps once for the last cumulative log-gate G_C and once to scale
+// the read keys by e^{G_s}, the write keys by e^{G_C - G_s} and the readout
+// queries by e^{G_loc}; the state's rows decay by e^{G_C} (every factor at most 1).
+template <typename T, int DK, int C, int BV, int NRT, bool CG = false>
 __global__ __launch_bounds__(kThreads) void dp_scan_kernel(FwdArgs p) {
   using OT = typename OpType<T>::type;  // MFMA operand type
   static_assert(sizeof(OT) == sizeof(T), "operand and input types share a width");
@@ -394,7 +496,8 @@ __global__ __launch_bounds__(kThreads) void dp_scan_kernel(FwdArgs p) {
   int* sLoc = reinterpret_cast<int*>(smem + p.oLoc);    // readout row -> sub-step in chunk
   long long* sRow = reinterpret_cast<long long*>(smem + p.oRow);  // [2][C] sub-step rows
   long long* sTok = reinterpret_cast<long long*>(smem + p.oTok);  // [2][RT] readout tokens
-  const OT* sKw = p.asym ? sKt : sK;
+  float* sDec = reinterpret_cast<float*>(smem + p.oDec);          // CG: e^{G_C} per key channel
+  const OT* sKw = (p.asym || CG) ? sKt : sK;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -413,6 +516,7 @@ __global__ __launch_bounds__(kThreads) void dp_scan_kernel(FwdArgs p) {
   const T* vp = static_cast<const T*>(p.v) + v0;
   const T* qp = static_cast<const T*>(p.q);
   const OT* wsT = static_cast<const OT*>(p.wsT) + (long long)bh * nc * C * C;
+  const OT* wsP = static_cast<const OT*>(p.wsP) + (long long)bh * nc * RT * C;
   const float2* wsS = p.wsS + (long long)bh * nc * C;
   const long long tok0 = tok_base(p, b) * p.H + h;  // token (b, 0, h)
 
@@ -439,7 +543,8 @@ __global__ __launch_bounds__(kThreads) void dp_scan_kernel(FwdArgs p) {
   };
 
   // ---- prefetch registers (one chunk)
-  u32x4_t rk[KIT], rkt[KIT], rq[QIT], rt[TIT], rvv[VIT];
+  constexpr int PV = RT * TPRC, PIT = (PV + kThreads - 1) / kThreads;  // CG scores
+  u32x4_t rk[KIT], rkt[KIT], rq[QIT], rt[TIT], rvv[VIT], rp[CG ? PIT : 1];
   float rinv[KIT];
   float rg;
 
@@ -461,6 +566,14 @@ __global__ __launch_bounds__(kThreads) void dp_scan_kernel(FwdArgs p) {
     for (int it = 0; it < TIT; ++it) {
       const int idx = (TV % kThreads == 0) ? tid + it * kThreads : min(tid + it * kThreads, TV - 1);
       rt[it] = ld16(tsrc + idx * VE);
+    }
+    if constexpr (CG) {
+      const OT* psrc = wsP + (long long)c * RT * C;
+#pragma unroll
+      for (int it = 0; it < PIT; ++it) {
+        const int idx = (PV % kThreads == 0) ? tid + it * kThreads : min(tid + it * kThreads, PV - 1);
+        rp[it] = ld16(psrc + idx * VE);
+      }
     }
     rg = ssrc[min(tid, C - 1)].y;
 #pragma unroll
@@ -492,6 +605,7 @@ __global__ __launch_bounds__(kThreads) void dp_scan_kernel(FwdArgs p) {
 #pragma unroll
         for (int e = 0; e < VE; ++e) fv[e] *= rinv[it];  // 1/|k|, 0 past the end
         st_vec16(sK + r * LDK + cg * VE, fv);
+        if (CG && !p.asym) st_vec16(sKt + r * LDK + cg * VE, fv);  // write keys: the unit keys
         if (p.asym) {
           unpack16(rkt[it], fv, T{});
           const float keep = (s0 + r < p.N) ? 1.f : 0.f;
@@ -506,6 +620,14 @@ __global__ __launch_bounds__(kThreads) void dp_scan_kernel(FwdArgs p) {
       const int idx = tid + it * kThreads;
       const int r = idx / TPRC, cg = idx % TPRC;
       if (TV % kThreads == 0 || idx < TV) st16(sT + r * LDC + cg * VE, rt[it]);
+    }
+    if constexpr (CG) {
+#pragma unroll
+      for (int it = 0; it < PIT; ++it) {
+        const int idx = tid + it * kThreads;
+        const int r = idx / TPRC, cg = idx % TPRC;
+        if (PV % kThreads == 0 || idx < PV) st16(sP + r * LDC + cg * VE, rp[it]);
+      }
     }
 #pragma unroll
     for (int it = 0; it < QIT; ++it) {
@@ -565,11 +687,47 @@ __global__ __launch_bounds__(kThreads) void dp_scan_kernel(FwdArgs p) {
     block_sync_lds();
     prefetch(0);
   }
+  // CG: log-gate of key channel ch at sub-step s (log alpha_t + log g_t at a
+  // token's first sub-step, 0 on the others and past the end)
+  auto log_gate = [&](int s, int ch) {
+    float l = 0.f;
+    if (s < p.N) {
+      const int t = fastdiv(s, p.nh_magic, p.nh_shift);
+      if (s == t * n_h) {
+        const long long tok = tok0 + (long long)t * p.H;
+        l = logf(fmaxf(p.ga[tok * DK + ch], FLT_MIN));
+        if (p.g != nullptr) l += logf(fmaxf(p.g[tok], FLT_MIN));
+      }
+    }
+    return l;
+  };
   for (int c = 0; c < nc; ++c) {
     const int s0 = c * C;
     block_sync_lds();  // the previous chunk is done with every tile below
     commit(c);
     block_sync_lds();
+    if constexpr (CG) {
+      if (tid < DK) {
+        float gl = 0.f;
+        for (int i = 0; i < C; ++i) gl += log_gate(s0 + i, tid);
+        const int loc0 = n_h - 1 - (s0 - fastdiv(s0, p.nh_magic, p.nh_shift) * n_h);
+        float acc = 0.f;
+        int nxt = loc0, r = 0;
+        for (int i = 0; i < C; ++i) {
+          acc += log_gate(s0 + i, tid);
+          const float ea = __expf(acc);
+          sK[i * LDK + tid] = from_f32<OT>(to_f32(sK[i * LDK + tid]) * ea);
+          sKt[i * LDK + tid] = from_f32<OT>(to_f32(sKt[i * LDK + tid]) * __expf(gl - acc));
+          if (i == nxt) {
+            if (r < RT) sQ[r * LDK + tid] = from_f32<OT>(to_f32(sQ[r * LDK + tid]) * ea);
+            ++r;
+            nxt += n_h;
+          }
+        }
+        sDec[tid] = __expf(gl);
+      }
+      block_sync_lds();
+    }
     if (c + 1 < nc) prefetch(c + 1);
 
     // ---- phase 1: X = V - diag(e^G) (Kn H0);  P^T = Kw Q^T (masked, gated);  Z = Q H0
@@ -584,12 +742,12 @@ __global__ __launch_bounds__(kThreads) void dp_scan_kernel(FwdArgs p) {
         const int r0 = ct * 16 + 4 * grp;
         float x[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = sV[(r0 + e) * LDV + nt * 16 + col] - sEG[r0 + e] * acc[e];
+        for (int e = 0; e < 4; ++e) x[e] = sV[(r0 + e) * LDV + nt * 16 + col] - (CG ? 1.f : sEG[r0 + e]) * acc[e];
         st4(sXt + (nt * 16 + col) * LDC + r0, x[0], x[1], x[2], x[3]);
       }
     }
 #pragma unroll
-    for (int u = 0; u < PPW; ++u) {
+    for (int u = 0; u < (CG ? 0 : PPW); ++u) {  // CG: the scores came with the chunk
       const int tile = wave + 4 * u;
       if (tile < NPT) {
         const int jt = tile / NRT, it = tile % NRT;
@@ -616,7 +774,7 @@ __global__ __launch_bounds__(kThreads) void dp_scan_kernel(FwdArgs p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int loc = sLoc[it * 16 + 4 * grp + e];
-          zacc[u][e] *= (loc >= 0) ? sEG[loc] : 0.f;
+          zacc[u][e] *= (loc >= 0) ? (CG ? 1.f : sEG[loc]) : 0.f;
         }
       }
     }
@@ -633,8 +791,11 @@ __global__ __launch_bounds__(kThreads) void dp_scan_kernel(FwdArgs p) {
         const int rowoff = (nt * 16 + col) * LDC + ct * 16 + 4 * grp;
         st4(sUo + rowoff, acc[0], acc[1], acc[2], acc[3]);
         const int j0 = ct * 16 + 4 * grp;
-        st4(sUs + rowoff, acc[0] * sEL[j0], acc[1] * sEL[j0 + 1], acc[2] * sEL[j0 + 2],
-            acc[3] * sEL[j0 + 3]);
+        if constexpr (CG)
+          st4(sUs + rowoff, acc[0], acc[1], acc[2], acc[3]);  // the decay is in the write keys
+        else
+          st4(sUs + rowoff, acc[0] * sEL[j0], acc[1] * sEL[j0 + 1], acc[2] * sEL[j0 + 2],
+              acc[3] * sEL[j0 + 3]);
       }
     }
     block_sync_lds();
@@ -667,7 +828,7 @@ __global__ __launch_bounds__(kThreads) void dp_scan_kernel(FwdArgs p) {
       if (tile < NHT) {
         const int dt = tile / NVT, nt = tile % NVT;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) hacc[u][e] *= dec;
+        for (int e = 0; e < 4; ++e) hacc[u][e] *= CG ? sDec[dt * 16 + 4 * grp + e] : dec;
         hacc[u] = mm_tile_ta<OT, C>(hacc[u], sKw, LDK, dt * 16, sUs, LDC, nt * 16);
         st4(sHt + (nt * 16 + col) * LDK + dt * 16 + 4 * grp, hacc[u][0], hacc[u][1], hacc[u][2],
             hacc[u][3]);
@@ -1439,6 +1600,58 @@ hipError_t launch_scan_nrt(const FwdArgs& a, int lds, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
+// Per-key-channel gate (either input type): dp_ut_kernel and dp_scan_kernel in
+// their CG form, operands in the input's operand type.
+template <typename T, int DK, int C>
+hipError_t launch_ut_cg(const FwdArgs& a, hipStream_t st) {
+  using OT = typename OpType<T>::type;
+  const int lds = ut_lds_bytes((int)sizeof(T), DK, C, a.asym, 1);
+  static const bool attr = allow_big_lds(reinterpret_cast<const void*>(&dp_ut_kernel<T, DK, C, OT, true, true>));
+  (void)attr;
+  const long long nchunks = (long long)a.B * a.H * a.nc;
+  if (nchunks == 0) return hipSuccess;
+  hipLaunchKernelGGL((dp_ut_kernel<T, DK, C, OT, true, true>), dim3((unsigned)nchunks), dim3(kThreads), lds, st, a);
+  return hipGetLastError();
+}
+
+template <typename T, int DK, int C, int BV, int NRT>
+hipError_t launch_scan_cg(const FwdArgs& a, int lds, hipStream_t st) {
+  static const bool attr =
+      allow_big_lds(reinterpret_cast<const void*>(&dp_scan_kernel<T, DK, C, BV, NRT, true>));
+  (void)attr;
+  const long long nwg = (long long)a.B * a.H * a.nvb;
+  hipLaunchKernelGGL((dp_scan_kernel<T, DK, C, BV, NRT, true>), dim3((unsigned)nwg), dim3(kThreads), lds, st, a);
+  return hipGetLastError();
+}
+
+template <typename T, int DK, int C, int BV>
+hipError_t launch_scan_cg_nrt(const FwdArgs& a, int lds, hipStream_t st) {
+  switch (a.RT / 16) {
+    case 1: return launch_scan_cg<T, DK, C, BV, 1>(a, lds, st);
+    case 2: if constexpr (C >= 32) return launch_scan_cg<T, DK, C, BV, 2>(a, lds, st); break;
+    case 3: if constexpr (C >= 64) return launch_scan_cg<T, DK, C, BV, 3>(a, lds, st); break;
+    case 4: if constexpr (C >= 64) return launch_scan_cg<T, DK, C, BV, 4>(a, lds, st); break;
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T, int DK, int C>
+hipError_t launch_cg(const FwdArgs& a, int BV, int lds_scan, int stages, hipStream_t st) {
+  if ((stages & 1) && a.nc > 0) {
+    const hipError_t e = launch_ut_cg<T, DK, C>(a, st);
+    if (e != hipSuccess) return e;
+  }
+  if (stages & 2) {
+    switch (BV) {
+      case 16: return launch_scan_cg_nrt<T, DK, C, 16>(a, lds_scan, st);
+      case 32: return launch_scan_cg_nrt<T, DK, C, 32>(a, lds_scan, st);
+      case 64: return launch_scan_cg_nrt<T, DK, C, 64>(a, lds_scan, st);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  return hipSuccess;
+}
+
 // Producer wavefronts per workgroup of dp_scan16_kernel for NWC consumers.
 constexpr int scan16_producers(int nwc) { return nwc >= 2 ? 2 : 1; }
 
@@ -1567,6 +1780,7 @@ hipError_t launch_fwd_dk(const FwdArgs& a, int C, int BV, int lds_scan, int stag
   hipError_t e = hipSuccess;
 #define DP_CASE_C(CC)                                                          \
   case CC:                                                                     \
+    if (a.ga != nullptr) return launch_cg<T, DK, CC>(a, BV, lds_scan, stages, st); \
     if constexpr (sizeof(T) == 2) {                                            \
       if (!a.asym) return launch_pair16<DK, CC, false>(a, BV, stages, st);     \
       if constexpr (chain_asym_ok(DK, CC))                                     \

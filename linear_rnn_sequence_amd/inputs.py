@@ -183,6 +183,15 @@ def write_keys(w: Workload, seed: int) -> torch.Tensor:
     return (kt * d).to(torch_dtype(w.dtype)).contiguous()
 
 
+def channel_gate(B: int, L: int, H: int, dk: int, seed: int, lo: float = 0.6) -> torch.Tensor:
+    """Per-key-channel gate alpha [B, L, H, dk] (fp32) for the KDA host: uniform
+    in [lo, 1] per element on a seed of its own (lo = 0.6: a few percent of decay
+    per token on average; a small lo gives fast-decaying channels)."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(seed)
+    return (lo + (1.0 - lo) * torch.rand(B, L, H, dk, generator=gen, dtype=torch.float32)).contiguous()
+
+
 def retention(B: int, L: int, H: int, seed: int, bias: float = 3.0) -> torch.Tensor:
     """Per-token, per-head retention values in (0, 1) for the preconditioner
     (the APF gate is a sigmoid of a learned projection; here sigmoid(N(0,1) +

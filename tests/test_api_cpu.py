@@ -96,7 +96,10 @@ def test_workspace_size_formula(lib):
     rc, n = ws(2, 1, 1, 33, 16, 16, 16, 2)  # ragged: 66 sub-steps -> 5 chunks
     assert rc == 0 and n == -(-5 * bf16_chunk_block(16, 16, 2) // 256) * 256 + 256
     rc, n = ws(2, 1, 1, 33, 16, 16, 16, 4)  # ragged: 66 sub-steps -> 5 chunks
-    assert rc == 0 and n == ((1 * 5 * 16 * 16 * 4 + 255) // 256) * 256 + 5 * 16 * 8
+    # fp32: T (C x C), the per-sub-step scalars, and the readout scores (RT x C, RT = 16)
+    # that the per-channel-gate form keeps, each region 256-byte aligned
+    up = lambda x: -(-x // 256) * 256
+    assert rc == 0 and n == up(5 * 16 * 16 * 4) + up(5 * 16 * 8) + up(5 * 16 * 16 * 4)
     assert ws(2, 1, 1, 0, 16, 16, 16, 4) == (0, 0)
 
 
@@ -117,11 +120,11 @@ def test_workspace_size_validation(lib, args, code):
 FAKE = 1 << 20  # a 256-aligned non-null address; validation fails before any use
 
 
-def fwd_call(lib, suffix="bf16", q=FAKE, k=FAKE, v=FAKE, beta=FAKE, g=None, n_h=2, B=1, H=1,
+def fwd_call(lib, suffix="bf16", q=FAKE, k=FAKE, v=FAKE, beta=FAKE, g=None, ga=None, n_h=2, B=1, H=1,
              L=8, dk=16, dv=16, chunk=16, out=FAKE, fs=None, h0=None, wsp=FAKE, wsb=1 << 30,
              kt=None, stages=3):
     fn = getattr(lib, f"dp_fwd_ex_{suffix}")
-    return fn(q, k, kt, v, beta, g, n_h, B, H, L, dk, dv, chunk, out, fs, h0, wsp, wsb, stages,
+    return fn(q, k, kt, v, beta, g, ga, n_h, B, H, L, dk, dv, chunk, out, fs, h0, wsp, wsb, stages,
               None)
 
 
@@ -149,6 +152,7 @@ def test_fwd_validation_errors_before_hip(lib, suffix):
     assert fwd_call(lib, suffix, stages=16 | 3) == E.DP_ENOTSUP
     assert fwd_call(lib, suffix, stages=16 | 1, dk=32, chunk=32) == E.DP_ENOTSUP
     assert fwd_call(lib, suffix, stages=16 | 3, dk=32, chunk=32, kt=FAKE) == E.DP_ENOTSUP
+    assert fwd_call(lib, suffix, stages=16 | 3, dk=32, chunk=32, ga=FAKE) == E.DP_ENOTSUP  # no channel gate
     if suffix == "f32":
         assert fwd_call(lib, suffix, stages=16 | 3, dk=32, chunk=32) == E.DP_ENOTSUP
     assert fwd_call(lib, suffix, wsb=16) == E.DP_EWORKSPACE           # too small
