@@ -17,7 +17,9 @@ contiguous float64 and calls it through ctypes.  Sources, by page title:
   differentiation of the same sequential definition (``bwd``).
 * "OSDN: Improving Delta Rule with Provable Online Preconditioning in Linear
   Attention" -- sec. 2.2 Eqs.(2)/(5) (asymmetric write key), sec. 2.4 Alg.1
-  (phase-1 preconditioner, emit-then-update).
+  (phase-1 preconditioner, emit-then-update), and its gradient (sec. 2.5,
+  closing paragraph: through the write key into d and k, then back through
+  the recursion; ``precond_bwd``, ``osdn_bwd``).
 """
 import ctypes
 import os
@@ -56,6 +58,11 @@ def _load():
                                           ctypes.c_int, ctypes.c_int, ctypes.c_double,
                                           ctypes.c_double, ctypes.c_double, ctypes.c_double,
                                           _D, _D, ctypes.c_int]
+        lib.oracle_precond_bwd.restype = ctypes.c_int
+        lib.oracle_precond_bwd.argtypes = [_D, _D, _D, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                                           ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                                           _D, _D, _D, _D, _D, _D, _D, ctypes.c_int]
         lib.oracle_bwd.restype = ctypes.c_int
         lib.oracle_bwd.argtypes = [_D, _D, _D, _D, _D, _D, ctypes.c_int, ctypes.c_int,
                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -175,6 +182,61 @@ def precond(k, beta, eta=3e-3, dmin=0.5, dmax=2.0, eps=1e-6, d0=None, nthreads=0
     if rc != 0:
         raise RuntimeError(f"oracle_precond_ex failed ({rc})")
     return kt, d
+
+
+def precond_bwd(k, beta, dkt, eta=3e-3, dmin=0.5, dmax=2.0, eps=1e-6, d0=None, dd_final=None,
+                nthreads=0, r=None, beta_aware=True):
+    """Gradient of :func:`precond` for a loss with gradient ``dkt [B,L,H,dk]``
+    on the emitted write keys and ``dd_final [B,H,dk]`` (None: zero) on the
+    final d.  Returns a dict of float64 arrays: ``k [B,L,H,dk]`` (raw keys),
+    ``beta [B,L,H]``, ``d0 [B,H,dk]`` and ``r [B,L,H]`` when a retention gate
+    is given."""
+    k, beta, dkt = _f64(k), _f64(beta), _f64(dkt)
+    if k.ndim != 4 or beta.shape != k.shape[:3] or dkt.shape != k.shape:
+        raise ValueError("expected k[B,L,H,dk], beta[B,L,H] and dkt[B,L,H,dk]")
+    B, L, H, dk = k.shape
+    r = None if r is None else _f64(r)
+    if r is not None and r.shape != beta.shape:
+        raise ValueError("r must be [B,L,H]")
+    d0 = None if d0 is None else _f64(d0)
+    dd_final = None if dd_final is None else _f64(dd_final)
+    for name, a in (("d0", d0), ("dd_final", dd_final)):
+        if a is not None and a.shape != (B, H, dk):
+            raise ValueError(f"{name} must be [B,H,dk]")
+    out = dict(k=np.zeros((B, L, H, dk)), beta=np.zeros((B, L, H)), d0=np.zeros((B, H, dk)))
+    if r is not None:
+        out["r"] = np.zeros((B, L, H))
+    rc = _load().oracle_precond_bwd(_ptr(k), _ptr(beta), _ptr(r), int(bool(beta_aware)), B, H, L,
+                                    dk, float(eta), float(dmin), float(dmax), float(eps), _ptr(d0),
+                                    _ptr(dkt), _ptr(dd_final), _ptr(out["k"]), _ptr(out["beta"]),
+                                    _ptr(out.get("r")), _ptr(out["d0"]), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_precond_bwd failed ({rc})")
+    return out
+
+
+def osdn_bwd(q, k, v, beta, dout, g=None, h0=None, dfinal=None, eta=3e-3, dmin=0.5, dmax=2.0,
+             eps=1e-6, d0=None, r=None, beta_aware=True, nthreads=0):
+    """Gradient of the whole OSDN layer for n_h = 1: phase 1 over ``k [B,L,H,dk]``
+    and ``beta [B,L,H]`` gives the write keys, then the write-key forward over
+    q, k, v, beta (``v [B,L,H,dv]``) -- the two gradients of :func:`bwd` (write
+    keys as inputs) and :func:`precond_bwd` (the write-key gradient carried
+    back through phase 1), summed where they meet (the raw keys and beta).
+    Returns float64 ``q, k, v, beta, h0, d0`` (+ ``g``, ``r`` when given)."""
+    k, beta = _f64(k), _f64(beta)
+    kt, _ = precond(k, beta, eta, dmin, dmax, eps, d0=d0, nthreads=nthreads, r=r,
+                    beta_aware=beta_aware)
+    g2 = bwd(q, k[:, :, :, None, :], _f64(v)[:, :, :, None, :], beta[..., None], dout, g=g,
+             kt=kt[:, :, :, None, :], h0=h0, dfinal=dfinal, nthreads=nthreads)
+    g1 = precond_bwd(k, beta, g2["kt"][:, :, :, 0, :], eta, dmin, dmax, eps, d0=d0,
+                     nthreads=nthreads, r=r, beta_aware=beta_aware)
+    res = dict(q=g2["q"], k=g2["k"][:, :, :, 0, :] + g1["k"], v=g2["v"][:, :, :, 0, :],
+               beta=g2["beta"][..., 0] + g1["beta"], h0=g2["h0"], d0=g1["d0"])
+    if g is not None:
+        res["g"] = g2["g"]
+    if r is not None:
+        res["r"] = g1["r"]
+    return res
 
 
 def _bwd_args(q, k, v, beta, dout, g, kt, h0, dfinal):

@@ -30,6 +30,9 @@
  *     sec. 4.1 / Sec.5.1: only the last sub-step of each token is kept).
  * Phase 1 of OSDN ([OSDN] sec. 2.4, Alg.1): emit d_t * k_t first, then
  * d <- clamp(d + eta*beta*(1 - beta<d, k*k>)/max(|k|^2, eps) * (k*k)).
+ Its gradient (oracle_precond_bwd) is the reverse-mode derivative of that
+ * scan ([OSDN] sec. 2.5, closing paragraph: through kt_t = d_t * k_t into d_t
+ * and k_t, then back through the recursion).
  *
  * All arithmetic is IEEE double, in the order written, no blocking, fusion or
  * reordering.  Heads (b, h) are independent, so they are spread over OpenMP
@@ -304,6 +307,137 @@ int oracle_precond(const double* k, const double* beta, int B, int H, int L, int
 {
     return oracle_precond_ex(k, beta, NULL, 1, B, H, L, dk, eta, dmin, dmax, eps, d_state,
                              kt_out, nthreads);
+}
+
+/*
+ * Gradient of the phase-1 scan (reverse mode, last token first).  [OSDN]
+ * sec. 2.5, closing paragraph (Sec.4.5): in training the write key
+ * kt_t = d_t * kh_t passes its gradient to both d_t and k_t, and the gradient
+ * of d then runs back through the preconditioner recursion of sec. 2.4 (with
+ * the retention of sec. 2.6 and the beta-free step of sec. 2.7 as in
+ * oracle_precond_ex).  Per token, with s = kh*kh, n = |kh|^2, nb = max(n, eps),
+ * a = bu <d, s>, coef = eta bu (1 - a) / nb and x = r d + coef s (before the
+ * projection onto the box):
+ *   dx     = dd' where dmin <= x <= dmax, else 0     (dd' = gradient on d_{t+1})
+ *   dd     = r dx - eta bu^2 / nb <dx, s> s + kh * dkt_t
+ *   dr     = <dx, d>
+ *   ds     = coef dx + <dx, s> (-eta bu^2 / nb d - [n > eps] coef / nb)
+ *   dbu    = <dx, s> eta (1 - 2a) / nb
+ *   dkh    = 2 kh * ds + d * dkt_t
+ * then the unit-key normalisation and the beta clamp as in the forward's
+ * gradient below (the derivative of a clamp at its end points is taken as 1).
+ * The beta-free step has no beta gradient.
+ *
+ * Inputs as oracle_precond_ex (d0 [B, H, dk] the initial d, NULL: ones), plus
+ * dkt [B, L, H, dk], the gradient on the emitted write keys, and dd_final
+ * [B, H, dk] (NULL: zero), the gradient on the final d.  Outputs dk [B, L, H,
+ * dk] (raw keys), dbeta [B, L, H], dret [B, L, H] (NULL: not returned; zero
+ * without ret) and dd0 [B, H, dk] (NULL: not returned).  The forward is run
+ * again first, keeping every d_t.  Returns 0, -1 on bad arguments, -2 when
+ * scratch memory could not be allocated.
+ */
+int oracle_precond_bwd(const double* k, const double* beta, const double* ret, int beta_aware,
+                       int B, int H, int L, int dk, double eta, double dmin, double dmax,
+                       double eps, const double* d0, const double* dkt, const double* dd_final,
+                       double* dk_out, double* dbeta, double* dret, double* dd0, int nthreads)
+{
+    if (!k || !beta || !dkt || !dk_out || !dbeta) return -1;
+    if (B < 0 || H < 0 || L < 0 || dk < 1) return -1;
+    long nbh = (long)B * H;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#else
+    (void)nthreads;
+#endif
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads) reduction(| : bad)
+    for (long bh = 0; bh < nbh; ++bh) {
+        const long b = bh / H, h = bh % H;
+        /* D[t]: d_t, the preconditioner before token t's update (t = 0 .. L-1) */
+        double* D = (double*)malloc(sizeof(double) * (size_t)dk * (size_t)(L > 0 ? L : 1));
+        double* d = (double*)malloc(sizeof(double) * (size_t)dk);
+        double* gd = (double*)malloc(sizeof(double) * (size_t)dk);
+        double* kh = (double*)malloc(sizeof(double) * (size_t)dk);
+        double* gx = (double*)malloc(sizeof(double) * (size_t)dk);
+        double* gkh = (double*)malloc(sizeof(double) * (size_t)dk);
+        if (!D || !d || !gd || !kh || !gx || !gkh) {
+            free(D); free(d); free(gd); free(kh); free(gx); free(gkh);
+            bad |= 1;
+            continue;
+        }
+        /* forward again, keeping d_t */
+        for (int r = 0; r < dk; ++r) d[r] = d0 ? d0[(size_t)bh * dk + r] : 1.0;
+        for (long t = 0; t < L; ++t) {
+            const size_t tok = ((size_t)b * L + t) * H + h;
+            memcpy(D + (size_t)t * dk, d, sizeof(double) * (size_t)dk);
+            unit_key(k + tok * dk, dk, kh);
+            const double bu = beta_aware ? clampd(beta[tok], 0.0, 2.0) : 1.0;
+            const double rt = ret ? ret[tok] : 1.0;
+            double n = 0.0, ds = 0.0;
+            for (int r = 0; r < dk; ++r) {
+                const double s = kh[r] * kh[r];
+                n += s;
+                ds += d[r] * s;
+            }
+            const double nb = n > eps ? n : eps;
+            const double coef = eta * bu * (1.0 - bu * ds) / nb;
+            for (int r = 0; r < dk; ++r) d[r] = clampd(rt * d[r] + coef * (kh[r] * kh[r]), dmin, dmax);
+        }
+        /* reverse sweep */
+        for (int r = 0; r < dk; ++r) gd[r] = dd_final ? dd_final[(size_t)bh * dk + r] : 0.0;
+        for (long t = L - 1; t >= 0; --t) {
+            const size_t tok = ((size_t)b * L + t) * H + h;
+            const double* dt = D + (size_t)t * dk;
+            const double* gk = dkt + tok * dk;
+            unit_key(k + tok * dk, dk, kh);
+            const double braw = beta[tok];
+            const double bu = beta_aware ? clampd(braw, 0.0, 2.0) : 1.0;
+            const double rt = ret ? ret[tok] : 1.0;
+            double n = 0.0, ds = 0.0;
+            for (int r = 0; r < dk; ++r) {
+                const double s = kh[r] * kh[r];
+                n += s;
+                ds += dt[r] * s;
+            }
+            const double a = bu * ds;
+            const double nb = n > eps ? n : eps;
+            const double coef = eta * bu * (1.0 - a) / nb;
+            /* through the projection */
+            double gxs = 0.0, gr = 0.0;
+            for (int r = 0; r < dk; ++r) {
+                const double x = rt * dt[r] + coef * (kh[r] * kh[r]);
+                gx[r] = (x >= dmin && x <= dmax) ? gd[r] : 0.0;
+                gxs += gx[r] * (kh[r] * kh[r]);
+                gr += gx[r] * dt[r];
+            }
+            if (dret) dret[tok] = ret ? gr : 0.0;
+            /* beta: coef = eta (bu - bu^2 <d, s>) / nb */
+            const double gbu = gxs * eta * (1.0 - 2.0 * a) / nb;
+            dbeta[tok] = (beta_aware && braw >= 0.0 && braw <= 2.0) ? gbu : 0.0;
+            /* s through x, a and n; kh through s and the emitted write key */
+            const double cn = n > eps ? coef / nb : 0.0;
+            double p = 0.0;
+            for (int r = 0; r < dk; ++r) {
+                const double gs = coef * gx[r] + gxs * (-eta * bu * bu / nb * dt[r] - cn);
+                gkh[r] = 2.0 * kh[r] * gs + dt[r] * gk[r];
+                p += kh[r] * gkh[r];
+            }
+            /* raw key through k / max(|k|, 1e-6) */
+            const double* kr = k + tok * dk;
+            double n2 = 0.0;
+            for (int r = 0; r < dk; ++r) n2 += kr[r] * kr[r];
+            const double nrm = sqrt(n2);
+            double* dko = dk_out + tok * dk;
+            for (int r = 0; r < dk; ++r)
+                dko[r] = nrm > ORACLE_KEY_EPS ? (gkh[r] - kh[r] * p) / nrm : gkh[r] / ORACLE_KEY_EPS;
+            /* d_t through x, a and the emitted write key */
+            for (int r = 0; r < dk; ++r)
+                gd[r] = rt * gx[r] - eta * bu * bu / nb * gxs * (kh[r] * kh[r]) + kh[r] * gk[r];
+        }
+        if (dd0) memcpy(dd0 + (size_t)bh * dk, gd, sizeof(double) * (size_t)dk);
+        free(D); free(d); free(gd); free(kh); free(gx); free(gkh);
+    }
+    return bad ? -2 : 0;
 }
 
 /*

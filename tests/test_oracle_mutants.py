@@ -70,6 +70,19 @@ BWD_MUTANTS = {
     "bwd_write_grad_missing_beta": ("dr += bt * acc;", "dr += acc;"),
     "bwd_gate_not_applied_to_state_grad": ("for (size_t x = 0; x < DS; ++x) dH[x] *= g[tok];",
                                            "for (size_t x = 0; x < DS; ++x) dH[x] *= 1.0;"),
+    # the phase-1 gradient
+    "p1bwd_drop_step_term_in_dd": ("gd[r] = rt * gx[r] - eta * bu * bu / nb * gxs * (kh[r] * kh[r]) + kh[r] * gk[r];",
+                                   "gd[r] = rt * gx[r] + kh[r] * gk[r];"),
+    "p1bwd_write_key_not_into_d": ("gd[r] = rt * gx[r] - eta * bu * bu / nb * gxs * (kh[r] * kh[r]) + kh[r] * gk[r];",
+                                   "gd[r] = rt * gx[r] - eta * bu * bu / nb * gxs * (kh[r] * kh[r]);"),
+    "p1bwd_write_key_not_into_k": ("gkh[r] = 2.0 * kh[r] * gs + dt[r] * gk[r];", "gkh[r] = 2.0 * kh[r] * gs;"),
+    "p1bwd_projection_mask_ignored": ("gx[r] = (x >= dmin && x <= dmax) ? gd[r] : 0.0;", "gx[r] = gd[r];"),
+    "p1bwd_retention_not_applied": ("gd[r] = rt * gx[r] - eta", "gd[r] = gx[r] - eta"),
+    "p1bwd_beta_term": ("const double gbu = gxs * eta * (1.0 - 2.0 * a) / nb;",
+                        "const double gbu = gxs * eta * (1.0 - a) / nb;"),
+    "p1bwd_norm_term_dropped": ("const double cn = n > eps ? coef / nb : 0.0;", "const double cn = 0.0;"),
+    "p1bwd_emitted_key_uses_next_d": ("gkh[r] = 2.0 * kh[r] * gs + dt[r] * gk[r];",
+                                      "gkh[r] = 2.0 * kh[r] * gs + (dt[r] + coef * kh[r] * kh[r]) * gk[r];"),
 }
 
 _EMIT_LATE = (
