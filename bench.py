@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step timing")
     ap.add_argument("--no-varlen", action="store_true", help="skip the packed variable-length timing")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward timing")
+    ap.add_argument("--no-osdn-bwd", action="store_true", help="skip the OSDN layer backward timing")
+    ap.add_argument("--no-kda", action="store_true", help="skip the per-channel-gate forward timing")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the copy / GEMM ceiling measurements")
     ap.add_argument("--cpu-heads", type=int, default=0, help="heads in the CPU sample (0: auto)")
@@ -491,6 +493,70 @@ def time_bwd(w, steps, warmup):
             "workspace_bytes": ws.numel()}
 
 
+def _event_time(step, steps, warmup):
+    import torch
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def time_osdn_bwd(steps, warmup):
+    """Backward of the whole OSDN layer (dp_osdn_bwd_bf16: phase 1 again with
+    its trajectory of d, the write-key backward, phase 1's reverse scan) on the
+    write-key workload's shape, inputs and workspace resident in HBM."""
+    import torch
+
+    import linear_rnn_sequence_amd as dp
+    from linear_rnn_sequence_amd.inputs import WORKLOADS, make, make_grads
+
+    w = WORKLOADS["c5"]
+    dev = torch.device("cuda:0")
+    inp = make(w)
+    gr = make_grads(w, final=False)
+    q = inp["q"].to(dev)
+    k = inp["k"][:, :, :, 0].contiguous().to(dev)
+    v = inp["v"][:, :, :, 0].contiguous().to(dev)
+    beta = inp["beta"][..., 0].contiguous().to(dev)
+    dout = gr["dout"].to(dev)
+    ws = torch.empty(dp.osdn_bwd_workspace_size(w.B, w.H, w.L, w.dk, w.dv), dtype=torch.uint8, device=dev)
+    grads = dp.osdn_bwd(q, k, v, beta, dout, workspace=ws)
+    ms = _event_time(lambda: dp.osdn_bwd(q, k, v, beta, dout, workspace=ws, grads=grads), steps, warmup)
+    return {"workload": f"OSDN layer backward (phase 1 + write-key forward) of {describe(w)}; "
+                        "fp32 arithmetic, 32-token chunks",
+            "value": w.B * w.L / (ms / 1e3), "unit": "tokens/s", "ms_per_step": ms,
+            "workspace_bytes": ws.numel()}
+
+
+def time_kda(steps, warmup):
+    """Chunkwise forward with the KDA host's per-key-channel gate on the
+    LM-layer shape (alpha uniform in [0.9, 1] per channel and token)."""
+    import torch
+
+    import linear_rnn_sequence_amd as dp
+    from linear_rnn_sequence_amd.inputs import WORKLOADS, channel_gate, make
+
+    w = WORKLOADS["c3"]
+    dev = torch.device("cuda:0")
+    inp = make(w)
+    d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    ga = channel_gate(w.B, w.L, w.H, w.dk, seed=w.seed + 17, lo=0.9).to(dev)
+    ws = dp.alloc_workspace(w.n_h, w.B, w.H, w.L, w.dk, w.dv, w.chunk, d["q"].dtype, dev)
+    out, fs = dp.fwd(d["q"], d["k"], d["v"], d["beta"], chunk=w.chunk, ga=ga, workspace=ws)
+    ms = _event_time(lambda: dp.fwd(d["q"], d["k"], d["v"], d["beta"], chunk=w.chunk, ga=ga, out=out,
+                                    final_state=fs, workspace=ws), steps, warmup)
+    return {"workload": f"{describe(w)} with a per-key-channel gate alpha [B,L,H,dk] (KDA host)",
+            "value": w.B * w.L / (ms / 1e3), "unit": "tokens/s", "ms_per_step": ms,
+            "kernels": "dp_ut_kernel + dp_scan_kernel in their per-channel-gate form"}
+
+
 def measure_ceilings():
     """What this GPU sustains on plain library work, next to the published
     peaks: a 1 GiB device-to-device copy (read + write bytes / time) and an
@@ -753,6 +819,10 @@ def main():
                           "b64": time_decode(64, 16, 3, 128, 128)}
     if not a.no_bwd:
         line["bwd"] = time_bwd(w, max(5, a.steps // 10), max(3, a.warmup // 10))
+    if not a.no_osdn_bwd:
+        line["osdn_bwd"] = time_osdn_bwd(max(5, a.steps // 10), max(3, a.warmup // 10))
+    if not a.no_kda:
+        line["kda"] = time_kda(max(5, a.steps // 10), max(2, a.warmup // 10))
     if not a.no_ceilings:
         line["ceilings"] = measure_ceilings()
     if not a.no_cpu_baseline:

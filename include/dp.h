@@ -26,7 +26,8 @@
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller; the
  *     library never allocates, frees or keeps them.  Layouts are dense,
- *     row-major, in the order given.  q, k, kt and v must be 16-byte aligned.
+ *     row-major, in the order given.  q, k, kt, v and dout must be 16-byte
+ *     aligned.
  *   - "T" is the path element type: IEEE float for *_f32 entry points,
  *     bfloat16 (raw uint16 bits) for *_bf16.  beta, g, h0, final_state and
  *     the phase-1 vector d are always float32.
@@ -421,6 +422,96 @@ int dp_bwd_bf16(const void* q, const void* k, const void* v, const float* beta, 
                 const float* h0, const void* dout, const float* dfinal, int n_h, int B, int H,
                 int L, int dk, int dv, float* dq, float* dk_out, float* dv_out, float* dbeta,
                 float* dg, float* dh0, void* workspace, size_t workspace_bytes, dp_stream stream);
+
+/*
+ * Gradient of the write-key forward (dp_fwd_wk_*; OSDN notes sec. 2.5 phase 2,
+ * App.A.2: M = strict_tril(diag(beta)(K W^T)), the state update and the
+ * readout scores with the write keys W, the state read and X with the unit
+ * read keys K).  Arguments as dp_bwd_*, plus
+ *   kt   [B, L, H, n_h, dk]  T    the write keys, as the forward used them
+ *   dkt  [B, L, H, n_h, dk]  f32  written: the gradient w.r.t. kt (kt is used
+ *                                 as given, so no normalisation is undone)
+ * and dk_out is then the gradient w.r.t. the raw read keys only.  Workspace:
+ * dp_bwd_workspace_size() bytes.  Errors as dp_bwd_*, and DP_EINVAL for a
+ * NULL kt or dkt when L > 0.
+ */
+int dp_bwd_wk_f32(const float* q, const float* k, const float* kt, const float* v, const float* beta,
+                  const float* g, const float* h0, const float* dout, const float* dfinal, int n_h, int B,
+                  int H, int L, int dk, int dv, float* dq, float* dk_out, float* dkt, float* dv_out,
+                  float* dbeta, float* dg, float* dh0, void* workspace, size_t workspace_bytes,
+                  dp_stream stream);
+int dp_bwd_wk_bf16(const void* q, const void* k, const void* kt, const void* v, const float* beta,
+                   const float* g, const float* h0, const void* dout, const float* dfinal, int n_h, int B,
+                   int H, int L, int dk, int dv, float* dq, float* dk_out, float* dkt, float* dv_out,
+                   float* dbeta, float* dg, float* dh0, void* workspace, size_t workspace_bytes,
+                   dp_stream stream);
+
+/*
+ * Gradient of OSDN phase 1 (OSDN notes sec. 2.5, closing paragraph: the write
+ * key kt_t = d_t o kh_t passes its gradient into d_t and k_t, and the
+ * gradient of d runs back through the recursion of sec. 2.4; with the
+ * retention of sec. 2.6 and the beta-free step of sec. 2.7).  The derivative
+ * of the projection onto the box is taken as 1 on [dmin, dmax] (end points
+ * included) and 0 outside, per coordinate, as for the beta clamp.  Phase 1 is
+ * run again first from d0, keeping every d_t in the workspace.
+ *   k, beta, r, flags, eta, dmin, dmax, eps: as dp_osdn_precond_ex_* (n_h = 1
+ *                layout; r may be NULL)
+ *   d0       [B, H, dk]    f32  d_1, or NULL (all ones)
+ *   dkt      [B, L, H, dk] f32  gradient on the emitted write keys
+ *   dd_final [B, H, dk]    f32  gradient on the final d, or NULL (zero)
+ *   dk_out   [B, L, H, dk] f32  ACCUMULATED into: += the raw-key gradient
+ *   dbeta    [B, L, H]     f32  ACCUMULATED into: += the beta gradient (none
+ *                               with DP_PRECOND_BETA_FREE or outside [0, 2])
+ *   dret     [B, L, H]     f32  written (zero without r), or NULL
+ *   dd0      [B, H, dk]    f32  written: the gradient on d_1, or NULL
+ * dk_out and dbeta accumulate so that they can already hold the write-key
+ * forward's gradients on the same keys and beta (dp_bwd_wk_*, n_h = 1); clear
+ * them first for phase 1 alone.  workspace: dp_osdn_precond_bwd_workspace_size()
+ * bytes, 256-byte aligned.  Errors: those of dp_osdn_precond_ex_*, DP_EINVAL
+ * for a NULL dkt, dk_out or dbeta when L > 0, DP_EWORKSPACE, DP_EHIP.
+ */
+int dp_osdn_precond_bwd_workspace_size(int B, int H, int L, int dk, size_t* bytes);
+int dp_osdn_precond_bwd_f32(const float* k, const float* beta, const float* r, const float* d0,
+                            const float* dkt, const float* dd_final, int flags, int B, int H, int L,
+                            int dk, float eta, float dmin, float dmax, float eps, float* dk_out,
+                            float* dbeta, float* dret, float* dd0, void* workspace,
+                            size_t workspace_bytes, dp_stream stream);
+int dp_osdn_precond_bwd_bf16(const void* k, const float* beta, const float* r, const float* d0,
+                             const float* dkt, const float* dd_final, int flags, int B, int H, int L,
+                             int dk, float eta, float dmin, float dmax, float eps, float* dk_out,
+                             float* dbeta, float* dret, float* dd0, void* workspace,
+                             size_t workspace_bytes, dp_stream stream);
+
+/*
+ * Gradient of the whole OSDN layer (n_h = 1; OSDN notes sec. 2.5): phase 1
+ * over (k, beta) emits the write keys, the write-key forward reads q, the raw
+ * keys k, v, beta, g and h0 with them.  One call runs phase 1 again (keeping
+ * d_t), the write-key backward, then phase 1's reverse scan; the two routes
+ * into k and beta are summed.
+ *   q [B,L,H,dk], k [B,L,H,dk], v [B,L,H,dv], dout [B,L,H,dv]   T
+ *   beta, r [B,L,H] f32; g [B,L,H] f32 or NULL; h0, dfinal [B,H,dk,dv] f32 or
+ *   NULL; d0, dd_final [B,H,dk] f32 or NULL; flags, eta, dmin, dmax, eps as
+ *   dp_osdn_precond_ex_*.
+ * Outputs (f32, written): dq, dk_out [B,L,H,dk], dv_out [B,L,H,dv], dbeta
+ * [B,L,H], dg (when g; may be NULL), dh0, dret, dd0 (each may be NULL).
+ * workspace: dp_osdn_bwd_workspace_size() bytes, 256-byte aligned (phase 1's
+ * trajectory and write keys, the write-key gradient, the backward's own).
+ * Every check runs before anything is enqueued.  Errors: those of dp_bwd_*
+ * and dp_osdn_precond_ex_*.
+ */
+int dp_osdn_bwd_workspace_size(int B, int H, int L, int dk, int dv, size_t* bytes);
+int dp_osdn_bwd_f32(const float* q, const float* k, const float* v, const float* beta, const float* g,
+                    const float* h0, const float* r, const float* d0, const float* dout,
+                    const float* dfinal, const float* dd_final, int flags, int B, int H, int L, int dk,
+                    int dv, float eta, float dmin, float dmax, float eps, float* dq, float* dk_out,
+                    float* dv_out, float* dbeta, float* dg, float* dh0, float* dret, float* dd0,
+                    void* workspace, size_t workspace_bytes, dp_stream stream);
+int dp_osdn_bwd_bf16(const void* q, const void* k, const void* v, const float* beta, const float* g,
+                     const float* h0, const float* r, const float* d0, const void* dout,
+                     const float* dfinal, const float* dd_final, int flags, int B, int H, int L, int dk,
+                     int dv, float eta, float dmin, float dmax, float eps, float* dq, float* dk_out,
+                     float* dv_out, float* dbeta, float* dg, float* dh0, float* dret, float* dd0,
+                     void* workspace, size_t workspace_bytes, dp_stream stream);
 
 #ifdef __cplusplus
 }

@@ -38,6 +38,9 @@ EXPORTS = (
     "dp_bwd_workspace_size", "dp_bwd_f32", "dp_bwd_bf16",
     "dp_osdn_fwd_workspace_size", "dp_osdn_fwd_bf16", "dp_pipeline_create", "dp_pipeline_destroy",
     "dp_fwd_varlen_noalloc_bf16",
+    "dp_bwd_wk_f32", "dp_bwd_wk_bf16",
+    "dp_osdn_precond_bwd_workspace_size", "dp_osdn_precond_bwd_f32", "dp_osdn_precond_bwd_bf16",
+    "dp_osdn_bwd_workspace_size", "dp_osdn_bwd_f32", "dp_osdn_bwd_bf16",
 )
 
 _lib = None
@@ -105,6 +108,22 @@ def load() -> ctypes.CDLL:
         for name in ("dp_bwd_f32", "dp_bwd_bf16"):
             getattr(lib, name).restype = _I
             getattr(lib, name).argtypes = bwd
+        bwd_wk = [_P] * 9 + [_I] * 6 + [_P] * 8 + [ctypes.c_size_t, _P]
+        for name in ("dp_bwd_wk_f32", "dp_bwd_wk_bf16"):
+            getattr(lib, name).restype = _I
+            getattr(lib, name).argtypes = bwd_wk
+        lib.dp_osdn_precond_bwd_workspace_size.restype = _I
+        lib.dp_osdn_precond_bwd_workspace_size.argtypes = [_I] * 4 + [ctypes.POINTER(ctypes.c_size_t)]
+        pbwd = [_P] * 6 + [_I] * 5 + [_F] * 4 + [_P] * 5 + [ctypes.c_size_t, _P]
+        for name in ("dp_osdn_precond_bwd_f32", "dp_osdn_precond_bwd_bf16"):
+            getattr(lib, name).restype = _I
+            getattr(lib, name).argtypes = pbwd
+        lib.dp_osdn_bwd_workspace_size.restype = _I
+        lib.dp_osdn_bwd_workspace_size.argtypes = [_I] * 5 + [ctypes.POINTER(ctypes.c_size_t)]
+        obwd = [_P] * 11 + [_I] * 6 + [_F] * 4 + [_P] * 9 + [ctypes.c_size_t, _P]
+        for name in ("dp_osdn_bwd_f32", "dp_osdn_bwd_bf16"):
+            getattr(lib, name).restype = _I
+            getattr(lib, name).argtypes = obwd
         lib.dp_osdn_fwd_workspace_size.restype = _I
         lib.dp_osdn_fwd_workspace_size.argtypes = [_I] * 7 + [ctypes.POINTER(ctypes.c_size_t)]
         lib.dp_osdn_fwd_bf16.restype = _I
@@ -498,15 +517,16 @@ def bwd_workspace_size(n_h, B, H, L, dk, dv) -> int:
     return n.value
 
 
-def bwd(q, k, v, beta, dout, g=None, *, h0=None, dfinal=None, workspace=None, grads=None,
+def bwd(q, k, v, beta, dout, g=None, *, h0=None, dfinal=None, kt=None, workspace=None, grads=None,
         stream=None) -> dict:
-    """Gradient of the symmetric forward through libdp (dp_bwd_f32 / dp_bwd_bf16).
+    """Gradient of the forward through libdp (dp_bwd_* / dp_bwd_wk_*).
 
     Inputs as :func:`fwd` (q, k, v and dout in one dtype, float32 or
     bfloat16), dout [B,L,H,dv] the gradient on out and dfinal [B,H,dk,dv] f32
-    (or None) the gradient on the final state.  Returns a dict of float32
-    gradients ``q, k, v, beta, h0`` and ``g`` when a gate is given; ``grads``
-    may hold preallocated tensors under those names.
+    (or None) the gradient on the final state; kt (the shape and dtype of k)
+    selects the write-key forward's gradient.  Returns a dict of float32
+    gradients ``q, k, v, beta, h0``, ``g`` when a gate is given and ``kt``
+    with write keys; ``grads`` may hold preallocated tensors under those names.
     """
     if q.dim() != 4 or k.dim() != 5 or v.dim() != 5:
         raise ValueError("expected q[B,L,H,dk], k[B,L,H,n_h,dk], v[B,L,H,n_h,dv]")
@@ -521,12 +541,15 @@ def bwd(q, k, v, beta, dout, g=None, *, h0=None, dfinal=None, workspace=None, gr
     _need(g, "g", torch.float32, (B, L, H), dev)
     _need(h0, "h0", torch.float32, (B, H, dk, dv), dev)
     _need(dfinal, "dfinal", torch.float32, (B, H, dk, dv), dev)
+    _need(kt, "kt", dt, (B, L, H, n_h, dk), dev)
     if not q.is_contiguous():
         raise ValueError("q must be contiguous")
     shapes = dict(q=(B, L, H, dk), k=(B, L, H, n_h, dk), v=(B, L, H, n_h, dv), beta=(B, L, H, n_h),
                   h0=(B, H, dk, dv))
     if g is not None:
         shapes["g"] = (B, L, H)
+    if kt is not None:
+        shapes["kt"] = (B, L, H, n_h, dk)
     out = dict(grads or {})
     for n, shp in shapes.items():
         if n not in out:
@@ -535,10 +558,127 @@ def bwd(q, k, v, beta, dout, g=None, *, h0=None, dfinal=None, workspace=None, gr
     if workspace is None:
         nbytes = bwd_workspace_size(n_h, B, H, L, dk, dv)
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
-    fn = getattr(load(), f"dp_bwd_{suf}")
-    rc = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(h0), _ptr(dout), _ptr(dfinal),
-            n_h, B, H, L, dk, dv, _ptr(out["q"]), _ptr(out["k"]), _ptr(out["v"]), _ptr(out["beta"]),
-            _ptr(out.get("g")), _ptr(out["h0"]), _ptr(workspace),
-            workspace.numel() * workspace.element_size(), _stream(stream))
-    _check(rc, f"dp_bwd_{suf}")
+    wsb = workspace.numel() * workspace.element_size()
+    if kt is None:
+        fn = getattr(load(), f"dp_bwd_{suf}")
+        rc = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(h0), _ptr(dout), _ptr(dfinal),
+                n_h, B, H, L, dk, dv, _ptr(out["q"]), _ptr(out["k"]), _ptr(out["v"]), _ptr(out["beta"]),
+                _ptr(out.get("g")), _ptr(out["h0"]), _ptr(workspace), wsb, _stream(stream))
+        _check(rc, f"dp_bwd_{suf}")
+    else:
+        fn = getattr(load(), f"dp_bwd_wk_{suf}")
+        rc = fn(_ptr(q), _ptr(k), _ptr(kt), _ptr(v), _ptr(beta), _ptr(g), _ptr(h0), _ptr(dout),
+                _ptr(dfinal), n_h, B, H, L, dk, dv, _ptr(out["q"]), _ptr(out["k"]), _ptr(out["kt"]),
+                _ptr(out["v"]), _ptr(out["beta"]), _ptr(out.get("g")), _ptr(out["h0"]), _ptr(workspace),
+                wsb, _stream(stream))
+        _check(rc, f"dp_bwd_wk_{suf}")
+    return out
+
+
+def osdn_precond_bwd_workspace_size(B, H, L, dk) -> int:
+    """Workspace bytes of :func:`osdn_precond_bwd`."""
+    n = ctypes.c_size_t(0)
+    _check(load().dp_osdn_precond_bwd_workspace_size(B, H, L, dk, ctypes.byref(n)),
+           "dp_osdn_precond_bwd_workspace_size")
+    return n.value
+
+
+def osdn_precond_bwd(k, beta, dkt, *, eta: float = 3e-3, dmin: float = 0.5, dmax: float = 2.0,
+                     eps: float = 1e-6, d0=None, dd_final=None, r=None, beta_aware: bool = True,
+                     dk=None, dbeta=None, workspace=None, stream=None) -> dict:
+    """Gradient of OSDN phase 1 through libdp (dp_osdn_precond_bwd_*).
+
+    k [B,L,H,dk] (float32 or bfloat16), beta [B,L,H] f32, dkt [B,L,H,dk] f32
+    the gradient on the emitted write keys, dd_final [B,H,dk] f32 or None on
+    the final d; d0, r, beta_aware and the constants as :func:`osdn_precond`.
+    The key and beta gradients are ADDED into ``dk`` / ``dbeta`` when given
+    (zero-filled tensors otherwise).  Returns float32 ``k, beta, d0`` and ``r``
+    when a retention gate is given.
+    """
+    if k.dim() != 4:
+        raise ValueError("expected k[B,L,H,dk]")
+    B, L, H, dkk = k.shape
+    dev, dt = k.device, k.dtype
+    suf = _suffix(dt)
+    _need(beta, "beta", torch.float32, (B, L, H), dev)
+    _need(dkt, "dkt", torch.float32, (B, L, H, dkk), dev)
+    _need(r, "r", torch.float32, (B, L, H), dev)
+    _need(d0, "d0", torch.float32, (B, H, dkk), dev)
+    _need(dd_final, "dd_final", torch.float32, (B, H, dkk), dev)
+    if not k.is_contiguous():
+        raise ValueError("k must be contiguous")
+    if dk is None:
+        dk = torch.zeros(B, L, H, dkk, dtype=torch.float32, device=dev)
+    if dbeta is None:
+        dbeta = torch.zeros(B, L, H, dtype=torch.float32, device=dev)
+    _need(dk, "dk", torch.float32, (B, L, H, dkk), dev)
+    _need(dbeta, "dbeta", torch.float32, (B, L, H), dev)
+    out = dict(k=dk, beta=dbeta, d0=torch.empty(B, H, dkk, dtype=torch.float32, device=dev))
+    if r is not None:
+        out["r"] = torch.empty(B, L, H, dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(osdn_precond_bwd_workspace_size(B, H, L, dkk), 1), dtype=torch.uint8,
+                                device=dev)
+    flags = 0 if beta_aware else PRECOND_BETA_FREE
+    fn = getattr(load(), f"dp_osdn_precond_bwd_{suf}")
+    rc = fn(_ptr(k), _ptr(beta), _ptr(r), _ptr(d0), _ptr(dkt), _ptr(dd_final), flags, B, H, L, dkk, eta,
+            dmin, dmax, eps, _ptr(out["k"]), _ptr(out["beta"]), _ptr(out.get("r")), _ptr(out["d0"]),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc, f"dp_osdn_precond_bwd_{suf}")
+    return out
+
+
+def osdn_bwd_workspace_size(B, H, L, dk, dv) -> int:
+    """Workspace bytes of :func:`osdn_bwd`."""
+    n = ctypes.c_size_t(0)
+    _check(load().dp_osdn_bwd_workspace_size(B, H, L, dk, dv, ctypes.byref(n)), "dp_osdn_bwd_workspace_size")
+    return n.value
+
+
+def osdn_bwd(q, k, v, beta, dout, g=None, *, h0=None, dfinal=None, r=None, d0=None, dd_final=None,
+             eta: float = 3e-3, dmin: float = 0.5, dmax: float = 2.0, eps: float = 1e-6,
+             beta_aware: bool = True, workspace=None, grads=None, stream=None) -> dict:
+    """Gradient of the whole OSDN layer (n_h = 1) through libdp (dp_osdn_bwd_*).
+
+    q, k [B,L,H,dk], v, dout [B,L,H,dv] in one dtype (float32 or bfloat16);
+    beta [B,L,H] f32; g [B,L,H], h0/dfinal [B,H,dk,dv], r [B,L,H], d0/dd_final
+    [B,H,dk] f32 or None; phase-1 constants as :func:`osdn_precond`.  Returns
+    float32 ``q, k, v, beta, h0, d0`` (+ ``g``, ``r`` when given).
+    """
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("expected q[B,L,H,dk], k[B,L,H,dk], v[B,L,H,dv]")
+    B, L, H, dk = q.shape
+    dv = v.shape[3]
+    dev, dt = q.device, q.dtype
+    suf = _suffix(dt)
+    _need(k, "k", dt, (B, L, H, dk), dev)
+    _need(v, "v", dt, (B, L, H, dv), dev)
+    _need(dout, "dout", dt, (B, L, H, dv), dev)
+    _need(beta, "beta", torch.float32, (B, L, H), dev)
+    for name, x, shp in (("g", g, (B, L, H)), ("r", r, (B, L, H)), ("h0", h0, (B, H, dk, dv)),
+                         ("dfinal", dfinal, (B, H, dk, dv)), ("d0", d0, (B, H, dk)), ("dd_final", dd_final, (B, H, dk))):
+        _need(x, name, torch.float32, shp, dev)
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    shapes = dict(q=(B, L, H, dk), k=(B, L, H, dk), v=(B, L, H, dv), beta=(B, L, H), h0=(B, H, dk, dv),
+                  d0=(B, H, dk))
+    if g is not None:
+        shapes["g"] = (B, L, H)
+    if r is not None:
+        shapes["r"] = (B, L, H)
+    out = dict(grads or {})
+    for n, shp in shapes.items():
+        if n not in out:
+            out[n] = torch.empty(shp, dtype=torch.float32, device=dev)
+        _need(out[n], "grad " + n, torch.float32, shp, dev)
+    if workspace is None:
+        workspace = torch.empty(max(osdn_bwd_workspace_size(B, H, L, dk, dv), 1), dtype=torch.uint8, device=dev)
+    flags = 0 if beta_aware else PRECOND_BETA_FREE
+    fn = getattr(load(), f"dp_osdn_bwd_{suf}")
+    rc = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(h0), _ptr(r), _ptr(d0), _ptr(dout),
+            _ptr(dfinal), _ptr(dd_final), flags, B, H, L, dk, dv, eta, dmin, dmax, eps, _ptr(out["q"]),
+            _ptr(out["k"]), _ptr(out["v"]), _ptr(out["beta"]), _ptr(out.get("g")), _ptr(out["h0"]),
+            _ptr(out.get("r")), _ptr(out["d0"]), _ptr(workspace), workspace.numel() * workspace.element_size(),
+            _stream(stream))
+    _check(rc, f"dp_osdn_bwd_{suf}")
     return out

@@ -97,11 +97,25 @@ size_t ws_blocks_bytes(const Shape& s) {
 size_t ws_sink_bytes(const Shape& s) { return align_up((size_t)s.B * s.H * (s.dv / 16) * 64 * 4, kWsAlign); }
 
 // The per-channel-gate form (UT / scan kernels) keeps T, the per-sub-step
-// scalars and the readout scores (RT x C) per chunk.
+// scalars and the readout scores (RT x C) per chunk, then the gated operands
+// the UT kernel writes for the scan: read and write keys (the layout of k),
+// readout queries (the layout of q) and the state decay per chunk (dk fp32).
 size_t ws_s_bytes(const Shape& s) { return align_up((size_t)s.B * s.H * num_chunks(s) * s.chunk * sizeof(float2), kWsAlign); }
+struct CgWs {
+  size_t p, kg, qg, dec;
+};
+CgWs cg_ws(const Shape& s, int elem) {
+  CgWs w;
+  const size_t nch = (size_t)s.B * s.H * num_chunks(s);
+  w.p = align_up(nch * readout_rows(s.chunk, s.n_h) * s.chunk * elem, kWsAlign);
+  w.kg = align_up((size_t)s.B * s.L * s.H * s.n_h * s.dk * elem, kWsAlign);
+  w.qg = align_up((size_t)s.B * s.L * s.H * s.dk * elem, kWsAlign);
+  w.dec = align_up(nch * s.dk * 4, kWsAlign);
+  return w;
+}
 size_t ws_cg_bytes(const Shape& s, int elem) {
-  return ws_t_bytes(s, elem) + ws_s_bytes(s) +
-         align_up((size_t)s.B * s.H * num_chunks(s) * readout_rows(s.chunk, s.n_h) * s.chunk * elem, kWsAlign);
+  const CgWs w = cg_ws(s, elem);
+  return ws_t_bytes(s, elem) + ws_s_bytes(s) + w.p + 2 * w.kg + w.qg + w.dec;
 }
 
 size_t ws_total(const Shape& s, int elem) {
@@ -365,7 +379,15 @@ int fwd_impl(int elem, const void* q, const void* k, const void* kt, const void*
     a.wsT = workspace;
     a.wsS = reinterpret_cast<float2*>(static_cast<char*>(workspace) + ws_t_bytes(s, elem));
     if (elem == 2) a.sink = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws_blocks_bytes(s));
-    if (ga != nullptr) a.wsP = static_cast<char*>(workspace) + ws_t_bytes(s, elem) + ws_s_bytes(s);
+    if (ga != nullptr) {
+      const CgWs w = cg_ws(s, elem);
+      char* base = static_cast<char*>(workspace) + ws_t_bytes(s, elem) + ws_s_bytes(s);
+      a.wsP = base;
+      a.wsKg = base + w.p;
+      a.wsKtg = base + w.p + w.kg;
+      a.wsQg = base + w.p + 2 * w.kg;
+      a.wsDec = reinterpret_cast<float*>(base + w.p + 2 * w.kg + w.qg);
+    }
   }
   a.ga = ga;
   a.N = L * n_h;
@@ -571,7 +593,9 @@ int precond_impl(int elem, const void* k, const float* beta, const float* ret, i
                  int B, int H, int L, int dk, float eta, float dmin, float dmax, float eps,
                  float* d_state, void* kt, bool open_box, dp_stream stream, int Ls = 0, int t0 = 0,
                  bool dry = false) {
-  if (k == nullptr || beta == nullptr || d_state == nullptr || kt == nullptr) return DP_EINVAL;
+  // with L == 0 the per-token tensors are empty and may be null
+  if (d_state == nullptr || (L > 0 && (k == nullptr || beta == nullptr || kt == nullptr))) return DP_EINVAL;
+  if (!aligned16(k) || !aligned16(kt)) return DP_EINVAL;
   if (B <= 0 || H <= 0 || L < 0) return DP_EINVAL;
   if ((flags & ~DP_PRECOND_BETA_FREE) != 0) return DP_EINVAL;
   if (!dim_ok(dk)) return DP_ENOTSUP;
@@ -672,12 +696,16 @@ int bwd_impl(int elem, const void* q, const void* k, const void* v, const float*
              const float* g, const float* h0, const void* dout, const float* dfinal, int n_h,
              int B, int H, int L, int dk, int dv, float* dq, float* dk_out, float* dv_out,
              float* dbeta, float* dg, float* dh0, void* workspace, size_t workspace_bytes,
-             dp_stream stream) {
+             dp_stream stream, const void* kt = nullptr, float* dkt = nullptr, bool wk = false,
+             bool dry = false) {
   const Shape s{n_h, B, H, L, dk, dv, dp::kBwdChunk};
   int rc = check_shape(s);
   if (rc != DP_OK) return rc;
   if (L > 0 && (q == nullptr || k == nullptr || v == nullptr || beta == nullptr || dout == nullptr ||
                 dq == nullptr || dk_out == nullptr || dv_out == nullptr || dbeta == nullptr))
+    return DP_EINVAL;
+  if (wk && L > 0 && (kt == nullptr || dkt == nullptr)) return DP_EINVAL;
+  if (L > 0 && (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || (wk && !aligned16(kt))))
     return DP_EINVAL;
   const BwdWs w = bwd_ws(s);
   if (workspace_bytes < w.total || workspace == nullptr) return DP_EWORKSPACE;
@@ -687,6 +715,8 @@ int bwd_impl(int elem, const void* q, const void* k, const void* v, const float*
   dp::FwdArgs fa;
   memset(&fa, 0, sizeof(fa));
   fa.k = k;
+  fa.kt = wk ? kt : nullptr;
+  fa.asym = wk ? 1 : 0;
   fa.beta = beta;
   fa.g = g;
   fa.wsT = ws;
@@ -708,6 +738,8 @@ int bwd_impl(int elem, const void* q, const void* k, const void* v, const float*
   a.beta = beta;
   a.g = g;
   a.h0 = h0;
+  a.kt = wk ? kt : nullptr;
+  a.dkt = wk ? dkt : nullptr;
   a.dout = dout;
   a.dfinal = dfinal;
   a.wsT = reinterpret_cast<const float*>(ws);
@@ -733,8 +765,171 @@ int bwd_impl(int elem, const void* q, const void* k, const void* v, const float*
   a.nh_magic = fa.nh_magic;
   a.nh_shift = fa.nh_shift;
   if (a.RT != 16 && a.RT != 32) return DP_ENOTSUP;
+  if (dry) return DP_OK;
   const hipError_t e = dispatch_bwd(elem, dk, fa, a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DP_OK : DP_EHIP;
+}
+
+hipError_t dispatch_precond_bwd(int elem, int dk, const dp::PrecondBwdArgs& a, hipStream_t st) {
+  if (elem == 4) {
+    switch (dk) {
+      case 16: return dp_launch_precond_bwd_f32_16(a, st);
+      case 32: return dp_launch_precond_bwd_f32_32(a, st);
+      case 64: return dp_launch_precond_bwd_f32_64(a, st);
+      case 128: return dp_launch_precond_bwd_f32_128(a, st);
+    }
+  } else {
+    switch (dk) {
+      case 16: return dp_launch_precond_bwd_bf16_16(a, st);
+      case 32: return dp_launch_precond_bwd_bf16_32(a, st);
+      case 64: return dp_launch_precond_bwd_bf16_64(a, st);
+      case 128: return dp_launch_precond_bwd_bf16_128(a, st);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+// Gradient of phase 1: the workspace holds d (B H dk f32), the trajectory of
+// d (B L H dk f32) and the write keys the forward emits again (B L H dk
+// elements of the input type; sized for fp32).
+struct PrecondBwdWs {
+  size_t d, dtr, kt, total;
+};
+PrecondBwdWs precond_bwd_ws(int B, int H, int L, int dk) {
+  PrecondBwdWs w;
+  w.d = align_up((size_t)B * H * dk * 4, kWsAlign);
+  w.dtr = align_up((size_t)B * L * H * dk * 4, kWsAlign);
+  w.kt = w.dtr;
+  w.total = w.d + w.dtr + w.kt;
+  return w;
+}
+
+// Phase 1 forward into `ws` with its trajectory of d: d_1 is d0 (NULL: ones).
+hipError_t precond_traj(int elem, const void* k, const float* beta, const float* ret, const float* d0,
+                        int flags, int B, int H, int L, int dk, float eta, float dmin, float dmax, float eps,
+                        char* ws, void* kt_ws, hipStream_t st) {
+  const PrecondBwdWs w = precond_bwd_ws(B, H, L, dk);
+  float* dws = reinterpret_cast<float*>(ws);
+  if (d0 != nullptr) {
+    const hipError_t e = hipMemcpyAsync(dws, d0, (size_t)B * H * dk * 4, hipMemcpyDeviceToDevice, st);
+    if (e != hipSuccess) return e;
+  }
+  dp::PrecondArgs a;
+  a.k = k;
+  a.beta = beta;
+  a.ret = ret;
+  a.d = dws;
+  a.kt = kt_ws;
+  a.B = B;
+  a.H = H;
+  a.L = L;
+  a.beta_aware = (flags & DP_PRECOND_BETA_FREE) ? 0 : 1;
+  a.eta = eta;
+  a.dmin = dmin;
+  a.dmax = dmax;
+  a.eps = eps;
+  a.dtr = reinterpret_cast<float*>(ws + w.d);
+  a.d_ones = d0 == nullptr ? 1 : 0;
+  return dispatch_precond(elem, dk, a, st);
+}
+
+// The reverse scan of phase 1, which adds its key and beta terms into dk_out
+// and dbeta.  have_traj: `ws` already holds the trajectory of d (an earlier
+// precond_traj on the same inputs); else phase 1 runs again first.
+int precond_bwd_impl(int elem, const void* k, const float* beta, const float* ret, const float* d0,
+                     const float* dkt, const float* dd_final, int flags, int B, int H, int L, int dk,
+                     float eta, float dmin, float dmax, float eps, float* dk_out, float* dbeta,
+                     float* dret, float* dd0, char* ws, void* kt_ws, dp_stream stream, bool dry,
+                     bool have_traj = false) {
+  const PrecondBwdWs w = precond_bwd_ws(B, H, L, dk);
+  float* dws = reinterpret_cast<float*>(ws);
+  float* dtr = reinterpret_cast<float*>(ws + w.d);
+  // the forward's own checks (open box allowed, as for the variants)
+  int rc = precond_impl(elem, k, beta, ret, flags, B, H, L, dk, eta, dmin, dmax, eps, dws, kt_ws, true,
+                        stream, 0, 0, true);
+  if (rc != DP_OK) return rc;
+  if (L > 0 && (dkt == nullptr || dk_out == nullptr || dbeta == nullptr)) return DP_EINVAL;
+  if (dry) return DP_OK;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  // (with L == 0 both kernels run no token: the reverse scan writes dd0 = dd_final)
+  if (!have_traj) {
+    const hipError_t e = precond_traj(elem, k, beta, ret, d0, flags, B, H, L, dk, eta, dmin, dmax, eps, ws,
+                                      kt_ws, st);
+    if (e != hipSuccess) return DP_EHIP;
+  }
+  dp::PrecondBwdArgs g;
+  g.k = k;
+  g.beta = beta;
+  g.ret = ret;
+  g.dtr = dtr;
+  g.dkt = dkt;
+  g.dd_final = dd_final;
+  g.dk = dk_out;
+  g.dbeta = dbeta;
+  g.dret = dret;
+  g.dd0 = dd0;
+  g.B = B;
+  g.H = H;
+  g.L = L;
+  g.beta_aware = (flags & DP_PRECOND_BETA_FREE) ? 0 : 1;
+  g.eta = eta;
+  g.dmin = dmin;
+  g.dmax = dmax;
+  g.eps = eps;
+  return dispatch_precond_bwd(elem, dk, g, st) == hipSuccess ? DP_OK : DP_EHIP;
+}
+
+// The whole OSDN layer's gradient (n_h = 1): phase 1 again, the write-key
+// backward, then phase 1's reverse scan into the same dk and dbeta.
+struct OsdnBwdWs {
+  size_t p1, kt, dkt, bwd, total;
+};
+OsdnBwdWs osdn_bwd_ws(int B, int H, int L, int dk, int dv) {
+  OsdnBwdWs w;
+  w.p1 = precond_bwd_ws(B, H, L, dk).total;
+  w.kt = align_up((size_t)B * L * H * dk * 4, kWsAlign);
+  w.dkt = w.kt;
+  const Shape s{1, B, H, L, dk, dv, dp::kBwdChunk};
+  w.bwd = bwd_ws(s).total;
+  w.total = w.p1 + w.kt + w.dkt + w.bwd;
+  return w;
+}
+
+int osdn_bwd_impl(int elem, const void* q, const void* k, const void* v, const float* beta,
+                  const float* g, const float* h0, const float* ret, const float* d0, const void* dout,
+                  const float* dfinal, const float* dd_final, int flags, int B, int H, int L, int dk,
+                  int dv, float eta, float dmin, float dmax, float eps, float* dq, float* dk_out,
+                  float* dv_out, float* dbeta, float* dg, float* dh0, float* dret, float* dd0,
+                  void* workspace, size_t workspace_bytes, dp_stream stream) {
+  const Shape s{1, B, H, L, dk, dv, dp::kBwdChunk};
+  int rc = check_shape(s);
+  if (rc != DP_OK) return rc;
+  if (L > 0 && (q == nullptr || v == nullptr || dout == nullptr || dq == nullptr || dv_out == nullptr))
+    return DP_EINVAL;
+  const OsdnBwdWs w = osdn_bwd_ws(B, H, L, dk, dv);
+  if (workspace_bytes < w.total || workspace == nullptr) return DP_EWORKSPACE;
+  if (((uintptr_t)workspace & (kWsAlign - 1)) != 0) return DP_EWORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  void* kt = ws + w.p1;
+  float* dkt = reinterpret_cast<float*>(ws + w.p1 + w.kt);
+  char* bws = ws + w.p1 + w.kt + w.dkt;
+  char* p1ws = ws;
+  // every check first: nothing is enqueued when any of them fails
+  rc = precond_bwd_impl(elem, k, beta, ret, d0, dkt, dd_final, flags, B, H, L, dk, eta, dmin, dmax, eps,
+                        dk_out, dbeta, dret, dd0, p1ws, kt, stream, true);
+  if (rc != DP_OK) return rc;
+  rc = bwd_impl(elem, q, k, v, beta, g, h0, dout, dfinal, 1, B, H, L, dk, dv, dq, dk_out, dv_out, dbeta, dg,
+                dh0, bws, w.bwd, stream, kt, dkt, true, true);
+  if (rc != DP_OK) return rc;
+  // phase 1 forward: the write keys for the write-key backward, and the trajectory of d
+  if (precond_traj(elem, k, beta, ret, d0, flags, B, H, L, dk, eta, dmin, dmax, eps, p1ws, kt,
+                   static_cast<hipStream_t>(stream)) != hipSuccess)
+    return DP_EHIP;
+  rc = bwd_impl(elem, q, k, v, beta, g, h0, dout, dfinal, 1, B, H, L, dk, dv, dq, dk_out, dv_out, dbeta, dg,
+                dh0, bws, w.bwd, stream, kt, dkt, true);
+  if (rc != DP_OK) return rc;
+  return precond_bwd_impl(elem, k, beta, ret, d0, dkt, dd_final, flags, B, H, L, dk, eta, dmin, dmax, eps,
+                          dk_out, dbeta, dret, dd0, p1ws, kt, stream, false, true);
 }
 
 }  // namespace
@@ -1031,6 +1226,98 @@ int dp_bwd_bf16(const void* q, const void* k, const void* v, const float* beta, 
                 float* dg, float* dh0, void* workspace, size_t workspace_bytes, dp_stream stream) {
   return bwd_impl(2, q, k, v, beta, g, h0, dout, dfinal, n_h, B, H, L, dk, dv, dq, dk_out, dv_out,
                   dbeta, dg, dh0, workspace, workspace_bytes, stream);
+}
+
+int dp_bwd_wk_f32(const float* q, const float* k, const float* kt, const float* v, const float* beta,
+                  const float* g, const float* h0, const float* dout, const float* dfinal, int n_h, int B,
+                  int H, int L, int dk, int dv, float* dq, float* dk_out, float* dkt, float* dv_out,
+                  float* dbeta, float* dg, float* dh0, void* workspace, size_t workspace_bytes,
+                  dp_stream stream) {
+  return bwd_impl(4, q, k, v, beta, g, h0, dout, dfinal, n_h, B, H, L, dk, dv, dq, dk_out, dv_out,
+                  dbeta, dg, dh0, workspace, workspace_bytes, stream, kt, dkt, true);
+}
+
+int dp_bwd_wk_bf16(const void* q, const void* k, const void* kt, const void* v, const float* beta,
+                   const float* g, const float* h0, const void* dout, const float* dfinal, int n_h, int B,
+                   int H, int L, int dk, int dv, float* dq, float* dk_out, float* dkt, float* dv_out,
+                   float* dbeta, float* dg, float* dh0, void* workspace, size_t workspace_bytes,
+                   dp_stream stream) {
+  return bwd_impl(2, q, k, v, beta, g, h0, dout, dfinal, n_h, B, H, L, dk, dv, dq, dk_out, dv_out,
+                  dbeta, dg, dh0, workspace, workspace_bytes, stream, kt, dkt, true);
+}
+
+int dp_osdn_precond_bwd_workspace_size(int B, int H, int L, int dk, size_t* bytes) {
+  if (bytes == nullptr) return DP_EINVAL;
+  if (B <= 0 || H <= 0 || L < 0) return DP_EINVAL;
+  if (!dim_ok(dk)) return DP_ENOTSUP;
+  if ((long long)B * H * (long long)L > (long long)1 << 40) return DP_ENOTSUP;
+  *bytes = precond_bwd_ws(B, H, L, dk).total;
+  return DP_OK;
+}
+
+static int precond_bwd_entry(int elem, const void* k, const float* beta, const float* r, const float* d0,
+                             const float* dkt, const float* dd_final, int flags, int B, int H, int L,
+                             int dk, float eta, float dmin, float dmax, float eps, float* dk_out,
+                             float* dbeta, float* dret, float* dd0, void* workspace,
+                             size_t workspace_bytes, dp_stream stream) {
+  size_t need = 0;
+  const int rc = dp_osdn_precond_bwd_workspace_size(B, H, L, dk, &need);
+  if (rc != DP_OK) return rc;
+  if (workspace == nullptr || workspace_bytes < need) return DP_EWORKSPACE;
+  if (((uintptr_t)workspace & (kWsAlign - 1)) != 0) return DP_EWORKSPACE;
+  const PrecondBwdWs w = precond_bwd_ws(B, H, L, dk);
+  char* ws = static_cast<char*>(workspace);
+  return precond_bwd_impl(elem, k, beta, r, d0, dkt, dd_final, flags, B, H, L, dk, eta, dmin, dmax, eps,
+                          dk_out, dbeta, dret, dd0, ws, ws + w.d + w.dtr, stream, false);
+}
+
+int dp_osdn_precond_bwd_f32(const float* k, const float* beta, const float* r, const float* d0,
+                            const float* dkt, const float* dd_final, int flags, int B, int H, int L,
+                            int dk, float eta, float dmin, float dmax, float eps, float* dk_out,
+                            float* dbeta, float* dret, float* dd0, void* workspace,
+                            size_t workspace_bytes, dp_stream stream) {
+  return precond_bwd_entry(4, k, beta, r, d0, dkt, dd_final, flags, B, H, L, dk, eta, dmin, dmax, eps,
+                           dk_out, dbeta, dret, dd0, workspace, workspace_bytes, stream);
+}
+
+int dp_osdn_precond_bwd_bf16(const void* k, const float* beta, const float* r, const float* d0,
+                             const float* dkt, const float* dd_final, int flags, int B, int H, int L,
+                             int dk, float eta, float dmin, float dmax, float eps, float* dk_out,
+                             float* dbeta, float* dret, float* dd0, void* workspace,
+                             size_t workspace_bytes, dp_stream stream) {
+  return precond_bwd_entry(2, k, beta, r, d0, dkt, dd_final, flags, B, H, L, dk, eta, dmin, dmax, eps,
+                           dk_out, dbeta, dret, dd0, workspace, workspace_bytes, stream);
+}
+
+int dp_osdn_bwd_workspace_size(int B, int H, int L, int dk, int dv, size_t* bytes) {
+  if (bytes == nullptr) return DP_EINVAL;
+  const Shape s{1, B, H, L, dk, dv, dp::kBwdChunk};
+  const int rc = check_shape(s);
+  if (rc != DP_OK) return rc;
+  *bytes = osdn_bwd_ws(B, H, L, dk, dv).total;
+  return DP_OK;
+}
+
+int dp_osdn_bwd_f32(const float* q, const float* k, const float* v, const float* beta, const float* g,
+                    const float* h0, const float* r, const float* d0, const float* dout,
+                    const float* dfinal, const float* dd_final, int flags, int B, int H, int L, int dk,
+                    int dv, float eta, float dmin, float dmax, float eps, float* dq, float* dk_out,
+                    float* dv_out, float* dbeta, float* dg, float* dh0, float* dret, float* dd0,
+                    void* workspace, size_t workspace_bytes, dp_stream stream) {
+  return osdn_bwd_impl(4, q, k, v, beta, g, h0, r, d0, dout, dfinal, dd_final, flags, B, H, L, dk, dv, eta,
+                       dmin, dmax, eps, dq, dk_out, dv_out, dbeta, dg, dh0, dret, dd0, workspace,
+                       workspace_bytes, stream);
+}
+
+int dp_osdn_bwd_bf16(const void* q, const void* k, const void* v, const float* beta, const float* g,
+                     const float* h0, const float* r, const float* d0, const void* dout,
+                     const float* dfinal, const float* dd_final, int flags, int B, int H, int L, int dk,
+                     int dv, float eta, float dmin, float dmax, float eps, float* dq, float* dk_out,
+                     float* dv_out, float* dbeta, float* dg, float* dh0, float* dret, float* dd0,
+                     void* workspace, size_t workspace_bytes, dp_stream stream) {
+  return osdn_bwd_impl(2, q, k, v, beta, g, h0, r, d0, dout, dfinal, dd_final, flags, B, H, L, dk, dv, eta,
+                       dmin, dmax, eps, dq, dk_out, dv_out, dbeta, dg, dh0, dret, dd0, workspace,
+                       workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -28,6 +28,14 @@
 //   dp_bwd_chunk_kernel    one workgroup per chunk, all in parallel: dq, dk,
 //                          dv, dbeta, dg from H0, dH1, dUp and the chunk
 // All arithmetic is fp32 (fp32 MFMA, 16x16x4), whatever the input type.
+//
+// ASYM: write keys W given apart from the read keys (the OSDN write-key
+// forward, sec. 2.5 phase 2): M = strict_tril(diag(beta)(E o K W^T)), the
+// state update and the readout scores use W, X and the state read use K.
+// The formulas above then split the key gradient in two:
+//   dK = -diag(e^G) dX H0^T + Z W                         (read keys)
+//   dW = diag(e^{G_C - G}) Up dH1^T + Gm^T Q + Z^T K       (write keys, as given)
+// with S = K W^T in the beta and gate terms and Q W^T in the scores.
 #pragma once
 
 #include "dp_kernels.hpp"
@@ -44,6 +52,8 @@ struct BwdArgs {
   const float* beta;
   const float* g;       // nullptr: no gate
   const float* h0;      // nullptr: zero initial state
+  const void* kt;       // ASYM: [B, L, H, n_h, dk] write keys, input type
+  float* dkt;           // ASYM: [B, L, H, n_h, dk] their gradient
   const void* dout;     // [B, L, H, dv], input type
   const float* dfinal;  // [B, H, dk, dv] or nullptr (zero)
   const float* wsT;     // [B*H*nc][C][C] T (fp32)
@@ -167,12 +177,13 @@ __device__ __forceinline__ void bwd_readout(const BwdArgs& p, int b, int h, int 
 // The operands every sequential kernel needs per chunk: the thread's slice of
 // the unit keys (with 1/|k| of its row), its four entries of T, and for
 // threads t < C the scalars of sub-step t (beta, G, G of the chunk's last).
-template <typename T, int DK, int C>
+template <typename T, int DK, int C, bool ASYM = false>
 struct BwdChunkCommon {
   static constexpr int TPR = 256 / C;  // threads per sub-step row
   static constexpr int EK = DK / TPR;  // key elements per thread
   static_assert(C * C == 4 * 256 && EK >= 1 && DK % TPR == 0, "32-sub-step chunks, 256 threads");
   RawSlice<T, EK> k;
+  RawSlice<T, ASYM ? EK : 1> w;  // ASYM: the write-key slice of the same row
   float rinv;  // 1/|k| of the key row (0 past the end)
   float4 t;    // T entries 4 tid .. 4 tid + 3
   float beta, g, gl;
@@ -181,9 +192,11 @@ struct BwdChunkCommon {
     const long long row = bwd_row(p, b, h, c * C + tid / TPR);
     if (row >= 0) {
       k.load(static_cast<const T*>(p.k) + row * DK + (tid % TPR) * EK);
+      if constexpr (ASYM) w.load(static_cast<const T*>(p.kt) + row * DK + (tid % TPR) * EK);
       rinv = p.wsS[chunk * C + tid / TPR].x;
     } else {
       k.zero();
+      if constexpr (ASYM) w.zero();
       rinv = 0.f;
     }
     t = *reinterpret_cast<const float4*>(p.wsT + chunk * C * C + 4 * tid);
@@ -195,11 +208,16 @@ struct BwdChunkCommon {
     }
   }
   template <int LDK, int LDC>
-  __device__ __forceinline__ void commit(float* sK, float* sT) const {
+  __device__ __forceinline__ void commit(float* sK, float* sT, float* sW = nullptr) const {
     const int tid = threadIdx.x;
     float* kd = sK + (tid / TPR) * LDK + (tid % TPR) * EK;
 #pragma unroll
     for (int i = 0; i < EK; ++i) kd[i] = k[i] * rinv;
+    if constexpr (ASYM) {
+      float* wd = sW + (tid / TPR) * LDK + (tid % TPR) * EK;
+#pragma unroll
+      for (int i = 0; i < EK; ++i) wd[i] = w[i];
+    }
     float* td = sT + ((4 * tid) / C) * LDC + (4 * tid) % C;
     td[0] = t.x;
     td[1] = t.y;
@@ -212,14 +230,16 @@ struct BwdChunkCommon {
 // dp_bwd_states_kernel: the forward's chunk-start states, one workgroup per
 // (head, block of BV value columns), sequential over the chunks.  The state
 // lives in LDS (fp32); each wavefront updates the tiles it owns.
-template <typename T, int DK, int C, int BV>
+template <typename T, int DK, int C, int BV, bool ASYM = false>
 __global__ __launch_bounds__(256) void dp_bwd_states_kernel(BwdArgs p) {
   constexpr int LDK = DK + 4, LDC = C + 4, LDB = BV + 4;
   constexpr int NCT = C / 16, NDT = DK / 16, NVT = BV / 16;
-  using Common = BwdChunkCommon<T, DK, C>;
+  using Common = BwdChunkCommon<T, DK, C, ASYM>;
   constexpr int TPR = Common::TPR, EV = BV / TPR;
   static_assert(EV >= 1 && BV % TPR == 0, "value slice");
   __shared__ float sK[C * LDK], sT[C * LDC], sH[DK * LDB], sXb[C * LDB], sU[C * LDB], sV[C * LDB];
+  __shared__ float sW[ASYM ? C * LDK : 1];  // ASYM: write keys
+  float* const sKw = ASYM ? sW : sK;        // the keys the state update writes with
   __shared__ float sB[C], sEG[C], sEL[C];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -255,7 +275,7 @@ __global__ __launch_bounds__(256) void dp_bwd_states_kernel(BwdArgs p) {
   auto body = [&](Next& nx, int c) {
     const long long chunk = (long long)bh * p.nc + c;
     __syncthreads();  // the previous chunk is done with every buffer
-    nx.x.template commit<LDK, LDC>(sK, sT);
+    nx.x.template commit<LDK, LDC>(sK, sT, sW);
     {
       float* vd = sV + (tid / TPR) * LDB + (tid % TPR) * EV;
 #pragma unroll
@@ -298,14 +318,14 @@ __global__ __launch_bounds__(256) void dp_bwd_states_kernel(BwdArgs p) {
       }
     }
     __syncthreads();
-    // H = e^{G_C} H + K^T (diag(e^{G_C - G}) Up): each wavefront its own tiles
+    // H = e^{G_C} H + W^T (diag(e^{G_C - G}) Up): each wavefront its own tiles
     const float egl = sEG[C - 1];
     for (int tile = wave; tile < NDT * NVT; tile += 4) {
       const int dt = tile / NVT, nt = tile % NVT;
       f32x4_t acc;
 #pragma unroll
       for (int e = 0; e < 4; ++e) acc[e] = egl * sH[(dt * 16 + 4 * grp + e) * LDB + nt * 16 + col];
-      acc = mm_tile_tt<C>(acc, sK, LDK, dt * 16, sU, LDB, nt * 16);
+      acc = mm_tile_tt<C>(acc, sKw, LDK, dt * 16, sU, LDB, nt * 16);
 #pragma unroll
       for (int e = 0; e < 4; ++e) sH[(dt * 16 + 4 * grp + e) * LDB + nt * 16 + col] = acc[e];
     }
@@ -321,18 +341,46 @@ __global__ __launch_bounds__(256) void dp_bwd_states_kernel(BwdArgs p) {
 // workgroup per (head, block of BV value columns), chunks last to first.
 // Writes dH1 (the gradient of each chunk's end state) and dUp per chunk, and
 // the gradient of the initial state.
-template <typename T, int DK, int C, int BV, int NRT>
+// LDS of dp_bwd_dstate_kernel (dynamic: with the write keys it passes 64 KB)
+template <int DK, int C, int BV, int RT, bool ASYM>
+__host__ __device__ constexpr int bwd_dstate_lds_floats() {
+  return (ASYM ? 2 : 1) * C * (DK + 4) + RT * (DK + 4) + C * (C + 4) + RT * (C + 4) + DK * (BV + 4) +
+         2 * RT * (BV + 4) + 2 * C * (BV + 4) + 4 * C;
+}
+template <int DK, int C, int BV, int RT, bool ASYM>
+__host__ __device__ constexpr int bwd_dstate_lds_bytes() {
+  return bwd_dstate_lds_floats<DK, C, BV, RT, ASYM>() * 4 + RT * 4;
+}
+
+template <typename T, int DK, int C, int BV, int NRT, bool ASYM = false>
 __global__ __launch_bounds__(256) void dp_bwd_dstate_kernel(BwdArgs p) {
   constexpr int RT = 16 * NRT;
   constexpr int LDK = DK + 4, LDC = C + 4, LDB = BV + 4;
   constexpr int NCT = C / 16, NDT = DK / 16, NVT = BV / 16;
-  using Common = BwdChunkCommon<T, DK, C>;
+  using Common = BwdChunkCommon<T, DK, C, ASYM>;
   constexpr int TPQ = 256 / RT, EQ = DK / TPQ, EO = BV / TPQ;  // per readout row
   static_assert(EQ >= 1 && EO >= 1 && DK % TPQ == 0 && BV % TPQ == 0, "readout slices");
-  __shared__ float sK[C * LDK], sQ[RT * LDK], sT[C * LDC], sP[RT * LDC];
-  __shared__ float sdH[DK * LDB], sdO[RT * LDB], sdOe[RT * LDB], sdUp[C * LDB], sdX[C * LDB];
-  __shared__ float sB[C], sG[C], sEG[C], sEL[C];
-  __shared__ int sLoc[RT];
+  extern __shared__ __align__(16) float smf[];
+  float* sK = smf;                     // C x LDK unit read keys
+  float* sW = sK + C * LDK;            // ASYM: C x LDK write keys
+  float* sQ = sW + (ASYM ? C * LDK : 0);
+  float* sT = sQ + RT * LDK;
+  float* sP = sT + C * LDC;
+  float* sdH = sP + RT * LDC;
+  float* sdO = sdH + DK * LDB;
+  float* sdOe = sdO + RT * LDB;
+  float* sdUp = sdOe + RT * LDB;
+  float* sdX = sdUp + C * LDB;
+  float* sB = sdX + C * LDB;
+  float* sG = sB + C;
+  float* sEG = sG + C;
+  float* sEL = sEG + C;
+  int* sLoc = reinterpret_cast<int*>(sEL + C);
+  static_assert(bwd_dstate_lds_floats<DK, C, BV, RT, ASYM>() ==
+                    (ASYM ? 2 : 1) * C * LDK + RT * LDK + C * LDC + RT * LDC + DK * LDB + 2 * RT * LDB +
+                        2 * C * LDB + 4 * C,
+                "LDS layout");
+  float* const sKw = ASYM ? sW : sK;  // the keys of the state update and the scores
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -377,7 +425,7 @@ __global__ __launch_bounds__(256) void dp_bwd_dstate_kernel(BwdArgs p) {
   auto body = [&](Next& nx, int c) {
     const long long chunk = (long long)bh * p.nc + c;
     __syncthreads();  // the previous chunk is done with every buffer
-    nx.x.template commit<LDK, LDC>(sK, sT);
+    nx.x.template commit<LDK, LDC>(sK, sT, sW);
     {
       const int rr = tid / TPQ, q0 = (tid % TPQ) * EQ, o0 = (tid % TPQ) * EO;
 #pragma unroll
@@ -408,7 +456,7 @@ __global__ __launch_bounds__(256) void dp_bwd_dstate_kernel(BwdArgs p) {
     for (int tile = wave; tile < NRT * NCT; tile += 4) {
       const int rt = tile / NCT, ct = tile % NCT;
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mm_tile<float, DK>(acc, sQ, LDK, rt * 16, sK, LDK, ct * 16);
+      acc = mm_tile<float, DK>(acc, sQ, LDK, rt * 16, sKw, LDK, ct * 16);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = rt * 16 + 4 * grp + e, j = ct * 16 + col;
@@ -417,11 +465,11 @@ __global__ __launch_bounds__(256) void dp_bwd_dstate_kernel(BwdArgs p) {
       }
     }
     __syncthreads();
-    // dUp = diag(e^{G_C - G}) K dH1 + P^T dO
+    // dUp = diag(e^{G_C - G}) W dH1 + P^T dO
     for (int tile = wave; tile < NCT * NVT; tile += 4) {
       const int ct = tile / NVT, nt = tile % NVT;
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
-      acc = mm_tile_tb<float, DK>(acc, sK, LDK, ct * 16, sdH, LDB, nt * 16);
+      acc = mm_tile_tb<float, DK>(acc, sKw, LDK, ct * 16, sdH, LDB, nt * 16);
       acc2 = mm_tile_tt<RT>(acc2, sP, LDC, ct * 16, sdO, LDB, nt * 16);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -485,17 +533,17 @@ __global__ __launch_bounds__(256) void dp_bwd_dstate_kernel(BwdArgs p) {
 //   dbeta_j = sum_i dTb_ij T_ij + sum_i' F_ji' e^{G_j - G_i'} S_ji'   (S = K K^T)
 //   dG    = the gate terms of each product, then dlog g = reverse cumsum of dG
 // and finally the key normalisation, the beta clamp and the log of the gate.
-template <int DK, int C, int RT>
+template <int DK, int C, int RT, bool ASYM = false>
 __host__ __device__ constexpr int bwd_chunk_lds_floats() {
-  return C * (DK + 4) + RT * (DK + 4) + 3 * C * (C + 4) + RT * (C + 4) + 2 * DK * 20 + 6 * C * 20 +
-         RT * 20 + 8 * C;
+  return (ASYM ? 2 : 1) * C * (DK + 4) + RT * (DK + 4) + 3 * C * (C + 4) + RT * (C + 4) + 2 * DK * 20 +
+         6 * C * 20 + RT * 20 + 8 * C;
 }
-template <int DK, int C, int RT>
+template <int DK, int C, int RT, bool ASYM = false>
 __host__ __device__ constexpr int bwd_chunk_lds_bytes() {
-  return bwd_chunk_lds_floats<DK, C, RT>() * 4 + C * 8 + RT * 12;
+  return bwd_chunk_lds_floats<DK, C, RT, ASYM>() * 4 + C * 8 + RT * 12;
 }
 
-template <typename T, int DK, int C, int NRT>
+template <typename T, int DK, int C, int NRT, bool ASYM = false>
 __global__ __launch_bounds__(256) void dp_bwd_chunk_kernel(BwdArgs p) {
   constexpr int BV = 16;
   constexpr int RT = 16 * NRT;
@@ -508,7 +556,8 @@ __global__ __launch_bounds__(256) void dp_bwd_chunk_kernel(BwdArgs p) {
 
   extern __shared__ __align__(16) float smf[];
   float* sK = smf;                   // C x LDK unit keys
-  float* sQ = sK + C * LDK;          // RT x LDK readout queries
+  float* sWk = sK + C * LDK;         // ASYM: C x LDK write keys
+  float* sQ = sWk + (ASYM ? C * LDK : 0);  // RT x LDK readout queries
   float* sT = sQ + RT * LDK;         // C x LDC  T
   float* sA = sT + C * LDC;          // C x LDC  dT, then Z
   float* sW = sA + C * LDC;          // C x LDC  T^T dT
@@ -533,9 +582,11 @@ __global__ __launch_bounds__(256) void dp_bwd_chunk_kernel(BwdArgs p) {
   long long* sRow = reinterpret_cast<long long*>(sRD + C);
   long long* sTok = sRow + C;
   int* sLoc = reinterpret_cast<int*>(sTok + RT);
-  static_assert(BV + 4 == 20 && bwd_chunk_lds_floats<DK, C, RT>() ==
-                    C * LDK + RT * LDK + 3 * C * LDC + RT * LDC + 2 * DK * LDB + 6 * C * LDB + RT * LDB + 8 * C,
+  static_assert(BV + 4 == 20 && bwd_chunk_lds_floats<DK, C, RT, ASYM>() ==
+                    (ASYM ? 2 : 1) * C * LDK + RT * LDK + 3 * C * LDC + RT * LDC + 2 * DK * LDB + 6 * C * LDB +
+                        RT * LDB + 8 * C,
                 "LDS layout");
+  float* const sKw = ASYM ? sWk : sK;  // the keys of M's right side, the state update and the scores
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -582,7 +633,7 @@ __global__ __launch_bounds__(256) void dp_bwd_chunk_kernel(BwdArgs p) {
       ndo.zero();
   };
   // the chunk's keys, T and readout queries, then value block 0, all issued up front
-  BwdChunkCommon<T, DK, C> cx;
+  BwdChunkCommon<T, DK, C, ASYM> cx;
   cx.load(p, b, h, c, chunk);
   constexpr int EQ = DK / TPQ;
   RawSlice<T, EQ> cq;
@@ -607,17 +658,17 @@ __global__ __launch_bounds__(256) void dp_bwd_chunk_kernel(BwdArgs p) {
     sEG[tid] = expf(sG[tid]);
     sEL[tid] = expf(sG[C - 1] - sG[tid]);
   }
-  cx.template commit<LDK, LDC>(sK, sT);
+  cx.template commit<LDK, LDC>(sK, sT, sWk);
 #pragma unroll
   for (int i = 0; i < EQ; ++i) sQ[orr * LDK + (tid % TPQ) * EQ + i] = cq[i];
   __syncthreads();
 
-  // S = K K^T (tile `wave`) and Q K^T (tile `wave` when < NRC), kept in registers
+  // S = K W^T (tile `wave`) and Q W^T (tile `wave` when < NRC), kept in registers (W = K when symmetric)
   const int cit = wave / NCT, cjt = wave % NCT;  // the C x C tile of this wavefront
   const int rrt = wave / NCT, rct = wave % NCT;  // the RT x C tile of this wavefront
   f32x4_t accS = {0.f, 0.f, 0.f, 0.f}, accQK = {0.f, 0.f, 0.f, 0.f};
-  if (wave < NCC) accS = mm_tile<float, DK>(accS, sK, LDK, cit * 16, sK, LDK, cjt * 16);
-  if (wave < NRC) accQK = mm_tile<float, DK>(accQK, sQ, LDK, rrt * 16, sK, LDK, rct * 16);
+  if (wave < NCC) accS = mm_tile<float, DK>(accS, sK, LDK, cit * 16, sKw, LDK, cjt * 16);
+  if (wave < NRC) accQK = mm_tile<float, DK>(accQK, sQ, LDK, rrt * 16, sKw, LDK, rct * 16);
 
   f32x4_t aXH[KPW], aY[KPW], aA[QPW];
   f32x4_t aP = {0.f, 0.f, 0.f, 0.f}, aTb = {0.f, 0.f, 0.f, 0.f};
@@ -776,7 +827,7 @@ __global__ __launch_bounds__(256) void dp_bwd_chunk_kernel(BwdArgs p) {
     if (grp == 0) atomicAdd(&sDG[j], -csum);
   }
   __syncthreads();
-  // dq = diag(e^{G_l}) A + Gm K;  dG_l += e^{G_l} q_r . A_r
+  // dq = diag(e^{G_l}) A + Gm W;  dG_l += e^{G_l} q_r . A_r
   float* dqp = p.dq;
 #pragma unroll
   for (int u = 0; u < QPW; ++u) {
@@ -784,7 +835,7 @@ __global__ __launch_bounds__(256) void dp_bwd_chunk_kernel(BwdArgs p) {
     if (tile < NQD) {
       const int rt = tile / NDT, dt = tile % NDT;
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mm_tile_tb<float, C>(acc, sGm, LDC, rt * 16, sK, LDK, dt * 16);
+      acc = mm_tile_tb<float, C>(acc, sGm, LDC, rt * 16, sKw, LDK, dt * 16);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = rt * 16 + 4 * grp + e, d = dt * 16 + col;
@@ -799,7 +850,9 @@ __global__ __launch_bounds__(256) void dp_bwd_chunk_kernel(BwdArgs p) {
       }
     }
   }
-  // dkn = -diag(e^G) dXH + diag(e^{G_C - G}) Y + Gm^T Q + Z K + Z^T K, and its gate terms
+  // dkn = -diag(e^G) dXH + diag(e^{G_C - G}) Y + Gm^T Q + Z K + Z^T K, and its gate terms;
+  // ASYM: dkn = -diag(e^G) dXH + Z W (read keys), and the write keys' gradient
+  // diag(e^{G_C - G}) Y + Gm^T Q + Z^T K goes out as it is
   f32x4_t dkn[KPW];
   float glast = 0.f;
 #pragma unroll
@@ -809,22 +862,46 @@ __global__ __launch_bounds__(256) void dp_bwd_chunk_kernel(BwdArgs p) {
     if (tile < NKD) {
       const int ct = tile / NDT, dt = tile % NDT;
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mm_tile_tt<RT>(acc, sGm, LDC, ct * 16, sQ, LDK, dt * 16);
-      acc = mm_tile_tb<float, C>(acc, sA, LDC, ct * 16, sK, LDK, dt * 16);
-      acc = mm_tile_tt<C>(acc, sA, LDC, ct * 16, sK, LDK, dt * 16);
+      if constexpr (ASYM) {
+        f32x4_t accw = {0.f, 0.f, 0.f, 0.f};
+        accw = mm_tile_tt<RT>(accw, sGm, LDC, ct * 16, sQ, LDK, dt * 16);
+        accw = mm_tile_tt<C>(accw, sA, LDC, ct * 16, sK, LDK, dt * 16);
+        acc = mm_tile_tb<float, C>(acc, sA, LDC, ct * 16, sWk, LDK, dt * 16);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = ct * 16 + 4 * grp + e, d = dt * 16 + col;
-        const float kv = sK[j * LDK + d];
-        const float xh = aXH[u][e], y = aY[u][e];
-        const float dk = acc[e] - sEG[j] * xh + sEL[j] * y;
-        dkn[u][e] = dk;
-        const float gj = sum16(-sEG[j] * kv * xh - sEL[j] * kv * y);
-        const float rd = sum16(kv * dk);
-        glast = fmaf(sEL[j], kv * y, glast);
-        if (col == 0) {
-          atomicAdd(&sDG[j], gj);
-          atomicAdd(&sRD[j], rd);
+        for (int e = 0; e < 4; ++e) {
+          const int j = ct * 16 + 4 * grp + e, d = dt * 16 + col;
+          const float kv = sK[j * LDK + d], wv = sWk[j * LDK + d];
+          const float xh = aXH[u][e], y = aY[u][e];
+          const float dk = acc[e] - sEG[j] * xh;
+          dkn[u][e] = dk;
+          const long long rw = sRow[j];
+          if (rw >= 0) p.dkt[rw * DK + d] = accw[e] + sEL[j] * y;
+          const float gj = sum16(-sEG[j] * kv * xh - sEL[j] * wv * y);
+          const float rd = sum16(kv * dk);
+          glast = fmaf(sEL[j], wv * y, glast);
+          if (col == 0) {
+            atomicAdd(&sDG[j], gj);
+            atomicAdd(&sRD[j], rd);
+          }
+        }
+      } else {
+        acc = mm_tile_tt<RT>(acc, sGm, LDC, ct * 16, sQ, LDK, dt * 16);
+        acc = mm_tile_tb<float, C>(acc, sA, LDC, ct * 16, sK, LDK, dt * 16);
+        acc = mm_tile_tt<C>(acc, sA, LDC, ct * 16, sK, LDK, dt * 16);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = ct * 16 + 4 * grp + e, d = dt * 16 + col;
+          const float kv = sK[j * LDK + d];
+          const float xh = aXH[u][e], y = aY[u][e];
+          const float dk = acc[e] - sEG[j] * xh + sEL[j] * y;
+          dkn[u][e] = dk;
+          const float gj = sum16(-sEG[j] * kv * xh - sEL[j] * kv * y);
+          const float rd = sum16(kv * dk);
+          glast = fmaf(sEL[j], kv * y, glast);
+          if (col == 0) {
+            atomicAdd(&sDG[j], gj);
+            atomicAdd(&sRD[j], rd);
+          }
         }
       }
     }
@@ -877,46 +954,255 @@ __global__ __launch_bounds__(256) void dp_bwd_chunk_kernel(BwdArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// Host-side launch of the four kernels.
+// dp_precond_bwd_kernel: gradient of OSDN phase 1 (OSDN study notes sec. 2.5,
+// closing paragraph: the write key kt_t = d_t o kh_t passes its gradient into
+// d_t and k_t, and the gradient of d runs back through the recursion of
+// sec. 2.4, with the retention of sec. 2.6 and the beta-free step of
+// sec. 2.7).  Per token, with s = kh o kh, n = sum s, nb = max(n, eps),
+// a = bu <d, s>, coef = eta bu (1 - a) / nb, x = r d + coef s and the
+// gradient gd' on d_{t+1}:
+//   gx  = gd' where dmin <= x <= dmax (else 0)
+//   gd  = r gx - (eta bu^2 / nb) <gx, s> s + kh o gkt
+//   gr  = <gx, d>,   gbu = <gx, s> eta (1 - 2a) / nb
+//   gs  = coef gx + <gx, s> (-(eta bu^2 / nb) d - [n > eps] coef / nb)
+//   gkh = 2 kh o gs + d o gkt,  then the normalisation kh = k / max(|k|, 1e-6)
+// The lane layout is the forward's (LPH lanes per head, EPL coordinates per
+// lane); tokens run last to first in blocks of PB.  Everything but gd is
+// formed for a whole block first (three head sums per token, off the
+// dependent chain); the chain itself is gx, <gx, s>, gd: one head sum per
+// token, as in the forward.  d_t comes from the trajectory the forward kernel
+// stored.  dk and dbeta are accumulated into (they already hold the write-key
+// forward's gradients), dret and dd0 written.
+struct PrecondBwdArgs {
+  const void* k;          // [B, L, H, dk] raw keys
+  const float* beta;      // [B, L, H]
+  const float* ret;       // [B, L, H] or nullptr
+  const float* dtr;       // [B, L, H, dk] d_t of every token
+  const float* dkt;       // [B, L, H, dk] gradient on the write keys
+  const float* dd_final;  // [B, H, dk] or nullptr (zero)
+  float* dk;              // [B, L, H, dk], accumulated into
+  float* dbeta;           // [B, L, H], accumulated into
+  float* dret;            // [B, L, H] or nullptr
+  float* dd0;             // [B, H, dk] or nullptr
+  int B, H, L, beta_aware;
+  float eta, dmin, dmax, eps;
+};
+
 template <typename T, int DK>
-hipError_t launch_bwd_dk(const FwdArgs& fa, const BwdArgs& a, hipStream_t st) {
+__global__ __launch_bounds__(64) void dp_precond_bwd_kernel(PrecondBwdArgs p) {
+  constexpr int LPH = DK < 64 ? DK : 64;  // lanes per head
+  constexpr int EPL = DK / LPH;           // coordinates per lane (1 or 2)
+  constexpr int HPW = 64 / LPH;           // heads per wavefront
+  constexpr int PB = 8;                   // tokens per block
+  static_assert(EPL == 1 || EPL == 2, "coordinates per lane");
+  const int lane = threadIdx.x & 63;
+  const int sl = lane % LPH;
+  const long long nbh = (long long)p.B * p.H;
+  const long long bh_raw = (long long)blockIdx.x * HPW + lane / LPH;
+  const bool active = bh_raw < nbh;
+  const long long bh = active ? bh_raw : 0;
+  const int b = (int)(bh / p.H), h = (int)(bh % p.H);
+  const long long row0 = (long long)b * p.L * p.H + h;  // token t: row row0 + t H
+  const long long kstride = (long long)p.H * DK;
+  const T* kp = static_cast<const T*>(p.k) + row0 * DK + sl * EPL;
+  const float* dtp = p.dtr + row0 * DK + sl * EPL;
+  const float* gkp = p.dkt + row0 * DK + sl * EPL;
+  float* dkp = p.dk + row0 * DK + sl * EPL;
+
+  float gd[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) gd[e] = p.dd_final != nullptr ? p.dd_final[bh * DK + sl * EPL + e] : 0.f;
+
+  // one block's inputs, and the values dk and dbeta already hold (the adds
+  // below then store without waiting on a read)
+  struct Blk {
+    T k[PB][EPL];
+    float d[PB][EPL], gk[PB][EPL], dk0[PB][EPL], beta[PB], ret[PB], db0[PB];
+  };
+  auto load = [&](int t0, Blk& r) {
+#pragma unroll
+    for (int i = 0; i < PB; ++i) {
+      const int t = t0 + i;
+      if (t < p.L) {
+        __builtin_memcpy(r.k[i], __builtin_assume_aligned(kp + t * kstride, EPL * sizeof(T)), EPL * sizeof(T));
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          r.d[i][e] = dtp[t * kstride + e];
+          r.gk[i][e] = gkp[t * kstride + e];
+          r.dk0[i][e] = dkp[t * kstride + e];
+        }
+        r.beta[i] = p.beta[row0 + (long long)t * p.H];
+        r.ret[i] = p.ret != nullptr ? p.ret[row0 + (long long)t * p.H] : 1.f;
+        r.db0[i] = p.dbeta[row0 + (long long)t * p.H];
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          r.k[i][e] = T{};
+          r.d[i][e] = 0.f;
+          r.gk[i][e] = 0.f;
+          r.dk0[i][e] = 0.f;
+        }
+        r.beta[i] = 0.f;
+        r.ret[i] = 1.f;
+        r.db0[i] = 0.f;
+      }
+    }
+  };
+  auto run_block = [&](const Blk& c, int t0) {
+    // the parts that do not depend on the incoming gradient
+    float kh[PB][EPL], sq[PB][EPL], msk[PB][EPL], rinv[PB], c2[PB], coef[PB], fb[PB], cn[PB];
+    bool tiny[PB];
+#pragma unroll
+    for (int i = 0; i < PB; ++i) {
+      float n2 = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) n2 = fmaf(to_f32(c.k[i][e]), to_f32(c.k[i][e]), n2);
+      n2 = head_sum<LPH>(n2);
+      rinv[i] = __builtin_amdgcn_rsqf(fmaxf(n2, 1e-12f));  // 1 / max(|k|, 1e-6)
+      tiny[i] = !(n2 > 1e-12f);
+      float ns = 0.f, ds = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        kh[i][e] = to_f32(c.k[i][e]) * rinv[i];
+        sq[i][e] = kh[i][e] * kh[i][e];
+        ns += sq[i][e];
+        ds = fmaf(c.d[i][e], sq[i][e], ds);
+      }
+      ns = head_sum<LPH>(ns);
+      ds = head_sum<LPH>(ds);
+      const float bu = p.beta_aware ? clamp_keep_nan(c.beta[i], 0.f, 2.f) : 1.f;
+      const float a = bu * ds;
+      const float rn = 1.f / fmaxf(ns, p.eps);
+      coef[i] = p.eta * bu * (1.f - a) * rn;
+      c2[i] = p.eta * bu * bu * rn;
+      fb[i] = p.eta * (1.f - 2.f * a) * rn;
+      cn[i] = ns > p.eps ? coef[i] * rn : 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const float x = fmaf(coef[i], sq[i][e], c.ret[i] * c.d[i][e]);
+        msk[i][e] = (x >= p.dmin && x <= p.dmax) ? 1.f : 0.f;
+      }
+    }
+    // the dependent chain, last token first, with each token's outputs
+#pragma unroll
+    for (int i = PB - 1; i >= 0; --i) {
+      const int t = t0 + i;
+      if (t < p.L) {
+        float gx[EPL], gxs = 0.f, gr = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          gx[e] = msk[i][e] * gd[e];
+          gxs = fmaf(gx[e], sq[i][e], gxs);
+          gr = fmaf(gx[e], c.d[i][e], gr);
+        }
+        gxs = head_sum<LPH>(gxs);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e)
+          gd[e] = fmaf(c.ret[i], gx[e], fmaf(-c2[i] * gxs, sq[i][e], kh[i][e] * c.gk[i][e]));
+        // off the chain: the key, beta and retention gradients of token t
+        float gkh[EPL], pp = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          const float gs = fmaf(coef[i], gx[e], gxs * fmaf(-c2[i], c.d[i][e], -cn[i]));
+          gkh[e] = fmaf(2.f * kh[i][e], gs, c.d[i][e] * c.gk[i][e]);
+          pp = fmaf(kh[i][e], gkh[e], pp);
+        }
+        pp = head_sum<LPH>(pp);
+        if (p.dret != nullptr) gr = head_sum<LPH>(gr);
+        if (active) {
+          const long long rw = row0 + (long long)t * p.H;
+          const float proj = tiny[i] ? 0.f : pp;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) dkp[t * kstride + e] = c.dk0[i][e] + (gkh[e] - kh[i][e] * proj) * rinv[i];
+          if (sl == 0) {
+            const float braw = c.beta[i];
+            if (p.beta_aware && braw >= 0.f && braw <= 2.f) p.dbeta[rw] = c.db0[i] + gxs * fb[i];
+            if (p.dret != nullptr) p.dret[rw] = p.ret != nullptr ? gr : 0.f;
+          }
+        }
+      }
+    }
+  };
+  const int nblk = (p.L + PB - 1) / PB;
+  Blk cur, nxt;
+  if (nblk > 0) load((nblk - 1) * PB, cur);
+  for (int blk = nblk - 1; blk >= 0; --blk) {
+    if (blk > 0) load((blk - 1) * PB, nxt);  // lands while this block runs
+    run_block(cur, blk * PB);
+    cur = nxt;
+  }
+  if (active && p.dd0 != nullptr) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) p.dd0[bh * DK + sl * EPL + e] = gd[e];
+  }
+}
+
+template <typename T, int DK>
+hipError_t launch_precond_bwd_dk(const PrecondBwdArgs& a, hipStream_t st) {
+  const long long nbh = (long long)a.B * a.H;
+  constexpr int HPW = 64 / (DK < 64 ? DK : 64);  // heads per wavefront
+  const unsigned blocks = (unsigned)((nbh + HPW - 1) / HPW);
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((dp_precond_bwd_kernel<T, DK>), dim3(blocks), dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launch of the four kernels.
+template <typename T, int DK, bool ASYM>
+hipError_t launch_bwd_form(const FwdArgs& fa, const BwdArgs& a, hipStream_t st) {
   constexpr int C = kBwdChunk, BV = kBwdBV;
   const long long nchunks = (long long)a.B * a.H * a.nc;
   if (nchunks > 0) {
-    const int lds = ut_lds_bytes((int)sizeof(T), DK, C, 0);
+    const int lds = ut_lds_bytes((int)sizeof(T), DK, C, ASYM);
     static const bool attr = allow_big_lds(reinterpret_cast<const void*>(&dp_ut_kernel<T, DK, C, float, false>));
     (void)attr;
     hipLaunchKernelGGL((dp_ut_kernel<T, DK, C, float, false>), dim3((unsigned)nchunks), dim3(kThreads), lds, st, fa);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((dp_bwd_states_kernel<T, DK, C, BV>), dim3((unsigned)(a.B * a.H * a.nvb)), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((dp_bwd_states_kernel<T, DK, C, BV, ASYM>), dim3((unsigned)(a.B * a.H * a.nvb)), dim3(256), 0,
+                       st, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const unsigned nwg = (unsigned)(a.B * a.H * a.nvb);
   if (nwg > 0) {
-    if (a.RT == 16)
-      hipLaunchKernelGGL((dp_bwd_dstate_kernel<T, DK, C, BV, 1>), dim3(nwg), dim3(256), 0, st, a);
-    else
-      hipLaunchKernelGGL((dp_bwd_dstate_kernel<T, DK, C, BV, 2>), dim3(nwg), dim3(256), 0, st, a);
+    if (a.RT == 16) {
+      static const bool attr =
+          allow_big_lds(reinterpret_cast<const void*>(&dp_bwd_dstate_kernel<T, DK, C, BV, 1, ASYM>));
+      (void)attr;
+      constexpr int lds = bwd_dstate_lds_bytes<DK, C, BV, 16, ASYM>();
+      hipLaunchKernelGGL((dp_bwd_dstate_kernel<T, DK, C, BV, 1, ASYM>), dim3(nwg), dim3(256), lds, st, a);
+    } else {
+      static const bool attr =
+          allow_big_lds(reinterpret_cast<const void*>(&dp_bwd_dstate_kernel<T, DK, C, BV, 2, ASYM>));
+      (void)attr;
+      constexpr int lds = bwd_dstate_lds_bytes<DK, C, BV, 32, ASYM>();
+      hipLaunchKernelGGL((dp_bwd_dstate_kernel<T, DK, C, BV, 2, ASYM>), dim3(nwg), dim3(256), lds, st, a);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (nchunks > 0) {
     if (a.RT == 16) {
-      static const bool attr = allow_big_lds(reinterpret_cast<const void*>(&dp_bwd_chunk_kernel<T, DK, C, 1>));
+      static const bool attr = allow_big_lds(reinterpret_cast<const void*>(&dp_bwd_chunk_kernel<T, DK, C, 1, ASYM>));
       (void)attr;
-      constexpr int lds = bwd_chunk_lds_bytes<DK, C, 16>();
-      hipLaunchKernelGGL((dp_bwd_chunk_kernel<T, DK, C, 1>), dim3((unsigned)nchunks), dim3(256), lds, st, a);
+      constexpr int lds = bwd_chunk_lds_bytes<DK, C, 16, ASYM>();
+      hipLaunchKernelGGL((dp_bwd_chunk_kernel<T, DK, C, 1, ASYM>), dim3((unsigned)nchunks), dim3(256), lds, st, a);
     } else {
-      static const bool attr = allow_big_lds(reinterpret_cast<const void*>(&dp_bwd_chunk_kernel<T, DK, C, 2>));
+      static const bool attr = allow_big_lds(reinterpret_cast<const void*>(&dp_bwd_chunk_kernel<T, DK, C, 2, ASYM>));
       (void)attr;
-      constexpr int lds = bwd_chunk_lds_bytes<DK, C, 32>();
-      hipLaunchKernelGGL((dp_bwd_chunk_kernel<T, DK, C, 2>), dim3((unsigned)nchunks), dim3(256), lds, st, a);
+      constexpr int lds = bwd_chunk_lds_bytes<DK, C, 32, ASYM>();
+      hipLaunchKernelGGL((dp_bwd_chunk_kernel<T, DK, C, 2, ASYM>), dim3((unsigned)nchunks), dim3(256), lds, st, a);
     }
     return hipGetLastError();
   }
   return hipSuccess;
+}
+
+template <typename T, int DK>
+hipError_t launch_bwd_dk(const FwdArgs& fa, const BwdArgs& a, hipStream_t st) {
+  return a.kt != nullptr ? launch_bwd_form<T, DK, true>(fa, a, st) : launch_bwd_form<T, DK, false>(fa, a, st);
 }
 
 }  // namespace dp
@@ -924,6 +1210,10 @@ hipError_t launch_bwd_dk(const FwdArgs& fa, const BwdArgs& a, hipStream_t st) {
 #define DP_DEFINE_BWD_LAUNCHER(T, TNAME, DK)                                                     \
   hipError_t dp_launch_bwd_##TNAME##_##DK(const dp::FwdArgs& fa, const dp::BwdArgs& a, hipStream_t st) { \
     return dp::launch_bwd_dk<T, DK>(fa, a, st);                                                  \
+  }                                                                                              \
+  hipError_t dp_launch_precond_bwd_##TNAME##_##DK(const dp::PrecondBwdArgs& a, hipStream_t st) {  \
+    return dp::launch_precond_bwd_dk<T, DK>(a, st);                                              \
   }
-#define DP_DECLARE_BWD_LAUNCHER(TNAME, DK) \
-  hipError_t dp_launch_bwd_##TNAME##_##DK(const dp::FwdArgs& fa, const dp::BwdArgs& a, hipStream_t st);
+#define DP_DECLARE_BWD_LAUNCHER(TNAME, DK)                                                                 \
+  hipError_t dp_launch_bwd_##TNAME##_##DK(const dp::FwdArgs& fa, const dp::BwdArgs& a, hipStream_t st); \
+  hipError_t dp_launch_precond_bwd_##TNAME##_##DK(const dp::PrecondBwdArgs& a, hipStream_t st);

@@ -86,6 +86,12 @@ __device__ __forceinline__ void unpack16(const u32x4_t& v, float* f, bf16_t /*ta
     f[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
   }
 }
+__device__ __forceinline__ void unpack16(const u32x4_t& v, float* f, f16_t /*tag*/) {
+  f16x8_t h;
+  __builtin_memcpy(&h, &v, 16);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = (float)h[i];
+}
 
 __device__ __forceinline__ u32x4_t ld16(const void* p) {
   return *reinterpret_cast<const u32x4_t*>(p);
@@ -104,6 +110,14 @@ __device__ __forceinline__ void st_vec16(f16_t* p, const float* f) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) v[i] = (f16_t)f[i];
   *reinterpret_cast<f16x8_t*>(p) = v;
+}
+
+__device__ __forceinline__ void st_vec16(bf16_t* p, const float* f) {
+  u32x4_t v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    v[i] = (uint32_t)from_f32<bf16_t>(f[2 * i]) | ((uint32_t)from_f32<bf16_t>(f[2 * i + 1]) << 16);
+  *reinterpret_cast<u32x4_t*>(p) = v;
 }
 
 // Store 4 consecutive elements (fp32 inputs) as T at p.

@@ -100,6 +100,14 @@ struct FwdArgs {
   // the UT kernel also writes each chunk's readout scores to wsP (RT x C)
   const float* ga = nullptr;
   void* wsP = nullptr;
+  // per-channel gate: operands the UT kernel writes for the scan, in the
+  // input layouts and type: read keys e^G o kn and write keys e^{G_C - G} o w
+  // ([B, L, H, n_h, dk]), readout queries e^{G_loc} o q ([B, L, H, dk]), and
+  // the chunk's state decay e^{G_C} ([B*H*nc][dk] fp32)
+  void* wsKg = nullptr;
+  void* wsKtg = nullptr;
+  void* wsQg = nullptr;
+  float* wsDec = nullptr;
   // dp_scan_kernel LDS byte offsets (oDec: the per-channel state decay, dk floats)
   int oK, oKt, oQ, oT, oHt, oXt, oUo, oUs, oP, oV, oG, oEG, oEL, oLoc, oRow, oTok, oDec;
 };
@@ -120,6 +128,8 @@ struct PrecondArgs {
   int beta_aware;    // 0: the beta-free phase-1 step
   float eta, dmin, dmax, eps;
   int Ls = 0, t0 = 0;  // a call on tokens t0 .. t0 + L - 1 of Ls-token sequences (0: Ls = L)
+  float* dtr = nullptr;  // [B, L, H, dk] fp32: d_t of every token (before its update), or nullptr
+  int d_ones = 0;        // 1: the scan starts from d = 1 (p.d is then written only)
 };
 
 __host__ __device__ constexpr int align16(int x) { return (x + 15) & ~15; }
@@ -182,7 +192,10 @@ __host__ __device__ constexpr int ut_lds_bytes(int elem, int DK, int C, int asym
 //   P_rj = sum_c q_r[c] w_j[c] e^{G_loc(r)[c] - G_j[c]}             (j <= loc(r))
 // Every factor is e^{G_a - G_b} with a >= b, at most 1: each entry is summed
 // pair by pair with its own factors, so no scaling can overflow however fast a
-// channel decays.  The scores go to wsP for the scan.
+// channel decays.  The scores go to wsP for the scan, and with them the
+// operands the scan then uses as they are (each factor again at most 1): the
+// read keys e^{G_s} o kn_s (wsKg), the write keys e^{G_C - G_s} o w_s
+// (wsKtg), the readout queries e^{G_loc} o q (wsQg) and e^{G_C} (wsDec).
 template <typename T, int DK, int C, typename WT = typename OpType<T>::type, bool TB = true, bool CG = false>
 __global__ __launch_bounds__(kThreads) void dp_ut_kernel(FwdArgs p) {
   using OT = WT;
@@ -272,28 +285,39 @@ __global__ __launch_bounds__(kThreads) void dp_ut_kernel(FwdArgs p) {
     }
   }
   if constexpr (CG) {
-    // cumulative log-gate of each key channel over the chunk's sub-steps: the
-    // gates act at a token's first sub-step (log alpha_t + log g_t there, 0 on
-    // the others and past the end)
+    // log-gate of each (sub-step, key channel) of the chunk, all threads at
+    // once: log alpha_t + log g_t at a token's first sub-step, 0 on the others
+    // and past the end (the loads are unconditional, at a valid address, so
+    // that they are all in flight together)
+    const long long tokb = tok_base(p, b) * p.H + h;
+    constexpr int GIT = C * DK / kThreads;
+    static_assert(C * DK % kThreads == 0, "gate tile");
+#pragma unroll 8
+    for (int it = 0; it < GIT; ++it) {
+      const int idx = tid + it * kThreads;
+      const int r = idx / DK, ch = idx % DK;
+      const int s = s0 + r;
+      const int t = fastdiv(min(s, p.N - 1), p.nh_magic, p.nh_shift);
+      const bool first = s < p.N && s == t * p.n_h;
+      const long long tok = tokb + (long long)t * p.H;
+      float l = logf(fmaxf(p.ga[tok * DK + ch], FLT_MIN));
+      if (p.g != nullptr) l += logf(fmaxf(p.g[tok], FLT_MIN));
+      sGam[r * LDG + ch] = first ? l : 0.f;
+    }
+    block_sync_lds();
+    // cumulative over the chunk's sub-steps, one key channel per thread
     if (tid < DK) {
-      const float* gap = p.ga;
       float acc = 0.f;
+#pragma unroll 8
       for (int r = 0; r < C; ++r) {
-        const int s = s0 + r;
-        if (s < p.N) {
-          const int t = fastdiv(s, p.nh_magic, p.nh_shift);
-          if (s == t * p.n_h) {
-            const long long tok = (tok_base(p, b) + t) * p.H + h;
-            acc += logf(fmaxf(gap[tok * DK + tid], FLT_MIN));
-            if (p.g != nullptr) acc += logf(fmaxf(p.g[tok], FLT_MIN));
-          }
-        }
+        acc += sGam[r * LDG + tid];
         sGam[r * LDG + tid] = acc;
       }
     }
   }
   block_sync_lds();
-  if (tid < C) p.wsS[chunk * C + tid] = make_float2(sR[tid], CG ? 0.f : sG[tid]);
+  // (CG: the scan reads pre-normalised keys, so its key scale is 1 on rows in range)
+  if (tid < C) p.wsS[chunk * C + tid] = CG ? make_float2(s0 + tid < p.N ? 1.f : 0.f, 0.f) : make_float2(sR[tid], sG[tid]);
 
   if constexpr (CG) {
     // 4'. M_ij (j < i), pair by pair over the key channels; symmetric keys are
@@ -313,6 +337,30 @@ __global__ __launch_bounds__(kThreads) void dp_ut_kernel(FwdArgs p) {
                    acc);
       sA[i * LDA + j] = sB[i] * sR[i] * (p.asym ? 1.f : sR[j]) * acc;
     }
+    // the scan's key operands: e^{G_s} o kn_s and e^{G_C - G_s} o w_s, rows in range
+    {
+      OT* kg = static_cast<OT*>(p.wsKg);  // in the operand type, as the scan's LDS tiles
+      OT* ktg = static_cast<OT*>(p.wsKtg);
+      const float* gC = sGam + (C - 1) * LDG;
+      for (int idx = tid; idx < KV; idx += kThreads) {
+        const int r = idx / TPR, cg = idx % TPR;
+        const int s = s0 + r;
+        if (s < p.N) {
+          const float* gr = sGam + r * LDG + cg * VE;
+          const float rr = sR[r], rw = p.asym ? 1.f : sR[r];
+          float fk[VE], fw[VE];
+#pragma unroll
+          for (int e = 0; e < VE; ++e) {
+            fk[e] = to_f32(sK[r * LDK + cg * VE + e]) * rr * __expf(gr[e]);
+            fw[e] = to_f32(sKt[r * LDK + cg * VE + e]) * rw * __expf(gC[cg * VE + e] - gr[e]);
+          }
+          const long long off = sub_row(p, s, b, h) * DK + cg * VE;
+          st_vec16(kg + off, fk);
+          st_vec16(ktg + off, fw);
+        }
+      }
+      if (tid < DK) p.wsDec[chunk * DK + tid] = __expf(gC[tid]);
+    }
     block_sync_lds();
     // 4''. readout scores P_rj (j <= loc(r)) to wsP; the query rows take the
     //      key rows' place (the keys are done)
@@ -327,6 +375,13 @@ __global__ __launch_bounds__(kThreads) void dp_ut_kernel(FwdArgs p) {
       if (s < s0 + C && s < p.N) {
         const long long tok = (tok_base(p, b) + fastdiv(s, p.nh_magic, p.nh_shift)) * p.H + h;
         v = ld16(qp + tok * DK + cg * VE);
+        // the scan's readout query: e^{G_loc} o q
+        float fq[VE];
+        unpack16(v, fq, T{});
+        const float* gl = sGam + (s - s0) * LDG + cg * VE;
+#pragma unroll
+        for (int e = 0; e < VE; ++e) fq[e] *= __expf(gl[e]);
+        st_vec16(static_cast<OT*>(p.wsQg) + tok * DK + cg * VE, fq);
       }
       st16(sK + r * LDK + cg * VE, v);
     }
@@ -448,11 +503,11 @@ __global__ __launch_bounds__(kThreads) void dp_ut_kernel(FwdArgs p) {
 // next chunk's sub-steps and readout tokens are computed once per chunk into
 // LDS.  All barriers order LDS only.  NRT = readout-row tiles per chunk.
 //
-// CG (per-key-channel gate, see dp_ut_kernel): the scores come from the UT
-// kernel (wsP); after a chunk is committed, each key channel's thread walks the
-// chunk's sub-steps once for the last cumulative log-gate G_C and once to scale
-// the read keys by e^{G_s}, the write keys by e^{G_C - G_s} and the readout
-// queries by e^{G_loc}; the state's rows decay by e^{G_C} (every factor at most 1).
+// CG (per-key-channel gate, see dp_ut_kernel): the scan runs on the UT
+// kernel's gated operands (read keys e^{G_s} o kn_s, write keys
+// e^{G_C - G_s} o w_s, readout queries e^{G_loc} o q, passed as k, kt and q
+// of a write-key launch) and its scores (wsP), with no scalar-gate factors;
+// the state's rows decay by e^{G_C} (wsDec).  Every factor is at most 1.
 template <typename T, int DK, int C, int BV, int NRT, bool CG = false>
 __global__ __launch_bounds__(kThreads) void dp_scan_kernel(FwdArgs p) {
   using OT = typename OpType<T>::type;  // MFMA operand type
@@ -546,7 +601,7 @@ __global__ __launch_bounds__(kThreads) void dp_scan_kernel(FwdArgs p) {
   constexpr int PV = RT * TPRC, PIT = (PV + kThreads - 1) / kThreads;  // CG scores
   u32x4_t rk[KIT], rkt[KIT], rq[QIT], rt[TIT], rvv[VIT], rp[CG ? PIT : 1];
   float rinv[KIT];
-  float rg;
+  float rg, rdec = 1.f;
 
   auto prefetch = [&](int c) {
     const long long* rows = sRow + (c & 1) * C;
@@ -576,6 +631,7 @@ __global__ __launch_bounds__(kThreads) void dp_scan_kernel(FwdArgs p) {
       }
     }
     rg = ssrc[min(tid, C - 1)].y;
+    if constexpr (CG) rdec = p.wsDec[((long long)bh * nc + c) * DK + min(tid, DK - 1)];
 #pragma unroll
     for (int it = 0; it < QIT; ++it) {
       const int idx = (QV % kThreads == 0) ? tid + it * kThreads : min(tid + it * kThreads, QV - 1);
@@ -600,14 +656,16 @@ __global__ __launch_bounds__(kThreads) void dp_scan_kernel(FwdArgs p) {
       const int idx = tid + it * kThreads;
       const int r = idx / TPR, cg = idx % TPR;
       if (KV % kThreads == 0 || idx < KV) {
+        // (CG: the UT kernel's gated operands, stored in the operand type)
+        using LT = std::conditional_t<CG, OT, T>;
         float fv[VE];
-        unpack16(rk[it], fv, T{});
+        unpack16(rk[it], fv, LT{});
 #pragma unroll
         for (int e = 0; e < VE; ++e) fv[e] *= rinv[it];  // 1/|k|, 0 past the end
         st_vec16(sK + r * LDK + cg * VE, fv);
         if (CG && !p.asym) st_vec16(sKt + r * LDK + cg * VE, fv);  // write keys: the unit keys
         if (p.asym) {
-          unpack16(rkt[it], fv, T{});
+          unpack16(rkt[it], fv, LT{});
           const float keep = (s0 + r < p.N) ? 1.f : 0.f;
 #pragma unroll
           for (int e = 0; e < VE; ++e) fv[e] *= keep;
@@ -635,7 +693,7 @@ __global__ __launch_bounds__(kThreads) void dp_scan_kernel(FwdArgs p) {
       const int i = idx / TPR, cg = idx % TPR;
       if (QV % kThreads == 0 || idx < QV) {
         float fv[VE];
-        unpack16(rq[it], fv, T{});
+        unpack16(rq[it], fv, std::conditional_t<CG, OT, T>{});
         const float keep = toks[i] >= 0 ? 1.f : 0.f;
 #pragma unroll
         for (int e = 0; e < VE; ++e) fv[e] *= keep;
@@ -660,6 +718,7 @@ __global__ __launch_bounds__(kThreads) void dp_scan_kernel(FwdArgs p) {
       sG[tid] = rg;
       sEG[tid] = expf(rg);
     }
+    if (CG && tid < DK) sDec[tid] = rdec;
     if (tid < RT) sLoc[tid] = toks[tid] >= 0 ? (s0 + (n_h - 1 - (s0 - fastdiv(s0, p.nh_magic, p.nh_shift) * n_h)) + tid * n_h) - s0 : -1;
     if (c + 1 < nc) index_chunk(c + 1);
   };
@@ -687,47 +746,11 @@ __global__ __launch_bounds__(kThreads) void dp_scan_kernel(FwdArgs p) {
     block_sync_lds();
     prefetch(0);
   }
-  // CG: log-gate of key channel ch at sub-step s (log alpha_t + log g_t at a
-  // token's first sub-step, 0 on the others and past the end)
-  auto log_gate = [&](int s, int ch) {
-    float l = 0.f;
-    if (s < p.N) {
-      const int t = fastdiv(s, p.nh_magic, p.nh_shift);
-      if (s == t * n_h) {
-        const long long tok = tok0 + (long long)t * p.H;
-        l = logf(fmaxf(p.ga[tok * DK + ch], FLT_MIN));
-        if (p.g != nullptr) l += logf(fmaxf(p.g[tok], FLT_MIN));
-      }
-    }
-    return l;
-  };
   for (int c = 0; c < nc; ++c) {
     const int s0 = c * C;
     block_sync_lds();  // the previous chunk is done with every tile below
     commit(c);
     block_sync_lds();
-    if constexpr (CG) {
-      if (tid < DK) {
-        float gl = 0.f;
-        for (int i = 0; i < C; ++i) gl += log_gate(s0 + i, tid);
-        const int loc0 = n_h - 1 - (s0 - fastdiv(s0, p.nh_magic, p.nh_shift) * n_h);
-        float acc = 0.f;
-        int nxt = loc0, r = 0;
-        for (int i = 0; i < C; ++i) {
-          acc += log_gate(s0 + i, tid);
-          const float ea = __expf(acc);
-          sK[i * LDK + tid] = from_f32<OT>(to_f32(sK[i * LDK + tid]) * ea);
-          sKt[i * LDK + tid] = from_f32<OT>(to_f32(sKt[i * LDK + tid]) * __expf(gl - acc));
-          if (i == nxt) {
-            if (r < RT) sQ[r * LDK + tid] = from_f32<OT>(to_f32(sQ[r * LDK + tid]) * ea);
-            ++r;
-            nxt += n_h;
-          }
-        }
-        sDec[tid] = __expf(gl);
-      }
-      block_sync_lds();
-    }
     if (c + 1 < nc) prefetch(c + 1);
 
     // ---- phase 1: X = V - diag(e^G) (Kn H0);  P^T = Kw Q^T (masked, gated);  Z = Q H0
@@ -1281,7 +1304,15 @@ __global__ __launch_bounds__(64) void dp_precond_kernel(PrecondArgs p) {
 
   float d[EPL];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) d[e] = p.d[bh * DK + sl * EPL + e];
+  for (int e = 0; e < EPL; ++e) d[e] = p.d_ones ? 1.f : p.d[bh * DK + sl * EPL + e];
+  // d_t of token t, kept for the backward when asked for
+  float* const dtp = p.dtr != nullptr ? p.dtr + row0 * DK + sl * EPL : nullptr;
+  auto store_d = [&](int t) {
+    if constexpr (EPL == 2)
+      *reinterpret_cast<float2*>(dtp + t * kstride) = make_float2(d[0], d[1]);
+    else
+      dtp[t * kstride] = d[0];
+  };
 
   // write key d o kh (EPL values, stored together) at dst
   auto store_kt_at = [&](T* dst, const float* kh) {
@@ -1381,6 +1412,7 @@ __global__ __launch_bounds__(64) void dp_precond_kernel(PrecondArgs p) {
           ds = head_sum<LPH>(ds);
           store_kt_at(kto, kh);
           kto += kstride;
+          if (dtp != nullptr) store_d(t);
           const float coef = fmaf(-bw, ds, w);
           if constexpr (RET) {
             const float rt = lane_val(rtv, i);
@@ -1481,6 +1513,7 @@ __global__ __launch_bounds__(64) void dp_precond_kernel(PrecondArgs p) {
         ds = head_sum<LPH>(ds);
         // emit the write key with the current d_t
         if (active) store_kt(t, kh[q]);
+        if (active && dtp != nullptr) store_d(t);
         const float coef = w[q] * (1.f - bt[q] * ds);
         // retention scales d_t (exactly 1 without the gate), the step uses d_t
 #pragma unroll
@@ -1642,10 +1675,16 @@ hipError_t launch_cg(const FwdArgs& a, int BV, int lds_scan, int stages, hipStre
     if (e != hipSuccess) return e;
   }
   if (stages & 2) {
+    // the scan reads the UT kernel's gated operands as its write-key inputs
+    FwdArgs s = a;
+    s.k = a.wsKg;
+    s.kt = a.wsKtg;
+    s.q = a.wsQg;
+    s.asym = 1;
     switch (BV) {
-      case 16: return launch_scan_cg_nrt<T, DK, C, 16>(a, lds_scan, st);
-      case 32: return launch_scan_cg_nrt<T, DK, C, 32>(a, lds_scan, st);
-      case 64: return launch_scan_cg_nrt<T, DK, C, 64>(a, lds_scan, st);
+      case 16: return launch_scan_cg_nrt<T, DK, C, 16>(s, lds_scan, st);
+      case 32: return launch_scan_cg_nrt<T, DK, C, 32>(s, lds_scan, st);
+      case 64: return launch_scan_cg_nrt<T, DK, C, 64>(s, lds_scan, st);
       default: return hipErrorInvalidValue;
     }
   }

@@ -93,13 +93,20 @@ def test_workspace_size_formula(lib):
     assert bf16_chunk_block(128, 64, 3, write_keys=True) == 35712 + 64 * 128 * 2
     sink = 4 * 16 * (128 // 16) * 64 * 4  # one fp32 slot per lane of every scan wavefront
     assert n == -(-4 * 16 * nc * (35712 + 16384) // 256) * 256 + sink
-    rc, n = ws(2, 1, 1, 33, 16, 16, 16, 2)  # ragged: 66 sub-steps -> 5 chunks
-    assert rc == 0 and n == -(-5 * bf16_chunk_block(16, 16, 2) // 256) * 256 + 256
-    rc, n = ws(2, 1, 1, 33, 16, 16, 16, 4)  # ragged: 66 sub-steps -> 5 chunks
-    # fp32: T (C x C), the per-sub-step scalars, and the readout scores (RT x C, RT = 16)
-    # that the per-channel-gate form keeps, each region 256-byte aligned
+    # the per-channel-gate form keeps T (C x C), the per-sub-step scalars, the
+    # readout scores (RT x C, RT = 16 here), gated read and write keys (the
+    # layout of k), gated readout queries (the layout of q) and a dk-float decay
+    # per chunk, each region 256-byte aligned; the size is the larger need
     up = lambda x: -(-x // 256) * 256
-    assert rc == 0 and n == up(5 * 16 * 16 * 4) + up(5 * 16 * 8) + up(5 * 16 * 16 * 4)
+
+    def cg(elem, nch=5, C=16, RT=16, toks=33, n_h=2, dk=16):
+        return (up(nch * C * C * elem) + up(nch * C * 8) + up(nch * RT * C * elem) + 2 * up(toks * n_h * dk * elem)
+                + up(toks * dk * elem) + up(nch * dk * 4))
+
+    rc, n = ws(2, 1, 1, 33, 16, 16, 16, 2)  # ragged: 66 sub-steps -> 5 chunks
+    assert rc == 0 and n == max(-(-5 * bf16_chunk_block(16, 16, 2) // 256) * 256 + 256, cg(2))
+    rc, n = ws(2, 1, 1, 33, 16, 16, 16, 4)  # ragged: 66 sub-steps -> 5 chunks
+    assert rc == 0 and n == cg(4)
     assert ws(2, 1, 1, 0, 16, 16, 16, 4) == (0, 0)
 
 
@@ -369,3 +376,73 @@ def test_noalloc_varlen_validation_before_hip(lib):
     assert call(nseq=0) == E.DP_EINVAL
     assert call(q=FAKE + 8) == E.DP_EINVAL
     assert "scratch" in dp.status_str(E.DP_ESCRATCH)
+
+
+def test_backward_entry_points_validate_before_hip(lib):
+    """The write-key backward, phase 1's backward and the OSDN layer's backward
+    return every validation status before any HIP call."""
+    E = dp.binding
+
+    def bwd_wk(q=FAKE, k=FAKE, kt=FAKE, v=FAKE, beta=FAKE, dout=FAKE, n_h=1, B=1, H=1, L=8, dk=16, dv=16,
+               dkt=FAKE, wsp=FAKE, wsb=1 << 30):
+        return lib.dp_bwd_wk_bf16(q, k, kt, v, beta, None, None, dout, None, n_h, B, H, L, dk, dv, FAKE, FAKE,
+                                  dkt, FAKE, FAKE, None, None, wsp, wsb, None)
+
+    assert bwd_wk(kt=None) == E.DP_EINVAL
+    assert bwd_wk(dkt=None) == E.DP_EINVAL
+    assert bwd_wk(kt=FAKE + 4) == E.DP_EINVAL      # misaligned
+    assert bwd_wk(dout=FAKE + 8) == E.DP_EINVAL
+    assert bwd_wk(dk=48) == E.DP_ENOTSUP
+    assert bwd_wk(wsp=None) == E.DP_EWORKSPACE
+    assert bwd_wk(wsb=16) == E.DP_EWORKSPACE
+    # the symmetric backward now checks alignment too
+    assert lib.dp_bwd_bf16(FAKE + 2, FAKE, FAKE, FAKE, None, None, FAKE, None, 1, 1, 1, 8, 16, 16, FAKE, FAKE,
+                           FAKE, FAKE, None, None, FAKE, 1 << 30, None) == E.DP_EINVAL
+
+    def pbwd(k=FAKE, beta=FAKE, dkt=FAKE, flags=0, B=1, H=1, L=4, dk=16, eta=3e-3, dmin=0.5, dmax=2.0,
+             eps=1e-6, dko=FAKE, db=FAKE, wsp=FAKE, wsb=1 << 30):
+        return lib.dp_osdn_precond_bwd_bf16(k, beta, None, None, dkt, None, flags, B, H, L, dk, eta, dmin, dmax,
+                                            eps, dko, db, None, None, wsp, wsb, None)
+
+    assert pbwd(k=None) == E.DP_EINVAL
+    assert pbwd(k=FAKE + 2) == E.DP_EINVAL
+    assert pbwd(dkt=None) == E.DP_EINVAL
+    assert pbwd(dko=None) == E.DP_EINVAL
+    assert pbwd(db=None) == E.DP_EINVAL
+    assert pbwd(flags=4) == E.DP_EINVAL
+    assert pbwd(dk=48) == E.DP_ENOTSUP
+    assert pbwd(eps=0.0) == E.DP_EINVAL
+    assert pbwd(wsp=None) == E.DP_EWORKSPACE
+    assert pbwd(wsp=FAKE + 16) == E.DP_EWORKSPACE
+    n = ctypes.c_size_t(0)
+    assert lib.dp_osdn_precond_bwd_workspace_size(2, 3, 5, 32, ctypes.byref(n)) == E.DP_OK
+    up = lambda x: (x + 255) // 256 * 256
+    assert n.value == up(2 * 3 * 32 * 4) + 2 * up(2 * 5 * 3 * 32 * 4)
+    assert pbwd(wsb=n.value - 1, B=2, H=3, L=5, dk=32) == E.DP_EWORKSPACE
+
+    def obwd(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, dout=FAKE, B=1, H=1, L=8, dk=16, dv=16, dq=FAKE, dko=FAKE,
+             dvo=FAKE, db=FAKE, eps=1e-6, wsp=FAKE, wsb=1 << 30):
+        return lib.dp_osdn_bwd_bf16(q, k, v, beta, None, None, None, None, dout, None, None, 0, B, H, L, dk, dv,
+                                    3e-3, 0.5, 2.0, eps, dq, dko, dvo, db, None, None, None, None, wsp, wsb, None)
+
+    for kw in (dict(q=None), dict(v=None), dict(dout=None), dict(dq=None), dict(dvo=None), dict(dko=None),
+               dict(db=None), dict(k=FAKE + 2), dict(v=FAKE + 4), dict(eps=-1.0)):
+        assert obwd(**kw) == E.DP_EINVAL, kw
+    assert obwd(dk=48) == E.DP_ENOTSUP
+    assert obwd(wsp=None) == E.DP_EWORKSPACE
+    assert lib.dp_osdn_bwd_workspace_size(2, 3, 70, 32, 64, ctypes.byref(n)) == E.DP_OK
+    pb, bw = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    lib.dp_osdn_precond_bwd_workspace_size(2, 3, 70, 32, ctypes.byref(pb))
+    lib.dp_bwd_workspace_size(1, 2, 3, 70, 32, 64, ctypes.byref(bw))
+    assert n.value == pb.value + 2 * up(2 * 70 * 3 * 32 * 4) + bw.value
+    assert obwd(wsb=n.value - 1, B=2, H=3, L=70, dk=32, dv=64) == E.DP_EWORKSPACE
+
+
+def test_backward_bindings_reject_bad_tensors_on_cpu():
+    import torch
+    k = torch.zeros(1, 4, 2, 16)
+    beta = torch.zeros(1, 4, 2)
+    with pytest.raises(TypeError):
+        dp.osdn_precond_bwd(k, beta, torch.zeros(1, 4, 2, 16, dtype=torch.float64))
+    with pytest.raises(ValueError):
+        dp.osdn_bwd(k, k, torch.zeros(1, 4, 2, 16), beta[:, :3], torch.zeros(1, 4, 2, 16))
