@@ -104,7 +104,8 @@ def _mutate(src, name):
     assert src.count(a) >= 1, name
     s = src.replace(a, b)
     if name == "phase1_emit_after_update":
-        s = s.replace(*_EMIT_LATE)
+        # the first update of d is phase 1's own (the gradient's forward pass repeats the line)
+        s = s.replace(*_EMIT_LATE, 1)
     if name == "readout_before_last_substep":
         # read out after the first sub-step instead of the last
         s = s.replace(_READOUT_FIX[0], _READOUT_FIX[1])
