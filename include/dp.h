@@ -45,7 +45,10 @@
  *     path the computed MFMA operands (normalised keys, queries, write keys,
  *     a rounded copy of the state, T diag(beta), pseudo-values, scores) are
  *     fp16, so q, kt, v and the state must stay within fp16 range
- *     (|x| < 65504); the fp32 path uses fp32 throughout.
+ *     (|x| < 65504): past it the operand is +-Inf, the results that depend
+ *     on it are not finite (a query: its token's output row; a pseudo-value:
+ *     its head from that chunk on) and other heads are unaffected.  The fp32
+ *     path uses fp32 throughout.
  *   - Supported shapes: dk, dv in {16, 32, 64, 128}; chunk in {16, 32, 64}
  *     (counted in sub-steps of the expanded sequence); 1 <= n_h <= 64.
  *     B, H >= 1, L >= 0.  L*n_h need not be a multiple of chunk: the tail is

@@ -968,7 +968,7 @@ __global__ __launch_bounds__(256) void dp_bwd_chunk_kernel(BwdArgs p) {
 //   gkh = 2 kh o gs + d o gkt,  then the normalisation kh = k / max(|k|, 1e-6)
 // The lane layout is the forward's (LPH lanes per head, EPL coordinates per
 // lane); tokens run last to first in blocks of PB.  Everything but gd is
-// formed for a whole block first (three head sums per token, off the
+// formed for a whole block first (two head sums per token, off the
 // dependent chain); the chain itself is gx, <gx, s>, gd: one head sum per
 // token, as in the forward.  d_t comes from the trajectory the forward kernel
 // stored.  dk and dbeta are accumulated into (they already hold the write-key
@@ -1060,19 +1060,18 @@ __global__ __launch_bounds__(64) void dp_precond_bwd_kernel(PrecondBwdArgs p) {
       n2 = head_sum<LPH>(n2);
       rinv[i] = __builtin_amdgcn_rsqf(fmaxf(n2, 1e-12f));  // 1 / max(|k|, 1e-6)
       tiny[i] = !(n2 > 1e-12f);
-      float ns = 0.f, ds = 0.f;
+      const float ns = n2 * rinv[i] * rinv[i];  // |kh|^2, as the forward forms it
+      float ds = 0.f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
         kh[i][e] = to_f32(c.k[i][e]) * rinv[i];
         sq[i][e] = kh[i][e] * kh[i][e];
-        ns += sq[i][e];
         ds = fmaf(c.d[i][e], sq[i][e], ds);
       }
-      ns = head_sum<LPH>(ns);
       ds = head_sum<LPH>(ds);
       const float bu = p.beta_aware ? clamp_keep_nan(c.beta[i], 0.f, 2.f) : 1.f;
       const float a = bu * ds;
-      const float rn = 1.f / fmaxf(ns, p.eps);
+      const float rn = __builtin_amdgcn_rcpf(fmaxf(ns, p.eps));
       coef[i] = p.eta * bu * (1.f - a) * rn;
       c2[i] = p.eta * bu * bu * rn;
       fb[i] = p.eta * (1.f - 2.f * a) * rn;
