@@ -488,7 +488,7 @@ def time_bwd(w, steps, warmup):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
-    return {"workload": f"backward of {describe(w)}; fp32 arithmetic, 32-sub-step chunks",
+    return {"workload": f"backward of {describe(w)}; fp32 state and accumulation, fp16 MFMA operands, 32-sub-step chunks",
             "value": w.B * w.L / (ms / 1e3), "unit": "tokens/s", "ms_per_step": ms,
             "workspace_bytes": ws.numel()}
 
@@ -530,7 +530,7 @@ def time_osdn_bwd(steps, warmup):
     grads = dp.osdn_bwd(q, k, v, beta, dout, workspace=ws)
     ms = _event_time(lambda: dp.osdn_bwd(q, k, v, beta, dout, workspace=ws, grads=grads), steps, warmup)
     return {"workload": f"OSDN layer backward (phase 1 + write-key forward) of {describe(w)}; "
-                        "fp32 arithmetic, 32-token chunks",
+                        "fp32 state and accumulation, fp16 MFMA operands, 32-token chunks",
             "value": w.B * w.L / (ms / 1e3), "unit": "tokens/s", "ms_per_step": ms,
             "workspace_bytes": ws.numel()}
 

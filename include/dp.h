@@ -411,7 +411,9 @@ int dp_decode_bf16(const void* q, const void* k, const void* kt, const void* v,
  * forward call is needed.  workspace: dp_bwd_workspace_size() bytes,
  * 256-byte aligned, caller-owned (T and the key scalars per 32-sub-step
  * chunk, the chunk-start states and their gradients, all fp32: about
- * 2 dk dv 4 B per 32 sub-steps per head).  All arithmetic is fp32.
+ * 2 dk dv 4 B per 32 sub-steps per head).  The state, its gradient and
+ * every accumulation are fp32; the MFMA operands are fp32 on the fp32 path
+ * and fp16 on the bf16 path (as the forward's, with the same range).
  * Errors: DP_EINVAL (null required pointer, sizes <= 0), DP_ENOTSUP (dk or
  * dv outside {16, 32, 64, 128}, n_h > 64, sizes past the 32-bit index
  * limits), DP_EWORKSPACE, DP_EHIP.

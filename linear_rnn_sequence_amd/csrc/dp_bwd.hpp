@@ -27,7 +27,9 @@
 //                          of every chunk -> workspace, dH0 of chunk 0 -> dh0
 //   dp_bwd_chunk_kernel    one workgroup per chunk, all in parallel: dq, dk,
 //                          dv, dbeta, dg from H0, dH1, dUp and the chunk
-// All arithmetic is fp32 (fp32 MFMA, 16x16x4), whatever the input type.
+// The state and its gradient are kept in fp32, and every product accumulates
+// in fp32; the MFMA operands are the input's operand type (fp16 for bf16
+// inputs, as the forward uses; fp32 for fp32 inputs).
 //
 // ASYM: write keys W given apart from the read keys (the OSDN write-key
 // forward, sec. 2.5 phase 2): M = strict_tril(diag(beta)(E o K W^T)), the
@@ -74,13 +76,28 @@ struct BwdArgs {
 
 // acc += A * B, A read transposed (element (m, k) at a[k * lda + ra + m]) and
 // B read k-major (element (k, n) at b[k * ldb + rb + n]).
+template <typename T, int K>
+__device__ __forceinline__ f32x4_t mm_tile_tt(f32x4_t acc, const T* a, int lda, int ra, const T* b, int ldb,
+                                              int rb) {
+  using M = Mfma<T>;
+  static_assert(K % M::KS == 0 || K % M::KS == 16, "contraction length");
+#pragma unroll
+  for (int k0 = 0; k0 + M::KS <= K; k0 += M::KS)
+    acc = M::mma(M::load_t(a, lda, ra, k0), M::load_t(b, ldb, rb, k0), acc);
+  if constexpr (K % M::KS == 16)
+    acc = M::mma4(M::load4_t(a, lda, ra, K - 16), M::load4_t(b, ldb, rb, K - 16), acc);
+  return acc;
+}
 template <int K>
 __device__ __forceinline__ f32x4_t mm_tile_tt(f32x4_t acc, const float* a, int lda, int ra, const float* b,
                                               int ldb, int rb) {
-  using M = Mfma<float>;
-#pragma unroll
-  for (int k0 = 0; k0 < K; k0 += M::KS) acc = M::mma(M::load_t(a, lda, ra, k0), M::load_t(b, ldb, rb, k0), acc);
-  return acc;
+  return mm_tile_tt<float, K>(acc, a, lda, ra, b, ldb, rb);
+}
+
+// Row pitch (elements) of an LDS operand buffer of n columns: n plus 16 bytes.
+template <typename OT>
+__host__ __device__ constexpr int bwd_ld(int n) {
+  return n + 16 / (int)sizeof(OT);
 }
 
 // Sum over the 16 lanes of one lane group (one accumulator row of a tile).
@@ -207,22 +224,22 @@ struct BwdChunkCommon {
       gl = p.wsS[chunk * C + C - 1].y;
     }
   }
-  template <int LDK, int LDC>
-  __device__ __forceinline__ void commit(float* sK, float* sT, float* sW = nullptr) const {
+  template <int LDK, int LDC, typename OT>
+  __device__ __forceinline__ void commit(OT* sK, OT* sT, OT* sW = nullptr) const {
     const int tid = threadIdx.x;
-    float* kd = sK + (tid / TPR) * LDK + (tid % TPR) * EK;
+    OT* kd = sK + (tid / TPR) * LDK + (tid % TPR) * EK;
 #pragma unroll
-    for (int i = 0; i < EK; ++i) kd[i] = k[i] * rinv;
+    for (int i = 0; i < EK; ++i) kd[i] = from_f32<OT>(k[i] * rinv);
     if constexpr (ASYM) {
-      float* wd = sW + (tid / TPR) * LDK + (tid % TPR) * EK;
+      OT* wd = sW + (tid / TPR) * LDK + (tid % TPR) * EK;
 #pragma unroll
-      for (int i = 0; i < EK; ++i) wd[i] = w[i];
+      for (int i = 0; i < EK; ++i) wd[i] = from_f32<OT>(w[i]);
     }
-    float* td = sT + ((4 * tid) / C) * LDC + (4 * tid) % C;
-    td[0] = t.x;
-    td[1] = t.y;
-    td[2] = t.z;
-    td[3] = t.w;
+    OT* td = sT + ((4 * tid) / C) * LDC + (4 * tid) % C;
+    td[0] = from_f32<OT>(t.x);
+    td[1] = from_f32<OT>(t.y);
+    td[2] = from_f32<OT>(t.z);
+    td[3] = from_f32<OT>(t.w);
   }
 };
 
@@ -232,14 +249,17 @@ struct BwdChunkCommon {
 // lives in LDS (fp32); each wavefront updates the tiles it owns.
 template <typename T, int DK, int C, int BV, bool ASYM = false>
 __global__ __launch_bounds__(256) void dp_bwd_states_kernel(BwdArgs p) {
-  constexpr int LDK = DK + 4, LDC = C + 4, LDB = BV + 4;
+  using OT = typename OpType<T>::type;  // MFMA operand type
+  constexpr int LDK = bwd_ld<OT>(DK), LDC = bwd_ld<OT>(C), LDB = bwd_ld<OT>(BV), LDF = BV + 4;
   constexpr int NCT = C / 16, NDT = DK / 16, NVT = BV / 16;
   using Common = BwdChunkCommon<T, DK, C, ASYM>;
   constexpr int TPR = Common::TPR, EV = BV / TPR;
   static_assert(EV >= 1 && BV % TPR == 0, "value slice");
-  __shared__ float sK[C * LDK], sT[C * LDC], sH[DK * LDB], sXb[C * LDB], sU[C * LDB], sV[C * LDB];
-  __shared__ float sW[ASYM ? C * LDK : 1];  // ASYM: write keys
-  float* const sKw = ASYM ? sW : sK;        // the keys the state update writes with
+  // sH: the fp32 state; sHo its operand copy; sV the values (fp32)
+  __shared__ __align__(16) OT sK[C * LDK], sT[C * LDC], sHo[DK * LDB], sXb[C * LDB], sU[C * LDB];
+  __shared__ __align__(16) float sH[DK * LDF], sV[C * LDF];
+  __shared__ __align__(16) OT sW[ASYM ? C * LDK : 1];  // ASYM: write keys
+  OT* const sKw = ASYM ? sW : sK;                      // the keys the state update writes with
   __shared__ float sB[C], sEG[C], sEL[C];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -268,7 +288,9 @@ __global__ __launch_bounds__(256) void dp_bwd_states_kernel(BwdArgs p) {
 
   for (int idx = tid; idx < DK * BV; idx += 256) {
     const int d = idx / BV, n = idx % BV;
-    sH[d * LDB + n] = p.h0 != nullptr ? p.h0[((long long)bh * DK + d) * p.dvd + v0 + n] : 0.f;
+    const float h0 = p.h0 != nullptr ? p.h0[((long long)bh * DK + d) * p.dvd + v0 + n] : 0.f;
+    sH[d * LDF + n] = h0;
+    sHo[d * LDB + n] = from_f32<OT>(h0);
   }
   if (p.nc > 0) prefetch(nb0, 0);
   if (p.nc > 1) prefetch(nb1, 1);
@@ -277,7 +299,7 @@ __global__ __launch_bounds__(256) void dp_bwd_states_kernel(BwdArgs p) {
     __syncthreads();  // the previous chunk is done with every buffer
     nx.x.template commit<LDK, LDC>(sK, sT, sW);
     {
-      float* vd = sV + (tid / TPR) * LDB + (tid % TPR) * EV;
+      float* vd = sV + (tid / TPR) * LDF + (tid % TPR) * EV;
 #pragma unroll
       for (int i = 0; i < EV; ++i) vd[i] = nx.v[i];
     }
@@ -290,7 +312,7 @@ __global__ __launch_bounds__(256) void dp_bwd_states_kernel(BwdArgs p) {
     float* hdst = p.hs + chunk * DK * p.dvd + v0;
     for (int idx = tid; idx < DK * BV; idx += 256) {
       const int d = idx / BV, n = idx % BV;
-      hdst[(long long)d * p.dvd + n] = sH[d * LDB + n];
+      hdst[(long long)d * p.dvd + n] = sH[d * LDF + n];
     }
     __syncthreads();
     if (c + 2 < p.nc) prefetch(nx, c + 2);  // lands while the next two chunks are computed
@@ -298,11 +320,11 @@ __global__ __launch_bounds__(256) void dp_bwd_states_kernel(BwdArgs p) {
     for (int tile = wave; tile < NCT * NVT; tile += 4) {
       const int ct = tile / NVT, nt = tile % NVT;
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mm_tile_tb<float, DK>(acc, sK, LDK, ct * 16, sH, LDB, nt * 16);
+      acc = mm_tile_tb<OT, DK>(acc, sK, LDK, ct * 16, sHo, LDB, nt * 16);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = ct * 16 + 4 * grp + e, n = nt * 16 + col;
-        sXb[r * LDB + n] = sB[r] * (sV[r * LDB + n] - sEG[r] * acc[e]);
+        sXb[r * LDB + n] = from_f32<OT>(sB[r] * (sV[r * LDF + n] - sEG[r] * acc[e]));
       }
     }
     __syncthreads();
@@ -310,11 +332,11 @@ __global__ __launch_bounds__(256) void dp_bwd_states_kernel(BwdArgs p) {
     for (int tile = wave; tile < NCT * NVT; tile += 4) {
       const int ct = tile / NVT, nt = tile % NVT;
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mm_tile_tb<float, C>(acc, sT, LDC, ct * 16, sXb, LDB, nt * 16);
+      acc = mm_tile_tb<OT, C>(acc, sT, LDC, ct * 16, sXb, LDB, nt * 16);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = ct * 16 + 4 * grp + e;
-        sU[r * LDB + nt * 16 + col] = sEL[r] * acc[e];
+        sU[r * LDB + nt * 16 + col] = from_f32<OT>(sEL[r] * acc[e]);
       }
     }
     __syncthreads();
@@ -324,10 +346,13 @@ __global__ __launch_bounds__(256) void dp_bwd_states_kernel(BwdArgs p) {
       const int dt = tile / NVT, nt = tile % NVT;
       f32x4_t acc;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = egl * sH[(dt * 16 + 4 * grp + e) * LDB + nt * 16 + col];
-      acc = mm_tile_tt<C>(acc, sKw, LDK, dt * 16, sU, LDB, nt * 16);
+      for (int e = 0; e < 4; ++e) acc[e] = egl * sH[(dt * 16 + 4 * grp + e) * LDF + nt * 16 + col];
+      acc = mm_tile_tt<OT, C>(acc, sKw, LDK, dt * 16, sU, LDB, nt * 16);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sH[(dt * 16 + 4 * grp + e) * LDB + nt * 16 + col] = acc[e];
+      for (int e = 0; e < 4; ++e) {
+        sH[(dt * 16 + 4 * grp + e) * LDF + nt * 16 + col] = acc[e];
+        sHo[(dt * 16 + 4 * grp + e) * LDB + nt * 16 + col] = from_f32<OT>(acc[e]);
+      }
     }
   };
   for (int c = 0; c < p.nc; c += 2) {
@@ -341,46 +366,43 @@ __global__ __launch_bounds__(256) void dp_bwd_states_kernel(BwdArgs p) {
 // workgroup per (head, block of BV value columns), chunks last to first.
 // Writes dH1 (the gradient of each chunk's end state) and dUp per chunk, and
 // the gradient of the initial state.
-// LDS of dp_bwd_dstate_kernel (dynamic: with the write keys it passes 64 KB)
-template <int DK, int C, int BV, int RT, bool ASYM>
-__host__ __device__ constexpr int bwd_dstate_lds_floats() {
-  return (ASYM ? 2 : 1) * C * (DK + 4) + RT * (DK + 4) + C * (C + 4) + RT * (C + 4) + DK * (BV + 4) +
-         2 * RT * (BV + 4) + 2 * C * (BV + 4) + 4 * C;
-}
-template <int DK, int C, int BV, int RT, bool ASYM>
+// LDS of dp_bwd_dstate_kernel (dynamic: with the write keys it passes 64 KB):
+// the operand buffers in OT, then the fp32 state gradient and the scalars.
+template <typename OT, int DK, int C, int BV, int RT, bool ASYM>
 __host__ __device__ constexpr int bwd_dstate_lds_bytes() {
-  return bwd_dstate_lds_floats<DK, C, BV, RT, ASYM>() * 4 + RT * 4;
+  constexpr int LDK = bwd_ld<OT>(DK), LDC = bwd_ld<OT>(C), LDB = bwd_ld<OT>(BV);
+  return ((ASYM ? 2 : 1) * C * LDK + RT * LDK + C * LDC + RT * LDC + DK * LDB + 2 * RT * LDB + 2 * C * LDB) *
+             (int)sizeof(OT) +
+         (DK * (BV + 4) + 4 * C) * 4 + RT * 4;
 }
 
 template <typename T, int DK, int C, int BV, int NRT, bool ASYM = false>
 __global__ __launch_bounds__(256) void dp_bwd_dstate_kernel(BwdArgs p) {
+  using OT = typename OpType<T>::type;  // MFMA operand type
   constexpr int RT = 16 * NRT;
-  constexpr int LDK = DK + 4, LDC = C + 4, LDB = BV + 4;
+  constexpr int LDK = bwd_ld<OT>(DK), LDC = bwd_ld<OT>(C), LDB = bwd_ld<OT>(BV), LDF = BV + 4;
   constexpr int NCT = C / 16, NDT = DK / 16, NVT = BV / 16;
   using Common = BwdChunkCommon<T, DK, C, ASYM>;
   constexpr int TPQ = 256 / RT, EQ = DK / TPQ, EO = BV / TPQ;  // per readout row
   static_assert(EQ >= 1 && EO >= 1 && DK % TPQ == 0 && BV % TPQ == 0, "readout slices");
-  extern __shared__ __align__(16) float smf[];
-  float* sK = smf;                     // C x LDK unit read keys
-  float* sW = sK + C * LDK;            // ASYM: C x LDK write keys
-  float* sQ = sW + (ASYM ? C * LDK : 0);
-  float* sT = sQ + RT * LDK;
-  float* sP = sT + C * LDC;
-  float* sdH = sP + RT * LDC;
-  float* sdO = sdH + DK * LDB;
-  float* sdOe = sdO + RT * LDB;
-  float* sdUp = sdOe + RT * LDB;
-  float* sdX = sdUp + C * LDB;
-  float* sB = sdX + C * LDB;
+  extern __shared__ __align__(16) unsigned char smb[];
+  OT* sK = reinterpret_cast<OT*>(smb);  // C x LDK unit read keys
+  OT* sW = sK + C * LDK;                // ASYM: C x LDK write keys
+  OT* sQ = sW + (ASYM ? C * LDK : 0);
+  OT* sT = sQ + RT * LDK;
+  OT* sP = sT + C * LDC;
+  OT* sdHo = sP + RT * LDC;  // operand copy of the state gradient
+  OT* sdO = sdHo + DK * LDB;
+  OT* sdOe = sdO + RT * LDB;
+  OT* sdUp = sdOe + RT * LDB;
+  OT* sdX = sdUp + C * LDB;
+  float* sdH = reinterpret_cast<float*>(sdX + C * LDB);  // the fp32 state gradient
+  float* sB = sdH + DK * LDF;
   float* sG = sB + C;
   float* sEG = sG + C;
   float* sEL = sEG + C;
   int* sLoc = reinterpret_cast<int*>(sEL + C);
-  static_assert(bwd_dstate_lds_floats<DK, C, BV, RT, ASYM>() ==
-                    (ASYM ? 2 : 1) * C * LDK + RT * LDK + C * LDC + RT * LDC + DK * LDB + 2 * RT * LDB +
-                        2 * C * LDB + 4 * C,
-                "LDS layout");
-  float* const sKw = ASYM ? sW : sK;  // the keys of the state update and the scores
+  OT* const sKw = ASYM ? sW : sK;  // the keys of the state update and the scores
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -418,7 +440,9 @@ __global__ __launch_bounds__(256) void dp_bwd_dstate_kernel(BwdArgs p) {
 
   for (int idx = tid; idx < DK * BV; idx += 256) {
     const int d = idx / BV, n = idx % BV;
-    sdH[d * LDB + n] = p.dfinal != nullptr ? p.dfinal[((long long)bh * DK + d) * p.dvd + v0 + n] : 0.f;
+    const float x = p.dfinal != nullptr ? p.dfinal[((long long)bh * DK + d) * p.dvd + v0 + n] : 0.f;
+    sdH[d * LDF + n] = x;
+    sdHo[d * LDB + n] = from_f32<OT>(x);
   }
   if (p.nc > 0) prefetch(nb0, p.nc - 1);
   if (p.nc > 1) prefetch(nb1, p.nc - 2);
@@ -429,12 +453,12 @@ __global__ __launch_bounds__(256) void dp_bwd_dstate_kernel(BwdArgs p) {
     {
       const int rr = tid / TPQ, q0 = (tid % TPQ) * EQ, o0 = (tid % TPQ) * EO;
 #pragma unroll
-      for (int i = 0; i < EQ; ++i) sQ[rr * LDK + q0 + i] = nx.q[i];
+      for (int i = 0; i < EQ; ++i) sQ[rr * LDK + q0 + i] = from_f32<OT>(nx.q[i]);
       const float e = nx.loc >= 0 ? expf(nx.g) : 0.f;
 #pragma unroll
       for (int i = 0; i < EO; ++i) {
-        sdO[rr * LDB + o0 + i] = nx.o[i];
-        sdOe[rr * LDB + o0 + i] = e * nx.o[i];
+        sdO[rr * LDB + o0 + i] = from_f32<OT>(nx.o[i]);
+        sdOe[rr * LDB + o0 + i] = from_f32<OT>(e * nx.o[i]);
       }
       if (tid % TPQ == 0) sLoc[rr] = nx.loc;
     }
@@ -448,7 +472,7 @@ __global__ __launch_bounds__(256) void dp_bwd_dstate_kernel(BwdArgs p) {
     float* ddst = p.dhe + chunk * DK * p.dvd + v0;
     for (int idx = tid; idx < DK * BV; idx += 256) {
       const int d = idx / BV, n = idx % BV;
-      ddst[(long long)d * p.dvd + n] = sdH[d * LDB + n];
+      ddst[(long long)d * p.dvd + n] = sdH[d * LDF + n];
     }
     __syncthreads();
     if (c > 1) prefetch(nx, c - 2);  // lands while the next two chunks are computed
@@ -456,12 +480,12 @@ __global__ __launch_bounds__(256) void dp_bwd_dstate_kernel(BwdArgs p) {
     for (int tile = wave; tile < NRT * NCT; tile += 4) {
       const int rt = tile / NCT, ct = tile % NCT;
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mm_tile<float, DK>(acc, sQ, LDK, rt * 16, sKw, LDK, ct * 16);
+      acc = mm_tile<OT, DK>(acc, sQ, LDK, rt * 16, sKw, LDK, ct * 16);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = rt * 16 + 4 * grp + e, j = ct * 16 + col;
         const int l = sLoc[r];
-        sP[r * LDC + j] = (l >= 0 && j <= l) ? acc[e] * expf(sG[l] - sG[j]) : 0.f;
+        sP[r * LDC + j] = from_f32<OT>((l >= 0 && j <= l) ? acc[e] * expf(sG[l] - sG[j]) : 0.f);
       }
     }
     __syncthreads();
@@ -469,13 +493,13 @@ __global__ __launch_bounds__(256) void dp_bwd_dstate_kernel(BwdArgs p) {
     for (int tile = wave; tile < NCT * NVT; tile += 4) {
       const int ct = tile / NVT, nt = tile % NVT;
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
-      acc = mm_tile_tb<float, DK>(acc, sKw, LDK, ct * 16, sdH, LDB, nt * 16);
-      acc2 = mm_tile_tt<RT>(acc2, sP, LDC, ct * 16, sdO, LDB, nt * 16);
+      acc = mm_tile_tb<OT, DK>(acc, sKw, LDK, ct * 16, sdHo, LDB, nt * 16);
+      acc2 = mm_tile_tt<OT, RT>(acc2, sP, LDC, ct * 16, sdO, LDB, nt * 16);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int j = ct * 16 + 4 * grp + e, n = nt * 16 + col;
         const float du = sEL[j] * acc[e] + acc2[e];
-        sdUp[j * LDB + n] = du;
+        sdUp[j * LDB + n] = from_f32<OT>(du);
         p.dup[(chunk * C + j) * p.dvd + v0 + n] = du;
       }
     }
@@ -484,11 +508,11 @@ __global__ __launch_bounds__(256) void dp_bwd_dstate_kernel(BwdArgs p) {
     for (int tile = wave; tile < NCT * NVT; tile += 4) {
       const int ct = tile / NVT, nt = tile % NVT;
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mm_tile_tt<C>(acc, sT, LDC, ct * 16, sdUp, LDB, nt * 16);
+      acc = mm_tile_tt<OT, C>(acc, sT, LDC, ct * 16, sdUp, LDB, nt * 16);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int j = ct * 16 + 4 * grp + e;
-        sdX[j * LDB + nt * 16 + col] = sEG[j] * sB[j] * acc[e];
+        sdX[j * LDB + nt * 16 + col] = from_f32<OT>(sEG[j] * sB[j] * acc[e]);
       }
     }
     __syncthreads();
@@ -498,11 +522,15 @@ __global__ __launch_bounds__(256) void dp_bwd_dstate_kernel(BwdArgs p) {
       const int dt = tile / NVT, nt = tile % NVT;
       f32x4_t acc, acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = egl * sdH[(dt * 16 + 4 * grp + e) * LDB + nt * 16 + col];
-      acc = mm_tile_tt<RT>(acc, sQ, LDK, dt * 16, sdOe, LDB, nt * 16);
-      acc2 = mm_tile_tt<C>(acc2, sK, LDK, dt * 16, sdX, LDB, nt * 16);
+      for (int e = 0; e < 4; ++e) acc[e] = egl * sdH[(dt * 16 + 4 * grp + e) * LDF + nt * 16 + col];
+      acc = mm_tile_tt<OT, RT>(acc, sQ, LDK, dt * 16, sdOe, LDB, nt * 16);
+      acc2 = mm_tile_tt<OT, C>(acc2, sK, LDK, dt * 16, sdX, LDB, nt * 16);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sdH[(dt * 16 + 4 * grp + e) * LDB + nt * 16 + col] = acc[e] - acc2[e];
+      for (int e = 0; e < 4; ++e) {
+        const float x = acc[e] - acc2[e];
+        sdH[(dt * 16 + 4 * grp + e) * LDF + nt * 16 + col] = x;
+        sdHo[(dt * 16 + 4 * grp + e) * LDB + nt * 16 + col] = from_f32<OT>(x);
+      }
     }
   };
   for (int c = p.nc - 1; c >= 0; c -= 2) {
@@ -513,7 +541,7 @@ __global__ __launch_bounds__(256) void dp_bwd_dstate_kernel(BwdArgs p) {
   if (p.dh0 != nullptr) {
     for (int idx = tid; idx < DK * BV; idx += 256) {
       const int d = idx / BV, n = idx % BV;
-      p.dh0[((long long)bh * DK + d) * p.dvd + v0 + n] = sdH[d * LDB + n];
+      p.dh0[((long long)bh * DK + d) * p.dvd + v0 + n] = sdH[d * LDF + n];
     }
   }
 }
@@ -533,60 +561,57 @@ __global__ __launch_bounds__(256) void dp_bwd_dstate_kernel(BwdArgs p) {
 //   dbeta_j = sum_i dTb_ij T_ij + sum_i' F_ji' e^{G_j - G_i'} S_ji'   (S = K K^T)
 //   dG    = the gate terms of each product, then dlog g = reverse cumsum of dG
 // and finally the key normalisation, the beta clamp and the log of the gate.
-template <int DK, int C, int RT, bool ASYM = false>
-__host__ __device__ constexpr int bwd_chunk_lds_floats() {
-  return (ASYM ? 2 : 1) * C * (DK + 4) + RT * (DK + 4) + 3 * C * (C + 4) + RT * (C + 4) + 2 * DK * 20 +
-         6 * C * 20 + RT * 20 + 8 * C;
-}
-template <int DK, int C, int RT, bool ASYM = false>
+// LDS of dp_bwd_chunk_kernel: the operand buffers in OT, then fp32 scalars and
+// the row indices.
+template <typename OT, int DK, int C, int RT, bool ASYM = false>
 __host__ __device__ constexpr int bwd_chunk_lds_bytes() {
-  return bwd_chunk_lds_floats<DK, C, RT, ASYM>() * 4 + C * 8 + RT * 12;
+  constexpr int LDK = bwd_ld<OT>(DK), LDC = bwd_ld<OT>(C), LDB = bwd_ld<OT>(16);
+  return ((ASYM ? 2 : 1) * C * LDK + RT * LDK + 3 * C * LDC + RT * LDC + 2 * DK * LDB + 6 * C * LDB +
+          RT * LDB) * (int)sizeof(OT) +
+         8 * C * 4 + C * 8 + RT * 12;
 }
 
 template <typename T, int DK, int C, int NRT, bool ASYM = false>
 __global__ __launch_bounds__(256) void dp_bwd_chunk_kernel(BwdArgs p) {
+  using OT = typename OpType<T>::type;  // MFMA operand type
   constexpr int BV = 16;
   constexpr int RT = 16 * NRT;
-  constexpr int LDK = DK + 4, LDC = C + 4, LDB = BV + 4;
+  constexpr int LDK = bwd_ld<OT>(DK), LDC = bwd_ld<OT>(C), LDB = bwd_ld<OT>(BV);
   constexpr int NCT = C / 16, NDT = DK / 16;
   constexpr int NKD = NCT * NDT, KPW = (NKD + 3) / 4;  // C x DK tiles
   constexpr int NQD = NRT * NDT, QPW = (NQD + 3) / 4;  // RT x DK tiles
   constexpr int NCC = NCT * NCT, NRC = NRT * NCT;
   static_assert(NCC <= 4 && NRC <= 4 && 2 * NCT <= 4, "one C x C and one RT x C tile per wavefront");
 
-  extern __shared__ __align__(16) float smf[];
-  float* sK = smf;                   // C x LDK unit keys
-  float* sWk = sK + C * LDK;         // ASYM: C x LDK write keys
-  float* sQ = sWk + (ASYM ? C * LDK : 0);  // RT x LDK readout queries
-  float* sT = sQ + RT * LDK;         // C x LDC  T
-  float* sA = sT + C * LDC;          // C x LDC  dT, then Z
-  float* sW = sA + C * LDC;          // C x LDC  T^T dT
-  float* sGm = sW + C * LDC;         // RT x LDC gated, masked dP
-  float* sH0 = sGm + RT * LDC;       // DK x LDB
-  float* sdHe = sH0 + DK * LDB;      // DK x LDB
-  float* sV = sdHe + DK * LDB;       // C x LDB
-  float* sdUp = sV + C * LDB;
-  float* sX = sdUp + C * LDB;
-  float* sXb = sX + C * LDB;         // beta X
-  float* sUp = sXb + C * LDB;
-  float* sdX = sUp + C * LDB;
-  float* sdO = sdX + C * LDB;        // RT x LDB
-  float* sB = sdO + RT * LDB;        // C scalars each
+  extern __shared__ __align__(16) unsigned char smb[];
+  OT* sK = reinterpret_cast<OT*>(smb);  // C x LDK unit keys
+  OT* sWk = sK + C * LDK;               // ASYM: C x LDK write keys
+  OT* sQ = sWk + (ASYM ? C * LDK : 0);  // RT x LDK readout queries
+  OT* sT = sQ + RT * LDK;               // C x LDC  T
+  OT* sA = sT + C * LDC;                // C x LDC  dT, then Z
+  OT* sW = sA + C * LDC;                // C x LDC  T^T dT
+  OT* sGm = sW + C * LDC;               // RT x LDC gated, masked dP
+  OT* sH0 = sGm + RT * LDC;             // DK x LDB
+  OT* sdHe = sH0 + DK * LDB;            // DK x LDB
+  OT* sV = sdHe + DK * LDB;             // C x LDB
+  OT* sdUp = sV + C * LDB;
+  OT* sX = sdUp + C * LDB;
+  OT* sXb = sX + C * LDB;  // beta X
+  OT* sUp = sXb + C * LDB;
+  OT* sdX = sUp + C * LDB;
+  OT* sdO = sdX + C * LDB;                             // RT x LDB
+  float* sB = reinterpret_cast<float*>(sdO + RT * LDB);  // C scalars each
   float* sG = sB + C;
   float* sEG = sG + C;
   float* sEL = sEG + C;
   float* sRinv = sEL + C;
-  float* sDB = sRinv + C;            // dbeta accumulator
-  float* sDG = sDB + C;              // dG accumulator
-  float* sRD = sDG + C;              // k . dkn per row
+  float* sDB = sRinv + C;  // dbeta accumulator
+  float* sDG = sDB + C;    // dG accumulator
+  float* sRD = sDG + C;    // k . dkn per row
   long long* sRow = reinterpret_cast<long long*>(sRD + C);
   long long* sTok = sRow + C;
   int* sLoc = reinterpret_cast<int*>(sTok + RT);
-  static_assert(BV + 4 == 20 && bwd_chunk_lds_floats<DK, C, RT, ASYM>() ==
-                    (ASYM ? 2 : 1) * C * LDK + RT * LDK + 3 * C * LDC + RT * LDC + 2 * DK * LDB + 6 * C * LDB +
-                        RT * LDB + 8 * C,
-                "LDS layout");
-  float* const sKw = ASYM ? sWk : sK;  // the keys of M's right side, the state update and the scores
+  OT* const sKw = ASYM ? sWk : sK;  // the keys of M's right side, the state update and the scores
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -660,15 +685,15 @@ __global__ __launch_bounds__(256) void dp_bwd_chunk_kernel(BwdArgs p) {
   }
   cx.template commit<LDK, LDC>(sK, sT, sWk);
 #pragma unroll
-  for (int i = 0; i < EQ; ++i) sQ[orr * LDK + (tid % TPQ) * EQ + i] = cq[i];
+  for (int i = 0; i < EQ; ++i) sQ[orr * LDK + (tid % TPQ) * EQ + i] = from_f32<OT>(cq[i]);
   __syncthreads();
 
   // S = K W^T (tile `wave`) and Q W^T (tile `wave` when < NRC), kept in registers (W = K when symmetric)
   const int cit = wave / NCT, cjt = wave % NCT;  // the C x C tile of this wavefront
   const int rrt = wave / NCT, rct = wave % NCT;  // the RT x C tile of this wavefront
   f32x4_t accS = {0.f, 0.f, 0.f, 0.f}, accQK = {0.f, 0.f, 0.f, 0.f};
-  if (wave < NCC) accS = mm_tile<float, DK>(accS, sK, LDK, cit * 16, sKw, LDK, cjt * 16);
-  if (wave < NRC) accQK = mm_tile<float, DK>(accQK, sQ, LDK, rrt * 16, sKw, LDK, rct * 16);
+  if (wave < NCC) accS = mm_tile<OT, DK>(accS, sK, LDK, cit * 16, sKw, LDK, cjt * 16);
+  if (wave < NRC) accQK = mm_tile<OT, DK>(accQK, sQ, LDK, rrt * 16, sKw, LDK, rct * 16);
 
   f32x4_t aXH[KPW], aY[KPW], aA[QPW];
   f32x4_t aP = {0.f, 0.f, 0.f, 0.f}, aTb = {0.f, 0.f, 0.f, 0.f};
@@ -683,41 +708,41 @@ __global__ __launch_bounds__(256) void dp_bwd_chunk_kernel(BwdArgs p) {
     const int v0 = vb * BV;
 #pragma unroll
     for (int i = 0; i < EH; ++i) {
-      sH0[hd * LDB + hn + i] = nh0[i];
-      sdHe[hd * LDB + hn + i] = ndh[i];
+      sH0[hd * LDB + hn + i] = from_f32<OT>(nh0[i]);
+      sdHe[hd * LDB + hn + i] = from_f32<OT>(ndh[i]);
       hdot = fmaf(nh0[i], ndh[i], hdot);
     }
 #pragma unroll
     for (int i = 0; i < EV; ++i) {
-      sV[vr * LDB + vn + i] = nv[i];
-      sdUp[vr * LDB + vn + i] = ndu[i];
+      sV[vr * LDB + vn + i] = from_f32<OT>(nv[i]);
+      sdUp[vr * LDB + vn + i] = from_f32<OT>(ndu[i]);
     }
 #pragma unroll
-    for (int i = 0; i < EO; ++i) sdO[orr * LDB + on + i] = ndo[i];
+    for (int i = 0; i < EO; ++i) sdO[orr * LDB + on + i] = from_f32<OT>(ndo[i]);
     __syncthreads();
     if (vb + 1 < p.nvb) prefetch(vb + 1);  // lands while this block is computed
     if (wave < NCT) {
       // X = V - diag(e^G) K H0
       const int ct = wave;
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mm_tile_tb<float, DK>(acc, sK, LDK, ct * 16, sH0, LDB, 0);
+      acc = mm_tile_tb<OT, DK>(acc, sK, LDK, ct * 16, sH0, LDB, 0);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = ct * 16 + 4 * grp + e;
-        const float x = sV[r * LDB + col] - sEG[r] * acc[e];
-        sX[r * LDB + col] = x;
-        sXb[r * LDB + col] = sB[r] * x;
+        const float x = to_f32(sV[r * LDB + col]) - sEG[r] * acc[e];
+        sX[r * LDB + col] = from_f32<OT>(x);
+        sXb[r * LDB + col] = from_f32<OT>(sB[r] * x);
       }
     } else if (wave < 2 * NCT) {
       // dX = diag(beta) T^T dUp, which is dv
       const int ct = wave - NCT;
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mm_tile_tt<C>(acc, sT, LDC, ct * 16, sdUp, LDB, 0);
+      acc = mm_tile_tt<OT, C>(acc, sT, LDC, ct * 16, sdUp, LDB, 0);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int j = ct * 16 + 4 * grp + e;
         const float dx = sB[j] * acc[e];
-        sdX[j * LDB + col] = dx;
+        sdX[j * LDB + col] = from_f32<OT>(dx);
         if (sRow[j] >= 0) p.dv[sRow[j] * p.dvd + v0 + col] = dx;
       }
     }
@@ -726,9 +751,9 @@ __global__ __launch_bounds__(256) void dp_bwd_chunk_kernel(BwdArgs p) {
       // Up = T (beta X)
       const int ct = wave;
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mm_tile_tb<float, C>(acc, sT, LDC, ct * 16, sXb, LDB, 0);
+      acc = mm_tile_tb<OT, C>(acc, sT, LDC, ct * 16, sXb, LDB, 0);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sUp[(ct * 16 + 4 * grp + e) * LDB + col] = acc[e];
+      for (int e = 0; e < 4; ++e) sUp[(ct * 16 + 4 * grp + e) * LDB + col] = from_f32<OT>(acc[e]);
     }
     __syncthreads();
 #pragma unroll
@@ -736,8 +761,8 @@ __global__ __launch_bounds__(256) void dp_bwd_chunk_kernel(BwdArgs p) {
       const int tile = wave + 4 * u;
       if (tile < NKD) {
         const int ct = tile / NDT, dt = tile % NDT;
-        aXH[u] = mm_tile<float, BV>(aXH[u], sdX, LDB, ct * 16, sH0, LDB, dt * 16);
-        aY[u] = mm_tile<float, BV>(aY[u], sUp, LDB, ct * 16, sdHe, LDB, dt * 16);
+        aXH[u] = mm_tile<OT, BV>(aXH[u], sdX, LDB, ct * 16, sH0, LDB, dt * 16);
+        aY[u] = mm_tile<OT, BV>(aY[u], sUp, LDB, ct * 16, sdHe, LDB, dt * 16);
       }
     }
 #pragma unroll
@@ -745,11 +770,11 @@ __global__ __launch_bounds__(256) void dp_bwd_chunk_kernel(BwdArgs p) {
       const int tile = wave + 4 * u;
       if (tile < NQD) {
         const int rt = tile / NDT, dt = tile % NDT;
-        aA[u] = mm_tile<float, BV>(aA[u], sdO, LDB, rt * 16, sH0, LDB, dt * 16);
+        aA[u] = mm_tile<OT, BV>(aA[u], sdO, LDB, rt * 16, sH0, LDB, dt * 16);
       }
     }
-    if (wave < NRC) aP = mm_tile<float, BV>(aP, sdO, LDB, rrt * 16, sUp, LDB, rct * 16);
-    if (wave < NCC) aTb = mm_tile<float, BV>(aTb, sdUp, LDB, cit * 16, sX, LDB, cjt * 16);
+    if (wave < NRC) aP = mm_tile<OT, BV>(aP, sdO, LDB, rrt * 16, sUp, LDB, rct * 16);
+    if (wave < NCC) aTb = mm_tile<OT, BV>(aTb, sdUp, LDB, cit * 16, sX, LDB, cjt * 16);
     __syncthreads();  // the next block overwrites the block buffers
   }
 
@@ -766,8 +791,8 @@ __global__ __launch_bounds__(256) void dp_bwd_chunk_kernel(BwdArgs p) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = cit * 16 + 4 * grp + e;
-      cs = fmaf(aTb[e], sT[i * LDC + j], cs);
-      sA[i * LDC + j] = aTb[e] * sB[j];
+      cs = fmaf(aTb[e], to_f32(sT[i * LDC + j]), cs);
+      sA[i * LDC + j] = from_f32<OT>(aTb[e] * sB[j]);
     }
     cs = sum_groups(cs);
     if (grp == 0) atomicAdd(&sDB[j], cs);
@@ -776,15 +801,15 @@ __global__ __launch_bounds__(256) void dp_bwd_chunk_kernel(BwdArgs p) {
   // T^T dT -> sW
   if (wave < NCC) {
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    acc = mm_tile_tt<C>(acc, sT, LDC, cit * 16, sA, LDC, cjt * 16);
+    acc = mm_tile_tt<OT, C>(acc, sT, LDC, cit * 16, sA, LDC, cjt * 16);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sW[(cit * 16 + 4 * grp + e) * LDC + cjt * 16 + col] = acc[e];
+    for (int e = 0; e < 4; ++e) sW[(cit * 16 + 4 * grp + e) * LDC + cjt * 16 + col] = from_f32<OT>(acc[e]);
   }
   __syncthreads();
   // F = -(T^T dT) T^T (strictly lower); the M terms of dbeta and dG; Z -> sA
   if (wave < NCC) {
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    acc = mm_tile<float, C>(acc, sW, LDC, cit * 16, sT, LDC, cjt * 16);
+    acc = mm_tile<OT, C>(acc, sW, LDC, cit * 16, sT, LDC, cjt * 16);
     const int j = cjt * 16 + col;
     float csum = 0.f;
 #pragma unroll
@@ -802,7 +827,7 @@ __global__ __launch_bounds__(256) void dp_bwd_chunk_kernel(BwdArgs p) {
         atomicAdd(&sDG[i], rg);
       }
       csum += zs;
-      sA[i * LDC + j] = z;
+      sA[i * LDC + j] = from_f32<OT>(z);
     }
     csum = sum_groups(csum);
     if (grp == 0) atomicAdd(&sDG[j], -csum);
@@ -821,7 +846,7 @@ __global__ __launch_bounds__(256) void dp_bwd_chunk_kernel(BwdArgs p) {
       const float rs = sum16(pr);
       if (col == 0 && l >= 0) atomicAdd(&sDG[l], rs);
       csum += pr;
-      sGm[r * LDC + j] = gm;
+      sGm[r * LDC + j] = from_f32<OT>(gm);
     }
     csum = sum_groups(csum);
     if (grp == 0) atomicAdd(&sDG[j], -csum);
@@ -835,14 +860,14 @@ __global__ __launch_bounds__(256) void dp_bwd_chunk_kernel(BwdArgs p) {
     if (tile < NQD) {
       const int rt = tile / NDT, dt = tile % NDT;
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      acc = mm_tile_tb<float, C>(acc, sGm, LDC, rt * 16, sKw, LDK, dt * 16);
+      acc = mm_tile_tb<OT, C>(acc, sGm, LDC, rt * 16, sKw, LDK, dt * 16);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = rt * 16 + 4 * grp + e, d = dt * 16 + col;
         const int l = sLoc[r];
         const float el = l >= 0 ? sEG[l] : 0.f;
         const float a = aA[u][e];
-        const float qd = sum16(sQ[r * LDK + d] * a * el);
+        const float qd = sum16(to_f32(sQ[r * LDK + d]) * a * el);
         if (l >= 0) {
           dqp[sTok[r] * DK + d] = el * a + acc[e];
           if (col == 0) atomicAdd(&sDG[l], qd);
@@ -864,13 +889,13 @@ __global__ __launch_bounds__(256) void dp_bwd_chunk_kernel(BwdArgs p) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
       if constexpr (ASYM) {
         f32x4_t accw = {0.f, 0.f, 0.f, 0.f};
-        accw = mm_tile_tt<RT>(accw, sGm, LDC, ct * 16, sQ, LDK, dt * 16);
-        accw = mm_tile_tt<C>(accw, sA, LDC, ct * 16, sK, LDK, dt * 16);
-        acc = mm_tile_tb<float, C>(acc, sA, LDC, ct * 16, sWk, LDK, dt * 16);
+        accw = mm_tile_tt<OT, RT>(accw, sGm, LDC, ct * 16, sQ, LDK, dt * 16);
+        accw = mm_tile_tt<OT, C>(accw, sA, LDC, ct * 16, sK, LDK, dt * 16);
+        acc = mm_tile_tb<OT, C>(acc, sA, LDC, ct * 16, sWk, LDK, dt * 16);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int j = ct * 16 + 4 * grp + e, d = dt * 16 + col;
-          const float kv = sK[j * LDK + d], wv = sWk[j * LDK + d];
+          const float kv = to_f32(sK[j * LDK + d]), wv = to_f32(sWk[j * LDK + d]);
           const float xh = aXH[u][e], y = aY[u][e];
           const float dk = acc[e] - sEG[j] * xh;
           dkn[u][e] = dk;
@@ -885,13 +910,13 @@ __global__ __launch_bounds__(256) void dp_bwd_chunk_kernel(BwdArgs p) {
           }
         }
       } else {
-        acc = mm_tile_tt<RT>(acc, sGm, LDC, ct * 16, sQ, LDK, dt * 16);
-        acc = mm_tile_tb<float, C>(acc, sA, LDC, ct * 16, sK, LDK, dt * 16);
-        acc = mm_tile_tt<C>(acc, sA, LDC, ct * 16, sK, LDK, dt * 16);
+        acc = mm_tile_tt<OT, RT>(acc, sGm, LDC, ct * 16, sQ, LDK, dt * 16);
+        acc = mm_tile_tb<OT, C>(acc, sA, LDC, ct * 16, sK, LDK, dt * 16);
+        acc = mm_tile_tt<OT, C>(acc, sA, LDC, ct * 16, sK, LDK, dt * 16);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int j = ct * 16 + 4 * grp + e, d = dt * 16 + col;
-          const float kv = sK[j * LDK + d];
+          const float kv = to_f32(sK[j * LDK + d]);
           const float xh = aXH[u][e], y = aY[u][e];
           const float dk = acc[e] - sEG[j] * xh + sEL[j] * y;
           dkn[u][e] = dk;
@@ -924,7 +949,7 @@ __global__ __launch_bounds__(256) void dp_bwd_chunk_kernel(BwdArgs p) {
         const long long rw = sRow[j];
         if (rw >= 0) {
           const float ri = sRinv[j];
-          const float proj = ri < rclamp ? sK[j * LDK + d] * sRD[j] : 0.f;
+          const float proj = ri < rclamp ? to_f32(sK[j * LDK + d]) * sRD[j] : 0.f;
           p.dk[rw * DK + d] = ri * (dkn[u][e] - proj);
         }
       }
@@ -1170,13 +1195,13 @@ hipError_t launch_bwd_form(const FwdArgs& fa, const BwdArgs& a, hipStream_t st) 
       static const bool attr =
           allow_big_lds(reinterpret_cast<const void*>(&dp_bwd_dstate_kernel<T, DK, C, BV, 1, ASYM>));
       (void)attr;
-      constexpr int lds = bwd_dstate_lds_bytes<DK, C, BV, 16, ASYM>();
+      constexpr int lds = bwd_dstate_lds_bytes<typename OpType<T>::type, DK, C, BV, 16, ASYM>();
       hipLaunchKernelGGL((dp_bwd_dstate_kernel<T, DK, C, BV, 1, ASYM>), dim3(nwg), dim3(256), lds, st, a);
     } else {
       static const bool attr =
           allow_big_lds(reinterpret_cast<const void*>(&dp_bwd_dstate_kernel<T, DK, C, BV, 2, ASYM>));
       (void)attr;
-      constexpr int lds = bwd_dstate_lds_bytes<DK, C, BV, 32, ASYM>();
+      constexpr int lds = bwd_dstate_lds_bytes<typename OpType<T>::type, DK, C, BV, 32, ASYM>();
       hipLaunchKernelGGL((dp_bwd_dstate_kernel<T, DK, C, BV, 2, ASYM>), dim3(nwg), dim3(256), lds, st, a);
     }
     const hipError_t e = hipGetLastError();
@@ -1186,12 +1211,12 @@ hipError_t launch_bwd_form(const FwdArgs& fa, const BwdArgs& a, hipStream_t st) 
     if (a.RT == 16) {
       static const bool attr = allow_big_lds(reinterpret_cast<const void*>(&dp_bwd_chunk_kernel<T, DK, C, 1, ASYM>));
       (void)attr;
-      constexpr int lds = bwd_chunk_lds_bytes<DK, C, 16, ASYM>();
+      constexpr int lds = bwd_chunk_lds_bytes<typename OpType<T>::type, DK, C, 16, ASYM>();
       hipLaunchKernelGGL((dp_bwd_chunk_kernel<T, DK, C, 1, ASYM>), dim3((unsigned)nchunks), dim3(256), lds, st, a);
     } else {
       static const bool attr = allow_big_lds(reinterpret_cast<const void*>(&dp_bwd_chunk_kernel<T, DK, C, 2, ASYM>));
       (void)attr;
-      constexpr int lds = bwd_chunk_lds_bytes<DK, C, 32, ASYM>();
+      constexpr int lds = bwd_chunk_lds_bytes<typename OpType<T>::type, DK, C, 32, ASYM>();
       hipLaunchKernelGGL((dp_bwd_chunk_kernel<T, DK, C, 2, ASYM>), dim3((unsigned)nchunks), dim3(256), lds, st, a);
     }
     return hipGetLastError();
