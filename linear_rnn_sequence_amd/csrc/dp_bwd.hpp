@@ -19,12 +19,14 @@
 //   dTb = dUp X^T,  dT = dTb diag(beta),  dM = -T^T dT T^T  (strictly lower)
 //
 // and the key, query, beta and log-gate terms collected in
-// dp_bwd_chunk_kernel.  Four launches:
+// dp_bwd_chunk_kernel.  Three launches:
 //   dp_ut_kernel<.., float, false>  T (fp32) and (1/|k|, G) per chunk
-//   dp_bwd_states_kernel   sequential over chunks per (head, value block):
-//                          the forward's chunk-start states H0 -> workspace
-//   dp_bwd_dstate_kernel   sequential over chunks in reverse: dH1 and dUp
-//                          of every chunk -> workspace, dH0 of chunk 0 -> dh0
+//   dp_bwd_scans_kernel    the two sequential scans side by side, one role
+//                          per workgroup: sequential over chunks in reverse,
+//                          dH1 and dUp of every chunk -> workspace and dH0 of
+//                          chunk 0 -> dh0 (bwd_dstate_body); sequential over
+//                          chunks, the forward's chunk-start states H0 ->
+//                          workspace (bwd_states_body)
 //   dp_bwd_chunk_kernel    one workgroup per chunk, all in parallel: dq, dk,
 //                          dv, dbeta, dg from H0, dH1, dUp and the chunk
 // The state and its gradient are kept in fp32, and every product accumulates
@@ -244,28 +246,42 @@ struct BwdChunkCommon {
 };
 
 // ---------------------------------------------------------------------------
-// dp_bwd_states_kernel: the forward's chunk-start states, one workgroup per
-// (head, block of BV value columns), sequential over the chunks.  The state
-// lives in LDS (fp32); each wavefront updates the tiles it owns.
-template <typename T, int DK, int C, int BV, bool ASYM = false>
-__global__ __launch_bounds__(256) void dp_bwd_states_kernel(BwdArgs p) {
+// The forward's chunk-start states: one workgroup per (head, block of BV value
+// columns), sequential over the chunks.  Each wavefront keeps the fp32 state
+// tiles it owns in registers; LDS holds their operand copy.
+template <typename T, int DK, int C, int BV, bool ASYM>
+__host__ __device__ constexpr int bwd_states_lds_bytes() {
+  using OT = typename OpType<T>::type;
+  constexpr int LDK = bwd_ld<OT>(DK), LDC = bwd_ld<OT>(C), LDB = bwd_ld<OT>(BV), LDF = BV + 4;
+  return ((ASYM ? 2 : 1) * C * LDK + C * LDC + DK * LDB + 2 * C * LDB) * (int)sizeof(OT) + (C * LDF + 3 * C) * 4;
+}
+
+template <typename T, int DK, int C, int BV, bool ASYM>
+__device__ __forceinline__ void bwd_states_body(const BwdArgs& p, unsigned char* smb, const int wg) {
   using OT = typename OpType<T>::type;  // MFMA operand type
   constexpr int LDK = bwd_ld<OT>(DK), LDC = bwd_ld<OT>(C), LDB = bwd_ld<OT>(BV), LDF = BV + 4;
   constexpr int NCT = C / 16, NDT = DK / 16, NVT = BV / 16;
+  constexpr int NHT = NDT * NVT, HPW = (NHT + 3) / 4;  // state tiles, per wavefront
   using Common = BwdChunkCommon<T, DK, C, ASYM>;
   constexpr int TPR = Common::TPR, EV = BV / TPR;
   static_assert(EV >= 1 && BV % TPR == 0, "value slice");
-  // sH: the fp32 state; sHo its operand copy; sV the values (fp32)
-  __shared__ __align__(16) OT sK[C * LDK], sT[C * LDC], sHo[DK * LDB], sXb[C * LDB], sU[C * LDB];
-  __shared__ __align__(16) float sH[DK * LDF], sV[C * LDF];
-  __shared__ __align__(16) OT sW[ASYM ? C * LDK : 1];  // ASYM: write keys
-  OT* const sKw = ASYM ? sW : sK;                      // the keys the state update writes with
-  __shared__ float sB[C], sEG[C], sEL[C];
+  OT* sK = reinterpret_cast<OT*>(smb);  // C x LDK unit read keys
+  OT* sW = sK + C * LDK;                // ASYM: write keys
+  OT* sT = sW + (ASYM ? C * LDK : 0);
+  OT* sHo = sT + C * LDC;  // operand copy of the state
+  OT* sXb = sHo + DK * LDB;
+  OT* sU = sXb + C * LDB;
+  float* sV = reinterpret_cast<float*>(sU + C * LDB);  // the values (fp32)
+  float* sB = sV + C * LDF;
+  float* sEG = sB + C;
+  float* sEL = sEG + C;
+  OT* const sKw = ASYM ? sW : sK;  // the keys the state update writes with
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
-  const int bh = blockIdx.x / p.nvb, vb = blockIdx.x % p.nvb;
+  const int nvb = p.dvd / BV;
+  const int bh = wg / nvb, vb = wg % nvb;
   const int b = bh / p.H, h = bh % p.H;
   const int v0 = vb * BV;
   const T* vp = static_cast<const T*>(p.v);
@@ -286,11 +302,21 @@ __global__ __launch_bounds__(256) void dp_bwd_states_kernel(BwdArgs p) {
       nx.v.zero();
   };
 
-  for (int idx = tid; idx < DK * BV; idx += 256) {
-    const int d = idx / BV, n = idx % BV;
-    const float h0 = p.h0 != nullptr ? p.h0[((long long)bh * DK + d) * p.dvd + v0 + n] : 0.f;
-    sH[d * LDF + n] = h0;
-    sHo[d * LDB + n] = from_f32<OT>(h0);
+  // the fp32 state: tile wave + 4u of the DK x BV block, rows 4 grp + e, column col
+  f32x4_t hacc[HPW];
+#pragma unroll
+  for (int u = 0; u < HPW; ++u) {
+    const int tile = wave + 4 * u;
+    hacc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (tile < NHT) {
+      const int dt = tile / NVT, nt = tile % NVT;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int d = dt * 16 + 4 * grp + e, n = nt * 16 + col;
+        if (p.h0 != nullptr) hacc[u][e] = p.h0[((long long)bh * DK + d) * p.dvd + v0 + n];
+        sHo[d * LDB + n] = from_f32<OT>(hacc[u][e]);
+      }
+    }
   }
   if (p.nc > 0) prefetch(nb0, 0);
   if (p.nc > 1) prefetch(nb1, 1);
@@ -308,11 +334,16 @@ __global__ __launch_bounds__(256) void dp_bwd_states_kernel(BwdArgs p) {
       sEG[tid] = expf(nx.x.g);
       sEL[tid] = expf(nx.x.gl - nx.x.g);
     }
-    // the state at the chunk start
+    // the state at the chunk start, from the tiles each wavefront holds
     float* hdst = p.hs + chunk * DK * p.dvd + v0;
-    for (int idx = tid; idx < DK * BV; idx += 256) {
-      const int d = idx / BV, n = idx % BV;
-      hdst[(long long)d * p.dvd + n] = sH[d * LDF + n];
+#pragma unroll
+    for (int u = 0; u < HPW; ++u) {
+      const int tile = wave + 4 * u;
+      if (tile < NHT) {
+        const int dt = tile / NVT, nt = tile % NVT;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hdst[(long long)(dt * 16 + 4 * grp + e) * p.dvd + nt * 16 + col] = hacc[u][e];
+      }
     }
     __syncthreads();
     if (c + 2 < p.nc) prefetch(nx, c + 2);  // lands while the next two chunks are computed
@@ -342,16 +373,18 @@ __global__ __launch_bounds__(256) void dp_bwd_states_kernel(BwdArgs p) {
     __syncthreads();
     // H = e^{G_C} H + W^T (diag(e^{G_C - G}) Up): each wavefront its own tiles
     const float egl = sEG[C - 1];
-    for (int tile = wave; tile < NDT * NVT; tile += 4) {
-      const int dt = tile / NVT, nt = tile % NVT;
-      f32x4_t acc;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = egl * sH[(dt * 16 + 4 * grp + e) * LDF + nt * 16 + col];
-      acc = mm_tile_tt<OT, C>(acc, sKw, LDK, dt * 16, sU, LDB, nt * 16);
+    for (int u = 0; u < HPW; ++u) {
+      const int tile = wave + 4 * u;
+      if (tile < NHT) {
+        const int dt = tile / NVT, nt = tile % NVT;
+        f32x4_t acc;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sH[(dt * 16 + 4 * grp + e) * LDF + nt * 16 + col] = acc[e];
-        sHo[(dt * 16 + 4 * grp + e) * LDB + nt * 16 + col] = from_f32<OT>(acc[e]);
+        for (int e = 0; e < 4; ++e) acc[e] = egl * hacc[u][e];
+        acc = mm_tile_tt<OT, C>(acc, sKw, LDK, dt * 16, sU, LDB, nt * 16);
+        hacc[u] = acc;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sHo[(dt * 16 + 4 * grp + e) * LDB + nt * 16 + col] = from_f32<OT>(acc[e]);
       }
     }
   };
@@ -362,11 +395,11 @@ __global__ __launch_bounds__(256) void dp_bwd_states_kernel(BwdArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// dp_bwd_dstate_kernel: the reverse chunk scan of the state gradient, one
+// The reverse chunk scan of the state gradient (bwd_dstate_body), one
 // workgroup per (head, block of BV value columns), chunks last to first.
 // Writes dH1 (the gradient of each chunk's end state) and dUp per chunk, and
 // the gradient of the initial state.
-// LDS of dp_bwd_dstate_kernel (dynamic: with the write keys it passes 64 KB):
+// LDS of the state-gradient scan (dynamic: with the write keys it passes 64 KB):
 // the operand buffers in OT, then the fp32 state gradient and the scalars.
 template <typename OT, int DK, int C, int BV, int RT, bool ASYM>
 __host__ __device__ constexpr int bwd_dstate_lds_bytes() {
@@ -376,8 +409,8 @@ __host__ __device__ constexpr int bwd_dstate_lds_bytes() {
          (DK * (BV + 4) + 4 * C) * 4 + RT * 4;
 }
 
-template <typename T, int DK, int C, int BV, int NRT, bool ASYM = false>
-__global__ __launch_bounds__(256) void dp_bwd_dstate_kernel(BwdArgs p) {
+template <typename T, int DK, int C, int BV, int NRT, bool ASYM>
+__device__ __forceinline__ void bwd_dstate_body(const BwdArgs& p, unsigned char* smb, const int wg) {
   using OT = typename OpType<T>::type;  // MFMA operand type
   constexpr int RT = 16 * NRT;
   constexpr int LDK = bwd_ld<OT>(DK), LDC = bwd_ld<OT>(C), LDB = bwd_ld<OT>(BV), LDF = BV + 4;
@@ -385,7 +418,6 @@ __global__ __launch_bounds__(256) void dp_bwd_dstate_kernel(BwdArgs p) {
   using Common = BwdChunkCommon<T, DK, C, ASYM>;
   constexpr int TPQ = 256 / RT, EQ = DK / TPQ, EO = BV / TPQ;  // per readout row
   static_assert(EQ >= 1 && EO >= 1 && DK % TPQ == 0 && BV % TPQ == 0, "readout slices");
-  extern __shared__ __align__(16) unsigned char smb[];
   OT* sK = reinterpret_cast<OT*>(smb);  // C x LDK unit read keys
   OT* sW = sK + C * LDK;                // ASYM: C x LDK write keys
   OT* sQ = sW + (ASYM ? C * LDK : 0);
@@ -407,7 +439,7 @@ __global__ __launch_bounds__(256) void dp_bwd_dstate_kernel(BwdArgs p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
-  const int bh = blockIdx.x / p.nvb, vb = blockIdx.x % p.nvb;
+  const int bh = wg / p.nvb, vb = wg % p.nvb;
   const int b = bh / p.H, h = bh % p.H;
   const int v0 = vb * BV;
   const T* dop = static_cast<const T*>(p.dout);
@@ -544,6 +576,22 @@ __global__ __launch_bounds__(256) void dp_bwd_dstate_kernel(BwdArgs p) {
       p.dh0[((long long)bh * DK + d) * p.dvd + v0 + n] = sdH[d * LDF + n];
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// dp_bwd_scans_kernel: the two sequential scans in one launch.  The reverse
+// scan of dH needs neither the forward's states nor their scan, so the
+// workgroups take one role each and run side by side: the first B*H*(dv/16)
+// the state gradient (16 value columns each, the longer scan, dispatched
+// first), the rest the chunk-start states (BVS value columns each).
+template <typename T, int DK, int C, int BVS, int NRT, bool ASYM>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void dp_bwd_scans_kernel(BwdArgs p) {
+  extern __shared__ __align__(16) unsigned char smb[];
+  const int nd = p.B * p.H * p.nvb;
+  if ((int)blockIdx.x < nd)
+    bwd_dstate_body<T, DK, C, kBwdBV, NRT, ASYM>(p, smb, (int)blockIdx.x);
+  else
+    bwd_states_body<T, DK, C, BVS, ASYM>(p, smb, (int)blockIdx.x - nd);
 }
 
 // ---------------------------------------------------------------------------
@@ -1173,38 +1221,39 @@ hipError_t launch_precond_bwd_dk(const PrecondBwdArgs& a, hipStream_t st) {
 
 // ---------------------------------------------------------------------------
 // Host-side launch of the four kernels.
+template <typename T, int DK, int BVS, int NRT, bool ASYM>
+hipError_t launch_bwd_scans(const BwdArgs& a, hipStream_t st) {
+  using OT = typename OpType<T>::type;
+  constexpr int C = kBwdChunk;
+  constexpr int l1 = bwd_dstate_lds_bytes<OT, DK, C, kBwdBV, 16 * NRT, ASYM>();
+  constexpr int l2 = bwd_states_lds_bytes<T, DK, C, BVS, ASYM>();
+  constexpr int lds = l1 > l2 ? l1 : l2;
+  static const bool attr = allow_big_lds(reinterpret_cast<const void*>(&dp_bwd_scans_kernel<T, DK, C, BVS, NRT, ASYM>));
+  (void)attr;
+  const unsigned nwg = (unsigned)(a.B * a.H * (a.nvb + a.dvd / BVS));
+  hipLaunchKernelGGL((dp_bwd_scans_kernel<T, DK, C, BVS, NRT, ASYM>), dim3(nwg), dim3(256), lds, st, a);
+  return hipGetLastError();
+}
+
 template <typename T, int DK, bool ASYM>
 hipError_t launch_bwd_form(const FwdArgs& fa, const BwdArgs& a, hipStream_t st) {
-  constexpr int C = kBwdChunk, BV = kBwdBV;
+  constexpr int C = kBwdChunk;
   const long long nchunks = (long long)a.B * a.H * a.nc;
   if (nchunks > 0) {
     const int lds = ut_lds_bytes((int)sizeof(T), DK, C, ASYM);
     static const bool attr = allow_big_lds(reinterpret_cast<const void*>(&dp_ut_kernel<T, DK, C, float, false>));
     (void)attr;
     hipLaunchKernelGGL((dp_ut_kernel<T, DK, C, float, false>), dim3((unsigned)nchunks), dim3(kThreads), lds, st, fa);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((dp_bwd_states_kernel<T, DK, C, BV, ASYM>), dim3((unsigned)(a.B * a.H * a.nvb)), dim3(256), 0,
-                       st, a);
-    e = hipGetLastError();
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const unsigned nwg = (unsigned)(a.B * a.H * a.nvb);
-  if (nwg > 0) {
-    if (a.RT == 16) {
-      static const bool attr =
-          allow_big_lds(reinterpret_cast<const void*>(&dp_bwd_dstate_kernel<T, DK, C, BV, 1, ASYM>));
-      (void)attr;
-      constexpr int lds = bwd_dstate_lds_bytes<typename OpType<T>::type, DK, C, BV, 16, ASYM>();
-      hipLaunchKernelGGL((dp_bwd_dstate_kernel<T, DK, C, BV, 1, ASYM>), dim3(nwg), dim3(256), lds, st, a);
-    } else {
-      static const bool attr =
-          allow_big_lds(reinterpret_cast<const void*>(&dp_bwd_dstate_kernel<T, DK, C, BV, 2, ASYM>));
-      (void)attr;
-      constexpr int lds = bwd_dstate_lds_bytes<typename OpType<T>::type, DK, C, BV, 32, ASYM>();
-      hipLaunchKernelGGL((dp_bwd_dstate_kernel<T, DK, C, BV, 2, ASYM>), dim3(nwg), dim3(256), lds, st, a);
-    }
-    const hipError_t e = hipGetLastError();
+  if (a.B * a.H * a.nvb > 0) {
+    // the chunk-start states in blocks of 32 value columns where dv allows
+    hipError_t e;
+    if (a.dvd >= 32)
+      e = a.RT == 16 ? launch_bwd_scans<T, DK, 32, 1, ASYM>(a, st) : launch_bwd_scans<T, DK, 32, 2, ASYM>(a, st);
+    else
+      e = a.RT == 16 ? launch_bwd_scans<T, DK, 16, 1, ASYM>(a, st) : launch_bwd_scans<T, DK, 16, 2, ASYM>(a, st);
     if (e != hipSuccess) return e;
   }
   if (nchunks > 0) {
