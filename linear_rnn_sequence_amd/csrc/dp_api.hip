@@ -744,9 +744,10 @@ int bwd_impl(int elem, const void* q, const void* k, const void* v, const float*
   a.dfinal = dfinal;
   a.wsT = reinterpret_cast<const float*>(ws);
   a.wsS = fa.wsS;
-  a.hs = reinterpret_cast<float*>(ws + w.t + w.s);
-  a.dhe = reinterpret_cast<float*>(ws + w.t + w.s + w.hs);
-  a.dup = reinterpret_cast<float*>(ws + w.t + w.s + w.hs + w.dhe);
+  // (sized for fp32; the bf16 path stores them in fp16 and uses half)
+  a.hs = ws + w.t + w.s;
+  a.dhe = ws + w.t + w.s + w.hs;
+  a.dup = ws + w.t + w.s + w.hs + w.dhe;
   a.dq = dq;
   a.dk = dk_out;
   a.dv = dv_out;

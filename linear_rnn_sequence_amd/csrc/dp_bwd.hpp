@@ -62,9 +62,11 @@ struct BwdArgs {
   const float* dfinal;  // [B, H, dk, dv] or nullptr (zero)
   const float* wsT;     // [B*H*nc][C][C] T (fp32)
   const float2* wsS;    // [B*H*nc][C] (1/|k|, G)
-  float* hs;            // [B*H*nc][dk][dv] chunk-start states
-  float* dhe;           // [B*H*nc][dk][dv] gradients of the chunk-end states
-  float* dup;           // [B*H*nc][C][dv] gradients of the pseudo-values
+  // in the MFMA operand type (the per-chunk kernel's only use of them is as
+  // operands): fp16 for bf16 inputs, fp32 for fp32 inputs
+  void* hs;             // [B*H*nc][dk][dv] chunk-start states
+  void* dhe;            // [B*H*nc][dk][dv] gradients of the chunk-end states
+  void* dup;            // [B*H*nc][C][dv] gradients of the pseudo-values
   float* dq;            // [B, L, H, dk]
   float* dk;            // [B, L, H, n_h, dk]
   float* dv;            // [B, L, H, n_h, dv]
@@ -335,14 +337,15 @@ __device__ __forceinline__ void bwd_states_body(const BwdArgs& p, unsigned char*
       sEL[tid] = expf(nx.x.gl - nx.x.g);
     }
     // the state at the chunk start, from the tiles each wavefront holds
-    float* hdst = p.hs + chunk * DK * p.dvd + v0;
+    OT* hdst = static_cast<OT*>(p.hs) + chunk * DK * p.dvd + v0;
 #pragma unroll
     for (int u = 0; u < HPW; ++u) {
       const int tile = wave + 4 * u;
       if (tile < NHT) {
         const int dt = tile / NVT, nt = tile % NVT;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) hdst[(long long)(dt * 16 + 4 * grp + e) * p.dvd + nt * 16 + col] = hacc[u][e];
+        for (int e = 0; e < 4; ++e)
+          hdst[(long long)(dt * 16 + 4 * grp + e) * p.dvd + nt * 16 + col] = from_f32<OT>(hacc[u][e]);
       }
     }
     __syncthreads();
@@ -501,10 +504,10 @@ __device__ __forceinline__ void bwd_dstate_body(const BwdArgs& p, unsigned char*
       sEL[tid] = expf(nx.x.gl - nx.x.g);
     }
     // the gradient of the chunk's end state
-    float* ddst = p.dhe + chunk * DK * p.dvd + v0;
+    OT* ddst = static_cast<OT*>(p.dhe) + chunk * DK * p.dvd + v0;
     for (int idx = tid; idx < DK * BV; idx += 256) {
       const int d = idx / BV, n = idx % BV;
-      ddst[(long long)d * p.dvd + n] = sdH[d * LDF + n];
+      ddst[(long long)d * p.dvd + n] = sdHo[d * LDB + n];
     }
     __syncthreads();
     if (c > 1) prefetch(nx, c - 2);  // lands while the next two chunks are computed
@@ -532,7 +535,7 @@ __device__ __forceinline__ void bwd_dstate_body(const BwdArgs& p, unsigned char*
         const int j = ct * 16 + 4 * grp + e, n = nt * 16 + col;
         const float du = sEL[j] * acc[e] + acc2[e];
         sdUp[j * LDB + n] = from_f32<OT>(du);
-        p.dup[(chunk * C + j) * p.dvd + v0 + n] = du;
+        static_cast<OT*>(p.dup)[(chunk * C + j) * p.dvd + v0 + n] = from_f32<OT>(du);
       }
     }
     __syncthreads();
@@ -670,9 +673,9 @@ __global__ __launch_bounds__(256) void dp_bwd_chunk_kernel(BwdArgs p) {
   const T* vp = static_cast<const T*>(p.v);
   const T* dop = static_cast<const T*>(p.dout);
   const BwdChunkMeta meta{sRow, sTok, sLoc};
-  const float* hsrc = p.hs + chunk * DK * p.dvd;
-  const float* dhsrc = p.dhe + chunk * DK * p.dvd;
-  const float* dusrc = p.dup + chunk * C * p.dvd;
+  const OT* hsrc = static_cast<const OT*>(p.hs) + chunk * DK * p.dvd;
+  const OT* dhsrc = static_cast<const OT*>(p.dhe) + chunk * DK * p.dvd;
+  const OT* dusrc = static_cast<const OT*>(p.dup) + chunk * C * p.dvd;
   // The next value block's operands, in registers: thread t holds EH
   // consecutive columns of row t / TPH of H0 and dH1, EV of sub-step row
   // t / TPR of V and dUp, and EO of readout row t / TPQ of dO.
@@ -687,9 +690,9 @@ __global__ __launch_bounds__(256) void dp_bwd_chunk_kernel(BwdArgs p) {
   long long otok;
   int oloc;
   bwd_readout(p, b, h, c, C, orr, &otok, &oloc);
-  RawSlice<float, EH> nh0, ndh;
+  RawSlice<OT, EH> nh0, ndh;
   RawSlice<T, EV> nv;
-  RawSlice<float, EV> ndu;
+  RawSlice<OT, EV> ndu;
   RawSlice<T, EO> ndo;
   auto prefetch = [&](int vb) {
     const int v0 = vb * BV;
