@@ -288,12 +288,13 @@ __device__ __forceinline__ void bwd_states_body(const BwdArgs& p, unsigned char*
   const int v0 = vb * BV;
   const T* vp = static_cast<const T*>(p.v);
 
-  // the operands of the next two chunks, in registers (two buffers, used alternately)
+  // the operands of the next chunk, in registers (one chunk of this scan is
+  // long enough to cover the loads)
   struct Next {
     Common x;
     RawSlice<T, EV> v;
   };
-  Next nb0, nb1;
+  Next nb;
   auto prefetch = [&](Next& nx, int c) {
     const long long chunk = (long long)bh * p.nc + c;
     nx.x.load(p, b, h, c, chunk);
@@ -320,8 +321,7 @@ __device__ __forceinline__ void bwd_states_body(const BwdArgs& p, unsigned char*
       }
     }
   }
-  if (p.nc > 0) prefetch(nb0, 0);
-  if (p.nc > 1) prefetch(nb1, 1);
+  if (p.nc > 0) prefetch(nb, 0);
   auto body = [&](Next& nx, int c) {
     const long long chunk = (long long)bh * p.nc + c;
     __syncthreads();  // the previous chunk is done with every buffer
@@ -349,7 +349,7 @@ __device__ __forceinline__ void bwd_states_body(const BwdArgs& p, unsigned char*
       }
     }
     __syncthreads();
-    if (c + 2 < p.nc) prefetch(nx, c + 2);  // lands while the next two chunks are computed
+    if (c + 1 < p.nc) prefetch(nx, c + 1);  // lands while this chunk is computed
     // beta X = beta (V - diag(e^G) K H0)
     for (int tile = wave; tile < NCT * NVT; tile += 4) {
       const int ct = tile / NVT, nt = tile % NVT;
@@ -391,10 +391,7 @@ __device__ __forceinline__ void bwd_states_body(const BwdArgs& p, unsigned char*
       }
     }
   };
-  for (int c = 0; c < p.nc; c += 2) {
-    body(nb0, c);
-    if (c + 1 < p.nc) body(nb1, c + 1);
-  }
+  for (int c = 0; c < p.nc; ++c) body(nb, c);
 }
 
 // ---------------------------------------------------------------------------
@@ -448,7 +445,8 @@ __device__ __forceinline__ void bwd_dstate_body(const BwdArgs& p, unsigned char*
   const T* dop = static_cast<const T*>(p.dout);
   const T* qp = static_cast<const T*>(p.q);
 
-  // the operands of the next two chunks, in registers (two buffers, used alternately)
+  // the operands of the next chunk, in registers (one chunk of this scan is
+  // long enough to cover the loads)
   struct Next {
     Common x;
     RawSlice<T, EQ> q;
@@ -456,7 +454,7 @@ __device__ __forceinline__ void bwd_dstate_body(const BwdArgs& p, unsigned char*
     int loc;
     float g;  // G at the readout row's sub-step
   };
-  Next nb0, nb1;
+  Next nb;
   auto prefetch = [&](Next& nx, int c) {
     const long long chunk = (long long)bh * p.nc + c;
     nx.x.load(p, b, h, c, chunk);
@@ -479,8 +477,7 @@ __device__ __forceinline__ void bwd_dstate_body(const BwdArgs& p, unsigned char*
     sdH[d * LDF + n] = x;
     sdHo[d * LDB + n] = from_f32<OT>(x);
   }
-  if (p.nc > 0) prefetch(nb0, p.nc - 1);
-  if (p.nc > 1) prefetch(nb1, p.nc - 2);
+  if (p.nc > 0) prefetch(nb, p.nc - 1);
   auto body = [&](Next& nx, int c) {
     const long long chunk = (long long)bh * p.nc + c;
     __syncthreads();  // the previous chunk is done with every buffer
@@ -510,7 +507,7 @@ __device__ __forceinline__ void bwd_dstate_body(const BwdArgs& p, unsigned char*
       ddst[(long long)d * p.dvd + n] = sdHo[d * LDB + n];
     }
     __syncthreads();
-    if (c > 1) prefetch(nx, c - 2);  // lands while the next two chunks are computed
+    if (c > 0) prefetch(nx, c - 1);  // lands while this chunk is computed
     // P = masked, gated scores (RT x C)
     for (int tile = wave; tile < NRT * NCT; tile += 4) {
       const int rt = tile / NCT, ct = tile % NCT;
@@ -568,10 +565,7 @@ __device__ __forceinline__ void bwd_dstate_body(const BwdArgs& p, unsigned char*
       }
     }
   };
-  for (int c = p.nc - 1; c >= 0; c -= 2) {
-    body(nb0, c);
-    if (c > 0) body(nb1, c - 1);
-  }
+  for (int c = p.nc - 1; c >= 0; --c) body(nb, c);
   __syncthreads();
   if (p.dh0 != nullptr) {
     for (int idx = tid; idx < DK * BV; idx += 256) {
