@@ -791,17 +791,23 @@ hipError_t dispatch_precond_bwd(int elem, int dk, const dp::PrecondBwdArgs& a, h
 }
 
 // Gradient of phase 1: the workspace holds d (B H dk f32), the trajectory of
-// d (B L H dk f32) and the write keys the forward emits again (B L H dk
-// elements of the input type; sized for fp32).
+// d (B L H dk f32), the write keys the forward emits again (B L H dk elements
+// of the input type; sized for fp32), then for the reverse scan the
+// projection mask (B L H dk bytes), the per-token factors (B L H float4) and
+// the gradient each token receives (B L H dk f32).
 struct PrecondBwdWs {
-  size_t d, dtr, kt, total;
+  size_t d, dtr, kt, msk, fac, gin, total;
 };
 PrecondBwdWs precond_bwd_ws(int B, int H, int L, int dk) {
   PrecondBwdWs w;
+  const size_t n = (size_t)B * L * H;
   w.d = align_up((size_t)B * H * dk * 4, kWsAlign);
-  w.dtr = align_up((size_t)B * L * H * dk * 4, kWsAlign);
+  w.dtr = align_up(n * dk * 4, kWsAlign);
   w.kt = w.dtr;
-  w.total = w.d + w.dtr + w.kt;
+  w.msk = align_up(n * dk, kWsAlign);
+  w.fac = align_up(n * 16, kWsAlign);
+  w.gin = w.dtr;
+  w.total = w.d + w.dtr + w.kt + w.msk + w.fac + w.gin;
   return w;
 }
 
@@ -869,6 +875,9 @@ int precond_bwd_impl(int elem, const void* k, const float* beta, const float* re
   g.dbeta = dbeta;
   g.dret = dret;
   g.dd0 = dd0;
+  g.msk = reinterpret_cast<unsigned char*>(ws + w.d + w.dtr + w.kt);
+  g.fac = reinterpret_cast<float4*>(ws + w.d + w.dtr + w.kt + w.msk);
+  g.gin = reinterpret_cast<float*>(ws + w.d + w.dtr + w.kt + w.msk + w.fac);
   g.B = B;
   g.H = H;
   g.L = L;

@@ -1024,25 +1024,29 @@ __global__ __launch_bounds__(256) void dp_bwd_chunk_kernel(BwdArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// dp_precond_bwd_kernel: gradient of OSDN phase 1 (OSDN study notes sec. 2.5,
-// closing paragraph: the write key kt_t = d_t o kh_t passes its gradient into
-// d_t and k_t, and the gradient of d runs back through the recursion of
-// sec. 2.4, with the retention of sec. 2.6 and the beta-free step of
-// sec. 2.7).  Per token, with s = kh o kh, n = sum s, nb = max(n, eps),
-// a = bu <d, s>, coef = eta bu (1 - a) / nb, x = r d + coef s and the
-// gradient gd' on d_{t+1}:
+// Gradient of OSDN phase 1 (OSDN study notes sec. 2.5, closing paragraph: the
+// write key kt_t = d_t o kh_t passes its gradient into d_t and k_t, and the
+// gradient of d runs back through the recursion of sec. 2.4, with the
+// retention of sec. 2.6 and the beta-free step of sec. 2.7).  Per token, with
+// s = kh o kh, n = sum s, nb = max(n, eps), a = bu <d, s>,
+// coef = eta bu (1 - a) / nb, x = r d + coef s and the gradient gd' on d_{t+1}:
 //   gx  = gd' where dmin <= x <= dmax (else 0)
 //   gd  = r gx - (eta bu^2 / nb) <gx, s> s + kh o gkt
 //   gr  = <gx, d>,   gbu = <gx, s> eta (1 - 2a) / nb
 //   gs  = coef gx + <gx, s> (-(eta bu^2 / nb) d - [n > eps] coef / nb)
 //   gkh = 2 kh o gs + d o gkt,  then the normalisation kh = k / max(|k|, 1e-6)
+// Only gd runs through the tokens, so three launches share the work:
+//   dp_precond_bwd_factors_kernel (parallel over tokens): the projection mask
+//     of every (token, coordinate) and the factors (1/|k|, r, eta bu^2 / nb);
+//   dp_precond_bwd_chain_kernel (sequential per head, last token first): the
+//     chain alone, gx, <gx, s> (one head sum) and gd, storing the gradient each
+//     token receives;
+//   dp_precond_bwd_grads_kernel (parallel over tokens): the key, beta and
+//     retention gradients of every token from the gradient it received.
 // The lane layout is the forward's (LPH lanes per head, EPL coordinates per
-// lane); tokens run last to first in blocks of PB.  Everything but gd is
-// formed for a whole block first (two head sums per token, off the
-// dependent chain); the chain itself is gx, <gx, s>, gd: one head sum per
-// token, as in the forward.  d_t comes from the trajectory the forward kernel
-// stored.  dk and dbeta are accumulated into (they already hold the write-key
-// forward's gradients), dret and dd0 written.
+// lane).  d_t comes from the trajectory the forward kernel stored.  dk and
+// dbeta are accumulated into (they already hold the write-key forward's
+// gradients), dret and dd0 written.
 struct PrecondBwdArgs {
   const void* k;          // [B, L, H, dk] raw keys
   const float* beta;      // [B, L, H]
@@ -1054,141 +1058,163 @@ struct PrecondBwdArgs {
   float* dbeta;           // [B, L, H], accumulated into
   float* dret;            // [B, L, H] or nullptr
   float* dd0;             // [B, H, dk] or nullptr
+  unsigned char* msk;     // [B, L, H, dk] 1 where the token's step stays inside the box
+  float4* fac;            // [B, L, H] (1/max(|k|, 1e-6), r, eta bu^2 / nb, 0)
+  float* gin;             // [B, L, H, dk] the gradient on d_{t+1} that token t receives
   int B, H, L, beta_aware;
   float eta, dmin, dmax, eps;
 };
 
-template <typename T, int DK>
-__global__ __launch_bounds__(64) void dp_precond_bwd_kernel(PrecondBwdArgs p) {
-  constexpr int LPH = DK < 64 ? DK : 64;  // lanes per head
-  constexpr int EPL = DK / LPH;           // coordinates per lane (1 or 2)
-  constexpr int HPW = 64 / LPH;           // heads per wavefront
-  constexpr int PB = 8;                   // tokens per block
+constexpr int kP1Tokens = 64;  // tokens per workgroup of the two parallel kernels
+
+// The per-token factors of the step, as the forward forms them.
+template <int LPH, int EPL>
+struct P1Tok {
+  float kh[EPL], sq[EPL], rinv, coef, c2, fb, cn;
+  bool tiny;
+};
+template <typename T, int LPH, int EPL>
+__device__ __forceinline__ P1Tok<LPH, EPL> p1_token(const T (&k)[EPL], const float (&d)[EPL], float beta,
+                                                    const PrecondBwdArgs& p) {
+  P1Tok<LPH, EPL> o;
+  float n2 = 0.f;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) n2 = fmaf(to_f32(k[e]), to_f32(k[e]), n2);
+  n2 = head_sum<LPH>(n2);
+  o.rinv = __builtin_amdgcn_rsqf(fmaxf(n2, 1e-12f));  // 1 / max(|k|, 1e-6)
+  o.tiny = !(n2 > 1e-12f);
+  const float ns = n2 * o.rinv * o.rinv;  // |kh|^2
+  float ds = 0.f;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    o.kh[e] = to_f32(k[e]) * o.rinv;
+    o.sq[e] = o.kh[e] * o.kh[e];
+    ds = fmaf(d[e], o.sq[e], ds);
+  }
+  ds = head_sum<LPH>(ds);
+  const float bu = p.beta_aware ? clamp_keep_nan(beta, 0.f, 2.f) : 1.f;
+  const float a = bu * ds;
+  const float rn = __builtin_amdgcn_rcpf(fmaxf(ns, p.eps));
+  o.coef = p.eta * bu * (1.f - a) * rn;
+  o.c2 = p.eta * bu * bu * rn;
+  o.fb = p.eta * (1.f - 2.f * a) * rn;
+  o.cn = ns > p.eps ? o.coef * rn : 0.f;
+  return o;
+}
+
+// Lane geometry shared by the three kernels: HPW heads per wavefront.
+template <int DK>
+struct P1Lanes {
+  static constexpr int LPH = DK < 64 ? DK : 64, EPL = DK / LPH, HPW = 64 / LPH;
   static_assert(EPL == 1 || EPL == 2, "coordinates per lane");
-  const int lane = threadIdx.x & 63;
-  const int sl = lane % LPH;
+};
+
+template <typename T, int DK>
+__global__ __launch_bounds__(64) void dp_precond_bwd_factors_kernel(PrecondBwdArgs p) {
+  using G = P1Lanes<DK>;
+  constexpr int LPH = G::LPH, EPL = G::EPL, HPW = G::HPW;
+  const int lane = threadIdx.x & 63, sl = lane % LPH;
+  const int nblk = (p.L + kP1Tokens - 1) / kP1Tokens;
+  const long long nbh = (long long)p.B * p.H;
+  const long long bh_raw = (long long)(blockIdx.x / nblk) * HPW + lane / LPH;
+  const int t0 = (int)(blockIdx.x % nblk) * kP1Tokens;
+  const bool active = bh_raw < nbh;
+  const long long bh = active ? bh_raw : 0;
+  const int b = (int)(bh / p.H), h = (int)(bh % p.H);
+  const long long row0 = (long long)b * p.L * p.H + h, kstride = (long long)p.H * DK;
+  const T* kp = static_cast<const T*>(p.k) + row0 * DK + sl * EPL;
+  const float* dtp = p.dtr + row0 * DK + sl * EPL;
+  const int t1 = min(t0 + kP1Tokens, p.L);
+#pragma unroll 4
+  for (int t = t0; t < t1; ++t) {
+    T kv[EPL];
+    float dv[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      kv[e] = kp[t * kstride + e];
+      dv[e] = dtp[t * kstride + e];
+    }
+    const long long rw = row0 + (long long)t * p.H;
+    const float r = p.ret != nullptr ? p.ret[rw] : 1.f;
+    const P1Tok<LPH, EPL> f = p1_token<T, LPH, EPL>(kv, dv, p.beta[rw], p);
+    if (active) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const float x = fmaf(f.coef, f.sq[e], r * dv[e]);
+        p.msk[rw * DK + sl * EPL + e] = (x >= p.dmin && x <= p.dmax) ? 1 : 0;
+      }
+      if (sl == 0) p.fac[rw] = make_float4(f.rinv, r, f.c2, 0.f);
+    }
+  }
+}
+
+template <typename T, int DK>
+__global__ __launch_bounds__(64) void dp_precond_bwd_chain_kernel(PrecondBwdArgs p) {
+  using G = P1Lanes<DK>;
+  constexpr int LPH = G::LPH, EPL = G::EPL, HPW = G::HPW;
+  constexpr int PB = 16;  // tokens per block (<= LPH: lane j of a head holds token j's factors)
+  static_assert(PB <= LPH, "one factor lane per token");
+  const int lane = threadIdx.x & 63, sl = lane % LPH, hl = lane - sl;
   const long long nbh = (long long)p.B * p.H;
   const long long bh_raw = (long long)blockIdx.x * HPW + lane / LPH;
   const bool active = bh_raw < nbh;
   const long long bh = active ? bh_raw : 0;
   const int b = (int)(bh / p.H), h = (int)(bh % p.H);
-  const long long row0 = (long long)b * p.L * p.H + h;  // token t: row row0 + t H
-  const long long kstride = (long long)p.H * DK;
+  const long long row0 = (long long)b * p.L * p.H + h, kstride = (long long)p.H * DK;
   const T* kp = static_cast<const T*>(p.k) + row0 * DK + sl * EPL;
-  const float* dtp = p.dtr + row0 * DK + sl * EPL;
   const float* gkp = p.dkt + row0 * DK + sl * EPL;
-  float* dkp = p.dk + row0 * DK + sl * EPL;
+  const unsigned char* mp = p.msk + row0 * DK + sl * EPL;
+  float* gip = p.gin + row0 * DK + sl * EPL;
 
   float gd[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) gd[e] = p.dd_final != nullptr ? p.dd_final[bh * DK + sl * EPL + e] : 0.f;
 
-  // one block's inputs, and the values dk and dbeta already hold (the adds
-  // below then store without waiting on a read)
   struct Blk {
     T k[PB][EPL];
-    float d[PB][EPL], gk[PB][EPL], dk0[PB][EPL], beta[PB], ret[PB], db0[PB];
+    float gk[PB][EPL];
+    unsigned char m[PB][EPL];
+    float4 f;  // lane j of the head: token t0 + j's factors
   };
   auto load = [&](int t0, Blk& r) {
 #pragma unroll
     for (int i = 0; i < PB; ++i) {
       const int t = t0 + i;
-      if (t < p.L) {
-        __builtin_memcpy(r.k[i], __builtin_assume_aligned(kp + t * kstride, EPL * sizeof(T)), EPL * sizeof(T));
+      const bool ok = t < p.L;
+      const long long o = (long long)(ok ? t : 0) * kstride;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          r.d[i][e] = dtp[t * kstride + e];
-          r.gk[i][e] = gkp[t * kstride + e];
-          r.dk0[i][e] = dkp[t * kstride + e];
-        }
-        r.beta[i] = p.beta[row0 + (long long)t * p.H];
-        r.ret[i] = p.ret != nullptr ? p.ret[row0 + (long long)t * p.H] : 1.f;
-        r.db0[i] = p.dbeta[row0 + (long long)t * p.H];
-      } else {
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          r.k[i][e] = T{};
-          r.d[i][e] = 0.f;
-          r.gk[i][e] = 0.f;
-          r.dk0[i][e] = 0.f;
-        }
-        r.beta[i] = 0.f;
-        r.ret[i] = 1.f;
-        r.db0[i] = 0.f;
+      for (int e = 0; e < EPL; ++e) {
+        r.k[i][e] = kp[o + e];
+        r.gk[i][e] = gkp[o + e];
+        r.m[i][e] = mp[o + e];
       }
     }
+    const int tj = t0 + (sl < PB ? sl : 0);
+    r.f = p.fac[row0 + (long long)(tj < p.L ? tj : 0) * p.H];
   };
   auto run_block = [&](const Blk& c, int t0) {
-    // the parts that do not depend on the incoming gradient
-    float kh[PB][EPL], sq[PB][EPL], msk[PB][EPL], rinv[PB], c2[PB], coef[PB], fb[PB], cn[PB];
-    bool tiny[PB];
-#pragma unroll
-    for (int i = 0; i < PB; ++i) {
-      float n2 = 0.f;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) n2 = fmaf(to_f32(c.k[i][e]), to_f32(c.k[i][e]), n2);
-      n2 = head_sum<LPH>(n2);
-      rinv[i] = __builtin_amdgcn_rsqf(fmaxf(n2, 1e-12f));  // 1 / max(|k|, 1e-6)
-      tiny[i] = !(n2 > 1e-12f);
-      const float ns = n2 * rinv[i] * rinv[i];  // |kh|^2, as the forward forms it
-      float ds = 0.f;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        kh[i][e] = to_f32(c.k[i][e]) * rinv[i];
-        sq[i][e] = kh[i][e] * kh[i][e];
-        ds = fmaf(c.d[i][e], sq[i][e], ds);
-      }
-      ds = head_sum<LPH>(ds);
-      const float bu = p.beta_aware ? clamp_keep_nan(c.beta[i], 0.f, 2.f) : 1.f;
-      const float a = bu * ds;
-      const float rn = __builtin_amdgcn_rcpf(fmaxf(ns, p.eps));
-      coef[i] = p.eta * bu * (1.f - a) * rn;
-      c2[i] = p.eta * bu * bu * rn;
-      fb[i] = p.eta * (1.f - 2.f * a) * rn;
-      cn[i] = ns > p.eps ? coef[i] * rn : 0.f;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        const float x = fmaf(coef[i], sq[i][e], c.ret[i] * c.d[i][e]);
-        msk[i][e] = (x >= p.dmin && x <= p.dmax) ? 1.f : 0.f;
-      }
-    }
-    // the dependent chain, last token first, with each token's outputs
 #pragma unroll
     for (int i = PB - 1; i >= 0; --i) {
       const int t = t0 + i;
       if (t < p.L) {
-        float gx[EPL], gxs = 0.f, gr = 0.f;
+        const float rinv = __shfl(c.f.x, hl + i), rt = __shfl(c.f.y, hl + i), c2 = __shfl(c.f.z, hl + i);
+        float kh[EPL], sq[EPL], gx[EPL], gxs = 0.f;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
-          gx[e] = msk[i][e] * gd[e];
-          gxs = fmaf(gx[e], sq[i][e], gxs);
-          gr = fmaf(gx[e], c.d[i][e], gr);
+          kh[e] = to_f32(c.k[i][e]) * rinv;
+          sq[e] = kh[e] * kh[e];
+          gx[e] = c.m[i][e] ? gd[e] : 0.f;
+          gxs = fmaf(gx[e], sq[e], gxs);
         }
         gxs = head_sum<LPH>(gxs);
-#pragma unroll
-        for (int e = 0; e < EPL; ++e)
-          gd[e] = fmaf(c.ret[i], gx[e], fmaf(-c2[i] * gxs, sq[i][e], kh[i][e] * c.gk[i][e]));
-        // off the chain: the key, beta and retention gradients of token t
-        float gkh[EPL], pp = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          const float gs = fmaf(coef[i], gx[e], gxs * fmaf(-c2[i], c.d[i][e], -cn[i]));
-          gkh[e] = fmaf(2.f * kh[i][e], gs, c.d[i][e] * c.gk[i][e]);
-          pp = fmaf(kh[i][e], gkh[e], pp);
-        }
-        pp = head_sum<LPH>(pp);
-        if (p.dret != nullptr) gr = head_sum<LPH>(gr);
         if (active) {
-          const long long rw = row0 + (long long)t * p.H;
-          const float proj = tiny[i] ? 0.f : pp;
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) dkp[t * kstride + e] = c.dk0[i][e] + (gkh[e] - kh[i][e] * proj) * rinv[i];
-          if (sl == 0) {
-            const float braw = c.beta[i];
-            if (p.beta_aware && braw >= 0.f && braw <= 2.f) p.dbeta[rw] = c.db0[i] + gxs * fb[i];
-            if (p.dret != nullptr) p.dret[rw] = p.ret != nullptr ? gr : 0.f;
-          }
+          if constexpr (EPL == 2)
+            *reinterpret_cast<float2*>(gip + t * kstride) = make_float2(gd[0], gd[1]);
+          else
+            gip[t * kstride] = gd[0];
         }
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) gd[e] = fmaf(rt, gx[e], fmaf(-c2 * gxs, sq[e], kh[e] * c.gk[i][e]));
       }
     }
   };
@@ -1207,12 +1233,84 @@ __global__ __launch_bounds__(64) void dp_precond_bwd_kernel(PrecondBwdArgs p) {
 }
 
 template <typename T, int DK>
+__global__ __launch_bounds__(64) void dp_precond_bwd_grads_kernel(PrecondBwdArgs p) {
+  using G = P1Lanes<DK>;
+  constexpr int LPH = G::LPH, EPL = G::EPL, HPW = G::HPW;
+  const int lane = threadIdx.x & 63, sl = lane % LPH;
+  const int nblk = (p.L + kP1Tokens - 1) / kP1Tokens;
+  const long long nbh = (long long)p.B * p.H;
+  const long long bh_raw = (long long)(blockIdx.x / nblk) * HPW + lane / LPH;
+  const int t0 = (int)(blockIdx.x % nblk) * kP1Tokens;
+  const bool active = bh_raw < nbh;
+  const long long bh = active ? bh_raw : 0;
+  const int b = (int)(bh / p.H), h = (int)(bh % p.H);
+  const long long row0 = (long long)b * p.L * p.H + h, kstride = (long long)p.H * DK;
+  const long long c0 = row0 * DK + sl * EPL;
+  const T* kp = static_cast<const T*>(p.k) + c0;
+  const int t1 = min(t0 + kP1Tokens, p.L);
+#pragma unroll 2
+  for (int t = t0; t < t1; ++t) {
+    const long long o = (long long)t * kstride;
+    T kv[EPL];
+    float dv[EPL], gk[EPL], gi[EPL], dk0[EPL];
+    bool in[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      kv[e] = kp[o + e];
+      dv[e] = p.dtr[c0 + o + e];
+      gk[e] = p.dkt[c0 + o + e];
+      gi[e] = p.gin[c0 + o + e];
+      dk0[e] = p.dk[c0 + o + e];
+      in[e] = p.msk[c0 + o + e] != 0;
+    }
+    const long long rw = row0 + (long long)t * p.H;
+    const float braw = p.beta[rw];
+    const P1Tok<LPH, EPL> f = p1_token<T, LPH, EPL>(kv, dv, braw, p);
+    float gx[EPL], gxs = 0.f, gr = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      gx[e] = in[e] ? gi[e] : 0.f;
+      gxs = fmaf(gx[e], f.sq[e], gxs);
+      gr = fmaf(gx[e], dv[e], gr);
+    }
+    gxs = head_sum<LPH>(gxs);
+    if (p.dret != nullptr) gr = head_sum<LPH>(gr);
+    float gkh[EPL], pp = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const float gs = fmaf(f.coef, gx[e], gxs * fmaf(-f.c2, dv[e], -f.cn));
+      gkh[e] = fmaf(2.f * f.kh[e], gs, dv[e] * gk[e]);
+      pp = fmaf(f.kh[e], gkh[e], pp);
+    }
+    pp = head_sum<LPH>(pp);
+    if (active) {
+      const float proj = f.tiny ? 0.f : pp;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) p.dk[c0 + o + e] = dk0[e] + (gkh[e] - f.kh[e] * proj) * f.rinv;
+      if (sl == 0) {
+        if (p.beta_aware && braw >= 0.f && braw <= 2.f) p.dbeta[rw] += gxs * f.fb;
+        if (p.dret != nullptr) p.dret[rw] = p.ret != nullptr ? gr : 0.f;
+      }
+    }
+  }
+}
+
+template <typename T, int DK>
 hipError_t launch_precond_bwd_dk(const PrecondBwdArgs& a, hipStream_t st) {
+  using G = P1Lanes<DK>;
   const long long nbh = (long long)a.B * a.H;
-  constexpr int HPW = 64 / (DK < 64 ? DK : 64);  // heads per wavefront
-  const unsigned blocks = (unsigned)((nbh + HPW - 1) / HPW);
-  if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((dp_precond_bwd_kernel<T, DK>), dim3(blocks), dim3(64), 0, st, a);
+  const unsigned groups = (unsigned)((nbh + G::HPW - 1) / G::HPW);
+  const unsigned nblk = (unsigned)((a.L + kP1Tokens - 1) / kP1Tokens);
+  if (groups == 0) return hipSuccess;
+  if (nblk > 0) {
+    hipLaunchKernelGGL((dp_precond_bwd_factors_kernel<T, DK>), dim3(groups * nblk), dim3(64), 0, st, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((dp_precond_bwd_chain_kernel<T, DK>), dim3(groups), dim3(64), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || nblk == 0) return e;
+  hipLaunchKernelGGL((dp_precond_bwd_grads_kernel<T, DK>), dim3(groups * nblk), dim3(64), 0, st, a);
   return hipGetLastError();
 }
 

@@ -417,7 +417,8 @@ def test_backward_entry_points_validate_before_hip(lib):
     n = ctypes.c_size_t(0)
     assert lib.dp_osdn_precond_bwd_workspace_size(2, 3, 5, 32, ctypes.byref(n)) == E.DP_OK
     up = lambda x: (x + 255) // 256 * 256
-    assert n.value == up(2 * 3 * 32 * 4) + 2 * up(2 * 5 * 3 * 32 * 4)
+    # d, the trajectory of d, the write keys, the mask bytes, the per-token factors, the received gradient
+    assert n.value == up(2 * 3 * 32 * 4) + 3 * up(2 * 5 * 3 * 32 * 4) + up(2 * 5 * 3 * 32) + up(2 * 5 * 3 * 16)
     assert pbwd(wsb=n.value - 1, B=2, H=3, L=5, dk=32) == E.DP_EWORKSPACE
 
     def obwd(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, dout=FAKE, B=1, H=1, L=8, dk=16, dv=16, dq=FAKE, dko=FAKE,
