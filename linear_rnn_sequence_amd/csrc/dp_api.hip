@@ -5,6 +5,7 @@
 // stream and returns.  The library allocates no device memory for a call and
 // keeps no state between calls (a dp_pipeline is the caller's object), except
 // the fixed `scratch` array of the no-alloc packed forward.
+#include <algorithm>
 #include <mutex>
 #include <new>
 #include <limits.h>
@@ -316,6 +317,57 @@ hipError_t dispatch_fwd(int elem, int dk, const dp::FwdArgs& a, int C, int BV, i
       case 32: return dp_launch_fwd_bf16_32(a, C, BV, lds, stages, st);
       case 64: return dp_launch_fwd_bf16_64(a, C, BV, lds, stages, st);
       case 128: return dp_launch_fwd_bf16_128(a, C, BV, lds, stages, st);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+// Phase 1 in 64-token chunks (dk >= 64): its workspace per call of L tokens.
+struct P1cWs {
+  size_t tm, v, fac, gt, dstart, gam, restart, total;
+};
+P1cWs p1c_ws(int B, int H, int L, int dk) {
+  P1cWs w;
+  const size_t nbh = (size_t)B * H, nch = nbh * ((L + dp::kP1Chunk - 1) / dp::kP1Chunk);
+  w.tm = align_up(nch * dp::kP1Chunk * dp::kP1Chunk * 4, kWsAlign);
+  w.v = align_up(nch * dp::kP1Chunk * 4, kWsAlign);
+  w.fac = align_up(nch * dp::kP1Chunk * 16, kWsAlign);
+  w.gt = align_up(nch * 4, kWsAlign);
+  w.dstart = align_up(nch * dk * 4, kWsAlign);
+  w.gam = w.v;
+  w.restart = align_up(nbh * 4, kWsAlign);
+  w.total = dk >= 64 ? w.tm + w.v + w.fac + w.gt + w.dstart + w.gam + w.restart : 0;
+  return w;
+}
+// point a's chunked-form buffers into ws (p1c_ws(B, H, L, dk).total bytes)
+void p1c_bind(dp::PrecondArgs& a, char* ws, int dk) {
+  const P1cWs w = p1c_ws(a.B, a.H, a.L, dk);
+  char* o = ws;
+  a.wsTm = reinterpret_cast<float*>(o);
+  o += w.tm;
+  a.wsV = reinterpret_cast<float*>(o);
+  o += w.v;
+  a.wsFac = reinterpret_cast<float4*>(o);
+  o += w.fac;
+  a.wsGT = reinterpret_cast<float*>(o);
+  o += w.gt;
+  a.dstart = reinterpret_cast<float*>(o);
+  o += w.dstart;
+  a.gam = reinterpret_cast<float*>(o);
+  o += w.gam;
+  a.restart = reinterpret_cast<int*>(o);
+}
+
+hipError_t dispatch_precond_chunked(int elem, int dk, const dp::PrecondArgs& a, hipStream_t st) {
+  if (elem == 4) {
+    switch (dk) {
+      case 64: return dp_launch_precond_chunked_f32_64(a, st);
+      case 128: return dp_launch_precond_chunked_f32_128(a, st);
+    }
+  } else {
+    switch (dk) {
+      case 64: return dp_launch_precond_chunked_bf16_64(a, st);
+      case 128: return dp_launch_precond_chunked_bf16_128(a, st);
     }
   }
   return hipErrorInvalidValue;
@@ -794,9 +846,11 @@ hipError_t dispatch_precond_bwd(int elem, int dk, const dp::PrecondBwdArgs& a, h
 // d (B L H dk f32), the write keys the forward emits again (B L H dk elements
 // of the input type; sized for fp32), then for the reverse scan the
 // projection mask (B L H dk bytes), the per-token factors (B L H float4) and
-// the gradient each token receives (B L H dk f32).
+// the gradient each token receives (B L H dk f32).  The forward's chunked
+// form (dk >= 64) uses the region of the last three before the reverse scan
+// needs it, so that region is the larger of the two.
 struct PrecondBwdWs {
-  size_t d, dtr, kt, msk, fac, gin, total;
+  size_t d, dtr, kt, msk, fac, gin, rev, total;
 };
 PrecondBwdWs precond_bwd_ws(int B, int H, int L, int dk) {
   PrecondBwdWs w;
@@ -807,7 +861,8 @@ PrecondBwdWs precond_bwd_ws(int B, int H, int L, int dk) {
   w.msk = align_up(n * dk, kWsAlign);
   w.fac = align_up(n * 16, kWsAlign);
   w.gin = w.dtr;
-  w.total = w.d + w.dtr + w.kt + w.msk + w.fac + w.gin;
+  w.rev = std::max(w.msk + w.fac + w.gin, p1c_ws(B, H, L, dk).total);
+  w.total = w.d + w.dtr + w.kt + w.rev;
   return w;
 }
 
@@ -837,6 +892,10 @@ hipError_t precond_traj(int elem, const void* k, const float* beta, const float*
   a.eps = eps;
   a.dtr = reinterpret_cast<float*>(ws + w.d);
   a.d_ones = d0 == nullptr ? 1 : 0;
+  if (dk >= 64) {
+    p1c_bind(a, ws + w.d + w.dtr + w.kt, dk);
+    return dispatch_precond_chunked(elem, dk, a, st);
+  }
   return dispatch_precond(elem, dk, a, st);
 }
 
@@ -1124,8 +1183,11 @@ int dp_osdn_fwd_bf16(const void* q, const void* k, const void* v, const float* b
   if (L > 0 && (q == nullptr || k == nullptr || v == nullptr || beta == nullptr || out == nullptr ||
                 kt == nullptr || d_state == nullptr))
     return DP_EINVAL;
-  const size_t need = ws_total(s, 2);
-  if (workspace_bytes < need || (need > 0 && workspace == nullptr)) return DP_EWORKSPACE;
+  // Phase 1 runs as the sequential scan here: with one wavefront per head it
+  // leaves most of the chip to the forward of the previous run, which the
+  // chunked form's parallel kernels would compete with.
+  const size_t fws = ws_total(s, 2);
+  if (workspace_bytes < fws || (fws > 0 && workspace == nullptr)) return DP_EWORKSPACE;
   if (nseg == 0) return fwd_impl(2, q, k, k, v, beta, nullptr, 1, B, H, 0, dk, dv, chunk, out, final_state,
                                  h0, workspace, workspace_bytes, DP_STAGE_ALL, stream);
   // Check every run before enqueueing the first.  The runs differ only in
@@ -1135,7 +1197,7 @@ int dp_osdn_fwd_bf16(const void* q, const void* k, const void* v, const float* b
                     stream, L, 0, true);
   if (rc != DP_OK) return rc;
   rc = fwd_impl(2, q, k, kt, v, beta, nullptr, 1, B, H, len, dk, dv, chunk, out, final_state, h0,
-                workspace, workspace_bytes, DP_STAGE_ALL, stream, L, 0, true);
+                workspace, fws, DP_STAGE_ALL, stream, L, 0, true);
   if (rc != DP_OK) return rc;
   std::unique_lock<std::mutex> hold;
   if (pipe != nullptr) {
@@ -1155,7 +1217,7 @@ int dp_osdn_fwd_bf16(const void* q, const void* k, const void* v, const float* b
                             hipStreamWaitEvent(st2, pipe->ev[sg], 0) != hipSuccess))
       return DP_EHIP;
     rc = fwd_impl(2, q, k, kt, v, beta, nullptr, 1, B, H, n, dk, dv, chunk, out, final_state,
-                  sg == 0 ? h0 : final_state, workspace, workspace_bytes, DP_STAGE_ALL, st2, L, t0);
+                  sg == 0 ? h0 : final_state, workspace, fws, DP_STAGE_ALL, st2, L, t0);
     if (rc != DP_OK) return rc;
   }
   if (pipe != nullptr && (hipEventRecord(pipe->ev[kMaxSegments], st2) != hipSuccess ||

@@ -130,6 +130,16 @@ struct PrecondArgs {
   int Ls = 0, t0 = 0;  // a call on tokens t0 .. t0 + L - 1 of Ls-token sequences (0: Ls = L)
   float* dtr = nullptr;  // [B, L, H, dk] fp32: d_t of every token (before its update), or nullptr
   int d_ones = 0;        // 1: the scan starts from d = 1 (p.d is then written only)
+  // the chunked form (dp_precond_chunk.hpp), per 64-token chunk of each head
+  float* wsTm = nullptr;    // [B*H*nc][64][64] (I + L diag(c2))^-1
+  float* wsV = nullptr;     // [B*H*nc][64] its product with L w
+  float4* wsFac = nullptr;  // [B*H*nc][64] (1/max(|k|, 1e-6), w, c2, G) per token
+  float* wsGT = nullptr;    // [B*H*nc] the chunk's total log-retention
+  float* dstart = nullptr;  // [B*H*nc][dk] d at each chunk start
+  float* gam = nullptr;     // [B*H*nc][64] w - c2 a per token
+  // [B*H] first chunk whose check failed (nc: none): with it, dp_precond_kernel
+  // runs the exact scan from that chunk's start d and leaves other heads alone
+  int* restart = nullptr;
 };
 
 __host__ __device__ constexpr int align16(int x) { return (x + 15) & ~15; }
@@ -1347,6 +1357,16 @@ __global__ __launch_bounds__(64) void dp_precond_kernel(PrecondArgs p) {
     // clamped beta); the sequential part reads them with v_readlane.
     if (!active) return;
     constexpr int PB = sizeof(T) == 2 ? 64 : 32;  // tokens per block
+    // after the chunked form: start at the head's first failed chunk, or not at all
+    int tbeg = 0;
+    if (p.restart != nullptr) {
+      const int nc = (p.L + 63) / 64;
+      const int sc = p.restart[bh];
+      if (sc >= nc) return;
+      tbeg = sc * 64;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) d[e] = p.dstart[((long long)bh * nc + sc) * DK + sl * EPL + e];
+    }
     constexpr int RB = DK * (int)sizeof(T);       // bytes per key row
     static_assert(RB % 16 == 0, "key rows in 16-byte pieces");
     const T* krow = static_cast<const T*>(p.k) + row0 * DK;
@@ -1425,9 +1445,9 @@ __global__ __launch_bounds__(64) void dp_precond_kernel(PrecondArgs p) {
         }
       }
     };
-    load_rows(0);
-    load_slices(0, sc);
-    for (int t0 = 0; t0 < p.L; t0 += PB) {
+    load_rows(tbeg);
+    load_slices(tbeg, sc);
+    for (int t0 = tbeg; t0 < p.L; t0 += PB) {
       token_scalars();
       if (t0 + PB < p.L) {
         load_rows(t0 + PB);
@@ -1598,6 +1618,7 @@ inline bool allow_big_lds(const void* fn) {
 #include "dp_fwd16.hpp"
 #include "dp_fused.hpp"
 #include "dp_decode.hpp"
+#include "dp_precond_chunk.hpp"
 
 namespace dp {
 
@@ -1858,6 +1879,7 @@ hipError_t launch_precond_dk(const PrecondArgs& a, hipStream_t st) {
   hipError_t dp_launch_fwd_##TNAME##_##DK(const dp::FwdArgs& a, int C, int BV, int lds_scan,   \
                                           int stages, hipStream_t st);                         \
   hipError_t dp_launch_precond_##TNAME##_##DK(const dp::PrecondArgs& a, hipStream_t st);   \
+  hipError_t dp_launch_precond_chunked_##TNAME##_##DK(const dp::PrecondArgs& a, hipStream_t st); \
   hipError_t dp_launch_decode_##TNAME##_##DK(const dp::DecodeArgs& a, hipStream_t st);
 
 #define DP_DEFINE_LAUNCHERS(T, TNAME, DK)                                                      \
@@ -1867,6 +1889,9 @@ hipError_t launch_precond_dk(const PrecondArgs& a, hipStream_t st) {
   }                                                                                            \
   hipError_t dp_launch_precond_##TNAME##_##DK(const dp::PrecondArgs& a, hipStream_t st) {      \
     return dp::launch_precond_dk<T, DK>(a, st);                                                \
+  }                                                                                            \
+  hipError_t dp_launch_precond_chunked_##TNAME##_##DK(const dp::PrecondArgs& a, hipStream_t st) { \
+    return dp::launch_precond_chunked_if<T, DK>(a, st);                                        \
   }                                                                                            \
   hipError_t dp_launch_decode_##TNAME##_##DK(const dp::DecodeArgs& a, hipStream_t st) {        \
     return dp::launch_decode_dk<T, DK>(a, st);                                                 \

@@ -1,0 +1,453 @@
+// dp_precond_chunk.hpp -- OSDN phase 1 in 64-token chunks (gfx950).
+//
+// Phase 1 (OSDN study notes sec. 2.4, Alg.1, with the retention of sec. 2.6
+// and the beta-free step of sec. 2.7) is, per head and token t,
+//   kt_t = d_t o kh_t,  a_t = <d_t, s_t>,  s_t = kh_t o kh_t,
+//   d_{t+1} = P[ r_t d_t + (w_t - c2_t a_t) s_t ],
+// w_t = eta bu_t / max(|kh_t|^2, eps), c2_t = bu_t w_t.  While the projection P
+// onto the box leaves every coordinate alone the step is linear in d (the
+// notes: affine without the clamp, piecewise affine with it).  Over a chunk
+// of T tokens from d_0, with G_t the cumulative log-retention before token t:
+//   d_t = e^{G_t} d_0 + sum_{u<t} e^{G_t - G_{u+1}} (w_u - c2_u a_u) s_u,
+//   (I + L diag(c2)) a = e^G o (S d_0) + L w,   L_tu = e^{G_t - G_{u+1}} <s_t, s_u>  (u < t)
+// The matrix depends on the keys, beta and r only, so it is inverted for every
+// chunk in parallel (dp_p1_ut_kernel); the sequential part per head is then
+// three small products per chunk (dp_p1_chain_kernel): p = S d_0, a = Tm
+// (e^G o p) + v, and the end-of-chunk d.  dp_p1_emit_kernel replays each
+// chunk coordinate by coordinate from its start d (a_t known), emits the write
+// keys and checks that no step came within a margin of the box (or is NaN).
+// A head whose check fails anywhere runs the exact sequential scan again from
+// the first such chunk's start (dp_precond_kernel with PrecondArgs::restart),
+// so the result is the sequential definition's whichever way it is reached.
+// The notes state phase 1's depth as the sequence length; this form keeps that
+// definition and only shortens the work on the sequential path while no
+// clamp binds.  Used for dk >= 64 (one head per wavefront in the fallback).
+#pragma once
+
+namespace dp {
+
+constexpr int kP1Chunk = 64;  // tokens per chunk
+constexpr int kP1Ld = kP1Chunk + 4;
+
+// --------------------------------------------------------------------------
+// dp_p1_ut_kernel: one workgroup per (head, chunk), all in parallel.
+template <typename T, int DK>
+__global__ __launch_bounds__(256) void dp_p1_ut_kernel(PrecondArgs p) {
+  constexpr int C = kP1Chunk, LDM = kP1Ld, NT = C / 16;
+  constexpr int VE = Vec<T>::N;
+  constexpr int LDS_ = DK + 4;   // fp32 s rows
+  constexpr int TPR = DK / VE;   // 16-byte granules per key row
+  constexpr int KV = C * TPR, KIT = (KV + 255) / 256;
+  static_assert(TPR <= 64 && 64 % TPR == 0, "row group must fit in a wavefront");
+  // the squared keys are dead once L is formed: Tm and the inverse's scratch
+  // take their place (three workgroups fit on a CU)
+  constexpr int NBIG = C * LDS_ > C * LDM + 4 * 16 * 17 ? C * LDS_ : C * LDM + 4 * 16 * 17;
+  __shared__ __align__(16) float sS[NBIG];
+  __shared__ __align__(16) float sM[C * LDM];
+  float* const sTm = sS;
+  float* const sSc = sS + C * LDM;
+  __shared__ float sN[C], sRinv[C], sW[C], sC2[C], sG[C + 1], sLw[C];
+  __shared__ float sLwp[NT * C];  // L w per column block, summed in a fixed order
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int nc = (p.L + C - 1) / C;
+  const long long chunk = blockIdx.x;
+  const long long bh = chunk / nc;
+  const int c = (int)(chunk % nc);
+  const int b = (int)(bh / p.H), h = (int)(bh % p.H);
+  const long long row0 = tok_base(p, b) * p.H + h;
+  const long long kstride = (long long)p.H * DK;
+  const int t0 = c * C;
+  const T* kp = static_cast<const T*>(p.k);
+
+  // 1. key rows -> squared unit keys (fp32) and the row norms
+  u32x4_t rk[KIT];
+#pragma unroll
+  for (int it = 0; it < KIT; ++it) {
+    const int idx = tid + it * 256;
+    const int r = idx / TPR, cg = idx % TPR;
+    rk[it] = u32x4_t{0u, 0u, 0u, 0u};
+    if (idx < KV && t0 + r < p.L) rk[it] = ld16(kp + (row0 + (long long)(t0 + r) * p.H) * DK + cg * VE);
+  }
+  float braw = 0.f, rr = 1.f;
+  if (tid < C && t0 + tid < p.L) {
+    const long long rw = row0 + (long long)(t0 + tid) * p.H;
+    braw = p.beta[rw];
+    if (p.ret != nullptr) rr = p.ret[rw];
+  }
+#pragma unroll
+  for (int it = 0; it < KIT; ++it) {
+    const int idx = tid + it * 256;
+    const int r = idx / TPR, cg = idx % TPR;
+    float f[VE];
+    unpack16(rk[it], f, T{});
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < VE; ++e) ss = fmaf(f[e], f[e], ss);
+    if constexpr (TPR <= 16)
+      ss = dpp_group_sum<TPR>(ss);
+    else
+      ss = group_sum<TPR>(ss);
+    const float rinv = __builtin_amdgcn_rsqf(fmaxf(ss, 1e-12f));  // 1 / max(|k|, 1e-6)
+    if (idx < KV) {
+#pragma unroll
+      for (int e = 0; e < VE; e += 4) {
+        const float a0 = f[e] * rinv, a1 = f[e + 1] * rinv, a2 = f[e + 2] * rinv, a3 = f[e + 3] * rinv;
+        *reinterpret_cast<float4*>(sS + r * LDS_ + cg * VE + e) = make_float4(a0 * a0, a1 * a1, a2 * a2, a3 * a3);
+      }
+      if (cg == 0) {
+        sN[r] = ss * rinv * rinv;  // |kh|^2, as the sequential scan forms it
+        sRinv[r] = rinv;
+      }
+    }
+  }
+  __syncthreads();
+  // 2. per-token factors and the cumulative log-retention (G_0 = 0)
+  if (wave == 0) {
+    const bool ok = lane < C && t0 + lane < p.L;
+    float w = 0.f, c2 = 0.f, lr = 0.f;
+    if (ok) {
+      const float bu = p.beta_aware ? clamp_keep_nan(braw, 0.f, 2.f) : 1.f;
+      w = p.eta * bu * __builtin_amdgcn_rcpf(fmaxf(sN[lane], p.eps));
+      c2 = bu * w;
+      lr = logf(fmaxf(rr, FLT_MIN));
+    }
+    const float incl = wave_inclusive_scan(lr);
+    if (lane < C) {
+      sW[lane] = w;
+      sC2[lane] = c2;
+      sG[lane] = incl - lr;
+    }
+    if (lane == C - 1) sG[C] = incl;
+  }
+  __syncthreads();
+  // 3. L (gated Gram matrix of the squared keys, strictly lower), M = L diag(c2), L w
+  for (int tile = wave; tile < NT * NT; tile += 4) {
+    const int ti = tile / NT, tj = tile % NT;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    if (tj <= ti) acc = mm_tile<float, DK>(acc, sS, LDS_, ti * 16, sS, LDS_, tj * 16);
+    const int u = tj * 16 + col;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = ti * 16 + 4 * grp + e;
+      const float l = (u < t) ? __expf(sG[t] - sG[u + 1]) * acc[e] : 0.f;
+      sM[t * LDM + u] = l * sC2[u];
+      float lw = l * sW[u];
+      lw += __shfl_xor(lw, 8);
+      lw += __shfl_xor(lw, 4);
+      lw += __shfl_xor(lw, 2);
+      lw += __shfl_xor(lw, 1);
+      if (col == 0 && tj <= ti) sLwp[tj * C + t] = lw;
+    }
+  }
+  __syncthreads();
+  // 4. Tm = (I + M)^{-1}: diagonal 16 x 16 blocks by forward substitution (one
+  //    16-lane group per block, one column per lane), then the off-diagonal
+  //    blocks level by level, Tm_ij = -Tm_ii sum_{k=j}^{i-1} M_ik Tm_kj
+  //    (meanwhile wave 1 sums L w over its column blocks)
+  if (wave == 1) {
+    float lw = 0.f;
+    for (int tb = 0; tb <= (lane >> 4); ++tb) lw += sLwp[tb * C + lane];
+    sLw[lane] = lw;
+  }
+  if (wave == 0) {
+    const int gb = lane >> 4, cc = lane & 15;
+    if (gb < NT) {
+      float t[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float acc = (i == cc) ? 1.f : 0.f;
+        const float* ar = sM + (gb * 16 + i) * LDM + gb * 16;
+#pragma unroll
+        for (int j = 0; j < i; ++j) acc = fmaf(-ar[j], t[j], acc);
+        t[i] = acc;
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sTm[(gb * 16 + i) * LDM + gb * 16 + cc] = t[i];
+    }
+  }
+  // the upper blocks of Tm are zero
+  for (int idx = tid; idx < C * C; idx += 256) {
+    const int i = idx / C, j = idx % C;
+    if ((j >> 4) > (i >> 4)) sTm[i * LDM + j] = 0.f;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int dist = 1; dist < NT; ++dist) {
+    const int j = wave, i = wave + dist;
+    float* sX = sSc + wave * 16 * 17;
+    if (i < NT) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      for (int kb = j; kb < i; ++kb)
+        acc = mm_tile_tb<float, 16>(acc, sM + i * 16 * LDM + kb * 16, LDM, 0, sTm + kb * 16 * LDM + j * 16, LDM, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sX[(4 * grp + e) * 17 + col] = acc[e];
+    }
+    __syncthreads();
+    if (i < NT) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mm_tile_tb<float, 16>(acc, sTm + i * 16 * LDM + i * 16, LDM, 0, sX, 17, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sTm[(i * 16 + 4 * grp + e) * LDM + j * 16 + col] = -acc[e];
+    }
+    __syncthreads();
+  }
+  // 5. outputs: Tm, v = Tm (L w), the per-token factors and the chunk's total log-retention
+  float* tm = p.wsTm + chunk * C * C;
+  for (int idx = tid; idx < C * C / 4; idx += 256) {
+    const int i = (4 * idx) / C, j = (4 * idx) % C;
+    *reinterpret_cast<float4*>(tm + 4 * idx) = *reinterpret_cast<const float4*>(sTm + i * LDM + j);
+  }
+  {  // v_t = sum_u Tm_tu (L w)_u: four threads per row
+    const int t = tid >> 2, q = tid & 3;
+    float v = 0.f;
+#pragma unroll
+    for (int u = q * (C / 4); u < (q + 1) * (C / 4); ++u) v = fmaf(sTm[t * LDM + u], sLw[u], v);
+    v += __shfl_xor(v, 1);
+    v += __shfl_xor(v, 2);
+    if (q == 0) p.wsV[chunk * C + t] = v;
+  }
+  if (tid < C) p.wsFac[chunk * C + tid] = make_float4(sRinv[tid], sW[tid], sC2[tid], sG[tid]);
+  if (tid == 0) p.wsGT[chunk] = sG[C];
+}
+
+// --------------------------------------------------------------------------
+// dp_p1_chain_kernel: one workgroup per head, sequential over its chunks.
+template <typename T, int DK>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void dp_p1_chain_kernel(PrecondArgs p) {
+  constexpr int C = kP1Chunk, LDM = kP1Ld;
+  constexpr int VE = Vec<T>::N;
+  constexpr int LDS_ = DK + 4;
+  constexpr int TPR = DK / VE;
+  constexpr int KV = C * TPR, KIT = (KV + 255) / 256;
+  constexpr int TMIT = C * C / 4 / 256;  // float4 pieces of Tm per thread
+  constexpr int NP = 256 / DK;           // partial sums per coordinate of the end-of-chunk d
+  static_assert(C * C / 4 == 256 * TMIT && 256 % DK == 0 && C % NP == 0, "thread layout");
+  __shared__ __align__(16) float sS[C * LDS_];
+  __shared__ __align__(16) float sTm[C * LDM];
+  __shared__ float sD[DK], sPart[NP * DK];
+  __shared__ float sW[C], sC2[C], sG[C + 1], sV[C], sRhs[C], sCoef[C];
+
+  const int tid = threadIdx.x;
+  const int nc = (p.L + C - 1) / C;
+  const long long bh = blockIdx.x;
+  const int b = (int)(bh / p.H), h = (int)(bh % p.H);
+  const long long row0 = tok_base(p, b) * p.H + h;
+  const T* kp = static_cast<const T*>(p.k);
+
+  // a chunk's operands in registers: two sets, loaded two chunks ahead of use
+  struct Stage {
+    u32x4_t rk[KIT];
+    float rinv[KIT];
+    float4 rtm[TMIT];
+    float4 rfac;
+    float rv, rgt;
+  };
+  auto prefetch = [&](Stage& S, int c) {
+    const long long chunk = bh * nc + c;
+    const int t0 = c * C;
+#pragma unroll
+    for (int it = 0; it < KIT; ++it) {
+      const int idx = tid + it * 256;
+      const int r = idx / TPR, cg = idx % TPR;
+      S.rk[it] = u32x4_t{0u, 0u, 0u, 0u};
+      S.rinv[it] = 0.f;
+      if (idx < KV && t0 + r < p.L) {
+        S.rk[it] = ld16(kp + (row0 + (long long)(t0 + r) * p.H) * DK + cg * VE);
+        S.rinv[it] = p.wsFac[chunk * C + r].x;
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < TMIT; ++it)
+      S.rtm[it] = reinterpret_cast<const float4*>(p.wsTm + chunk * C * C)[tid + it * 256];
+    S.rfac = make_float4(0.f, 0.f, 0.f, 0.f);
+    S.rv = 0.f;
+    S.rgt = 0.f;
+    if (tid < C) {
+      S.rfac = p.wsFac[chunk * C + tid];
+      S.rv = p.wsV[chunk * C + tid];
+    }
+    if (tid == 0) S.rgt = p.wsGT[chunk];
+  };
+
+  if (tid < DK) sD[tid] = p.d_ones ? 1.f : p.d[bh * DK + tid];
+  if (tid == 0) p.restart[bh] = nc;
+  auto body = [&](Stage& S, int c) {
+    const long long chunk = bh * nc + c;
+    __syncthreads();  // the previous chunk is done with every buffer
+    const u32x4_t* rk = S.rk;
+    const float* rinv = S.rinv;
+#pragma unroll
+    for (int it = 0; it < KIT; ++it) {
+      const int idx = tid + it * 256;
+      const int r = idx / TPR, cg = idx % TPR;
+      if (idx < KV) {
+        float f[VE];
+        unpack16(rk[it], f, T{});
+#pragma unroll
+        for (int e = 0; e < VE; e += 4) {
+          const float a0 = f[e] * rinv[it], a1 = f[e + 1] * rinv[it], a2 = f[e + 2] * rinv[it],
+                      a3 = f[e + 3] * rinv[it];
+          *reinterpret_cast<float4*>(sS + r * LDS_ + cg * VE + e) =
+              make_float4(a0 * a0, a1 * a1, a2 * a2, a3 * a3);
+        }
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < TMIT; ++it) {
+      const int q = tid + it * 256;
+      const int i = (4 * q) / C, j = (4 * q) % C;
+      *reinterpret_cast<float4*>(sTm + i * LDM + j) = S.rtm[it];
+    }
+    if (tid < C) {
+      sW[tid] = S.rfac.y;
+      sC2[tid] = S.rfac.z;
+      sG[tid] = S.rfac.w;
+      sV[tid] = S.rv;
+    }
+    if (tid == 0) sG[C] = S.rgt;
+    __syncthreads();
+    if (tid < DK) p.dstart[chunk * DK + tid] = sD[tid];
+    if (c + 2 < nc) prefetch(S, c + 2);  // lands while this chunk and the next are computed
+    // p_t = <s_t, d_0>: four threads per token
+    {
+      const int t = tid >> 2, q = tid & 3;
+      float acc = 0.f;
+#pragma unroll 8
+      for (int j = q * (DK / 4); j < (q + 1) * (DK / 4); ++j) acc = fmaf(sS[t * LDS_ + j], sD[j], acc);
+      acc += __shfl_xor(acc, 1);
+      acc += __shfl_xor(acc, 2);
+      if (q == 0) sRhs[t] = __expf(sG[t]) * acc;
+    }
+    __syncthreads();
+    // a = Tm (e^G o p) + v;  gamma = w - c2 a;  coef_u = e^{G_C - G_{u+1}} gamma_u
+    {
+      const int t = tid >> 2, q = tid & 3;
+      float acc = 0.f;
+#pragma unroll
+      for (int u = q * (C / 4); u < (q + 1) * (C / 4); ++u) acc = fmaf(sTm[t * LDM + u], sRhs[u], acc);
+      acc += __shfl_xor(acc, 1);
+      acc += __shfl_xor(acc, 2);
+      if (q == 0) {
+        const float gm = fmaf(-sC2[t], acc + sV[t], sW[t]);
+        p.gam[chunk * C + t] = gm;
+        sCoef[t] = __expf(sG[C] - sG[t + 1]) * gm;
+      }
+    }
+    __syncthreads();
+    // d_C = e^{G_C} d_0 + sum_u coef_u s_u
+    {
+      const int j = tid % DK, part = tid / DK;
+      float acc = 0.f;
+#pragma unroll 8
+      for (int u = part * (C / NP); u < (part + 1) * (C / NP); ++u) acc = fmaf(sS[u * LDS_ + j], sCoef[u], acc);
+      sPart[part * DK + j] = acc;
+    }
+    __syncthreads();
+    if (tid < DK) {
+      float x = __expf(sG[C]) * sD[tid];
+#pragma unroll
+      for (int q = 0; q < NP; ++q) x += sPart[q * DK + tid];
+      sD[tid] = x;
+    }
+  };
+  Stage sa, sb;
+  if (nc > 0) prefetch(sa, 0);
+  if (nc > 1) prefetch(sb, 1);
+  for (int c = 0; c < nc; c += 2) {
+    body(sa, c);
+    if (c + 1 < nc) body(sb, c + 1);
+  }
+  __syncthreads();
+  if (tid < DK) p.d[bh * DK + tid] = sD[tid];
+}
+
+// --------------------------------------------------------------------------
+// dp_p1_emit_kernel: one workgroup per (head, chunk), all in parallel; thread j
+// replays coordinate j of the chunk from its start d with the solved a_t,
+// emits the write keys (and d_t when asked), and checks every step against
+// the box with a margin.  A failing chunk marks its head for the exact scan.
+// The chunk's keys and factors are staged in LDS first (one memory round trip).
+template <typename T, int DK>
+__global__ __launch_bounds__(DK) void dp_p1_emit_kernel(PrecondArgs p) {
+  constexpr int C = kP1Chunk;
+  constexpr int VE = Vec<T>::N;
+  constexpr int TPR = DK / VE, KV = C * TPR, KIT = (KV + DK - 1) / DK;
+  __shared__ __align__(16) T sK[C * DK];
+  __shared__ float4 sFac[C];
+  __shared__ float sGam[C], sR[C];
+  const int j = threadIdx.x;
+  const int nc = (p.L + C - 1) / C;
+  const long long chunk = blockIdx.x;
+  const long long bh = chunk / nc;
+  const int c = (int)(chunk % nc);
+  const int b = (int)(bh / p.H), h = (int)(bh % p.H);
+  const long long row0 = tok_base(p, b) * p.H + h;
+  const int t0 = c * C, n = min(C, p.L - t0);
+  const long long ks = (long long)p.H * DK;
+  const T* kp = static_cast<const T*>(p.k) + (row0 + (long long)t0 * p.H) * DK;
+#pragma unroll
+  for (int it = 0; it < KIT; ++it) {
+    const int idx = j + it * DK;
+    const int r = idx / TPR, cg = idx % TPR;
+    if (idx < KV && r < n) st16(sK + r * DK + cg * VE, ld16(kp + r * ks + cg * VE));
+  }
+  if (j < n) {
+    sFac[j] = p.wsFac[chunk * C + j];
+    sGam[j] = p.gam[chunk * C + j];
+    sR[j] = p.ret != nullptr ? p.ret[row0 + (long long)(t0 + j) * p.H] : 1.f;
+  }
+  float d = p.dstart[chunk * DK + j];
+  __syncthreads();
+  T* ktp = static_cast<T*>(p.kt) + (row0 + (long long)t0 * p.H) * DK + j;
+  float* dtp = p.dtr != nullptr ? p.dtr + (row0 + (long long)t0 * p.H) * DK + j : nullptr;
+  // a step within this margin of a finite bound is not trusted to the chunked form
+  // (an infinite bound keeps no margin: -inf + inf would be NaN and fail every step)
+  const float lo = isfinite(p.dmin) ? p.dmin + 1e-5f * fmaxf(1.f, fabsf(p.dmin)) : p.dmin;
+  const float hi = isfinite(p.dmax) ? p.dmax - 1e-5f * fmaxf(1.f, fabsf(p.dmax)) : p.dmax;
+  bool ok = true;
+#pragma unroll 8
+  for (int i = 0; i < n; ++i) {
+    const float kh = to_f32(sK[i * DK + j]) * sFac[i].x;
+    ktp[i * ks] = from_f32<T>(d * kh);
+    if (dtp != nullptr) dtp[i * ks] = d;
+    const float x = fmaf(sGam[i], kh * kh, sR[i] * d);
+    ok = ok && (x >= lo && x <= hi);
+    d = x;
+  }
+  if (__any(!ok) && (j & 63) == 0) atomicMin(&p.restart[bh], c);
+}
+
+template <typename T, int DK>
+hipError_t launch_precond_chunked(const PrecondArgs& a, hipStream_t st) {
+  static_assert(DK >= 64, "the exact fallback runs one head per wavefront");
+  const long long nbh = (long long)a.B * a.H;
+  const int nc = (a.L + kP1Chunk - 1) / kP1Chunk;
+  if (nbh == 0) return hipSuccess;
+  if (nc > 0) {
+    hipLaunchKernelGGL((dp_p1_ut_kernel<T, DK>), dim3((unsigned)(nbh * nc)), dim3(256), 0, st, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((dp_p1_chain_kernel<T, DK>), dim3((unsigned)nbh), dim3(256), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || nc == 0) return e;
+  hipLaunchKernelGGL((dp_p1_emit_kernel<T, DK>), dim3((unsigned)(nbh * nc)), dim3(DK), 0, st, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // the exact scan from the first chunk that failed the check (heads with none return at once)
+  hipLaunchKernelGGL((dp_precond_kernel<T, DK>), dim3((unsigned)nbh), dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
+// dk < 64 has no chunked form (several heads share a wavefront in the exact scan)
+template <typename T, int DK>
+hipError_t launch_precond_chunked_if(const PrecondArgs& a, hipStream_t st) {
+  if constexpr (DK >= 64)
+    return launch_precond_chunked<T, DK>(a, st);
+  else
+    return hipErrorInvalidValue;
+}
+
+}  // namespace dp

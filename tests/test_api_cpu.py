@@ -420,6 +420,16 @@ def test_backward_entry_points_validate_before_hip(lib):
     # d, the trajectory of d, the write keys, the mask bytes, the per-token factors, the received gradient
     assert n.value == up(2 * 3 * 32 * 4) + 3 * up(2 * 5 * 3 * 32 * 4) + up(2 * 5 * 3 * 32) + up(2 * 5 * 3 * 16)
     assert pbwd(wsb=n.value - 1, B=2, H=3, L=5, dk=32) == E.DP_EWORKSPACE
+    # dk >= 64: the forward's chunked form (per 64-token chunk: the 64 x 64
+    # inverse, v, the token factors, the chunk's log-retention, its start d and
+    # gamma; one restart index per head) shares the reverse scan's region
+    assert lib.dp_osdn_precond_bwd_workspace_size(2, 3, 5, 128, ctypes.byref(n)) == E.DP_OK
+    nch = 2 * 3 * 1
+    chunked = (up(nch * 64 * 64 * 4) + 2 * up(nch * 64 * 4) + up(nch * 64 * 16) + up(nch * 4)
+               + up(nch * 128 * 4) + up(2 * 3 * 4))
+    rev = up(2 * 5 * 3 * 128) + up(2 * 5 * 3 * 16) + up(2 * 5 * 3 * 128 * 4)
+    assert chunked > rev
+    assert n.value == up(2 * 3 * 128 * 4) + 2 * up(2 * 5 * 3 * 128 * 4) + max(rev, chunked)
 
     def obwd(q=FAKE, k=FAKE, v=FAKE, beta=FAKE, dout=FAKE, B=1, H=1, L=8, dk=16, dv=16, dq=FAKE, dko=FAKE,
              dvo=FAKE, db=FAKE, eps=1e-6, wsp=FAKE, wsb=1 << 30):

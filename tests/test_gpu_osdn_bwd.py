@@ -6,7 +6,10 @@ differences, tests/test_oracle_bwd_pins.py):
 * the write-key forward's gradient (dp.bwd with kt: dp_bwd_wk_*) against
   oracle.bwd with the same write keys, for every input and for kt;
 * phase 1's gradient (dp.osdn_precond_bwd) against oracle.precond_bwd, with
-  retention, the beta-free step, a clamping box, d0 and a final-d gradient;
+  retention, the beta-free step, a clamping box, d0 and a final-d gradient
+  (for dk >= 64 the forward pass inside it runs in 64-token chunks and hands
+  a head to the sequential scan where the box comes near: cases where that
+  happens on some heads late in the sequence, and on every head at once);
 * the whole layer (dp.osdn_bwd: phase 1, then the write-key forward, n_h = 1)
   against oracle.osdn_bwd, small and at the full c5 shape on sampled heads.
 
@@ -94,6 +97,13 @@ P1 = [  # (B, L, H, dk), options
     ((2, 90, 1, 32), dict(beta_free=True, ret=True)),
     ((1, 40, 5, 16), dict(eta=0.5, dmin=0.9, dmax=1.1, d0=True)),        # clamps bind
     ((1, 64, 2, 128), dict(eta=0.05, dmin=float("-inf"), dmax=float("inf"), final=True)),  # open box
+    # dk >= 64 replays phase 1 in 64-token chunks and hands a head to the
+    # sequential scan from the chunk where a step first comes near the box.
+    # The bound is crossed by a decay of 1% (or ~5%) a token, so no step ends
+    # within rounding of it (there the clamp's gradient, 0 or 1, would be
+    # decided by rounding alone):
+    ((2, 300, 3, 128), dict(ret="late")),           # heads 0 and 2 reach dmin near token 69
+    ((2, 300, 3, 128), dict(ret=True, d0=True)),    # every head, in the first chunk
 ]
 
 
@@ -105,6 +115,9 @@ def test_phase1_backward_matches_oracle(shape, opt, dtype):
     tdt = torch.float32 if dtype == "f32" else torch.bfloat16
     k, beta, dkt, d0, ddf = p1_inputs(B, L, H, dk, tdt, seed=31 + L)
     r = retention(B, L, H, seed=5 + L) if opt.get("ret") else None
+    if opt.get("ret") == "late":
+        r = torch.ones(B, L, H)
+        r[:, :, 0::2] = 0.99
     d0 = d0 if opt.get("d0") else None
     ddf = ddf if opt.get("final") else None
     kw = dict(eta=opt.get("eta", 3e-3), dmin=opt.get("dmin", 0.5), dmax=opt.get("dmax", 2.0),

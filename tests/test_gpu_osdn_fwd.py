@@ -2,8 +2,8 @@
 
 It runs the same kernels on the same chunks as OSDN phase 1 followed by the
 write-key forward, cut into token runs (the state and d pass between runs in
-fp32), so its results must equal the two-call path bit for bit; one case is also
-checked against the fp64 oracle.
+fp32), so its results must equal the two-call path bit for bit; cases with and
+without binding clamps are also checked against the fp64 oracle.
 """
 import pytest
 import torch
@@ -28,6 +28,13 @@ def two_calls(q, k1, v1, b1, h0, chunk):
     out, fs = dp.fwd(q, k1.unsqueeze(3), v1.unsqueeze(3), b1.unsqueeze(3), chunk=chunk, h0=h0,
                      kt=kt.unsqueeze(3))
     return out, fs, kt, d
+
+
+def oracle_layer(q, k1, v1, b1, h0=None, **box):
+    kto, do = oracle.precond(k1.cpu(), b1.cpu(), **box)
+    oo, fo = oracle.fwd(q.cpu(), k1.cpu().unsqueeze(3), v1.cpu().unsqueeze(3), b1.cpu().unsqueeze(3),
+                        kt=kto[:, :, :, None, :], h0=None if h0 is None else h0.cpu())
+    return oo, fo, kto, do
 
 
 def inputs(B, H, L, dk, dv, with_h0=False):
@@ -151,3 +158,34 @@ def test_argument_errors():
         dp.osdn_fwd(q, k1, v1, b1, segments=0)
     with pytest.raises(dp.DPError):
         dp.osdn_fwd(q, k1, v1, b1, segments=17)
+
+
+CLAMP = [  # eta, dmax; the phase-1 clamp binds in: (dk 128, L 300, c5 inputs)
+    (1e-2, 1.0059),   # some heads only, late in the sequence
+    (1e-2, 1.002),    # every head, after the first chunk
+    (3e-2, 1.002),    # every head, within the first chunk
+]
+
+
+@pytest.mark.parametrize("eta,dmax", CLAMP)
+def test_clamping_box_matches_oracle(eta, dmax):
+    """With the upper bound of the box binding (on some heads or all, late or
+    within the first chunk) the pipelined call meets the oracle, clamps
+    included, and equals the two-call path."""
+    B, H, L, dk, dv = 2, 3, 300, 128, 128
+    say(f"case osdn_fwd clamps B={B} H={H} L={L} eta={eta} dmax={dmax}")
+    q, k1, v1, b1, _ = inputs(B, H, L, dk, dv)
+    box = dict(eta=eta, dmin=0.5, dmax=dmax)
+    ref = oracle_layer(q, k1, v1, b1, **box)
+    at_bound = (ref[3] >= dmax).any(axis=-1)
+    say(f"  heads ending at the bound: {int(at_bound.sum())} of {B * H}")
+    assert at_bound.any()
+    got = dp.osdn_fwd(q, k1, v1, b1, segments=2, **box)
+    kt, d = dp.osdn_precond(k1, b1, **box)
+    torch.cuda.synchronize()
+    for name, x, r in zip(("out", "final_state", "kt", "d"), got, ref):
+        e = rel_err(f64(x), r)
+        say(f"  {name}: err {e:.3e}")
+        assert e <= TOL["bf16"], f"{name}: err {e:.3e}"
+    assert torch.all(got[3] <= dmax) and torch.all(got[3] >= 0.5)
+    assert torch.equal(got[2], kt) and torch.equal(got[3], d)
