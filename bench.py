@@ -27,7 +27,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "tokens/sec & MFMA TFLOP/s, DeltaProduct fwd n_h=2/3, dk=dv=128, L=4096"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
-PIPELINE_SEGMENTS = 8          # token runs of the pipelined write-key forward
+PIPELINE_SEGMENTS = 4          # token runs of the pipelined write-key forward
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
 FP32_PEAK_TFLOPS = 157.3       # MI355X dense fp32 MFMA
 

@@ -267,13 +267,20 @@ int dp_pipeline_destroy(dp_pipeline pipe);
 /* OSDN phase 1 and the write-key forward in one call, pipelined over token
  * segments (OSDN notes sec. 2.4 Alg. 1 for phase 1, sec. 2.5 for phase 2; the
  * DeltaProduct notes sec. 2.2 and 2.6 for the recurrence, with n_h = 1).
- * Computes exactly what dp_osdn_precond_bf16 followed by dp_fwd_wk_bf16 with
- * the emitted write keys computes (the same kernels, the same chunks), but the
- * sequence is cut into `segments` runs of whole chunks: while the forward of
- * one run proceeds on the second stream of `pipe`, phase 1 already scans the
- * next run on `stream`, and `stream` waits for both at the end.  With pipe ==
- * NULL the runs go one after another on `stream` (no overlap; the same
- * results bit for bit).
+ * Computes what dp_osdn_precond_bf16 followed by dp_fwd_wk_bf16 with the
+ * emitted write keys computes, but the sequence is cut into `segments` runs
+ * of whole chunks: while the forward of one run proceeds on the second stream
+ * of `pipe`, phase 1 already runs on the next run on `stream`, and `stream`
+ * waits for both at the end.  With pipe == NULL the runs go one after another
+ * on `stream` (no overlap; the same results bit for bit).
+ * Phase 1 here: for dk < 64 the sequential scan of dp_osdn_precond_bf16 (the
+ * same results bit for bit); for dk >= 64 its chunked form: each run's
+ * 64-token chunks solve their linear system in parallel, d passes from chunk
+ * to chunk, and a head whose step comes within 1e-5 (relative, at least
+ * 1e-5 absolute) of a finite bound of the box, or is NaN, runs the
+ * sequential scan again from the start of that chunk.  The result is the
+ * sequential definition's to fp32 rounding (not bit for bit: the sums are
+ * ordered differently).
  *   q [B,L,H,dk], k [B,L,H,dk] (raw read keys), v [B,L,H,dv]  bf16
  *   beta [B,L,H] f32;  h0 [B,H,dk,dv] f32 or NULL (zero)
  *   eta, dmin, dmax, eps: the phase-1 constants (3e-3, 0.5, 2, 1e-6)
@@ -282,7 +289,8 @@ int dp_pipeline_destroy(dp_pipeline pipe);
  *   out [B,L,H,dv] bf16 written;  final_state [B,H,dk,dv] f32 written (the
  *   state passes through it between runs: it must not be NULL when the call
  *   makes more than one run, and may alias h0)
- *   workspace: dp_osdn_fwd_workspace_size() bytes (one run's forward), 256-byte aligned
+ *   workspace: dp_osdn_fwd_workspace_size() bytes (one run's forward, then for
+ *              dk >= 64 one run's chunked phase 1), 256-byte aligned
  *   segments: 1 .. 16 (runs of ceil(ceil(L / segments) / chunk) chunks)
  *   pipe: a handle from dp_pipeline_create on the current device, or NULL
  * Every argument of every run is checked before the first run is enqueued:

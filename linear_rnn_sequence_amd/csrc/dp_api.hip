@@ -644,7 +644,7 @@ int decode_impl(int elem, const void* q, const void* k, const void* kt, const vo
 int precond_impl(int elem, const void* k, const float* beta, const float* ret, int flags,
                  int B, int H, int L, int dk, float eta, float dmin, float dmax, float eps,
                  float* d_state, void* kt, bool open_box, dp_stream stream, int Ls = 0, int t0 = 0,
-                 bool dry = false) {
+                 bool dry = false, char* p1c = nullptr) {
   // with L == 0 the per-token tensors are empty and may be null
   if (d_state == nullptr || (L > 0 && (k == nullptr || beta == nullptr || kt == nullptr))) return DP_EINVAL;
   if (!aligned16(k) || !aligned16(kt)) return DP_EINVAL;
@@ -671,6 +671,13 @@ int precond_impl(int elem, const void* k, const float* beta, const float* ret, i
   a.eps = eps;
   a.Ls = Ls;
   a.t0 = t0;
+  // with a workspace for it (p1c_ws) and dk >= 64, the chunked form, whose
+  // hand-over to the exact scan keeps the sequential definition's result
+  if (p1c != nullptr && dk >= 64) {
+    p1c_bind(a, p1c, dk);
+    const hipError_t e = dispatch_precond_chunked(elem, dk, a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? DP_OK : DP_EHIP;
+  }
   const hipError_t e = dispatch_precond(elem, dk, a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DP_OK : DP_EHIP;
 }
@@ -1141,7 +1148,7 @@ int dp_osdn_fwd_workspace_size(int B, int H, int L, int dk, int dv, int chunk, i
   const Shape s{1, B, H, seg_len(L, chunk, segments), dk, dv, chunk};
   const int rc = check_shape(s);
   if (rc != DP_OK) return rc;
-  *bytes = ws_total(s, 2);
+  *bytes = align_up(ws_total(s, 2), kWsAlign) + p1c_ws(B, H, s.L, dk).total;
   return DP_OK;
 }
 
@@ -1183,11 +1190,12 @@ int dp_osdn_fwd_bf16(const void* q, const void* k, const void* v, const float* b
   if (L > 0 && (q == nullptr || k == nullptr || v == nullptr || beta == nullptr || out == nullptr ||
                 kt == nullptr || d_state == nullptr))
     return DP_EINVAL;
-  // Phase 1 runs as the sequential scan here: with one wavefront per head it
-  // leaves most of the chip to the forward of the previous run, which the
-  // chunked form's parallel kernels would compete with.
-  const size_t fws = ws_total(s, 2);
-  if (workspace_bytes < fws || (fws > 0 && workspace == nullptr)) return DP_EWORKSPACE;
+  // the workspace: one run's forward, then (dk >= 64) one run's chunked phase 1
+  const size_t fws = align_up(ws_total(s, 2), kWsAlign);
+  const size_t need = fws + p1c_ws(B, H, len, dk).total;
+  if (workspace_bytes < need || (need > 0 && workspace == nullptr)) return DP_EWORKSPACE;
+  if (((uintptr_t)workspace & (kWsAlign - 1)) != 0) return DP_EWORKSPACE;
+  char* p1c = p1c_ws(B, H, len, dk).total > 0 ? static_cast<char*>(workspace) + fws : nullptr;
   if (nseg == 0) return fwd_impl(2, q, k, k, v, beta, nullptr, 1, B, H, 0, dk, dv, chunk, out, final_state,
                                  h0, workspace, workspace_bytes, DP_STAGE_ALL, stream);
   // Check every run before enqueueing the first.  The runs differ only in
@@ -1211,7 +1219,7 @@ int dp_osdn_fwd_bf16(const void* q, const void* k, const void* v, const float* b
   for (int sg = 0; sg < nseg; ++sg) {
     const int t0 = sg * len, n = L - t0 < len ? L - t0 : len;
     rc = precond_impl(2, k, beta, nullptr, 0, B, H, n, dk, eta, dmin, dmax, eps, d_state, kt, false,
-                      stream, L, t0);
+                      stream, L, t0, false, p1c);
     if (rc != DP_OK) return rc;
     if (pipe != nullptr && (hipEventRecord(pipe->ev[sg], st) != hipSuccess ||
                             hipStreamWaitEvent(st2, pipe->ev[sg], 0) != hipSuccess))

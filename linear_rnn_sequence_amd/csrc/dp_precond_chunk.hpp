@@ -29,25 +29,43 @@ namespace dp {
 constexpr int kP1Chunk = 64;  // tokens per chunk
 constexpr int kP1Ld = kP1Chunk + 4;
 
+// N (4 or 8) values as fp16 at p (8 or 16 bytes, aligned to that)
+template <int N>
+__device__ __forceinline__ void st_f16s(f16_t* p, const float* f) {
+  if constexpr (N == 8) {
+    st_vec16(p, f);
+  } else {
+    f16x4_t v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = (f16_t)f[i];
+    *reinterpret_cast<f16x4_t*>(p) = v;
+  }
+}
+
 // --------------------------------------------------------------------------
 // dp_p1_ut_kernel: one workgroup per (head, chunk), all in parallel.
 template <typename T, int DK>
 __global__ __launch_bounds__(256) void dp_p1_ut_kernel(PrecondArgs p) {
   constexpr int C = kP1Chunk, LDM = kP1Ld, NT = C / 16;
   constexpr int VE = Vec<T>::N;
-  constexpr int LDS_ = DK + 4;   // fp32 s rows
   constexpr int TPR = DK / VE;   // 16-byte granules per key row
   constexpr int KV = C * TPR, KIT = (KV + 255) / 256;
   static_assert(TPR <= 64 && 64 % TPR == 0, "row group must fit in a wavefront");
-  // the squared keys are dead once L is formed: Tm and the inverse's scratch
-  // take their place (three workgroups fit on a CU)
-  constexpr int NBIG = C * LDS_ > C * LDM + 4 * 16 * 17 ? C * LDS_ : C * LDM + 4 * 16 * 17;
-  __shared__ __align__(16) float sS[NBIG];
-  __shared__ __align__(16) float sM[C * LDM];
-  float* const sTm = sS;
-  float* const sSc = sS + C * LDM;
+  // The squared unit keys s, scaled by 2^10 (into fp16's normal range), as
+  // fp16 pairs hi + lo: the Gram matrix is hi hi' + hi lo' + lo hi' on fp16
+  // MFMA (the dropped lo lo' is 2^-22 of a term: fp32 accuracy).  They are
+  // dead once the Gram tiles are in registers: M, Tm and the inverse's
+  // scratch take their place (about 40 KB in all: four workgroups per CU).
+  constexpr int LDH = DK + 8;  // fp16 row stride (16-byte rows)
+  constexpr int NMT = 2 * C * LDM + 4 * 16 * 17;
+  constexpr int NBIG = C * LDH > NMT ? C * LDH : NMT;  // floats
+  __shared__ __align__(16) float sBig[NBIG];
+  f16_t* const sSh = reinterpret_cast<f16_t*>(sBig);
+  f16_t* const sSl = sSh + C * LDH;
+  float* const sTm = sBig;
+  float* const sM = sBig + C * LDM;
+  float* const sSc = sBig + 2 * C * LDM;
   __shared__ float sN[C], sRinv[C], sW[C], sC2[C], sG[C + 1], sLw[C];
-  __shared__ float sLwp[NT * C];  // L w per column block, summed in a fixed order
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
@@ -57,11 +75,10 @@ __global__ __launch_bounds__(256) void dp_p1_ut_kernel(PrecondArgs p) {
   const int c = (int)(chunk % nc);
   const int b = (int)(bh / p.H), h = (int)(bh % p.H);
   const long long row0 = tok_base(p, b) * p.H + h;
-  const long long kstride = (long long)p.H * DK;
   const int t0 = c * C;
   const T* kp = static_cast<const T*>(p.k);
 
-  // 1. key rows -> squared unit keys (fp32) and the row norms
+  // 1. key rows -> squared unit keys (fp16 pairs) and the row norms
   u32x4_t rk[KIT];
 #pragma unroll
   for (int it = 0; it < KIT; ++it) {
@@ -91,11 +108,16 @@ __global__ __launch_bounds__(256) void dp_p1_ut_kernel(PrecondArgs p) {
       ss = group_sum<TPR>(ss);
     const float rinv = __builtin_amdgcn_rsqf(fmaxf(ss, 1e-12f));  // 1 / max(|k|, 1e-6)
     if (idx < KV) {
+      float hi[VE], lo[VE];
 #pragma unroll
-      for (int e = 0; e < VE; e += 4) {
-        const float a0 = f[e] * rinv, a1 = f[e + 1] * rinv, a2 = f[e + 2] * rinv, a3 = f[e + 3] * rinv;
-        *reinterpret_cast<float4*>(sS + r * LDS_ + cg * VE + e) = make_float4(a0 * a0, a1 * a1, a2 * a2, a3 * a3);
+      for (int e = 0; e < VE; ++e) {
+        const float a = f[e] * rinv;
+        const float sc = a * a * 1024.f;
+        hi[e] = (float)(f16_t)sc;
+        lo[e] = sc - hi[e];
       }
+      st_f16s<VE>(sSh + r * LDH + cg * VE, hi);
+      st_f16s<VE>(sSl + r * LDH + cg * VE, lo);
       if (cg == 0) {
         sN[r] = ss * rinv * rinv;  // |kh|^2, as the sequential scan forms it
         sRinv[r] = rinv;
@@ -122,35 +144,49 @@ __global__ __launch_bounds__(256) void dp_p1_ut_kernel(PrecondArgs p) {
     if (lane == C - 1) sG[C] = incl;
   }
   __syncthreads();
-  // 3. L (gated Gram matrix of the squared keys, strictly lower), M = L diag(c2), L w
-  for (int tile = wave; tile < NT * NT; tile += 4) {
-    const int ti = tile / NT, tj = tile % NT;
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    if (tj <= ti) acc = mm_tile<float, DK>(acc, sS, LDS_, ti * 16, sS, LDS_, tj * 16);
-    const int u = tj * 16 + col;
+  // 3. L (gated Gram matrix of the squared keys, strictly lower): wave w forms
+  //    the tiles of column block w in registers, then (once no wave reads the
+  //    keys any more) writes them over the keys' space
+  static_assert(NT == 4, "one column block of tiles per wave");
+  f32x4_t acc[NT];
+#pragma unroll
+  for (int ti = 0; ti < NT; ++ti) {
+    acc[ti] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (wave <= ti) {
+      acc[ti] = mm_tile<f16_t, DK>(acc[ti], sSh, LDH, ti * 16, sSh, LDH, wave * 16);
+      acc[ti] = mm_tile<f16_t, DK>(acc[ti], sSh, LDH, ti * 16, sSl, LDH, wave * 16);
+      acc[ti] = mm_tile<f16_t, DK>(acc[ti], sSl, LDH, ti * 16, sSh, LDH, wave * 16);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int ti = 0; ti < NT; ++ti) {
+    const int u = wave * 16 + col;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int t = ti * 16 + 4 * grp + e;
-      const float l = (u < t) ? __expf(sG[t] - sG[u + 1]) * acc[e] : 0.f;
-      sM[t * LDM + u] = l * sC2[u];
-      float lw = l * sW[u];
-      lw += __shfl_xor(lw, 8);
-      lw += __shfl_xor(lw, 4);
-      lw += __shfl_xor(lw, 2);
-      lw += __shfl_xor(lw, 1);
-      if (col == 0 && tj <= ti) sLwp[tj * C + t] = lw;
+      sM[t * LDM + u] = (u < t) ? __expf(sG[t] - sG[u + 1]) * (acc[ti][e] * 0x1p-20f) : 0.f;
     }
+  }
+  __syncthreads();
+  // L w, and M = L diag(c2) in place: four threads per row, each a quarter of it
+  {
+    const int t = tid >> 2, q = tid & 3;
+    float lw = 0.f;
+#pragma unroll
+    for (int u = q * (C / 4); u < (q + 1) * (C / 4); ++u) {
+      const float l = sM[t * LDM + u];
+      lw = fmaf(l, sW[u], lw);
+      sM[t * LDM + u] = l * sC2[u];
+    }
+    lw += __shfl_xor(lw, 1);
+    lw += __shfl_xor(lw, 2);
+    if (q == 0) sLw[t] = lw;
   }
   __syncthreads();
   // 4. Tm = (I + M)^{-1}: diagonal 16 x 16 blocks by forward substitution (one
   //    16-lane group per block, one column per lane), then the off-diagonal
   //    blocks level by level, Tm_ij = -Tm_ii sum_{k=j}^{i-1} M_ik Tm_kj
-  //    (meanwhile wave 1 sums L w over its column blocks)
-  if (wave == 1) {
-    float lw = 0.f;
-    for (int tb = 0; tb <= (lane >> 4); ++tb) lw += sLwp[tb * C + lane];
-    sLw[lane] = lw;
-  }
   if (wave == 0) {
     const int gb = lane >> 4, cc = lane & 15;
     if (gb < NT) {
@@ -213,23 +249,29 @@ __global__ __launch_bounds__(256) void dp_p1_ut_kernel(PrecondArgs p) {
 }
 
 // --------------------------------------------------------------------------
-// dp_p1_chain_kernel: one workgroup per head, sequential over its chunks.
+// dp_p1_chain_kernel: one workgroup per head, sequential over its chunks.  The
+// chunk's squared unit keys and Tm stay in registers where they were loaded
+// (a row group of DK / (16 / sizeof(T)) lanes per key row, 16 lanes per Tm
+// row); the products are lane partials summed within the group by DPP, and
+// the end-of-chunk d sums the row groups' partials through LDS.  Its barriers
+// order LDS only, so the loads of the chunk after next stay in flight; every
+// global load and store in the loop is issued by every lane on every path
+// (clamped addresses, duplicate stores of equal values), so the compiler
+// counts the loads in flight exactly and waits only for the ones it uses.
 template <typename T, int DK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void dp_p1_chain_kernel(PrecondArgs p) {
-  constexpr int C = kP1Chunk, LDM = kP1Ld;
+  constexpr int C = kP1Chunk;
   constexpr int VE = Vec<T>::N;
-  constexpr int LDS_ = DK + 4;
-  constexpr int TPR = DK / VE;
-  constexpr int KV = C * TPR, KIT = (KV + 255) / 256;
-  constexpr int TMIT = C * C / 4 / 256;  // float4 pieces of Tm per thread
-  constexpr int NP = 256 / DK;           // partial sums per coordinate of the end-of-chunk d
-  static_assert(C * C / 4 == 256 * TMIT && 256 % DK == 0 && C % NP == 0, "thread layout");
-  __shared__ __align__(16) float sS[C * LDS_];
-  __shared__ __align__(16) float sTm[C * LDM];
-  __shared__ float sD[DK], sPart[NP * DK];
-  __shared__ float sW[C], sC2[C], sG[C + 1], sV[C], sRhs[C], sCoef[C];
+  constexpr int TPR = DK / VE;           // lanes per key row
+  constexpr int KIT = C * TPR / 256;     // key rows per thread
+  constexpr int RPI = 256 / TPR;         // key rows per pass of the workgroup (row groups)
+  constexpr int TMIT = C * C / 4 / 256;  // Tm rows per thread (four values each)
+  static_assert(C * TPR == 256 * KIT && TMIT == 4 && TPR <= 64 && 64 % TPR == 0, "thread layout");
+  __shared__ __align__(16) float sPart[RPI * DK];
+  __shared__ __align__(16) float sRhs[C];
+  __shared__ float sD[DK], sCoef[C], sW[C], sC2[C], sG[C + 1], sV[C];
 
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, cg = tid % TPR, rg = tid / TPR;
   const int nc = (p.L + C - 1) / C;
   const long long bh = blockIdx.x;
   const int b = (int)(bh / p.H), h = (int)(bh % p.H);
@@ -238,68 +280,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   // a chunk's operands in registers: two sets, loaded two chunks ahead of use
   struct Stage {
-    u32x4_t rk[KIT];
-    float rinv[KIT];
-    float4 rtm[TMIT];
-    float4 rfac;
+    u32x4_t rk[KIT];    // key granule of rows rg + RPI it
+    float4 rf[KIT];     // their factors (1/|k|, w, c2, G)
+    float4 rtm[TMIT];   // Tm row tid / 16 + 16 it, columns 4 (tid % 16) ..
+    float4 rfac;        // factors of row tid (tid < C)
     float rv, rgt;
   };
-  auto prefetch = [&](Stage& S, int c) {
+  auto prefetch = [&](Stage& S, int c) {  // 0 <= c < nc
     const long long chunk = bh * nc + c;
     const int t0 = c * C;
 #pragma unroll
     for (int it = 0; it < KIT; ++it) {
-      const int idx = tid + it * 256;
-      const int r = idx / TPR, cg = idx % TPR;
-      S.rk[it] = u32x4_t{0u, 0u, 0u, 0u};
-      S.rinv[it] = 0.f;
-      if (idx < KV && t0 + r < p.L) {
-        S.rk[it] = ld16(kp + (row0 + (long long)(t0 + r) * p.H) * DK + cg * VE);
-        S.rinv[it] = p.wsFac[chunk * C + r].x;
-      }
+      const int r = rg + RPI * it;
+      const int tr = min(t0 + r, p.L - 1);  // rows past the end: loaded in bounds, then zeroed
+      const u32x4_t v = ld16(kp + (row0 + (long long)tr * p.H) * DK + cg * VE);
+      const bool in = t0 + r < p.L;
+      S.rk[it] = u32x4_t{in ? v[0] : 0u, in ? v[1] : 0u, in ? v[2] : 0u, in ? v[3] : 0u};
+      S.rf[it] = p.wsFac[chunk * C + r];
     }
 #pragma unroll
     for (int it = 0; it < TMIT; ++it)
       S.rtm[it] = reinterpret_cast<const float4*>(p.wsTm + chunk * C * C)[tid + it * 256];
-    S.rfac = make_float4(0.f, 0.f, 0.f, 0.f);
-    S.rv = 0.f;
-    S.rgt = 0.f;
-    if (tid < C) {
-      S.rfac = p.wsFac[chunk * C + tid];
-      S.rv = p.wsV[chunk * C + tid];
-    }
-    if (tid == 0) S.rgt = p.wsGT[chunk];
+    S.rfac = p.wsFac[chunk * C + (tid & (C - 1))];
+    S.rv = p.wsV[chunk * C + (tid & (C - 1))];
+    S.rgt = p.wsGT[chunk];
   };
 
   if (tid < DK) sD[tid] = p.d_ones ? 1.f : p.d[bh * DK + tid];
   if (tid == 0) p.restart[bh] = nc;
   auto body = [&](Stage& S, int c) {
     const long long chunk = bh * nc + c;
-    __syncthreads();  // the previous chunk is done with every buffer
-    const u32x4_t* rk = S.rk;
-    const float* rinv = S.rinv;
-#pragma unroll
-    for (int it = 0; it < KIT; ++it) {
-      const int idx = tid + it * 256;
-      const int r = idx / TPR, cg = idx % TPR;
-      if (idx < KV) {
-        float f[VE];
-        unpack16(rk[it], f, T{});
-#pragma unroll
-        for (int e = 0; e < VE; e += 4) {
-          const float a0 = f[e] * rinv[it], a1 = f[e + 1] * rinv[it], a2 = f[e + 2] * rinv[it],
-                      a3 = f[e + 3] * rinv[it];
-          *reinterpret_cast<float4*>(sS + r * LDS_ + cg * VE + e) =
-              make_float4(a0 * a0, a1 * a1, a2 * a2, a3 * a3);
-        }
-      }
-    }
-#pragma unroll
-    for (int it = 0; it < TMIT; ++it) {
-      const int q = tid + it * 256;
-      const int i = (4 * q) / C, j = (4 * q) % C;
-      *reinterpret_cast<float4*>(sTm + i * LDM + j) = S.rtm[it];
-    }
+    block_sync_lds();  // d of this chunk's start is in sD; the last chunk's reads are done
     if (tid < C) {
       sW[tid] = S.rfac.y;
       sC2[tid] = S.rfac.z;
@@ -307,59 +318,91 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       sV[tid] = S.rv;
     }
     if (tid == 0) sG[C] = S.rgt;
-    __syncthreads();
-    if (tid < DK) p.dstart[chunk * DK + tid] = sD[tid];
-    if (c + 2 < nc) prefetch(S, c + 2);  // lands while this chunk and the next are computed
-    // p_t = <s_t, d_0>: four threads per token
-    {
-      const int t = tid >> 2, q = tid & 3;
-      float acc = 0.f;
-#pragma unroll 8
-      for (int j = q * (DK / 4); j < (q + 1) * (DK / 4); ++j) acc = fmaf(sS[t * LDS_ + j], sD[j], acc);
-      acc += __shfl_xor(acc, 1);
-      acc += __shfl_xor(acc, 2);
-      if (q == 0) sRhs[t] = __expf(sG[t]) * acc;
-    }
-    __syncthreads();
-    // a = Tm (e^G o p) + v;  gamma = w - c2 a;  coef_u = e^{G_C - G_{u+1}} gamma_u
-    {
-      const int t = tid >> 2, q = tid & 3;
-      float acc = 0.f;
+    p.dstart[chunk * DK + tid % DK] = sD[tid % DK];
+    // the squared unit keys of this thread's rows and columns
+    float sv[KIT][VE];
 #pragma unroll
-      for (int u = q * (C / 4); u < (q + 1) * (C / 4); ++u) acc = fmaf(sTm[t * LDM + u], sRhs[u], acc);
-      acc += __shfl_xor(acc, 1);
-      acc += __shfl_xor(acc, 2);
-      if (q == 0) {
-        const float gm = fmaf(-sC2[t], acc + sV[t], sW[t]);
-        p.gam[chunk * C + t] = gm;
-        sCoef[t] = __expf(sG[C] - sG[t + 1]) * gm;
+    for (int it = 0; it < KIT; ++it) {
+      float f[VE];
+      unpack16(S.rk[it], f, T{});
+#pragma unroll
+      for (int e = 0; e < VE; ++e) {
+        const float a = f[e] * S.rf[it].x;
+        sv[it][e] = a * a;
       }
     }
-    __syncthreads();
-    // d_C = e^{G_C} d_0 + sum_u coef_u s_u
-    {
-      const int j = tid % DK, part = tid / DK;
+    float dv[VE];
+#pragma unroll
+    for (int e = 0; e < VE; ++e) dv[e] = sD[cg * VE + e];
+    // p_t = <s_t, d_0>, rhs_t = e^{G_t} p_t
+#pragma unroll
+    for (int it = 0; it < KIT; ++it) {
       float acc = 0.f;
-#pragma unroll 8
-      for (int u = part * (C / NP); u < (part + 1) * (C / NP); ++u) acc = fmaf(sS[u * LDS_ + j], sCoef[u], acc);
-      sPart[part * DK + j] = acc;
+#pragma unroll
+      for (int e = 0; e < VE; ++e) acc = fmaf(sv[it][e], dv[e], acc);
+      if constexpr (TPR <= 16)
+        acc = dpp_group_sum<TPR>(acc);
+      else
+        acc = group_sum<TPR>(acc);
+      if (cg == 0) sRhs[rg + RPI * it] = __expf(S.rf[it].w) * acc;
     }
-    __syncthreads();
+    block_sync_lds();
+    // a = Tm rhs + v;  gamma = w - c2 a;  coef_u = e^{G_C - G_{u+1}} gamma_u
+    {
+      const float4 rh = reinterpret_cast<const float4*>(sRhs)[tid & 15];
+#pragma unroll
+      for (int it = 0; it < TMIT; ++it) {
+        const float4 tm = S.rtm[it];
+        float x = fmaf(tm.x, rh.x, fmaf(tm.y, rh.y, fmaf(tm.z, rh.z, tm.w * rh.w)));
+        x = dpp_group_sum<16>(x);
+        const int i = (tid >> 4) + 16 * it;
+        // every lane of the row's group holds the sum: all store the same values
+        const float gm = fmaf(-sC2[i], x + sV[i], sW[i]);
+        p.gam[chunk * C + i] = gm;
+        sCoef[i] = __expf(sG[C] - sG[i + 1]) * gm;
+      }
+    }
+    prefetch(S, min(c + 2, nc - 1));  // lands while this chunk and the next are computed
+    block_sync_lds();
+    // d_C = e^{G_C} d_0 + sum_u coef_u s_u: each row group's partial, then their sum
+    {
+      float part[VE];
+#pragma unroll
+      for (int e = 0; e < VE; ++e) part[e] = 0.f;
+#pragma unroll
+      for (int it = 0; it < KIT; ++it) {
+        const float cf = sCoef[rg + RPI * it];
+#pragma unroll
+        for (int e = 0; e < VE; ++e) part[e] = fmaf(cf, sv[it][e], part[e]);
+      }
+#pragma unroll
+      for (int e = 0; e < VE; e += 4)
+        *reinterpret_cast<float4*>(sPart + rg * DK + cg * VE + e) =
+            make_float4(part[e], part[e + 1], part[e + 2], part[e + 3]);
+    }
+    block_sync_lds();
     if (tid < DK) {
       float x = __expf(sG[C]) * sD[tid];
-#pragma unroll
-      for (int q = 0; q < NP; ++q) x += sPart[q * DK + tid];
+#pragma unroll 8
+      for (int q = 0; q < RPI; ++q) x += sPart[q * DK + tid];
       sD[tid] = x;
     }
   };
   Stage sa, sb;
-  if (nc > 0) prefetch(sa, 0);
-  if (nc > 1) prefetch(sb, 1);
-  for (int c = 0; c < nc; c += 2) {
-    body(sa, c);
-    if (c + 1 < nc) body(sb, c + 1);
+  if (nc > 0) {
+    prefetch(sa, 0);
+    __builtin_amdgcn_sched_barrier(0);  // the second set's loads after all of the first's, as in the loop
+    prefetch(sb, min(1, nc - 1));
   }
-  __syncthreads();
+  // pairs of chunks, then an odd last one (the loop's back edge follows the
+  // second set's chunk only, so the wait counts at its head are exact)
+  int c = 0;
+  for (; c + 1 < nc; c += 2) {
+    body(sa, c);
+    body(sb, c + 1);
+  }
+  if (c < nc) body(sa, c);
+  block_sync_lds();
   if (tid < DK) p.d[bh * DK + tid] = sD[tid];
 }
 

@@ -351,6 +351,24 @@ def test_osdn_fwd_checks_every_run_before_the_first(lib):
     assert call(dk=24) == E.DP_ENOTSUP
 
 
+def test_osdn_fwd_workspace_size(lib):
+    """One run's forward (the run of ceil(ceil(L / segments) / chunk) chunks),
+    then for dk >= 64 one run's chunked phase 1: per 64-token chunk the 64 x 64
+    inverse, v, the token factors, the chunk's log-retention, its start d and
+    gamma; one restart index per head; each region 256-byte aligned."""
+    up = lambda x: -(-x // 256) * 256
+    for B, H, L, dk, dv, C, S in ((8, 16, 4096, 128, 128, 64, 4), (2, 3, 300, 64, 32, 32, 3), (1, 2, 100, 32, 32, 32, 2)):
+        n = ctypes.c_size_t(0)
+        assert lib.dp_osdn_fwd_workspace_size(B, H, L, dk, dv, C, S, ctypes.byref(n)) == 0
+        run = -(-(-(-L // S)) // C) * C
+        f = ctypes.c_size_t(0)
+        assert lib.dp_fwd_workspace_size(1, B, H, run, dk, dv, C, 2, ctypes.byref(f)) == 0
+        nch = B * H * -(-run // 64)
+        chunked = (up(nch * 64 * 64 * 4) + 2 * up(nch * 64 * 4) + up(nch * 64 * 16) + up(nch * 4)
+                   + up(nch * dk * 4) + up(B * H * 4)) if dk >= 64 else 0
+        assert n.value == up(f.value) + chunked, (B, H, L, dk)
+
+
 def test_pipeline_handle_arguments(lib):
     E = dp.binding
     assert lib.dp_pipeline_create(None) == E.DP_EINVAL

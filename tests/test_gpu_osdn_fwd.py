@@ -1,9 +1,13 @@
 """GPU checks of the pipelined write-key forward (dp_osdn_fwd_bf16).
 
-It runs the same kernels on the same chunks as OSDN phase 1 followed by the
-write-key forward, cut into token runs (the state and d pass between runs in
-fp32), so its results must equal the two-call path bit for bit; cases with and
-without binding clamps are also checked against the fp64 oracle.
+It runs OSDN phase 1 followed by the write-key forward, cut into token runs
+(the state and d pass between runs in fp32).  With the pipeline and without it
+the results are the same bit for bit.  For dk < 64 phase 1 is the sequential
+scan of dp_osdn_precond_bf16, so they also equal the two-call path bit for
+bit; for dk >= 64 phase 1 takes the chunked form (solved 64-token chunks, with
+the sequential scan again from the first chunk where a clamp comes near),
+which rounds differently: there d meets the two-call path's to fp32 rounding
+and every result meets the oracle.  Clamping cases check that hand-over.
 """
 import pytest
 import torch
@@ -72,18 +76,32 @@ def test_pipelined_equals_two_calls(B, H, L, dk, dv, chunk, segments, with_h0):
     torch.cuda.synchronize()
     pipe.close()
     for name, x, y, r in zip(("out", "final_state", "kt", "d"), got, seq, ref):
-        assert torch.equal(x, r), f"{name} (pipelined) differs from the two-call path"
-        assert torch.equal(y, r), f"{name} (runs in order, no pipeline) differs from the two-call path"
+        assert torch.equal(x, y), f"{name}: the pipelined and in-order runs differ"
+        if dk < 64:
+            assert torch.equal(x, r), f"{name} differs from the two-call path"
+    if dk >= 64:
+        # d is fp32 throughout: it meets the sequential scan's to fp32 rounding;
+        # the bf16 results meet the oracle (two bf16 roundings of nearly equal
+        # values may differ by an ulp, so they are not compared to each other)
+        e = rel_err(f64(got[3]), f64(ref[3]))
+        say(f"  d: vs two calls {e:.3e}")
+        assert e <= TOL["f32"]
+        orc = oracle_layer(q, k1, v1, b1, h0=h0)
+        for name, x, r in zip(("out", "final_state", "kt", "d"), got, orc):
+            e = rel_err(f64(x), r)
+            say(f"  {name}: err {e:.3e}")
+            assert e <= TOL["bf16"], f"{name}: err {e:.3e}"
 
 
 def test_one_pipeline_serves_calls_from_two_threads():
     """A handle may be shared: each call holds it for its enqueue sequence, so
-    calls from two host threads on their own streams give the two-call results."""
+    calls from two host threads on their own streams give the results of one
+    call without a pipeline."""
     import threading
 
     B, H, L, dk, dv = 1, 2, 300, 128, 128
     q, k1, v1, b1, _ = inputs(B, H, L, dk, dv)
-    ref = two_calls(q, k1, v1, b1, None, 64)
+    ref = dp.osdn_fwd(q, k1, v1, b1, segments=4)
     torch.cuda.synchronize()
     pipe = dp.Pipeline()
     results = [None, None]
@@ -105,7 +123,7 @@ def test_one_pipeline_serves_calls_from_two_threads():
     pipe.close()
     for got in results:
         for name, x, r in zip(("out", "final_state", "kt", "d"), got, ref):
-            assert torch.equal(x, r), f"{name} differs from the two-call path"
+            assert torch.equal(x, r), f"{name} differs from the call without a pipeline"
 
 
 def test_failed_call_leaves_outputs_untouched():
@@ -170,8 +188,9 @@ CLAMP = [  # eta, dmax; the phase-1 clamp binds in: (dk 128, L 300, c5 inputs)
 @pytest.mark.parametrize("eta,dmax", CLAMP)
 def test_clamping_box_matches_oracle(eta, dmax):
     """With the upper bound of the box binding (on some heads or all, late or
-    within the first chunk) the pipelined call meets the oracle, clamps
-    included, and equals the two-call path."""
+    within the first chunk) the chunked phase 1 hands those heads to the
+    sequential scan from the chunk where a step first came near the bound:
+    the call meets the oracle, clamps included, and the two-call path's d."""
     B, H, L, dk, dv = 2, 3, 300, 128, 128
     say(f"case osdn_fwd clamps B={B} H={H} L={L} eta={eta} dmax={dmax}")
     q, k1, v1, b1, _ = inputs(B, H, L, dk, dv)
@@ -188,4 +207,4 @@ def test_clamping_box_matches_oracle(eta, dmax):
         say(f"  {name}: err {e:.3e}")
         assert e <= TOL["bf16"], f"{name}: err {e:.3e}"
     assert torch.all(got[3] <= dmax) and torch.all(got[3] >= 0.5)
-    assert torch.equal(got[2], kt) and torch.equal(got[3], d)
+    assert rel_err(f64(got[3]), f64(d)) <= TOL["f32"]
