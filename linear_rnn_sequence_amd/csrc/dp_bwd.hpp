@@ -173,6 +173,11 @@ struct RawSlice {
 #pragma unroll
     for (int i = 0; i < E; ++i) v[i] = T{};
   }
+  // zero unless `in` (a select per element: no branch around the load before it)
+  __device__ __forceinline__ void keep(bool in) {
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] = in ? v[i] : T{};
+  }
   __device__ __forceinline__ float operator[](int i) const { return to_f32(v[i]); }
 };
 
@@ -197,7 +202,11 @@ __device__ __forceinline__ void bwd_readout(const BwdArgs& p, int b, int h, int 
 
 // The operands every sequential kernel needs per chunk: the thread's slice of
 // the unit keys (with 1/|k| of its row), its four entries of T, and for
-// threads t < C the scalars of sub-step t (beta, G, G of the chunk's last).
+// threads t < C the scalars of sub-step t (the raw beta, G, G of the chunk's
+// last).  Every lane loads on every path (rows past the end read row 0, in
+// bounds, and are zeroed by a select), so the compiler counts the loads in
+// flight exactly and waits only where a value is used, a chunk later; beta
+// is clamped where it is committed.
 template <typename T, int DK, int C, bool ASYM = false>
 struct BwdChunkCommon {
   static constexpr int TPR = 256 / C;  // threads per sub-step row
@@ -211,22 +220,23 @@ struct BwdChunkCommon {
   __device__ __forceinline__ void load(const BwdArgs& p, int b, int h, int c, long long chunk) {
     const int tid = threadIdx.x;
     const long long row = bwd_row(p, b, h, c * C + tid / TPR);
-    if (row >= 0) {
-      k.load(static_cast<const T*>(p.k) + row * DK + (tid % TPR) * EK);
-      if constexpr (ASYM) w.load(static_cast<const T*>(p.kt) + row * DK + (tid % TPR) * EK);
-      rinv = p.wsS[chunk * C + tid / TPR].x;
-    } else {
-      k.zero();
-      if constexpr (ASYM) w.zero();
-      rinv = 0.f;
+    const bool in = row >= 0;
+    const long long rr = in ? row : 0;
+    k.load(static_cast<const T*>(p.k) + rr * DK + (tid % TPR) * EK);
+    k.keep(in);
+    if constexpr (ASYM) {
+      w.load(static_cast<const T*>(p.kt) + rr * DK + (tid % TPR) * EK);
+      w.keep(in);
     }
+    const float ri = p.wsS[chunk * C + tid / TPR].x;
+    rinv = in ? ri : 0.f;
     t = *reinterpret_cast<const float4*>(p.wsT + chunk * C * C + 4 * tid);
-    if (tid < C) {
-      const long long rs = bwd_row(p, b, h, c * C + tid);
-      beta = rs >= 0 ? clamp_keep_nan(p.beta[rs], 0.f, 2.f) : 0.f;
-      g = p.wsS[chunk * C + tid].y;
-      gl = p.wsS[chunk * C + C - 1].y;
-    }
+    const int ts = tid & (C - 1);  // threads t < C keep sub-step t's scalars
+    const long long rs = bwd_row(p, b, h, c * C + ts);
+    const float bt = p.beta[rs >= 0 ? rs : 0];
+    beta = rs >= 0 ? bt : 0.f;
+    g = p.wsS[chunk * C + ts].y;
+    gl = p.wsS[chunk * C + C - 1].y;
   }
   template <int LDK, int LDC, typename OT>
   __device__ __forceinline__ void commit(OT* sK, OT* sT, OT* sW = nullptr) const {
@@ -299,10 +309,8 @@ __device__ __forceinline__ void bwd_states_body(const BwdArgs& p, unsigned char*
     const long long chunk = (long long)bh * p.nc + c;
     nx.x.load(p, b, h, c, chunk);
     const long long row = bwd_row(p, b, h, c * C + tid / TPR);
-    if (row >= 0)
-      nx.v.load(vp + row * p.dvd + v0 + (tid % TPR) * EV);
-    else
-      nx.v.zero();
+    nx.v.load(vp + (row >= 0 ? row : 0) * p.dvd + v0 + (tid % TPR) * EV);
+    nx.v.keep(row >= 0);
   };
 
   // the fp32 state: tile wave + 4u of the DK x BV block, rows 4 grp + e, column col
@@ -332,7 +340,7 @@ __device__ __forceinline__ void bwd_states_body(const BwdArgs& p, unsigned char*
       for (int i = 0; i < EV; ++i) vd[i] = nx.v[i];
     }
     if (tid < C) {
-      sB[tid] = nx.x.beta;
+      sB[tid] = clamp_keep_nan(nx.x.beta, 0.f, 2.f);
       sEG[tid] = expf(nx.x.g);
       sEL[tid] = expf(nx.x.gl - nx.x.g);
     }
@@ -349,7 +357,7 @@ __device__ __forceinline__ void bwd_states_body(const BwdArgs& p, unsigned char*
       }
     }
     __syncthreads();
-    if (c + 1 < p.nc) prefetch(nx, c + 1);  // lands while this chunk is computed
+    prefetch(nx, min(c + 1, p.nc - 1));  // lands while this chunk is computed (the last one again at the end)
     // beta X = beta (V - diag(e^G) K H0)
     for (int tile = wave; tile < NCT * NVT; tile += 4) {
       const int ct = tile / NVT, nt = tile % NVT;
@@ -460,15 +468,14 @@ __device__ __forceinline__ void bwd_dstate_body(const BwdArgs& p, unsigned char*
     nx.x.load(p, b, h, c, chunk);
     long long tok;
     bwd_readout(p, b, h, c, C, tid / TPQ, &tok, &nx.loc);
-    if (tok >= 0) {
-      nx.q.load(qp + tok * DK + (tid % TPQ) * EQ);
-      nx.o.load(dop + tok * p.dvd + v0 + (tid % TPQ) * EO);
-      nx.g = p.wsS[chunk * C + nx.loc].y;
-    } else {
-      nx.q.zero();
-      nx.o.zero();
-      nx.g = 0.f;
-    }
+    const bool in = tok >= 0;  // loads on every path, then selects (as in BwdChunkCommon)
+    const long long tt = in ? tok : 0;
+    nx.q.load(qp + tt * DK + (tid % TPQ) * EQ);
+    nx.q.keep(in);
+    nx.o.load(dop + tt * p.dvd + v0 + (tid % TPQ) * EO);
+    nx.o.keep(in);
+    const float gg = p.wsS[chunk * C + (in ? nx.loc : 0)].y;
+    nx.g = in ? gg : 0.f;
   };
 
   for (int idx = tid; idx < DK * BV; idx += 256) {
@@ -495,7 +502,7 @@ __device__ __forceinline__ void bwd_dstate_body(const BwdArgs& p, unsigned char*
       if (tid % TPQ == 0) sLoc[rr] = nx.loc;
     }
     if (tid < C) {
-      sB[tid] = nx.x.beta;
+      sB[tid] = clamp_keep_nan(nx.x.beta, 0.f, 2.f);
       sG[tid] = nx.x.g;
       sEG[tid] = expf(nx.x.g);
       sEL[tid] = expf(nx.x.gl - nx.x.g);
@@ -507,7 +514,7 @@ __device__ __forceinline__ void bwd_dstate_body(const BwdArgs& p, unsigned char*
       ddst[(long long)d * p.dvd + n] = sdHo[d * LDB + n];
     }
     __syncthreads();
-    if (c > 0) prefetch(nx, c - 1);  // lands while this chunk is computed
+    prefetch(nx, max(c - 1, 0));  // lands while this chunk is computed (the first one again at the end)
     // P = masked, gated scores (RT x C)
     for (int tile = wave; tile < NRT * NCT; tile += 4) {
       const int rt = tile / NCT, ct = tile % NCT;
@@ -517,7 +524,9 @@ __device__ __forceinline__ void bwd_dstate_body(const BwdArgs& p, unsigned char*
       for (int e = 0; e < 4; ++e) {
         const int r = rt * 16 + 4 * grp + e, j = ct * 16 + col;
         const int l = sLoc[r];
-        sP[r * LDC + j] = from_f32<OT>((l >= 0 && j <= l) ? acc[e] * expf(sG[l] - sG[j]) : 0.f);
+        // read for every lane (in bounds), then masked: no per-lane branch around the reads
+        const float ex = expf(sG[max(l, 0)] - sG[j]);
+        sP[r * LDC + j] = from_f32<OT>((l >= 0 && j <= l) ? acc[e] * ex : 0.f);
       }
     }
     __syncthreads();
@@ -724,7 +733,7 @@ __global__ __launch_bounds__(256) void dp_bwd_chunk_kernel(BwdArgs p) {
   }
   __syncthreads();
   if (tid < C) {
-    sB[tid] = cx.beta;
+    sB[tid] = clamp_keep_nan(cx.beta, 0.f, 2.f);
     sEG[tid] = expf(sG[tid]);
     sEL[tid] = expf(sG[C - 1] - sG[tid]);
   }
@@ -861,7 +870,8 @@ __global__ __launch_bounds__(256) void dp_bwd_chunk_kernel(BwdArgs p) {
     for (int e = 0; e < 4; ++e) {
       const int i = cit * 16 + 4 * grp + e;
       const bool ok = j < i && sRow[i] >= 0;
-      const float ex = ok ? expf(sG[i] - sG[j]) : 0.f;
+      const float exr = expf(sG[i] - sG[j]);  // every lane reads, then the mask selects
+      const float ex = ok ? exr : 0.f;
       const float fm = ok ? -acc[e] * ex : 0.f;  // F_ij e^{G_i - G_j}
       const float z = fm * sB[i];
       const float zs = z * accS[e];
@@ -886,7 +896,8 @@ __global__ __launch_bounds__(256) void dp_bwd_chunk_kernel(BwdArgs p) {
       const int r = rrt * 16 + 4 * grp + e;
       const int l = sLoc[r];
       const bool ok = l >= 0 && j <= l;
-      const float gm = ok ? aP[e] * expf(sG[l] - sG[j]) : 0.f;
+      const float exr = expf(sG[max(l, 0)] - sG[j]);  // in bounds for every lane; masked below
+      const float gm = ok ? aP[e] * exr : 0.f;
       const float pr = gm * accQK[e];
       const float rs = sum16(pr);
       if (col == 0 && l >= 0) atomicAdd(&sDG[l], rs);
