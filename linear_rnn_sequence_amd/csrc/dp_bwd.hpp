@@ -697,34 +697,33 @@ __global__ __launch_bounds__(256) void dp_bwd_chunk_kernel(BwdArgs p) {
   RawSlice<T, EV> nv;
   RawSlice<OT, EV> ndu;
   RawSlice<T, EO> ndo;
+  // every lane loads on every path (rows past the end read row 0, in bounds,
+  // then a select zeroes them), so the compiler's wait counts stay exact
+  const bool vin = vrow >= 0, oin = otok >= 0;
+  const long long vrr = vin ? vrow : 0, orow = oin ? otok : 0;
   auto prefetch = [&](int vb) {
     const int v0 = vb * BV;
     nh0.load(hsrc + (long long)hd * p.dvd + v0 + hn);
     ndh.load(dhsrc + (long long)hd * p.dvd + v0 + hn);
     ndu.load(dusrc + (long long)vr * p.dvd + v0 + vn);
-    if (vrow >= 0)
-      nv.load(vp + vrow * p.dvd + v0 + vn);
-    else
-      nv.zero();
-    if (otok >= 0)
-      ndo.load(dop + otok * p.dvd + v0 + on);
-    else
-      ndo.zero();
+    nv.load(vp + vrr * p.dvd + v0 + vn);
+    nv.keep(vin);
+    ndo.load(dop + orow * p.dvd + v0 + on);
+    ndo.keep(oin);
   };
-  // the chunk's keys, T and readout queries, then value block 0, all issued up front
+  // the chunk's scalars first (committed at once), then its keys, T and readout
+  // queries and value block 0, which land while the chunk's scores are formed
+  const float2 sc = p.wsS[chunk * C + (tid & (C - 1))];
   BwdChunkCommon<T, DK, C, ASYM> cx;
   cx.load(p, b, h, c, chunk);
   constexpr int EQ = DK / TPQ;
   RawSlice<T, EQ> cq;
-  if (otok >= 0)
-    cq.load(static_cast<const T*>(p.q) + otok * DK + (tid % TPQ) * EQ);
-  else
-    cq.zero();
-  if (p.nvb > 0) prefetch(0);  // lands while the chunk's scores are formed
+  cq.load(static_cast<const T*>(p.q) + orow * DK + (tid % TPQ) * EQ);
+  cq.keep(oin);
+  if (p.nvb > 0) prefetch(0);
 
   bwd_index_chunk<C>(p, b, h, c, RT, meta);
   if (tid < C) {
-    const float2 sc = p.wsS[chunk * C + tid];
     sRinv[tid] = sc.x;
     sG[tid] = sc.y;
     sDB[tid] = 0.f;
@@ -774,7 +773,7 @@ __global__ __launch_bounds__(256) void dp_bwd_chunk_kernel(BwdArgs p) {
 #pragma unroll
     for (int i = 0; i < EO; ++i) sdO[orr * LDB + on + i] = from_f32<OT>(ndo[i]);
     __syncthreads();
-    if (vb + 1 < p.nvb) prefetch(vb + 1);  // lands while this block is computed
+    prefetch(min(vb + 1, p.nvb - 1));  // lands while this block is computed (the last one again at the end)
     if (wave < NCT) {
       // X = V - diag(e^G) K H0
       const int ct = wave;
