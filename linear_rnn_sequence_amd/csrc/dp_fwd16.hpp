@@ -209,32 +209,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void d
   const bf16_t* qp = static_cast<const bf16_t*>(p.q);
   unsigned char* wsc = static_cast<unsigned char*>(p.wsT) + chunk * W.bytes;
 
-  // 1. global loads: key rows, readout query rows, beta, gate
+  // 1. global loads: key rows, readout query rows, beta, gate.  Every lane
+  //    loads on every path: rows past the end (or the padding of a ragged
+  //    chunk) read the chunk's first sub-step, which exists, and are masked
+  //    where the value is first used.  (A load inside a branch joins a
+  //    zero-initialised copy of its register, and that copy waits for the
+  //    load at once: the loads would go out as several round trips.)
   constexpr bool QREG = prep_q_in_regs(DK);
   constexpr int QKS = DK / 32;  // 32-deep steps of a query fragment row
   u32x4_t rk[KIT], rq[QIT], rkw[ASYM ? KIT : 1];
+  bool kin[KIT], qin[QREG ? NRT : QIT];
+  auto sub_row = [&](int s) {  // row of sub-step s in the [.., n_h, DK] tensors, without the column
+    const int t = fastdiv(s, p.nh_magic, p.nh_shift);
+    return ((tok0 + (long long)t * p.H) * n_h + (s - t * n_h)) * DK;
+  };
 #pragma unroll
   for (int it = 0; it < KIT; ++it) {
     const int idx = tid + it * 256;
     const int r = idx / TPR, cg = idx % TPR;
     const int s = s0 + r;
-    rk[it] = u32x4_t{0u, 0u, 0u, 0u};
-    if constexpr (ASYM) rkw[it] = u32x4_t{0u, 0u, 0u, 0u};
-    if (idx < KV && s < N) {
-      const int t = fastdiv(s, p.nh_magic, p.nh_shift);
-      const long long row = ((tok0 + (long long)t * p.H) * n_h + (s - t * n_h)) * DK + cg * 8;
-      rk[it] = ld16(kp + row);
-      if constexpr (ASYM) rkw[it] = ld16(kwp + row);
-    }
+    kin[it] = idx < KV && s < N;
+    const long long row = sub_row(kin[it] ? s : s0) + cg * 8;
+    rk[it] = ld16(kp + row);
+    if constexpr (ASYM) rkw[it] = ld16(kwp + row);
   }
-  float braw = 0.f, lam = 0.f;
-  if (tid < C && s0 + tid < N) {
-    const int s = s0 + tid;
+  // beta and the gate of sub-step tid (threads tid < C; the others read sub-step s0)
+  const bool bin = tid < C && s0 + tid < N;
+  float braw, graw = 1.f;
+  bool gin;
+  {
+    const int s = bin ? s0 + tid : s0;
     const int t = fastdiv(s, p.nh_magic, p.nh_shift);
     const int j = s - t * n_h;
     const long long tok = tok0 + (long long)t * p.H;
     braw = p.beta[tok * n_h + j];
-    if (p.g != nullptr && j == 0) lam = logf(fmaxf(p.g[tok], FLT_MIN));
+    if (p.g != nullptr) graw = p.g[tok];
+    gin = bin && j == 0 && p.g != nullptr;
   }
 
   // queries: loaded with the keys (one memory round trip per chunk) when
@@ -251,16 +261,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void d
         const int i = it * 16 + (lane & 15);
         const int s = r0 + i * n_h;
         const bool ok = s < s0 + C && s < N;
+        qin[it] = ok;  // masked where the fragments are converted
         const long long tk = tok0 + (long long)fastdiv(ok ? s : s0, p.nh_magic, p.nh_shift) * p.H;
 #pragma unroll
         for (int t = 0; t < QKS; ++t) {
-          qr[it][t] = u32x4_t{0u, 0u, 0u, 0u};
-          if (ok) {
-            const bf16_t* src = qp + tk * DK + 32 * t + 4 * (lane >> 4);
-            const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(src);
-            const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(src + 16);
-            qr[it][t] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-          }
+          const bf16_t* src = qp + tk * DK + 32 * t + 4 * (lane >> 4);
+          const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(src);
+          const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(src + 16);
+          qr[it][t] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
         }
       }
     } else {
@@ -269,11 +277,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void d
         const int idx = tid + it * 256;
         const int i = idx / TPR, cg = idx % TPR;
         const int s = r0 + i * n_h;
-        rq[it] = u32x4_t{0u, 0u, 0u, 0u};
-        if (idx < QV && s < s0 + C && s < N) {
-          const long long tk = tok0 + (long long)fastdiv(s, p.nh_magic, p.nh_shift) * p.H;
-          rq[it] = ld16(qp + tk * DK + cg * 8);
-        }
+        qin[it] = idx < QV && s < s0 + C && s < N;  // masked where the rows are stored
+        const long long tk = tok0 + (long long)fastdiv(qin[it] ? s : s0, p.nh_magic, p.nh_shift) * p.H;
+        rq[it] = ld16(qp + tk * DK + cg * 8);
       }
     }
   };
@@ -286,6 +292,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void d
     const int r = idx / TPR, cg = idx % TPR;
     float f[8];
     unpack16(rk[it], f, bf16_t{});
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = kin[it] ? f[e] : 0.f;
     float ss = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss = fmaf(f[e], f[e], ss);
@@ -296,6 +304,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void d
     if (idx < KV) st_vec16(sK + r * LDK + cg * 8, f);
     if constexpr (ASYM) {
       unpack16(rkw[it], f, bf16_t{});
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = kin[it] ? f[e] : 0.f;
       if (idx < KV) st_vec16(sKW + r * LDK + cg * 8, f);
     }
   }
@@ -309,7 +319,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void d
         float f[8];
         unpack16(qr[it][t], f, bf16_t{});
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qf[it][t][e] = (f16_t)f[e];
+        for (int e = 0; e < 8; ++e) qf[it][t][e] = (f16_t)(qin[it] ? f[e] : 0.f);
       }
   } else {
 #pragma unroll
@@ -318,12 +328,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void d
       const int i = idx / TPR, cg = idx % TPR;
       float f[8];
       unpack16(rq[it], f, bf16_t{});
+#pragma unroll
+      for (int e = 0; e < 8; ++e) f[e] = qin[it] ? f[e] : 0.f;
       if (idx < QV) st_vec16(sQ + i * LDK + cg * 8, f);
     }
   }
 
   // 3. beta range, cumulative log-gate and the per-chunk scalars (wave 0)
   if (wave == 0) {
+    const float lam = gin ? logf(fmaxf(graw, FLT_MIN)) : 0.f;
     const float G = p.g != nullptr ? wave_inclusive_scan(lam) : 0.f;  // no gate: all zero
     const float Gl = __shfl(G, C - 1, 64);
     float* sEG = reinterpret_cast<float*>(wsc + W.oS + W.oEG);
@@ -331,7 +344,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void d
     float* sEGL = reinterpret_cast<float*>(wsc + W.oS + W.oEGL);
     long long* sOff = reinterpret_cast<long long*>(wsc + W.oS + W.oOff);
     if (lane < C) {
-      sB[lane] = clamp_keep_nan(braw, 0.f, 2.f);
+      sB[lane] = clamp_keep_nan(bin ? braw : 0.f, 0.f, 2.f);  // 0 past the end
       sG[lane] = G;
       sEG[lane] = expf(G);
       sEL[lane] = expf(Gl - G);
