@@ -181,8 +181,11 @@ __device__ __forceinline__ long long sub_row(const FwdArgs& p, int s, int b, int
 // LDS bytes of dp_ut_kernel: K (and Kw) rows, fp32 M, 3 scalar vectors,
 // fp32 T and the per-wave partial-sum tiles of the blocked inverse; with a
 // per-channel gate (cg) both key regions and the cumulative log-gates G
-// (C x (dk + 4) fp32).
+// (C x (dk + 4) fp32).  With 16-bit inputs the rebased fp16 operand rows of
+// M's off-diagonal tiles (C x (dk + 8)) use the space of T and the inverse's
+// scratch, which are not needed until M is complete.
 __host__ __device__ constexpr int ut_gam_ld(int DK) { return DK + 4; }
+__host__ __device__ constexpr int ut_cg_op_ld(int DK) { return DK + 8; }
 __host__ __device__ constexpr int ut_lds_bytes(int elem, int DK, int C, int asym, int cg = 0) {
   return align16((asym || cg ? 2 : 1) * C * (DK + 16 / elem) * elem) + align16(C * (C + 4) * 4) +
          3 * C * 4 + C * (C + 4) * 4 + 4 * 16 * 17 * 4 + (cg ? C * ut_gam_ld(DK) * 4 : 0);
@@ -330,22 +333,72 @@ __global__ __launch_bounds__(kThreads) void dp_ut_kernel(FwdArgs p) {
   if (tid < C) p.wsS[chunk * C + tid] = CG ? make_float2(s0 + tid < p.N ? 1.f : 0.f, 0.f) : make_float2(sR[tid], sG[tid]);
 
   if constexpr (CG) {
-    // 4'. M_ij (j < i), pair by pair over the key channels; symmetric keys are
-    //     normalised here (sR), write keys used as given
-    constexpr int NPAIR = C * (C - 1) / 2;
+    // 4'. M_ij (j < i); symmetric keys are normalised here (sR), write keys
+    //     used as given.  With fp32 inputs, and on the diagonal 16 x 16 tiles,
+    //     pair by pair over the key channels.  With 16-bit inputs the tiles
+    //     below the diagonal run on MFMA: for block row a (rows i >= r = 16 a)
+    //     and columns j < r, e^{G_i - G_j} = e^{G_i - G_r} e^{G_r - G_j} with
+    //     both factors at most 1, so the rebased rows kn_i o e^{G_i - G_r} and
+    //     w_j o e^{G_r - G_j} are fp16 operands of one product.
+    constexpr bool MM = sizeof(OT) == 2;
+    constexpr int NPAIR = C * (C - 1) / 2, DPAIR = 16 * 15 / 2;
     for (int pr = tid; pr < C * C; pr += kThreads) sA[(pr / C) * LDA + pr % C] = 0.f;
     block_sync_lds();
-    for (int pr = tid; pr < NPAIR; pr += kThreads) {
-      int i = (int)((1.f + sqrtf(1.f + 8.f * (float)pr)) * 0.5f);
-      while (i * (i - 1) / 2 > pr) --i;
-      while ((i + 1) * i / 2 <= pr) ++i;
-      const int j = pr - i * (i - 1) / 2;
+    auto pair_sum = [&](int i, int j) {
       float acc = 0.f;
 #pragma unroll 4
       for (int c = 0; c < DK; ++c)
         acc = fmaf(to_f32(sK[i * LDK + c]) * to_f32(sKt[j * LDK + c]), __expf(sGam[i * LDG + c] - sGam[j * LDG + c]),
                    acc);
       sA[i * LDA + j] = sB[i] * sR[i] * (p.asym ? 1.f : sR[j]) * acc;
+    };
+    auto tri = [](int q) {  // q -> (i, j), j < i, in row-major order of the strict lower triangle
+      int i = (int)((1.f + sqrtf(1.f + 8.f * (float)q)) * 0.5f);
+      while (i * (i - 1) / 2 > q) --i;
+      while ((i + 1) * i / 2 <= q) ++i;
+      return make_int2(i, q - i * (i - 1) / 2);
+    };
+    if constexpr (!MM) {
+      for (int pr = tid; pr < NPAIR; pr += kThreads) {
+        const int2 ij = tri(pr);
+        pair_sum(ij.x, ij.y);
+      }
+    } else {
+      for (int pr = tid; pr < NT * DPAIR; pr += kThreads) {
+        const int2 ij = tri(pr % DPAIR);
+        const int base = 16 * (pr / DPAIR);
+        pair_sum(base + ij.x, base + ij.y);
+      }
+      constexpr int LDO = ut_cg_op_ld(DK);
+      static_assert(C * LDO * (int)sizeof(OT) <= (C * LDA + 4 * 16 * 17) * 4, "operand rows fit T's space");
+      OT* sOa = reinterpret_cast<OT*>(sTf);  // 16 rebased key rows, then up to C - 16 write rows
+      OT* sOb = sOa + 16 * LDO;
+      for (int a = 1; a < NT; ++a) {
+        const int r = 16 * a;
+        for (int idx = tid; idx < (16 + r) * DK; idx += kThreads) {
+          const int row = idx / DK, ch = idx % DK;
+          if (row < 16) {
+            const int i = r + row;
+            sOa[row * LDO + ch] =
+                from_f32<OT>(to_f32(sK[i * LDK + ch]) * sR[i] * __expf(sGam[i * LDG + ch] - sGam[r * LDG + ch]));
+          } else {
+            const int j = row - 16;
+            const float wj = to_f32(sKt[j * LDK + ch]) * (p.asym ? 1.f : sR[j]);
+            sOb[j * LDO + ch] = from_f32<OT>(wj * __expf(sGam[r * LDG + ch] - sGam[j * LDG + ch]));
+          }
+        }
+        block_sync_lds();
+        if (wave < a) {  // tile (a, wave)
+          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+          acc = mm_tile<OT, DK>(acc, sOa, LDO, 0, sOb, LDO, wave * 16);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = r + 4 * (lane >> 4) + e;
+            sA[i * LDA + wave * 16 + (lane & 15)] = sB[i] * acc[e];
+          }
+        }
+        block_sync_lds();  // the operand rows are rebased again for the next block row
+      }
     }
     // the scan's key operands: e^{G_s} o kn_s and e^{G_C - G_s} o w_s, rows in range
     {
