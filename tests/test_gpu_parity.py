@@ -109,6 +109,34 @@ def test_full_size_sampled_heads(name, nsel):
     assert torch.isfinite(out.float()).all()
 
 
+def test_full_size_c5_pipelined_call():
+    """The c5 step as bench.py times it: one dp_osdn_fwd_bf16 call over the
+    bench's token runs with a pipeline handle, phase 1 in its chunked form
+    (dk = 128), against the oracle's phase 1 and forward on sampled heads."""
+    import bench
+    w = WORKLOADS["c5"]
+    S = bench.PIPELINE_SEGMENTS
+    say(f"case full c5 pipelined: B={w.B} H={w.H} L={w.L} runs={S}")
+    inp = make(w)
+    heads = sampled_heads(w.B, w.H, 12)
+    H = w.H
+    k1 = inp["k"][:, :, :, 0, :].contiguous()
+    v1 = inp["v"][:, :, :, 0, :].contiguous()
+    b1 = inp["beta"][..., 0].contiguous()
+    pipe = dp.Pipeline()
+    out, fs, kt, d = dp.osdn_fwd(inp["q"].cuda(), k1.cuda(), v1.cuda(), b1.cuda(), chunk=w.chunk, segments=S,
+                                 pipeline=pipe)
+    torch.cuda.synchronize()
+    pipe.close()
+    kto, do = oracle.precond(select_heads(k1, heads, H), select_heads(b1, heads, H))
+    sub = {kk: select_heads(inp[kk], heads, H) for kk in ("q", "k", "v", "beta")}
+    oo, fo = oracle.fwd(sub["q"], sub["k"], sub["v"], sub["beta"], kt=kto[:, :, :, None, :])
+    res = dict(kt=(f64(select_heads(kt.cpu(), heads, H)), kto), d=(f64(select_state(d.cpu(), heads, H)), do),
+               out=(f64(select_heads(out.cpu(), heads, H)), oo), fs=(f64(select_state(fs.cpu(), heads, H)), fo))
+    check(res, TOL["bf16"], "full-c5-pipelined")
+    assert torch.isfinite(out.float()).all()
+
+
 # ------------------------------------------------------------------ write keys on every shape
 
 WK = [  # workload, overrides: head dims 32..128, chunk 32 and 64, n_h 1..3, gate and h0
