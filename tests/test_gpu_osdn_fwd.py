@@ -208,3 +208,35 @@ def test_clamping_box_matches_oracle(eta, dmax):
         assert e <= TOL["bf16"], f"{name}: err {e:.3e}"
     assert torch.all(got[3] <= dmax) and torch.all(got[3] >= 0.5)
     assert rel_err(f64(got[3]), f64(d)) <= TOL["f32"]
+
+
+def test_nan_beta_hands_over_to_the_sequential_scan():
+    """A NaN beta at token 150 of head 1 (dk = 128, two runs): the chunked
+    phase 1 meets the NaN in that chunk's check and runs the sequential scan
+    from the chunk's start, so d and the write keys are NaN exactly where the
+    oracle's are (head 1 from token 151 on, through the second run), and the
+    other heads still meet the oracle."""
+    import numpy as np
+    B, H, L, dk, dv = 1, 3, 300, 128, 128
+    q, k1, v1, b1, _ = inputs(B, H, L, dk, dv)
+    b1 = b1.clone()
+    b1[0, 150, 1] = float("nan")
+    kto, do = oracle.precond(k1.cpu(), b1.cpu())
+    out, fs, kt, d = dp.osdn_fwd(q, k1, v1, b1, segments=2)
+    torch.cuda.synchronize()
+    ktn, dn = f64(kt), f64(d)
+    assert np.array_equal(np.isnan(ktn), np.isnan(kto)), "NaN pattern of the write keys"
+    assert np.array_equal(np.isnan(dn), np.isnan(do)), "NaN pattern of d"
+    assert np.isnan(ktn[0, 151:, 1]).all() and np.isfinite(ktn[0, :151, 1]).all()
+    for h in (0, 2):
+        e = max(rel_err(ktn[0, :, h], kto[0, :, h]), rel_err(dn[0, h], do[0, h]))
+        say(f"  head {h}: err {e:.3e}")
+        assert e <= TOL["bf16"]
+    e = rel_err(ktn[0, :151, 1], kto[0, :151, 1])
+    say(f"  head 1 before the NaN: err {e:.3e}")
+    assert e <= TOL["bf16"]
+    oo, fo = oracle.fwd(q.cpu()[:, :, 0::2], k1.cpu()[:, :, 0::2].unsqueeze(3), v1.cpu()[:, :, 0::2].unsqueeze(3),
+                        b1.cpu()[:, :, 0::2].unsqueeze(3), kt=kto[:, :, 0::2, None, :])
+    e = max(rel_err(f64(out)[:, :, 0::2], oo), rel_err(f64(fs)[:, 0::2], fo))
+    say(f"  outputs of heads 0 and 2: err {e:.3e}")
+    assert e <= TOL["bf16"]
