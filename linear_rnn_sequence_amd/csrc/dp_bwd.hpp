@@ -1228,14 +1228,21 @@ __global__ __launch_bounds__(64) void dp_precond_bwd_chain_kernel(PrecondBwdArgs
       }
     }
   };
+  // Two register sets, each loaded one block ahead of its use, and the loop
+  // over pairs of blocks: every load is issued on every path (the last one
+  // clamped to block 0) and no loaded set is copied, so the compiler counts
+  // the loads in flight exactly and waits only for the block it runs.
   const int nblk = (p.L + PB - 1) / PB;
-  Blk cur, nxt;
-  if (nblk > 0) load((nblk - 1) * PB, cur);
-  for (int blk = nblk - 1; blk >= 0; --blk) {
-    if (blk > 0) load((blk - 1) * PB, nxt);  // lands while this block runs
-    run_block(cur, blk * PB);
-    cur = nxt;
+  Blk ba, bb;
+  int blk = nblk - 1;
+  if (nblk > 0) load(blk * PB, ba);
+  for (; blk >= 1; blk -= 2) {
+    load((blk - 1) * PB, bb);  // lands while block blk runs
+    run_block(ba, blk * PB);
+    load(max(blk - 2, 0) * PB, ba);
+    run_block(bb, (blk - 1) * PB);
   }
+  if (blk == 0) run_block(ba, 0);
   if (active && p.dd0 != nullptr) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) p.dd0[bh * DK + sl * EPL + e] = gd[e];
