@@ -298,7 +298,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void d
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss = fmaf(f[e], f[e], ss);
     ss = dpp_group_sum<TPR>(ss);
-    const float rinv = 1.f / fmaxf(sqrtf(ss), 1e-6f);
+    const float rinv = __builtin_amdgcn_rsqf(fmaxf(ss, 1e-12f));  // 1 / max(|k|, 1e-6)
 #pragma unroll
     for (int e = 0; e < 8; ++e) f[e] *= rinv;
     if (idx < KV) st_vec16(sK + r * LDK + cg * 8, f);
@@ -488,14 +488,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(5))) void d
   // 8. T diag(beta) to the workspace, block-major (upper tiles zero, or left
   //    out in the trimmed layout: granule idx is then tile t's block g, row i)
   constexpr bool TRIM = t_trimmed(DK, C);
+  static_assert(!TRIM || C == 64, "the trimmed layout has two tile rows");
   for (int idx = tid; idx < t_bytes(DK, C) / 16; idx += 256) {
     int q = idx / C, i = idx % C;
     if constexpr (TRIM) {
       int t = 0;
       while (t + 1 < C / 32 && idx >= t_block_byte(C, t + 1) / 16) ++t;
-      const int rel = idx - t_block_byte(C, t) / 16, rows = C - 32 * t;
-      q = 4 * t + rel / rows;
-      i = 32 * t + rel % rows;
+      // rows = C - 32 t: a select of constant divisions, not a division by a variable
+      const int rel = idx - t_block_byte(C, t) / 16;
+      q = 4 * t + (t == 0 ? rel / C : rel / (C - 32));
+      i = 32 * t + (t == 0 ? rel % C : rel % (C - 32));
     }
     // The reads are unconditional: for any row block ib and column block jb
     // below C/16, prep_mblock(ib, jb) stays inside the packed lower blocks, so
