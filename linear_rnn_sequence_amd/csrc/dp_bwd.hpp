@@ -1207,7 +1207,18 @@ __global__ __launch_bounds__(64) void dp_precond_bwd_chain_kernel(PrecondBwdArgs
     for (int i = PB - 1; i >= 0; --i) {
       const int t = t0 + i;
       if (t < p.L) {
-        const float rinv = __shfl(c.f.x, hl + i), rt = __shfl(c.f.y, hl + i), c2 = __shfl(c.f.z, hl + i);
+        // token t's factors from lane i of the head: with one head per
+        // wavefront a scalar read of that lane, else a lane shuffle
+        float rinv, rt, c2;
+        if constexpr (LPH == 64) {
+          rinv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c.f.x), i));
+          rt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c.f.y), i));
+          c2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c.f.z), i));
+        } else {
+          rinv = __shfl(c.f.x, hl + i);
+          rt = __shfl(c.f.y, hl + i);
+          c2 = __shfl(c.f.z, hl + i);
+        }
         float kh[EPL], sq[EPL], gx[EPL], gxs = 0.f;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
