@@ -334,6 +334,49 @@ int dp_fwd_varlen_bf16(const void* q, const void* k, const void* v, const float*
                        void* workspace, size_t workspace_bytes, int flags, dp_stream stream);
 
 /*
+ * Packed variable-length write-key forward (OSDN notes sec. 2.5 phase 2, on
+ * the packed batches of sec. 3.4: documents packed along one token axis, the
+ * state restarting at each document): dp_fwd_varlen_bf16 with the write keys
+ * kt [T, H, n_h, dk] bf16 (e.g. from dp_osdn_precond_varlen_bf16) in the
+ * state update and the readout scores, as dp_fwd_wk_bf16 does for one batch.
+ * Each result equals dp_fwd_wk_bf16 run on that sequence alone.  Runs on the
+ * prep / chain pair: dk and chunk multiples of 32, else DP_ENOTSUP.
+ * workspace: dp_fwd_varlen_workspace_size() bytes (one size serves both
+ * packed forms).  Errors: as dp_fwd_varlen_bf16; kt NULL with T > 0 or not
+ * 16-byte aligned is DP_EINVAL; DP_FWD_FUSED is DP_ENOTSUP.
+ */
+int dp_fwd_varlen_wk_bf16(const void* q, const void* k, const void* kt, const void* v,
+                          const float* beta, const float* g, const int* cu_seqlens, int nseq,
+                          int n_h, int H, int T, int dk, int dv, int chunk, void* out,
+                          float* final_state, const float* h0, void* workspace,
+                          size_t workspace_bytes, int flags, dp_stream stream);
+
+/*
+ * Packed variable-length OSDN phase 1 (OSDN notes sec. 2.4 and the packed
+ * batches of sec. 3.4): the exact scan of dp_osdn_precond_ex_* run on each of
+ * nseq sequences packed along one token axis, every sequence from its own d.
+ *   k [T, H, dk] T, beta [T, H] f32, r [T, H] f32 or NULL, kt [T, H, dk] T
+ *   cu_seqlens [nseq + 1] int32, DEVICE memory; sequence d is tokens
+ *              cu_seqlens[d] .. cu_seqlens[d+1]-1.  A sequence is read only if
+ *              0 = cu[0], cu[d] <= cu[d+1] and cu[nseq] = T; otherwise it is
+ *              empty: no kt row of it is written and its d is left as it was.
+ *   d_state [nseq, H, dk] f32   in: each sequence's d_1; out: its d after its
+ *              last token.
+ *   flags, eta, dmin, dmax, eps: as dp_osdn_precond_ex_* (the box may be open).
+ * Each sequence's kt and d equal dp_osdn_precond_ex_* run on it alone, bit for
+ * bit.  Errors: as dp_osdn_precond_ex_*; cu_seqlens NULL or nseq < 1 is
+ * DP_EINVAL.
+ */
+int dp_osdn_precond_varlen_f32(const float* k, const float* beta, const float* r, int flags,
+                               const int* cu_seqlens, int nseq, int H, int T, int dk, float eta,
+                               float dmin, float dmax, float eps, float* d_state, float* kt,
+                               dp_stream stream);
+int dp_osdn_precond_varlen_bf16(const void* k, const float* beta, const float* r, int flags,
+                                const int* cu_seqlens, int nseq, int H, int T, int dk, float eta,
+                                float dmin, float dmax, float eps, float* d_state, void* kt,
+                                dp_stream stream);
+
+/*
  * For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc):
  * dp_fwd_varlen_bf16 with DP_FWD_FUSED, without a workspace.  The fused

@@ -41,6 +41,7 @@ EXPORTS = (
     "dp_bwd_wk_f32", "dp_bwd_wk_bf16",
     "dp_osdn_precond_bwd_workspace_size", "dp_osdn_precond_bwd_f32", "dp_osdn_precond_bwd_bf16",
     "dp_osdn_bwd_workspace_size", "dp_osdn_bwd_f32", "dp_osdn_bwd_bf16",
+    "dp_fwd_varlen_wk_bf16", "dp_osdn_precond_varlen_f32", "dp_osdn_precond_varlen_bf16",
 )
 
 _lib = None
@@ -90,11 +91,18 @@ def load() -> ctypes.CDLL:
         for name in ("dp_osdn_precond_ex_f32", "dp_osdn_precond_ex_bf16"):
             getattr(lib, name).restype = _I
             getattr(lib, name).argtypes = pre_ex
+        # k, beta, r, flags, cu_seqlens, nseq, H, T, dk, eta, dmin, dmax, eps, d, kt, stream
+        pre_var = [_P, _P, _P, _I, _P, _I, _I, _I, _I, _F, _F, _F, _F, _P, _P, _P]
+        for name in ("dp_osdn_precond_varlen_f32", "dp_osdn_precond_varlen_bf16"):
+            getattr(lib, name).restype = _I
+            getattr(lib, name).argtypes = pre_var
         lib.dp_fwd_varlen_workspace_size.restype = _I
         lib.dp_fwd_varlen_workspace_size.argtypes = [_I] * 7 + [ctypes.POINTER(ctypes.c_size_t)]
         lib.dp_fwd_varlen_bf16.restype = _I
         lib.dp_fwd_varlen_bf16.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P,
                                            _P, _P, ctypes.c_size_t, _I, _P]
+        lib.dp_fwd_varlen_wk_bf16.restype = _I
+        lib.dp_fwd_varlen_wk_bf16.argtypes = [_P] * 7 + [_I] * 7 + [_P] * 4 + [ctypes.c_size_t, _I, _P]
         lib.dp_fwd_varlen_noalloc_bf16.restype = _I
         lib.dp_fwd_varlen_noalloc_bf16.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P,
                                                    _P, _P, _I, _P]
@@ -294,6 +302,41 @@ def osdn_precond(k, beta, *, eta: float = 3e-3, dmin: float = 0.5, dmax: float =
     return kt, d_state
 
 
+def osdn_precond_varlen(k, beta, cu_seqlens, *, eta: float = 3e-3, dmin: float = 0.5,
+                        dmax: float = 2.0, eps: float = 1e-6, d_state=None, kt=None, r=None,
+                        beta_aware: bool = True, stream=None):
+    """Packed variable-length OSDN phase 1 through libdp: k [T,H,dk], beta [T,H]
+    f32, cu_seqlens [nseq+1] int32 on the device.  d_state [nseq,H,dk] f32 is
+    each sequence's d_1 on entry (default ones) and its last d on return.  r
+    [T,H] f32 and beta_aware as for :func:`osdn_precond`.  Returns
+    (kt [T,H,dk], d_state)."""
+    if k.dim() != 3:
+        raise ValueError("expected k[T,H,dk]")
+    T, H, dk = k.shape
+    dev, dt = k.device, k.dtype
+    suf = _suffix(dt)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be [nseq + 1]")
+    nseq = cu_seqlens.numel() - 1
+    _need(cu_seqlens, "cu_seqlens", torch.int32, (nseq + 1,), dev)
+    _need(beta, "beta", torch.float32, (T, H), dev)
+    _need(r, "r", torch.float32, (T, H), dev)
+    if not k.is_contiguous():
+        raise ValueError("k must be contiguous")
+    if d_state is None:
+        d_state = torch.ones(nseq, H, dk, dtype=torch.float32, device=dev)
+    _need(d_state, "d_state", torch.float32, (nseq, H, dk), dev)
+    if kt is None:
+        kt = torch.empty(T, H, dk, dtype=dt, device=dev)
+    _need(kt, "kt", dt, (T, H, dk), dev)
+    name = f"dp_osdn_precond_varlen_{suf}"
+    flags = 0 if beta_aware else PRECOND_BETA_FREE
+    rc = getattr(load(), name)(_ptr(k), _ptr(beta), _ptr(r), flags, _ptr(cu_seqlens), nseq, H, T,
+                               dk, eta, dmin, dmax, eps, _ptr(d_state), _ptr(kt), _stream(stream))
+    _check(rc, name)
+    return kt, d_state
+
+
 def osdn_fwd_workspace_size(B, H, L, dk, dv, chunk, segments) -> int:
     """Workspace bytes of :func:`osdn_fwd` (dp_osdn_fwd_workspace_size)."""
     n = ctypes.c_size_t(0)
@@ -420,14 +463,16 @@ def varlen_workspace_size(n_h, nseq, H, T, dk, dv, chunk) -> int:
     return n.value
 
 
-def fwd_varlen(q, k, v, beta, cu_seqlens, g=None, *, chunk: int = 64, h0=None, out=None,
+def fwd_varlen(q, k, v, beta, cu_seqlens, g=None, *, chunk: int = 64, h0=None, kt=None, out=None,
                final_state=None, return_state: bool = True, workspace=None,
                stages: int = STAGE_ALL, out_dtype=None, path: str = "auto", stream=None):
-    """Packed variable-length forward (bf16, symmetric keys) through libdp.
+    """Packed variable-length forward (bf16) through libdp.
 
     q [T,H,dk], k [T,H,n_h,dk], v [T,H,n_h,dv] bfloat16, beta [T,H,n_h] f32,
     g [T,H] f32 or None, cu_seqlens [nseq+1] int32 on the device, h0
-    [nseq,H,dk,dv] f32 or None.  path as for fwd.  Returns (out [T,H,dv], final_state).
+    [nseq,H,dk,dv] f32 or None.  kt [T,H,n_h,dk] bfloat16: the write keys
+    (dp_fwd_varlen_wk_bf16), else symmetric keys.  path as for fwd.  Returns
+    (out [T,H,dv], final_state).
     """
     if q.dim() != 3 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("expected q[T,H,dk], k[T,H,n_h,dk], v[T,H,n_h,dv]")
@@ -441,6 +486,7 @@ def fwd_varlen(q, k, v, beta, cu_seqlens, g=None, *, chunk: int = 64, h0=None, o
     nseq = cu_seqlens.numel() - 1
     _need(cu_seqlens, "cu_seqlens", torch.int32, (nseq + 1,), dev)
     _need(k, "k", dt, (T, H, n_h, dk), dev)
+    _need(kt, "kt", dt, (T, H, n_h, dk), dev)
     _need(v, "v", dt, (T, H, n_h, dv), dev)
     _need(beta, "beta", torch.float32, (T, H, n_h), dev)
     _need(g, "g", torch.float32, (T, H), dev)
@@ -462,12 +508,16 @@ def fwd_varlen(q, k, v, beta, cu_seqlens, g=None, *, chunk: int = 64, h0=None, o
     if workspace is None:
         nbytes = varlen_workspace_size(n_h, nseq, H, T, dk, dv, chunk)
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
-    rc = load().dp_fwd_varlen_bf16(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(cu_seqlens),
-                                   nseq, n_h, H, T, dk, dv, chunk, _ptr(out), _ptr(final_state),
-                                   _ptr(h0), _ptr(workspace),
-                                   workspace.numel() * workspace.element_size(), flags,
-                                   _stream(stream))
-    _check(rc, "dp_fwd_varlen_bf16")
+    tail = (_ptr(v), _ptr(beta), _ptr(g), _ptr(cu_seqlens), nseq, n_h, H, T, dk, dv, chunk,
+            _ptr(out), _ptr(final_state), _ptr(h0), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), flags, _stream(stream))
+    if kt is None:
+        name = "dp_fwd_varlen_bf16"
+        rc = load().dp_fwd_varlen_bf16(_ptr(q), _ptr(k), *tail)
+    else:
+        name = "dp_fwd_varlen_wk_bf16"
+        rc = load().dp_fwd_varlen_wk_bf16(_ptr(q), _ptr(k), _ptr(kt), *tail)
+    _check(rc, name)
     return out, final_state
 
 

@@ -495,7 +495,10 @@ long long varlen_nwork(const VarShape& v) {
 }
 
 size_t varlen_blocks_bytes(const VarShape& v) {
-  const dp::Chunk16Layout W = dp::chunk16_layout(v.dk, v.chunk, readout_rows(v.chunk, v.n_h));
+  // sized for the write-key form wherever it runs (as ws_blocks_bytes), so
+  // one size serves both forward forms
+  const bool asym = dp::chain_asym_ok(v.dk, v.chunk);
+  const dp::Chunk16Layout W = dp::chunk16_layout(v.dk, v.chunk, readout_rows(v.chunk, v.n_h), asym);
   return align_up((size_t)varlen_nwork(v) * W.bytes, kWsAlign);
 }
 size_t varlen_cbase_bytes(const VarShape& v) { return align_up((size_t)(v.nseq + 1) * 4, kWsAlign); }
@@ -508,22 +511,26 @@ size_t varlen_ws_need(const VarShape& v, bool fused) { return fused ? varlen_cba
 
 // table: when not NULL, the fused kernel's chunk-offset table lives there (at
 // least nseq + 1 ints) and no workspace is used.  dry: validate and plan only.
+// kt: the write keys (the prep / chain pair's write-key form), or NULL.
 int varlen_impl(const void* q, const void* k, const void* v, const float* beta, const float* g,
                 const int* cu_seqlens, int nseq, int n_h, int H, int T, int dk, int dv, int chunk,
                 void* out, float* final_state, const float* h0, void* workspace,
                 size_t workspace_bytes, int flags, dp_stream stream, int* table = nullptr,
-                bool dry = false) {
+                bool dry = false, const void* kt = nullptr) {
   const VarShape vs{n_h, nseq, H, T, dk, dv, chunk};
   int rc = check_varlen(vs);
   if (rc != DP_OK) return rc;
-  rc = check_fwd_flags(2, false, dk, chunk, flags);
+  const bool asym = kt != nullptr;
+  rc = check_fwd_flags(2, asym, dk, chunk, flags);
   if (rc != DP_OK) return rc;
+  // the packed write-key form runs on the prep / chain pair only
+  if (asym && !dp::chain_asym_ok(dk, chunk)) return DP_ENOTSUP;
   const int stages = flags & DP_STAGE_ALL;
   if (cu_seqlens == nullptr) return DP_EINVAL;
   if (T > 0 && (q == nullptr || k == nullptr || v == nullptr || beta == nullptr || out == nullptr))
     return DP_EINVAL;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return DP_EINVAL;
-  const bool fused = use_fused(2, false, dk, dv, chunk, flags);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(kt)) return DP_EINVAL;
+  const bool fused = use_fused(2, asym, dk, dv, chunk, flags);
   if (table != nullptr) {
     if (!fused) return DP_ENOTSUP;  // only the fused kernel runs on the table alone
   } else {
@@ -558,8 +565,9 @@ int varlen_impl(const void* q, const void* k, const void* v, const float* beta, 
   a.L = T;  // total tokens (the chunk-offset kernel checks cu[nseq] == T)
   a.n_h = n_h;
   a.dv = dv;
+  a.kt = kt;
   a.RT = readout_rows(chunk, n_h);
-  a.asym = 0;
+  a.asym = asym ? 1 : 0;
   a.out_f32 = (flags & DP_OUT_F32) != 0 ? 1 : 0;
   fastdiv_magic(n_h, &a.nh_magic, &a.nh_shift);
 
@@ -644,7 +652,7 @@ int decode_impl(int elem, const void* q, const void* k, const void* kt, const vo
 int precond_impl(int elem, const void* k, const float* beta, const float* ret, int flags,
                  int B, int H, int L, int dk, float eta, float dmin, float dmax, float eps,
                  float* d_state, void* kt, bool open_box, dp_stream stream, int Ls = 0, int t0 = 0,
-                 bool dry = false, char* p1c = nullptr) {
+                 bool dry = false, char* p1c = nullptr, const int* cu = nullptr) {
   // with L == 0 the per-token tensors are empty and may be null
   if (d_state == nullptr || (L > 0 && (k == nullptr || beta == nullptr || kt == nullptr))) return DP_EINVAL;
   if (!aligned16(k) || !aligned16(kt)) return DP_EINVAL;
@@ -671,9 +679,10 @@ int precond_impl(int elem, const void* k, const float* beta, const float* ret, i
   a.eps = eps;
   a.Ls = Ls;
   a.t0 = t0;
+  a.cu = cu;  // packed sequences: B of them over L tokens (the exact scan)
   // with a workspace for it (p1c_ws) and dk >= 64, the chunked form, whose
   // hand-over to the exact scan keeps the sequential definition's result
-  if (p1c != nullptr && dk >= 64) {
+  if (p1c != nullptr && dk >= 64 && cu == nullptr) {
     p1c_bind(a, p1c, dk);
     const hipError_t e = dispatch_precond_chunked(elem, dk, a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? DP_OK : DP_EHIP;
@@ -1142,6 +1151,24 @@ int dp_osdn_precond_ex_bf16(const void* k, const float* beta, const float* r, in
                       stream);
 }
 
+int dp_osdn_precond_varlen_f32(const float* k, const float* beta, const float* r, int flags,
+                               const int* cu_seqlens, int nseq, int H, int T, int dk, float eta,
+                               float dmin, float dmax, float eps, float* d_state, float* kt,
+                               dp_stream stream) {
+  if (cu_seqlens == nullptr || nseq <= 0) return DP_EINVAL;
+  return precond_impl(4, k, beta, r, flags, nseq, H, T, dk, eta, dmin, dmax, eps, d_state, kt, true,
+                      stream, 0, 0, false, nullptr, cu_seqlens);
+}
+
+int dp_osdn_precond_varlen_bf16(const void* k, const float* beta, const float* r, int flags,
+                                const int* cu_seqlens, int nseq, int H, int T, int dk, float eta,
+                                float dmin, float dmax, float eps, float* d_state, void* kt,
+                                dp_stream stream) {
+  if (cu_seqlens == nullptr || nseq <= 0) return DP_EINVAL;
+  return precond_impl(2, k, beta, r, flags, nseq, H, T, dk, eta, dmin, dmax, eps, d_state, kt, true,
+                      stream, 0, 0, false, nullptr, cu_seqlens);
+}
+
 int dp_osdn_fwd_workspace_size(int B, int H, int L, int dk, int dv, int chunk, int segments,
                                size_t* bytes) {
   if (bytes == nullptr || segments < 1 || segments > kMaxSegments || chunk <= 0 || L < 0) return DP_EINVAL;
@@ -1250,6 +1277,16 @@ int dp_fwd_varlen_bf16(const void* q, const void* k, const void* v, const float*
                        void* workspace, size_t workspace_bytes, int flags, dp_stream stream) {
   return varlen_impl(q, k, v, beta, g, cu_seqlens, nseq, n_h, H, T, dk, dv, chunk, out, final_state,
                      h0, workspace, workspace_bytes, flags, stream);
+}
+
+int dp_fwd_varlen_wk_bf16(const void* q, const void* k, const void* kt, const void* v,
+                          const float* beta, const float* g, const int* cu_seqlens, int nseq,
+                          int n_h, int H, int T, int dk, int dv, int chunk, void* out,
+                          float* final_state, const float* h0, void* workspace,
+                          size_t workspace_bytes, int flags, dp_stream stream) {
+  if (T > 0 && kt == nullptr) return DP_EINVAL;
+  return varlen_impl(q, k, v, beta, g, cu_seqlens, nseq, n_h, H, T, dk, dv, chunk, out, final_state,
+                     h0, workspace, workspace_bytes, flags, stream, nullptr, false, kt);
 }
 
 int dp_fwd_varlen_noalloc_bf16(const void* q, const void* k, const void* v, const float* beta,

@@ -140,6 +140,9 @@ struct PrecondArgs {
   // [B*H] first chunk whose check failed (nc: none): with it, dp_precond_kernel
   // runs the exact scan from that chunk's start d and leaves other heads alone
   int* restart = nullptr;
+  // packed sequences (exact scan only): B of them along one axis of L tokens,
+  // sequence b being tokens cu[b] .. cu[b+1]-1 (device memory), or nullptr
+  const int* cu = nullptr;
 };
 
 __host__ __device__ constexpr int align16(int x) { return (x + 15) & ~15; }
@@ -1357,8 +1360,18 @@ __global__ __launch_bounds__(64) void dp_precond_kernel(PrecondArgs p) {
   const bool active = bh_raw < nbh;
   const long long bh = active ? bh_raw : 0;
   const int b = (int)(bh / p.H), h = (int)(bh % p.H);
-  // token t of this head: row ((b L + t) H + h) of the token-major tensors
-  const long long row0 = tok_base(p, b) * p.H + h;
+  // this head's tokens: L of them from token tb (packed: sequence b's own run;
+  // offsets outside 0 = cu[0], cu[b] <= cu[b+1] <= cu[B] = L make it empty)
+  int L = p.L;
+  long long tb = tok_base(p, b);
+  if (p.cu != nullptr) {
+    const int lo = p.cu[b], hi = p.cu[b + 1];
+    const bool ok = p.cu[0] == 0 && p.cu[p.B] == p.L && 0 <= lo && lo <= hi && hi <= p.L;
+    tb = ok ? lo : 0;
+    L = ok ? hi - lo : 0;
+  }
+  // token t of this head: row ((tb + t) H + h) of the token-major tensors
+  const long long row0 = tb * p.H + h;
   const T* kp = static_cast<const T*>(p.k) + row0 * DK + sl * EPL;
   T* ktp = static_cast<T*>(p.kt) + row0 * DK + sl * EPL;
   const float* bp = p.beta + row0;
@@ -1427,7 +1440,7 @@ __global__ __launch_bounds__(64) void dp_precond_kernel(PrecondArgs p) {
     float bnx = 0.f, rnx = 1.f;
     auto load_rows = [&](int t0) {
       const int t = t0 + lane;
-      if (lane < PB && t < p.L) {
+      if (lane < PB && t < L) {
         const uint4* src = reinterpret_cast<const uint4*>(krow + t * kstride);
 #pragma unroll
         for (int q = 0; q < RB / 16; ++q) rowraw[q] = src[q];
@@ -1444,7 +1457,7 @@ __global__ __launch_bounds__(64) void dp_precond_kernel(PrecondArgs p) {
     auto load_slices = [&](int t0, T (&sv)[PB][EPL]) {
 #pragma unroll
       for (int i = 0; i < PB; ++i) {
-        if (t0 + i < p.L)
+        if (t0 + i < L)
           __builtin_memcpy(sv[i], __builtin_assume_aligned(kp + (t0 + i) * kstride, EPL * sizeof(T)), EPL * sizeof(T));
         else
 #pragma unroll
@@ -1473,7 +1486,7 @@ __global__ __launch_bounds__(64) void dp_precond_kernel(PrecondArgs p) {
 #pragma unroll
       for (int i = 0; i < PB; ++i) {
         const int t = t0 + i;
-        if (FULL || t < p.L) {
+        if (FULL || t < L) {
           const float r = lane_val(rv, i), w = lane_val(wv, i), bw = lane_val(bwv, i);
           float kh[EPL], sq[EPL], ds = 0.f;
 #pragma unroll
@@ -1500,13 +1513,13 @@ __global__ __launch_bounds__(64) void dp_precond_kernel(PrecondArgs p) {
     };
     load_rows(tbeg);
     load_slices(tbeg, sc);
-    for (int t0 = tbeg; t0 < p.L; t0 += PB) {
+    for (int t0 = tbeg; t0 < L; t0 += PB) {
       token_scalars();
-      if (t0 + PB < p.L) {
+      if (t0 + PB < L) {
         load_rows(t0 + PB);
         load_slices(t0 + PB, sn);
       }
-      const bool full = t0 + PB <= p.L;
+      const bool full = t0 + PB <= L;
       if (rp != nullptr) {
         if (full)
           run_block(std::true_type{}, std::true_type{}, t0);
@@ -1537,7 +1550,7 @@ __global__ __launch_bounds__(64) void dp_precond_kernel(PrecondArgs p) {
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
       const int t = t0 + i;
-      if (t < p.L) {
+      if (t < L) {
         __builtin_memcpy(r.k[i], __builtin_assume_aligned(kp + t * kstride, EPL * sizeof(T)), EPL * sizeof(T));
         r.beta[i] = bp[(long long)t * p.H];
         r.ret[i] = rp != nullptr ? rp[(long long)t * p.H] : 1.f;
@@ -1579,7 +1592,7 @@ __global__ __launch_bounds__(64) void dp_precond_kernel(PrecondArgs p) {
       if (i + LAH < PF) prep_tok(i + LAH);
       const int q = i % NSL;
       const int t = t0 + i;
-      if (FULL || t < p.L) {
+      if (FULL || t < L) {
         float ds = 0.f;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) ds = fmaf(d[e], s[q][e], ds);
@@ -1595,9 +1608,9 @@ __global__ __launch_bounds__(64) void dp_precond_kernel(PrecondArgs p) {
     }
   };
   load_block(0, cur);
-  for (int t0 = 0; t0 < p.L; t0 += PF) {
-    if (t0 + PF < p.L) load_block(t0 + PF, nxt);
-    if (t0 + PF <= p.L)
+  for (int t0 = 0; t0 < L; t0 += PF) {
+    if (t0 + PF < L) load_block(t0 + PF, nxt);
+    if (t0 + PF <= L)
       run_block(std::true_type{}, t0);
     else
       run_block(std::false_type{}, t0);

@@ -56,3 +56,19 @@ def oracle_heads(inp, heads, kt=None):
     h0 = None if inp["h0"] is None else select_state(inp["h0"], heads, H)
     return oracle.fwd(sel(inp["q"]), sel(inp["k"]), sel(inp["v"]), sel(inp["beta"]),
                       g=sel(inp["g"]), kt=None if kt is None else sel(kt), h0=h0)
+
+
+def check_bf16_stored(x, ref, label):
+    """Write keys stored in bf16: each element is d_t * k_t (fp32, ~1e-6 relative
+    from the oracle's fp64 value) rounded to nearest even, so it lies within
+    2^-8 |ref| of the reference (half a unit in the last place at the bottom of
+    a binade), plus the fp32 part.  The scan is judged on d (fp32, max/RMS
+    bound); max/RMS of the stored keys measures their rounding, which for
+    keys spread over a decade exceeds 2e-2 by itself."""
+    ref = np.asarray(ref, np.float64)
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    bound = 2.0 ** -8 * np.abs(ref) * (1 + 1e-3) + 1e-5 * rms
+    excess = float(np.max(np.abs(x - ref) - bound))
+    say(f"  {label} kt: max/RMS {rel_err(x, ref):.3e}; worst |err| - 2^-8 |ref| bound {excess:.3e}")
+    assert np.all(np.isfinite(x)), f"{label} kt: non-finite values"
+    assert excess <= 0.0, f"{label} kt: an element is off by more than bf16 rounding"

@@ -288,13 +288,56 @@ def test_varlen_validation_errors_before_hip(lib):
     assert call(wsp=FAKE + 16) == E.DP_EWORKSPACE
 
 
+def test_varlen_wk_validation_errors_before_hip(lib):
+    E = dp.binding
+    f = lib.dp_fwd_varlen_wk_bf16
+
+    def call(q=FAKE, k=FAKE, kt=FAKE, v=FAKE, beta=FAKE, g=None, cu=FAKE, nseq=2, n_h=1, H=1, T=8,
+             dk=32, dv=32, chunk=32, out=FAKE, fs=None, h0=None, wsp=FAKE, wsb=1 << 30, flags=3):
+        return f(q, k, kt, v, beta, g, cu, nseq, n_h, H, T, dk, dv, chunk, out, fs, h0, wsp, wsb,
+                 flags, None)
+
+    assert call(kt=None) == E.DP_EINVAL
+    assert call(kt=FAKE + 8) == E.DP_EINVAL       # misaligned
+    assert call(cu=None) == E.DP_EINVAL
+    assert call(nseq=0) == E.DP_EINVAL
+    assert call(flags=16 | 3) == E.DP_ENOTSUP     # no fused write-key kernel
+    assert call(dk=16) == E.DP_ENOTSUP            # the pair needs dk and chunk in 32s
+    assert call(chunk=16) == E.DP_ENOTSUP
+    assert call(wsb=16) == E.DP_EWORKSPACE
+
+
+def test_precond_varlen_validation_errors_before_hip(lib):
+    E = dp.binding
+    for f in (lib.dp_osdn_precond_varlen_f32, lib.dp_osdn_precond_varlen_bf16):
+        def call(k=FAKE, beta=FAKE, r=None, flags=0, cu=FAKE, nseq=2, H=1, T=8, dk=16, eta=3e-3,
+                 dmin=0.5, dmax=2.0, eps=1e-6, d=FAKE, kt=FAKE):
+            return f(k, beta, r, flags, cu, nseq, H, T, dk, eta, dmin, dmax, eps, d, kt, None)
+
+        assert call(cu=None) == E.DP_EINVAL
+        assert call(nseq=0) == E.DP_EINVAL
+        assert call(d=None) == E.DP_EINVAL
+        assert call(kt=FAKE + 4) == E.DP_EINVAL
+        assert call(flags=2) == E.DP_EINVAL
+        assert call(eps=0.0) == E.DP_EINVAL
+        assert call(dmin=3.0) == E.DP_EINVAL         # dmin > dmax
+        assert call(dk=24) == E.DP_ENOTSUP
+        assert call(T=0) == E.DP_OK                  # nothing to scan: no launch
+
+
 def test_varlen_workspace_size(lib):
     n = SZ(0)
     # 3 heads, 1000 tokens, n_h 3, chunk 64: blocks for 3 (ceil(3000 / 64) + 5) chunks,
-    # then 6 ints of chunk offsets and the sink (5 x 3 x 8 wavefront slots)
+    # then 6 ints of chunk offsets and the sink (5 x 3 x 8 wavefront slots).  The
+    # blocks are sized with the write keys (dk and chunk multiples of 32), so one
+    # size serves the symmetric and the write-key packed forward.
     assert lib.dp_fwd_varlen_workspace_size(3, 5, 3, 1000, 128, 128, 64, ctypes.byref(n)) == 0
-    blocks = -(-3 * (47 + 5) * bf16_chunk_block(128, 64, 3) // 256) * 256
+    blocks = -(-3 * (47 + 5) * bf16_chunk_block(128, 64, 3, write_keys=True) // 256) * 256
     assert n.value == blocks + 256 + -(-5 * 3 * 8 * 64 * 4 // 256) * 256
+    # dk 16: no write-key form on the pair, blocks without write keys
+    assert lib.dp_fwd_varlen_workspace_size(3, 5, 3, 1000, 16, 16, 64, ctypes.byref(n)) == 0
+    blocks = -(-3 * (47 + 5) * bf16_chunk_block(16, 64, 3) // 256) * 256
+    assert n.value == blocks + 256 + -(-5 * 3 * 1 * 64 * 4 // 256) * 256
     assert lib.dp_fwd_varlen_workspace_size(3, 0, 3, 1000, 128, 128, 64, ctypes.byref(n)) == \
         dp.binding.DP_EINVAL
 

@@ -11,7 +11,7 @@ import linear_rnn_sequence_amd as dp
 import oracle
 from linear_rnn_sequence_amd.inputs import WORKLOADS, make, retention, sampled_heads, \
     select_heads, select_state
-from parity import TOL, f64, gpu_forward, rel_err, say
+from parity import TOL, check_bf16_stored, f64, gpu_forward, rel_err, say
 
 pytestmark = pytest.mark.gpu
 
@@ -29,22 +29,6 @@ def check(pairs, tol, label):
         say(f"  {label} {name}: err {e:.3e} (tol {tol:.0e})")
         assert np.all(np.isfinite(x)), f"{label} {name}: non-finite values"
         assert e <= tol, f"{label} {name}: err {e:.3e} > {tol}"
-
-
-def check_bf16_stored(x, ref, label):
-    """Write keys stored in bf16: each element is d_t * k_t (fp32, ~1e-6 relative
-    from the oracle's fp64 value) rounded to nearest even, so it lies within
-    2^-8 |ref| of the reference (half a unit in the last place at the bottom of
-    a binade), plus the fp32 part.  The scan is judged on d (fp32, max/RMS
-    bound); max/RMS of the stored keys measures their rounding, which for
-    keys spread over a decade exceeds 2e-2 by itself."""
-    ref = np.asarray(ref, np.float64)
-    rms = float(np.sqrt(np.mean(ref * ref)))
-    bound = 2.0 ** -8 * np.abs(ref) * (1 + 1e-3) + 1e-5 * rms
-    excess = float(np.max(np.abs(x - ref) - bound))
-    say(f"  {label} kt: max/RMS {rel_err(x, ref):.3e}; worst |err| - 2^-8 |ref| bound {excess:.3e}")
-    assert np.all(np.isfinite(x)), f"{label} kt: non-finite values"
-    assert excess <= 0.0, f"{label} kt: an element is off by more than bf16 rounding"
 
 
 def check_phase1(ktg, kto, dg, do, dtype, label):
