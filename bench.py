@@ -11,7 +11,8 @@ scan first.  Prints ONE JSON line on stdout; diagnostics go to stderr.
 Per-kernel durations come from HIP events recorded on the launch stream
 around every launch inside the timed region.  The CPU baseline is the fp64
 oracle on a bounded sample of heads of the same workload, on this host.  The
-same line also carries a packed variable-length batch (`varlen`), the
+same line also carries a packed variable-length batch (`varlen`) and the
+packed OSDN layer forward on it (`varlen_osdn`), the
 one-token decode step at batch 1 and 64 (`decode`), the chunkwise backward on
 the default workload's shape (`bwd`), each with its own figures, and what the
 GPU sustains on a plain copy and a library GEMM (`ceilings`).
@@ -456,6 +457,59 @@ def time_varlen(steps, warmup, T=65536):
             "value": T / (ms / 1e3), "unit": "tokens/s", "ms_per_step": ms}
 
 
+def time_varlen_osdn(steps, warmup, T=65536):
+    """Packed OSDN layer forward: T tokens of log-normal document lengths at the
+    write-key workload's head shape (H=16, dk=dv=128, n_h=1, bf16); every
+    document runs phase 1 from d = 1 (a fill of d is part of the step) and then
+    the write-key forward from a zero state."""
+    import itertools
+
+    import torch
+
+    import linear_rnn_sequence_amd as dp
+    from linear_rnn_sequence_amd.inputs import WORKLOADS, make, packed_lengths
+
+    dev = torch.device("cuda:0")
+    w = WORKLOADS["c5"]
+    lengths = packed_lengths(T, seed=11)
+    inp = make(w.scaled(B=1, L=T))
+    d = {n: inp[n][0].contiguous().to(dev) for n in ("q", "k", "v", "beta")}
+    k1, b1 = d["k"][:, :, 0].contiguous(), d["beta"][:, :, 0].contiguous()
+    cu = torch.tensor([0] + list(itertools.accumulate(lengths)), dtype=torch.int32, device=dev)
+    nseq = len(lengths)
+    ws = torch.empty(dp.varlen_workspace_size(w.n_h, nseq, w.H, T, w.dk, w.dv, w.chunk),
+                     dtype=torch.uint8, device=dev)
+    dst = torch.empty(nseq, w.H, w.dk, dtype=torch.float32, device=dev)
+    kt = torch.empty(T, w.H, w.dk, dtype=torch.bfloat16, device=dev)
+    out = torch.empty(T, w.H, w.dv, dtype=torch.bfloat16, device=dev)
+    fs = torch.empty(nseq, w.H, w.dk, w.dv, dtype=torch.float32, device=dev)
+
+    def phase1():
+        dst.fill_(1.0)
+        dp.osdn_precond_varlen(k1, b1, cu, d_state=dst, kt=kt)
+
+    def step():
+        phase1()
+        dp.fwd_varlen(d["q"], d["k"], d["v"], d["beta"], cu, chunk=w.chunk, kt=kt.unsqueeze(2),
+                      out=out, final_state=fs, workspace=ws)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        return 1e3 * (time.perf_counter() - t0) / steps
+
+    ms, ms1 = timed(step), timed(phase1)
+    return {"workload": f"packed OSDN layer forward: {nseq} documents, T={T} tokens, H={w.H} "
+                        f"n_h={w.n_h} dk={w.dk} dv={w.dv} chunk={w.chunk} bf16, phase 1 per document "
+                        f"(longest {max(lengths)} tokens) then the write-key forward",
+            "value": T / (ms / 1e3), "unit": "tokens/s", "ms_per_step": ms, "phase1_ms": ms1}
+
+
 def time_bwd(w, steps, warmup):
     """Chunkwise backward (dp_bwd_*) on the forward workload ``w``'s shape:
     gradients w.r.t. q, k, v, beta (and g, h0) for a seeded output gradient,
@@ -813,6 +867,7 @@ def main():
         line["also"] = also
     if not a.no_varlen:
         line["varlen"] = time_varlen(a.steps, a.warmup)
+        line["varlen_osdn"] = time_varlen_osdn(a.steps, a.warmup)
     if not a.no_decode:
         # the pages' decode protocol (batch 1) and a serving-size batch, head shape of c3
         line["decode"] = {"b1": time_decode(1, 16, 3, 128, 128),
