@@ -460,8 +460,9 @@ def time_varlen(steps, warmup, T=65536):
 def time_varlen_osdn(steps, warmup, T=65536):
     """Packed OSDN layer forward: T tokens of log-normal document lengths at the
     write-key workload's head shape (H=16, dk=dv=128, n_h=1, bf16); every
-    document runs phase 1 from d = 1 (a fill of d is part of the step) and then
-    the write-key forward from a zero state."""
+    document runs phase 1 from d = 1 (a fill of d is part of the step; the
+    chunked form, 64-token chunks from each document's start) and then the
+    write-key forward from a zero state."""
     import itertools
 
     import torch
@@ -480,13 +481,15 @@ def time_varlen_osdn(steps, warmup, T=65536):
     ws = torch.empty(dp.varlen_workspace_size(w.n_h, nseq, w.H, T, w.dk, w.dv, w.chunk),
                      dtype=torch.uint8, device=dev)
     dst = torch.empty(nseq, w.H, w.dk, dtype=torch.float32, device=dev)
+    pws = torch.empty(max(dp.osdn_precond_varlen_workspace_size(nseq, w.H, T, w.dk), 1),
+                      dtype=torch.uint8, device=dev)
     kt = torch.empty(T, w.H, w.dk, dtype=torch.bfloat16, device=dev)
     out = torch.empty(T, w.H, w.dv, dtype=torch.bfloat16, device=dev)
     fs = torch.empty(nseq, w.H, w.dk, w.dv, dtype=torch.float32, device=dev)
 
     def phase1():
         dst.fill_(1.0)
-        dp.osdn_precond_varlen(k1, b1, cu, d_state=dst, kt=kt)
+        dp.osdn_precond_varlen(k1, b1, cu, d_state=dst, kt=kt, workspace=pws)
 
     def step():
         phase1()
@@ -506,7 +509,7 @@ def time_varlen_osdn(steps, warmup, T=65536):
     ms, ms1 = timed(step), timed(phase1)
     return {"workload": f"packed OSDN layer forward: {nseq} documents, T={T} tokens, H={w.H} "
                         f"n_h={w.n_h} dk={w.dk} dv={w.dv} chunk={w.chunk} bf16, phase 1 per document "
-                        f"(longest {max(lengths)} tokens) then the write-key forward",
+                        f"(chunked; longest {max(lengths)} tokens) then the write-key forward",
             "value": T / (ms / 1e3), "unit": "tokens/s", "ms_per_step": ms, "phase1_ms": ms1}
 
 

@@ -353,28 +353,38 @@ int dp_fwd_varlen_wk_bf16(const void* q, const void* k, const void* kt, const vo
 
 /*
  * Packed variable-length OSDN phase 1 (OSDN notes sec. 2.4 and the packed
- * batches of sec. 3.4): the exact scan of dp_osdn_precond_ex_* run on each of
- * nseq sequences packed along one token axis, every sequence from its own d.
+ * batches of sec. 3.4): phase 1 of dp_osdn_precond_ex_* run on each of nseq
+ * sequences packed along one token axis, every sequence from its own d.
  *   k [T, H, dk] T, beta [T, H] f32, r [T, H] f32 or NULL, kt [T, H, dk] T
  *   cu_seqlens [nseq + 1] int32, DEVICE memory; sequence d is tokens
- *              cu_seqlens[d] .. cu_seqlens[d+1]-1.  A sequence is read only if
- *              0 = cu[0], cu[d] <= cu[d+1] and cu[nseq] = T; otherwise it is
- *              empty: no kt row of it is written and its d is left as it was.
+ *              cu_seqlens[d] .. cu_seqlens[d+1]-1.
  *   d_state [nseq, H, dk] f32   in: each sequence's d_1; out: its d after its
  *              last token.
  *   flags, eta, dmin, dmax, eps: as dp_osdn_precond_ex_* (the box may be open).
- * Each sequence's kt and d equal dp_osdn_precond_ex_* run on it alone, bit for
- * bit.  Errors: as dp_osdn_precond_ex_*; cu_seqlens NULL or nseq < 1 is
- * DP_EINVAL.
+ *   workspace: NULL, or dp_osdn_precond_varlen_workspace_size() bytes, 256-byte
+ *              aligned.  Without one, the exact sequential scan per sequence:
+ *              each sequence's kt and d equal dp_osdn_precond_ex_* on it alone,
+ *              bit for bit.  With one and dk >= 64, the 64-token chunked form
+ *              of dp_osdn_fwd_bf16 (chunks from each sequence's start; a head
+ *              that comes within a margin of the box, or meets a NaN, runs the
+ *              exact scan from that chunk): the same values up to rounding.
+ * Offsets: in the exact scan a sequence is read only if 0 = cu[0], cu[d] <=
+ * cu[d+1] and cu[nseq] = T; in the chunked form every sequence is empty
+ * unless 0 = cu[0] <= cu[1] <= .. <= cu[nseq] = T.  An empty sequence writes
+ * no kt row and keeps its d.  Offsets that decrease make sequences overlap in
+ * the exact scan, and the kt rows they share are then undefined.
+ * Errors: as dp_osdn_precond_ex_*; cu_seqlens NULL, nseq < 1 or T < 0 is
+ * DP_EINVAL; a workspace too small or misaligned is DP_EWORKSPACE.
  */
+int dp_osdn_precond_varlen_workspace_size(int nseq, int H, int T, int dk, size_t* bytes);
 int dp_osdn_precond_varlen_f32(const float* k, const float* beta, const float* r, int flags,
                                const int* cu_seqlens, int nseq, int H, int T, int dk, float eta,
                                float dmin, float dmax, float eps, float* d_state, float* kt,
-                               dp_stream stream);
+                               void* workspace, size_t workspace_bytes, dp_stream stream);
 int dp_osdn_precond_varlen_bf16(const void* k, const float* beta, const float* r, int flags,
                                 const int* cu_seqlens, int nseq, int H, int T, int dk, float eta,
                                 float dmin, float dmax, float eps, float* d_state, void* kt,
-                                dp_stream stream);
+                                void* workspace, size_t workspace_bytes, dp_stream stream);
 
 /*
  * For callers that cannot allocate device memory (code under HIP graph

@@ -42,6 +42,7 @@ EXPORTS = (
     "dp_osdn_precond_bwd_workspace_size", "dp_osdn_precond_bwd_f32", "dp_osdn_precond_bwd_bf16",
     "dp_osdn_bwd_workspace_size", "dp_osdn_bwd_f32", "dp_osdn_bwd_bf16",
     "dp_fwd_varlen_wk_bf16", "dp_osdn_precond_varlen_f32", "dp_osdn_precond_varlen_bf16",
+    "dp_osdn_precond_varlen_workspace_size",
 )
 
 _lib = None
@@ -91,8 +92,10 @@ def load() -> ctypes.CDLL:
         for name in ("dp_osdn_precond_ex_f32", "dp_osdn_precond_ex_bf16"):
             getattr(lib, name).restype = _I
             getattr(lib, name).argtypes = pre_ex
-        # k, beta, r, flags, cu_seqlens, nseq, H, T, dk, eta, dmin, dmax, eps, d, kt, stream
-        pre_var = [_P, _P, _P, _I, _P, _I, _I, _I, _I, _F, _F, _F, _F, _P, _P, _P]
+        # k, beta, r, flags, cu_seqlens, nseq, H, T, dk, eta, dmin, dmax, eps, d, kt, ws, bytes, stream
+        pre_var = [_P, _P, _P, _I, _P, _I, _I, _I, _I, _F, _F, _F, _F, _P, _P, _P, ctypes.c_size_t, _P]
+        lib.dp_osdn_precond_varlen_workspace_size.restype = _I
+        lib.dp_osdn_precond_varlen_workspace_size.argtypes = [_I] * 4 + [ctypes.POINTER(ctypes.c_size_t)]
         for name in ("dp_osdn_precond_varlen_f32", "dp_osdn_precond_varlen_bf16"):
             getattr(lib, name).restype = _I
             getattr(lib, name).argtypes = pre_var
@@ -302,14 +305,23 @@ def osdn_precond(k, beta, *, eta: float = 3e-3, dmin: float = 0.5, dmax: float =
     return kt, d_state
 
 
+def osdn_precond_varlen_workspace_size(nseq, H, T, dk) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().dp_osdn_precond_varlen_workspace_size(nseq, H, T, dk, ctypes.byref(n)),
+           "dp_osdn_precond_varlen_workspace_size")
+    return n.value
+
+
 def osdn_precond_varlen(k, beta, cu_seqlens, *, eta: float = 3e-3, dmin: float = 0.5,
                         dmax: float = 2.0, eps: float = 1e-6, d_state=None, kt=None, r=None,
-                        beta_aware: bool = True, stream=None):
+                        beta_aware: bool = True, chunked: bool = False, workspace=None,
+                        stream=None):
     """Packed variable-length OSDN phase 1 through libdp: k [T,H,dk], beta [T,H]
     f32, cu_seqlens [nseq+1] int32 on the device.  d_state [nseq,H,dk] f32 is
     each sequence's d_1 on entry (default ones) and its last d on return.  r
-    [T,H] f32 and beta_aware as for :func:`osdn_precond`.  Returns
-    (kt [T,H,dk], d_state)."""
+    [T,H] f32 and beta_aware as for :func:`osdn_precond`.  chunked (or a given
+    workspace): the 64-token chunked form at dk >= 64, else the exact scan.
+    Returns (kt [T,H,dk], d_state)."""
     if k.dim() != 3:
         raise ValueError("expected k[T,H,dk]")
     T, H, dk = k.shape
@@ -329,10 +341,15 @@ def osdn_precond_varlen(k, beta, cu_seqlens, *, eta: float = 3e-3, dmin: float =
     if kt is None:
         kt = torch.empty(T, H, dk, dtype=dt, device=dev)
     _need(kt, "kt", dt, (T, H, dk), dev)
+    if chunked and workspace is None:
+        nbytes = osdn_precond_varlen_workspace_size(nseq, H, T, dk)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     name = f"dp_osdn_precond_varlen_{suf}"
     flags = 0 if beta_aware else PRECOND_BETA_FREE
     rc = getattr(load(), name)(_ptr(k), _ptr(beta), _ptr(r), flags, _ptr(cu_seqlens), nseq, H, T,
-                               dk, eta, dmin, dmax, eps, _ptr(d_state), _ptr(kt), _stream(stream))
+                               dk, eta, dmin, dmax, eps, _ptr(d_state), _ptr(kt), _ptr(workspace), wsb,
+                               _stream(stream))
     _check(rc, name)
     return kt, d_state
 

@@ -324,11 +324,11 @@ hipError_t dispatch_fwd(int elem, int dk, const dp::FwdArgs& a, int C, int BV, i
 
 // Phase 1 in 64-token chunks (dk >= 64): its workspace per call of L tokens.
 struct P1cWs {
-  size_t tm, v, fac, gt, dstart, gam, restart, total;
+  size_t tm, v, fac, gt, dstart, gam, restart, cbase, total;
 };
-P1cWs p1c_ws(int B, int H, int L, int dk) {
+// nbh heads, nch chunks over all heads, ncb ints of per-sequence chunk offsets
+P1cWs p1c_ws_n(size_t nbh, size_t nch, int dk, size_t ncb) {
   P1cWs w;
-  const size_t nbh = (size_t)B * H, nch = nbh * ((L + dp::kP1Chunk - 1) / dp::kP1Chunk);
   w.tm = align_up(nch * dp::kP1Chunk * dp::kP1Chunk * 4, kWsAlign);
   w.v = align_up(nch * dp::kP1Chunk * 4, kWsAlign);
   w.fac = align_up(nch * dp::kP1Chunk * 16, kWsAlign);
@@ -336,12 +336,23 @@ P1cWs p1c_ws(int B, int H, int L, int dk) {
   w.dstart = align_up(nch * dk * 4, kWsAlign);
   w.gam = w.v;
   w.restart = align_up(nbh * 4, kWsAlign);
-  w.total = dk >= 64 ? w.tm + w.v + w.fac + w.gt + w.dstart + w.gam + w.restart : 0;
+  w.cbase = align_up(ncb * 4, kWsAlign);
+  w.total = dk >= 64 ? w.tm + w.v + w.fac + w.gt + w.dstart + w.gam + w.restart + w.cbase : 0;
   return w;
 }
-// point a's chunked-form buffers into ws (p1c_ws(B, H, L, dk).total bytes)
+P1cWs p1c_ws(int B, int H, int L, int dk) {
+  const size_t nbh = (size_t)B * H;
+  return p1c_ws_n(nbh, nbh * ((L + dp::kP1Chunk - 1) / dp::kP1Chunk), dk, 0);
+}
+// packed: nseq sequences over T tokens, at most ceil(T / C) + nseq chunks per head
+P1cWs p1c_ws_var(int nseq, int H, int T, int dk) {
+  return p1c_ws_n((size_t)nseq * H, (size_t)H * ((T + dp::kP1Chunk - 1) / dp::kP1Chunk + nseq), dk,
+                  (size_t)nseq + 1);
+}
+// point a's chunked-form buffers into ws (p1c_ws(B, H, L, dk).total bytes, or
+// p1c_ws_var(B, H, L, dk).total with packed sequences)
 void p1c_bind(dp::PrecondArgs& a, char* ws, int dk) {
-  const P1cWs w = p1c_ws(a.B, a.H, a.L, dk);
+  const P1cWs w = a.cu != nullptr ? p1c_ws_var(a.B, a.H, a.L, dk) : p1c_ws(a.B, a.H, a.L, dk);
   char* o = ws;
   a.wsTm = reinterpret_cast<float*>(o);
   o += w.tm;
@@ -356,6 +367,8 @@ void p1c_bind(dp::PrecondArgs& a, char* ws, int dk) {
   a.gam = reinterpret_cast<float*>(o);
   o += w.gam;
   a.restart = reinterpret_cast<int*>(o);
+  o += w.restart;
+  a.cbase = a.cu != nullptr ? reinterpret_cast<int*>(o) : nullptr;
 }
 
 hipError_t dispatch_precond_chunked(int elem, int dk, const dp::PrecondArgs& a, hipStream_t st) {
@@ -679,10 +692,11 @@ int precond_impl(int elem, const void* k, const float* beta, const float* ret, i
   a.eps = eps;
   a.Ls = Ls;
   a.t0 = t0;
-  a.cu = cu;  // packed sequences: B of them over L tokens (the exact scan)
-  // with a workspace for it (p1c_ws) and dk >= 64, the chunked form, whose
-  // hand-over to the exact scan keeps the sequential definition's result
-  if (p1c != nullptr && dk >= 64 && cu == nullptr) {
+  a.cu = cu;  // packed sequences: B of them over L tokens
+  // with a workspace for it (p1c_ws, or p1c_ws_var when packed) and dk >= 64,
+  // the chunked form, whose hand-over to the exact scan keeps the sequential
+  // definition's result
+  if (p1c != nullptr && dk >= 64) {
     p1c_bind(a, p1c, dk);
     const hipError_t e = dispatch_precond_chunked(elem, dk, a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? DP_OK : DP_EHIP;
@@ -1151,22 +1165,46 @@ int dp_osdn_precond_ex_bf16(const void* k, const float* beta, const float* r, in
                       stream);
 }
 
+int dp_osdn_precond_varlen_workspace_size(int nseq, int H, int T, int dk, size_t* bytes) {
+  if (bytes == nullptr || nseq <= 0 || H <= 0 || T < 0) return DP_EINVAL;
+  if (!dim_ok(dk)) return DP_ENOTSUP;
+  *bytes = p1c_ws_var(nseq, H, T, dk).total;
+  return DP_OK;
+}
+
+namespace {
+int precond_varlen(int elem, const void* k, const float* beta, const float* r, int flags,
+                   const int* cu_seqlens, int nseq, int H, int T, int dk, float eta, float dmin,
+                   float dmax, float eps, float* d_state, void* kt, void* workspace,
+                   size_t workspace_bytes, dp_stream stream) {
+  if (cu_seqlens == nullptr || nseq <= 0 || H <= 0 || T < 0) return DP_EINVAL;
+  char* p1c = nullptr;
+  if (workspace != nullptr && dim_ok(dk)) {
+    const size_t need = p1c_ws_var(nseq, H, T, dk).total;
+    if (workspace_bytes < need || ((uintptr_t)workspace & (kWsAlign - 1)) != 0) return DP_EWORKSPACE;
+    if (need > 0) p1c = static_cast<char*>(workspace);
+  }
+  if ((long long)H * ((T + dp::kP1Chunk - 1) / dp::kP1Chunk + (long long)nseq) > (long long)INT_MAX)
+    return DP_ENOTSUP;
+  return precond_impl(elem, k, beta, r, flags, nseq, H, T, dk, eta, dmin, dmax, eps, d_state, kt, true,
+                      stream, 0, 0, false, p1c, cu_seqlens);
+}
+}  // namespace
+
 int dp_osdn_precond_varlen_f32(const float* k, const float* beta, const float* r, int flags,
                                const int* cu_seqlens, int nseq, int H, int T, int dk, float eta,
                                float dmin, float dmax, float eps, float* d_state, float* kt,
-                               dp_stream stream) {
-  if (cu_seqlens == nullptr || nseq <= 0) return DP_EINVAL;
-  return precond_impl(4, k, beta, r, flags, nseq, H, T, dk, eta, dmin, dmax, eps, d_state, kt, true,
-                      stream, 0, 0, false, nullptr, cu_seqlens);
+                               void* workspace, size_t workspace_bytes, dp_stream stream) {
+  return precond_varlen(4, k, beta, r, flags, cu_seqlens, nseq, H, T, dk, eta, dmin, dmax, eps, d_state,
+                        kt, workspace, workspace_bytes, stream);
 }
 
 int dp_osdn_precond_varlen_bf16(const void* k, const float* beta, const float* r, int flags,
                                 const int* cu_seqlens, int nseq, int H, int T, int dk, float eta,
                                 float dmin, float dmax, float eps, float* d_state, void* kt,
-                                dp_stream stream) {
-  if (cu_seqlens == nullptr || nseq <= 0) return DP_EINVAL;
-  return precond_impl(2, k, beta, r, flags, nseq, H, T, dk, eta, dmin, dmax, eps, d_state, kt, true,
-                      stream, 0, 0, false, nullptr, cu_seqlens);
+                                void* workspace, size_t workspace_bytes, dp_stream stream) {
+  return precond_varlen(2, k, beta, r, flags, cu_seqlens, nseq, H, T, dk, eta, dmin, dmax, eps, d_state,
+                        kt, workspace, workspace_bytes, stream);
 }
 
 int dp_osdn_fwd_workspace_size(int B, int H, int L, int dk, int dv, int chunk, int segments,

@@ -140,9 +140,11 @@ struct PrecondArgs {
   // [B*H] first chunk whose check failed (nc: none): with it, dp_precond_kernel
   // runs the exact scan from that chunk's start d and leaves other heads alone
   int* restart = nullptr;
-  // packed sequences (exact scan only): B of them along one axis of L tokens,
-  // sequence b being tokens cu[b] .. cu[b+1]-1 (device memory), or nullptr
+  // packed sequences: B of them along one axis of L tokens, sequence b being
+  // tokens cu[b] .. cu[b+1]-1 (device memory), or nullptr; with the chunked
+  // form also cbase[B+1], the first 64-token chunk of every sequence
   const int* cu = nullptr;
+  int* cbase = nullptr;
 };
 
 __host__ __device__ constexpr int align16(int x) { return (x + 15) & ~15; }
@@ -1426,12 +1428,18 @@ __global__ __launch_bounds__(64) void dp_precond_kernel(PrecondArgs p) {
     // after the chunked form: start at the head's first failed chunk, or not at all
     int tbeg = 0;
     if (p.restart != nullptr) {
-      const int nc = (p.L + 63) / 64;
+      // the head's chunks: nc of them from blk0 (packed: sequence b's, head-major)
+      int nc = (p.L + 63) / 64;
+      long long blk0 = bh * nc;
+      if (p.cu != nullptr) {
+        nc = p.cbase[b + 1] - p.cbase[b];
+        blk0 = (long long)p.cbase[b] * p.H + (long long)h * nc;
+      }
       const int sc = p.restart[bh];
       if (sc >= nc) return;
       tbeg = sc * 64;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) d[e] = p.dstart[((long long)bh * nc + sc) * DK + sl * EPL + e];
+      for (int e = 0; e < EPL; ++e) d[e] = p.dstart[(blk0 + sc) * DK + sl * EPL + e];
     }
     constexpr int RB = DK * (int)sizeof(T);       // bytes per key row
     static_assert(RB % 16 == 0, "key rows in 16-byte pieces");

@@ -44,6 +44,56 @@ __device__ __forceinline__ void st_f16s(f16_t* p, const float* f) {
 
 // --------------------------------------------------------------------------
 // dp_p1_ut_kernel: one workgroup per (head, chunk), all in parallel.
+// Where a head's chunks live.  Fixed length: B H heads of L tokens, nc =
+// ceil(L / C) chunks each, chunk c of head bh at bh nc + c.  Packed sequences
+// (p.cu; p.cbase from dp_varlen_chunks_kernel with n_h = 1): sequence s has
+// cbase[s+1] - cbase[s] chunks per head, stored head by head from cbase[s] H.
+// All-zero offsets (what that kernel leaves for malformed cu) make every
+// sequence empty.
+struct P1Head {
+  long long row0;  // token-major row of the head's first token
+  long long blk0;  // its first chunk in the per-chunk arrays
+  int L, nc;       // its tokens and chunks
+};
+__device__ __forceinline__ P1Head p1_head(const PrecondArgs& p, long long bh) {
+  const int b = (int)(bh / p.H), h = (int)(bh % p.H);
+  P1Head g;
+  if (p.cu == nullptr) {
+    g.L = p.L;
+    g.nc = (p.L + kP1Chunk - 1) / kP1Chunk;
+    g.row0 = tok_base(p, b) * p.H + h;
+    g.blk0 = bh * g.nc;
+  } else {
+    g.nc = p.cbase[b + 1] - p.cbase[b];
+    g.L = g.nc > 0 ? p.cu[b + 1] - p.cu[b] : 0;
+    g.row0 = (g.nc > 0 ? (long long)p.cu[b] : 0ll) * p.H + h;
+    g.blk0 = (long long)p.cbase[b] * p.H + (long long)h * g.nc;
+  }
+  return g;
+}
+// Work item w of the per-chunk kernels -> head bh and chunk c; false past the
+// last chunk (packed: the grid is an upper bound).
+__device__ __forceinline__ bool p1_item(const PrecondArgs& p, long long w, long long& bh, int& c) {
+  if (p.cu == nullptr) {
+    const int nc = (p.L + kP1Chunk - 1) / kP1Chunk;
+    bh = w / nc;
+    c = (int)(w % nc);
+    return true;
+  }
+  if (w >= (long long)p.cbase[p.B] * p.H) return false;
+  // the last sequence s with cbase[s] H <= w; it has chunks, since cbase[s+1] H > w
+  int lo = 0, hi = p.B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((long long)p.cbase[mid] * p.H <= w) lo = mid; else hi = mid - 1;
+  }
+  const int ncs = p.cbase[lo + 1] - p.cbase[lo];
+  const long long rel = w - (long long)p.cbase[lo] * p.H;
+  bh = (long long)lo * p.H + rel / ncs;
+  c = (int)(rel % ncs);
+  return true;
+}
+
 template <typename T, int DK>
 __global__ __launch_bounds__(256) void dp_p1_ut_kernel(PrecondArgs p) {
   constexpr int C = kP1Chunk, LDM = kP1Ld, NT = C / 16;
@@ -69,12 +119,13 @@ __global__ __launch_bounds__(256) void dp_p1_ut_kernel(PrecondArgs p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
-  const int nc = (p.L + C - 1) / C;
-  const long long chunk = blockIdx.x;
-  const long long bh = chunk / nc;
-  const int c = (int)(chunk % nc);
-  const int b = (int)(bh / p.H), h = (int)(bh % p.H);
-  const long long row0 = tok_base(p, b) * p.H + h;
+  long long bh;
+  int c;
+  if (!p1_item(p, blockIdx.x, bh, c)) return;
+  const P1Head hg = p1_head(p, bh);
+  const long long chunk = hg.blk0 + c;
+  const long long row0 = hg.row0;
+  const int L = hg.L;
   const int t0 = c * C;
   const T* kp = static_cast<const T*>(p.k);
 
@@ -85,10 +136,10 @@ __global__ __launch_bounds__(256) void dp_p1_ut_kernel(PrecondArgs p) {
     const int idx = tid + it * 256;
     const int r = idx / TPR, cg = idx % TPR;
     rk[it] = u32x4_t{0u, 0u, 0u, 0u};
-    if (idx < KV && t0 + r < p.L) rk[it] = ld16(kp + (row0 + (long long)(t0 + r) * p.H) * DK + cg * VE);
+    if (idx < KV && t0 + r < L) rk[it] = ld16(kp + (row0 + (long long)(t0 + r) * p.H) * DK + cg * VE);
   }
   float braw = 0.f, rr = 1.f;
-  if (tid < C && t0 + tid < p.L) {
+  if (tid < C && t0 + tid < L) {
     const long long rw = row0 + (long long)(t0 + tid) * p.H;
     braw = p.beta[rw];
     if (p.ret != nullptr) rr = p.ret[rw];
@@ -127,7 +178,7 @@ __global__ __launch_bounds__(256) void dp_p1_ut_kernel(PrecondArgs p) {
   __syncthreads();
   // 2. per-token factors and the cumulative log-retention (G_0 = 0)
   if (wave == 0) {
-    const bool ok = lane < C && t0 + lane < p.L;
+    const bool ok = lane < C && t0 + lane < L;
     float w = 0.f, c2 = 0.f, lr = 0.f;
     if (ok) {
       const float bu = p.beta_aware ? clamp_keep_nan(braw, 0.f, 2.f) : 1.f;
@@ -272,10 +323,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   __shared__ float sD[DK], sCoef[C], sW[C], sC2[C], sG[C + 1], sV[C];
 
   const int tid = threadIdx.x, cg = tid % TPR, rg = tid / TPR;
-  const int nc = (p.L + C - 1) / C;
   const long long bh = blockIdx.x;
-  const int b = (int)(bh / p.H), h = (int)(bh % p.H);
-  const long long row0 = tok_base(p, b) * p.H + h;
+  const P1Head hg = p1_head(p, bh);
+  const int nc = hg.nc, L = hg.L;
+  const long long row0 = hg.row0;
   const T* kp = static_cast<const T*>(p.k);
 
   // a chunk's operands in registers: two sets, loaded two chunks ahead of use
@@ -287,14 +338,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     float rv, rgt;
   };
   auto prefetch = [&](Stage& S, int c) {  // 0 <= c < nc
-    const long long chunk = bh * nc + c;
+    const long long chunk = hg.blk0 + c;
     const int t0 = c * C;
 #pragma unroll
     for (int it = 0; it < KIT; ++it) {
       const int r = rg + RPI * it;
-      const int tr = min(t0 + r, p.L - 1);  // rows past the end: loaded in bounds, then zeroed
+      const int tr = min(t0 + r, L - 1);  // rows past the end: loaded in bounds, then zeroed
       const u32x4_t v = ld16(kp + (row0 + (long long)tr * p.H) * DK + cg * VE);
-      const bool in = t0 + r < p.L;
+      const bool in = t0 + r < L;
       S.rk[it] = u32x4_t{in ? v[0] : 0u, in ? v[1] : 0u, in ? v[2] : 0u, in ? v[3] : 0u};
       S.rf[it] = p.wsFac[chunk * C + r];
     }
@@ -309,7 +360,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   if (tid < DK) sD[tid] = p.d_ones ? 1.f : p.d[bh * DK + tid];
   if (tid == 0) p.restart[bh] = nc;
   auto body = [&](Stage& S, int c) {
-    const long long chunk = bh * nc + c;
+    const long long chunk = hg.blk0 + c;
     block_sync_lds();  // d of this chunk's start is in sD; the last chunk's reads are done
     if (tid < C) {
       sW[tid] = S.rfac.y;
@@ -421,13 +472,13 @@ __global__ __launch_bounds__(DK) void dp_p1_emit_kernel(PrecondArgs p) {
   __shared__ float4 sFac[C];
   __shared__ float sGam[C], sR[C];
   const int j = threadIdx.x;
-  const int nc = (p.L + C - 1) / C;
-  const long long chunk = blockIdx.x;
-  const long long bh = chunk / nc;
-  const int c = (int)(chunk % nc);
-  const int b = (int)(bh / p.H), h = (int)(bh % p.H);
-  const long long row0 = tok_base(p, b) * p.H + h;
-  const int t0 = c * C, n = min(C, p.L - t0);
+  long long bh;
+  int c;
+  if (!p1_item(p, blockIdx.x, bh, c)) return;
+  const P1Head hg = p1_head(p, bh);
+  const long long chunk = hg.blk0 + c;
+  const long long row0 = hg.row0;
+  const int t0 = c * C, n = min(C, hg.L - t0);
   const long long ks = (long long)p.H * DK;
   const T* kp = static_cast<const T*>(p.k) + (row0 + (long long)t0 * p.H) * DK;
 #pragma unroll
@@ -466,17 +517,26 @@ template <typename T, int DK>
 hipError_t launch_precond_chunked(const PrecondArgs& a, hipStream_t st) {
   static_assert(DK >= 64, "the exact fallback runs one head per wavefront");
   const long long nbh = (long long)a.B * a.H;
-  const int nc = (a.L + kP1Chunk - 1) / kP1Chunk;
   if (nbh == 0) return hipSuccess;
-  if (nc > 0) {
-    hipLaunchKernelGGL((dp_p1_ut_kernel<T, DK>), dim3((unsigned)(nbh * nc)), dim3(256), 0, st, a);
+  // per-chunk work items: every chunk of every head (packed: an upper bound,
+  // ceil(L / C) + B chunks per head, the extra items exit)
+  long long nwork = nbh * ((a.L + kP1Chunk - 1) / kP1Chunk);
+  if (a.cu != nullptr) {
+    hipLaunchKernelGGL((dp_varlen_chunks_kernel<kP1Chunk>), dim3(1), dim3(256), 0, st, a.cu, a.B, 1, a.L,
+                       a.cbase);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    nwork = (long long)a.H * ((a.L + kP1Chunk - 1) / kP1Chunk + a.B);
+  }
+  if (nwork > 0) {
+    hipLaunchKernelGGL((dp_p1_ut_kernel<T, DK>), dim3((unsigned)nwork), dim3(256), 0, st, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL((dp_p1_chain_kernel<T, DK>), dim3((unsigned)nbh), dim3(256), 0, st, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || nc == 0) return e;
-  hipLaunchKernelGGL((dp_p1_emit_kernel<T, DK>), dim3((unsigned)(nbh * nc)), dim3(DK), 0, st, a);
+  if (e != hipSuccess || nwork == 0) return e;
+  hipLaunchKernelGGL((dp_p1_emit_kernel<T, DK>), dim3((unsigned)nwork), dim3(DK), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   // the exact scan from the first chunk that failed the check (heads with none return at once)

@@ -311,8 +311,9 @@ def test_precond_varlen_validation_errors_before_hip(lib):
     E = dp.binding
     for f in (lib.dp_osdn_precond_varlen_f32, lib.dp_osdn_precond_varlen_bf16):
         def call(k=FAKE, beta=FAKE, r=None, flags=0, cu=FAKE, nseq=2, H=1, T=8, dk=16, eta=3e-3,
-                 dmin=0.5, dmax=2.0, eps=1e-6, d=FAKE, kt=FAKE):
-            return f(k, beta, r, flags, cu, nseq, H, T, dk, eta, dmin, dmax, eps, d, kt, None)
+                 dmin=0.5, dmax=2.0, eps=1e-6, d=FAKE, kt=FAKE, wsp=None, wsb=0):
+            return f(k, beta, r, flags, cu, nseq, H, T, dk, eta, dmin, dmax, eps, d, kt, wsp, wsb,
+                     None)
 
         assert call(cu=None) == E.DP_EINVAL
         assert call(nseq=0) == E.DP_EINVAL
@@ -323,6 +324,28 @@ def test_precond_varlen_validation_errors_before_hip(lib):
         assert call(dmin=3.0) == E.DP_EINVAL         # dmin > dmax
         assert call(dk=24) == E.DP_ENOTSUP
         assert call(T=0) == E.DP_OK                  # nothing to scan: no launch
+        assert call(dk=64, wsp=FAKE, wsb=16) == E.DP_EWORKSPACE          # too small
+        assert call(dk=64, wsp=FAKE + 16, wsb=1 << 30) == E.DP_EWORKSPACE  # misaligned
+
+
+def test_precond_varlen_workspace_size(lib):
+    """The chunked form's arrays sized for ceil(T / 64) + nseq chunks per head,
+    then one restart slot per head and the nseq + 1 chunk offsets, each region
+    256-byte aligned; dk < 64 has no chunked form (0 bytes)."""
+    n = SZ(0)
+    up = lambda x: -(-x // 256) * 256
+    nseq, H, T, dk = 5, 3, 1000, 128
+    nch = H * (-(-T // 64) + nseq)
+    want = (up(nch * 64 * 64 * 4) + 2 * up(nch * 64 * 4) + up(nch * 64 * 16) + up(nch * 4)
+            + up(nch * dk * 4) + up(nseq * H * 4) + up((nseq + 1) * 4))
+    assert lib.dp_osdn_precond_varlen_workspace_size(nseq, H, T, dk, ctypes.byref(n)) == 0
+    assert n.value == want
+    assert lib.dp_osdn_precond_varlen_workspace_size(nseq, H, T, 32, ctypes.byref(n)) == 0
+    assert n.value == 0
+    assert lib.dp_osdn_precond_varlen_workspace_size(0, H, T, dk, ctypes.byref(n)) == \
+        dp.binding.DP_EINVAL
+    assert lib.dp_osdn_precond_varlen_workspace_size(nseq, H, T, 24, ctypes.byref(n)) == \
+        dp.binding.DP_ENOTSUP
 
 
 def test_varlen_workspace_size(lib):

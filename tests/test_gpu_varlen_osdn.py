@@ -201,3 +201,110 @@ def test_varlen_wk_general_write_keys_gate_and_n_h():
     for name, e in errs.items():
         say(f"  {name}: worst err {e:.3e} (tol {TOL['bf16']:.0e})")
         assert e <= TOL["bf16"], f"{name}: err {e:.3e} > {TOL['bf16']}"
+
+
+CHUNK_CASES = [  # dtype, H, dk, lengths
+    ("bf16", 2, 128, [0, 200, 7, 64, 129, 1, 65]),
+    ("bf16", 3, 64, [130, 1, 0, 65, 300]),
+    ("f32", 2, 128, [100, 0, 64, 257]),
+]
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("dtype,H,dk,lengths", CHUNK_CASES, ids=[f"{c[0]}-dk{c[2]}-{i}" for i, c in enumerate(CHUNK_CASES)])
+def test_precond_varlen_chunked_matches_oracle(dtype, H, dk, lengths, variant):
+    """The chunked form on packed sequences (64-token chunks from each sequence's
+    start) against the oracle on each sequence alone: d at the bound, the keys
+    at the bound (f32) or within bf16 rounding (bf16)."""
+    say(f"case precond varlen chunked {dtype} H={H} dk={dk} lengths={lengths} {variant}")
+    k, b, r, d0 = packed_keys(H, dk, lengths, dtype, seed=3)
+    cu = offsets(lengths)
+    rr = r if variant == "apf" else None
+    aware = variant != "beta_free"
+    cuda = lambda x: None if x is None else x.cuda()
+    kt, d = dp.osdn_precond_varlen(k.cuda(), b.cuda(), cu.cuda(), d_state=d0.clone().cuda(),
+                                   r=cuda(rr), beta_aware=aware, chunked=True)
+    torch.cuda.synchronize()
+    kt, d = kt.cpu(), d.cpu()
+    errs = {"d": 0.0} if dtype == "bf16" else {"kt": 0.0, "d": 0.0}
+    for s, n in enumerate(lengths):
+        a = int(cu[s])
+        if n == 0:
+            assert torch.equal(d[s], d0[s]), f"sequence {s}: an empty sequence changed its d"
+            continue
+        one = lambda x: None if x is None else x[a:a + n].unsqueeze(0)
+        kto, do = oracle.precond(one(k), one(b), d0=d0[s:s + 1], r=one(rr), beta_aware=aware)
+        if dtype == "bf16":
+            check_bf16_stored(f64(kt[a:a + n]), kto[0], f"sequence {s}")
+        else:
+            errs["kt"] = max(errs["kt"], rel_err(f64(kt[a:a + n]), kto[0]))
+        errs["d"] = max(errs["d"], rel_err(f64(d[s]), do[0]))
+    for name, e in errs.items():
+        say(f"  {name}: worst err {e:.3e} (tol {TOL[dtype]:.0e})")
+        assert e <= TOL[dtype], f"{name}: err {e:.3e} > {TOL[dtype]}"
+
+
+def test_precond_varlen_chunked_equals_the_layer_phase1_bit_for_bit():
+    """Each packed sequence's chunked phase 1 is the chunked phase 1 that
+    dp_osdn_fwd_bf16 runs on that sequence alone (one run): same chunks, same
+    kernels, so the same bits."""
+    H, dk, dv = 2, 128, 64
+    lengths = [200, 1, 0, 64, 129]
+    k, b, _, _ = packed_keys(H, dk, lengths, "bf16", seed=5)
+    cu = offsets(lengths)
+    kt, d = dp.osdn_precond_varlen(k.cuda(), b.cuda(), cu.cuda(), chunked=True)
+    torch.cuda.synchronize()
+    kt, d = kt.cpu(), d.cpu()
+    gen = torch.Generator().manual_seed(6)
+    for s, n in enumerate(lengths):
+        if n == 0:
+            continue
+        a = int(cu[s])
+        one = lambda x: x[a:a + n].unsqueeze(0).contiguous().cuda()
+        q = torch.randn(1, n, H, dk, generator=gen).to(torch.bfloat16).cuda()
+        v = torch.randn(1, n, H, dv, generator=gen).to(torch.bfloat16).cuda()
+        _, _, kt1, d1 = dp.osdn_fwd(q, one(k), v, one(b), segments=1)
+        torch.cuda.synchronize()
+        assert torch.equal(kt[a:a + n], kt1[0].cpu()), f"sequence {s}: kt differs from the layer's phase 1"
+        assert torch.equal(d[s], d1[0].cpu()), f"sequence {s}: d differs from the layer's phase 1"
+
+
+def test_precond_varlen_chunked_hands_clamped_heads_to_the_exact_scan():
+    """A large step size makes the box bind inside some chunks: those heads
+    continue with the exact scan from their first such chunk (per sequence,
+    from the chunk's start d), and every sequence still meets the oracle."""
+    H, dk = 3, 128
+    lengths = [150, 0, 70, 300, 5]
+    k, b, _, _ = packed_keys(H, dk, lengths, "f32", seed=7)
+    cu = offsets(lengths)
+    box = dict(eta=0.8, dmin=0.95, dmax=1.05)  # a narrow box: coordinates end on its bounds
+    kt, d = dp.osdn_precond_varlen(k.cuda(), b.cuda(), cu.cuda(), chunked=True, **box)
+    torch.cuda.synchronize()
+    kt, d = kt.cpu(), d.cpu()
+    clamped = 0
+    for s, n in enumerate(lengths):
+        if n == 0:
+            assert bool((d[s] == 1.0).all())
+            continue
+        a = int(cu[s])
+        one = lambda x: x[a:a + n].unsqueeze(0)
+        kto, do = oracle.precond(one(k), one(b), **box)
+        clamped += int(np.sum((do[0] <= 0.95) | (do[0] >= 1.05)))
+        e_kt, e_d = rel_err(f64(kt[a:a + n]), kto[0]), rel_err(f64(d[s]), do[0])
+        say(f"  sequence {s}: kt err {e_kt:.3e}, d err {e_d:.3e}")
+        assert e_kt <= TOL["f32"] and e_d <= TOL["f32"]
+    assert clamped > 0, "the case should make the box bind"
+
+
+def test_precond_varlen_chunked_malformed_offsets_read_nothing():
+    """In the chunked form, offsets that are not a valid packing make every
+    sequence empty: kt is left as it was and d keeps its value."""
+    k, b, _, d0 = packed_keys(2, 128, [30, 30], "bf16", seed=9)  # T = 60, two sequences
+    for bad in ([0, 70, 60], [0, 30, 50]):
+        cu = torch.tensor(bad, dtype=torch.int32).cuda()
+        kt = torch.full((60, 2, 128), 7.0, dtype=torch.bfloat16, device="cuda")
+        d = d0.clone().cuda()
+        dp.osdn_precond_varlen(k.cuda(), b.cuda(), cu, d_state=d, kt=kt, chunked=True)
+        torch.cuda.synchronize()
+        assert bool((kt == 7.0).all()), f"offsets {bad}: kt was written"
+        assert torch.equal(d.cpu(), d0), f"offsets {bad}: d changed"
