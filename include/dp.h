@@ -334,6 +334,23 @@ int dp_fwd_varlen_bf16(const void* q, const void* k, const void* v, const float*
                        void* workspace, size_t workspace_bytes, int flags, dp_stream stream);
 
 /*
+ * The packed forward on fp32 inputs (q, k, kt, v and out all float32; the
+ * UT / scan kernels), symmetric keys or write keys; otherwise as
+ * dp_fwd_varlen_bf16 and dp_fwd_varlen_wk_bf16, with the same workspace size.
+ * Each result equals dp_fwd_f32 / dp_fwd_wk_f32 run on that sequence alone.
+ * Errors: as dp_fwd_ex_f32; kt NULL with T > 0 (write keys) is DP_EINVAL.
+ */
+int dp_fwd_varlen_f32(const float* q, const float* k, const float* v, const float* beta,
+                      const float* g, const int* cu_seqlens, int nseq, int n_h, int H, int T,
+                      int dk, int dv, int chunk, float* out, float* final_state, const float* h0,
+                      void* workspace, size_t workspace_bytes, int flags, dp_stream stream);
+int dp_fwd_varlen_wk_f32(const float* q, const float* k, const float* kt, const float* v,
+                         const float* beta, const float* g, const int* cu_seqlens, int nseq,
+                         int n_h, int H, int T, int dk, int dv, int chunk, float* out,
+                         float* final_state, const float* h0, void* workspace,
+                         size_t workspace_bytes, int flags, dp_stream stream);
+
+/*
  * Packed variable-length write-key forward (OSDN notes sec. 2.5 phase 2, on
  * the packed batches of sec. 3.4: documents packed along one token axis, the
  * state restarting at each document): dp_fwd_varlen_bf16 with the write keys

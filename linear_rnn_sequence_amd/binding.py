@@ -42,7 +42,7 @@ EXPORTS = (
     "dp_osdn_precond_bwd_workspace_size", "dp_osdn_precond_bwd_f32", "dp_osdn_precond_bwd_bf16",
     "dp_osdn_bwd_workspace_size", "dp_osdn_bwd_f32", "dp_osdn_bwd_bf16",
     "dp_fwd_varlen_wk_bf16", "dp_osdn_precond_varlen_f32", "dp_osdn_precond_varlen_bf16",
-    "dp_osdn_precond_varlen_workspace_size",
+    "dp_osdn_precond_varlen_workspace_size", "dp_fwd_varlen_f32", "dp_fwd_varlen_wk_f32",
 )
 
 _lib = None
@@ -106,6 +106,10 @@ def load() -> ctypes.CDLL:
                                            _P, _P, ctypes.c_size_t, _I, _P]
         lib.dp_fwd_varlen_wk_bf16.restype = _I
         lib.dp_fwd_varlen_wk_bf16.argtypes = [_P] * 7 + [_I] * 7 + [_P] * 4 + [ctypes.c_size_t, _I, _P]
+        lib.dp_fwd_varlen_f32.restype = _I
+        lib.dp_fwd_varlen_f32.argtypes = lib.dp_fwd_varlen_bf16.argtypes
+        lib.dp_fwd_varlen_wk_f32.restype = _I
+        lib.dp_fwd_varlen_wk_f32.argtypes = lib.dp_fwd_varlen_wk_bf16.argtypes
         lib.dp_fwd_varlen_noalloc_bf16.restype = _I
         lib.dp_fwd_varlen_noalloc_bf16.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P,
                                                    _P, _P, _I, _P]
@@ -483,9 +487,9 @@ def varlen_workspace_size(n_h, nseq, H, T, dk, dv, chunk) -> int:
 def fwd_varlen(q, k, v, beta, cu_seqlens, g=None, *, chunk: int = 64, h0=None, kt=None, out=None,
                final_state=None, return_state: bool = True, workspace=None,
                stages: int = STAGE_ALL, out_dtype=None, path: str = "auto", stream=None):
-    """Packed variable-length forward (bf16) through libdp.
+    """Packed variable-length forward through libdp.
 
-    q [T,H,dk], k [T,H,n_h,dk], v [T,H,n_h,dv] bfloat16, beta [T,H,n_h] f32,
+    q [T,H,dk], k [T,H,n_h,dk], v [T,H,n_h,dv] bfloat16 or float32, beta [T,H,n_h] f32,
     g [T,H] f32 or None, cu_seqlens [nseq+1] int32 on the device, h0
     [nseq,H,dk,dv] f32 or None.  kt [T,H,n_h,dk] bfloat16: the write keys
     (dp_fwd_varlen_wk_bf16), else symmetric keys.  path as for fwd.  Returns
@@ -496,8 +500,9 @@ def fwd_varlen(q, k, v, beta, cu_seqlens, g=None, *, chunk: int = 64, h0=None, k
     T, H, dk = q.shape
     n_h, dv = k.shape[2], v.shape[3]
     dev, dt = q.device, q.dtype
-    if dt != torch.bfloat16:
-        raise TypeError("fwd_varlen takes bfloat16 q, k, v")
+    if dt not in (torch.bfloat16, torch.float32):
+        raise TypeError("fwd_varlen takes bfloat16 or float32 q, k, v")
+    suf = _suffix(dt)
     if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
         raise ValueError("cu_seqlens must be [nseq + 1]")
     nseq = cu_seqlens.numel() - 1
@@ -529,11 +534,11 @@ def fwd_varlen(q, k, v, beta, cu_seqlens, g=None, *, chunk: int = 64, h0=None, k
             _ptr(out), _ptr(final_state), _ptr(h0), _ptr(workspace),
             workspace.numel() * workspace.element_size(), flags, _stream(stream))
     if kt is None:
-        name = "dp_fwd_varlen_bf16"
-        rc = load().dp_fwd_varlen_bf16(_ptr(q), _ptr(k), *tail)
+        name = f"dp_fwd_varlen_{suf}"
+        rc = getattr(load(), name)(_ptr(q), _ptr(k), *tail)
     else:
-        name = "dp_fwd_varlen_wk_bf16"
-        rc = load().dp_fwd_varlen_wk_bf16(_ptr(q), _ptr(k), _ptr(kt), *tail)
+        name = f"dp_fwd_varlen_wk_{suf}"
+        rc = getattr(load(), name)(_ptr(q), _ptr(k), _ptr(kt), *tail)
     _check(rc, name)
     return out, final_state
 

@@ -515,12 +515,27 @@ size_t varlen_blocks_bytes(const VarShape& v) {
   return align_up((size_t)varlen_nwork(v) * W.bytes, kWsAlign);
 }
 size_t varlen_cbase_bytes(const VarShape& v) { return align_up((size_t)(v.nseq + 1) * 4, kWsAlign); }
-size_t varlen_ws_total(const VarShape& v) {
+// fp32 inputs (UT / scan kernels): T (C x C fp32) and the per-sub-step
+// scalars (C float2) of every work item, then the first chunks
+size_t varlen_t32_bytes(const VarShape& v) {
+  return align_up((size_t)varlen_nwork(v) * v.chunk * v.chunk * 4, kWsAlign);
+}
+size_t varlen_s32_bytes(const VarShape& v) {
+  return align_up((size_t)varlen_nwork(v) * v.chunk * sizeof(float2), kWsAlign);
+}
+size_t varlen_ws_total16(const VarShape& v) {
   return varlen_blocks_bytes(v) + varlen_cbase_bytes(v) +
          align_up((size_t)v.nseq * v.H * (v.dv / 16) * 64 * 4, kWsAlign);
 }
+size_t varlen_ws_total32(const VarShape& v) {
+  return varlen_t32_bytes(v) + varlen_s32_bytes(v) + varlen_cbase_bytes(v);
+}
+// one size serves both input types and both packed forms
+size_t varlen_ws_total(const VarShape& v) { return std::max(varlen_ws_total16(v), varlen_ws_total32(v)); }
 // the fused kernel needs only the per-sequence first chunks
-size_t varlen_ws_need(const VarShape& v, bool fused) { return fused ? varlen_cbase_bytes(v) : varlen_ws_total(v); }
+size_t varlen_ws_need(const VarShape& v, bool fused, int elem) {
+  return fused ? varlen_cbase_bytes(v) : elem == 4 ? varlen_ws_total32(v) : varlen_ws_total16(v);
+}
 
 // table: when not NULL, the fused kernel's chunk-offset table lives there (at
 // least nseq + 1 ints) and no workspace is used.  dry: validate and plan only.
@@ -529,25 +544,25 @@ int varlen_impl(const void* q, const void* k, const void* v, const float* beta, 
                 const int* cu_seqlens, int nseq, int n_h, int H, int T, int dk, int dv, int chunk,
                 void* out, float* final_state, const float* h0, void* workspace,
                 size_t workspace_bytes, int flags, dp_stream stream, int* table = nullptr,
-                bool dry = false, const void* kt = nullptr) {
+                bool dry = false, const void* kt = nullptr, int elem = 2) {
   const VarShape vs{n_h, nseq, H, T, dk, dv, chunk};
   int rc = check_varlen(vs);
   if (rc != DP_OK) return rc;
   const bool asym = kt != nullptr;
-  rc = check_fwd_flags(2, asym, dk, chunk, flags);
+  rc = check_fwd_flags(elem, asym, dk, chunk, flags);
   if (rc != DP_OK) return rc;
-  // the packed write-key form runs on the prep / chain pair only
-  if (asym && !dp::chain_asym_ok(dk, chunk)) return DP_ENOTSUP;
+  // bf16: the packed write-key form runs on the prep / chain pair only
+  if (elem == 2 && asym && !dp::chain_asym_ok(dk, chunk)) return DP_ENOTSUP;
   const int stages = flags & DP_STAGE_ALL;
   if (cu_seqlens == nullptr) return DP_EINVAL;
   if (T > 0 && (q == nullptr || k == nullptr || v == nullptr || beta == nullptr || out == nullptr))
     return DP_EINVAL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(kt)) return DP_EINVAL;
-  const bool fused = use_fused(2, asym, dk, dv, chunk, flags);
+  const bool fused = use_fused(elem, asym, dk, dv, chunk, flags);
   if (table != nullptr) {
     if (!fused) return DP_ENOTSUP;  // only the fused kernel runs on the table alone
   } else {
-    const size_t need = varlen_ws_need(vs, fused);
+    const size_t need = varlen_ws_need(vs, fused, elem);
     if (workspace_bytes < need || workspace == nullptr) return DP_EWORKSPACE;
     if (((uintptr_t)workspace & (kWsAlign - 1)) != 0) return DP_EWORKSPACE;
   }
@@ -565,6 +580,11 @@ int varlen_impl(const void* q, const void* k, const void* v, const float* beta, 
   a.cu = cu_seqlens;
   if (fused) {
     a.cbase = table != nullptr ? table : static_cast<int*>(workspace);
+  } else if (elem == 4) {
+    a.wsT = workspace;
+    a.wsS = reinterpret_cast<float2*>(static_cast<char*>(workspace) + varlen_t32_bytes(vs));
+    a.cbase = reinterpret_cast<int*>(static_cast<char*>(workspace) + varlen_t32_bytes(vs) +
+                                     varlen_s32_bytes(vs));
   } else {
     a.wsT = workspace;
     a.cbase = reinterpret_cast<int*>(static_cast<char*>(workspace) + varlen_blocks_bytes(vs));
@@ -581,13 +601,13 @@ int varlen_impl(const void* q, const void* k, const void* v, const float* beta, 
   a.kt = kt;
   a.RT = readout_rows(chunk, n_h);
   a.asym = asym ? 1 : 0;
-  a.out_f32 = (flags & DP_OUT_F32) != 0 ? 1 : 0;
+  a.out_f32 = (elem == 4 || (flags & DP_OUT_F32) != 0) ? 1 : 0;
   fastdiv_magic(n_h, &a.nh_magic, &a.nh_shift);
 
   int BV = 0, lds = 0;
-  rc = plan(a, 2, dk, chunk, &BV, &lds);
+  rc = plan(a, elem, dk, chunk, &BV, &lds);
   if (rc != DP_OK || dry) return rc;
-  const hipError_t e = dispatch_fwd(2, dk, a, chunk, BV, lds, stages, static_cast<hipStream_t>(stream));
+  const hipError_t e = dispatch_fwd(elem, dk, a, chunk, BV, lds, stages, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DP_OK : DP_EHIP;
 }
 
@@ -1315,6 +1335,24 @@ int dp_fwd_varlen_bf16(const void* q, const void* k, const void* v, const float*
                        void* workspace, size_t workspace_bytes, int flags, dp_stream stream) {
   return varlen_impl(q, k, v, beta, g, cu_seqlens, nseq, n_h, H, T, dk, dv, chunk, out, final_state,
                      h0, workspace, workspace_bytes, flags, stream);
+}
+
+int dp_fwd_varlen_f32(const float* q, const float* k, const float* v, const float* beta,
+                      const float* g, const int* cu_seqlens, int nseq, int n_h, int H, int T,
+                      int dk, int dv, int chunk, float* out, float* final_state, const float* h0,
+                      void* workspace, size_t workspace_bytes, int flags, dp_stream stream) {
+  return varlen_impl(q, k, v, beta, g, cu_seqlens, nseq, n_h, H, T, dk, dv, chunk, out, final_state,
+                     h0, workspace, workspace_bytes, flags, stream, nullptr, false, nullptr, 4);
+}
+
+int dp_fwd_varlen_wk_f32(const float* q, const float* k, const float* kt, const float* v,
+                         const float* beta, const float* g, const int* cu_seqlens, int nseq,
+                         int n_h, int H, int T, int dk, int dv, int chunk, float* out,
+                         float* final_state, const float* h0, void* workspace,
+                         size_t workspace_bytes, int flags, dp_stream stream) {
+  if (T > 0 && kt == nullptr) return DP_EINVAL;
+  return varlen_impl(q, k, v, beta, g, cu_seqlens, nseq, n_h, H, T, dk, dv, chunk, out, final_state,
+                     h0, workspace, workspace_bytes, flags, stream, nullptr, false, kt, 4);
 }
 
 int dp_fwd_varlen_wk_bf16(const void* q, const void* k, const void* kt, const void* v,

@@ -175,6 +175,35 @@ __device__ __forceinline__ SeqGeom seq_geom(const FwdArgs& p, int d, int h, int 
   return g;
 }
 
+// Work item `chunk` of a per-chunk kernel -> head bh (sequence-major) and its
+// chunk c.  Packed sequences: sequence d owns items cbase[d] H .. cbase[d+1] H
+// - 1, head-major inside; false past the last one (the grid is an upper bound).
+__device__ __forceinline__ bool chunk_item(const FwdArgs& p, long long chunk, int& bh, int& c) {
+  if (p.cu == nullptr) {
+    bh = (int)(chunk / p.nc);
+    c = (int)(chunk % p.nc);
+    return true;
+  }
+  if (chunk >= (long long)p.cbase[p.B] * p.H) return false;
+  int lo = 0, hi = p.B - 1;  // the last sequence whose first item is <= chunk: it has chunks
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((long long)p.cbase[mid] * p.H <= chunk) lo = mid; else hi = mid - 1;
+  }
+  const int ncd = p.cbase[lo + 1] - p.cbase[lo];
+  const int rel = (int)(chunk - (long long)p.cbase[lo] * p.H);
+  bh = lo * p.H + rel / ncd;
+  c = rel % ncd;
+  return true;
+}
+
+// Row of sub-step s of a head whose token 0 is token `tok` in a [.., H, n_h, *]
+// token-major tensor: ((tok + t) H + h) n_h + j with t = s / n_h, j = s % n_h.
+__device__ __forceinline__ long long sub_row_at(const FwdArgs& p, long long tok, int s, int h) {
+  const int t = fastdiv(s, p.nh_magic, p.nh_shift);
+  return ((tok + t) * p.H + h) * p.n_h + (s - t * p.n_h);
+}
+
 // Row of sub-step s of head (b, h) in a [B, L, H, n_h, *] tensor:
 // ((b L + t) H + h) n_h + j with t = s / n_h, j = s % n_h.
 __device__ __forceinline__ long long sub_row(const FwdArgs& p, int s, int b, int h) {
@@ -241,8 +270,11 @@ __global__ __launch_bounds__(kThreads) void dp_ut_kernel(FwdArgs p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const long long chunk = blockIdx.x;
-  const int bh = (int)(chunk / p.nc), c = (int)(chunk % p.nc);
+  int bh, c;
+  if (!chunk_item(p, chunk, bh, c)) return;
   const int b = bh / p.H, h = bh % p.H;
+  const SeqGeom sg = seq_geom(p, b, h, C);  // packed: this sequence's tokens and sub-steps
+  const int N = sg.N;
   const int s0 = c * C;
   const T* kp = static_cast<const T*>(p.k);
   const T* ktp = static_cast<const T*>(p.kt);
@@ -256,19 +288,19 @@ __global__ __launch_bounds__(kThreads) void dp_ut_kernel(FwdArgs p) {
     const int s = s0 + r;
     rk[it] = u32x4_t{0u, 0u, 0u, 0u};
     rkt[it] = u32x4_t{0u, 0u, 0u, 0u};
-    if (idx < KV && s < p.N) {
-      const long long off = sub_row(p, s, b, h) * DK + cg * VE;
+    if (idx < KV && s < N) {
+      const long long off = sub_row_at(p, sg.tok, s, h) * DK + cg * VE;
       rk[it] = ld16(kp + off);
       if (p.asym) rkt[it] = ld16(ktp + off);
     }
   }
   float braw = 0.f, lam = 0.f;
   bool first = false;
-  if (tid < C && s0 + tid < p.N) {
+  if (tid < C && s0 + tid < N) {
     const int s = s0 + tid;
     const int t = fastdiv(s, p.nh_magic, p.nh_shift);
     const int j = s - t * p.n_h;
-    const long long tok = (tok_base(p, b) + t) * p.H + h;
+    const long long tok = (sg.tok + t) * p.H + h;
     braw = p.beta[tok * p.n_h + j];
     first = (j == 0);
     if (p.g != nullptr && first) lam = logf(fmaxf(p.g[tok], FLT_MIN));
@@ -292,7 +324,7 @@ __global__ __launch_bounds__(kThreads) void dp_ut_kernel(FwdArgs p) {
       ss = dpp_group_sum<TPR>(ss);  // inside one DPP row
     else
       ss = group_sum<TPR>(ss);
-    if (idx < KV && cg == 0) sR[r] = (s0 + r < p.N) ? 1.f / fmaxf(sqrtf(ss), 1e-6f) : 0.f;
+    if (idx < KV && cg == 0) sR[r] = (s0 + r < N) ? 1.f / fmaxf(sqrtf(ss), 1e-6f) : 0.f;
   }
   // 3. beta range and chunk-local cumulative log-gate (C <= 64: wave 0)
   if (wave == 0) {
@@ -307,7 +339,7 @@ __global__ __launch_bounds__(kThreads) void dp_ut_kernel(FwdArgs p) {
     // once: log alpha_t + log g_t at a token's first sub-step, 0 on the others
     // and past the end (the loads are unconditional, at a valid address, so
     // that they are all in flight together)
-    const long long tokb = tok_base(p, b) * p.H + h;
+    const long long tokb = sg.tok * p.H + h;
     constexpr int GIT = C * DK / kThreads;
     static_assert(C * DK % kThreads == 0, "gate tile");
 #pragma unroll 8
@@ -315,8 +347,8 @@ __global__ __launch_bounds__(kThreads) void dp_ut_kernel(FwdArgs p) {
       const int idx = tid + it * kThreads;
       const int r = idx / DK, ch = idx % DK;
       const int s = s0 + r;
-      const int t = fastdiv(min(s, p.N - 1), p.nh_magic, p.nh_shift);
-      const bool first = s < p.N && s == t * p.n_h;
+      const int t = fastdiv(min(s, N - 1), p.nh_magic, p.nh_shift);
+      const bool first = s < N && s == t * p.n_h;
       const long long tok = tokb + (long long)t * p.H;
       float l = logf(fmaxf(p.ga[tok * DK + ch], FLT_MIN));
       if (p.g != nullptr) l += logf(fmaxf(p.g[tok], FLT_MIN));
@@ -335,7 +367,7 @@ __global__ __launch_bounds__(kThreads) void dp_ut_kernel(FwdArgs p) {
   }
   block_sync_lds();
   // (CG: the scan reads pre-normalised keys, so its key scale is 1 on rows in range)
-  if (tid < C) p.wsS[chunk * C + tid] = CG ? make_float2(s0 + tid < p.N ? 1.f : 0.f, 0.f) : make_float2(sR[tid], sG[tid]);
+  if (tid < C) p.wsS[chunk * C + tid] = CG ? make_float2(s0 + tid < N ? 1.f : 0.f, 0.f) : make_float2(sR[tid], sG[tid]);
 
   if constexpr (CG) {
     // 4'. M_ij (j < i); symmetric keys are normalised here (sR), write keys
@@ -413,7 +445,7 @@ __global__ __launch_bounds__(kThreads) void dp_ut_kernel(FwdArgs p) {
       for (int idx = tid; idx < KV; idx += kThreads) {
         const int r = idx / TPR, cg = idx % TPR;
         const int s = s0 + r;
-        if (s < p.N) {
+        if (s < N) {
           const float* gr = sGam + r * LDG + cg * VE;
           const float rr = sR[r], rw = p.asym ? 1.f : sR[r];
           float fk[VE], fw[VE];
@@ -422,7 +454,7 @@ __global__ __launch_bounds__(kThreads) void dp_ut_kernel(FwdArgs p) {
             fk[e] = to_f32(sK[r * LDK + cg * VE + e]) * rr * __expf(gr[e]);
             fw[e] = to_f32(sKt[r * LDK + cg * VE + e]) * rw * __expf(gC[cg * VE + e] - gr[e]);
           }
-          const long long off = sub_row(p, s, b, h) * DK + cg * VE;
+          const long long off = sub_row_at(p, sg.tok, s, h) * DK + cg * VE;
           st_vec16(kg + off, fk);
           st_vec16(ktg + off, fw);
         }
@@ -440,8 +472,8 @@ __global__ __launch_bounds__(kThreads) void dp_ut_kernel(FwdArgs p) {
       const int r = idx / TPR, cg = idx % TPR;
       const int s = r0 + r * n_h;
       u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-      if (s < s0 + C && s < p.N) {
-        const long long tok = (tok_base(p, b) + fastdiv(s, p.nh_magic, p.nh_shift)) * p.H + h;
+      if (s < s0 + C && s < N) {
+        const long long tok = (sg.tok + fastdiv(s, p.nh_magic, p.nh_shift)) * p.H + h;
         v = ld16(qp + tok * DK + cg * VE);
         // the scan's readout query: e^{G_loc} o q
         float fq[VE];
@@ -458,7 +490,7 @@ __global__ __launch_bounds__(kThreads) void dp_ut_kernel(FwdArgs p) {
     for (int e = tid; e < RT * C; e += kThreads) {
       const int r = e / C, j = e % C;
       const int s = r0 + r * n_h;
-      const int loc = (s < s0 + C && s < p.N) ? s - s0 : -1;
+      const int loc = (s < s0 + C && s < N) ? s - s0 : -1;
       float acc = 0.f;
       if (j <= loc) {
         const float rw = p.asym ? 1.f : sR[j];
@@ -633,15 +665,16 @@ __global__ __launch_bounds__(kThreads) void dp_scan_kernel(FwdArgs p) {
   const int bh = f / p.nvb, vb = f % p.nvb;
   const int b = bh / p.H, h = bh % p.H;
   const int v0 = vb * BV;
-  const int n_h = p.n_h, nc = p.nc;
+  const SeqGeom sg = seq_geom(p, b, h, C);  // packed: this sequence's tokens, sub-steps, chunks
+  const int n_h = p.n_h, nc = sg.nc, N = sg.N;
   const T* kp = static_cast<const T*>(p.k);
   const T* ktp = static_cast<const T*>(p.kt);
   const T* vp = static_cast<const T*>(p.v) + v0;
   const T* qp = static_cast<const T*>(p.q);
-  const OT* wsT = static_cast<const OT*>(p.wsT) + (long long)bh * nc * C * C;
-  const OT* wsP = static_cast<const OT*>(p.wsP) + (long long)bh * nc * RT * C;
-  const float2* wsS = p.wsS + (long long)bh * nc * C;
-  const long long tok0 = tok_base(p, b) * p.H + h;  // token (b, 0, h)
+  const OT* wsT = static_cast<const OT*>(p.wsT) + sg.blk0 * C * C;
+  const OT* wsP = static_cast<const OT*>(p.wsP) + sg.blk0 * RT * C;
+  const float2* wsS = p.wsS + sg.blk0 * C;
+  const long long tok0 = sg.tok * p.H + h;  // token (b, 0, h)
 
   // row indices of chunk c's sub-steps / readout tokens into buffer c & 1
   auto index_chunk = [&](int c) {
@@ -651,7 +684,7 @@ __global__ __launch_bounds__(kThreads) void dp_scan_kernel(FwdArgs p) {
     if (tid < C) {
       const int s = s0 + tid;
       long long row = 0;
-      if (s < p.N) {
+      if (s < N) {
         const int t = fastdiv(s, p.nh_magic, p.nh_shift);
         row = (tok0 + (long long)t * p.H) * n_h + (s - t * n_h);
       }
@@ -660,7 +693,7 @@ __global__ __launch_bounds__(kThreads) void dp_scan_kernel(FwdArgs p) {
     if (tid < RT) {
       const int r0 = s0 + (n_h - 1 - (s0 - fastdiv(s0, p.nh_magic, p.nh_shift) * n_h));
       const int s = r0 + tid * n_h;
-      toks[tid] = (s < s0 + C && s < p.N) ? tok0 + (long long)fastdiv(s, p.nh_magic, p.nh_shift) * p.H
+      toks[tid] = (s < s0 + C && s < N) ? tok0 + (long long)fastdiv(s, p.nh_magic, p.nh_shift) * p.H
                                            : -1;
     }
   };
@@ -699,7 +732,7 @@ __global__ __launch_bounds__(kThreads) void dp_scan_kernel(FwdArgs p) {
       }
     }
     rg = ssrc[min(tid, C - 1)].y;
-    if constexpr (CG) rdec = p.wsDec[((long long)bh * nc + c) * DK + min(tid, DK - 1)];
+    if constexpr (CG) rdec = p.wsDec[(sg.blk0 + c) * DK + min(tid, DK - 1)];
 #pragma unroll
     for (int it = 0; it < QIT; ++it) {
       const int idx = (QV % kThreads == 0) ? tid + it * kThreads : min(tid + it * kThreads, QV - 1);
@@ -734,7 +767,7 @@ __global__ __launch_bounds__(kThreads) void dp_scan_kernel(FwdArgs p) {
         if (CG && !p.asym) st_vec16(sKt + r * LDK + cg * VE, fv);  // write keys: the unit keys
         if (p.asym) {
           unpack16(rkt[it], fv, LT{});
-          const float keep = (s0 + r < p.N) ? 1.f : 0.f;
+          const float keep = (s0 + r < N) ? 1.f : 0.f;
 #pragma unroll
           for (int e = 0; e < VE; ++e) fv[e] *= keep;
           st_vec16(sKt + r * LDK + cg * VE, fv);
@@ -775,7 +808,7 @@ __global__ __launch_bounds__(kThreads) void dp_scan_kernel(FwdArgs p) {
       if (VV % kThreads == 0 || idx < VV) {
         float fv[VE];
         unpack16(rvv[it], fv, T{});
-        const float keep = (s0 + r < p.N) ? 1.f : 0.f;
+        const float keep = (s0 + r < N) ? 1.f : 0.f;
 #pragma unroll
         for (int e = 0; e < VE; e += 4)
           st4(sV + r * LDV + cv * VE + e, fv[e] * keep, fv[e + 1] * keep, fv[e + 2] * keep,
@@ -1701,7 +1734,14 @@ hipError_t launch_ut(const FwdArgs& a, hipStream_t st) {
   const int lds = ut_lds_bytes((int)sizeof(T), DK, C, a.asym);
   static const bool attr = allow_big_lds(reinterpret_cast<const void*>(&dp_ut_kernel<T, DK, C>));
   (void)attr;
-  const long long nchunks = (long long)a.B * a.H * a.nc;
+  long long nchunks = (long long)a.B * a.H * a.nc;
+  if (a.cu != nullptr) {  // packed sequences: per-sequence chunk counts first
+    hipLaunchKernelGGL((dp_varlen_chunks_kernel<C>), dim3(1), dim3(256), 0, st, a.cu, a.B, a.n_h, a.L, a.cbase);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    nchunks = a.nwork;
+  }
+  if (nchunks == 0) return hipSuccess;
   hipLaunchKernelGGL((dp_ut_kernel<T, DK, C>), dim3((unsigned)nchunks), dim3(kThreads), lds, st, a);
   return hipGetLastError();
 }

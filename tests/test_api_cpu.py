@@ -357,10 +357,17 @@ def test_varlen_workspace_size(lib):
     assert lib.dp_fwd_varlen_workspace_size(3, 5, 3, 1000, 128, 128, 64, ctypes.byref(n)) == 0
     blocks = -(-3 * (47 + 5) * bf16_chunk_block(128, 64, 3, write_keys=True) // 256) * 256
     assert n.value == blocks + 256 + -(-5 * 3 * 8 * 64 * 4 // 256) * 256
+    # the fp32 layout (T, C x C fp32, and C float2 per work item, then the chunk
+    # offsets) is the larger one at dk 16; one size serves both input types
+    up = lambda x: -(-x // 256) * 256
+    nwork = 3 * (47 + 5)
+    fp32 = up(nwork * 64 * 64 * 4) + up(nwork * 64 * 8) + 256
+    assert fp32 < n.value  # dk 128: the bf16 blocks are larger
     # dk 16: no write-key form on the pair, blocks without write keys
     assert lib.dp_fwd_varlen_workspace_size(3, 5, 3, 1000, 16, 16, 64, ctypes.byref(n)) == 0
     blocks = -(-3 * (47 + 5) * bf16_chunk_block(16, 64, 3) // 256) * 256
-    assert n.value == blocks + 256 + -(-5 * 3 * 1 * 64 * 4 // 256) * 256
+    bf16 = blocks + 256 + -(-5 * 3 * 1 * 64 * 4 // 256) * 256
+    assert n.value == max(bf16, fp32) == fp32
     assert lib.dp_fwd_varlen_workspace_size(3, 0, 3, 1000, 128, 128, 64, ctypes.byref(n)) == \
         dp.binding.DP_EINVAL
 

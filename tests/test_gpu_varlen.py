@@ -171,3 +171,54 @@ def test_long_sequence_32k_sampled_heads():
     e_fs = rel_err(f64(fs.cpu()[:, heads]), fo)
     say(f"  L=32768 out err {e_out:.3e}, state err {e_fs:.3e}")
     assert e_out <= TOL["bf16"] and e_fs <= TOL["bf16"]
+
+
+# fp32 inputs: the UT / scan kernels on packed sequences
+F32_CASES = [
+    ("c1", dict(H=3), [0, 1, 17, 64, 100, 5, 0, 33]),               # dk 16, chunk 16
+    ("c3", dict(H=2, dk=64, dv=64, dtype="f32"), [90, 0, 257, 33, 1]),
+    ("c4", dict(H=2, dk=32, dv=64, dtype="f32"), [70, 1, 0, 129]),   # gated, h0
+]
+
+
+@pytest.mark.parametrize("name,kw,lengths", F32_CASES, ids=[f"{c[0]}-{i}" for i, c in enumerate(F32_CASES)])
+def test_varlen_f32_matches_each_sequence_alone(name, kw, lengths):
+    """The fp32 packed forward against the oracle on each sequence alone (1e-4)
+    and against dp_fwd_f32 on each sequence alone, bit for bit."""
+    w = WORKLOADS[name].scaled(**kw)
+    assert w.dtype == "f32"
+    say(f"case varlen f32 {name} {kw} lengths={lengths}")
+    pk, h0, cu = packed_inputs(w, lengths)
+    out, fs = run_gpu(pk, h0, cu, w.chunk)
+    check_all(out, fs, pk, h0, cu, TOL["f32"], f"varlen-f32-{name}")
+    for d, n in enumerate(lengths):
+        if n == 0:
+            continue
+        a = int(cu[d])
+        one = lambda x: None if x is None else x[a:a + n].unsqueeze(0).cuda()
+        o1, f1 = dp.fwd(one(pk["q"]), one(pk["k"]), one(pk["v"]), one(pk["beta"]), one(pk["g"]),
+                        chunk=w.chunk, h0=None if h0 is None else h0[d:d + 1].cuda())
+        torch.cuda.synchronize()
+        assert torch.equal(out[a:a + n], o1[0].cpu()), f"sequence {d}: out differs"
+        assert torch.equal(fs[d], f1[0].cpu()), f"sequence {d}: final state differs"
+
+
+def test_varlen_f32_write_keys():
+    """The fp32 packed forward with write keys (dp_fwd_varlen_wk_f32) against the
+    oracle on each sequence alone."""
+    w = WORKLOADS["c3"].scaled(H=2, dk=32, dv=32, n_h=2, dtype="f32")
+    lengths = [40, 0, 97, 1, 64]
+    pk, h0, cu = packed_inputs(w, lengths)
+    T = int(sum(lengths))
+    kt = 0.5 * make(w.scaled(B=1, L=T), seed=w.seed + 9)["k"][0].contiguous()
+    out, fs = dp.fwd_varlen(pk["q"].cuda(), pk["k"].cuda(), pk["v"].cuda(), pk["beta"].cuda(), cu.cuda(),
+                            chunk=w.chunk, kt=kt.cuda())
+    torch.cuda.synchronize()
+    out, fs = out.cpu(), fs.cpu()
+    for d, n in enumerate(lengths):
+        a = int(cu[d])
+        sl = lambda x: x[a:a + n].unsqueeze(0)
+        oo, fo = oracle.fwd(sl(pk["q"]), sl(pk["k"]), sl(pk["v"]), sl(pk["beta"]), kt=sl(kt))
+        if n > 0:
+            assert rel_err(f64(out[a:a + n]), oo[0]) <= TOL["f32"], f"sequence {d}: out"
+        assert rel_err(f64(fs[d]), fo[0]) <= TOL["f32"], f"sequence {d}: final state"
